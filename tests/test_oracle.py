@@ -1,0 +1,343 @@
+"""Pins for the CPU oracle, independent of its own code (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one in the causal bound,
+a wrong fork point) fails at least one of them:
+
+* stream-level fp64 brute force with a dense tree mask and a token-level
+  recurrence that follows parent pointers (tests/brute.py), over every parent
+  array with up to 5 segments and several length patterns;
+* library scaled-dot-product attention on single-segment and chain trees;
+* closed forms of the Gated DeltaNet recurrence;
+* option independence: adding, removing or permuting sibling options leaves
+  every other branch bitwise unchanged (Flide page on techfi24.com, section
+  "Presentation": one answer per request, independent of the other options).
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import brute
+from tree_structured_decision_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def all_parent_arrays(S):
+    choices = [[-1]] + [list(range(-1, s)) for s in range(1, S)]
+    for combo in itertools.product(*choices):
+        yield np.array(combo, np.int32)
+
+
+def rand_inputs(rng, T, H=2, Hkv=1, D=8, dk=4, dv=3):
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    gq = rng.standard_normal((T, H, dk)).astype(np.float32)
+    gk = rng.standard_normal((T, H, dk)).astype(np.float32)
+    gk /= np.linalg.norm(gk, axis=-1, keepdims=True)
+    gv = rng.standard_normal((T, H, dv)).astype(np.float32)
+    a = rng.uniform(0.8, 1.0, (T, H)).astype(np.float32)
+    b = rng.uniform(0.0, 1.0, (T, H)).astype(np.float32)
+    return q, k, v, gq, gk, gv, a, b
+
+
+# ----------------------------------------------------------------- metadata
+
+def independent_meta(parent, seg_len):
+    """Index arrays by a different route: numpy cumsum/repeat and an explicit
+    ancestor walk per token."""
+    seg_len = np.asarray(seg_len, np.int64)
+    start = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
+    tok_seg = np.repeat(np.arange(len(seg_len)), seg_len)
+    tok_pos = np.arange(seg_len.sum()) - start[tok_seg]
+    anc = [sum(seg_len[x] for x in brute.ancestors(parent, s)) for s in range(len(parent))]
+    depth = [len(brute.ancestors(parent, s)) for s in range(len(parent))]
+    root = [([s] + brute.ancestors(parent, s))[-1] for s in range(len(parent))]
+    return dict(seg_start=start, tok_seg=tok_seg, tok_pos=tok_pos,
+                tok_iso_pos=np.asarray(anc)[tok_seg] + tok_pos, anc_len=np.asarray(anc),
+                depth=np.asarray(depth), root=np.asarray(root))
+
+
+def test_meta_golden_tiny_tree():
+    """Hand-written index arrays for the 32 + 4x8 tree (tests/golden)."""
+    path = os.path.join(GOLDEN, "meta_prefix32_4x8.txt")
+    gold = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            name, vals = line.split(":")
+            gold[name.strip()] = np.array([int(x) for x in vals.split()], np.int32)
+    m = oracle.meta(gold["parent"], gold["seg_len"])
+    for name in ("seg_start", "depth", "root", "anc_len", "tok_seg", "tok_pos", "tok_iso_pos"):
+        np.testing.assert_array_equal(m[name], gold[name], err_msg=name)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_meta_and_mask_exhaustive(S):
+    for parent in all_parent_arrays(S):
+        for lens in itertools.product([1, 2, 3], repeat=S):
+            lens = np.array(lens, np.int32)
+            m = oracle.meta(parent, lens)
+            ref = independent_meta(parent, lens)
+            for name, val in ref.items():
+                np.testing.assert_array_equal(m[name], val, err_msg=name)
+            np.testing.assert_array_equal(oracle.mask(parent, lens).astype(bool),
+                                          brute.brute_mask(parent, lens))
+
+
+def test_invalid_trees_rejected():
+    bad = [([0], [1]), ([-1, 1], [1, 1]), ([-1, 2, 0], [1, 1, 1]), ([-2], [1]),
+           ([-1, 0], [1, 0]), ([-1], [-3])]
+    for parent, lens in bad:
+        with pytest.raises(oracle.OracleError):
+            oracle.meta(np.array(parent, np.int32), np.array(lens, np.int32))
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
+def test_attention_vs_stream_brute_force(S):
+    rng = np.random.default_rng(10 + S)
+    patterns = [np.ones(S), np.full(S, 2), (np.arange(S) % 3) + 1]
+    for parent in all_parent_arrays(S):
+        for lens in patterns:
+            lens = lens.astype(np.int32)
+            T = int(lens.sum())
+            q, k, v = rand_inputs(rng, T, H=4, Hkv=2)[:3]
+            o, lse = oracle.attention(parent, lens, q, k, v)
+            ob, lb = brute.brute_attention(parent, lens, q, k, v)
+            np.testing.assert_allclose(o, ob, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(lse, lb, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_random_deeper_trees():
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        parent, lens = W.random_tree(rng, n_segments=int(rng.integers(3, 9)), max_len=5,
+                                     max_depth=4, roots=int(rng.integers(1, 3)))
+        T = int(lens.sum())
+        q, k, v = rand_inputs(rng, T, H=6, Hkv=3, D=5)[:3]
+        o, lse = oracle.attention(parent, lens, q, k, v, scale=0.7)
+        ob, lb = brute.brute_attention(parent, lens, q, k, v, scale=0.7)
+        np.testing.assert_allclose(o, ob, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, lb, rtol=1e-10, atol=1e-12)
+
+
+def _sdpa_causal(q, k, v, G):
+    """torch fp64 causal SDPA over one sequence; q [T,H,D], k/v [T,Hkv,D]."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(G, dim=1).permute(1, 0, 2)
+    vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(G, dim=1).permute(1, 0, 2)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    return out.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (8, 1)])
+def test_single_segment_is_causal_sdpa(H, Hkv):
+    rng = np.random.default_rng(H * 10 + Hkv)
+    T, D = 37, 16
+    q, k, v = rand_inputs(rng, T, H=H, Hkv=Hkv, D=D)[:3]
+    o, _ = oracle.attention(np.array([-1], np.int32), np.array([T], np.int32), q, k, v)
+    np.testing.assert_allclose(o, _sdpa_causal(q, k, v, H // Hkv), rtol=1e-10, atol=1e-12)
+
+
+def test_chain_tree_equals_one_sequence():
+    rng = np.random.default_rng(3)
+    lens = np.array([5, 1, 7, 3, 9], np.int32)
+    parent = np.array([-1, 0, 1, 2, 3], np.int32)
+    T = int(lens.sum())
+    q, k, v = rand_inputs(rng, T, H=4, Hkv=2, D=8)[:3]
+    o, _ = oracle.attention(parent, lens, q, k, v)
+    np.testing.assert_allclose(o, _sdpa_causal(q, k, v, 2), rtol=1e-10, atol=1e-12)
+    o1, _ = oracle.attention(np.array([-1], np.int32), np.array([T], np.int32), q, k, v)
+    np.testing.assert_array_equal(o, o1)
+
+
+def test_option_branch_equals_isolated_sequence():
+    """Each option's rows equal the tail of causal SDPA over prefix + option."""
+    rng = np.random.default_rng(4)
+    parent, lens = W.tree_one_level(11, [3, 6, 2])
+    T = int(lens.sum())
+    q, k, v = rand_inputs(rng, T, H=4, Hkv=2, D=8)[:3]
+    o, _ = oracle.attention(parent, lens, q, k, v)
+    st = brute.seg_starts(lens)
+    for s in range(1, 4):
+        idx = np.concatenate([np.arange(11), np.arange(st[s], st[s] + lens[s])])
+        ref = _sdpa_causal(q[idx], k[idx], v[idx], 2)
+        np.testing.assert_allclose(o[st[s]:st[s] + lens[s]], ref[11:], rtol=1e-10, atol=1e-12)
+
+
+def test_token_select_matches_full():
+    wl = W.tiny_one_level()
+    o, lse = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v)
+    sel = np.zeros(wl.T, np.uint8)
+    sel[[0, 5, 31, 32, 47, 63]] = 1
+    os_, ls = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, tok_select=sel)
+    rows = sel.astype(bool)
+    np.testing.assert_array_equal(os_[rows], o[rows])
+    np.testing.assert_array_equal(ls[rows], lse[rows])
+    assert np.isnan(os_[~rows]).all()
+
+
+# --------------------------------------------------------------------- GDN
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
+def test_gdn_vs_stream_brute_force(S):
+    rng = np.random.default_rng(100 + S)
+    patterns = [np.ones(S), (np.arange(S) % 3) + 1]
+    for parent in all_parent_arrays(S):
+        for lens in patterns:
+            lens = lens.astype(np.int32)
+            T = int(lens.sum())
+            _, _, _, gq, gk, gv, a, b = rand_inputs(rng, T, H=2)
+            R = int((parent < 0).sum())
+            rs = (0.3 * rng.standard_normal((R, 2, 3, 4))).astype(np.float32)
+            o, s0, s1 = oracle.gdn(parent, lens, gq, gk, gv, a, b, root_state=rs, scale=0.9)
+            ob, b0, b1 = brute.brute_gdn(parent, lens, gq, gk, gv, a, b, root_state=rs, scale=0.9)
+            np.testing.assert_allclose(o, ob, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(s0, b0, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(s1, b1, rtol=1e-10, atol=1e-12)
+
+
+def test_gdn_random_deeper_trees_zero_root():
+    rng = np.random.default_rng(9)
+    for trial in range(10):
+        parent, lens = W.random_tree(rng, n_segments=int(rng.integers(3, 9)), max_len=6,
+                                     max_depth=4, roots=int(rng.integers(1, 3)))
+        T = int(lens.sum())
+        _, _, _, gq, gk, gv, a, b = rand_inputs(rng, T, H=3, dk=5, dv=4)
+        o, s0, s1 = oracle.gdn(parent, lens, gq, gk, gv, a, b)
+        ob, b0, b1 = brute.brute_gdn(parent, lens, gq, gk, gv, a, b)
+        np.testing.assert_allclose(o, ob, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(s0, b0, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(s1, b1, rtol=1e-10, atol=1e-12)
+
+
+def test_gdn_no_write_is_pure_decay():
+    """b = 0: o_t = (prod of a up to t) * S0 q_t, and the state only decays."""
+    rng = np.random.default_rng(11)
+    parent, lens = W.tree_one_level(6, [4, 3])
+    T = int(lens.sum())
+    _, _, _, gq, gk, gv, a, _ = rand_inputs(rng, T, H=2, dk=4, dv=3)
+    b = np.zeros_like(a)
+    S0 = rng.standard_normal((1, 2, 3, 4)).astype(np.float32)
+    o, s0, s1 = oracle.gdn(parent, lens, gq, gk, gv, a, b, root_state=S0)
+    st = brute.seg_starts(lens)
+    for s in range(3):
+        path = ([0] if s else []) + [s]
+        toks = np.concatenate([np.arange(st[x], st[x] + lens[x]) for x in path])
+        cum = np.cumprod(a[toks].astype(np.float64), axis=0)
+        own = toks[-lens[s]:]
+        for i, t in enumerate(own):
+            c = cum[len(toks) - lens[s] + i]
+            for h in range(2):
+                ref = c[h] * (S0[0, h].astype(np.float64) @ gq[t, h].astype(np.float64))
+                np.testing.assert_allclose(o[t, h], ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(s1[s], cum[-1][:, None, None] * S0[0], rtol=1e-12)
+
+
+def test_gdn_full_write_reads_back_value():
+    """a = 1, b = 1, unit k: S_t k_t = v_t, so q_t = k_t returns v_t; after
+    writing orthonormal keys, reading any of them returns its value."""
+    rng = np.random.default_rng(12)
+    dk, dv = 8, 3
+    # rows of blockdiag(H4, H4) / 2 (H4 a 4x4 Hadamard matrix): entries +-0.5,
+    # exactly orthonormal in float32
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], np.float32)
+    basis = np.zeros((dk, dk), np.float32)
+    basis[:4, :4] = h4 / 2
+    basis[4:, 4:] = h4 / 2
+    parent, lens = W.tree_one_level(4, [2, 2])
+    T = 8
+    gk = np.zeros((T, 1, dk), np.float32)
+    order = [0, 1, 2, 3, 4, 5, 4, 5]
+    for t, i in enumerate(order):
+        gk[t, 0] = basis[i]
+    gv = rng.standard_normal((T, 1, dv)).astype(np.float32)
+    a = np.ones((T, 1), np.float32)
+    b = np.ones((T, 1), np.float32)
+    o, s0, s1 = oracle.gdn(parent, lens, gk.copy(), gk, gv, a, b)
+    np.testing.assert_allclose(o[:, 0], gv[:, 0], atol=1e-12)
+    # after the prefix + first option (keys 0..5), reading key i returns its value
+    S = s1[1, 0]
+    for t, i in enumerate(order[:6]):
+        np.testing.assert_allclose(S @ basis[i].astype(np.float64), gv[t, 0], atol=1e-12)
+    # the second option was forked from the prefix: its start state knows keys 0..3 only
+    np.testing.assert_array_equal(s0[2], s1[0])
+    np.testing.assert_allclose(s0[2, 0] @ basis[4].astype(np.float64), 0, atol=1e-12)
+
+
+def test_gdn_identity_dynamics_keep_state():
+    """a = 1, b = 0: the state never changes, o_t = S0 q_t."""
+    rng = np.random.default_rng(13)
+    parent, lens = W.tree_three_level(3, 2, 2, 2, 2)
+    T = int(lens.sum())
+    _, _, _, gq, gk, gv, _, _ = rand_inputs(rng, T, H=2, dk=4, dv=3)
+    a = np.ones((T, 2), np.float32)
+    b = np.zeros((T, 2), np.float32)
+    S0 = rng.standard_normal((1, 2, 3, 4)).astype(np.float32)
+    o, s0, s1 = oracle.gdn(parent, lens, gq, gk, gv, a, b, root_state=S0)
+    for s in range(len(parent)):
+        np.testing.assert_array_equal(s0[s], S0[0])
+        np.testing.assert_array_equal(s1[s], S0[0])
+    ref = np.einsum("hvk,thk->thv", S0[0].astype(np.float64), gq.astype(np.float64))
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_fork_copies_parent_end_state():
+    wl = W.tiny_one_level()
+    o, s0, s1 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b)
+    for s in range(1, wl.S):
+        np.testing.assert_array_equal(s0[s], s1[0])
+    assert np.all(s0[0] == 0)
+
+
+# ------------------------------------------------------ option independence
+
+def test_sibling_add_remove_permute_bitwise():
+    """Adding, removing or reordering options leaves every other branch's rows
+    bitwise unchanged."""
+    rng = np.random.default_rng(21)
+    prefix = 9
+    opt_lens = [3, 5, 2, 4]
+    D, dk, dv = 8, 4, 3
+    pre = rand_inputs(rng, prefix, H=2, Hkv=1, D=D, dk=dk, dv=dv)
+    opts = [rand_inputs(rng, L, H=2, Hkv=1, D=D, dk=dk, dv=dv) for L in opt_lens]
+
+    def run(order):
+        parent, lens = W.tree_one_level(prefix, [opt_lens[i] for i in order])
+        cat = [np.concatenate([pre[j]] + [opts[i][j] for i in order]) for j in range(8)]
+        q, k, v, gq, gk, gv, a, b = cat
+        o, _ = oracle.attention(parent, lens, q, k, v)
+        go, _, _ = oracle.gdn(parent, lens, gq, gk, gv, a, b)
+        st = brute.seg_starts(lens)
+        rows = {i: (o[st[n + 1]:st[n + 1] + lens[n + 1]], go[st[n + 1]:st[n + 1] + lens[n + 1]])
+                for n, i in enumerate(order)}
+        return rows, (o[:prefix], go[:prefix])
+
+    base, base_pre = run([0, 1, 2, 3])
+    for order in ([3, 1, 0, 2], [2], [1, 3], [0, 1, 2, 3, 3]):
+        rows, pre_rows = run(order)
+        np.testing.assert_array_equal(pre_rows[0], base_pre[0])
+        np.testing.assert_array_equal(pre_rows[1], base_pre[1])
+        for i in set(order):
+            np.testing.assert_array_equal(rows[i][0], base[i][0])
+            np.testing.assert_array_equal(rows[i][1], base[i][1])
+
+
+def test_f32_build_close_to_f64():
+    wl = W.tiny_one_level()
+    o64, l64 = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v)
+    o32, l32 = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, prec="f32")
+    assert o32.dtype == np.float32
+    np.testing.assert_allclose(o32, o64, atol=1e-5)
+    g64 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b)[0]
+    g32 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b, prec="f32")[0]
+    np.testing.assert_allclose(g32, g64, atol=1e-4)
