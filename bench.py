@@ -1,0 +1,399 @@
+"""Benchmark of the ForkAttention hot path on one MI355X.
+
+A step is one pass of the whole path over one decision request: segment
+metadata build (host plan + upload + per-token expansion), tree attention and
+the forked Gated DeltaNet layer. The headline workload is one decision request
+(prefix 2048 + 16 options of 16-48 tokens, bf16, attention 16/2/128, Gated
+DeltaNet 16 x 128 x 128). `value` is stream tokens per second (every physical
+token counted once) with inputs resident in HBM.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel's algorithmic work per launch over its mean
+                launch time (HIP events on the launch stream) vs MI355X peak;
+  cpu_baseline  the CPU oracle timed on this host's cores on the same request;
+  fidelity      total-variation distance of per-option softmax scores vs the
+                float32 oracle, argmax agreement;
+  workloads     throughput of all five synthetic workloads (the request mix
+                runs as graph replay of a capacity bucket).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "branch tokens/s for ForkAttention + GDN fork layer; % of HBM/MFMA roofline"
+PEAK_BF16_MFMA = 2.5e15      # dense, FLOP/s
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12            # B/s
+# capacity buckets for graph replay (tokens, segments)
+BUCKETS_T = [1 << 16, 1 << 17, 1 << 18, 3 << 17, 1 << 19]
+BUCKETS_S = [1 << 9, 1 << 12, 1 << 13]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic work
+
+def visible_pairs(parent, seg_len) -> int:
+    """Sum over tokens of (ancestor tokens + position in segment + 1)."""
+    parent = np.asarray(parent)
+    seg_len = np.asarray(seg_len, np.int64)
+    anc = np.zeros(len(parent), np.int64)
+    for s in range(len(parent)):
+        if parent[s] >= 0:
+            anc[s] = anc[parent[s]] + seg_len[parent[s]]
+    return int(np.sum(anc * seg_len + seg_len * (seg_len + 1) // 2))
+
+
+def attn_work(parent, seg_len, H, Hkv, D, elt):
+    T = int(np.sum(seg_len))
+    flops = 4.0 * D * H * visible_pairs(parent, seg_len)
+    bytes_ = float(T * (2 * H + 2 * Hkv) * D * elt)
+    return flops, bytes_
+
+
+def gdn_work(parent, seg_len, H, dk, dv, elt, root_state: bool):
+    T = int(np.sum(seg_len))
+    S = len(parent)
+    R = int(np.sum(np.asarray(parent) < 0))
+    io = T * H * ((2 * dk + 2 * dv) * elt + 8)        # q, k, v, o + a, b
+    fork = S * H * dk * dv * 4                         # every segment's start state written once
+    rs = R * H * dk * dv * 4 if root_state else 0
+    return float(io + fork + rs)
+
+
+# ------------------------------------------------------------------ runners
+
+def pick_bucket(T, S):
+    for tc in BUCKETS_T:
+        for sc in BUCKETS_S:
+            if T <= tc and S <= sc:
+                return tc, sc
+    return int(T), int(S)
+
+
+class Runner:
+    """Device buffers and one step of the path for one workload."""
+
+    def __init__(self, wl_meta: dict, tensors: dict, graph: bool):
+        import torch
+        from tree_structured_decision_amd.session import ForkSession
+
+        self.m = wl_meta
+        self.t = tensors
+        T, S = wl_meta["T"], wl_meta["S"]
+        depth = wl_meta["depth"]
+        if graph:
+            t_cap, s_cap = pick_bucket(T, S)
+            depth_cap = max(3, depth)
+        else:
+            t_cap, s_cap, depth_cap = T, S, depth
+        self.caps = (t_cap, s_cap, depth_cap)
+        self.sess = ForkSession(t_cap, s_cap, depth_cap, wl_meta["H"] // wl_meta["Hkv"],
+                                gH=wl_meta["gH"], dk=wl_meta["dk"], dv=wl_meta["dv"])
+        dev = "cuda"
+        qd = tensors["q"].dtype
+        H, D, gH, dv, dk = wl_meta["H"], wl_meta["D"], wl_meta["gH"], wl_meta["dv"], wl_meta["dk"]
+        self.o = torch.empty((t_cap, H, D), dtype=qd, device=dev)
+        self.lse = torch.empty((t_cap, H), dtype=torch.float32, device=dev)
+        self.go = torch.empty((t_cap, gH, dv), dtype=qd, device=dev)
+        self.st0 = torch.empty((s_cap, gH, dv, dk), dtype=torch.float32, device=dev)
+        self.graph = graph
+        self.sess.build(wl_meta["parent"], wl_meta["seg_len"])
+        if graph:
+            t = tensors
+            self.sess.capture(dict(q=t["q"], k=t["k"], v=t["v"], o=self.o, lse=self.lse),
+                              dict(q=t["gq"], k=t["gk"], v=t["gv"], a=t["a"], b=t["b"],
+                                   root_state=t.get("root_state"), o=self.go,
+                                   seg_start_state=self.st0))
+
+    def step(self, ev=None):
+        t = self.t
+        self.sess.build(self.m["parent"], self.m["seg_len"])
+        if self.graph:
+            if ev:
+                ev[0].record()
+            self.sess.replay()
+            if ev:
+                ev[2].record()
+            return
+        if ev:
+            ev[0].record()
+        self.sess.attention(t["q"], t["k"], t["v"], self.o, self.lse)
+        if ev:
+            ev[1].record()
+        self.sess.gdn(t["gq"], t["gk"], t["gv"], t["a"], t["b"], self.go, self.st0,
+                      root_state=t.get("root_state"))
+        if ev:
+            ev[2].record()
+
+
+def time_runner(r: Runner, steps: int, warmup: int):
+    import torch
+
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        r.step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if r.graph:
+        pair = [e[0].elapsed_time(e[2]) for e in evs]
+        attn = gdn = None
+    else:
+        attn = [e[0].elapsed_time(e[1]) for e in evs]
+        gdn = [e[1].elapsed_time(e[2]) for e in evs]
+        pair = [a + g for a, g in zip(attn, gdn)]
+    med = lambda x: None if x is None else float(np.median(x)) * 1e-3  # seconds
+    mean = lambda x: None if x is None else float(np.mean(x)) * 1e-3
+    return dict(wall=wall, ms_per_step=wall / steps * 1e3, attn_mean=mean(attn),
+                attn_p50=med(attn), gdn_mean=mean(gdn), gdn_p50=med(gdn), pair_p50=med(pair),
+                pair_p95=None if pair is None else float(np.percentile(pair, 95)) * 1e-3)
+
+
+def tensors_from_numpy(wl):
+    from tree_structured_decision_amd.session import to_device
+
+    return to_device(wl, "cuda")
+
+
+def tensors_on_device(name, parent, seg_len, H, Hkv, D, gH, dk, dv, seed, gates, root_std):
+    """Draw a workload's tensors directly on the GPU (same shapes and
+    distributions as the numpy workloads; used for the large ones where a
+    host-side draw would dominate the run)."""
+    import torch
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    T = int(np.sum(seg_len))
+    R = int(np.sum(np.asarray(parent) < 0))
+    bf = torch.bfloat16
+    rn = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+    q = rn(T, H, D).to(bf)
+    k = rn(T, Hkv, D).to(bf)
+    v = rn(T, Hkv, D).to(bf)
+    gq = rn(T, gH, dk).to(bf)
+    gk = rn(T, gH, dk)
+    gk = (gk / gk.norm(dim=-1, keepdim=True)).to(bf)
+    gv = rn(T, gH, dv).to(bf)
+    if gates == "uniform":
+        a = 0.9 + 0.1 * torch.rand(T, gH, generator=g, device="cuda")
+        b = torch.rand(T, gH, generator=g, device="cuda")
+    else:
+        a = torch.sigmoid(3.0 + 0.5 * rn(T, gH))
+        b = torch.sigmoid(rn(T, gH))
+    out = dict(q=q, k=k, v=v, gq=gq, gk=gk, gv=gv, a=a.contiguous(), b=b.contiguous())
+    out["root_state"] = None if root_std is None else (root_std * rn(R, gH, dv, dk)).contiguous()
+    return out
+
+
+def depth_of(parent):
+    parent = np.asarray(parent)
+    d = np.zeros(len(parent), np.int64)
+    for s in range(len(parent)):
+        if parent[s] >= 0:
+            d[s] = d[parent[s]] + 1
+    return int(d.max())
+
+
+def wl_meta_of(parent, seg_len, H, Hkv, D, gH, dk, dv):
+    return dict(parent=np.asarray(parent, np.int32), seg_len=np.asarray(seg_len, np.int32),
+                T=int(np.sum(seg_len)), S=len(parent), depth=depth_of(parent), H=H, Hkv=Hkv, D=D,
+                gH=gH, dk=dk, dv=dv)
+
+
+# --------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, threads):
+    import oracle
+
+    oracle.set_threads(threads, "f32")
+    t0 = time.perf_counter()
+    o, _ = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, prec="f32")
+    go, _, _ = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b,
+                          root_state=wl.root_state, prec="f32")
+    dt = time.perf_counter() - t0
+    return dt, o, go
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-workloads", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the path's multi-GPU sharding is a design note, not an implementation.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tree_structured_decision_amd import metrics
+    from tree_structured_decision_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    if args.only:
+        run_one(args.only, args.steps, args.warmup)
+        return
+
+    # ---------------- headline: one decision request
+    wl = W.one_request()
+    meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
+    r = Runner(meta, tensors_from_numpy(wl), graph=False)
+    log(f"headline {wl.name}: T={wl.T} S={wl.S}; warmup {args.warmup}, steps {args.steps}")
+    res = time_runner(r, args.steps, args.warmup)
+    T = wl.T
+    fl, ab = attn_work(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, 2)
+    gb = gdn_work(wl.parent, wl.seg_len, wl.gH, wl.dk, wl.dv, 2, wl.root_state is not None)
+    attn_ach = fl / res["attn_mean"]
+    gdn_ach = gb / res["gdn_mean"]
+    kernels = {
+        "fork_attn_forward": dict(mean_us=res["attn_mean"] * 1e6, p50_us=res["attn_p50"] * 1e6,
+                                  algorithmic_flop=fl, algorithmic_bytes=ab,
+                                  achieved_tflops=attn_ach / 1e12,
+                                  mfma_frac=attn_ach / PEAK_BF16_MFMA),
+        "gdn_fork_forward": dict(mean_us=res["gdn_mean"] * 1e6, p50_us=res["gdn_p50"] * 1e6,
+                                 algorithmic_bytes=gb, achieved_gbs=gdn_ach / 1e9,
+                                 hbm_frac=gdn_ach / PEAK_HBM),
+    }
+    if res["attn_mean"] >= res["gdn_mean"]:
+        roof = dict(kernel="fork_attn_forward", bound="mfma", achieved=attn_ach / 1e12,
+                    peak=PEAK_BF16_MFMA / 1e12, unit="TFLOP/s", frac=attn_ach / PEAK_BF16_MFMA,
+                    traffic=None)
+    else:
+        roof = dict(kernel="gdn_fork_forward", bound="hbm", achieved=gdn_ach / 1e9,
+                    peak=PEAK_HBM / 1e9, unit="GB/s", frac=gdn_ach / PEAK_HBM, traffic=None)
+
+    # fidelity + CPU baseline (the float32 oracle serves both)
+    o_gpu = r.o[:T].float().cpu().numpy()
+    go_gpu = r.go[:T].float().cpu().numpy()
+    cpu = None
+    fid = None
+    if not args.no_cpu:
+        threads = min(len(os.sched_getaffinity(0)), 16)
+        log(f"cpu baseline: fp32 oracle, {threads} threads")
+        dt, o_ref, go_ref = cpu_baseline(wl, threads)
+        cpu = dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"the whole headline request (T={T}, both layers), fp32 oracle, "
+                          f"{dt:.2f} s wall")
+        fid = dict(attention=metrics.decision_fidelity(o_gpu, o_ref, wl.w_attn, wl.parent, wl.seg_len),
+                   gdn=metrics.decision_fidelity(go_gpu, go_ref, wl.w_gdn, wl.parent, wl.seg_len),
+                   reference="float32 oracle")
+
+    out = {
+        "metric": METRIC,
+        "value": T / (res["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one decision request: prefix 2048 + 16 options of 16-48 tokens; "
+                               "attention 16 q / 2 kv heads, head_dim 128; Gated DeltaNet 16 heads, "
+                               "dk = dv = 128",
+                   "tokens": T, "segments": wl.S, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "layer_pair_p50_us": res["pair_p50"] * 1e6,
+        "layer_pair_p95_us": res["pair_p95"] * 1e6,
+        "fidelity": fid,
+    }
+    if not args.no_workloads:
+        out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
+    print(json.dumps(out), flush=True)
+
+
+def build_workload(name):
+    """(meta dict, device tensors, graph?) of a named workload."""
+    from tree_structured_decision_amd import workloads as W
+
+    if name in ("tiny_one_level", "one_request", "agent_history"):
+        wl = W.WORKLOADS[name]()
+        meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
+        return meta, tensors_from_numpy(wl), False, wl.dtype
+    if name == "wide_options":
+        parent, seg_len = W.tree_one_level(8192, [8] * 256)
+        meta = wl_meta_of(parent, seg_len, 32, 4, 128, 16, 128, 128)
+        t = tensors_on_device(name, parent, seg_len, 32, 4, 128, 16, 128, 128, 1003, "uniform", None)
+        return meta, t, False, "bf16"
+    if name == "request_mix":
+        rng = np.random.Generator(np.random.PCG64(W.SEED_BASE + 5))
+        parent, seg_len = W.request_mix_tree(rng)
+        meta = wl_meta_of(parent, seg_len, 16, 2, 128, 16, 128, 128)
+        t = tensors_on_device(name, parent, seg_len, 16, 2, 128, 16, 128, 128, 1005, "sigmoid", None)
+        return meta, t, True, "bf16"
+    raise ValueError(name)
+
+
+def workload_report(name, meta, res, graph, dtype):
+    elt = 2 if dtype == "bf16" else 4
+    fl, ab = attn_work(meta["parent"], meta["seg_len"], meta["H"], meta["Hkv"], meta["D"], elt)
+    gb = gdn_work(meta["parent"], meta["seg_len"], meta["gH"], meta["dk"], meta["dv"], elt, False)
+    peak = PEAK_BF16_MFMA if dtype == "bf16" else PEAK_F32_MFMA
+    roof_t = max(fl / peak, ab / PEAK_HBM) + gb / PEAK_HBM
+    pair = res["pair_p50"]
+    rep = dict(tokens=meta["T"], segments=meta["S"], graph=graph,
+               stream_tokens_per_s=meta["T"] / (res["ms_per_step"] * 1e-3),
+               layer_pair_p50_us=pair * 1e6,
+               layer_pair_tokens_per_s=meta["T"] / pair,
+               pair_roofline_frac=roof_t / pair)
+    if not graph:
+        rep.update(attn_p50_us=res["attn_p50"] * 1e6, gdn_p50_us=res["gdn_p50"] * 1e6,
+                   attn_frac=max(fl / peak, ab / PEAK_HBM) / res["attn_p50"],
+                   attn_tflops=fl / res["attn_p50"] / 1e12,
+                   gdn_hbm_frac=(gb / PEAK_HBM) / res["gdn_p50"])
+    return rep
+
+
+def all_workloads(steps, warmup):
+    import torch
+
+    rep = {}
+    for name in ("tiny_one_level", "one_request", "wide_options", "agent_history", "request_mix"):
+        log(f"workload {name}")
+        meta, t, graph, dtype = build_workload(name)
+        r = Runner(meta, t, graph)
+        res = time_runner(r, steps, warmup)
+        rep[name] = workload_report(name, meta, res, graph, dtype)
+        log(f"  {rep[name]}")
+        r.sess.close()
+        del r, t
+        torch.cuda.empty_cache()
+    return rep
+
+
+def run_one(name, steps, warmup):
+    meta, t, graph, dtype = build_workload(name)
+    r = Runner(meta, t, graph)
+    res = time_runner(r, steps, warmup)
+    print(json.dumps({name: workload_report(name, meta, res, graph, dtype)}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

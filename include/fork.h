@@ -1,0 +1,222 @@
+/*
+ * fork.h - C ABI of the MI355X (gfx950) ForkAttention hot path.
+ *
+ * A decision request is a tree of token segments: a shared context prefix,
+ * then child segments (candidate options or nested history branches). The
+ * tree is executed as ONE flattened token stream whose topology is held as
+ * GPU-resident segment metadata (Flide, kongchang.com page, intro and section
+ * "ForkAttention: exact forking in GPU indices"). Every token attends to all
+ * tokens of its ancestor segments and to the tokens of its own segment up to
+ * itself; tokens of different branches never see each other (same page,
+ * section "attention masks and probability distortion"). In the recurrent
+ * Gated DeltaNet layer the state at the end of a parent segment is copied
+ * exactly into every child (techfi24.com page, section "Exact State Forking";
+ * kongchang.com page, "Gated DeltaNet layer"). Each branch's result equals an
+ * isolated forward pass of that branch, up to floating-point rounding.
+ *
+ * Stream layout: segment s holds seg_len[s] >= 1 tokens; segments are laid out
+ * contiguously in index order (segment 0 first); parent[s] is -1 for a root or
+ * an index < s. T = sum(seg_len). Several roots (independent requests) may
+ * share one stream.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless their name ends in _h (host).
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*); no call
+ *     allocates device memory or synchronises the stream, except those marked
+ *     "synchronises".
+ *   - All validation happens on the host before anything is enqueued, so a
+ *     call that returns an error has enqueued nothing and written nothing.
+ *   - Tensors are contiguous row-major. GQA: kv head of query head h is
+ *     h / (H / Hkv).
+ *   - On error the call returns a negative fork_status and fork_last_error()
+ *     returns a message (thread-local, valid until the next call on the same
+ *     thread).
+ *   - The caller owns every buffer. The library owns only fork_graph objects.
+ */
+#ifndef FORK_H_
+#define FORK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FORK_OK = 0,
+  FORK_E_ARG = -1,          /* null pointer, bad size, inconsistent arguments */
+  FORK_E_TREE = -2,         /* invalid tree: parent >= s or < -1, seg_len < 1, too deep */
+  FORK_E_UNSUPPORTED = -3,  /* head size or dtype this build has no kernel for */
+  FORK_E_WORKSPACE = -4,    /* workspace or staging buffer too small */
+  FORK_E_CAPACITY = -5,     /* tree larger than the capacities the blob was sized for */
+  FORK_E_HIP = -6           /* a HIP runtime call failed */
+} fork_status;
+
+typedef enum { FORK_F32 = 0, FORK_BF16 = 1 } fork_dtype;
+
+/* Capacities a metadata blob is sized for. A blob built once can hold any tree
+ * within them, which is what lets a captured graph be replayed on new trees. */
+typedef struct fork_caps {
+  int32_t t_cap;      /* max tokens in the stream */
+  int32_t s_cap;      /* max segments */
+  int32_t depth_cap;  /* max segment depth (a root has depth 0) */
+  int32_t gqa_group;  /* H / Hkv of the attention layers served; 1..128 */
+} fork_caps;
+
+/* Host descriptor of a built metadata blob. The arrays live in `dev`. */
+typedef struct fork_meta {
+  int32_t num_tokens;      /* T */
+  int32_t num_segments;    /* S */
+  int32_t num_roots;       /* R */
+  int32_t max_depth;       /* deepest segment depth */
+  int32_t num_attn_tiles;  /* query tiles of the attention work list */
+  int32_t num_chunks;      /* Gated DeltaNet chunks (never crossing a segment) */
+  int32_t tile_tokens;     /* tokens per attention query tile */
+  int32_t reserved;
+  fork_caps caps;
+  void* dev;               /* caller-owned device blob, >= fork_meta_size bytes */
+  size_t dev_bytes;
+} fork_meta;
+
+/* Array ids for fork_meta_export. */
+enum {
+  FORK_ARR_TOK_SEG = 0,      /* [T] segment of each token */
+  FORK_ARR_TOK_POS = 1,      /* [T] position inside its segment */
+  FORK_ARR_TOK_ISO_POS = 2,  /* [T] position in the isolated root-to-segment sequence */
+  FORK_ARR_SEG_START = 3,    /* [S] first token of each segment */
+  FORK_ARR_DEPTH = 4,        /* [S] number of ancestors */
+  FORK_ARR_ANC_LEN = 5,      /* [S] total tokens of the ancestors */
+  FORK_ARR_ROOT = 6          /* [S] root segment of each segment */
+};
+
+/* Bytes of device memory (dev) and of host staging a blob with these
+ * capacities needs. Either output pointer may be null. */
+fork_status fork_meta_size(const fork_caps* caps_h, size_t* dev_bytes_h, size_t* staging_bytes_h);
+
+/*
+ * Segment metadata builder (the GPU-resident indices of the tree).
+ * Validates the tree, lays out per-segment arrays and work lists (attention
+ * query tiles, Gated DeltaNet chunks and per-depth segment lists) into
+ * staging_h on the host, copies them to dev with one hipMemcpyAsync on
+ * `stream`, and launches a kernel that expands the per-token arrays
+ * (segment, position in segment, position in the isolated sequence).
+ * staging_h should be pinned host memory; it must stay untouched until the
+ * stream has passed the copy. out_h receives the descriptor the forward calls
+ * take.
+ */
+fork_status fork_meta_build(const int32_t* parent_h, const int32_t* seg_len_h,
+                            int32_t num_segments, const fork_caps* caps_h,
+                            void* dev, size_t dev_bytes,
+                            void* staging_h, size_t staging_bytes,
+                            fork_meta* out_h, void* stream);
+
+/*
+ * Host half of fork_meta_build only: validation and layout into staging_h,
+ * no HIP call. Returns in *upload_bytes_h how many leading bytes of staging_h
+ * fork_meta_build would copy. For tests and for callers that upload
+ * themselves. out_h->dev is set to null.
+ */
+fork_status fork_meta_plan(const int32_t* parent_h, const int32_t* seg_len_h,
+                           int32_t num_segments, const fork_caps* caps_h,
+                           void* staging_h, size_t staging_bytes,
+                           size_t* upload_bytes_h, fork_meta* out_h);
+
+/* Copy one metadata array (FORK_ARR_*) from the device into dst_h (int32,
+ * T or S entries). Synchronises the stream. For tests. */
+fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_h, void* stream);
+
+/* Dense [T, T] uint8 visibility mask computed on the GPU from the device
+ * metadata: mask[t*T + j] = 1 iff token t attends to token j. T <= 8192.
+ * For tests. */
+fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream);
+
+/* ---------------------------------------------------------------- attention
+ * Tree-masked softmax attention over the flattened stream
+ * (kongchang.com page, section "ForkAttention: exact forking in GPU indices").
+ * q [T,H,D], k/v [T,Hkv,D] and o [T,H,D] of dtype dt; lse [T,H] float32 or
+ * null (natural-log sum of exp of the scaled scores). Scores are scale * q.k
+ * with scale <= 0 meaning 1/sqrt(D). Each prefix key/value tile is staged in
+ * LDS once per query tile and reused by every packed query row (GQA heads x
+ * tokens of sibling segments). Supported: D in {64, 128}; H / Hkv must equal
+ * the gqa_group the metadata was built for. The workspace may be null when
+ * fork_attn_workspace reports 0 bytes.
+ */
+fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int32_t D,
+                                fork_dtype dt, size_t* bytes_h);
+fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, const void* v,
+                              void* o, float* lse, int32_t H, int32_t Hkv, int32_t D,
+                              float scale, fork_dtype dt, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ----------------------------------------------------------- Gated DeltaNet
+ * Forked Gated DeltaNet: per head, the dv x dk state follows
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = scale * S_t q_t
+ * along each branch; a segment starts from its parent's end state (the fork:
+ * that state is written exactly into seg_start_state of every child), a root
+ * from root_state or zero. (The pages describe the layer and the fork in
+ * prose: techfi24.com page, "Exact State Forking"; kongchang.com page,
+ * "Gated DeltaNet layer".)
+ * q/k [T,H,dk], v [T,H,dv], o [T,H,dv] of dtype dt; a/b [T,H] float32;
+ * root_state [R,H,dv,dk] float32 or null (zero; R roots in index order);
+ * seg_start_state [S,H,dv,dk] float32 (required: the fork copies);
+ * seg_final_state [S,H,dv,dk] float32 or null. States are row-major dv x dk.
+ * Supported: dk == dv in {32, 64, 128}. The workspace holds per-chunk
+ * intermediates; fork_gdn_workspace sizes it for the blob's capacities.
+ */
+fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv,
+                               fork_dtype dt, size_t* bytes_h);
+fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, const void* v,
+                             const float* a, const float* b, const float* root_state,
+                             void* o, float* seg_start_state, float* seg_final_state,
+                             int32_t H, int32_t dk, int32_t dv, float scale, fork_dtype dt,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ graph buckets
+ * A compact set of pre-recorded execution graphs serves varied request mixes
+ * (kongchang.com page, section "pre-recorded execution graphs"). A fork_graph
+ * records fork_attn_forward followed by gdn_fork_forward for a metadata blob
+ * with fixed capacities (the bucket); its kernels read the tree from the blob
+ * at run time. To run a new tree: fork_meta_build into the same blob (same
+ * capacities, same dev pointer), then fork_graph_launch. All buffers in args
+ * must be sized for the bucket's t_cap / s_cap and stay valid while the graph
+ * lives. Tokens beyond the current T are neither read nor written.
+ */
+typedef struct fork_graph_args {
+  /* attention */
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int32_t H, Hkv, D;
+  float scale;
+  void* attn_ws;
+  size_t attn_ws_bytes;
+  /* Gated DeltaNet */
+  const void *gq, *gk, *gv;
+  const float *a, *b, *root_state;
+  void* go;
+  float *seg_start_state, *seg_final_state;
+  int32_t gH, dk, dv;
+  float gscale;
+  void* gdn_ws;
+  size_t gdn_ws_bytes;
+  fork_dtype dt;
+} fork_graph_args;
+
+typedef struct fork_graph fork_graph;
+
+fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* args_h, void* stream,
+                              fork_graph** out_h);
+fork_status fork_graph_launch(fork_graph* g, void* stream);
+fork_status fork_graph_destroy(fork_graph* g);
+
+/* Message for the last error on this thread ("" if none). */
+const char* fork_last_error(void);
+
+/* Library version string. */
+const char* fork_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FORK_H_ */

@@ -1,0 +1,400 @@
+// Host half of the ForkAttention library: tree validation, the metadata plan
+// (segment arrays and work lists laid out for one upload), argument checks and
+// the public C ABI entry points declared in include/fork.h.
+//
+// The tree is held as GPU-resident indices over one flattened token stream,
+// not as duplicated graphs or re-batched requests (Flide, kongchang.com page,
+// section "ForkAttention: exact forking in GPU indices").
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace fork {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+fork_status fail(fork_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+  return st == hipStreamCaptureStatusActive;
+}
+
+static fork_status check_caps(const fork_caps* c) {
+  if (!c) return fail(FORK_E_ARG, "caps is null");
+  if (c->t_cap < 1 || c->t_cap > (1 << 29)) return fail(FORK_E_ARG, "t_cap %d out of range [1, 2^29]", c->t_cap);
+  if (c->s_cap < 1 || c->s_cap > (1 << 24)) return fail(FORK_E_ARG, "s_cap %d out of range [1, 2^24]", c->s_cap);
+  if (c->depth_cap < 0 || c->depth_cap > kMaxDepthCap)
+    return fail(FORK_E_ARG, "depth_cap %d out of range [0, %d]", c->depth_cap, kMaxDepthCap);
+  if (c->gqa_group < 1 || c->gqa_group > kAttnRows)
+    return fail(FORK_E_UNSUPPORTED, "gqa_group %d out of range [1, %d]", c->gqa_group, kAttnRows);
+  return FORK_OK;
+}
+
+fork_status check_meta(const fork_meta* m) {
+  if (!m) return fail(FORK_E_ARG, "meta is null");
+  fork_status st = check_caps(&m->caps);
+  if (st) return st;
+  if (!m->dev) return fail(FORK_E_ARG, "meta has no device blob (built with fork_meta_plan?)");
+  BlobLayout L = blob_layout(m->caps);
+  if (m->dev_bytes < (size_t)L.total_words * 4) return fail(FORK_E_WORKSPACE, "device blob too small");
+  if (m->num_tokens < 1 || m->num_tokens > m->caps.t_cap || m->num_segments < 1 ||
+      m->num_segments > m->caps.s_cap || m->max_depth > m->caps.depth_cap)
+    return fail(FORK_E_ARG, "meta descriptor counts are inconsistent with its capacities");
+  return FORK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The plan: everything the kernels need that depends on the tree only.
+static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int32_t S,
+                             const fork_caps* caps, void* staging, size_t staging_bytes,
+                             size_t* upload_bytes, fork_meta* out) {
+  fork_status st = check_caps(caps);
+  if (st) return st;
+  if (!parent || !seg_len || !staging || !out) return fail(FORK_E_ARG, "null pointer argument");
+  if (S < 1) return fail(FORK_E_TREE, "a tree needs at least one segment (got %d)", S);
+  if (S > caps->s_cap) return fail(FORK_E_CAPACITY, "%d segments exceed s_cap %d", S, caps->s_cap);
+  const BlobLayout L = blob_layout(*caps);
+  if (staging_bytes < (size_t)L.upload_cap_words * 4)
+    return fail(FORK_E_WORKSPACE, "staging buffer holds %zu bytes, needs %lld", staging_bytes,
+                (long long)L.upload_cap_words * 4);
+
+  // validate: parent before child, positive lengths, depth and token capacity
+  std::vector<int32_t> depth(S), start(S), root(S), anc(S), root_ord(S, -1), first_child(S, -1);
+  int64_t T = 0;
+  int32_t max_depth = 0, R = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t p = parent[s];
+    if (seg_len[s] < 1) return fail(FORK_E_TREE, "segment %d has length %d (must be >= 1)", s, seg_len[s]);
+    if (p < -1 || p >= s)
+      return fail(FORK_E_TREE, "segment %d has parent %d (must be -1 or in [0, %d))", s, p, s);
+    start[s] = (int32_t)T;
+    T += seg_len[s];
+    if (T > caps->t_cap) return fail(FORK_E_CAPACITY, "stream exceeds t_cap %d tokens", caps->t_cap);
+    if (p < 0) {
+      depth[s] = 0;
+      root[s] = s;
+      anc[s] = 0;
+      root_ord[s] = R++;
+    } else {
+      depth[s] = depth[p] + 1;
+      root[s] = root[p];
+      anc[s] = anc[p] + seg_len[p];
+      if (first_child[p] < 0) first_child[p] = s;
+    }
+    if (depth[s] > caps->depth_cap)
+      return fail(FORK_E_CAPACITY, "segment %d has depth %d > depth_cap %d", s, depth[s], caps->depth_cap);
+    max_depth = std::max(max_depth, depth[s]);
+  }
+
+  // GDN chunks: never cross a segment boundary; the last one may be partial
+  std::vector<int32_t> chunk_base(S);
+  int64_t nchunks = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    chunk_base[s] = (int32_t)nchunks;
+    nchunks += (seg_len[s] + kChunk - 1) / kChunk;
+  }
+
+  // GDN levels: segments by depth, longest first within a depth (stable)
+  std::vector<int32_t> level_off(max_depth + 2, 0), level_seg(S);
+  for (int32_t s = 0; s < S; ++s) level_off[depth[s] + 1]++;
+  for (int32_t d = 0; d <= max_depth; ++d) level_off[d + 1] += level_off[d];
+  {
+    std::vector<int32_t> fill(level_off.begin(), level_off.end() - 1);
+    for (int32_t s = 0; s < S; ++s) level_seg[fill[depth[s]]++] = s;
+    for (int32_t d = 0; d <= max_depth; ++d)
+      std::stable_sort(level_seg.begin() + level_off[d], level_seg.begin() + level_off[d + 1],
+                       [&](int32_t x, int32_t y) { return seg_len[x] > seg_len[y]; });
+  }
+
+  // Attention query tiles. Short non-root siblings that follow each other in
+  // the stream share their ancestor keys, so they are packed into common
+  // tiles: every staged ancestor key/value tile then serves all their rows.
+  const int32_t TT = L.tile_tokens;
+  std::vector<AttnTile> tiles;
+  std::vector<int64_t> cost;
+  tiles.reserve((size_t)(T / TT + S));
+  cost.reserve(tiles.capacity());
+  auto packable = [&](int32_t s) { return parent[s] >= 0 && seg_len[s] < TT; };
+  for (int32_t s = 0; s < S;) {
+    int32_t e = s + 1;
+    if (packable(s))
+      while (e < S && packable(e) && parent[e] == parent[s]) ++e;
+    const int32_t lo = start[s], hi = start[e - 1] + seg_len[e - 1];
+    int32_t seg_of_t0 = s;
+    for (int32_t t0 = lo; t0 < hi; t0 += TT) {
+      const int32_t t1 = std::min(hi, t0 + TT);
+      while (start[seg_of_t0] + seg_len[seg_of_t0] <= t0) ++seg_of_t0;
+      int32_t seg_last = seg_of_t0;
+      while (start[seg_last] + seg_len[seg_last] < t1) ++seg_last;
+      AttnTile tl;
+      tl.t0 = t0;
+      tl.t1 = t1;
+      tl.own_lo = start[seg_of_t0];
+      tl.info = (parent[s] + 1) | (seg_last != seg_of_t0 ? kTileMulti : 0);
+      tiles.push_back(tl);
+      cost.push_back((int64_t)anc[s] + (t1 - tl.own_lo));
+    }
+    s = e;
+  }
+  if ((int64_t)tiles.size() > L.tile_cap) return fail(FORK_E_CAPACITY, "tile list overflow");
+  // most expensive first (counting sort on 64-key units, stable)
+  std::vector<AttnTile> sorted(tiles.size());
+  {
+    const int64_t nb = T / kAttnKeys + 2;
+    std::vector<int64_t> cnt(nb + 1, 0);
+    for (int64_t c : cost) cnt[nb - 1 - std::min<int64_t>(c / kAttnKeys, nb - 1)]++;
+    int64_t acc = 0;
+    for (int64_t i = 0; i <= nb; ++i) {
+      int64_t x = cnt[i];
+      cnt[i] = acc;
+      acc += x;
+    }
+    for (size_t i = 0; i < tiles.size(); ++i)
+      sorted[cnt[nb - 1 - std::min<int64_t>(cost[i] / kAttnKeys, nb - 1)]++] = tiles[i];
+  }
+
+  // lay out the upload region
+  int32_t* w = (int32_t*)staging;
+  memset(w, 0, MH_WORDS * 4);
+  int64_t off = MH_WORDS;
+  auto put = [&](int hdr_slot, const int32_t* src, int64_t n) {
+    off = (off + 3) & ~int64_t(3);
+    w[hdr_slot] = (int32_t)off;
+    if (n) memcpy(w + off, src, (size_t)n * 4);
+    off += n;
+  };
+  put(MH_OFF_PARENT, parent, S);
+  put(MH_OFF_SEGLEN, seg_len, S);
+  put(MH_OFF_SEGSTART, start.data(), S);
+  put(MH_OFF_DEPTH, depth.data(), S);
+  put(MH_OFF_ROOT, root.data(), S);
+  put(MH_OFF_ROOTORD, root_ord.data(), S);
+  put(MH_OFF_ANCLEN, anc.data(), S);
+  put(MH_OFF_FIRSTCHILD, first_child.data(), S);
+  put(MH_OFF_CHUNKBASE, chunk_base.data(), S);
+  put(MH_OFF_LEVELOFF, level_off.data(), max_depth + 2);
+  put(MH_OFF_LEVELSEG, level_seg.data(), S);
+  {
+    off = (off + 3) & ~int64_t(3);
+    w[MH_OFF_CHUNKS] = (int32_t)off;
+    for (int32_t s = 0; s < S; ++s)
+      for (int32_t c0 = 0; c0 < seg_len[s]; c0 += kChunk) {
+        w[off++] = start[s] + c0;
+        w[off++] = std::min(kChunk, seg_len[s] - c0);
+      }
+  }
+  put(MH_OFF_TILES, (const int32_t*)sorted.data(), (int64_t)sorted.size() * 4);
+  if (off > L.upload_cap_words) return fail(FORK_E_CAPACITY, "metadata upload region overflow");
+  const int64_t tstride = ((int64_t)caps->t_cap + 63) / 64 * 64;
+  w[MH_MAGIC] = kMetaMagic;
+  w[MH_T] = (int32_t)T;
+  w[MH_S] = S;
+  w[MH_R] = R;
+  w[MH_MAXDEPTH] = max_depth;
+  w[MH_NTILES] = (int32_t)sorted.size();
+  w[MH_NCHUNKS] = (int32_t)nchunks;
+  w[MH_TILE_TOKENS] = TT;
+  w[MH_GQA] = caps->gqa_group;
+  w[MH_OFF_TOKSEG] = (int32_t)L.tok_off_words;
+  w[MH_OFF_TOKPOS] = (int32_t)(L.tok_off_words + tstride);
+  w[MH_OFF_TOKISO] = (int32_t)(L.tok_off_words + 2 * tstride);
+  w[MH_UPLOAD_WORDS] = (int32_t)off;
+
+  memset(out, 0, sizeof(*out));
+  out->num_tokens = (int32_t)T;
+  out->num_segments = S;
+  out->num_roots = R;
+  out->max_depth = max_depth;
+  out->num_attn_tiles = (int32_t)sorted.size();
+  out->num_chunks = (int32_t)nchunks;
+  out->tile_tokens = TT;
+  out->caps = *caps;
+  if (upload_bytes) *upload_bytes = (size_t)off * 4;
+  return FORK_OK;
+}
+
+}  // namespace fork
+
+using namespace fork;
+
+extern "C" {
+
+const char* fork_last_error(void) { return g_err; }
+
+const char* fork_version(void) { return "forkattn-gfx950 0.1"; }
+
+fork_status fork_meta_size(const fork_caps* caps_h, size_t* dev_bytes_h, size_t* staging_bytes_h) {
+  g_err[0] = 0;
+  fork_status st = check_caps(caps_h);
+  if (st) return st;
+  BlobLayout L = blob_layout(*caps_h);
+  if (dev_bytes_h) *dev_bytes_h = (size_t)L.total_words * 4;
+  if (staging_bytes_h) *staging_bytes_h = (size_t)L.upload_cap_words * 4;
+  return FORK_OK;
+}
+
+fork_status fork_meta_plan(const int32_t* parent_h, const int32_t* seg_len_h, int32_t num_segments,
+                           const fork_caps* caps_h, void* staging_h, size_t staging_bytes,
+                           size_t* upload_bytes_h, fork_meta* out_h) {
+  g_err[0] = 0;
+  return plan_impl(parent_h, seg_len_h, num_segments, caps_h, staging_h, staging_bytes,
+                   upload_bytes_h, out_h);
+}
+
+fork_status fork_meta_build(const int32_t* parent_h, const int32_t* seg_len_h, int32_t num_segments,
+                            const fork_caps* caps_h, void* dev, size_t dev_bytes, void* staging_h,
+                            size_t staging_bytes, fork_meta* out_h, void* stream) {
+  g_err[0] = 0;
+  if (!dev) return fail(FORK_E_ARG, "dev is null");
+  fork_status st = check_caps(caps_h);
+  if (st) return st;
+  BlobLayout L = blob_layout(*caps_h);
+  if (dev_bytes < (size_t)L.total_words * 4)
+    return fail(FORK_E_WORKSPACE, "device blob holds %zu bytes, needs %lld", dev_bytes,
+                (long long)L.total_words * 4);
+  fork_meta m;
+  size_t up = 0;
+  st = plan_impl(parent_h, seg_len_h, num_segments, caps_h, staging_h, staging_bytes, &up, &m);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  FORK_HIP_CHECK(hipMemcpyAsync(dev, staging_h, up, hipMemcpyHostToDevice, s));
+  m.dev = dev;
+  m.dev_bytes = dev_bytes;
+  st = launch_meta_expand(&m, s);
+  if (st) return st;
+  *out_h = m;
+  return FORK_OK;
+}
+
+fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_h, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!dst_h) return fail(FORK_E_ARG, "dst is null");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t hdr[MH_WORDS];
+  FORK_HIP_CHECK(hipMemcpyAsync(hdr, m->dev, sizeof(hdr), hipMemcpyDeviceToHost, s));
+  FORK_HIP_CHECK(hipStreamSynchronize(s));
+  int slot;
+  int64_t n;
+  switch (array_id) {
+    case FORK_ARR_TOK_SEG: slot = MH_OFF_TOKSEG; n = hdr[MH_T]; break;
+    case FORK_ARR_TOK_POS: slot = MH_OFF_TOKPOS; n = hdr[MH_T]; break;
+    case FORK_ARR_TOK_ISO_POS: slot = MH_OFF_TOKISO; n = hdr[MH_T]; break;
+    case FORK_ARR_SEG_START: slot = MH_OFF_SEGSTART; n = hdr[MH_S]; break;
+    case FORK_ARR_DEPTH: slot = MH_OFF_DEPTH; n = hdr[MH_S]; break;
+    case FORK_ARR_ANC_LEN: slot = MH_OFF_ANCLEN; n = hdr[MH_S]; break;
+    case FORK_ARR_ROOT: slot = MH_OFF_ROOT; n = hdr[MH_S]; break;
+    default: return fail(FORK_E_ARG, "unknown array id %d", array_id);
+  }
+  FORK_HIP_CHECK(hipMemcpyAsync(dst_h, (const int32_t*)m->dev + hdr[slot], (size_t)n * 4,
+                                hipMemcpyDeviceToHost, s));
+  FORK_HIP_CHECK(hipStreamSynchronize(s));
+  return FORK_OK;
+}
+
+fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!mask) return fail(FORK_E_ARG, "mask is null");
+  if (m->num_tokens > 8192) return fail(FORK_E_ARG, "dense mask limited to T <= 8192");
+  return launch_dense_mask(m, mask, (hipStream_t)stream);
+}
+
+fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int32_t D, fork_dtype dt,
+                                size_t* bytes_h) {
+  g_err[0] = 0;
+  fork_status st = check_caps(m ? &m->caps : nullptr);
+  if (st) return st;
+  if (!bytes_h) return fail(FORK_E_ARG, "bytes_h is null");
+  (void)H; (void)Hkv; (void)D; (void)dt;
+  *bytes_h = 0;
+  return FORK_OK;
+}
+
+fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, const void* v, void* o,
+                              float* lse, int32_t H, int32_t Hkv, int32_t D, float scale,
+                              fork_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)ws; (void)ws_bytes;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!q || !k || !v || !o) return fail(FORK_E_ARG, "q, k, v and o must be non-null");
+  if (H < 1 || Hkv < 1 || H % Hkv) return fail(FORK_E_ARG, "H=%d must be a positive multiple of Hkv=%d", H, Hkv);
+  if (H / Hkv != m->caps.gqa_group)
+    return fail(FORK_E_ARG, "H/Hkv=%d differs from the gqa_group %d the metadata was built for", H / Hkv,
+                m->caps.gqa_group);
+  if (D != 64 && D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", D);
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_attention(m, q, k, v, o, lse, H, Hkv, D, scale, dt, (hipStream_t)stream);
+}
+
+fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv, fork_dtype dt,
+                               size_t* bytes_h) {
+  g_err[0] = 0;
+  fork_status st = check_caps(m ? &m->caps : nullptr);
+  if (st) return st;
+  if (!bytes_h) return fail(FORK_E_ARG, "bytes_h is null");
+  if (H < 1 || dk < 1 || dv < 1) return fail(FORK_E_ARG, "bad head shape");
+  (void)dt;
+  *bytes_h = gdn_workspace_bytes(m, H, dk, dv);
+  return FORK_OK;
+}
+
+fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, const void* v,
+                             const float* a, const float* b, const float* root_state, void* o,
+                             float* seg_start_state, float* seg_final_state, int32_t H, int32_t dk,
+                             int32_t dv, float scale, fork_dtype dt, void* ws, size_t ws_bytes,
+                             void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!q || !k || !v || !a || !b || !o || !seg_start_state)
+    return fail(FORK_E_ARG, "q, k, v, a, b, o and seg_start_state must be non-null");
+  if (H < 1) return fail(FORK_E_ARG, "H=%d", H);
+  if (dk != dv || (dk != 32 && dk != 64 && dk != 128))
+    return fail(FORK_E_UNSUPPORTED, "dk=%d dv=%d unsupported (dk == dv in {32, 64, 128})", dk, dv);
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  const size_t need = gdn_workspace_bytes(m, H, dk, dv);
+  if (!ws || ws_bytes < need) return fail(FORK_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  return launch_gdn(m, q, k, v, a, b, root_state, o, seg_start_state, seg_final_state, H, dk, dv, scale,
+                    dt, ws, ws_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"

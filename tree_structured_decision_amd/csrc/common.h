@@ -1,0 +1,127 @@
+// Internal definitions shared by the host code and the HIP kernels of the
+// ForkAttention library: the layout of the metadata blob, launch helpers and
+// the error channel. Nothing here is part of the public C ABI (include/fork.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fork.h"
+
+namespace fork {
+
+// ---------------------------------------------------------------------------
+// Metadata blob. The blob starts with MH_WORDS int32 header words; arrays are
+// addressed by word offsets stored in the header, so kernels recorded in a
+// graph find the arrays of whatever tree was built last. The header and the
+// host-built arrays form one contiguous "upload" region copied in a single
+// hipMemcpyAsync; the per-token arrays follow at offsets fixed by the
+// capacities and are written on the device.
+enum MetaHeader : int {
+  MH_MAGIC = 0,
+  MH_T,            // tokens
+  MH_S,            // segments
+  MH_R,            // roots
+  MH_MAXDEPTH,     // deepest segment depth
+  MH_NTILES,       // attention query tiles
+  MH_NCHUNKS,      // Gated DeltaNet chunks
+  MH_TILE_TOKENS,  // tokens per attention query tile
+  MH_GQA,          // H / Hkv the tiles were cut for
+  MH_OFF_PARENT,   // [S] parent segment or -1
+  MH_OFF_SEGLEN,   // [S]
+  MH_OFF_SEGSTART, // [S] first token
+  MH_OFF_DEPTH,    // [S]
+  MH_OFF_ROOT,     // [S] root segment
+  MH_OFF_ROOTORD,  // [S] ordinal of the segment among roots (-1 for non-roots)
+  MH_OFF_ANCLEN,   // [S] tokens in ancestors
+  MH_OFF_FIRSTCHILD,  // [S] lowest-index child or -1
+  MH_OFF_CHUNKBASE,   // [S] index of the segment's first chunk
+  MH_OFF_LEVELOFF,    // [MAXDEPTH + 2] start of each depth in LEVELSEG
+  MH_OFF_LEVELSEG,    // [S] segments by depth, longest first within a depth
+  MH_OFF_CHUNKS,      // [NCHUNKS] int2 {first token, length}
+  MH_OFF_TILES,       // [NTILES] AttnTile, most expensive first
+  MH_OFF_TOKSEG,      // [T] (device-written)
+  MH_OFF_TOKPOS,      // [T] (device-written)
+  MH_OFF_TOKISO,      // [T] (device-written)
+  MH_UPLOAD_WORDS,    // size of the upload region in words
+  MH_WORDS = 64
+};
+
+constexpr int32_t kMetaMagic = 0x464B4D31;  // "FKM1"
+constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
+constexpr int kAttnRows = 128;              // query rows (token x GQA head) per attention tile
+constexpr int kAttnKeys = 64;               // keys per staged key/value tile
+constexpr int kMaxDepthCap = 4096;
+
+// One attention query tile: tokens [t0, t1) of one or several consecutive
+// sibling segments. own_lo is the first token of t0's segment; info packs the
+// segment whose ancestor path (itself included) every row sees in full
+// (anc + 1, 0 for a root tile) in bits 0..29 and "tile spans several
+// segments" in bit 30.
+struct AttnTile {
+  int32_t t0, t1, own_lo, info;
+};
+constexpr int32_t kTileMulti = 1 << 30;
+constexpr int32_t kTileAncMask = (1 << 30) - 1;
+
+struct BlobLayout {
+  int64_t tile_cap, chunk_cap;
+  int64_t upload_cap_words;  // capacity of the upload region (header included)
+  int64_t tok_off_words;     // first per-token array
+  int64_t total_words;
+  int32_t tile_tokens;
+};
+
+// Tokens per attention tile for a GQA group size (each token brings G rows).
+inline int32_t tile_tokens_for(int32_t gqa) { return gqa >= kAttnRows ? 1 : kAttnRows / gqa; }
+
+inline BlobLayout blob_layout(const fork_caps& c) {
+  BlobLayout L;
+  L.tile_tokens = tile_tokens_for(c.gqa_group);
+  L.tile_cap = ((int64_t)c.t_cap + L.tile_tokens - 1) / L.tile_tokens + c.s_cap;
+  L.chunk_cap = ((int64_t)c.t_cap + kChunk - 1) / kChunk + c.s_cap;
+  // header + 10 segment arrays + level offsets + 2 words per chunk + 4 per tile,
+  // with each array aligned to 4 words
+  L.upload_cap_words = MH_WORDS + 10 * ((int64_t)c.s_cap + 4) + (c.depth_cap + 2 + 4) +
+                       2 * L.chunk_cap + 4 + 4 * L.tile_cap + 4;
+  L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
+  L.tok_off_words = L.upload_cap_words;
+  L.total_words = L.tok_off_words + 3 * (((int64_t)c.t_cap + 63) / 64 * 64);
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Error channel (thread-local message, see fork_last_error).
+void set_error(const char* fmt, ...);
+fork_status fail(fork_status st, const char* fmt, ...);
+
+#define FORK_HIP_CHECK(expr)                                                        \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return ::fork::fail(FORK_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Resident workgroups that fit the device at `per_cu` workgroups per compute unit.
+int device_cu_count();
+
+// True when `stream` is being captured into a graph.
+bool stream_capturing(hipStream_t stream);
+
+// Validates a descriptor against its blob.
+fork_status check_meta(const fork_meta* m);
+
+// Kernel launchers (defined with their kernels).
+fork_status launch_meta_expand(const fork_meta* m, hipStream_t stream);
+fork_status launch_dense_mask(const fork_meta* m, uint8_t* mask, hipStream_t stream);
+fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
+                             void* o, float* lse, int H, int Hkv, int D, float scale,
+                             fork_dtype dt, hipStream_t stream);
+size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);
+fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v,
+                       const float* a, const float* b, const float* root_state, void* o,
+                       float* seg_start_state, float* seg_final_state, int H, int dk, int dv,
+                       float scale, fork_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace fork

@@ -1,0 +1,597 @@
+// Forked Gated DeltaNet over the flattened decision stream (gfx950).
+//
+// Per head the dv x dk state follows S_t = a_t S_{t-1} (I - b_t k_t k_t^T) +
+// b_t v_t k_t^T with output o_t = scale * S_t q_t. Each segment starts from its
+// parent's end state, copied exactly into the segment's start slot (the fork;
+// techfi24.com page, "Exact State Forking"; kongchang.com page, "Gated
+// DeltaNet layer": every branch's state evolves in the isolated update order).
+//
+// Chunked form (chunks of 64 tokens that never cross a segment boundary). With
+// g_i the in-chunk cumulative sum of log a, gamma_i = exp(g_i), S0 the state
+// before the chunk:
+//   A   = strictly_lower(diag(b) (K K^T) * exp(g_i - g_j)),  T = (I + A)^-1
+//   T'' = T diag(b)
+//   U   = T'' (V - diag(gamma) K S0^T)
+//   O   = diag(gamma) Q S0^T + (Q K^T * Gamma) U,  Gamma_ij = exp(g_i - g_j), j <= i
+//   S_C = gamma_C S0 + U^T diag(gamma_C / gamma) K
+// (derived by unrolling the recurrence; u_t = b_t (v_t - a_t S_{t-1} k_t)).
+//
+// Kernels:
+//   gdn_prep: one workgroup per (chunk, head), fully parallel. Computes g,
+//     T'' and Q K^T * Gamma into the workspace.
+//   gdn_scan: one launch per tree depth. A work item is (segment, head,
+//     16-row slice of the state); rows of the state evolve independently, so
+//     slices need no communication. It walks its segment's chunks serially
+//     and at the end writes its final state into the first child's start
+//     slot; the other children copy it from there at the next depth.
+//
+// Precision. In bf16 mode q/k/v are exact bf16, so products with them as the
+// only rounded-free operands use one bf16 MFMA; operands that are computed in
+// fp32 (the state, T'', Q K^T * Gamma, U) are split into bf16 hi + lo parts and
+// multiplied with hi*hi + hi*lo + lo*hi, which keeps about 16 mantissa bits
+// (the usual operand-splitting refinement for low-precision matrix units). The
+// state stays fp32 in registers. fp32 mode uses fp32 MFMA throughout.
+#include <type_traits>
+
+#include "common.h"
+
+namespace fork {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int CH = kChunk;  // 64
+constexpr int VSL = 16;     // state rows per scan work item
+
+// Per (chunk, head) workspace block: T'' [64x64] and P = QK^T*Gamma [64x64],
+// each as bf16 hi/lo planes (bf16 mode) or one fp32 plane (fp32 mode), then g.
+constexpr size_t kWsPlane = (size_t)CH * CH * 4;  // bytes of one 64x64 operand
+constexpr size_t kWsChunk = 2 * kWsPlane + 256;   // T'', P, g (64 floats)
+
+template <bool BF16>
+struct GT {
+  using E = typename std::conditional<BF16, unsigned short, float>::type;
+  using F = typename std::conditional<BF16, bf16x8_t, float>::type;
+  static constexpr int KSTEP = BF16 ? 32 : 4;  // k per 16x16 MFMA
+  static constexpr int EPC = BF16 ? 8 : 4;     // elements per 16-byte chunk
+  static constexpr int PAD = BF16 ? 8 : 4;
+};
+
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+  return __builtin_bit_cast(unsigned short, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_val(unsigned short u) {
+  return __uint_as_float((unsigned)u << 16);
+}
+__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - bf16_val(hi));
+}
+
+// A/B fragment of an operand stored row-major with k contiguous: lane holds
+// (row, k0 + slice) where slice = lane / 16.
+template <bool BF16>
+__device__ __forceinline__ typename GT<BF16>::F ld_rowk(const typename GT<BF16>::E* base, int ld, int row,
+                                                        int k0, int kq) {
+  if constexpr (BF16)
+    return *(const bf16x8_t*)(base + row * ld + k0 + 8 * kq);
+  else
+    return base[row * ld + k0 + kq];
+}
+// Fragment of an operand stored with k along rows (k-major): element (k, col).
+template <bool BF16>
+__device__ __forceinline__ typename GT<BF16>::F ld_kcol(const typename GT<BF16>::E* base, int ld, int col,
+                                                        int k0, int kq) {
+  if constexpr (BF16) {
+    bf16x8_t f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      f[jj] = __builtin_bit_cast(__bf16, base[(k0 + 8 * kq + jj) * ld + col]);
+    return f;
+  } else {
+    return base[(k0 + kq) * ld + col];
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mma(typename GT<BF16>::F a, typename GT<BF16>::F b, f32x4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Store a computed fp32 value as a "split" operand element.
+template <bool BF16>
+__device__ __forceinline__ void put_split(typename GT<BF16>::E* hi, typename GT<BF16>::E* lo, int idx,
+                                          float x) {
+  if constexpr (BF16) {
+    unsigned short h, l;
+    split_bf16(x, h, l);
+    hi[idx] = h;
+    lo[idx] = l;
+  } else {
+    hi[idx] = x;
+  }
+}
+
+struct GdnArgs {
+  const int32_t* blob;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  const float* root_state;
+  void* o;
+  float* seg_start;
+  float* seg_final;
+  unsigned char* ws;
+  int H;
+  float scale;
+  int level;
+};
+
+// Load rows [t0, t0 + len) of one head of a [T, H, DK] tensor into a padded
+// LDS tile [64][DK + PAD]; rows >= len are zero.
+template <bool BF16, int DK>
+__device__ __forceinline__ void load_rows(typename GT<BF16>::E* dst, const typename GT<BF16>::E* src, int t0,
+                                          int len, int H, int h, int tid) {
+  using G = GT<BF16>;
+  constexpr int CPR = DK / G::EPC;
+  constexpr int LD = DK + G::PAD;
+  for (int task = tid; task < CH * CPR; task += 256) {
+    const int row = task / CPR, ch = task % CPR;
+    u32x4_t val = {0u, 0u, 0u, 0u};
+    if (row < len) val = *(const u32x4_t*)(src + ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC);
+    *(u32x4_t*)(dst + row * LD + ch * G::EPC) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep: per (chunk, head) compute g, T'' = (I + A)^-1 diag(b), P = QK^T * Gamma.
+template <bool BF16, int DK>
+__global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs args) {
+  using G = GT<BF16>;
+  using E = typename G::E;
+  constexpr int LDK = DK + G::PAD;
+  constexpr int LDA = CH + 4;  // fp32 64x64 tiles
+  __shared__ __attribute__((aligned(16))) E Ks[CH * LDK];
+  __shared__ __attribute__((aligned(16))) E Qs[CH * LDK];
+  __shared__ float As[CH * LDA];
+  __shared__ float Ts[CH * LDA];
+  __shared__ float Zs[4][16 * 20];
+  __shared__ float gs[CH], bs[CH];
+
+  const int32_t* __restrict__ blob = args.blob;
+  const int nchunks = blob[MH_NCHUNKS];
+  const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
+  const int H = args.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const E* __restrict__ Kg = (const E*)args.k;
+  const E* __restrict__ Qg = (const E*)args.q;
+
+  for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x) {
+    const int c = item / H, h = item - c * H;
+    const int2 ck = chunks[c];
+    const int t0 = ck.x, len = ck.y;
+    unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
+
+    __syncthreads();  // LDS reuse across items
+    load_rows<BF16, DK>(Ks, Kg, t0, len, H, h, tid);
+    load_rows<BF16, DK>(Qs, Qg, t0, len, H, h, tid);
+    if (w == 0) {
+      // g = inclusive cumulative sum of log a (padding: a = 1, b = 0)
+      const int i = lane;
+      float la = 0.f, bb = 0.f;
+      if (i < len) {
+        la = logf(args.a[(size_t)(t0 + i) * H + h]);
+        bb = args.b[(size_t)(t0 + i) * H + h];
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(la, off);
+        if (i >= off) la += y;
+      }
+      gs[i] = la;
+      bs[i] = bb;
+      ((float*)(wsb + 2 * kWsPlane))[i] = la;
+    }
+    // zero Ts (upper blocks stay zero)
+    for (int i = tid; i < CH * LDA; i += 256) Ts[i] = 0.f;
+    __syncthreads();
+
+    // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal)
+    {
+      E* Ph = (E*)(wsb + kWsPlane);
+      E* Pl = BF16 ? (E*)(wsb + kWsPlane) + CH * CH : nullptr;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        f32x4_t kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += G::KSTEP) {
+          const typename G::F bK = ld_rowk<BF16>(Ks, LDK, 16 * J + c16, k0, q4);
+          kk = mma<BF16>(ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4), bK, kk);
+          qk = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * q4 + r, j = 16 * J + c16;
+          const float dec = j <= i ? __expf(gs[i] - gs[j]) : 0.f;
+          As[i * LDA + j] = j < i ? bs[i] * dec * kk[r] : 0.f;
+          put_split<BF16>(Ph, Pl, i * CH + j, dec * qk[r]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution
+    if (lane < 16) {
+      const int base = 16 * w, col = lane;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == col) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc -= As[(base + i) * LDA + base + j] * x[j];
+        x[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Ts[(base + i) * LDA + base + col] = x[i];
+    }
+    __syncthreads();
+
+    // off-diagonal blocks: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, by distance
+#pragma unroll
+    for (int dist = 1; dist < 4; ++dist) {
+      const int I = w + dist, J = w;
+      const bool act = I < 4;
+      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      if (act) {
+        for (int Kb = J; Kb < I; ++Kb)
+#pragma unroll
+          for (int k0 = 0; k0 < 16; k0 += 4)
+            z = mma_f32(As[(16 * I + c16) * LDA + 16 * Kb + k0 + q4],
+                        Ts[(16 * Kb + k0 + q4) * LDA + 16 * J + c16], z);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Zs[w][(4 * q4 + r) * 20 + c16] = z[r];
+      }
+      __syncthreads();
+      if (act) {
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4)
+          t = mma_f32(Ts[(16 * I + c16) * LDA + 16 * I + k0 + q4], Zs[w][(k0 + q4) * 20 + c16], t);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * q4 + r) * LDA + 16 * J + c16] = -t[r];
+      }
+      __syncthreads();
+    }
+
+    // T'' = T diag(b) -> workspace
+    {
+      E* Th = (E*)wsb;
+      E* Tl = BF16 ? (E*)wsb + CH * CH : nullptr;
+      for (int idx = tid; idx < CH * CH; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        put_split<BF16>(Th, Tl, idx, Ts[i * LDA + j] * bs[j]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scan: one launch per depth; items (segment, head, 16-row state slice).
+template <bool BF16, int DK>
+__global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
+  using G = GT<BF16>;
+  using E = typename G::E;
+  constexpr int DV = DK;
+  constexpr int NS = DV / VSL;       // slices per head
+  constexpr int LDK = DK + G::PAD;   // K, Q tiles
+  constexpr int LDT = CH + G::PAD;   // T'', P tiles
+  constexpr int LDSS = DK + G::PAD;  // state slice
+  constexpr int LDR = CH + G::PAD;   // transposed R, U, U'
+  constexpr int NDB = DK / 16;       // 16-col d blocks of the state slice
+  constexpr int DBW = (NDB + 3) / 4; // d blocks per wave
+  constexpr bool SPLIT = BF16;
+  __shared__ __attribute__((aligned(16))) E Ks[CH * LDK];
+  __shared__ __attribute__((aligned(16))) E Qs[CH * LDK];
+  __shared__ __attribute__((aligned(16))) E Th[CH * LDT];
+  __shared__ __attribute__((aligned(16))) E Tl[SPLIT ? CH * LDT : 8];
+  __shared__ __attribute__((aligned(16))) E Ph[CH * LDT];
+  __shared__ __attribute__((aligned(16))) E Pl[SPLIT ? CH * LDT : 8];
+  __shared__ __attribute__((aligned(16))) E Sh[VSL * LDSS];
+  __shared__ __attribute__((aligned(16))) E Sl[SPLIT ? VSL * LDSS : 8];
+  __shared__ __attribute__((aligned(16))) E Rh[VSL * LDR];
+  __shared__ __attribute__((aligned(16))) E Rl[SPLIT ? VSL * LDR : 8];
+  __shared__ __attribute__((aligned(16))) E Uh[VSL * LDR];
+  __shared__ __attribute__((aligned(16))) E Ul[SPLIT ? VSL * LDR : 8];
+  __shared__ __attribute__((aligned(16))) E U2h[VSL * LDR];
+  __shared__ __attribute__((aligned(16))) E U2l[SPLIT ? VSL * LDR : 8];
+  __shared__ float Vs[CH * VSL];
+  __shared__ float gam[CH], rr[CH];
+
+  const int32_t* __restrict__ blob = args.blob;
+  const int level = args.level;
+  if (level > blob[MH_MAXDEPTH]) return;
+  const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
+  const int32_t* __restrict__ level_seg = blob + blob[MH_OFF_LEVELSEG];
+  const int32_t* __restrict__ parent = blob + blob[MH_OFF_PARENT];
+  const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
+  const int32_t* __restrict__ root_ord = blob + blob[MH_OFF_ROOTORD];
+  const int32_t* __restrict__ first_child = blob + blob[MH_OFF_FIRSTCHILD];
+  const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
+  const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
+  const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
+  const int H = args.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const E* __restrict__ Kg = (const E*)args.k;
+  const E* __restrict__ Qg = (const E*)args.q;
+  const E* __restrict__ Vg = (const E*)args.v;
+  E* __restrict__ Og = (E*)args.o;
+  const size_t SZ = (size_t)DV * DK;
+
+  for (int item = blockIdx.x; item < nlev * H * NS; item += gridDim.x) {
+    const int sl = item % NS, h = (item / NS) % H, li = item / (NS * H);
+    const int s = level_seg[lv0 + li];
+    const int e0 = sl * VSL;
+
+    // ---- start state: root_state / zero, or the parent's end state
+    f32x4_t Sreg[DBW];
+    {
+      const float* src = nullptr;
+      float* dst = nullptr;
+      const int p = parent[s];
+      if (p < 0) {
+        if (args.root_state) src = args.root_state + ((size_t)root_ord[s] * H + h) * SZ;
+        dst = args.seg_start + ((size_t)s * H + h) * SZ;
+      } else {
+        const int fc = first_child[p];
+        src = args.seg_start + ((size_t)fc * H + h) * SZ;
+        if (fc != s) dst = args.seg_start + ((size_t)s * H + h) * SZ;
+      }
+#pragma unroll
+      for (int bi = 0; bi < DBW; ++bi) {
+        const int db = w * DBW + bi;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = 0.f;
+          if (db < NDB) {
+            const size_t idx = (size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16;
+            x = src ? src[idx] : 0.f;
+            if (dst) dst[idx] = x;
+          }
+          Sreg[bi][r] = x;
+        }
+      }
+    }
+
+    const int nck = (seg_len[s] + CH - 1) / CH;
+    const int cb = chunk_base[s];
+    for (int ci = 0; ci < nck; ++ci) {
+      const int c = cb + ci;
+      const int2 ck = chunks[c];
+      const int t0 = ck.x, len = ck.y;
+      const unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
+
+      __syncthreads();  // previous chunk done with every LDS tile
+      // state slice -> LDS operand
+#pragma unroll
+      for (int bi = 0; bi < DBW; ++bi) {
+        const int db = w * DBW + bi;
+        if (db < NDB)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) put_split<BF16>(Sh, Sl, (4 * q4 + r) * LDSS + 16 * db + c16, Sreg[bi][r]);
+      }
+      load_rows<BF16, DK>(Ks, Kg, t0, len, H, h, tid);
+      load_rows<BF16, DK>(Qs, Qg, t0, len, H, h, tid);
+      {
+        const E* Tw = (const E*)wsb;
+        const E* Pw = (const E*)(wsb + kWsPlane);
+        constexpr int CPR = CH / G::EPC;
+        for (int task = tid; task < CH * CPR; task += 256) {
+          const int row = task / CPR, ch = task % CPR;
+          const int so = row * CH + ch * G::EPC, dofs = row * LDT + ch * G::EPC;
+          *(u32x4_t*)(Th + dofs) = *(const u32x4_t*)(Tw + so);
+          *(u32x4_t*)(Ph + dofs) = *(const u32x4_t*)(Pw + so);
+          if constexpr (SPLIT) {
+            *(u32x4_t*)(Tl + dofs) = *(const u32x4_t*)(Tw + CH * CH + so);
+            *(u32x4_t*)(Pl + dofs) = *(const u32x4_t*)(Pw + CH * CH + so);
+          }
+        }
+      }
+      for (int idx = tid; idx < CH * VSL; idx += 256) {
+        const int i = idx / VSL, e = idx % VSL;
+        float x = 0.f;
+        if (i < len) {
+          const E raw = Vg[((size_t)(t0 + i) * H + h) * DV + e0 + e];
+          if constexpr (BF16) x = bf16_val(raw); else x = raw;
+        }
+        Vs[idx] = x;
+      }
+      if (tid < CH) {
+        const float* gw = (const float*)(wsb + 2 * kWsPlane);
+        const float gi = gw[tid], gl = gw[CH - 1];
+        gam[tid] = __expf(gi);
+        rr[tid] = __expf(gl - gi);
+      }
+      __syncthreads();
+
+      // (1) X = K S^T, Y = Q S^T   (rows 16w.., cols e)
+      f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += G::KSTEP) {
+        const typename G::F aK = ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4);
+        const typename G::F aQ = ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4);
+        const typename G::F bh = ld_rowk<BF16>(Sh, LDSS, c16, k0, q4);
+        X = mma<BF16>(aK, bh, X);
+        Y = mma<BF16>(aQ, bh, Y);
+        if constexpr (SPLIT) {
+          const typename G::F bl = ld_rowk<BF16>(Sl, LDSS, c16, k0, q4);
+          X = mma<BF16>(aK, bl, X);
+          Y = mma<BF16>(aQ, bl, Y);
+        }
+      }
+      // (2) R = V - gamma * X  -> R^T
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * q4 + r;
+        const float R = Vs[i * VSL + c16] - gam[i] * X[r];
+        put_split<BF16>(Rh, Rl, c16 * LDR + i, R);
+      }
+      __syncthreads();
+
+      // (3) U = T'' R  (T'' lower triangular: k < 16(w+1))
+      const int kend = 16 * (w + 1);
+      f32x4_t Uacc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < kend; k0 += G::KSTEP) {
+        const typename G::F ah = ld_rowk<BF16>(Th, LDT, 16 * w + c16, k0, q4);
+        const typename G::F bh = ld_rowk<BF16>(Rh, LDR, c16, k0, q4);
+        Uacc = mma<BF16>(ah, bh, Uacc);
+        if constexpr (SPLIT) {
+          Uacc = mma<BF16>(ah, ld_rowk<BF16>(Rl, LDR, c16, k0, q4), Uacc);
+          Uacc = mma<BF16>(ld_rowk<BF16>(Tl, LDT, 16 * w + c16, k0, q4), bh, Uacc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * q4 + r;
+        put_split<BF16>(Uh, Ul, c16 * LDR + i, Uacc[r]);
+        put_split<BF16>(U2h, U2l, c16 * LDR + i, Uacc[r] * rr[i]);
+      }
+      __syncthreads();
+
+      // (4) O = gamma * Y + P U
+      {
+        f32x4_t Z = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < kend; k0 += G::KSTEP) {
+          const typename G::F ah = ld_rowk<BF16>(Ph, LDT, 16 * w + c16, k0, q4);
+          const typename G::F bh = ld_rowk<BF16>(Uh, LDR, c16, k0, q4);
+          Z = mma<BF16>(ah, bh, Z);
+          if constexpr (SPLIT) {
+            Z = mma<BF16>(ah, ld_rowk<BF16>(Ul, LDR, c16, k0, q4), Z);
+            Z = mma<BF16>(ld_rowk<BF16>(Pl, LDT, 16 * w + c16, k0, q4), bh, Z);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * q4 + r;
+          if (i < len) {
+            const float val = args.scale * (gam[i] * Y[r] + Z[r]);
+            E* dst = Og + ((size_t)(t0 + i) * H + h) * DV + e0 + c16;
+            if constexpr (BF16) *dst = bf16_bits(val); else *dst = val;
+          }
+        }
+      }
+      // (5) S = gamma_C S + U'^T K
+      {
+        const float gC = gam[CH - 1];
+#pragma unroll
+        for (int bi = 0; bi < DBW; ++bi) {
+          const int db = w * DBW + bi;
+          if (db < NDB) {
+            f32x4_t acc = Sreg[bi] * gC;
+#pragma unroll
+            for (int k0 = 0; k0 < CH; k0 += G::KSTEP) {
+              const typename G::F bk = ld_kcol<BF16>(Ks, LDK, 16 * db + c16, k0, q4);
+              acc = mma<BF16>(ld_rowk<BF16>(U2h, LDR, c16, k0, q4), bk, acc);
+              if constexpr (SPLIT) acc = mma<BF16>(ld_rowk<BF16>(U2l, LDR, c16, k0, q4), bk, acc);
+            }
+            Sreg[bi] = acc;
+          }
+        }
+      }
+    }
+
+    // ---- end state: seg_final_state and the first child's start slot (the fork)
+    {
+      const int fc = first_child[s];
+      float* d1 = args.seg_final ? args.seg_final + ((size_t)s * H + h) * SZ : nullptr;
+      float* d2 = fc >= 0 ? args.seg_start + ((size_t)fc * H + h) * SZ : nullptr;
+#pragma unroll
+      for (int bi = 0; bi < DBW; ++bi) {
+        const int db = w * DBW + bi;
+        if (db < NDB)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const size_t idx = (size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16;
+            if (d1) d1[idx] = Sreg[bi][r];
+            if (d2) d2[idx] = Sreg[bi][r];
+          }
+      }
+    }
+  }
+}
+
+template <bool BF16, int DK>
+fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
+  const bool cap = stream_capturing(stream);
+  const int cus = device_cu_count();
+  int grid = 4 * cus;
+  if (!cap) {
+    const long long items = (long long)m->num_chunks * a.H;
+    if (items < grid) grid = (int)(items > 0 ? items : 1);
+  }
+  hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a);
+  FORK_HIP_CHECK(hipGetLastError());
+  // One scan launch per depth (children start after their parents ended).
+  // Under capture, every depth up to the capacity is recorded; depths beyond
+  // the current tree exit at once.
+  const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
+  const int sgrid = 2 * cus;
+  for (int lv = 0; lv < levels; ++lv) {
+    a.level = lv;
+    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(256), 0, stream, a);
+    FORK_HIP_CHECK(hipGetLastError());
+  }
+  return FORK_OK;
+}
+
+}  // namespace
+
+size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv) {
+  (void)dk;
+  (void)dv;
+  const BlobLayout L = blob_layout(m->caps);
+  return (size_t)L.chunk_cap * H * kWsChunk;
+}
+
+fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v, const float* a,
+                       const float* b, const float* root_state, void* o, float* seg_start_state,
+                       float* seg_final_state, int H, int dk, int dv, float scale, fork_dtype dt,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)dv;
+  (void)ws_bytes;
+  GdnArgs g;
+  g.blob = (const int32_t*)m->dev;
+  g.q = q;
+  g.k = k;
+  g.v = v;
+  g.a = a;
+  g.b = b;
+  g.root_state = root_state;
+  g.o = o;
+  g.seg_start = seg_start_state;
+  g.seg_final = seg_final_state;
+  g.ws = (unsigned char*)ws;
+  g.H = H;
+  g.scale = scale;
+  g.level = 0;
+  if (dt == FORK_BF16) {
+    if (dk == 128) return launch_gdn_t<true, 128>(m, g, stream);
+    if (dk == 64) return launch_gdn_t<true, 64>(m, g, stream);
+    return launch_gdn_t<true, 32>(m, g, stream);
+  }
+  if (dk == 128) return launch_gdn_t<false, 128>(m, g, stream);
+  if (dk == 64) return launch_gdn_t<false, 64>(m, g, stream);
+  return launch_gdn_t<false, 32>(m, g, stream);
+}
+
+}  // namespace fork

@@ -1,0 +1,135 @@
+"""Device buffers and calls of the hot path for one capacity bucket.
+
+PyTorch provides device memory, pinned host memory and streams; every step of
+the path runs in libforkattn.so through ``binding``. A ForkSession owns:
+
+* the metadata blob (device) and a ring of pinned staging buffers, so a new
+  tree can be planned on the host while the previous upload is still queued;
+* the Gated DeltaNet workspace (sized for the bucket's capacities);
+* optionally a recorded graph of both layers (``capture``).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+FORK_DT = {"f32": B.FORK_F32, "bf16": B.FORK_BF16}
+
+
+class ForkSession:
+    def __init__(self, t_cap: int, s_cap: int, depth_cap: int, gqa_group: int,
+                 gH: int = 0, dk: int = 0, dv: int = 0, device: str = "cuda", ring: int = 2):
+        self.caps = B.make_caps(t_cap, s_cap, depth_cap, gqa_group)
+        dev_bytes, stg_bytes = B.fork_meta_size(self.caps)
+        self.device = torch.device(device)
+        self.blob = torch.empty(dev_bytes, dtype=torch.uint8, device=self.device)
+        self.staging = [torch.empty(stg_bytes, dtype=torch.uint8, pin_memory=True)
+                        for _ in range(ring)]
+        self.events = [None] * ring
+        self._slot = 0
+        self.meta = None
+        self.gdn_ws = None
+        if gH:
+            probe = B.fork_meta()
+            probe.caps = self.caps
+            n = B.gdn_fork_workspace(probe, gH, dk, dv, B.FORK_BF16)
+            self.gdn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        self.graph = None
+
+    # -- metadata -----------------------------------------------------------
+    def build(self, parent, seg_len, stream=None) -> B.fork_meta:
+        parent = np.ascontiguousarray(parent, np.int32)
+        seg_len = np.ascontiguousarray(seg_len, np.int32)
+        i = self._slot
+        self._slot = (i + 1) % len(self.staging)
+        if self.events[i] is not None:
+            self.events[i].synchronize()  # the upload that last used this buffer is done
+        self.meta = B.fork_meta_build(parent, seg_len, self.caps, self.blob, self.staging[i],
+                                      stream=stream)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream() if stream is None else stream)
+        self.events[i] = ev
+        return self.meta
+
+    # -- layers -------------------------------------------------------------
+    def attention(self, q, k, v, o, lse=None, scale: float = 0.0, stream=None):
+        T, H, D = q.shape
+        Hkv = k.shape[1]
+        dt = B.FORK_BF16 if q.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_attn_forward(self.meta, q, k, v, o, lse, H, Hkv, D, scale, dt, None, 0,
+                            stream=stream)
+
+    def gdn(self, q, k, v, a, b, o, seg_start_state, seg_final_state=None, root_state=None,
+            scale: float = 1.0, stream=None):
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        dt = B.FORK_BF16 if q.dtype == torch.bfloat16 else B.FORK_F32
+        B.gdn_fork_forward(self.meta, q, k, v, a, b, root_state, o, seg_start_state,
+                           seg_final_state, H, dk, dv, scale, dt, self.gdn_ws,
+                           self.gdn_ws.numel(), stream=stream)
+
+    # -- graphs -------------------------------------------------------------
+    def capture(self, attn: dict, gdn: dict, stream=None) -> int:
+        """Record both layers for this bucket. attn: q, k, v, o, lse, scale;
+        gdn: q, k, v, a, b, root_state, o, seg_start_state, seg_final_state, scale.
+        Tensors must be sized for the bucket capacity."""
+        A = B.fork_graph_args()
+        p = B._ptr
+        A.q, A.k, A.v, A.o = p(attn["q"]), p(attn["k"]), p(attn["v"]), p(attn["o"])
+        A.lse = p(attn.get("lse"))
+        A.H, A.Hkv, A.D = attn["q"].shape[1], attn["k"].shape[1], attn["q"].shape[2]
+        A.scale = float(attn.get("scale", 0.0))
+        A.attn_ws, A.attn_ws_bytes = None, 0
+        A.gq, A.gk, A.gv = p(gdn["q"]), p(gdn["k"]), p(gdn["v"])
+        A.a, A.b = p(gdn["a"]), p(gdn["b"])
+        A.root_state = p(gdn.get("root_state"))
+        A.go = p(gdn["o"])
+        A.seg_start_state = p(gdn["seg_start_state"])
+        A.seg_final_state = p(gdn.get("seg_final_state"))
+        A.gH, A.dk, A.dv = gdn["q"].shape[1], gdn["q"].shape[2], gdn["v"].shape[2]
+        A.gscale = float(gdn.get("scale", 1.0))
+        A.gdn_ws, A.gdn_ws_bytes = p(self.gdn_ws), self.gdn_ws.numel()
+        A.dt = B.FORK_BF16 if attn["q"].dtype == torch.bfloat16 else B.FORK_F32
+        if self.graph is not None:
+            B.fork_graph_destroy(self.graph)
+        self.graph = B.fork_graph_create(self.meta, A, stream=stream)
+        return self.graph
+
+    def replay(self, stream=None):
+        B.fork_graph_launch(self.graph, stream=stream)
+
+    def close(self):
+        if self.graph is not None:
+            B.fork_graph_destroy(self.graph)
+            self.graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=None):
+    """Exact capacities of one tree (eager use)."""
+    parent = np.asarray(parent)
+    depth = np.zeros(len(parent), np.int64)
+    for s in range(len(parent)):
+        if parent[s] >= 0:
+            depth[s] = depth[parent[s]] + 1
+    return dict(t_cap=t_cap or int(np.sum(seg_len)), s_cap=s_cap or len(parent),
+                depth_cap=depth_cap if depth_cap is not None else int(depth.max()),
+                gqa_group=gqa_group)
+
+
+def to_device(wl, device="cuda"):
+    """Device tensors of a workload (q/k/v in its dtype, a/b/root fp32)."""
+    dt = TORCH_DT[wl.dtype]
+    t = lambda x, d=dt: torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=d)
+    out = dict(q=t(wl.q), k=t(wl.k), v=t(wl.v), gq=t(wl.gq), gk=t(wl.gk), gv=t(wl.gv),
+               a=t(wl.a, torch.float32), b=t(wl.b, torch.float32))
+    out["root_state"] = None if wl.root_state is None else t(wl.root_state, torch.float32)
+    return out
