@@ -54,66 +54,147 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Stage keys [j0, j0 + 64) of kv head g: K row-major into Ks, V transposed into
-// Vt. Rows past `jmax` repeat row jmax (in range; their scores are masked).
-template <bool BF16, int D, typename E>
-__device__ __forceinline__ void stage_kv(E* __restrict__ Ks, E* __restrict__ Vt,
-                                         const E* __restrict__ K, const E* __restrict__ V,
-                                         int j0, int jmax, int g, int Hkv, int tid) {
+// Key/value tile of 64 keys held in registers between its global load and
+// its LDS store, so the next tile's loads are in flight while the current
+// tile is being computed.
+template <bool BF16, int D>
+struct KVRegs {
   using C = AttnCfg<BF16, D>;
+  static constexpr int KT = kAttnKeys * C::CPR / 256;     // 16-byte K loads per thread
+  static constexpr int VTASKS = (kAttnKeys / 4) * C::CPR;  // (4 keys x 16 bytes) V tasks
+  static constexpr int VT = (VTASKS + 255) / 256;
+  u32x4_t k[KT];
+  u32x4_t v[VT][4];
+};
+
+// Global loads of keys [j0, j0 + 64) of kv head g; rows past `jmax` repeat
+// row jmax (in range; their scores are masked).
+template <bool BF16, int D, typename E>
+__device__ __forceinline__ void kv_load(KVRegs<BF16, D>& r, const E* __restrict__ K,
+                                        const E* __restrict__ V, int j0, int jmax, int g, int Hkv,
+                                        int tid) {
+  using C = AttnCfg<BF16, D>;
+  using R = KVRegs<BF16, D>;
 #pragma unroll
-  for (int task = tid; task < kAttnKeys * C::CPR; task += 256) {
+  for (int i = 0; i < R::KT; ++i) {
+    const int task = tid + 256 * i;
     const int row = task / C::CPR, ch = task % C::CPR;
     const int j = min(j0 + row, jmax);
-    const u32x4_t val = *(const u32x4_t*)(K + ((size_t)j * Hkv + g) * D + ch * C::EPC);
-    *(u32x4_t*)(Ks + row * C::KS + ch * C::EPC) = val;
+    r.k[i] = *(const u32x4_t*)(K + ((size_t)j * Hkv + g) * D + ch * C::EPC);
   }
 #pragma unroll
-  for (int task = tid; task < (kAttnKeys / 4) * C::CPR; task += 256) {
-    const int kq = task / C::CPR, ch = task % C::CPR;
-    u32x4_t x[4];
+  for (int i = 0; i < R::VT; ++i) {
+    const int task = tid + 256 * i;
+    if (task < R::VTASKS) {
+      const int kq = task / C::CPR, ch = task % C::CPR;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = min(j0 + 4 * kq + jj, jmax);
-      x[jj] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
-    }
-    if constexpr (BF16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int w = i >> 1, sh = (i & 1) * 16;
-        const unsigned e0 = (x[0][w] >> sh) & 0xffffu, e1 = (x[1][w] >> sh) & 0xffffu;
-        const unsigned e2 = (x[2][w] >> sh) & 0xffffu, e3 = (x[3][w] >> sh) & 0xffffu;
-        uint2 pk;
-        pk.x = e0 | (e1 << 16);
-        pk.y = e2 | (e3 << 16);
-        *(uint2*)(Vt + (ch * 8 + i) * C::VS + 4 * kq) = pk;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x4_t pk;
-        pk[0] = x[0][i];
-        pk[1] = x[1][i];
-        pk[2] = x[2][i];
-        pk[3] = x[3][i];
-        *(u32x4_t*)(Vt + (ch * 4 + i) * C::VS + 4 * kq) = pk;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = min(j0 + 4 * kq + jj, jmax);
+        r.v[i][jj] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
       }
     }
   }
 }
 
+// LDS stores of a loaded tile: K row-major into Ks, V transposed into Vt.
+template <bool BF16, int D, typename E>
+__device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict__ Ks,
+                                         E* __restrict__ Vt, int tid) {
+  using C = AttnCfg<BF16, D>;
+  using R = KVRegs<BF16, D>;
+#pragma unroll
+  for (int i = 0; i < R::KT; ++i) {
+    const int task = tid + 256 * i;
+    const int row = task / C::CPR, ch = task % C::CPR;
+    *(u32x4_t*)(Ks + row * C::KS + ch * C::EPC) = r.k[i];
+  }
+#pragma unroll
+  for (int i2 = 0; i2 < R::VT; ++i2) {
+    const int task = tid + 256 * i2;
+    if (task < R::VTASKS) {
+      const int kq = task / C::CPR, ch = task % C::CPR;
+      const u32x4_t* x = r.v[i2];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int w = i >> 1, sh = (i & 1) * 16;
+          const unsigned e0 = (x[0][w] >> sh) & 0xffffu, e1 = (x[1][w] >> sh) & 0xffffu;
+          const unsigned e2 = (x[2][w] >> sh) & 0xffffu, e3 = (x[3][w] >> sh) & 0xffffu;
+          uint2 pk;
+          pk.x = e0 | (e1 << 16);
+          pk.y = e2 | (e3 << 16);
+          *(uint2*)(Vt + (ch * 8 + i) * C::VS + 4 * kq) = pk;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4_t pk;
+          pk[0] = x[0][i];
+          pk[1] = x[1][i];
+          pk[2] = x[2][i];
+          pk[3] = x[3][i];
+          *(u32x4_t*)(Vt + (ch * 4 + i) * C::VS + 4 * kq) = pk;
+        }
+      }
+    }
+  }
+}
+
+// Walks the key tiles of a query tile: every ancestor segment's range (fully
+// visible), nearest ancestor first, then the tile's own range (tree-masked).
+struct TileIter {
+  int a, j0, hi;
+  bool own, done;
+};
+
+__device__ __forceinline__ void iter_init(TileIter& it, const AttnTile& tile,
+                                          const int32_t* __restrict__ seg_start,
+                                          const int32_t* __restrict__ seg_len) {
+  it.a = (tile.info & kTileAncMask) - 1;
+  it.done = false;
+  if (it.a >= 0) {
+    it.own = false;
+    it.j0 = seg_start[it.a];
+    it.hi = it.j0 + seg_len[it.a];
+  } else {
+    it.own = true;
+    it.j0 = tile.own_lo;
+    it.hi = tile.t1;
+  }
+}
+
+__device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
+                                          const int32_t* __restrict__ parent,
+                                          const int32_t* __restrict__ seg_start,
+                                          const int32_t* __restrict__ seg_len) {
+  it.j0 += kAttnKeys;
+  if (it.j0 < it.hi) return;
+  if (!it.own) {
+    it.a = parent[it.a];
+    if (it.a >= 0) {
+      it.j0 = seg_start[it.a];
+      it.hi = it.j0 + seg_len[it.a];
+    } else {
+      it.own = true;
+      it.j0 = tile.own_lo;
+      it.hi = tile.t1;
+    }
+    return;
+  }
+  it.done = true;
+}
+
+// Two workgroups per CU (<= 256 VGPRs) except fp32 with D = 128, whose larger
+// fragments need the whole register file.
 template <bool BF16, int D>
-__global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
+__global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
+    fork_attn_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
   using C = AttnCfg<BF16, D>;
   using E = typename std::conditional<BF16, unsigned short, float>::type;
   using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
   __shared__ __attribute__((aligned(16))) E Ks[kAttnKeys * C::KS];
   __shared__ __attribute__((aligned(16))) E Vt[D * C::VS];
 
-  const int32_t* __restrict__ blob = args.blob;
   const int ntiles = blob[MH_NTILES];
   const int TT = blob[MH_TILE_TOKENS];
   const AttnTile* __restrict__ tiles = (const AttnTile*)(blob + blob[MH_OFF_TILES]);
@@ -133,7 +214,11 @@ __global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int ti = item / Hkv, g = item - ti * Hkv;
-    const AttnTile tile = tiles[ti];
+    AttnTile tile;  // uniform across the workgroup: keep it in scalar registers
+    tile.t0 = __builtin_amdgcn_readfirstlane(tiles[ti].t0);
+    tile.t1 = __builtin_amdgcn_readfirstlane(tiles[ti].t1);
+    tile.own_lo = __builtin_amdgcn_readfirstlane(tiles[ti].own_lo);
+    tile.info = __builtin_amdgcn_readfirstlane(tiles[ti].info);
 
     // this lane's query row (rows past the tile are clamped and not stored)
     const int r = wave * 32 + l32;
@@ -162,11 +247,8 @@ __global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-    // one 64-key tile of range [lo, hi_): own == tree-masked own range
-    auto kv_tile = [&](int j0, int hi_, bool own) {
-      __syncthreads();  // previous tile fully consumed
-      stage_kv<BF16, D, E>(Ks, Vt, K, V, j0, hi_ - 1, g, Hkv, tid);
-      __syncthreads();
+    // compute one staged 64-key tile of range [j0, hi_); own == tree-masked own range
+    auto kv_compute = [&](int j0, int hi_, bool own) {
 
       f32x16_t s[2];
 #pragma unroll
@@ -187,42 +269,52 @@ __global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
         }
       }
 
-      // scale, mask, online softmax (scores in log2 units)
+      // Online softmax in log2 units, p = exp2(s * c - m) with c = scale * log2(e).
+      // A lane raises its running max m only when the tile's max exceeds it by
+      // more than 8 (a factor of 256); otherwise the stale max is kept. That is
+      // exact (numerator and denominator share m), keeps p <= 256, and skips
+      // rescaling the accumulators unless some lane of the wave raised its max.
       const bool need_mask = own ? ((tile.info & kTileMulti) != 0 || j0 + kAttnKeys > tile.t0)
                                  : (j0 + kAttnKeys > hi_);
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * b + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool vis = (j < hi_) & (!own | ((j >= lo_row) & (j <= t_row)));
+            s[b][i] = vis ? s[b][i] : -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[b][i] * args.scale_log2;
-          if (need_mask) {
-            const int j = j0 + 32 * b + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool vis = j < hi_ && (!own || (j >= lo_row && j <= t_row));
-            x = vis ? x : -INFINITY;
-          }
-          s[b][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * args.scale_log2;
+      const bool grow = mx > m_run + 8.f;
+      float alpha = 1.f;
+      if (grow) {
+        alpha = __builtin_amdgcn_exp2f(m_run - mx);
+        m_run = mx;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
       float psum = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[b][i] - m_use);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][i], args.scale_log2, mneg));
           s[b][i] = p;
           psum += p;
         }
       l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
       // O^T += V^T P^T
 #pragma unroll
@@ -261,13 +353,21 @@ __global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
       }
     };
 
-    // ancestors: each fully visible
-    for (int a = (tile.info & kTileAncMask) - 1; a >= 0; a = parent[a]) {
-      const int lo = seg_start[a], hi_ = lo + seg_len[a];
-      for (int j0 = lo; j0 < hi_; j0 += kAttnKeys) kv_tile(j0, hi_, false);
+    // software pipeline: tile i+1 is loaded into registers while tile i computes
+    TileIter it;
+    iter_init(it, tile, seg_start, seg_len);
+    KVRegs<BF16, D> rg;
+    kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+    while (!it.done) {
+      const int j0 = it.j0, hi_ = it.hi;
+      const bool own = it.own;
+      __syncthreads();  // every wave is done with the previous tile
+      kv_store<BF16, D, E>(rg, Ks, Vt, tid);
+      __syncthreads();
+      iter_next(it, tile, parent, seg_start, seg_len);
+      if (!it.done) kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+      kv_compute(j0, hi_, own);
     }
-    // own range, tree-masked
-    for (int j0 = tile.own_lo; j0 < tile.t1; j0 += kAttnKeys) kv_tile(j0, tile.t1, true);
 
     // finalize
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -303,7 +403,7 @@ __global__ void __launch_bounds__(256, 2) fork_attn_kernel(AttnArgs args) {
 
 template <bool BF16, int D>
 fork_status launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
@@ -327,7 +427,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.scale_log2 = sc * 1.4426950408889634f;
   // Persistent grid: two workgroups per CU. Under capture the tree can change
   // between replays, so the grid must not depend on the current tile count.
-  int grid = 2 * device_cu_count();
+  int grid = (dt == FORK_F32 && D == 128 ? 1 : 2) * device_cu_count();
   if (!stream_capturing(stream)) {
     const long long items = (long long)m->num_attn_tiles * Hkv;
     if (items < grid) grid = (int)(items > 0 ? items : 1);

@@ -136,26 +136,10 @@ struct GdnArgs {
   int level;
 };
 
-// Load rows [t0, t0 + len) of one head of a [T, H, DK] tensor into a padded
-// LDS tile [64][DK + PAD]; rows >= len are zero.
-template <bool BF16, int DK>
-__device__ __forceinline__ void load_rows(typename GT<BF16>::E* dst, const typename GT<BF16>::E* src, int t0,
-                                          int len, int H, int h, int tid) {
-  using G = GT<BF16>;
-  constexpr int CPR = DK / G::EPC;
-  constexpr int LD = DK + G::PAD;
-  for (int task = tid; task < CH * CPR; task += 256) {
-    const int row = task / CPR, ch = task % CPR;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (row < len) val = *(const u32x4_t*)(src + ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC);
-    *(u32x4_t*)(dst + row * LD + ch * G::EPC) = val;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Prep: per (chunk, head) compute g, T'' = (I + A)^-1 diag(b), P = QK^T * Gamma.
 template <bool BF16, int DK>
-__global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs args) {
+__global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
   using G = GT<BF16>;
   using E = typename G::E;
   constexpr int LDK = DK + G::PAD;
@@ -167,7 +151,6 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs args) {
   __shared__ float Zs[4][16 * 20];
   __shared__ float gs[CH], bs[CH];
 
-  const int32_t* __restrict__ blob = args.blob;
   const int nchunks = blob[MH_NCHUNKS];
   const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
   const int H = args.H;
@@ -176,35 +159,62 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs args) {
   const E* __restrict__ Kg = (const E*)args.k;
   const E* __restrict__ Qg = (const E*)args.q;
 
-  for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x) {
+  // registers of the next item: its k and q rows, a and b (prefetched while
+  // the current item computes)
+  constexpr int CPR = DK / G::EPC;
+  constexpr int KL = CH * CPR / 256;
+  u32x4_t rk[KL], rq[KL];
+  float ra = 1.f, rb = 0.f;
+  int rlen = 0;
+  // rows past the chunk are clamped to its last row (in range) and zeroed at
+  // the LDS store, so no load sits in a divergent branch
+  auto prep_load = [&](int item) {
     const int c = item / H, h = item - c * H;
     const int2 ck = chunks[c];
-    const int t0 = ck.x, len = ck.y;
+    rlen = ck.y;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int task = tid + 256 * i, row = min(task / CPR, ck.y - 1), ch = task % CPR;
+      const size_t off = ((size_t)(ck.x + row) * H + h) * DK + ch * G::EPC;
+      rk[i] = *(const u32x4_t*)(Kg + off);
+      rq[i] = *(const u32x4_t*)(Qg + off);
+    }
+    const size_t ab = (size_t)(ck.x + min(tid & (CH - 1), ck.y - 1)) * H + h;
+    ra = args.a[ab];
+    rb = args.b[ab];
+  };
+  if (blockIdx.x < nchunks * H) prep_load(blockIdx.x);
+
+  for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x) {
+    const int c = item / H, h = item - c * H;
     unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
 
     __syncthreads();  // LDS reuse across items
-    load_rows<BF16, DK>(Ks, Kg, t0, len, H, h, tid);
-    load_rows<BF16, DK>(Qs, Qg, t0, len, H, h, tid);
+    const int len = rlen;
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int task = tid + 256 * i, row = task / CPR, ch = task % CPR;
+      *(u32x4_t*)(Ks + row * LDK + ch * G::EPC) = row < len ? rk[i] : z4;
+      *(u32x4_t*)(Qs + row * LDK + ch * G::EPC) = row < len ? rq[i] : z4;
+    }
     if (w == 0) {
       // g = inclusive cumulative sum of log a (padding: a = 1, b = 0)
       const int i = lane;
-      float la = 0.f, bb = 0.f;
-      if (i < len) {
-        la = logf(args.a[(size_t)(t0 + i) * H + h]);
-        bb = args.b[(size_t)(t0 + i) * H + h];
-      }
+      float la = i < len ? logf(ra) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(la, off);
         if (i >= off) la += y;
       }
       gs[i] = la;
-      bs[i] = bb;
+      bs[i] = i < len ? rb : 0.f;
       ((float*)(wsb + 2 * kWsPlane))[i] = la;
     }
     // zero Ts (upper blocks stay zero)
     for (int i = tid; i < CH * LDA; i += 256) Ts[i] = 0.f;
     __syncthreads();
+    if (item + (int)gridDim.x < nchunks * H) prep_load(item + gridDim.x);
 
     // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal)
     {
@@ -285,10 +295,60 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs args) {
   }
 }
 
+// Everything one scan chunk reads from global memory, held in registers
+// between its loads (issued while the previous chunk computes) and its LDS
+// stores.
+template <bool BF16, int DK>
+struct ScanRegs {
+  using G = GT<BF16>;
+  static constexpr int KL = CH * (DK / G::EPC) / 256;  // 16-byte K (and Q) loads per thread
+  static constexpr int WL = (int)(kWsPlane / 16) / 256; // 16-byte T'' (and P) loads per thread
+  static constexpr int VL = CH * VSL / 256;             // V elements per thread
+  u32x4_t k[KL], q[KL], t[WL], p[WL];
+  typename G::E v[VL];
+  float g, glast;
+};
+
+// Issues every load of chunk (t0, len) of head h. Rows past len are clamped to
+// the chunk's last row (always in range) and zeroed when stored to LDS, so no
+// load sits in a divergent branch (which would force an early wait on every
+// outstanding load).
+template <bool BF16, int DK>
+__device__ __forceinline__ void scan_load(ScanRegs<BF16, DK>& r, const typename GT<BF16>::E* Kg,
+                                          const typename GT<BF16>::E* Qg, const typename GT<BF16>::E* Vg,
+                                          const unsigned char* wsb, int t0, int len, int H, int h, int e0,
+                                          int tid) {
+  using G = GT<BF16>;
+  using R = ScanRegs<BF16, DK>;
+  constexpr int CPR = DK / G::EPC;
+#pragma unroll
+  for (int i = 0; i < R::KL; ++i) {
+    const int task = tid + 256 * i, row = min(task / CPR, len - 1), ch = task % CPR;
+    const size_t off = ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC;
+    r.k[i] = *(const u32x4_t*)(Kg + off);
+    r.q[i] = *(const u32x4_t*)(Qg + off);
+  }
+  const u32x4_t* Tw = (const u32x4_t*)wsb;
+  const u32x4_t* Pw = (const u32x4_t*)(wsb + kWsPlane);
+#pragma unroll
+  for (int i = 0; i < R::WL; ++i) {
+    r.t[i] = Tw[tid + 256 * i];
+    r.p[i] = Pw[tid + 256 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < R::VL; ++i) {
+    const int idx = tid + 256 * i, row = min(idx / VSL, len - 1), e = idx % VSL;
+    r.v[i] = Vg[((size_t)(t0 + row) * H + h) * DK + e0 + e];
+  }
+  const float* gw = (const float*)(wsb + 2 * kWsPlane);
+  r.g = gw[tid & (CH - 1)];
+  r.glast = gw[CH - 1];
+}
+
 // ---------------------------------------------------------------------------
 // Scan: one launch per depth; items (segment, head, 16-row state slice).
 template <bool BF16, int DK>
-__global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
+__global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
   using G = GT<BF16>;
   using E = typename G::E;
   constexpr int DV = DK;
@@ -317,7 +377,6 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
   __shared__ float Vs[CH * VSL];
   __shared__ float gam[CH], rr[CH];
 
-  const int32_t* __restrict__ blob = args.blob;
   const int level = args.level;
   if (level > blob[MH_MAXDEPTH]) return;
   const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
@@ -327,7 +386,7 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
   const int32_t* __restrict__ root_ord = blob + blob[MH_OFF_ROOTORD];
   const int32_t* __restrict__ first_child = blob + blob[MH_OFF_FIRSTCHILD];
   const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
-  const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
+  const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
   const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
   const int H = args.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -340,49 +399,63 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
 
   for (int item = blockIdx.x; item < nlev * H * NS; item += gridDim.x) {
     const int sl = item % NS, h = (item / NS) % H, li = item / (NS * H);
-    const int s = level_seg[lv0 + li];
+    // per-item metadata, uniform across the workgroup (scalar loads)
+    const int s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + li]);
     const int e0 = sl * VSL;
+    const int p = __builtin_amdgcn_readfirstlane(parent[s]);
+    const int L = __builtin_amdgcn_readfirstlane(seg_len[s]);
+    const int st = __builtin_amdgcn_readfirstlane(seg_start[s]);
+    const int cb = __builtin_amdgcn_readfirstlane(chunk_base[s]);
+    const int fc_p = p >= 0 ? __builtin_amdgcn_readfirstlane(first_child[p]) : -1;
+    const int ro = p < 0 ? __builtin_amdgcn_readfirstlane(root_ord[s]) : 0;
+    // chunk ci of the segment covers tokens [st + 64 ci, st + min(64 (ci + 1), L))
+    const int nck = (L + CH - 1) / CH;
 
-    // ---- start state: root_state / zero, or the parent's end state
+    // ---- start state: root_state / zero, or the parent's end state (read from
+    // the first child's start slot, where the parent's scan left it)
+    const float* src = nullptr;
+    float* dst = nullptr;
+    float* own_slot = args.seg_start + ((size_t)s * H + h) * SZ;
+    if (p < 0) {
+      if (args.root_state) src = args.root_state + ((size_t)ro * H + h) * SZ;
+      dst = own_slot;
+    } else {
+      src = args.seg_start + ((size_t)fc_p * H + h) * SZ;
+      if (fc_p != s) dst = own_slot;
+    }
+    // branch-free loads from an always-valid address; zero when there is no source
+    const bool has_src = src != nullptr;
+    const float* lsrc = has_src ? src : own_slot;
     f32x4_t Sreg[DBW];
-    {
-      const float* src = nullptr;
-      float* dst = nullptr;
-      const int p = parent[s];
-      if (p < 0) {
-        if (args.root_state) src = args.root_state + ((size_t)root_ord[s] * H + h) * SZ;
-        dst = args.seg_start + ((size_t)s * H + h) * SZ;
-      } else {
-        const int fc = first_child[p];
-        src = args.seg_start + ((size_t)fc * H + h) * SZ;
-        if (fc != s) dst = args.seg_start + ((size_t)s * H + h) * SZ;
+#pragma unroll
+    for (int bi = 0; bi < DBW; ++bi) {
+      const int db = min(w * DBW + bi, NDB - 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = lsrc[(size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16];
+        Sreg[bi][r] = has_src ? x : 0.f;
       }
+    }
+    // first chunk's loads go out together with the state loads
+    ScanRegs<BF16, DK> rg;
+    scan_load<BF16, DK>(rg, Kg, Qg, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h,
+                        e0, tid);
+    if (dst) {
 #pragma unroll
       for (int bi = 0; bi < DBW; ++bi) {
         const int db = w * DBW + bi;
+        if (db < NDB)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = 0.f;
-          if (db < NDB) {
-            const size_t idx = (size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16;
-            x = src ? src[idx] : 0.f;
-            if (dst) dst[idx] = x;
-          }
-          Sreg[bi][r] = x;
-        }
+          for (int r = 0; r < 4; ++r) dst[(size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16] = Sreg[bi][r];
       }
     }
 
-    const int nck = (seg_len[s] + CH - 1) / CH;
-    const int cb = chunk_base[s];
     for (int ci = 0; ci < nck; ++ci) {
       const int c = cb + ci;
-      const int2 ck = chunks[c];
-      const int t0 = ck.x, len = ck.y;
-      const unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
+      const int t0 = st + CH * ci, len = min(CH, L - CH * ci);
 
       __syncthreads();  // previous chunk done with every LDS tile
-      // state slice -> LDS operand
+      // state slice and the prefetched chunk -> LDS operands
 #pragma unroll
       for (int bi = 0; bi < DBW; ++bi) {
         const int db = w * DBW + bi;
@@ -390,39 +463,46 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) put_split<BF16>(Sh, Sl, (4 * q4 + r) * LDSS + 16 * db + c16, Sreg[bi][r]);
       }
-      load_rows<BF16, DK>(Ks, Kg, t0, len, H, h, tid);
-      load_rows<BF16, DK>(Qs, Qg, t0, len, H, h, tid);
       {
-        const E* Tw = (const E*)wsb;
-        const E* Pw = (const E*)(wsb + kWsPlane);
-        constexpr int CPR = CH / G::EPC;
-        for (int task = tid; task < CH * CPR; task += 256) {
-          const int row = task / CPR, ch = task % CPR;
-          const int so = row * CH + ch * G::EPC, dofs = row * LDT + ch * G::EPC;
-          *(u32x4_t*)(Th + dofs) = *(const u32x4_t*)(Tw + so);
-          *(u32x4_t*)(Ph + dofs) = *(const u32x4_t*)(Pw + so);
+        using R = ScanRegs<BF16, DK>;
+        constexpr int CPR = DK / G::EPC;
+        const u32x4_t z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < R::KL; ++i) {
+          const int task = tid + 256 * i, row = task / CPR, ch = task % CPR;
+          *(u32x4_t*)(Ks + row * LDK + ch * G::EPC) = row < len ? rg.k[i] : z4;
+          *(u32x4_t*)(Qs + row * LDK + ch * G::EPC) = row < len ? rg.q[i] : z4;
+        }
+#pragma unroll
+        for (int i = 0; i < R::WL; ++i) {
+          const int cidx = tid + 256 * i;  // 16-byte chunk of a 16 KB operand region
           if constexpr (SPLIT) {
-            *(u32x4_t*)(Tl + dofs) = *(const u32x4_t*)(Tw + CH * CH + so);
-            *(u32x4_t*)(Pl + dofs) = *(const u32x4_t*)(Pw + CH * CH + so);
+            const int plane = cidx / (CH * CH / 8), rem = cidx % (CH * CH / 8);
+            const int dofs = (rem / 8) * LDT + (rem % 8) * 8;
+            *(u32x4_t*)((plane ? Tl : Th) + dofs) = rg.t[i];
+            *(u32x4_t*)((plane ? Pl : Ph) + dofs) = rg.p[i];
+          } else {
+            const int dofs = (cidx / 16) * LDT + (cidx % 16) * 4;
+            *(u32x4_t*)(Th + dofs) = rg.t[i];
+            *(u32x4_t*)(Ph + dofs) = rg.p[i];
           }
         }
-      }
-      for (int idx = tid; idx < CH * VSL; idx += 256) {
-        const int i = idx / VSL, e = idx % VSL;
-        float x = 0.f;
-        if (i < len) {
-          const E raw = Vg[((size_t)(t0 + i) * H + h) * DV + e0 + e];
-          if constexpr (BF16) x = bf16_val(raw); else x = raw;
+#pragma unroll
+        for (int i = 0; i < R::VL; ++i) {
+          const int idx = tid + 256 * i;
+          float x;
+          if constexpr (BF16) x = bf16_val(rg.v[i]); else x = rg.v[i];
+          Vs[idx] = idx / VSL < len ? x : 0.f;
         }
-        Vs[idx] = x;
-      }
-      if (tid < CH) {
-        const float* gw = (const float*)(wsb + 2 * kWsPlane);
-        const float gi = gw[tid], gl = gw[CH - 1];
-        gam[tid] = __expf(gi);
-        rr[tid] = __expf(gl - gi);
+        if (tid < CH) {
+          gam[tid] = __expf(rg.g);
+          rr[tid] = __expf(rg.glast - rg.g);
+        }
       }
       __syncthreads();
+      if (ci + 1 < nck)
+        scan_load<BF16, DK>(rg, Kg, Qg, Vg, args.ws + ((size_t)(c + 1) * H + h) * kWsChunk, t0 + CH,
+                            min(CH, L - CH * (ci + 1)), H, h, e0, tid);
 
       // (1) X = K S^T, Y = Q S^T   (rows 16w.., cols e)
       f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
@@ -512,7 +592,7 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(GdnArgs args) {
 
     // ---- end state: seg_final_state and the first child's start slot (the fork)
     {
-      const int fc = first_child[s];
+      const int fc = __builtin_amdgcn_readfirstlane(first_child[s]);
       float* d1 = args.seg_final ? args.seg_final + ((size_t)s * H + h) * SZ : nullptr;
       float* d2 = fc >= 0 ? args.seg_start + ((size_t)fc * H + h) * SZ : nullptr;
 #pragma unroll
@@ -534,12 +614,12 @@ template <bool BF16, int DK>
 fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const bool cap = stream_capturing(stream);
   const int cus = device_cu_count();
-  int grid = 4 * cus;
+  int grid = 2 * cus;
   if (!cap) {
     const long long items = (long long)m->num_chunks * a.H;
     if (items < grid) grid = (int)(items > 0 ? items : 1);
   }
-  hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
   // One scan launch per depth (children start after their parents ended).
   // Under capture, every depth up to the capacity is recorded; depths beyond
@@ -548,7 +628,7 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const int sgrid = 2 * cus;
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
-    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(256), 0, stream, a.blob, a);
     FORK_HIP_CHECK(hipGetLastError());
   }
   return FORK_OK;
