@@ -295,54 +295,87 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
   }
 }
 
-// Everything one scan chunk reads from global memory, held in registers
-// between its loads (issued while the previous chunk computes) and its LDS
-// stores.
+// Everything one scan chunk reads from global memory, in registers between
+// its loads (issued while the previous chunk computes) and its use. K is the
+// only chunk operand every wave needs in full, so it alone goes through LDS;
+// the other operands are loaded directly in the MFMA fragment layout of the
+// wave that uses them: rows 16w..16w+15 of Q, T'' and P as A fragments, and
+// v and g at the rows of this lane's accumulator elements.
 template <bool BF16, int DK>
-struct ScanRegs {
+struct ChunkRegs {
   using G = GT<BF16>;
-  static constexpr int KL = CH * (DK / G::EPC) / 256;  // 16-byte K (and Q) loads per thread
-  static constexpr int WL = (int)(kWsPlane / 16) / 256; // 16-byte T'' (and P) loads per thread
-  static constexpr int VL = CH * VSL / 256;             // V elements per thread
-  u32x4_t k[KL], q[KL], t[WL], p[WL];
-  typename G::E v[VL];
-  float g, glast;
+  using F = typename G::F;
+  static constexpr int KL = CH * (DK / G::EPC) / 256;  // 16-byte K loads per thread
+  static constexpr int NQ = DK / G::KSTEP;             // Q fragments (k-steps over dk)
+  static constexpr int NT = CH / G::KSTEP;             // T'', P fragments (k-steps over the chunk)
+  static constexpr int NP = BF16 ? 2 : 1;              // hi/lo planes
+  u32x4_t k[KL];
+  F q[NQ];
+  F t[NP][NT], p[NP][NT];
+  // one 32-bit register per v element: packing two 16-bit loads into one
+  // register would wait for them (and, the counter being in order, for every
+  // load issued before them)
+  typename std::conditional<BF16, unsigned, float>::type v[4];
+  float g[4], gl;
 };
 
-// Issues every load of chunk (t0, len) of head h. Rows past len are clamped to
-// the chunk's last row (always in range) and zeroed when stored to LDS, so no
-// load sits in a divergent branch (which would force an early wait on every
-// outstanding load).
+// Issues every load of chunk (t0, len) for head h and state slice e0. Rows past
+// len are clamped to the chunk's last row: they only meet zero coefficients
+// (b = 0 there, so T'' has zero columns and U zero rows) or produce output rows
+// that are never stored, so they need no masking and no load is divergent.
 template <bool BF16, int DK>
-__device__ __forceinline__ void scan_load(ScanRegs<BF16, DK>& r, const typename GT<BF16>::E* Kg,
-                                          const typename GT<BF16>::E* Qg, const typename GT<BF16>::E* Vg,
-                                          const unsigned char* wsb, int t0, int len, int H, int h, int e0,
-                                          int tid) {
+__device__ __forceinline__ void chunk_load(ChunkRegs<BF16, DK>& r, const typename GT<BF16>::E* __restrict__ Kg,
+                                           const typename GT<BF16>::E* __restrict__ Qg,
+                                           const typename GT<BF16>::E* __restrict__ Vg,
+                                           const unsigned char* __restrict__ wsb, int t0, int len, int H, int h,
+                                           int e0, int tid) {
   using G = GT<BF16>;
-  using R = ScanRegs<BF16, DK>;
+  using R = ChunkRegs<BF16, DK>;
+  using E = typename G::E;
   constexpr int CPR = DK / G::EPC;
+  const int lane = tid & 63, w = tid >> 6, c16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int i = 0; i < R::KL; ++i) {
     const int task = tid + 256 * i, row = min(task / CPR, len - 1), ch = task % CPR;
-    const size_t off = ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC;
-    r.k[i] = *(const u32x4_t*)(Kg + off);
-    r.q[i] = *(const u32x4_t*)(Qg + off);
+    r.k[i] = *(const u32x4_t*)(Kg + ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC);
   }
-  const u32x4_t* Tw = (const u32x4_t*)wsb;
-  const u32x4_t* Pw = (const u32x4_t*)(wsb + kWsPlane);
+  const int arow = 16 * w + c16;  // A-fragment row of this lane
+  {
+    const E* qrow = Qg + ((size_t)(t0 + min(arow, len - 1)) * H + h) * DK;
 #pragma unroll
-  for (int i = 0; i < R::WL; ++i) {
-    r.t[i] = Tw[tid + 256 * i];
-    r.p[i] = Pw[tid + 256 * i];
+    for (int f = 0; f < R::NQ; ++f) {
+      if constexpr (BF16)
+        r.q[f] = *(const bf16x8_t*)(qrow + f * G::KSTEP + 8 * q4);
+      else
+        r.q[f] = qrow[f * G::KSTEP + q4];
+    }
   }
+  const int kend = 16 * (w + 1);  // T'' and P are lower triangular
 #pragma unroll
-  for (int i = 0; i < R::VL; ++i) {
-    const int idx = tid + 256 * i, row = min(idx / VSL, len - 1), e = idx % VSL;
-    r.v[i] = Vg[((size_t)(t0 + row) * H + h) * DK + e0 + e];
+  for (int pl = 0; pl < R::NP; ++pl) {
+    const E* Tw = (const E*)wsb + pl * CH * CH + arow * CH;
+    const E* Pw = (const E*)(wsb + kWsPlane) + pl * CH * CH + arow * CH;
+#pragma unroll
+    for (int f = 0; f < R::NT; ++f) {
+      if (f * G::KSTEP < kend) {
+        if constexpr (BF16) {
+          r.t[pl][f] = *(const bf16x8_t*)(Tw + f * G::KSTEP + 8 * q4);
+          r.p[pl][f] = *(const bf16x8_t*)(Pw + f * G::KSTEP + 8 * q4);
+        } else {
+          r.t[pl][f] = Tw[f * G::KSTEP + q4];
+          r.p[pl][f] = Pw[f * G::KSTEP + q4];
+        }
+      }
+    }
   }
   const float* gw = (const float*)(wsb + 2 * kWsPlane);
-  r.g = gw[tid & (CH - 1)];
-  r.glast = gw[CH - 1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 16 * w + 4 * q4 + j;  // accumulator row of element j
+    r.v[j] = Vg[((size_t)(t0 + min(i, len - 1)) * H + h) * DK + e0 + c16];
+    r.g[j] = gw[i];
+  }
+  r.gl = gw[CH - 1];
 }
 
 // ---------------------------------------------------------------------------
@@ -351,21 +384,18 @@ template <bool BF16, int DK>
 __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
   using G = GT<BF16>;
   using E = typename G::E;
+  using F = typename G::F;
+  using R = ChunkRegs<BF16, DK>;
   constexpr int DV = DK;
   constexpr int NS = DV / VSL;       // slices per head
-  constexpr int LDK = DK + G::PAD;   // K, Q tiles
-  constexpr int LDT = CH + G::PAD;   // T'', P tiles
+  constexpr int LDK = DK + G::PAD;   // K tile
   constexpr int LDSS = DK + G::PAD;  // state slice
   constexpr int LDR = CH + G::PAD;   // transposed R, U, U'
   constexpr int NDB = DK / 16;       // 16-col d blocks of the state slice
   constexpr int DBW = (NDB + 3) / 4; // d blocks per wave
   constexpr bool SPLIT = BF16;
+  constexpr int CPR = DK / G::EPC;
   __shared__ __attribute__((aligned(16))) E Ks[CH * LDK];
-  __shared__ __attribute__((aligned(16))) E Qs[CH * LDK];
-  __shared__ __attribute__((aligned(16))) E Th[CH * LDT];
-  __shared__ __attribute__((aligned(16))) E Tl[SPLIT ? CH * LDT : 8];
-  __shared__ __attribute__((aligned(16))) E Ph[CH * LDT];
-  __shared__ __attribute__((aligned(16))) E Pl[SPLIT ? CH * LDT : 8];
   __shared__ __attribute__((aligned(16))) E Sh[VSL * LDSS];
   __shared__ __attribute__((aligned(16))) E Sl[SPLIT ? VSL * LDSS : 8];
   __shared__ __attribute__((aligned(16))) E Rh[VSL * LDR];
@@ -374,8 +404,6 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
   __shared__ __attribute__((aligned(16))) E Ul[SPLIT ? VSL * LDR : 8];
   __shared__ __attribute__((aligned(16))) E U2h[VSL * LDR];
   __shared__ __attribute__((aligned(16))) E U2l[SPLIT ? VSL * LDR : 8];
-  __shared__ float Vs[CH * VSL];
-  __shared__ float gam[CH], rr[CH];
 
   const int level = args.level;
   if (level > blob[MH_MAXDEPTH]) return;
@@ -396,9 +424,19 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
   const E* __restrict__ Vg = (const E*)args.v;
   E* __restrict__ Og = (E*)args.o;
   const size_t SZ = (size_t)DV * DK;
+  const int kend = 16 * (w + 1);  // T'' and P are lower triangular
 
-  for (int item = blockIdx.x; item < nlev * H * NS; item += gridDim.x) {
-    const int sl = item % NS, h = (item / NS) % H, li = item / (NS * H);
+  // Work items: (segment, head, slice). Workgroups are dispatched round-robin
+  // over the 8 XCDs (workgroup id mod 8; the grid is a multiple of 8), so item
+  // i runs on XCD i mod 8. Heads are assigned so that all slices of one head
+  // run on the same XCD and share its L2 for the chunk operands (k, q, T'', P)
+  // they all read.
+  const int NH8 = (H + 7) / 8;
+  for (int item = blockIdx.x; item < nlev * NH8 * 8 * NS; item += gridDim.x) {
+    const int x = item & 7, j = item >> 3;
+    const int sl = j % NS, j2 = j / NS;
+    const int h = (j2 % NH8) * 8 + x, li = j2 / NH8;
+    if (h >= H) continue;
     // per-item metadata, uniform across the workgroup (scalar loads)
     const int s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + li]);
     const int e0 = sl * VSL;
@@ -437,9 +475,9 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
       }
     }
     // first chunk's loads go out together with the state loads
-    ScanRegs<BF16, DK> rg;
-    scan_load<BF16, DK>(rg, Kg, Qg, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h,
-                        e0, tid);
+    R nx;
+    chunk_load<BF16, DK>(nx, Kg, Qg, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h, e0,
+                         tid);
     if (dst) {
 #pragma unroll
       for (int bi = 0; bi < DBW; ++bi) {
@@ -450,12 +488,32 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
       }
     }
 
+    // output rows of the previous chunk, stored one iteration late (after the
+    // next chunk's loads are issued)
+    float oval[4] = {0.f, 0.f, 0.f, 0.f};
+    int orow0 = 0, olen = 0;
+    auto flush_o = [&]() {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * q4 + r;
+        if (i < olen) {
+          E* d = Og + ((size_t)(orow0 + i) * H + h) * DV + e0 + c16;
+          if constexpr (BF16) *d = bf16_bits(oval[r]); else *d = oval[r];
+        }
+      }
+    };
+
     for (int ci = 0; ci < nck; ++ci) {
       const int c = cb + ci;
       const int t0 = st + CH * ci, len = min(CH, L - CH * ci);
+      R cur = nx;  // this chunk's operands
 
-      __syncthreads();  // previous chunk done with every LDS tile
-      // state slice and the prefetched chunk -> LDS operands
+      __syncthreads();  // previous chunk done with Ks, Sh/Sl and the exchange tiles
+#pragma unroll
+      for (int i = 0; i < R::KL; ++i) {
+        const int task = tid + 256 * i, row = task / CPR, ch = task % CPR;
+        *(u32x4_t*)(Ks + row * LDK + ch * G::EPC) = cur.k[i];
+      }
 #pragma unroll
       for (int bi = 0; bi < DBW; ++bi) {
         const int db = w * DBW + bi;
@@ -463,132 +521,109 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
 #pragma unroll
           for (int r = 0; r < 4; ++r) put_split<BF16>(Sh, Sl, (4 * q4 + r) * LDSS + 16 * db + c16, Sreg[bi][r]);
       }
-      {
-        using R = ScanRegs<BF16, DK>;
-        constexpr int CPR = DK / G::EPC;
-        const u32x4_t z4 = {0u, 0u, 0u, 0u};
+      float gam[4], rr[4];
 #pragma unroll
-        for (int i = 0; i < R::KL; ++i) {
-          const int task = tid + 256 * i, row = task / CPR, ch = task % CPR;
-          *(u32x4_t*)(Ks + row * LDK + ch * G::EPC) = row < len ? rg.k[i] : z4;
-          *(u32x4_t*)(Qs + row * LDK + ch * G::EPC) = row < len ? rg.q[i] : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < R::WL; ++i) {
-          const int cidx = tid + 256 * i;  // 16-byte chunk of a 16 KB operand region
-          if constexpr (SPLIT) {
-            const int plane = cidx / (CH * CH / 8), rem = cidx % (CH * CH / 8);
-            const int dofs = (rem / 8) * LDT + (rem % 8) * 8;
-            *(u32x4_t*)((plane ? Tl : Th) + dofs) = rg.t[i];
-            *(u32x4_t*)((plane ? Pl : Ph) + dofs) = rg.p[i];
-          } else {
-            const int dofs = (cidx / 16) * LDT + (cidx % 16) * 4;
-            *(u32x4_t*)(Th + dofs) = rg.t[i];
-            *(u32x4_t*)(Ph + dofs) = rg.p[i];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < R::VL; ++i) {
-          const int idx = tid + 256 * i;
-          float x;
-          if constexpr (BF16) x = bf16_val(rg.v[i]); else x = rg.v[i];
-          Vs[idx] = idx / VSL < len ? x : 0.f;
-        }
-        if (tid < CH) {
-          gam[tid] = __expf(rg.g);
-          rr[tid] = __expf(rg.glast - rg.g);
-        }
+      for (int r = 0; r < 4; ++r) {
+        gam[r] = __expf(cur.g[r]);
+        rr[r] = __expf(cur.gl - cur.g[r]);
       }
+      const float gC = __expf(cur.gl);
       __syncthreads();
+      // next chunk's loads first, then the previous chunk's output stores: a
+      // load issued after a possibly aliasing store waits for that store, so
+      // stores go out a whole chunk ahead of the next loads
       if (ci + 1 < nck)
-        scan_load<BF16, DK>(rg, Kg, Qg, Vg, args.ws + ((size_t)(c + 1) * H + h) * kWsChunk, t0 + CH,
-                            min(CH, L - CH * (ci + 1)), H, h, e0, tid);
+        chunk_load<BF16, DK>(nx, Kg, Qg, Vg, args.ws + ((size_t)(c + 1) * H + h) * kWsChunk, t0 + CH,
+                             min(CH, L - CH * (ci + 1)), H, h, e0, tid);
+      flush_o();
 
-      // (1) X = K S^T, Y = Q S^T   (rows 16w.., cols e)
+      // (1) X = K S^T, Y = Q S^T   (rows 16w.., cols e); separate hi/lo chains
       f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t X2 = {0.f, 0.f, 0.f, 0.f}, Y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += G::KSTEP) {
-        const typename G::F aK = ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4);
-        const typename G::F aQ = ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4);
-        const typename G::F bh = ld_rowk<BF16>(Sh, LDSS, c16, k0, q4);
+      for (int f = 0; f < R::NQ; ++f) {
+        const int k0 = f * G::KSTEP;
+        const F aK = ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4);
+        const F bh = ld_rowk<BF16>(Sh, LDSS, c16, k0, q4);
         X = mma<BF16>(aK, bh, X);
-        Y = mma<BF16>(aQ, bh, Y);
+        Y = mma<BF16>(cur.q[f], bh, Y);
         if constexpr (SPLIT) {
-          const typename G::F bl = ld_rowk<BF16>(Sl, LDSS, c16, k0, q4);
-          X = mma<BF16>(aK, bl, X);
-          Y = mma<BF16>(aQ, bl, Y);
+          const F bl = ld_rowk<BF16>(Sl, LDSS, c16, k0, q4);
+          X2 = mma<BF16>(aK, bl, X2);
+          Y2 = mma<BF16>(cur.q[f], bl, Y2);
         }
       }
       // (2) R = V - gamma * X  -> R^T
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * q4 + r;
-        const float R = Vs[i * VSL + c16] - gam[i] * X[r];
-        put_split<BF16>(Rh, Rl, c16 * LDR + i, R);
+        float vv;
+        if constexpr (BF16) vv = __uint_as_float(cur.v[r] << 16); else vv = cur.v[r];
+        put_split<BF16>(Rh, Rl, c16 * LDR + i, vv - gam[r] * (X[r] + X2[r]));
       }
       __syncthreads();
 
       // (3) U = T'' R  (T'' lower triangular: k < 16(w+1))
-      const int kend = 16 * (w + 1);
-      f32x4_t Uacc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < kend; k0 += G::KSTEP) {
-        const typename G::F ah = ld_rowk<BF16>(Th, LDT, 16 * w + c16, k0, q4);
-        const typename G::F bh = ld_rowk<BF16>(Rh, LDR, c16, k0, q4);
-        Uacc = mma<BF16>(ah, bh, Uacc);
-        if constexpr (SPLIT) {
-          Uacc = mma<BF16>(ah, ld_rowk<BF16>(Rl, LDR, c16, k0, q4), Uacc);
-          Uacc = mma<BF16>(ld_rowk<BF16>(Tl, LDT, 16 * w + c16, k0, q4), bh, Uacc);
+      f32x4_t Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < R::NT; ++f) {
+        const int k0 = f * G::KSTEP;
+        if (k0 < kend) {
+          const F bh = ld_rowk<BF16>(Rh, LDR, c16, k0, q4);
+          Ua = mma<BF16>(cur.t[0][f], bh, Ua);
+          if constexpr (SPLIT) {
+            Ub = mma<BF16>(cur.t[0][f], ld_rowk<BF16>(Rl, LDR, c16, k0, q4), Ub);
+            Ub = mma<BF16>(cur.t[SPLIT ? 1 : 0][f], bh, Ub);
+          }
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * q4 + r;
-        put_split<BF16>(Uh, Ul, c16 * LDR + i, Uacc[r]);
-        put_split<BF16>(U2h, U2l, c16 * LDR + i, Uacc[r] * rr[i]);
+        const float u = Ua[r] + Ub[r];
+        put_split<BF16>(Uh, Ul, c16 * LDR + i, u);
+        put_split<BF16>(U2h, U2l, c16 * LDR + i, u * rr[r]);
       }
       __syncthreads();
 
-      // (4) O = gamma * Y + P U
+      // (4) O = scale * (gamma * Y + P U), stored at the next iteration
       {
-        f32x4_t Z = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < kend; k0 += G::KSTEP) {
-          const typename G::F ah = ld_rowk<BF16>(Ph, LDT, 16 * w + c16, k0, q4);
-          const typename G::F bh = ld_rowk<BF16>(Uh, LDR, c16, k0, q4);
-          Z = mma<BF16>(ah, bh, Z);
-          if constexpr (SPLIT) {
-            Z = mma<BF16>(ah, ld_rowk<BF16>(Ul, LDR, c16, k0, q4), Z);
-            Z = mma<BF16>(ld_rowk<BF16>(Pl, LDT, 16 * w + c16, k0, q4), bh, Z);
+        f32x4_t Za = {0.f, 0.f, 0.f, 0.f}, Zb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < R::NT; ++f) {
+          const int k0 = f * G::KSTEP;
+          if (k0 < kend) {
+            const F bh = ld_rowk<BF16>(Uh, LDR, c16, k0, q4);
+            Za = mma<BF16>(cur.p[0][f], bh, Za);
+            if constexpr (SPLIT) {
+              Zb = mma<BF16>(cur.p[0][f], ld_rowk<BF16>(Ul, LDR, c16, k0, q4), Zb);
+              Zb = mma<BF16>(cur.p[SPLIT ? 1 : 0][f], bh, Zb);
+            }
           }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * w + 4 * q4 + r;
-          if (i < len) {
-            const float val = args.scale * (gam[i] * Y[r] + Z[r]);
-            E* dst = Og + ((size_t)(t0 + i) * H + h) * DV + e0 + c16;
-            if constexpr (BF16) *dst = bf16_bits(val); else *dst = val;
-          }
-        }
+        for (int r = 0; r < 4; ++r) oval[r] = args.scale * (gam[r] * (Y[r] + Y2[r]) + Za[r] + Zb[r]);
+        orow0 = t0;
+        olen = len;
       }
       // (5) S = gamma_C S + U'^T K
-      {
-        const float gC = gam[CH - 1];
 #pragma unroll
-        for (int bi = 0; bi < DBW; ++bi) {
-          const int db = w * DBW + bi;
-          if (db < NDB) {
-            f32x4_t acc = Sreg[bi] * gC;
+      for (int bi = 0; bi < DBW; ++bi) {
+        const int db = w * DBW + bi;
+        if (db < NDB) {
+          f32x4_t acc = Sreg[bi] * gC;
+          f32x4_t acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k0 = 0; k0 < CH; k0 += G::KSTEP) {
-              const typename G::F bk = ld_kcol<BF16>(Ks, LDK, 16 * db + c16, k0, q4);
-              acc = mma<BF16>(ld_rowk<BF16>(U2h, LDR, c16, k0, q4), bk, acc);
-              if constexpr (SPLIT) acc = mma<BF16>(ld_rowk<BF16>(U2l, LDR, c16, k0, q4), bk, acc);
-            }
-            Sreg[bi] = acc;
+          for (int k0 = 0; k0 < CH; k0 += G::KSTEP) {
+            const F bk = ld_kcol<BF16>(Ks, LDK, 16 * db + c16, k0, q4);
+            acc = mma<BF16>(ld_rowk<BF16>(U2h, LDR, c16, k0, q4), bk, acc);
+            if constexpr (SPLIT) acc2 = mma<BF16>(ld_rowk<BF16>(U2l, LDR, c16, k0, q4), bk, acc2);
           }
+          Sreg[bi] = acc + acc2;
         }
       }
     }
+    flush_o();
 
     // ---- end state: seg_final_state and the first child's start slot (the fork)
     {
@@ -625,7 +660,7 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   // Under capture, every depth up to the capacity is recorded; depths beyond
   // the current tree exit at once.
   const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
-  const int sgrid = 2 * cus;
+  const int sgrid = (2 * cus + 7) / 8 * 8;  // a multiple of 8: item i runs on XCD i mod 8
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
     hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(256), 0, stream, a.blob, a);

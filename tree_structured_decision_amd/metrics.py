@@ -1,7 +1,7 @@
 """Host-side evaluation of layer outputs: per-option scores, total-variation
 distance and decision agreement.
 
-Fidelity is judged by the total-variation distance (half the L1 distance) of
+Fidelity is measured by the total-variation distance (half the L1 distance) of
 output probabilities to a float32 reference (Flide, kongchang.com page,
 section "Performance"), and by whether accelerated runs keep the same
 decisions (openai-hub.com page, section on accuracy and calibration).
