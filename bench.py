@@ -118,6 +118,7 @@ class Runner:
             t_cap, s_cap, depth_cap = T, S, depth
         self.caps = (t_cap, s_cap, depth_cap)
         self.sess = ForkSession(t_cap, s_cap, depth_cap, wl_meta["H"] // wl_meta["Hkv"],
+                                kv_heads=wl_meta["Hkv"], D=wl_meta["D"],
                                 gH=wl_meta["gH"], dk=wl_meta["dk"], dv=wl_meta["dv"])
         dev = "cuda"
         qd = tensors["q"].dtype

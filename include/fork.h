@@ -62,6 +62,9 @@ typedef struct fork_caps {
   int32_t s_cap;      /* max segments */
   int32_t depth_cap;  /* max segment depth (a root has depth 0) */
   int32_t gqa_group;  /* H / Hkv of the attention layers served; 1..128 */
+  int32_t kv_heads;   /* Hkv of those layers, or 0. When given, query tiles with long
+                         key ranges are split into parts (merged by log-sum-exp) so a
+                         small tree still fills the GPU; see fork_attn_workspace. */
 } fork_caps;
 
 /* Host descriptor of a built metadata blob. The arrays live in `dev`. */
@@ -73,7 +76,7 @@ typedef struct fork_meta {
   int32_t num_attn_tiles;  /* query tiles of the attention work list */
   int32_t num_chunks;      /* Gated DeltaNet chunks (never crossing a segment) */
   int32_t tile_tokens;     /* tokens per attention query tile */
-  int32_t reserved;
+  int32_t num_attn_merges; /* query tiles split into key-range parts */
   fork_caps caps;
   void* dev;               /* caller-owned device blob, >= fork_meta_size bytes */
   size_t dev_bytes;
@@ -139,8 +142,10 @@ fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream
  * with scale <= 0 meaning 1/sqrt(D). Each prefix key/value tile is staged in
  * LDS once per query tile and reused by every packed query row (GQA heads x
  * tokens of sibling segments). Supported: D in {64, 128}; H / Hkv must equal
- * the gqa_group the metadata was built for. The workspace may be null when
- * fork_attn_workspace reports 0 bytes.
+ * the gqa_group the metadata was built for, and Hkv its kv_heads when that is
+ * nonzero. The workspace holds fp32 partial results of split query tiles
+ * (kv_heads != 0): fork_attn_workspace gives its size for the blob's
+ * capacities; it may be null when that size is 0.
  */
 fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int32_t D,
                                 fork_dtype dt, size_t* bytes_h);

@@ -21,12 +21,13 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_hip(wl, *, attn=True, gdn=True, sess=None, final=True, device="cuda"):
-    """Run the requested layers on the GPU; returns numpy float64 outputs."""
+def run_hip(wl, *, attn=True, gdn=True, sess=None, final=True, device="cuda", split=True):
+    """Run the requested layers on the GPU; returns numpy float64 outputs.
+    split: plan split query tiles (kv_heads given) or not."""
     own = sess is None
     if own:
-        caps = caps_for(wl.parent, wl.seg_len, wl.H // wl.Hkv)
-        sess = ForkSession(**caps, gH=wl.gH, dk=wl.dk, dv=wl.dv, device=device)
+        caps = caps_for(wl.parent, wl.seg_len, wl.H // wl.Hkv, kv_heads=wl.Hkv if split else 0)
+        sess = ForkSession(**caps, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv, device=device)
     d = to_device(wl, device)
     sess.build(wl.parent, wl.seg_len)
     out = {}

@@ -53,7 +53,7 @@ def np64(x, n):
 
 
 def test_graph_replay_matches_eager_and_oracle():
-    sess = ForkSession(T_CAP, S_CAP, DEPTH_CAP, H // HKV, gH=GH, dk=DK, dv=DK)
+    sess = ForkSession(T_CAP, S_CAP, DEPTH_CAP, H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
     t, out = bucket_tensors()
     wa = make_tree_wl(1, 3)
     assert wa.T <= T_CAP and wa.S <= S_CAP

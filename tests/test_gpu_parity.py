@@ -203,3 +203,16 @@ def test_determinism_bitwise():
     b = run_hip(wl)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_split_and_whole_tiles_agree():
+    """Split query tiles (key-range parts merged by log-sum-exp) and whole tiles
+    give the same attention within tolerance; both match the oracle."""
+    wl = W.one_request()
+    a = run_hip(wl, gdn=False, split=True)
+    b = run_hip(wl, gdn=False, split=False)
+    o, lse = oracle_attn(wl)
+    check_close("split attn.o", a["o"], o, wl.dtype)
+    check_close("whole attn.o", b["o"], o, wl.dtype)
+    check_close("split attn.lse", a["lse"], lse, wl.dtype, kind="f32")
+    check_close("whole attn.lse", b["lse"], lse, wl.dtype, kind="f32")

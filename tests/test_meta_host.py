@@ -19,7 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS", "GQA",
            "OFF_PARENT", "OFF_SEGLEN", "OFF_SEGSTART", "OFF_DEPTH", "OFF_ROOT", "OFF_ROOTORD",
            "OFF_ANCLEN", "OFF_FIRSTCHILD", "OFF_CHUNKBASE", "OFF_LEVELOFF", "OFF_LEVELSEG",
-           "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS"]
+           "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
+           "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
 
 
@@ -40,10 +41,10 @@ def test_exports_every_declared_symbol():
     assert B.fork_version().startswith("forkattn")
 
 
-def plan(parent, seg_len, gqa=8, t_cap=None, s_cap=None, depth_cap=8):
+def plan(parent, seg_len, gqa=8, t_cap=None, s_cap=None, depth_cap=8, kv_heads=0):
     parent = np.asarray(parent, np.int32)
     seg_len = np.asarray(seg_len, np.int32)
-    caps = B.make_caps(t_cap or int(seg_len.sum()), s_cap or len(parent), depth_cap, gqa)
+    caps = B.make_caps(t_cap or int(seg_len.sum()), s_cap or len(parent), depth_cap, gqa, kv_heads)
     _, stg = B.fork_meta_size(caps)
     staging = np.zeros(stg // 4, np.int32)
     meta, up = B.fork_meta_plan(parent, seg_len, caps, staging)
@@ -55,10 +56,10 @@ def arr(w, name, n):
     return w[off:off + n]
 
 
-def check_plan(parent, seg_len, gqa):
+def check_plan(parent, seg_len, gqa, kv_heads=0):
     parent = np.asarray(parent, np.int32)
     seg_len = np.asarray(seg_len, np.int32)
-    meta, w, up = plan(parent, seg_len, gqa)
+    meta, w, up = plan(parent, seg_len, gqa, kv_heads=kv_heads)
     S, T = len(parent), int(seg_len.sum())
     assert w[HI["MAGIC"]] == 0x464B4D31
     assert (w[HI["T"]], w[HI["S"]]) == (T, S) == (meta.num_tokens, meta.num_segments)
@@ -98,31 +99,59 @@ def check_plan(parent, seg_len, gqa):
         want = [(ref["seg_start"][s] + 64 * i, min(64, seg_len[s] - 64 * i)) for i in range(n)]
         np.testing.assert_array_equal(got, np.array(want).reshape(-1, 2))
     assert nch == sum(-(-int(L) // 64) for L in seg_len)
-    # tiles: every token in exactly one tile; tile tokens share one parent
+    # tiles: every token in exactly one query tile; tile tokens share one parent;
+    # the entries of a tile cover its key-tile sequence [0, ktiles) exactly
     TT = w[HI["TILE_TOKENS"]]
     assert TT == max(1, 128 // gqa)
     nt = w[HI["NTILES"]]
-    tiles = arr(w, "TILES", 4 * nt).reshape(-1, 4)
-    cover = np.zeros(T, np.int32)
+    ent = arr(w, "TILES", 8 * nt).reshape(-1, 8)
     tok_seg = ref["tok_seg"]
     st = ref["seg_start"]
-    anc_total = ref["anc_len"]
-    costs = []
-    for t0, t1, own_lo, info in tiles:
+    anc_kt = np.zeros(S, np.int64)
+    for s_ in range(S):
+        if parent[s_] >= 0:
+            anc_kt[s_] = anc_kt[parent[s_]] + -(-int(seg_len[parent[s_]]) // 64)
+    parts = {}
+    for t0, t1, own_lo, info, kt0, kt1, slot, _ in ent:
+        parts.setdefault((t0, t1), []).append((kt0, kt1, slot))
+    cover = np.zeros(T, np.int32)
+    used_slots = []
+    for (t0, t1), lst in parts.items():
         assert 0 <= t0 < t1 <= T and t1 - t0 <= TT
         cover[t0:t1] += 1
         segs = np.unique(tok_seg[t0:t1])
         assert len(set(parent[segs].tolist())) == 1
         if len(segs) > 1:
             assert np.all(parent[segs] >= 0) and np.all(seg_len[segs] < TT)
+        kt = anc_kt[segs[0]] + -(-(t1 - st[tok_seg[t0]]) // 64)
+        lst.sort()
+        assert lst[0][0] == 0 and lst[-1][1] == kt
+        for a_, b_ in zip(lst, lst[1:]):
+            assert a_[1] == b_[0]
+        if len(lst) == 1:
+            assert lst[0][2] == -1
+        else:
+            used_slots += [x[2] for x in lst]
+    for t0, t1, own_lo, info, kt0, kt1, slot, _ in ent:
+        segs = np.unique(tok_seg[t0:t1])
         assert own_lo == st[tok_seg[t0]]
         assert (info & ((1 << 30) - 1)) == parent[segs[0]] + 1
         assert bool(info & (1 << 30)) == (len(segs) > 1)
-        costs.append((anc_total[segs[0]] + t1 - own_lo) // 64)
     np.testing.assert_array_equal(cover, 1)
-    assert np.all(np.diff(costs) <= 0), "tiles must be ordered most expensive first"
-
-
+    costs = ent[:, 5] - ent[:, 4]
+    assert np.all(np.diff(costs) <= 0), "work entries must be ordered most expensive first"
+    # merge groups: consecutive partial slots, one group per split tile
+    nm = w[HI["NMERGE"]]
+    assert meta.num_attn_merges == nm
+    mg = arr(w, "MERGE", 4 * nm).reshape(-1, 4)
+    assert sorted(used_slots) == list(range(len(used_slots))) == list(range(w[HI["NPARTS"]]))
+    for t0, t1, npart, slot0 in mg:
+        lst = parts[(t0, t1)]
+        assert len(lst) == npart and sorted(x[2] for x in lst) == list(range(slot0, slot0 + npart))
+    assert w[HI["NPARTS"]] * max(kv_heads, 1) <= 2048
+    if kv_heads == 0:
+        assert nm == 0
+    return nm
 @pytest.mark.parametrize("name", ["tiny_one_level", "one_request", "wide_options",
                                   "agent_history"])
 def test_plan_workload_trees(name):
@@ -134,12 +163,26 @@ def test_plan_workload_trees(name):
     parent, seg_len = wl_tree()
     for gqa in (1, 2, 8, 16):
         check_plan(parent, seg_len, gqa)
+        check_plan(parent, seg_len, gqa, kv_heads=2)
+
+
+def test_plan_splits_long_tiles_of_a_small_tree():
+    """The one-request tree has too few query tiles for the GPU: long ones are
+    split into key-range parts when kv_heads is given."""
+    rng = np.random.default_rng(0)
+    parent, seg_len = W.tree_one_level(2048, rng.integers(16, 49, 16))
+    assert check_plan(parent, seg_len, 8, kv_heads=2) > 0
+    assert check_plan(parent, seg_len, 8, kv_heads=0) == 0
+    # a large tree needs no splitting
+    parent, seg_len = W.tree_one_level(8192, [8] * 256)
+    assert check_plan(parent, seg_len, 8, kv_heads=4) == 0
 
 
 def test_plan_request_mix_tree():
     rng = np.random.Generator(np.random.PCG64(1005))
     parent, seg_len = W.request_mix_tree(rng)
     check_plan(parent, seg_len, 8)
+    check_plan(parent, seg_len, 8, kv_heads=2)
 
 
 def test_plan_random_trees():
@@ -147,7 +190,8 @@ def test_plan_random_trees():
     for _ in range(60):
         parent, seg_len = W.random_tree(rng, int(rng.integers(1, 30)), int(rng.integers(1, 90)),
                                         max_depth=5, roots=int(rng.integers(1, 4)))
-        check_plan(parent, seg_len, int(rng.choice([1, 2, 3, 8, 16, 128])))
+        check_plan(parent, seg_len, int(rng.choice([1, 2, 3, 8, 16, 128])),
+                   kv_heads=int(rng.choice([0, 1, 2, 8])))
 
 
 def _status(fn):

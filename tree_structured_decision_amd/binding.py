@@ -35,14 +35,15 @@ class ForkError(RuntimeError):
 
 class fork_caps(ctypes.Structure):
     _fields_ = [("t_cap", ctypes.c_int32), ("s_cap", ctypes.c_int32),
-                ("depth_cap", ctypes.c_int32), ("gqa_group", ctypes.c_int32)]
+                ("depth_cap", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32)]
 
 
 class fork_meta(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("num_roots", ctypes.c_int32), ("max_depth", ctypes.c_int32),
                 ("num_attn_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
-                ("tile_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("num_attn_merges", ctypes.c_int32),
                 ("caps", fork_caps), ("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_size_t)]
 
 
@@ -145,8 +146,8 @@ def fork_version() -> str:
     return lib().fork_version().decode()
 
 
-def make_caps(t_cap: int, s_cap: int, depth_cap: int, gqa_group: int) -> fork_caps:
-    return fork_caps(int(t_cap), int(s_cap), int(depth_cap), int(gqa_group))
+def make_caps(t_cap: int, s_cap: int, depth_cap: int, gqa_group: int, kv_heads: int = 0) -> fork_caps:
+    return fork_caps(int(t_cap), int(s_cap), int(depth_cap), int(gqa_group), int(kv_heads))
 
 
 def fork_meta_size(caps: fork_caps):

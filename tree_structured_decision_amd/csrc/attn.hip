@@ -21,6 +21,7 @@
 // registers, so the online-softmax row max needs one cross-lane step and the
 // row sum none until the end. V is written transposed into LDS so that the
 // A operand of O^T = V^T P^T reads contiguous keys.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -31,6 +32,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 template <bool BF16, int D>
 struct AttnCfg {
@@ -38,7 +41,11 @@ struct AttnCfg {
   static constexpr int EPC = 16 / ESZ;                 // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                  // chunks per K/V row
   static constexpr int KS = D + EPC;                   // Ks row stride (elements)
-  static constexpr int VS = kAttnKeys + (BF16 ? 8 : 4);  // Vt row stride (elements)
+  // bf16: V is staged row-major [key][d] with a 288-byte pitch (4 consecutive
+  // key rows then fall on distinct LDS banks for the transposing reads);
+  // fp32: V is staged transposed [d][key].
+  static constexpr int VS = BF16 ? D + 16 : kAttnKeys + 4;
+  static constexpr int VROWS = BF16 ? kAttnKeys : D;  // rows of the V tile in LDS
   static constexpr int NKF = BF16 ? D / 16 : D / 2;    // MFMA k-steps over D
   static constexpr int NDB = D / 32;                   // 32-row d blocks of O^T
 };
@@ -50,6 +57,7 @@ struct AttnArgs {
   const void* v;
   void* o;
   float* lse;
+  float* ws;  // partial results of split tiles: [slot][kv head] x (128 rows x D outputs, 128 lse)
   int H, Hkv, G;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -96,7 +104,8 @@ __device__ __forceinline__ void kv_load(KVRegs<BF16, D>& r, const E* __restrict_
   }
 }
 
-// LDS stores of a loaded tile: K row-major into Ks, V transposed into Vt.
+// LDS stores of a loaded tile: K row-major into Ks; V row-major (bf16) or
+// transposed (fp32) into Vt.
 template <bool BF16, int D, typename E>
 __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict__ Ks,
                                          E* __restrict__ Vt, int tid) {
@@ -115,16 +124,9 @@ __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict
       const int kq = task / C::CPR, ch = task % C::CPR;
       const u32x4_t* x = r.v[i2];
       if constexpr (BF16) {
+        // row-major, like K: 4 key rows of one 16-byte chunk each
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w = i >> 1, sh = (i & 1) * 16;
-          const unsigned e0 = (x[0][w] >> sh) & 0xffffu, e1 = (x[1][w] >> sh) & 0xffffu;
-          const unsigned e2 = (x[2][w] >> sh) & 0xffffu, e3 = (x[3][w] >> sh) & 0xffffu;
-          uint2 pk;
-          pk.x = e0 | (e1 << 16);
-          pk.y = e2 | (e3 << 16);
-          *(uint2*)(Vt + (ch * 8 + i) * C::VS + 4 * kq) = pk;
-        }
+        for (int jj = 0; jj < 4; ++jj) *(u32x4_t*)(Vt + (4 * kq + jj) * C::VS + ch * 8) = x[jj];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -140,26 +142,41 @@ __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict
   }
 }
 
-// Walks the key tiles of a query tile: every ancestor segment's range (fully
-// visible), nearest ancestor first, then the tile's own range (tree-masked).
+// Walks the key tiles of a work entry: the query tile's key-tile sequence is
+// every ancestor segment's range (fully visible), nearest ancestor first, then
+// the tile's own range (tree-masked), 64 keys per tile; the entry covers tiles
+// [kt0, kt1) of it.
 struct TileIter {
-  int a, j0, hi;
+  int a, j0, hi, left;
   bool own, done;
 };
 
 __device__ __forceinline__ void iter_init(TileIter& it, const AttnTile& tile,
+                                          const int32_t* __restrict__ parent,
                                           const int32_t* __restrict__ seg_start,
                                           const int32_t* __restrict__ seg_len) {
+  int skip = tile.kt0;
+  it.left = tile.kt1 - tile.kt0;
+  it.done = it.left <= 0;
   it.a = (tile.info & kTileAncMask) - 1;
-  it.done = false;
-  if (it.a >= 0) {
-    it.own = false;
-    it.j0 = seg_start[it.a];
-    it.hi = it.j0 + seg_len[it.a];
-  } else {
-    it.own = true;
-    it.j0 = tile.own_lo;
-    it.hi = tile.t1;
+  for (;;) {
+    if (it.a >= 0) {
+      const int lo = seg_start[it.a], len = seg_len[it.a];
+      const int n = (len + kAttnKeys - 1) / kAttnKeys;
+      if (skip < n) {
+        it.own = false;
+        it.j0 = lo + kAttnKeys * skip;
+        it.hi = lo + len;
+        return;
+      }
+      skip -= n;
+      it.a = parent[it.a];
+    } else {
+      it.own = true;
+      it.j0 = tile.own_lo + kAttnKeys * skip;
+      it.hi = tile.t1;
+      return;
+    }
   }
 }
 
@@ -167,6 +184,10 @@ __device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
                                           const int32_t* __restrict__ parent,
                                           const int32_t* __restrict__ seg_start,
                                           const int32_t* __restrict__ seg_len) {
+  if (--it.left <= 0) {
+    it.done = true;
+    return;
+  }
   it.j0 += kAttnKeys;
   if (it.j0 < it.hi) return;
   if (!it.own) {
@@ -193,7 +214,7 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
   using E = typename std::conditional<BF16, unsigned short, float>::type;
   using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
   __shared__ __attribute__((aligned(16))) E Ks[kAttnKeys * C::KS];
-  __shared__ __attribute__((aligned(16))) E Vt[D * C::VS];
+  __shared__ __attribute__((aligned(16))) E Vt[C::VROWS * C::VS];
 
   const int ntiles = blob[MH_NTILES];
   const int TT = blob[MH_TILE_TOKENS];
@@ -219,6 +240,9 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
     tile.t1 = __builtin_amdgcn_readfirstlane(tiles[ti].t1);
     tile.own_lo = __builtin_amdgcn_readfirstlane(tiles[ti].own_lo);
     tile.info = __builtin_amdgcn_readfirstlane(tiles[ti].info);
+    tile.kt0 = __builtin_amdgcn_readfirstlane(tiles[ti].kt0);
+    tile.kt1 = __builtin_amdgcn_readfirstlane(tiles[ti].kt1);
+    tile.slot = __builtin_amdgcn_readfirstlane(tiles[ti].slot);
 
     // this lane's query row (rows past the tile are clamped and not stored)
     const int r = wave * 32 + l32;
@@ -325,17 +349,22 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
             bf16x8_t pb;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) pb[jj] = (__bf16)s[b][8 * hf + jj];
+            // A = V^T fragments by transposing LDS reads: within each group of
+            // 16 lanes, lane L points at key row (L / 4) of a 4-key block and
+            // d column 4 (L % 4); lane i of the group receives the 4 keys at
+            // d = d0 + i. Two reads give keys {+0..3} and {+8..11}, matching
+            // the key order of the P^T fragment.
+            const int g16 = lane >> 4, L16 = lane & 15;
+            const int krow = 32 * b + 16 * hf + 4 * hi + (L16 >> 2);
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-              const E* vrow = Vt + (32 * db + l32) * C::VS + 32 * b + 16 * hf + 4 * hi;
-              const uint2 x0 = *(const uint2*)vrow;
-              const uint2 x1 = *(const uint2*)(vrow + 8);
-              u32x4_t w;
-              w[0] = x0.x;
-              w[1] = x0.y;
-              w[2] = x1.x;
-              w[3] = x1.y;
-              const bf16x8_t va = __builtin_bit_cast(bf16x8_t, w);
+              const int col = 32 * db + 16 * (g16 & 1) + 4 * (L16 & 3);
+              const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + krow * C::VS + col));
+              const s16x4_t hi4 =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + (krow + 8) * C::VS + col));
+              typedef short s16x8_t __attribute__((ext_vector_type(8)));
+              const s16x8_t w8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+              const bf16x8_t va = __builtin_bit_cast(bf16x8_t, w8);
               oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
             }
           }
@@ -355,7 +384,7 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
 
     // software pipeline: tile i+1 is loaded into registers while tile i computes
     TileIter it;
-    iter_init(it, tile, seg_start, seg_len);
+    iter_init(it, tile, parent, seg_start, seg_len);
     KVRegs<BF16, D> rg;
     kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
     while (!it.done) {
@@ -369,10 +398,24 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
       kv_compute(j0, hi_, own);
     }
 
-    // finalize
+    // finalize: normalise; whole tiles store the output, parts of a split tile
+    // store fp32 partials (normalised rows + log-sum-exp) for the merge pass
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    if (valid) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_row = l_tot > 0.f ? m_run * 0.6931471805599453f + __logf(l_tot) : -INFINITY;
+    if (valid && tile.slot >= 0) {
+      float* part = args.ws + ((size_t)tile.slot * Hkv + g) * (kAttnRows * D + kAttnRows);
+      float* prow = part + r * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = 32 * db + 8 * rq + 4 * hi;
+          *(float4*)(prow + d0) = make_float4(oacc[db][4 * rq + 0] * inv, oacc[db][4 * rq + 1] * inv,
+                                              oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
+        }
+      if (hi == 0) part[kAttnRows * D + r] = lse_row;
+    } else if (valid) {
       E* orow = O + ((size_t)t_row * H + h) * D;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -396,22 +439,89 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
             *(float4*)(orow + d0) = make_float4(v0, v1, v2, v3);
           }
         }
-      if (args.lse && hi == 0) args.lse[(size_t)t_row * H + h] = m_run * 0.6931471805599453f + __logf(l_tot);
+      if (args.lse && hi == 0) args.lse[(size_t)t_row * H + h] = lse_row;
+    }
+  }
+}
+
+// Combines the parts of split query tiles: for each row,
+// o = sum_p exp(lse_p - lse) o_p with lse = log sum_p exp(lse_p).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
+  using E = typename std::conditional<BF16, unsigned short, float>::type;
+  const int nmerge = blob[MH_NMERGE];
+  const int TT = blob[MH_TILE_TOKENS];
+  const AttnMerge* __restrict__ merges = (const AttnMerge*)(blob + blob[MH_OFF_MERGE]);
+  const int H = args.H, Hkv = args.Hkv, G = args.G;
+  constexpr int PS = kAttnRows * D + kAttnRows;  // floats per partial slot
+  for (int item = blockIdx.x; item < nmerge * Hkv; item += gridDim.x) {
+    const int mi = item / Hkv, g = item - mi * Hkv;
+    const int t0 = merges[mi].t0, t1 = merges[mi].t1, np = merges[mi].nparts, s0 = merges[mi].slot0;
+    for (int task = threadIdx.x; task < kAttnRows * (D / 4); task += blockDim.x) {
+      const int r = task / (D / 4), c4 = task % (D / 4);
+      const int tl = r / G, hg = r - tl * G;
+      if (tl >= TT || t0 + tl >= t1) continue;
+      const int t = t0 + tl, h = g * G + hg;
+      float m = -INFINITY;
+      for (int p = 0; p < np; ++p) m = fmaxf(m, args.ws[((size_t)(s0 + p) * Hkv + g) * PS + kAttnRows * D + r]);
+      float den = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < np; ++p) {
+        const float* part = args.ws + ((size_t)(s0 + p) * Hkv + g) * PS;
+        const float lp = part[kAttnRows * D + r];
+        const float wgt = lp == -INFINITY ? 0.f : __expf(lp - m);
+        const float4 x = *(const float4*)(part + r * D + 4 * c4);
+        den += wgt;
+        acc.x += wgt * x.x;
+        acc.y += wgt * x.y;
+        acc.z += wgt * x.z;
+        acc.w += wgt * x.w;
+      }
+      const float inv = 1.f / den;
+      E* orow = (E*)args.o + ((size_t)t * H + h) * D + 4 * c4;
+      if constexpr (BF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        bf16x2_t p0, p1;
+        p0[0] = (__bf16)(acc.x * inv);
+        p0[1] = (__bf16)(acc.y * inv);
+        p1[0] = (__bf16)(acc.z * inv);
+        p1[1] = (__bf16)(acc.w * inv);
+        uint2 pk;
+        pk.x = __builtin_bit_cast(unsigned, p0);
+        pk.y = __builtin_bit_cast(unsigned, p1);
+        *(uint2*)orow = pk;
+      } else {
+        *(float4*)orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      }
+      if (args.lse && c4 == 0) args.lse[(size_t)t * H + h] = m + __logf(den);
     }
   }
 }
 
 template <bool BF16, int D>
-fork_status launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
+fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
+  // merge pass for split tiles: under capture whenever splitting is possible,
+  // otherwise only when this tree has split tiles
+  const bool cap = stream_capturing(stream);
+  if (m->caps.kv_heads > 0 && (cap || m->num_attn_merges > 0)) {
+    int mgrid = 2 * device_cu_count();
+    if (!cap) mgrid = std::min(mgrid, m->num_attn_merges * a.Hkv);
+    hipLaunchKernelGGL((fork_attn_merge_kernel<BF16, D>), dim3(mgrid), dim3(256), 0, stream, a.blob, a);
+    FORK_HIP_CHECK(hipGetLastError());
+  }
   return FORK_OK;
 }
 
 }  // namespace
 
+size_t attn_workspace_bytes(const fork_caps& c, int D) {
+  return c.kv_heads > 0 ? (size_t)kMaxPartSlots * (kAttnRows * (size_t)D + kAttnRows) * sizeof(float) : 0;
+}
+
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v, void* o,
-                             float* lse, int H, int Hkv, int D, float scale, fork_dtype dt,
+                             float* lse, int H, int Hkv, int D, float scale, fork_dtype dt, void* ws,
                              hipStream_t stream) {
   AttnArgs a;
   a.blob = (const int32_t*)m->dev;
@@ -420,6 +530,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.ws = (float*)ws;
   a.H = H;
   a.Hkv = Hkv;
   a.G = H / Hkv;
@@ -432,8 +543,9 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
     const long long items = (long long)m->num_attn_tiles * Hkv;
     if (items < grid) grid = (int)(items > 0 ? items : 1);
   }
-  if (dt == FORK_BF16) return D == 128 ? launch_one<true, 128>(a, grid, stream) : launch_one<true, 64>(a, grid, stream);
-  return D == 128 ? launch_one<false, 128>(a, grid, stream) : launch_one<false, 64>(a, grid, stream);
+  if (dt == FORK_BF16)
+    return D == 128 ? launch_one<true, 128>(m, a, grid, stream) : launch_one<true, 64>(m, a, grid, stream);
+  return D == 128 ? launch_one<false, 128>(m, a, grid, stream) : launch_one<false, 64>(m, a, grid, stream);
 }
 
 }  // namespace fork

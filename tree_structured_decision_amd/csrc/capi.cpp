@@ -62,6 +62,8 @@ static fork_status check_caps(const fork_caps* c) {
     return fail(FORK_E_ARG, "depth_cap %d out of range [0, %d]", c->depth_cap, kMaxDepthCap);
   if (c->gqa_group < 1 || c->gqa_group > kAttnRows)
     return fail(FORK_E_UNSUPPORTED, "gqa_group %d out of range [1, %d]", c->gqa_group, kAttnRows);
+  if (c->kv_heads < 0 || c->kv_heads > kMaxPartSlots)
+    return fail(FORK_E_ARG, "kv_heads %d out of range [0, %d]", c->kv_heads, kMaxPartSlots);
   return FORK_OK;
 }
 
@@ -144,11 +146,16 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   // Attention query tiles. Short non-root siblings that follow each other in
   // the stream share their ancestor keys, so they are packed into common
   // tiles: every staged ancestor key/value tile then serves all their rows.
+  // A tile's work is measured in 64-key tiles: its ancestors' (anc_kt) plus
+  // its own range's.
   const int32_t TT = L.tile_tokens;
+  std::vector<int64_t> anc_kt(S);
+  for (int32_t s = 0; s < S; ++s)
+    anc_kt[s] = parent[s] < 0 ? 0 : anc_kt[parent[s]] + (seg_len[parent[s]] + kAttnKeys - 1) / kAttnKeys;
   std::vector<AttnTile> tiles;
-  std::vector<int64_t> cost;
+  std::vector<int64_t> ktiles;
   tiles.reserve((size_t)(T / TT + S));
-  cost.reserve(tiles.capacity());
+  ktiles.reserve(tiles.capacity());
   auto packable = [&](int32_t s) { return parent[s] >= 0 && seg_len[s] < TT; };
   for (int32_t s = 0; s < S;) {
     int32_t e = s + 1;
@@ -166,26 +173,84 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
       tl.t1 = t1;
       tl.own_lo = start[seg_of_t0];
       tl.info = (parent[s] + 1) | (seg_last != seg_of_t0 ? kTileMulti : 0);
+      tl.kt0 = 0;
+      tl.kt1 = (int32_t)(anc_kt[s] + (t1 - tl.own_lo + kAttnKeys - 1) / kAttnKeys);
+      tl.slot = -1;
+      tl.pad = 0;
       tiles.push_back(tl);
-      cost.push_back((int64_t)anc[s] + (t1 - tl.own_lo));
+      ktiles.push_back(tl.kt1);
     }
     s = e;
   }
-  if ((int64_t)tiles.size() > L.tile_cap) return fail(FORK_E_CAPACITY, "tile list overflow");
-  // most expensive first (counting sort on 64-key units, stable)
-  std::vector<AttnTile> sorted(tiles.size());
+
+  // Split plan: when the tiles are too few to keep every resident workgroup
+  // busy, a tile whose key-tile count exceeds the fair share P of the total
+  // work is cut into parts of about P key tiles; each part writes a partial
+  // result (normalised output and log-sum-exp per row) that a merge pass
+  // combines. P doubles until the partial slots fit the workspace.
+  const int64_t Hkv = caps->kv_heads;
+  int64_t P = INT64_MAX;
+  auto nparts_of = [&](int64_t kt) -> int64_t {
+    return kt > P ? std::min<int64_t>(kMaxSplit, (kt + P - 1) / P) : 1;
+  };
+  if (Hkv > 0) {
+    int64_t W = 0;
+    for (int64_t kt : ktiles) W += kt * Hkv;
+    P = std::max<int64_t>(kMinPartTiles, (W + kAttnSlots - 1) / kAttnSlots);
+    for (;;) {
+      int64_t slots = 0, groups = 0;
+      for (int64_t kt : ktiles)
+        if (nparts_of(kt) > 1) {
+          slots += nparts_of(kt);
+          ++groups;
+        }
+      if (slots * Hkv <= kMaxPartSlots && groups <= L.merge_cap) break;
+      P *= 2;
+    }
+  }
+  std::vector<AttnTile> entries;
+  std::vector<int64_t> cost;
+  std::vector<AttnMerge> merges;
+  int32_t nslots = 0;
+  for (size_t i = 0; i < tiles.size(); ++i) {
+    const int64_t kt = ktiles[i], n = nparts_of(kt);
+    if (n == 1) {
+      entries.push_back(tiles[i]);
+      cost.push_back(kt);
+      continue;
+    }
+    AttnMerge mg;
+    mg.t0 = tiles[i].t0;
+    mg.t1 = tiles[i].t1;
+    mg.nparts = (int32_t)n;
+    mg.slot0 = nslots;
+    merges.push_back(mg);
+    for (int64_t p = 0; p < n; ++p) {
+      AttnTile e = tiles[i];
+      e.kt0 = (int32_t)(kt * p / n);
+      e.kt1 = (int32_t)(kt * (p + 1) / n);
+      e.slot = nslots + (int32_t)p;
+      entries.push_back(e);
+      cost.push_back(e.kt1 - e.kt0);
+    }
+    nslots += (int32_t)n;
+  }
+  if ((int64_t)entries.size() > L.tile_cap) return fail(FORK_E_CAPACITY, "tile list overflow");
+  // most expensive first (counting sort on key tiles, stable)
+  std::vector<AttnTile> sorted(entries.size());
   {
-    const int64_t nb = T / kAttnKeys + 2;
+    int64_t maxc = 0;
+    for (int64_t c : cost) maxc = std::max(maxc, c);
+    const int64_t nb = maxc + 1;
     std::vector<int64_t> cnt(nb + 1, 0);
-    for (int64_t c : cost) cnt[nb - 1 - std::min<int64_t>(c / kAttnKeys, nb - 1)]++;
+    for (int64_t c : cost) cnt[maxc - c]++;
     int64_t acc = 0;
     for (int64_t i = 0; i <= nb; ++i) {
       int64_t x = cnt[i];
       cnt[i] = acc;
       acc += x;
     }
-    for (size_t i = 0; i < tiles.size(); ++i)
-      sorted[cnt[nb - 1 - std::min<int64_t>(cost[i] / kAttnKeys, nb - 1)]++] = tiles[i];
+    for (size_t i = 0; i < entries.size(); ++i) sorted[cnt[maxc - cost[i]]++] = entries[i];
   }
 
   // lay out the upload region
@@ -218,7 +283,8 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
         w[off++] = std::min(kChunk, seg_len[s] - c0);
       }
   }
-  put(MH_OFF_TILES, (const int32_t*)sorted.data(), (int64_t)sorted.size() * 4);
+  put(MH_OFF_TILES, (const int32_t*)sorted.data(), (int64_t)sorted.size() * 8);
+  put(MH_OFF_MERGE, (const int32_t*)merges.data(), (int64_t)merges.size() * 4);
   if (off > L.upload_cap_words) return fail(FORK_E_CAPACITY, "metadata upload region overflow");
   const int64_t tstride = ((int64_t)caps->t_cap + 63) / 64 * 64;
   w[MH_MAGIC] = kMetaMagic;
@@ -234,6 +300,9 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   w[MH_OFF_TOKPOS] = (int32_t)(L.tok_off_words + tstride);
   w[MH_OFF_TOKISO] = (int32_t)(L.tok_off_words + 2 * tstride);
   w[MH_UPLOAD_WORDS] = (int32_t)off;
+  w[MH_NMERGE] = (int32_t)merges.size();
+  w[MH_NPARTS] = nslots;
+  w[MH_KV_HEADS] = (int32_t)Hkv;
 
   memset(out, 0, sizeof(*out));
   out->num_tokens = (int32_t)T;
@@ -243,6 +312,7 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   out->num_attn_tiles = (int32_t)sorted.size();
   out->num_chunks = (int32_t)nchunks;
   out->tile_tokens = TT;
+  out->num_attn_merges = (int32_t)merges.size();
   out->caps = *caps;
   if (upload_bytes) *upload_bytes = (size_t)off * 4;
   return FORK_OK;
@@ -343,8 +413,9 @@ fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int3
   fork_status st = check_caps(m ? &m->caps : nullptr);
   if (st) return st;
   if (!bytes_h) return fail(FORK_E_ARG, "bytes_h is null");
-  (void)H; (void)Hkv; (void)D; (void)dt;
-  *bytes_h = 0;
+  (void)H; (void)Hkv; (void)dt;
+  if (D != 64 && D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", D);
+  *bytes_h = attn_workspace_bytes(m->caps, D);
   return FORK_OK;
 }
 
@@ -352,7 +423,6 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
                               float* lse, int32_t H, int32_t Hkv, int32_t D, float scale,
                               fork_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  (void)ws; (void)ws_bytes;
   fork_status st = check_meta(m);
   if (st) return st;
   if (!q || !k || !v || !o) return fail(FORK_E_ARG, "q, k, v and o must be non-null");
@@ -362,7 +432,13 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
                 m->caps.gqa_group);
   if (D != 64 && D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", D);
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  return launch_attention(m, q, k, v, o, lse, H, Hkv, D, scale, dt, (hipStream_t)stream);
+  if (m->caps.kv_heads != 0 && Hkv != m->caps.kv_heads)
+    return fail(FORK_E_ARG, "Hkv=%d differs from the kv_heads %d the metadata was built for", Hkv,
+                m->caps.kv_heads);
+  const size_t need = attn_workspace_bytes(m->caps, D);
+  if (need && (!ws || ws_bytes < need))
+    return fail(FORK_E_WORKSPACE, "attention workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  return launch_attention(m, q, k, v, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);
 }
 
 fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv, fork_dtype dt,

@@ -40,11 +40,15 @@ enum MetaHeader : int {
   MH_OFF_LEVELOFF,    // [MAXDEPTH + 2] start of each depth in LEVELSEG
   MH_OFF_LEVELSEG,    // [S] segments by depth, longest first within a depth
   MH_OFF_CHUNKS,      // [NCHUNKS] int2 {first token, length}
-  MH_OFF_TILES,       // [NTILES] AttnTile, most expensive first
+  MH_OFF_TILES,       // [NTILES] AttnTile work entries, most expensive first
   MH_OFF_TOKSEG,      // [T] (device-written)
   MH_OFF_TOKPOS,      // [T] (device-written)
   MH_OFF_TOKISO,      // [T] (device-written)
   MH_UPLOAD_WORDS,    // size of the upload region in words
+  MH_NMERGE,          // split query tiles (merge groups)
+  MH_OFF_MERGE,       // [NMERGE] AttnMerge
+  MH_NPARTS,          // partial-result slots used by split tiles (per kv head)
+  MH_KV_HEADS,        // kv heads the split plan assumed (0: no splitting)
   MH_WORDS = 64
 };
 
@@ -53,20 +57,37 @@ constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
 constexpr int kAttnRows = 128;              // query rows (token x GQA head) per attention tile
 constexpr int kAttnKeys = 64;               // keys per staged key/value tile
 constexpr int kMaxDepthCap = 4096;
+// Split plan for query tiles with long key ranges: the target number of
+// concurrently resident attention workgroups (2 per CU on a 256-CU MI355X),
+// the smallest part (in 64-key tiles), the most parts per tile, and the
+// partial-result slots the workspace holds (parts x kv heads).
+constexpr int kAttnSlots = 512;
+constexpr int kMinPartTiles = 4;
+constexpr int kMaxSplit = 16;
+constexpr int kMaxPartSlots = 2048;
 
-// One attention query tile: tokens [t0, t1) of one or several consecutive
-// sibling segments. own_lo is the first token of t0's segment; info packs the
+// One attention work entry: query tokens [t0, t1) of one or several
+// consecutive sibling segments, and the part [kt0, kt1) of its key-tile
+// sequence (ancestor segments nearest first, then the own range, 64 keys per
+// tile) it covers. own_lo is the first token of t0's segment; info packs the
 // segment whose ancestor path (itself included) every row sees in full
 // (anc + 1, 0 for a root tile) in bits 0..29 and "tile spans several
-// segments" in bit 30.
+// segments" in bit 30. slot is -1 for a whole tile (written straight to the
+// output) or the partial-result slot of a split tile's part.
 struct AttnTile {
   int32_t t0, t1, own_lo, info;
+  int32_t kt0, kt1, slot, pad;
+};
+// A split query tile: its tokens and the `nparts` consecutive partial slots
+// (from slot0) its parts wrote.
+struct AttnMerge {
+  int32_t t0, t1, nparts, slot0;
 };
 constexpr int32_t kTileMulti = 1 << 30;
 constexpr int32_t kTileAncMask = (1 << 30) - 1;
 
 struct BlobLayout {
-  int64_t tile_cap, chunk_cap;
+  int64_t tile_cap, chunk_cap, merge_cap;
   int64_t upload_cap_words;  // capacity of the upload region (header included)
   int64_t tok_off_words;     // first per-token array
   int64_t total_words;
@@ -79,12 +100,14 @@ inline int32_t tile_tokens_for(int32_t gqa) { return gqa >= kAttnRows ? 1 : kAtt
 inline BlobLayout blob_layout(const fork_caps& c) {
   BlobLayout L;
   L.tile_tokens = tile_tokens_for(c.gqa_group);
-  L.tile_cap = ((int64_t)c.t_cap + L.tile_tokens - 1) / L.tile_tokens + c.s_cap;
+  // base tiles, plus at most kMaxPartSlots extra entries from splitting
+  L.tile_cap = ((int64_t)c.t_cap + L.tile_tokens - 1) / L.tile_tokens + c.s_cap + kMaxPartSlots;
   L.chunk_cap = ((int64_t)c.t_cap + kChunk - 1) / kChunk + c.s_cap;
-  // header + 10 segment arrays + level offsets + 2 words per chunk + 4 per tile,
-  // with each array aligned to 4 words
+  L.merge_cap = kMaxPartSlots / 2;
+  // header + 10 segment arrays + level offsets + 2 words per chunk + 8 per tile
+  // + 4 per merge group, each array aligned to 4 words
   L.upload_cap_words = MH_WORDS + 10 * ((int64_t)c.s_cap + 4) + (c.depth_cap + 2 + 4) +
-                       2 * L.chunk_cap + 4 + 4 * L.tile_cap + 4;
+                       2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4;
   L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
   L.tok_off_words = L.upload_cap_words;
   L.total_words = L.tok_off_words + 3 * (((int64_t)c.t_cap + 63) / 64 * 64);
@@ -115,9 +138,10 @@ fork_status check_meta(const fork_meta* m);
 // Kernel launchers (defined with their kernels).
 fork_status launch_meta_expand(const fork_meta* m, hipStream_t stream);
 fork_status launch_dense_mask(const fork_meta* m, uint8_t* mask, hipStream_t stream);
+size_t attn_workspace_bytes(const fork_caps& c, int D);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              void* o, float* lse, int H, int Hkv, int D, float scale,
-                             fork_dtype dt, hipStream_t stream);
+                             fork_dtype dt, void* ws, hipStream_t stream);
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);
 fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v,
                        const float* a, const float* b, const float* root_state, void* o,

@@ -32,6 +32,11 @@ fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* a, void
   if (a->H < 1 || a->Hkv < 1 || a->H % a->Hkv || a->H / a->Hkv != m->caps.gqa_group)
     return fail(FORK_E_ARG, "attention heads do not match the metadata's gqa_group");
   if (a->D != 64 && a->D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported", a->D);
+  if (m->caps.kv_heads != 0 && a->Hkv != m->caps.kv_heads)
+    return fail(FORK_E_ARG, "attention kv heads do not match the metadata's kv_heads");
+  const size_t aneed = attn_workspace_bytes(m->caps, a->D);
+  if (aneed && (!a->attn_ws || a->attn_ws_bytes < aneed))
+    return fail(FORK_E_WORKSPACE, "attention workspace too small");
   if (a->dk != a->dv || (a->dk != 32 && a->dk != 64 && a->dk != 128))
     return fail(FORK_E_UNSUPPORTED, "dk=%d dv=%d unsupported", a->dk, a->dv);
 
@@ -49,7 +54,7 @@ fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* a, void
     if (own) (void)hipStreamDestroy(own);
     return fail(FORK_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
   }
-  st = launch_attention(m, a->q, a->k, a->v, a->o, a->lse, a->H, a->Hkv, a->D, a->scale, a->dt, s);
+  st = launch_attention(m, a->q, a->k, a->v, a->o, a->lse, a->H, a->Hkv, a->D, a->scale, a->dt, a->attn_ws, s);
   if (st == FORK_OK)
     st = launch_gdn(m, a->gq, a->gk, a->gv, a->a, a->b, a->root_state, a->go, a->seg_start_state,
                     a->seg_final_state, a->gH, a->dk, a->dv, a->gscale, a->dt, a->gdn_ws, a->gdn_ws_bytes, s);

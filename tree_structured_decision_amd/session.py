@@ -20,9 +20,13 @@ FORK_DT = {"f32": B.FORK_F32, "bf16": B.FORK_BF16}
 
 
 class ForkSession:
+    """kv_heads and D (attention) enable split query tiles and size their
+    workspace; gH, dk, dv (Gated DeltaNet) size the scan workspace."""
+
     def __init__(self, t_cap: int, s_cap: int, depth_cap: int, gqa_group: int,
-                 gH: int = 0, dk: int = 0, dv: int = 0, device: str = "cuda", ring: int = 2):
-        self.caps = B.make_caps(t_cap, s_cap, depth_cap, gqa_group)
+                 kv_heads: int = 0, D: int = 0, gH: int = 0, dk: int = 0, dv: int = 0,
+                 device: str = "cuda", ring: int = 2):
+        self.caps = B.make_caps(t_cap, s_cap, depth_cap, gqa_group, kv_heads)
         dev_bytes, stg_bytes = B.fork_meta_size(self.caps)
         self.device = torch.device(device)
         self.blob = torch.empty(dev_bytes, dtype=torch.uint8, device=self.device)
@@ -32,11 +36,16 @@ class ForkSession:
         self._slot = 0
         self.meta = None
         self.gdn_ws = None
+        self.attn_ws = None
+        probe = B.fork_meta()
+        probe.caps = self.caps
         if gH:
-            probe = B.fork_meta()
-            probe.caps = self.caps
             n = B.gdn_fork_workspace(probe, gH, dk, dv, B.FORK_BF16)
             self.gdn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        if kv_heads and D:
+            n = B.fork_attn_workspace(probe, gqa_group * kv_heads, kv_heads, D, B.FORK_BF16)
+            if n:
+                self.attn_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
         self.graph = None
 
     # -- metadata -----------------------------------------------------------
@@ -59,8 +68,9 @@ class ForkSession:
         T, H, D = q.shape
         Hkv = k.shape[1]
         dt = B.FORK_BF16 if q.dtype == torch.bfloat16 else B.FORK_F32
-        B.fork_attn_forward(self.meta, q, k, v, o, lse, H, Hkv, D, scale, dt, None, 0,
-                            stream=stream)
+        ws = self.attn_ws
+        B.fork_attn_forward(self.meta, q, k, v, o, lse, H, Hkv, D, scale, dt, ws,
+                            0 if ws is None else ws.numel(), stream=stream)
 
     def gdn(self, q, k, v, a, b, o, seg_start_state, seg_final_state=None, root_state=None,
             scale: float = 1.0, stream=None):
@@ -82,7 +92,8 @@ class ForkSession:
         A.lse = p(attn.get("lse"))
         A.H, A.Hkv, A.D = attn["q"].shape[1], attn["k"].shape[1], attn["q"].shape[2]
         A.scale = float(attn.get("scale", 0.0))
-        A.attn_ws, A.attn_ws_bytes = None, 0
+        A.attn_ws = p(self.attn_ws)
+        A.attn_ws_bytes = 0 if self.attn_ws is None else self.attn_ws.numel()
         A.gq, A.gk, A.gv = p(gdn["q"]), p(gdn["k"]), p(gdn["v"])
         A.a, A.b = p(gdn["a"]), p(gdn["b"])
         A.root_state = p(gdn.get("root_state"))
@@ -113,7 +124,8 @@ class ForkSession:
             pass
 
 
-def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=None):
+def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=None,
+             kv_heads: int = 0):
     """Exact capacities of one tree (eager use)."""
     parent = np.asarray(parent)
     depth = np.zeros(len(parent), np.int64)
@@ -122,7 +134,7 @@ def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=
             depth[s] = depth[parent[s]] + 1
     return dict(t_cap=t_cap or int(np.sum(seg_len)), s_cap=s_cap or len(parent),
                 depth_cap=depth_cap if depth_cap is not None else int(depth.max()),
-                gqa_group=gqa_group)
+                gqa_group=gqa_group, kv_heads=kv_heads)
 
 
 def to_device(wl, device="cuda"):
