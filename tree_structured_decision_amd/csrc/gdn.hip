@@ -80,20 +80,9 @@ __device__ __forceinline__ typename GT<BF16>::F ld_rowk(const typename GT<BF16>:
   else
     return base[row * ld + k0 + kq];
 }
-// Fragment of an operand stored with k along rows (k-major): element (k, col).
-template <bool BF16>
-__device__ __forceinline__ typename GT<BF16>::F ld_kcol(const typename GT<BF16>::E* base, int ld, int col,
-                                                        int k0, int kq) {
-  if constexpr (BF16) {
-    bf16x8_t f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      f[jj] = __builtin_bit_cast(__bf16, base[(k0 + 8 * kq + jj) * ld + col]);
-    return f;
-  } else {
-    return base[(k0 + kq) * ld + col];
-  }
-}
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;  // operand of the LDS transpose read
+
 template <bool BF16>
 __device__ __forceinline__ f32x4_t mma(typename GT<BF16>::F a, typename GT<BF16>::F b, f32x4_t c) {
   if constexpr (BF16)
@@ -295,115 +284,271 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
   }
 }
 
-// Everything one scan chunk reads from global memory, in registers between
-// its loads (issued while the previous chunk computes) and its use. K is the
-// only chunk operand every wave needs in full, so it alone goes through LDS;
-// the other operands are loaded directly in the MFMA fragment layout of the
-// wave that uses them: rows 16w..16w+15 of Q, T'' and P as A fragments, and
-// v and g at the rows of this lane's accumulator elements.
+// ---------------------------------------------------------------------------
+// Scan: one launch per tree depth. A work item is (segment, head, group of
+// NSW 16-row slices of the state). Rows of the state evolve independently, so
+// slices never communicate: one wave owns one slice and processes all 64 rows
+// of every chunk for it. The chunk operands (k, q, T'', P, v, the decays) are
+// loaded once per workgroup, coalesced, into LDS and shared by its waves.
+//
+// Register-resident chain. Every product is a 16x16 MFMA whose reduction index
+// is enumerated in the order in which an accumulator already holds it: a
+// 16x16 accumulator block gives lane (col c, group q) the rows 4q..4q+3, so a
+// reduction step over 32 indices takes blocks 2f and 2f+1 and lane group q
+// covers indices 32f + 4q + {0..3} and 32f + 16 + 4q + {0..3}. Operands read
+// from LDS use the same order (two 8-byte reads per fragment, or two LDS
+// transpose reads for a transposed operand). So the state S (held as S^T
+// blocks), R = V - gamma X, U and U' pass from one product to the next in
+// registers: no exchange through memory and no synchronisation inside a chunk.
+//   X   = K S^T            (rows i, cols e)   A = K from LDS, B = S from regs
+//   Y^T = S Q^T            (rows e, cols i)   A = S regs,     B = Q from LDS
+//   U   = T'' R            (rows i, cols e)   A = T'' LDS,    B = R regs
+//   Z^T = U^T P^T          (rows e, cols i)   A = U regs,     B = P LDS
+//   S^T = gamma_C S^T + K^T U'  (rows d, cols e)  A = K^T (LDS transpose), B = U'
+// fp32 mode uses the 16x16x4 fp32 MFMA with the same index order (step f is
+// block f / 4, register f % 4).
 template <bool BF16, int DK>
-struct ChunkRegs {
+struct ScanCfg {
   using G = GT<BF16>;
-  using F = typename G::F;
-  static constexpr int KL = CH * (DK / G::EPC) / 256;  // 16-byte K loads per thread
-  static constexpr int NQ = DK / G::KSTEP;             // Q fragments (k-steps over dk)
-  static constexpr int NT = CH / G::KSTEP;             // T'', P fragments (k-steps over the chunk)
-  static constexpr int NP = BF16 ? 2 : 1;              // hi/lo planes
-  u32x4_t k[KL];
-  F q[NQ];
-  F t[NP][NT], p[NP][NT];
-  // one 32-bit register per v element: packing two 16-bit loads into one
-  // register would wait for them (and, the counter being in order, for every
-  // load issued before them)
-  typename std::conditional<BF16, unsigned, float>::type v[4];
-  float g[4], gl;
+  static constexpr int DV = DK;
+  static constexpr int NSW = (BF16 ? 4 : 2) < DV / 16 ? (BF16 ? 4 : 2) : DV / 16;  // slices per workgroup
+  static constexpr int NT = 64 * NSW;           // threads (one wave per slice)
+  static constexpr int NG = DV / (16 * NSW);    // slice groups per head
+  // Padded row lengths of the LDS tiles (elements). The LDS serves a 64-bit
+  // read 16 lanes at a time over 32 four-byte banks: T'' and P rows of 34
+  // dwords make the 16-row fragment reads conflict-free, V rows of 40 dwords
+  // the transpose reads (4 rows x 4 columns per 16 lanes); K and Q rows of 68
+  // dwords leave both kinds of read at most 2-way.
+  static constexpr int LDK = DK + G::PAD;                 // K, Q tiles
+  static constexpr int LDT = CH + (BF16 ? 4 : G::PAD);    // T'', P tiles
+  static constexpr int VW = 16 * NSW;                     // v columns of the group
+  static constexpr int LDV = VW + (BF16 ? 16 : G::PAD);
+  static constexpr int NDB = DK / 16;           // 16-wide d blocks of the state
+  static constexpr int NKD = DK / G::KSTEP;     // reduction steps over d
+  static constexpr int NKI = CH / G::KSTEP;     // reduction steps over chunk rows
+  // reduction steps of the lower-triangular products for output row block I,
+  // and the total over the four row blocks
+  static constexpr int nk(int I) { return (16 * (I + 1) + G::KSTEP - 1) / G::KSTEP; }
+  static constexpr int tri(int I) { return I == 0 ? 0 : tri(I - 1) + nk(I - 1); }
+  static constexpr int NTRI = tri(4);
+  // 16-byte chunks per thread of each staged operand
+  static constexpr int KCH = CH * (DK / G::EPC) / NT;
+  static constexpr int WCH = (int)(kWsPlane / 16) / NT;
+  static constexpr int VCH = CH * (VW / G::EPC) / NT;
+  static_assert(KCH * NT == CH * (DK / G::EPC), "K/Q staging must divide evenly");
+  static_assert(WCH * NT == (int)(kWsPlane / 16), "T''/P staging must divide evenly");
+  static_assert(VCH * NT == CH * (VW / G::EPC), "V staging must divide evenly");
+  // LDS elements of one buffer's tiles; two buffers when they fit
+  static constexpr int SK = CH * LDK, ST = CH * LDT, SV = CH * LDV;
+  static constexpr int NPL = BF16 ? 2 : 1;  // planes of T'' and P (hi, lo)
+  static constexpr size_t BUF_BYTES = (size_t)(2 * SK + 2 * NPL * ST + SV) * sizeof(typename G::E) + 2 * CH * 4;
+  static constexpr int NBUF = 2 * BUF_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
-// Issues every load of chunk (t0, len) for head h and state slice e0. Rows past
-// len are clamped to the chunk's last row: they only meet zero coefficients
-// (b = 0 there, so T'' has zero columns and U zero rows) or produce output rows
-// that are never stored, so they need no masking and no load is divergent.
+// Element offset of (row r, column col) in a row-major LDS tile with rows of
+// W elements (padded, so that the reads below spread over the LDS banks).
+template <bool BF16, int W>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * W + col;
+}
+// Stores one 16-byte group (8 bf16 / 4 fp32 elements starting at column col).
+template <bool BF16, int W>
+__device__ __forceinline__ void tile_put16(typename GT<BF16>::E* tile, int r, int col, u32x4_t v) {
+  *(u32x4_t*)(tile + r * W + col) = v;
+}
+
 template <bool BF16, int DK>
-__device__ __forceinline__ void chunk_load(ChunkRegs<BF16, DK>& r, const typename GT<BF16>::E* __restrict__ Kg,
-                                           const typename GT<BF16>::E* __restrict__ Qg,
-                                           const typename GT<BF16>::E* __restrict__ Vg,
-                                           const unsigned char* __restrict__ wsb, int t0, int len, int H, int h,
-                                           int e0, int tid) {
+struct ScanPrefetch {
+  using C = ScanCfg<BF16, DK>;
+  u32x4_t k[C::KCH], q[C::KCH], t[C::WCH], p[C::WCH], v[C::VCH];
+  float g, gl;
+};
+
+// Global loads of chunk (t0, len) for head h and v columns [ve0, ve0 + VW),
+// in two parts (k, q; then T'', P, v, g) so their issue spreads over the
+// previous chunk's compute. Rows past len are clamped to the chunk's last row:
+// they only meet zero coefficients (b = 0 there, so T'' has zero rows and
+// columns and U zero rows) or produce output rows that are never stored, so
+// no load needs a divergent branch.
+template <bool BF16, int DK>
+__device__ __forceinline__ void prefetch_kq(ScanPrefetch<BF16, DK>& r, const typename GT<BF16>::E* __restrict__ Kg,
+                                            const typename GT<BF16>::E* __restrict__ Qg, int t0, int len, int H,
+                                            int h, int tid) {
   using G = GT<BF16>;
-  using R = ChunkRegs<BF16, DK>;
-  using E = typename G::E;
+  using C = ScanCfg<BF16, DK>;
   constexpr int CPR = DK / G::EPC;
-  const int lane = tid & 63, w = tid >> 6, c16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < R::KL; ++i) {
-    const int task = tid + 256 * i, row = min(task / CPR, len - 1), ch = task % CPR;
-    r.k[i] = *(const u32x4_t*)(Kg + ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC);
+  for (int i = 0; i < C::KCH; ++i) {
+    const int task = tid + C::NT * i, row = min(task / CPR, len - 1), ch = task % CPR;
+    const size_t off = ((size_t)(t0 + row) * H + h) * DK + ch * G::EPC;
+    r.k[i] = *(const u32x4_t*)(Kg + off);
+    r.q[i] = *(const u32x4_t*)(Qg + off);
   }
-  const int arow = 16 * w + c16;  // A-fragment row of this lane
-  {
-    const E* qrow = Qg + ((size_t)(t0 + min(arow, len - 1)) * H + h) * DK;
+}
+template <bool BF16, int DK>
+__device__ __forceinline__ void prefetch_rest(ScanPrefetch<BF16, DK>& r, const typename GT<BF16>::E* __restrict__ Vg,
+                                              const unsigned char* __restrict__ wsb, int t0, int len, int H, int h,
+                                              int ve0, int tid) {
+  using G = GT<BF16>;
+  using C = ScanCfg<BF16, DK>;
+  const u32x4_t* Tw = (const u32x4_t*)wsb;
+  const u32x4_t* Pw = (const u32x4_t*)(wsb + kWsPlane);
 #pragma unroll
-    for (int f = 0; f < R::NQ; ++f) {
-      if constexpr (BF16)
-        r.q[f] = *(const bf16x8_t*)(qrow + f * G::KSTEP + 8 * q4);
-      else
-        r.q[f] = qrow[f * G::KSTEP + q4];
-    }
+  for (int i = 0; i < C::WCH; ++i) {
+    r.t[i] = Tw[tid + C::NT * i];
+    r.p[i] = Pw[tid + C::NT * i];
   }
-  const int kend = 16 * (w + 1);  // T'' and P are lower triangular
+  constexpr int VCPR = C::VW / G::EPC;
 #pragma unroll
-  for (int pl = 0; pl < R::NP; ++pl) {
-    const E* Tw = (const E*)wsb + pl * CH * CH + arow * CH;
-    const E* Pw = (const E*)(wsb + kWsPlane) + pl * CH * CH + arow * CH;
-#pragma unroll
-    for (int f = 0; f < R::NT; ++f) {
-      if (f * G::KSTEP < kend) {
-        if constexpr (BF16) {
-          r.t[pl][f] = *(const bf16x8_t*)(Tw + f * G::KSTEP + 8 * q4);
-          r.p[pl][f] = *(const bf16x8_t*)(Pw + f * G::KSTEP + 8 * q4);
-        } else {
-          r.t[pl][f] = Tw[f * G::KSTEP + q4];
-          r.p[pl][f] = Pw[f * G::KSTEP + q4];
-        }
-      }
-    }
+  for (int i = 0; i < C::VCH; ++i) {
+    const int task = tid + C::NT * i;
+    const int row = min(task / VCPR, len - 1), ch = task % VCPR;
+    r.v[i] = *(const u32x4_t*)(Vg + ((size_t)(t0 + row) * H + h) * C::DV + ve0 + ch * G::EPC);
   }
   const float* gw = (const float*)(wsb + 2 * kWsPlane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 16 * w + 4 * q4 + j;  // accumulator row of element j
-    r.v[j] = Vg[((size_t)(t0 + min(i, len - 1)) * H + h) * DK + e0 + c16];
-    r.g[j] = gw[i];
-  }
+  r.g = gw[tid & (CH - 1)];
   r.gl = gw[CH - 1];
 }
 
-// ---------------------------------------------------------------------------
-// Scan: one launch per depth; items (segment, head, 16-row state slice).
+// One LDS buffer of chunk tiles.
 template <bool BF16, int DK>
-__global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
+struct ScanTiles {
+  using E = typename GT<BF16>::E;
+  using C = ScanCfg<BF16, DK>;
+  E* K;
+  E* Q;
+  E* Th;
+  E* Tl;
+  E* Ph;
+  E* Pl;
+  E* V;
+  float* gam;
+  float* rr;
+  __device__ __forceinline__ ScanTiles(unsigned char* base) {
+    E* e = (E*)base;
+    K = e;
+    Q = e + C::SK;
+    Th = e + 2 * C::SK;
+    Tl = Th + (C::NPL - 1) * C::ST;
+    Ph = Th + C::NPL * C::ST;
+    Pl = Ph + (C::NPL - 1) * C::ST;
+    V = Ph + C::NPL * C::ST;
+    gam = (float*)(V + C::SV);
+    rr = gam + CH;
+  }
+};
+
+template <bool BF16, int DK>
+__device__ __forceinline__ void stage_kq(const ScanTiles<BF16, DK>& b, const ScanPrefetch<BF16, DK>& r, int tid) {
+  using G = GT<BF16>;
+  using C = ScanCfg<BF16, DK>;
+  constexpr int CPR = DK / G::EPC;
+#pragma unroll
+  for (int i = 0; i < C::KCH; ++i) {
+    const int task = tid + C::NT * i, row = task / CPR, ch = task % CPR;
+    tile_put16<BF16, C::LDK>(b.K, row, ch * G::EPC, r.k[i]);
+    tile_put16<BF16, C::LDK>(b.Q, row, ch * G::EPC, r.q[i]);
+  }
+}
+template <bool BF16, int DK>
+__device__ __forceinline__ void stage_rest(const ScanTiles<BF16, DK>& b, const ScanPrefetch<BF16, DK>& r, int tid) {
+  using G = GT<BF16>;
+  using C = ScanCfg<BF16, DK>;
+#pragma unroll
+  for (int i = 0; i < C::WCH; ++i) {
+    const int cidx = tid + C::NT * i;  // 16-byte chunk of a 16 KB operand region
+    if constexpr (BF16) {
+      const int plane = cidx / (CH * CH / 8), rem = cidx % (CH * CH / 8);
+      tile_put16<BF16, C::LDT>(plane ? b.Tl : b.Th, rem / 8, (rem % 8) * 8, r.t[i]);
+      tile_put16<BF16, C::LDT>(plane ? b.Pl : b.Ph, rem / 8, (rem % 8) * 8, r.p[i]);
+    } else {
+      tile_put16<BF16, C::LDT>(b.Th, cidx / 16, (cidx % 16) * 4, r.t[i]);
+      tile_put16<BF16, C::LDT>(b.Ph, cidx / 16, (cidx % 16) * 4, r.p[i]);
+    }
+  }
+  constexpr int VCPR = C::VW / G::EPC;
+#pragma unroll
+  for (int i = 0; i < C::VCH; ++i) {
+    const int task = tid + C::NT * i;
+    tile_put16<BF16, C::LDV>(b.V, task / VCPR, (task % VCPR) * G::EPC, r.v[i]);
+  }
+  if (tid < CH) {
+    b.gam[tid] = __expf(r.g);
+    b.rr[tid] = __expf(r.gl - r.g);
+  }
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Reduction step f of accumulator blocks X[] as an operand fragment (hi part,
+// and in bf16 mode the lo part x - hi).
+template <bool BF16>
+__device__ __forceinline__ void reg_frag(const f32x4_t* X, int f, typename GT<BF16>::F& hi,
+                                         typename GT<BF16>::F& lo) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = X[2 * f + (j >> 2)][j & 3];
+      const __bf16 hb = (__bf16)x;
+      hi[j] = hb;
+      lo[j] = (__bf16)(x - (float)hb);
+    }
+  } else {
+    hi = X[f >> 2][f & 3];
+    lo = 0.f;
+  }
+}
+
+// Operand fragment of a row-major LDS matrix M[row][k] at reduction step f in
+// the accumulator index order.
+template <bool BF16, int W>
+__device__ __forceinline__ typename GT<BF16>::F ld_perm(const typename GT<BF16>::E* base, int row, int f, int q4) {
+  if constexpr (BF16) {
+    const u32x2_t a = *(const u32x2_t*)(base + tile_off<BF16, W>(row, 32 * f + 4 * q4));
+    const u32x2_t b = *(const u32x2_t*)(base + tile_off<BF16, W>(row, 32 * f + 16 + 4 * q4));
+    const u32x4_t v = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, v);
+  } else {
+    return base[tile_off<BF16, W>(row, 16 * (f >> 2) + 4 * q4 + (f & 3))];
+  }
+}
+
+// Operand fragment of the transpose of a row-major LDS matrix M[k][col]
+// (row of the fragment = column col0 + lane % 16 of M), step f in the
+// accumulator index order. bf16: LDS transpose reads; within each 16-lane
+// group lane m supplies row kb + m / 4, column col0 + 4 (m % 4), and lane i
+// receives rows kb .. kb + 3 of column col0 + i.
+template <bool BF16, int W>
+__device__ __forceinline__ typename GT<BF16>::F ld_perm_t(const typename GT<BF16>::E* base, int col0, int f,
+                                                          int lane) {
+  const int q4 = lane >> 4, m = lane & 15;
+  if constexpr (BF16) {
+    const int r0 = 32 * f + 4 * q4 + (m >> 2), col = col0 + 4 * (m & 3);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + tile_off<BF16, W>(r0, col)));
+    const s16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + tile_off<BF16, W>(r0 + 16, col)));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    return base[tile_off<BF16, W>(16 * (f >> 2) + 4 * q4 + (f & 3), col0 + m)];
+  }
+}
+
+// Keeps the scheduler from moving instructions across this point, so LDS
+// reads issued for the next group of products stay ahead of the current
+// group's MFMAs (with one wave per SIMD nothing else hides their latency).
+#define SCAN_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <bool BF16, int DK>
+__global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const int32_t* __restrict__ blob,
+                                                                        GdnArgs args) {
   using G = GT<BF16>;
   using E = typename G::E;
   using F = typename G::F;
-  using R = ChunkRegs<BF16, DK>;
-  constexpr int DV = DK;
-  constexpr int NS = DV / VSL;       // slices per head
-  constexpr int LDK = DK + G::PAD;   // K tile
-  constexpr int LDSS = DK + G::PAD;  // state slice
-  constexpr int LDR = CH + G::PAD;   // transposed R, U, U'
-  constexpr int NDB = DK / 16;       // 16-col d blocks of the state slice
-  constexpr int DBW = (NDB + 3) / 4; // d blocks per wave
+  using C = ScanCfg<BF16, DK>;
+  using PF = ScanPrefetch<BF16, DK>;
+  using TL = ScanTiles<BF16, DK>;
   constexpr bool SPLIT = BF16;
-  constexpr int CPR = DK / G::EPC;
-  __shared__ __attribute__((aligned(16))) E Ks[CH * LDK];
-  __shared__ __attribute__((aligned(16))) E Sh[VSL * LDSS];
-  __shared__ __attribute__((aligned(16))) E Sl[SPLIT ? VSL * LDSS : 8];
-  __shared__ __attribute__((aligned(16))) E Rh[VSL * LDR];
-  __shared__ __attribute__((aligned(16))) E Rl[SPLIT ? VSL * LDR : 8];
-  __shared__ __attribute__((aligned(16))) E Uh[VSL * LDR];
-  __shared__ __attribute__((aligned(16))) E Ul[SPLIT ? VSL * LDR : 8];
-  __shared__ __attribute__((aligned(16))) E U2h[VSL * LDR];
-  __shared__ __attribute__((aligned(16))) E U2l[SPLIT ? VSL * LDR : 8];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::NBUF * C::BUF_BYTES];
 
   const int level = args.level;
   if (level > blob[MH_MAXDEPTH]) return;
@@ -417,40 +562,39 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
   const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
   const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
   const int H = args.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, sw = tid >> 6;  // wave = slice within the group
   const int c16 = lane & 15, q4 = lane >> 4;
   const E* __restrict__ Kg = (const E*)args.k;
   const E* __restrict__ Qg = (const E*)args.q;
   const E* __restrict__ Vg = (const E*)args.v;
   E* __restrict__ Og = (E*)args.o;
-  const size_t SZ = (size_t)DV * DK;
-  const int kend = 16 * (w + 1);  // T'' and P are lower triangular
+  const size_t SZ = (size_t)C::DV * DK;
 
-  // Work items: (segment, head, slice). Workgroups are dispatched round-robin
-  // over the 8 XCDs (workgroup id mod 8; the grid is a multiple of 8), so item
-  // i runs on XCD i mod 8. Heads are assigned so that all slices of one head
-  // run on the same XCD and share its L2 for the chunk operands (k, q, T'', P)
-  // they all read.
+  // Workgroups are dispatched round-robin over the 8 XCDs (workgroup id mod 8;
+  // the grid is a multiple of 8), so item i runs on XCD i mod 8. Heads are
+  // assigned so that all slice groups of one head share an XCD and its L2.
   const int NH8 = (H + 7) / 8;
-  for (int item = blockIdx.x; item < nlev * NH8 * 8 * NS; item += gridDim.x) {
+  for (int item = blockIdx.x; item < nlev * NH8 * 8 * C::NG; item += gridDim.x) {
     const int x = item & 7, j = item >> 3;
-    const int sl = j % NS, j2 = j / NS;
+    const int sg = j % C::NG, j2 = j / C::NG;
     const int h = (j2 % NH8) * 8 + x, li = j2 / NH8;
     if (h >= H) continue;
     // per-item metadata, uniform across the workgroup (scalar loads)
     const int s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + li]);
-    const int e0 = sl * VSL;
     const int p = __builtin_amdgcn_readfirstlane(parent[s]);
     const int L = __builtin_amdgcn_readfirstlane(seg_len[s]);
     const int st = __builtin_amdgcn_readfirstlane(seg_start[s]);
     const int cb = __builtin_amdgcn_readfirstlane(chunk_base[s]);
     const int fc_p = p >= 0 ? __builtin_amdgcn_readfirstlane(first_child[p]) : -1;
     const int ro = p < 0 ? __builtin_amdgcn_readfirstlane(root_ord[s]) : 0;
+    const int ve0 = C::VW * sg;    // first v column (state row) of the group
+    const int e0 = ve0 + 16 * sw;  // first state row of this wave's slice
     // chunk ci of the segment covers tokens [st + 64 ci, st + min(64 (ci + 1), L))
     const int nck = (L + CH - 1) / CH;
 
     // ---- start state: root_state / zero, or the parent's end state (read from
-    // the first child's start slot, where the parent's scan left it)
+    // the first child's start slot, where the parent's scan left it).
+    // St[db]: lane (c16, q4) holds S[e0 + c16][16 db + 4 q4 + r], r = 0..3.
     const float* src = nullptr;
     float* dst = nullptr;
     float* own_slot = args.seg_start + ((size_t)s * H + h) * SZ;
@@ -461,44 +605,48 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
       src = args.seg_start + ((size_t)fc_p * H + h) * SZ;
       if (fc_p != s) dst = own_slot;
     }
-    // branch-free loads from an always-valid address; zero when there is no source
     const bool has_src = src != nullptr;
-    const float* lsrc = has_src ? src : own_slot;
-    f32x4_t Sreg[DBW];
+    const float* lsrc = has_src ? src : own_slot;  // always a valid address
+    const size_t srow = (size_t)(e0 + c16) * DK + 4 * q4;
+    f32x4_t St[C::NDB];
 #pragma unroll
-    for (int bi = 0; bi < DBW; ++bi) {
-      const int db = min(w * DBW + bi, NDB - 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = lsrc[(size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16];
-        Sreg[bi][r] = has_src ? x : 0.f;
-      }
+    for (int db = 0; db < C::NDB; ++db) {
+      const f32x4_t xv = *(const f32x4_t*)(lsrc + srow + 16 * db);
+      St[db] = has_src ? xv : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // first chunk's loads go out together with the state loads
-    R nx;
-    chunk_load<BF16, DK>(nx, Kg, Qg, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h, e0,
-                         tid);
+    PF nx;
+    prefetch_kq<BF16, DK>(nx, Kg, Qg, st, min(CH, L), H, h, tid);
+    prefetch_rest<BF16, DK>(nx, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h, ve0, tid);
     if (dst) {
 #pragma unroll
-      for (int bi = 0; bi < DBW; ++bi) {
-        const int db = w * DBW + bi;
-        if (db < NDB)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16] = Sreg[bi][r];
-      }
+      for (int db = 0; db < C::NDB; ++db) *(f32x4_t*)(dst + srow + 16 * db) = St[db];
+    }
+    if constexpr (C::NBUF == 2) {
+      __syncthreads();  // the previous item's last chunk no longer reads buffer 0
+      const TL b0(lds);
+      stage_kq<BF16, DK>(b0, nx, tid);
+      stage_rest<BF16, DK>(b0, nx, tid);
     }
 
-    // output rows of the previous chunk, stored one iteration late (after the
-    // next chunk's loads are issued)
-    float oval[4] = {0.f, 0.f, 0.f, 0.f};
+    // output tile of the previous chunk (O^T blocks: lane (c16, q4) holds
+    // O[16 I + c16][e0 + 4 q4 + r]), stored one chunk late, after the next
+    // chunk's loads are issued (a load issued after a possibly aliasing store
+    // waits for that store)
+    f32x4_t oval[4];
     int orow0 = 0, olen = 0;
     auto flush_o = [&]() {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * q4 + r;
+      for (int I = 0; I < 4; ++I) {
+        const int i = 16 * I + c16;
         if (i < olen) {
-          E* d = Og + ((size_t)(orow0 + i) * H + h) * DV + e0 + c16;
-          if constexpr (BF16) *d = bf16_bits(oval[r]); else *d = oval[r];
+          E* d = Og + ((size_t)(orow0 + i) * H + h) * C::DV + e0 + 4 * q4;
+          if constexpr (BF16) {
+            const u32x2_t pk = {(unsigned)bf16_bits(oval[I][0]) | ((unsigned)bf16_bits(oval[I][1]) << 16),
+                                (unsigned)bf16_bits(oval[I][2]) | ((unsigned)bf16_bits(oval[I][3]) << 16)};
+            *(u32x2_t*)d = pk;
+          } else {
+            *(f32x4_t*)d = oval[I];
+          }
         }
       }
     };
@@ -506,122 +654,175 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
     for (int ci = 0; ci < nck; ++ci) {
       const int c = cb + ci;
       const int t0 = st + CH * ci, len = min(CH, L - CH * ci);
-      R cur = nx;  // this chunk's operands
+      const bool more = ci + 1 < nck;
+      const int nt0 = t0 + CH, nlen = min(CH, L - CH * (ci + 1));
+      const unsigned char* nws = args.ws + ((size_t)(c + 1) * H + h) * kWsChunk;
+      const int bi = C::NBUF == 2 ? (ci & 1) : 0;
+      const TL cur(lds + bi * C::BUF_BYTES);
+      const TL nxt(lds + (C::NBUF == 2 ? (bi ^ 1) : 0) * C::BUF_BYTES);
 
-      __syncthreads();  // previous chunk done with Ks, Sh/Sl and the exchange tiles
-#pragma unroll
-      for (int i = 0; i < R::KL; ++i) {
-        const int task = tid + 256 * i, row = task / CPR, ch = task % CPR;
-        *(u32x4_t*)(Ks + row * LDK + ch * G::EPC) = cur.k[i];
+      __syncthreads();  // this chunk's tiles are complete; the other buffer is free
+      if constexpr (C::NBUF == 1) {
+        stage_kq<BF16, DK>(cur, nx, tid);
+        stage_rest<BF16, DK>(cur, nx, tid);
+        __syncthreads();
       }
+      if (more) prefetch_kq<BF16, DK>(nx, Kg, Qg, nt0, nlen, H, h, tid);
+
+      // (1) X = K S^T and Y^T = S Q^T, LDS reads one reduction step ahead
+      f32x4_t X[4], Yt[4];
 #pragma unroll
-      for (int bi = 0; bi < DBW; ++bi) {
-        const int db = w * DBW + bi;
-        if (db < NDB)
+      for (int I = 0; I < 4; ++I) X[I] = Yt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      F ka[2][4], qb[2][4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) put_split<BF16>(Sh, Sl, (4 * q4 + r) * LDSS + 16 * db + c16, Sreg[bi][r]);
+      for (int I = 0; I < 4; ++I) {
+        ka[0][I] = ld_perm<BF16, C::LDK>(cur.K, 16 * I + c16, 0, q4);
+        qb[0][I] = ld_perm<BF16, C::LDK>(cur.Q, 16 * I + c16, 0, q4);
       }
-      float gam[4], rr[4];
+      F th[C::NTRI], tl[C::NTRI];
+      f32x4_t vq[4], gq[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        gam[r] = __expf(cur.g[r]);
-        rr[r] = __expf(cur.gl - cur.g[r]);
+      for (int f = 0; f < C::NKD; ++f) {
+        if (f + 1 < C::NKD) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            ka[(f + 1) & 1][I] = ld_perm<BF16, C::LDK>(cur.K, 16 * I + c16, f + 1, q4);
+            qb[(f + 1) & 1][I] = ld_perm<BF16, C::LDK>(cur.Q, 16 * I + c16, f + 1, q4);
+          }
+        } else {
+          // operands of steps (2) and (3)
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            if constexpr (BF16) {
+              const unsigned short* pv =
+                  cur.V + tile_off<BF16, C::LDV>(16 * I + 4 * q4 + (c16 >> 2), 16 * sw + 4 * (c16 & 3));
+              const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) vq[I][r] = bf16_val((unsigned short)t[r]);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) vq[I][r] = cur.V[tile_off<BF16, C::LDV>(16 * I + 4 * q4 + r, 16 * sw + c16)];
+            }
+            gq[I] = *(const f32x4_t*)(cur.gam + 16 * I + 4 * q4);
+          }
+#pragma unroll
+          for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int kf = 0; kf < C::nk(I); ++kf) {
+              th[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Th, 16 * I + c16, kf, q4);
+              if constexpr (SPLIT) tl[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Tl, 16 * I + c16, kf, q4);
+            }
+        }
+        SCAN_FENCE();
+        F sh, sl;
+        reg_frag<BF16>(St, f, sh, sl);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          X[I] = mma<BF16>(ka[f & 1][I], sh, X[I]);
+          Yt[I] = mma<BF16>(sh, qb[f & 1][I], Yt[I]);
+          if constexpr (SPLIT) {
+            X[I] = mma<BF16>(ka[f & 1][I], sl, X[I]);
+            Yt[I] = mma<BF16>(sl, qb[f & 1][I], Yt[I]);
+          }
+        }
+        SCAN_FENCE();
       }
-      const float gC = __expf(cur.gl);
-      __syncthreads();
-      // next chunk's loads first, then the previous chunk's output stores: a
-      // load issued after a possibly aliasing store waits for that store, so
-      // stores go out a whole chunk ahead of the next loads
-      if (ci + 1 < nck)
-        chunk_load<BF16, DK>(nx, Kg, Qg, Vg, args.ws + ((size_t)(c + 1) * H + h) * kWsChunk, t0 + CH,
-                             min(CH, L - CH * (ci + 1)), H, h, e0, tid);
+      if (more) prefetch_rest<BF16, DK>(nx, Vg, nws, nt0, nlen, H, h, ve0, tid);
       flush_o();
 
-      // (1) X = K S^T, Y = Q S^T   (rows 16w.., cols e); separate hi/lo chains
-      f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-      f32x4_t X2 = {0.f, 0.f, 0.f, 0.f}, Y2 = {0.f, 0.f, 0.f, 0.f};
+      // (2) R = V - gamma X  (lane (c16, q4), block I holds rows 16 I + 4 q4 + r)
+      f32x4_t R[4];
 #pragma unroll
-      for (int f = 0; f < R::NQ; ++f) {
-        const int k0 = f * G::KSTEP;
-        const F aK = ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4);
-        const F bh = ld_rowk<BF16>(Sh, LDSS, c16, k0, q4);
-        X = mma<BF16>(aK, bh, X);
-        Y = mma<BF16>(cur.q[f], bh, Y);
-        if constexpr (SPLIT) {
-          const F bl = ld_rowk<BF16>(Sl, LDSS, c16, k0, q4);
-          X2 = mma<BF16>(aK, bl, X2);
-          Y2 = mma<BF16>(cur.q[f], bl, Y2);
+      for (int I = 0; I < 4; ++I) R[I] = vq[I] - gq[I] * X[I];
+      F rh[C::NKI], rl[C::NKI];
+#pragma unroll
+      for (int f = 0; f < C::NKI; ++f) reg_frag<BF16>(R, f, rh[f], rl[f]);
+      // (3) U = T'' R  (T'' lower triangular: row block I needs indices < 16 (I + 1));
+      // the P fragments of step (4) are read meanwhile
+      F ph[C::NTRI], pl[C::NTRI];
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int kf = 0; kf < C::nk(I); ++kf) {
+          ph[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Ph, 16 * I + c16, kf, q4);
+          if constexpr (SPLIT) pl[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Pl, 16 * I + c16, kf, q4);
         }
-      }
-      // (2) R = V - gamma * X  -> R^T
+      SCAN_FENCE();
+      f32x4_t U[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * q4 + r;
-        float vv;
-        if constexpr (BF16) vv = __uint_as_float(cur.v[r] << 16); else vv = cur.v[r];
-        put_split<BF16>(Rh, Rl, c16 * LDR + i, vv - gam[r] * (X[r] + X2[r]));
-      }
-      __syncthreads();
-
-      // (3) U = T'' R  (T'' lower triangular: k < 16(w+1))
-      f32x4_t Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
+      for (int I = 0; I < 4; ++I) {
+        U[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int f = 0; f < R::NT; ++f) {
-        const int k0 = f * G::KSTEP;
-        if (k0 < kend) {
-          const F bh = ld_rowk<BF16>(Rh, LDR, c16, k0, q4);
-          Ua = mma<BF16>(cur.t[0][f], bh, Ua);
+        for (int kf = 0; kf < C::nk(I); ++kf) {
+          U[I] = mma<BF16>(th[C::tri(I) + kf], rh[kf], U[I]);
           if constexpr (SPLIT) {
-            Ub = mma<BF16>(cur.t[0][f], ld_rowk<BF16>(Rl, LDR, c16, k0, q4), Ub);
-            Ub = mma<BF16>(cur.t[SPLIT ? 1 : 0][f], bh, Ub);
+            U[I] = mma<BF16>(th[C::tri(I) + kf], rl[kf], U[I]);
+            U[I] = mma<BF16>(tl[C::tri(I) + kf], rh[kf], U[I]);
           }
         }
       }
+      SCAN_FENCE();
+      // (4) O^T = scale (S Q^T * gamma + U^T P^T), stored one chunk late; the
+      // first K^T fragments of step (5) and the decays are read meanwhile
+      F uh[C::NKI], ul[C::NKI];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * q4 + r;
-        const float u = Ua[r] + Ub[r];
-        put_split<BF16>(Uh, Ul, c16 * LDR + i, u);
-        put_split<BF16>(U2h, U2l, c16 * LDR + i, u * rr[r]);
+      for (int f = 0; f < C::NKI; ++f) reg_frag<BF16>(U, f, uh[f], ul[f]);
+      F kt[2][C::NDB];
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) kt[0][db] = ld_perm_t<BF16, C::LDK>(cur.K, 16 * db, 0, lane);
+      f32x4_t rq[4];
+      float gi[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        rq[I] = *(const f32x4_t*)(cur.rr + 16 * I + 4 * q4);
+        gi[I] = cur.gam[16 * I + c16];
       }
-      __syncthreads();
-
-      // (4) O = scale * (gamma * Y + P U), stored at the next iteration
-      {
-        f32x4_t Za = {0.f, 0.f, 0.f, 0.f}, Zb = {0.f, 0.f, 0.f, 0.f};
+      const float gC = cur.gam[CH - 1];
+      SCAN_FENCE();
+      f32x4_t Zt[4];
 #pragma unroll
-        for (int f = 0; f < R::NT; ++f) {
-          const int k0 = f * G::KSTEP;
-          if (k0 < kend) {
-            const F bh = ld_rowk<BF16>(Uh, LDR, c16, k0, q4);
-            Za = mma<BF16>(cur.p[0][f], bh, Za);
-            if constexpr (SPLIT) {
-              Zb = mma<BF16>(cur.p[0][f], ld_rowk<BF16>(Ul, LDR, c16, k0, q4), Zb);
-              Zb = mma<BF16>(cur.p[SPLIT ? 1 : 0][f], bh, Zb);
-            }
+      for (int I = 0; I < 4; ++I) {
+        Zt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < C::nk(I); ++kf) {
+          Zt[I] = mma<BF16>(uh[kf], ph[C::tri(I) + kf], Zt[I]);
+          if constexpr (SPLIT) {
+            Zt[I] = mma<BF16>(ul[kf], ph[C::tri(I) + kf], Zt[I]);
+            Zt[I] = mma<BF16>(uh[kf], pl[C::tri(I) + kf], Zt[I]);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oval[r] = args.scale * (gam[r] * (Y[r] + Y2[r]) + Za[r] + Zb[r]);
-        orow0 = t0;
-        olen = len;
       }
-      // (5) S = gamma_C S + U'^T K
+      SCAN_FENCE();
+      if constexpr (C::NBUF == 2)
+        if (more) stage_kq<BF16, DK>(nxt, nx, tid);
 #pragma unroll
-      for (int bi = 0; bi < DBW; ++bi) {
-        const int db = w * DBW + bi;
-        if (db < NDB) {
-          f32x4_t acc = Sreg[bi] * gC;
-          f32x4_t acc2 = {0.f, 0.f, 0.f, 0.f};
+      for (int I = 0; I < 4; ++I) oval[I] = args.scale * (gi[I] * Yt[I] + Zt[I]);
+      orow0 = t0;
+      olen = len;
+      // (5) S^T = gamma_C S^T + K^T U',  U' = diag(gamma_C / gamma) U
 #pragma unroll
-          for (int k0 = 0; k0 < CH; k0 += G::KSTEP) {
-            const F bk = ld_kcol<BF16>(Ks, LDK, 16 * db + c16, k0, q4);
-            acc = mma<BF16>(ld_rowk<BF16>(U2h, LDR, c16, k0, q4), bk, acc);
-            if constexpr (SPLIT) acc2 = mma<BF16>(ld_rowk<BF16>(U2l, LDR, c16, k0, q4), bk, acc2);
-          }
-          Sreg[bi] = acc + acc2;
+      for (int I = 0; I < 4; ++I) U[I] *= rq[I];
+#pragma unroll
+      for (int f = 0; f < C::NKI; ++f) reg_frag<BF16>(U, f, uh[f], ul[f]);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) St[db] *= gC;
+#pragma unroll
+      for (int f = 0; f < C::NKI; ++f) {
+        if (f + 1 < C::NKI) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            kt[(f + 1) & 1][db] = ld_perm_t<BF16, C::LDK>(cur.K, 16 * db, f + 1, lane);
         }
+        SCAN_FENCE();
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          St[db] = mma<BF16>(kt[f & 1][db], uh[f], St[db]);
+          if constexpr (SPLIT) St[db] = mma<BF16>(kt[f & 1][db], ul[f], St[db]);
+        }
+        SCAN_FENCE();
       }
+      if constexpr (C::NBUF == 2)
+        if (more) stage_rest<BF16, DK>(nxt, nx, tid);
     }
     flush_o();
 
@@ -631,15 +832,9 @@ __global__ void __launch_bounds__(256) gdn_scan_kernel(const int32_t* __restrict
       float* d1 = args.seg_final ? args.seg_final + ((size_t)s * H + h) * SZ : nullptr;
       float* d2 = fc >= 0 ? args.seg_start + ((size_t)fc * H + h) * SZ : nullptr;
 #pragma unroll
-      for (int bi = 0; bi < DBW; ++bi) {
-        const int db = w * DBW + bi;
-        if (db < NDB)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const size_t idx = (size_t)(e0 + 4 * q4 + r) * DK + 16 * db + c16;
-            if (d1) d1[idx] = Sreg[bi][r];
-            if (d2) d2[idx] = Sreg[bi][r];
-          }
+      for (int db = 0; db < C::NDB; ++db) {
+        if (d1) *(f32x4_t*)(d1 + srow + 16 * db) = St[db];
+        if (d2) *(f32x4_t*)(d2 + srow + 16 * db) = St[db];
       }
     }
   }
@@ -660,10 +855,11 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   // Under capture, every depth up to the capacity is recorded; depths beyond
   // the current tree exit at once.
   const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
-  const int sgrid = (2 * cus + 7) / 8 * 8;  // a multiple of 8: item i runs on XCD i mod 8
+  const int sgrid = (cus + 7) / 8 * 8;  // one workgroup per CU (LDS); a multiple of 8: item i runs on XCD i mod 8
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
-    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(256), 0, stream, a.blob, a);
+    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream, a.blob,
+                       a);
     FORK_HIP_CHECK(hipGetLastError());
   }
   return FORK_OK;
