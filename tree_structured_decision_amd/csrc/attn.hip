@@ -58,6 +58,7 @@ struct AttnArgs {
   void* o;
   float* lse;
   float* ws;  // partial results of split tiles: [slot][kv head] x (128 rows x D outputs, 128 lse)
+  int32_t* ctr;  // the blob's work counters: next item per XCD (8), finished workgroups
   int H, Hkv, G;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -232,8 +233,23 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
   const int l32 = lane & 31, hi = lane >> 5;
   const int H = args.H, Hkv = args.Hkv, G = args.G;
   const int nitems = ntiles * Hkv;
+  __shared__ int s_item;
 
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  // Work items (most expensive first) are handed out dynamically, per XCD:
+  // workgroups are dispatched round-robin over the 8 XCDs (the grid is a
+  // multiple of 8), and the workgroups of XCD x take items x, x + 8, x + 16,
+  // ... from that XCD's counter in the blob. A workgroup that finishes early
+  // takes the next item, while each XCD keeps to the kv heads g = item mod Hkv
+  // it started with, so their keys and values stay in its L2. The counters are
+  // zero when the blob is built; the last workgroup to run out of work resets
+  // them for the next launch.
+  const int xcd = blockIdx.x & (kNumXcd - 1);
+  for (;;) {
+    __syncthreads();  // every thread has read the previous item
+    if (tid == 0) s_item = atomicAdd(args.ctr + xcd, 1) * kNumXcd + xcd;
+    __syncthreads();
+    const int item = s_item;
+    if (item >= nitems) break;
     const int ti = item / Hkv, g = item - ti * Hkv;
     AttnTile tile;  // uniform across the workgroup: keep it in scalar registers
     tile.t0 = __builtin_amdgcn_readfirstlane(tiles[ti].t0);
@@ -442,59 +458,85 @@ __global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
       if (args.lse && hi == 0) args.lse[(size_t)t_row * H + h] = lse_row;
     }
   }
+  if (tid == 0 && atomicAdd(args.ctr + kNumXcd, 1) == (int)gridDim.x - 1) {
+    // every other workgroup has taken its last item: reset for the next launch
+    for (int x = 0; x <= kNumXcd; ++x) atomicExch(args.ctr + x, 0);
+  }
 }
 
 // Combines the parts of split query tiles: for each row,
 // o = sum_p exp(lse_p - lse) o_p with lse = log sum_p exp(lse_p).
+// A work item is (split tile, kv head, group of 16 rows); 16 threads share a
+// row and each combines D / 16 of its columns, with the loads of all parts
+// issued together.
+constexpr int kMergeRows = 16;
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
   using E = typename std::conditional<BF16, unsigned short, float>::type;
+  constexpr int PS = kAttnRows * D + kAttnRows;  // floats per partial slot
+  constexpr int NRG = kAttnRows / kMergeRows;    // row groups per tile
+  constexpr int C4 = D / 4 / 16;                 // float4 columns per thread
   const int nmerge = blob[MH_NMERGE];
   const int TT = blob[MH_TILE_TOKENS];
   const AttnMerge* __restrict__ merges = (const AttnMerge*)(blob + blob[MH_OFF_MERGE]);
   const int H = args.H, Hkv = args.Hkv, G = args.G;
-  constexpr int PS = kAttnRows * D + kAttnRows;  // floats per partial slot
-  for (int item = blockIdx.x; item < nmerge * Hkv; item += gridDim.x) {
-    const int mi = item / Hkv, g = item - mi * Hkv;
+  const int rr = threadIdx.x >> 4, cq = threadIdx.x & 15;
+  for (int item = blockIdx.x; item < nmerge * Hkv * NRG; item += gridDim.x) {
+    const int rg = item % NRG, mg = item / NRG;
+    const int mi = mg / Hkv, g = mg - mi * Hkv;
     const int t0 = merges[mi].t0, t1 = merges[mi].t1, np = merges[mi].nparts, s0 = merges[mi].slot0;
-    for (int task = threadIdx.x; task < kAttnRows * (D / 4); task += blockDim.x) {
-      const int r = task / (D / 4), c4 = task % (D / 4);
-      const int tl = r / G, hg = r - tl * G;
-      if (tl >= TT || t0 + tl >= t1) continue;
-      const int t = t0 + tl, h = g * G + hg;
-      float m = -INFINITY;
-      for (int p = 0; p < np; ++p) m = fmaxf(m, args.ws[((size_t)(s0 + p) * Hkv + g) * PS + kAttnRows * D + r]);
-      float den = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int p = 0; p < np; ++p) {
-        const float* part = args.ws + ((size_t)(s0 + p) * Hkv + g) * PS;
-        const float lp = part[kAttnRows * D + r];
-        const float wgt = lp == -INFINITY ? 0.f : __expf(lp - m);
-        const float4 x = *(const float4*)(part + r * D + 4 * c4);
+    const int r = kMergeRows * rg + rr;
+    const int tl = r / G, hg = r - tl * G;
+    if (tl >= TT || t0 + tl >= t1) continue;
+    const float* part0 = args.ws + ((size_t)s0 * Hkv + g) * PS;
+    const size_t pstride = (size_t)Hkv * PS;
+    float lp[kMaxSplit];
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p) {
+      lp[p] = p < np ? part0[p * pstride + kAttnRows * D + r] : -INFINITY;
+      m = fmaxf(m, lp[p]);
+    }
+    float den = 0.f;
+    float4 acc[C4];
+#pragma unroll
+    for (int c = 0; c < C4; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p) {
+      if (p < np) {
+        const float wgt = lp[p] == -INFINITY ? 0.f : __expf(lp[p] - m);
         den += wgt;
-        acc.x += wgt * x.x;
-        acc.y += wgt * x.y;
-        acc.z += wgt * x.z;
-        acc.w += wgt * x.w;
+#pragma unroll
+        for (int c = 0; c < C4; ++c) {
+          const float4 x = *(const float4*)(part0 + p * pstride + (size_t)r * D + 4 * (cq + 16 * c));
+          acc[c].x += wgt * x.x;
+          acc[c].y += wgt * x.y;
+          acc[c].z += wgt * x.z;
+          acc[c].w += wgt * x.w;
+        }
       }
-      const float inv = 1.f / den;
-      E* orow = (E*)args.o + ((size_t)t * H + h) * D + 4 * c4;
+    }
+    const float inv = 1.f / den;
+    const int t = t0 + tl, h = g * G + hg;
+#pragma unroll
+    for (int c = 0; c < C4; ++c) {
+      E* orow = (E*)args.o + ((size_t)t * H + h) * D + 4 * (cq + 16 * c);
       if constexpr (BF16) {
         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
         bf16x2_t p0, p1;
-        p0[0] = (__bf16)(acc.x * inv);
-        p0[1] = (__bf16)(acc.y * inv);
-        p1[0] = (__bf16)(acc.z * inv);
-        p1[1] = (__bf16)(acc.w * inv);
+        p0[0] = (__bf16)(acc[c].x * inv);
+        p0[1] = (__bf16)(acc[c].y * inv);
+        p1[0] = (__bf16)(acc[c].z * inv);
+        p1[1] = (__bf16)(acc[c].w * inv);
         uint2 pk;
         pk.x = __builtin_bit_cast(unsigned, p0);
         pk.y = __builtin_bit_cast(unsigned, p1);
         *(uint2*)orow = pk;
       } else {
-        *(float4*)orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        *(float4*)orow = make_float4(acc[c].x * inv, acc[c].y * inv, acc[c].z * inv, acc[c].w * inv);
       }
-      if (args.lse && c4 == 0) args.lse[(size_t)t * H + h] = m + __logf(den);
     }
+    if (args.lse && cq == 0) args.lse[(size_t)t * H + h] = m + __logf(den);
   }
 }
 
@@ -506,8 +548,8 @@ fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStrea
   // otherwise only when this tree has split tiles
   const bool cap = stream_capturing(stream);
   if (m->caps.kv_heads > 0 && (cap || m->num_attn_merges > 0)) {
-    int mgrid = 2 * device_cu_count();
-    if (!cap) mgrid = std::min(mgrid, m->num_attn_merges * a.Hkv);
+    int mgrid = 4 * device_cu_count();
+    if (!cap) mgrid = std::min(mgrid, m->num_attn_merges * a.Hkv * (kAttnRows / kMergeRows));
     hipLaunchKernelGGL((fork_attn_merge_kernel<BF16, D>), dim3(mgrid), dim3(256), 0, stream, a.blob, a);
     FORK_HIP_CHECK(hipGetLastError());
   }
@@ -531,6 +573,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.o = o;
   a.lse = lse;
   a.ws = (float*)ws;
+  a.ctr = (int32_t*)m->dev + kAttnCtrWord;
   a.H = H;
   a.Hkv = Hkv;
   a.G = H / Hkv;
@@ -543,6 +586,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
     const long long items = (long long)m->num_attn_tiles * Hkv;
     if (items < grid) grid = (int)(items > 0 ? items : 1);
   }
+  grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;  // whole rounds over the XCDs
   if (dt == FORK_BF16)
     return D == 128 ? launch_one<true, 128>(m, a, grid, stream) : launch_one<true, 64>(m, a, grid, stream);
   return D == 128 ? launch_one<false, 128>(m, a, grid, stream) : launch_one<false, 64>(m, a, grid, stream);

@@ -51,6 +51,14 @@ enum MetaHeader : int {
   MH_KV_HEADS,        // kv heads the split plan assumed (0: no splitting)
   MH_WORDS = 64
 };
+// Header words 48..56 hold the attention work counters: the next work item of
+// each of the 8 XCDs (workgroup id mod 8), then the number of workgroups that
+// found no more work. They are zero in a freshly built blob and the kernel
+// leaves them zero.
+constexpr int kAttnCtrWord = 48;
+constexpr int kNumXcd = 8;
+static_assert(kAttnCtrWord > MH_KV_HEADS && kAttnCtrWord + kNumXcd < MH_WORDS, "counter words inside the header");
+
 
 constexpr int32_t kMetaMagic = 0x464B4D31;  // "FKM1"
 constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
