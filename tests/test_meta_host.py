@@ -22,6 +22,8 @@ H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS
            "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
            "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
+ATTN_ROWS = int(re.search(r"kAttnRows = (\d+);", open(os.path.join(
+    ROOT, "tree_structured_decision_amd", "csrc", "common.h")).read()).group(1))
 
 
 def test_header_indices_match_source():
@@ -102,7 +104,7 @@ def check_plan(parent, seg_len, gqa, kv_heads=0):
     # tiles: every token in exactly one query tile; tile tokens share one parent;
     # the entries of a tile cover its key-tile sequence [0, ktiles) exactly
     TT = w[HI["TILE_TOKENS"]]
-    assert TT == max(1, 128 // gqa)
+    assert TT == max(1, ATTN_ROWS // gqa)
     nt = w[HI["NTILES"]]
     ent = arr(w, "TILES", 8 * nt).reshape(-1, 8)
     tok_seg = ref["tok_seg"]
@@ -210,7 +212,7 @@ def test_plan_errors():
     assert _status(lambda: plan(ok_p, ok_l, s_cap=1)) == -5      # segment capacity
     assert _status(lambda: plan([-1, 0, 1, 2], [1, 1, 1, 1], depth_cap=2)) == -5
     assert _status(lambda: plan(ok_p, ok_l, gqa=0)) == -3
-    assert _status(lambda: plan(ok_p, ok_l, gqa=129)) == -3
+    assert _status(lambda: plan(ok_p, ok_l, gqa=ATTN_ROWS + 1)) == -3
     caps = B.make_caps(6, 2, 2, 8)
     small = np.zeros(16, np.int32)
     assert _status(lambda: B.fork_meta_plan(ok_p, ok_l, caps, small)) == -4

@@ -15,7 +15,9 @@
 // and used by all 128 rows, so a long shared prefix is read once per tile of
 // packed branch queries instead of once per branch.
 //
-// Kernel shape: 256 threads = 4 wave64s, each wave owns 32 query rows.
+// Kernel shape: 512 threads = 8 wave64s (two per SIMD, one workgroup per CU),
+// each wave owns 32 of the tile's 256 query rows, so every staged key/value
+// tile feeds 256 rows.
 // S^T = K Q^T and O^T = V^T P^T on MFMA (32x32x16 bf16, or 32x32x2 f32): with
 // keys on the MFMA M dimension, each lane holds one query row's scores in its
 // registers, so the online-softmax row max needs one cross-lane step and the
@@ -57,7 +59,7 @@ struct AttnArgs {
   const void* v;
   void* o;
   float* lse;
-  float* ws;  // partial results of split tiles: [slot][kv head] x (128 rows x D outputs, 128 lse)
+  float* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
   int32_t* ctr;  // the blob's work counters: next item per XCD (8), finished workgroups
   int H, Hkv, G;
   float scale_log2;  // softmax scale * log2(e)
@@ -66,14 +68,18 @@ struct AttnArgs {
 // Key/value tile of 64 keys held in registers between its global load and
 // its LDS store, so the next tile's loads are in flight while the current
 // tile is being computed.
+constexpr int kAttnThreads = 512;
+
 template <bool BF16, int D>
 struct KVRegs {
   using C = AttnCfg<BF16, D>;
-  static constexpr int KT = kAttnKeys * C::CPR / 256;     // 16-byte K loads per thread
-  static constexpr int VTASKS = (kAttnKeys / 4) * C::CPR;  // (4 keys x 16 bytes) V tasks
-  static constexpr int VT = (VTASKS + 255) / 256;
+  static constexpr int KT = kAttnKeys * C::CPR / kAttnThreads;  // 16-byte K (and bf16 V) loads per thread
+  // fp32 V is transposed on its way to LDS, in tasks of 4 keys x 16 bytes
+  static constexpr int VTASKS = (kAttnKeys / 4) * C::CPR;
+  static constexpr int VT = BF16 ? 1 : (VTASKS + kAttnThreads - 1) / kAttnThreads;
+  static_assert(KT * kAttnThreads == kAttnKeys * C::CPR, "K tile loads must divide evenly");
   u32x4_t k[KT];
-  u32x4_t v[VT][4];
+  u32x4_t v[BF16 ? KT : VT][BF16 ? 1 : 4];
 };
 
 // Global loads of keys [j0, j0 + 64) of kv head g; rows past `jmax` repeat
@@ -86,20 +92,23 @@ __device__ __forceinline__ void kv_load(KVRegs<BF16, D>& r, const E* __restrict_
   using R = KVRegs<BF16, D>;
 #pragma unroll
   for (int i = 0; i < R::KT; ++i) {
-    const int task = tid + 256 * i;
+    const int task = tid + kAttnThreads * i;
     const int row = task / C::CPR, ch = task % C::CPR;
     const int j = min(j0 + row, jmax);
     r.k[i] = *(const u32x4_t*)(K + ((size_t)j * Hkv + g) * D + ch * C::EPC);
+    if constexpr (BF16) r.v[i][0] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
   }
+  if constexpr (!BF16) {
 #pragma unroll
-  for (int i = 0; i < R::VT; ++i) {
-    const int task = tid + 256 * i;
-    if (task < R::VTASKS) {
-      const int kq = task / C::CPR, ch = task % C::CPR;
+    for (int i = 0; i < R::VT; ++i) {
+      const int task = tid + kAttnThreads * i;
+      if (task < R::VTASKS) {
+        const int kq = task / C::CPR, ch = task % C::CPR;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = min(j0 + 4 * kq + jj, jmax);
-        r.v[i][jj] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = min(j0 + 4 * kq + jj, jmax);
+          r.v[i][jj] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
+        }
       }
     }
   }
@@ -114,21 +123,18 @@ __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict
   using R = KVRegs<BF16, D>;
 #pragma unroll
   for (int i = 0; i < R::KT; ++i) {
-    const int task = tid + 256 * i;
+    const int task = tid + kAttnThreads * i;
     const int row = task / C::CPR, ch = task % C::CPR;
     *(u32x4_t*)(Ks + row * C::KS + ch * C::EPC) = r.k[i];
+    if constexpr (BF16) *(u32x4_t*)(Vt + row * C::VS + ch * C::EPC) = r.v[i][0];
   }
+  if constexpr (!BF16) {
 #pragma unroll
-  for (int i2 = 0; i2 < R::VT; ++i2) {
-    const int task = tid + 256 * i2;
-    if (task < R::VTASKS) {
-      const int kq = task / C::CPR, ch = task % C::CPR;
-      const u32x4_t* x = r.v[i2];
-      if constexpr (BF16) {
-        // row-major, like K: 4 key rows of one 16-byte chunk each
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) *(u32x4_t*)(Vt + (4 * kq + jj) * C::VS + ch * 8) = x[jj];
-      } else {
+    for (int i2 = 0; i2 < R::VT; ++i2) {
+      const int task = tid + kAttnThreads * i2;
+      if (task < R::VTASKS) {
+        const int kq = task / C::CPR, ch = task % C::CPR;
+        const u32x4_t* x = r.v[i2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x4_t pk;
@@ -206,10 +212,9 @@ __device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
   it.done = true;
 }
 
-// Two workgroups per CU (<= 256 VGPRs) except fp32 with D = 128, whose larger
-// fragments need the whole register file.
+// One workgroup of 8 waves per CU: two waves per SIMD, <= 256 VGPRs each.
 template <bool BF16, int D>
-__global__ void __launch_bounds__(256, (BF16 || D == 64) ? 2 : 1)
+__global__ void __launch_bounds__(kAttnThreads, 1)
     fork_attn_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
   using C = AttnCfg<BF16, D>;
   using E = typename std::conditional<BF16, unsigned short, float>::type;
@@ -542,7 +547,7 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
 
 template <bool BF16, int D>
 fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(256), 0, stream, a.blob, a);
+  hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(kAttnThreads), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
   // merge pass for split tiles: under capture whenever splitting is possible,
   // otherwise only when this tree has split tiles
@@ -579,9 +584,9 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.G = H / Hkv;
   const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  // Persistent grid: two workgroups per CU. Under capture the tree can change
+  // Persistent grid: one workgroup per CU. Under capture the tree can change
   // between replays, so the grid must not depend on the current tile count.
-  int grid = (dt == FORK_F32 && D == 128 ? 1 : 2) * device_cu_count();
+  int grid = device_cu_count();
   if (!stream_capturing(stream)) {
     const long long items = (long long)m->num_attn_tiles * Hkv;
     if (items < grid) grid = (int)(items > 0 ? items : 1);

@@ -62,17 +62,17 @@ static_assert(kAttnCtrWord > MH_KV_HEADS && kAttnCtrWord + kNumXcd < MH_WORDS, "
 
 constexpr int32_t kMetaMagic = 0x464B4D31;  // "FKM1"
 constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
-constexpr int kAttnRows = 128;              // query rows (token x GQA head) per attention tile
+constexpr int kAttnRows = 256;              // query rows (token x GQA head) per attention tile
 constexpr int kAttnKeys = 64;               // keys per staged key/value tile
 constexpr int kMaxDepthCap = 4096;
 // Split plan for query tiles with long key ranges: the target number of
-// concurrently resident attention workgroups (2 per CU on a 256-CU MI355X),
+// concurrently resident attention workgroups (1 per CU on a 256-CU MI355X),
 // the smallest part (in 64-key tiles), the most parts per tile, and the
 // partial-result slots the workspace holds (parts x kv heads).
-constexpr int kAttnSlots = 512;
+constexpr int kAttnSlots = 256;
 constexpr int kMinPartTiles = 4;
 constexpr int kMaxSplit = 16;
-constexpr int kMaxPartSlots = 2048;
+constexpr int kMaxPartSlots = 1024;
 
 // One attention work entry: query tokens [t0, t1) of one or several
 // consecutive sibling segments, and the part [kt0, kt1) of its key-tile
