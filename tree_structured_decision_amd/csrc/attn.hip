@@ -43,10 +43,11 @@ struct AttnCfg {
   static constexpr int EPC = 16 / ESZ;                 // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                  // chunks per K/V row
   static constexpr int KS = D + EPC;                   // Ks row stride (elements)
-  // bf16: V is staged row-major [key][d] with a 288-byte pitch (4 consecutive
-  // key rows then fall on distinct LDS banks for the transposing reads);
-  // fp32: V is staged transposed [d][key].
-  static constexpr int VS = BF16 ? D + 16 : kAttnKeys + 4;
+  // bf16: V is staged row-major [key][d] with a pitch of D + 32 elements (a
+  // multiple of 64 bytes past a 128-byte period), which keeps the transposing
+  // reads free of LDS bank conflicts (measured); fp32: V is staged
+  // transposed [d][key].
+  static constexpr int VS = BF16 ? D + 32 : kAttnKeys + 4;
   static constexpr int VROWS = BF16 ? kAttnKeys : D;  // rows of the V tile in LDS
   static constexpr int NKF = BF16 ? D / 16 : D / 2;    // MFMA k-steps over D
   static constexpr int NDB = D / 32;                   // 32-row d blocks of O^T

@@ -314,12 +314,13 @@ struct ScanCfg {
   static constexpr int NSW = (BF16 ? 4 : 2) < DV / 16 ? (BF16 ? 4 : 2) : DV / 16;  // slices per workgroup
   static constexpr int NT = 64 * NSW;           // threads (one wave per slice)
   static constexpr int NG = DV / (16 * NSW);    // slice groups per head
-  // Padded row lengths of the LDS tiles (elements). The LDS serves a 64-bit
-  // read 16 lanes at a time over 32 four-byte banks: T'' and P rows of 34
-  // dwords make the 16-row fragment reads conflict-free, V rows of 40 dwords
-  // the transpose reads (4 rows x 4 columns per 16 lanes); K and Q rows of 68
-  // dwords leave both kinds of read at most 2-way.
-  static constexpr int LDK = DK + G::PAD;                 // K, Q tiles
+  // Padded row lengths of the LDS tiles (elements), chosen from measured LDS
+  // bank conflicts on gfx950 (the bank pattern repeats every 64 bf16): rows
+  // of 4 or 12 (mod 64) make the 16-row fragment reads (ld_perm) conflict-free,
+  // rows of 16 (mod 64) the transpose reads; K (read both ways) uses 12, which
+  // leaves the transpose reads nearly free. Rows that are not a multiple of 16
+  // bytes are staged with 8-byte stores.
+  static constexpr int LDK = DK + (BF16 ? 12 : G::PAD);   // K, Q tiles
   static constexpr int LDT = CH + (BF16 ? 4 : G::PAD);    // T'', P tiles
   static constexpr int VW = 16 * NSW;                     // v columns of the group
   static constexpr int LDV = VW + (BF16 ? 16 : G::PAD);
@@ -351,10 +352,18 @@ template <bool BF16, int W>
 __device__ __forceinline__ int tile_off(int r, int col) {
   return r * W + col;
 }
-// Stores one 16-byte group (8 bf16 / 4 fp32 elements starting at column col).
+// Stores one 16-byte group (8 bf16 / 4 fp32 elements starting at column col);
+// as two 8-byte stores when rows are not 16-byte aligned.
 template <bool BF16, int W>
 __device__ __forceinline__ void tile_put16(typename GT<BF16>::E* tile, int r, int col, u32x4_t v) {
-  *(u32x4_t*)(tile + r * W + col) = v;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr ((W * sizeof(typename GT<BF16>::E)) % 16 == 0) {
+    *(u32x4_t*)(tile + r * W + col) = v;
+  } else {
+    constexpr int HALF = 8 / sizeof(typename GT<BF16>::E);
+    *(u32x2*)(tile + r * W + col) = u32x2{v.x, v.y};
+    *(u32x2*)(tile + r * W + col + HALF) = u32x2{v.z, v.w};
+  }
 }
 
 template <bool BF16, int DK>
