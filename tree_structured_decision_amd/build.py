@@ -1,8 +1,10 @@
 """Build libforkattn.so (HIP, gfx950) in-tree.
 
 Every source in csrc/ is compiled with hipcc for gfx950 only, with packed-FP32
-instruction selection disabled (``-packed-fp32-ops``), then linked into
-``libforkattn.so`` next to this file.
+instruction selection disabled (``-packed-fp32-ops``) and MFMA accumulators
+kept in architectural VGPRs (``-amdgpu-mfma-vgpr-form``: the scan kernels read
+their accumulators with VALU every chunk, and accumulators held in AGPRs would
+cost a copy each way), then linked into ``libforkattn.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -31,6 +33,7 @@ def hipcc() -> str:
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument"]
 
 

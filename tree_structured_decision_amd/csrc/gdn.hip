@@ -490,18 +490,28 @@ __device__ __forceinline__ void stage_rest(const ScanTiles<BF16, DK>& b, const S
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Reduction step f of accumulator blocks X[] as an operand fragment (hi part,
-// and in bf16 mode the lo part x - hi).
+// and in bf16 mode the lo part x - hi). Values are converted in pairs: one
+// packed conversion gives both hi halves, whose float values are the packed
+// word shifted / masked, so a pair costs 6 VALU operations.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 template <bool BF16>
 __device__ __forceinline__ void reg_frag(const f32x4_t* X, int f, typename GT<BF16>::F& hi,
                                          typename GT<BF16>::F& lo) {
   if constexpr (BF16) {
+    u32x4_t h, l;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = X[2 * f + (j >> 2)][j & 3];
-      const __bf16 hb = (__bf16)x;
-      hi[j] = hb;
-      lo[j] = (__bf16)(x - (float)hb);
+    for (int p = 0; p < 4; ++p) {
+      const float a = X[2 * f + (p >> 1)][2 * (p & 1)], b = X[2 * f + (p >> 1)][2 * (p & 1) + 1];
+      const unsigned w = pack_bf16x2(a, b);
+      h[p] = w;
+      l[p] = pack_bf16x2(a - __uint_as_float(w << 16), b - __uint_as_float(w & 0xffff0000u));
     }
+    hi = __builtin_bit_cast(bf16x8_t, h);
+    lo = __builtin_bit_cast(bf16x8_t, l);
   } else {
     hi = X[f >> 2][f & 3];
     lo = 0.f;
