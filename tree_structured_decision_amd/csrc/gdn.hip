@@ -65,10 +65,6 @@ __device__ __forceinline__ unsigned short bf16_bits(float x) {
 __device__ __forceinline__ float bf16_val(unsigned short u) {
   return __uint_as_float((unsigned)u << 16);
 }
-__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
-  hi = bf16_bits(x);
-  lo = bf16_bits(x - bf16_val(hi));
-}
 
 // A/B fragment of an operand stored row-major with k contiguous: lane holds
 // (row, k0 + slice) where slice = lane / 16.
@@ -94,18 +90,10 @@ __device__ __forceinline__ f32x4_t mma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Store a computed fp32 value as a "split" operand element.
-template <bool BF16>
-__device__ __forceinline__ void put_split(typename GT<BF16>::E* hi, typename GT<BF16>::E* lo, int idx,
-                                          float x) {
-  if constexpr (BF16) {
-    unsigned short h, l;
-    split_bf16(x, h, l);
-    hi[idx] = h;
-    lo[idx] = l;
-  } else {
-    hi[idx] = x;
-  }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 struct GdnArgs {
@@ -133,8 +121,12 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
   using E = typename G::E;
   constexpr int LDK = DK + G::PAD;
   constexpr int LDA = CH + 4;  // fp32 64x64 tiles
-  __shared__ __attribute__((aligned(16))) E Ks[CH * LDK];
-  __shared__ __attribute__((aligned(16))) E Qs[CH * LDK];
+  // K and Q tiles; once the products are formed, the same bytes hold P (fp32)
+  constexpr size_t KQ_BYTES = 2 * CH * LDK * sizeof(E);
+  constexpr size_t KQP_BYTES = KQ_BYTES > CH * LDA * 4 ? KQ_BYTES : CH * LDA * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char kqp[KQP_BYTES];
+  E* Ks = (E*)kqp;
+  E* Qs = Ks + CH * LDK;
   __shared__ float As[CH * LDA];
   __shared__ float Ts[CH * LDA];
   __shared__ float Zs[4][16 * 20];
@@ -205,27 +197,32 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
     __syncthreads();
     if (item + (int)gridDim.x < nchunks * H) prep_load(item + gridDim.x);
 
-    // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal)
+    // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal).
+    // P is staged in LDS over the K/Q tiles (dead once every wave has its
+    // products) and written out below in 16-byte groups.
+    float* Ps = (float*)kqp;
     {
-      E* Ph = (E*)(wsb + kWsPlane);
-      E* Pl = BF16 ? (E*)(wsb + kWsPlane) + CH * CH : nullptr;
+      f32x4_t kk[4], qk[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        f32x4_t kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+        kk[J] = qk[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += G::KSTEP) {
           const typename G::F bK = ld_rowk<BF16>(Ks, LDK, 16 * J + c16, k0, q4);
-          kk = mma<BF16>(ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4), bK, kk);
-          qk = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk);
+          kk[J] = mma<BF16>(ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4), bK, kk[J]);
+          qk[J] = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk[J]);
         }
+      }
+      __syncthreads();  // every wave is done reading Ks / Qs
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * w + 4 * q4 + r, j = 16 * J + c16;
           const float dec = j <= i ? __expf(gs[i] - gs[j]) : 0.f;
-          As[i * LDA + j] = j < i ? bs[i] * dec * kk[r] : 0.f;
-          put_split<BF16>(Ph, Pl, i * CH + j, dec * qk[r]);
+          As[i * LDA + j] = j < i ? bs[i] * dec * kk[J][r] : 0.f;
+          Ps[i * LDA + j] = dec * qk[J][r];
         }
-      }
     }
     __syncthreads();
 
@@ -272,13 +269,44 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
       __syncthreads();
     }
 
-    // T'' = T diag(b) -> workspace
+    // T'' = T diag(b) and P -> workspace, 8 consecutive elements of a row per
+    // task: bf16 hi and lo planes as one 16-byte store each (fp32: two)
     {
-      E* Th = (E*)wsb;
-      E* Tl = BF16 ? (E*)wsb + CH * CH : nullptr;
-      for (int idx = tid; idx < CH * CH; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        put_split<BF16>(Th, Tl, idx, Ts[i * LDA + j] * bs[j]);
+#pragma unroll
+      for (int k = 0; k < CH * CH / 8 / 256; ++k) {
+        const int idx8 = tid + 256 * k, i = idx8 >> 3, j0 = (idx8 & 7) * 8;
+        float tv[8], pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          tv[e] = Ts[i * LDA + j0 + e] * bs[j0 + e];
+          pv[e] = Ps[i * LDA + j0 + e];
+        }
+        const size_t off = (size_t)i * CH + j0;  // element offset in a 64 x 64 plane
+        if constexpr (BF16) {
+          u32x4_t th, tlo, ph, plo;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const unsigned wt = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
+            th[q] = wt;
+            tlo[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wt << 16), tv[2 * q + 1] - __uint_as_float(wt & 0xffff0000u));
+            const unsigned wp = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+            ph[q] = wp;
+            plo[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(wp << 16), pv[2 * q + 1] - __uint_as_float(wp & 0xffff0000u));
+          }
+          unsigned short* Tw = (unsigned short*)wsb;
+          unsigned short* Pw = (unsigned short*)(wsb + kWsPlane);
+          *(u32x4_t*)(Tw + off) = th;
+          *(u32x4_t*)(Tw + CH * CH + off) = tlo;
+          *(u32x4_t*)(Pw + off) = ph;
+          *(u32x4_t*)(Pw + CH * CH + off) = plo;
+        } else {
+          float* Tw = (float*)wsb;
+          float* Pw = (float*)(wsb + kWsPlane);
+          *(f32x4_t*)(Tw + off) = f32x4_t{tv[0], tv[1], tv[2], tv[3]};
+          *(f32x4_t*)(Tw + off + 4) = f32x4_t{tv[4], tv[5], tv[6], tv[7]};
+          *(f32x4_t*)(Pw + off) = f32x4_t{pv[0], pv[1], pv[2], pv[3]};
+          *(f32x4_t*)(Pw + off + 4) = f32x4_t{pv[4], pv[5], pv[6], pv[7]};
+        }
       }
     }
   }
@@ -493,11 +521,6 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // and in bf16 mode the lo part x - hi). Values are converted in pairs: one
 // packed conversion gives both hi halves, whose float values are the packed
 // word shifted / masked, so a pair costs 6 VALU operations.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 template <bool BF16>
 __device__ __forceinline__ void reg_frag(const f32x4_t* X, int f, typename GT<BF16>::F& hi,
                                          typename GT<BF16>::F& lo) {
