@@ -260,8 +260,8 @@ def main():
                     help="finish with three plain 512 MiB device copies (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the path's multi-GPU sharding is a design note, not an implementation.",
+        print(f"bench.py: the hot path runs on one GPU (got --gpus {args.gpus}); "
+              "sharding across GPUs is described in the design notes, not implemented.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -47,7 +47,7 @@ typedef enum {
   FORK_OK = 0,
   FORK_E_ARG = -1,          /* null pointer, bad size, inconsistent arguments */
   FORK_E_TREE = -2,         /* invalid tree: parent >= s or < -1, seg_len < 1, too deep */
-  FORK_E_UNSUPPORTED = -3,  /* head size or dtype this build has no kernel for */
+  FORK_E_UNSUPPORTED = -3,  /* head size or dtype with no kernel in the library */
   FORK_E_WORKSPACE = -4,    /* workspace or staging buffer too small */
   FORK_E_CAPACITY = -5,     /* tree larger than the capacities the blob was sized for */
   FORK_E_HIP = -6           /* a HIP runtime call failed */
@@ -145,7 +145,9 @@ fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream
  * the gqa_group the metadata was built for, and Hkv its kv_heads when that is
  * nonzero. The workspace holds fp32 partial results of split query tiles
  * (kv_heads != 0): fork_attn_workspace gives its size for the blob's
- * capacities; it may be null when that size is 0.
+ * capacities; it may be null when that size is 0. Work is handed out from
+ * counters kept in the metadata blob (zero after fork_meta_build, reset by
+ * each launch): two attention launches on one blob must not overlap in time.
  */
 fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int32_t D,
                                 fork_dtype dt, size_t* bytes_h);
@@ -167,7 +169,7 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
  * seg_start_state [S,H,dv,dk] float32 (required: the fork copies);
  * seg_final_state [S,H,dv,dk] float32 or null. States are row-major dv x dk.
  * Supported: dk == dv in {32, 64, 128}. The workspace holds per-chunk
- * intermediates; fork_gdn_workspace sizes it for the blob's capacities.
+ * intermediates; gdn_fork_workspace sizes it for the blob's capacities.
  */
 fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv,
                                fork_dtype dt, size_t* bytes_h);
