@@ -60,7 +60,7 @@ struct AttnArgs {
   const void* v;
   void* o;
   float* lse;
-  float* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
+  unsigned char* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
   int32_t* ctr;  // the blob's work counters: next item per XCD (8), finished workgroups
   int H, Hkv, G;
   float scale_log2;  // softmax scale * log2(e)
@@ -425,20 +425,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_row = l_tot > 0.f ? m_run * 0.6931471805599453f + __logf(l_tot) : -INFINITY;
-    if (valid && tile.slot >= 0) {
-      float* part = args.ws + ((size_t)tile.slot * Hkv + g) * (kAttnRows * D + kAttnRows);
-      float* prow = part + r * D;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = 32 * db + 8 * rq + 4 * hi;
-          *(float4*)(prow + d0) = make_float4(oacc[db][4 * rq + 0] * inv, oacc[db][4 * rq + 1] * inv,
-                                              oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
-        }
-      if (hi == 0) part[kAttnRows * D + r] = lse_row;
-    } else if (valid) {
-      E* orow = O + ((size_t)t_row * H + h) * D;
+    // whole tiles store the output row; parts of a split tile store their
+    // normalised row (output dtype) and log-sum-exp into the tile's slot
+    constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;
+    unsigned char* part = tile.slot >= 0 ? args.ws + ((size_t)tile.slot * Hkv + g) * SLOT : nullptr;
+    if (valid) {
+      E* orow = tile.slot >= 0 ? (E*)part + r * D : O + ((size_t)t_row * H + h) * D;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -461,7 +453,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
             *(float4*)(orow + d0) = make_float4(v0, v1, v2, v3);
           }
         }
-      if (args.lse && hi == 0) args.lse[(size_t)t_row * H + h] = lse_row;
+      if (hi == 0) {
+        if (tile.slot >= 0)
+          ((float*)((E*)part + kAttnRows * D))[r] = lse_row;
+        else if (args.lse)
+          args.lse[(size_t)t_row * H + h] = lse_row;
+      }
     }
   }
   if (tid == 0 && atomicAdd(args.ctr + kNumXcd, 1) == (int)gridDim.x - 1) {
@@ -479,9 +476,9 @@ constexpr int kMergeRows = 16;
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
   using E = typename std::conditional<BF16, unsigned short, float>::type;
-  constexpr int PS = kAttnRows * D + kAttnRows;  // floats per partial slot
-  constexpr int NRG = kAttnRows / kMergeRows;    // row groups per tile
-  constexpr int C4 = D / 4 / 16;                 // float4 columns per thread
+  constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;  // bytes per partial slot
+  constexpr int NRG = kAttnRows / kMergeRows;  // row groups per tile
+  constexpr int C4 = D / 4 / 16;               // 4-column groups per thread
   const int nmerge = blob[MH_NMERGE];
   const int TT = blob[MH_TILE_TOKENS];
   const AttnMerge* __restrict__ merges = (const AttnMerge*)(blob + blob[MH_OFF_MERGE]);
@@ -494,13 +491,13 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
     const int r = kMergeRows * rg + rr;
     const int tl = r / G, hg = r - tl * G;
     if (tl >= TT || t0 + tl >= t1) continue;
-    const float* part0 = args.ws + ((size_t)s0 * Hkv + g) * PS;
-    const size_t pstride = (size_t)Hkv * PS;
+    const unsigned char* part0 = args.ws + ((size_t)s0 * Hkv + g) * SLOT;
+    const size_t pstride = (size_t)Hkv * SLOT;
     float lp[kMaxSplit];
     float m = -INFINITY;
 #pragma unroll
     for (int p = 0; p < kMaxSplit; ++p) {
-      lp[p] = p < np ? part0[p * pstride + kAttnRows * D + r] : -INFINITY;
+      lp[p] = p < np ? ((const float*)(part0 + p * pstride + (size_t)kAttnRows * D * sizeof(E)))[r] : -INFINITY;
       m = fmaxf(m, lp[p]);
     }
     float den = 0.f;
@@ -512,9 +509,17 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
       if (p < np) {
         const float wgt = lp[p] == -INFINITY ? 0.f : __expf(lp[p] - m);
         den += wgt;
+        const E* prow = (const E*)(part0 + p * pstride) + (size_t)r * D;
 #pragma unroll
         for (int c = 0; c < C4; ++c) {
-          const float4 x = *(const float4*)(part0 + p * pstride + (size_t)r * D + 4 * (cq + 16 * c));
+          float4 x;
+          if constexpr (BF16) {
+            const uint2 u = *(const uint2*)(prow + 4 * (cq + 16 * c));
+            x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+          } else {
+            x = *(const float4*)(prow + 4 * (cq + 16 * c));
+          }
           acc[c].x += wgt * x.x;
           acc[c].y += wgt * x.y;
           acc[c].z += wgt * x.z;
@@ -564,8 +569,8 @@ fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStrea
 
 }  // namespace
 
-size_t attn_workspace_bytes(const fork_caps& c, int D) {
-  return c.kv_heads > 0 ? (size_t)kMaxPartSlots * (kAttnRows * (size_t)D + kAttnRows) * sizeof(float) : 0;
+size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt) {
+  return c.kv_heads > 0 ? (size_t)kMaxPartSlots * attn_slot_bytes(D, dt) : 0;
 }
 
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v, void* o,
@@ -578,7 +583,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.v = v;
   a.o = o;
   a.lse = lse;
-  a.ws = (float*)ws;
+  a.ws = (unsigned char*)ws;
   a.ctr = (int32_t*)m->dev + kAttnCtrWord;
   a.H = H;
   a.Hkv = Hkv;

@@ -415,7 +415,7 @@ fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int3
   if (!bytes_h) return fail(FORK_E_ARG, "bytes_h is null");
   (void)H; (void)Hkv; (void)dt;
   if (D != 64 && D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", D);
-  *bytes_h = attn_workspace_bytes(m->caps, D);
+  *bytes_h = attn_workspace_bytes(m->caps, D, dt);
   return FORK_OK;
 }
 
@@ -435,7 +435,7 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
   if (m->caps.kv_heads != 0 && Hkv != m->caps.kv_heads)
     return fail(FORK_E_ARG, "Hkv=%d differs from the kv_heads %d the metadata was built for", Hkv,
                 m->caps.kv_heads);
-  const size_t need = attn_workspace_bytes(m->caps, D);
+  const size_t need = attn_workspace_bytes(m->caps, D, dt);
   if (need && (!ws || ws_bytes < need))
     return fail(FORK_E_WORKSPACE, "attention workspace holds %zu bytes, needs %zu", ws_bytes, need);
   return launch_attention(m, q, k, v, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);

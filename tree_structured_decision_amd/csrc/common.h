@@ -146,7 +146,12 @@ fork_status check_meta(const fork_meta* m);
 // Kernel launchers (defined with their kernels).
 fork_status launch_meta_expand(const fork_meta* m, hipStream_t stream);
 fork_status launch_dense_mask(const fork_meta* m, uint8_t* mask, hipStream_t stream);
-size_t attn_workspace_bytes(const fork_caps& c, int D);
+// Bytes of one partial-result slot of a split query tile: kAttnRows x D
+// normalised outputs in the output dtype, then kAttnRows fp32 log-sum-exps.
+inline size_t attn_slot_bytes(int D, fork_dtype dt) {
+  return (size_t)kAttnRows * D * (dt == FORK_BF16 ? 2 : 4) + (size_t)kAttnRows * 4;
+}
+size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              void* o, float* lse, int H, int Hkv, int D, float scale,
                              fork_dtype dt, void* ws, hipStream_t stream);

@@ -34,7 +34,7 @@ fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* a, void
   if (a->D != 64 && a->D != 128) return fail(FORK_E_UNSUPPORTED, "head_dim %d unsupported", a->D);
   if (m->caps.kv_heads != 0 && a->Hkv != m->caps.kv_heads)
     return fail(FORK_E_ARG, "attention kv heads do not match the metadata's kv_heads");
-  const size_t aneed = attn_workspace_bytes(m->caps, a->D);
+  const size_t aneed = attn_workspace_bytes(m->caps, a->D, a->dt);
   if (aneed && (!a->attn_ws || a->attn_ws_bytes < aneed))
     return fail(FORK_E_WORKSPACE, "attention workspace too small");
   if (a->dk != a->dv || (a->dk != 32 && a->dk != 64 && a->dk != 128))

@@ -43,7 +43,8 @@ class ForkSession:
             n = B.gdn_fork_workspace(probe, gH, dk, dv, B.FORK_BF16)
             self.gdn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
         if kv_heads and D:
-            n = B.fork_attn_workspace(probe, gqa_group * kv_heads, kv_heads, D, B.FORK_BF16)
+            # sized for fp32 partials, the larger of the two dtypes
+            n = B.fork_attn_workspace(probe, gqa_group * kv_heads, kv_heads, D, B.FORK_F32)
             if n:
                 self.attn_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
         self.graph = None
