@@ -7,12 +7,12 @@
 // exactly the softmax of an isolated forward pass.
 //
 // Work decomposition. A work item is (query tile, kv head). A query tile holds
-// up to 128 rows = tokens x GQA heads of one kv head, taken from one segment or
+// up to 256 rows = tokens x GQA heads of one kv head, taken from one segment or
 // from several consecutive short sibling segments (which share all ancestor
 // keys). The item walks the ancestor segments' key ranges (fully visible, no
 // mask except the ragged end of a range) and then its own range (masked by
 // seg_start(row) <= j <= t(row)). Every 64-key K/V tile is staged in LDS once
-// and used by all 128 rows, so a long shared prefix is read once per tile of
+// and used by all 256 rows, so a long shared prefix is read once per tile of
 // packed branch queries instead of once per branch.
 //
 // Kernel shape: 512 threads = 8 wave64s (two per SIMD, one workgroup per CU),
@@ -21,8 +21,9 @@
 // S^T = K Q^T and O^T = V^T P^T on MFMA (32x32x16 bf16, or 32x32x2 f32): with
 // keys on the MFMA M dimension, each lane holds one query row's scores in its
 // registers, so the online-softmax row max needs one cross-lane step and the
-// row sum none until the end. V is written transposed into LDS so that the
-// A operand of O^T = V^T P^T reads contiguous keys.
+// row sum none until the end. bf16 tiles arrive in LDS by DMA, row-major, and
+// the V^T operand of O^T = V^T P^T comes from transposing LDS reads; fp32
+// tiles are staged through registers, V transposed on its way to LDS.
 #include <algorithm>
 #include <type_traits>
 
@@ -37,21 +38,58 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
+constexpr int kAttnThreads = 512;  // 8 waves per workgroup, one workgroup per CU
+
 template <bool BF16, int D>
 struct AttnCfg {
   static constexpr int ESZ = BF16 ? 2 : 4;
   static constexpr int EPC = 16 / ESZ;                 // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                  // chunks per K/V row
-  static constexpr int KS = D + EPC;                   // Ks row stride (elements)
-  // bf16: V is staged row-major [key][d] with a pitch of D + 32 elements (a
-  // multiple of 64 bytes past a 128-byte period), which keeps the transposing
-  // reads free of LDS bank conflicts (measured); fp32: V is staged
-  // transposed [d][key].
-  static constexpr int VS = BF16 ? D + 32 : kAttnKeys + 4;
-  static constexpr int VROWS = BF16 ? kAttnKeys : D;  // rows of the V tile in LDS
+  // fp32 tiles: K row stride in LDS; V transposed [d][key] and its pitch
+  static constexpr int KS = D + EPC;
+  static constexpr int VS = kAttnKeys + 4;
+  static constexpr int VROWS = D;                      // rows of the fp32 V^T tile
   static constexpr int NKF = BF16 ? D / 16 : D / 2;    // MFMA k-steps over D
   static constexpr int NDB = D / 32;                   // 32-row d blocks of O^T
+  // bf16 tiles: unpadded rows of D elements (CPR 16-byte chunks), one K and
+  // one V tile per buffer
+  static constexpr int TILE_BYTES = kAttnKeys * D * ESZ;
+  static constexpr int BUF_BYTES = BF16 ? 2 * TILE_BYTES
+                                        : (kAttnKeys * KS > VROWS * VS ? kAttnKeys * KS : VROWS * VS) * ESZ;
 };
+
+// bf16 K/V tiles are written by DMA as whole 16-byte chunks, unpadded, with the
+// chunks of each row permuted so that the reads below meet no LDS bank
+// conflicts: chunk c of key row r sits at position c ^ (r mod 8) in K (8
+// consecutive rows read the same chunk) and at c ^ 2 (r mod 4) in V (4
+// consecutive rows read 2 adjacent chunks through the transposing reads).
+__device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) << 1); }
+
+// DMA of keys [j0, j0 + 64) of kv head g (rows past jmax repeat row jmax) into
+// one K/V buffer: the buffer is a sequence of 1 KB blocks, block n filled by
+// one 64-lane instruction (lane l writes 16 bytes at n * 1024 + 16 l); each
+// wave issues its share of the blocks.
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int D>
+__device__ __forceinline__ void kv_dma(unsigned char* buf, const unsigned short* __restrict__ K,
+                                       const unsigned short* __restrict__ V, int j0, int jmax, int g, int Hkv,
+                                       int wave, int lane) {
+  constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  constexpr int NBLK = kAttnKeys * D * 2 / 1024;      // 1 KB blocks per tile
+  constexpr int PER_WAVE = NBLK / (kAttnThreads / 64);
+  static_assert(PER_WAVE * (kAttnThreads / 64) == NBLK, "tile blocks must divide over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int n = wave * PER_WAVE + i;
+    const int slot = n * 64 + lane, r = slot / CPR, pos = slot % CPR;
+    const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
+    __builtin_amdgcn_global_load_lds((const void*)(K + row * D + 8 * k_chunk_pos(r, pos)),
+                                     (lds_void_t*)(buf + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos(r, pos)),
+                                     (lds_void_t*)(buf + kAttnKeys * D * 2 + n * 1024), 16, 0, 0);
+  }
+}
 
 struct AttnArgs {
   const int32_t* blob;
@@ -66,21 +104,20 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-// Key/value tile of 64 keys held in registers between its global load and
+// fp32 key/value tile of 64 keys held in registers between its global load and
 // its LDS store, so the next tile's loads are in flight while the current
-// tile is being computed.
-constexpr int kAttnThreads = 512;
-
+// tile is being computed (bf16 tiles go to LDS by DMA instead).
 template <bool BF16, int D>
 struct KVRegs {
+  static_assert(!BF16, "bf16 tiles are staged by DMA");
   using C = AttnCfg<BF16, D>;
-  static constexpr int KT = kAttnKeys * C::CPR / kAttnThreads;  // 16-byte K (and bf16 V) loads per thread
+  static constexpr int KT = kAttnKeys * C::CPR / kAttnThreads;  // 16-byte K loads per thread
   // fp32 V is transposed on its way to LDS, in tasks of 4 keys x 16 bytes
   static constexpr int VTASKS = (kAttnKeys / 4) * C::CPR;
-  static constexpr int VT = BF16 ? 1 : (VTASKS + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int VT = (VTASKS + kAttnThreads - 1) / kAttnThreads;
   static_assert(KT * kAttnThreads == kAttnKeys * C::CPR, "K tile loads must divide evenly");
   u32x4_t k[KT];
-  u32x4_t v[BF16 ? KT : VT][BF16 ? 1 : 4];
+  u32x4_t v[VT][4];
 };
 
 // Global loads of keys [j0, j0 + 64) of kv head g; rows past `jmax` repeat
@@ -97,9 +134,8 @@ __device__ __forceinline__ void kv_load(KVRegs<BF16, D>& r, const E* __restrict_
     const int row = task / C::CPR, ch = task % C::CPR;
     const int j = min(j0 + row, jmax);
     r.k[i] = *(const u32x4_t*)(K + ((size_t)j * Hkv + g) * D + ch * C::EPC);
-    if constexpr (BF16) r.v[i][0] = *(const u32x4_t*)(V + ((size_t)j * Hkv + g) * D + ch * C::EPC);
   }
-  if constexpr (!BF16) {
+  {
 #pragma unroll
     for (int i = 0; i < R::VT; ++i) {
       const int task = tid + kAttnThreads * i;
@@ -115,8 +151,7 @@ __device__ __forceinline__ void kv_load(KVRegs<BF16, D>& r, const E* __restrict_
   }
 }
 
-// LDS stores of a loaded tile: K row-major into Ks; V row-major (bf16) or
-// transposed (fp32) into Vt.
+// LDS stores of a loaded fp32 tile: K row-major into Ks, V transposed into Vt.
 template <bool BF16, int D, typename E>
 __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict__ Ks,
                                          E* __restrict__ Vt, int tid) {
@@ -127,9 +162,8 @@ __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict
     const int task = tid + kAttnThreads * i;
     const int row = task / C::CPR, ch = task % C::CPR;
     *(u32x4_t*)(Ks + row * C::KS + ch * C::EPC) = r.k[i];
-    if constexpr (BF16) *(u32x4_t*)(Vt + row * C::VS + ch * C::EPC) = r.v[i][0];
   }
-  if constexpr (!BF16) {
+  {
 #pragma unroll
     for (int i2 = 0; i2 < R::VT; ++i2) {
       const int task = tid + kAttnThreads * i2;
@@ -220,8 +254,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
   using C = AttnCfg<BF16, D>;
   using E = typename std::conditional<BF16, unsigned short, float>::type;
   using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
-  __shared__ __attribute__((aligned(16))) E Ks[kAttnKeys * C::KS];
-  __shared__ __attribute__((aligned(16))) E Vt[C::VROWS * C::VS];
+  // bf16: three K/V tile buffers (static arrays, so the compiler can tell the
+  // buffer being read from the ones being filled by DMA); fp32: one K tile in
+  // lds0 and the transposed V tile in lds1.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[BF16 ? C::BUF_BYTES : 16];
 
   const int ntiles = blob[MH_NTILES];
   const int TT = blob[MH_TILE_TOKENS];
@@ -294,83 +332,90 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
     // compute one staged 64-key tile of range [j0, hi_); own == tree-masked own range
-    auto kv_compute = [&](int j0, int hi_, bool own) {
-
+    auto kv_compute = [&](const E* __restrict__ Ks, const E* __restrict__ Vt, int j0, int hi_, bool own) {
+      // The 64-key tile is processed as two 32-key halves, software-pipelined
+      // so that MFMA work and softmax VALU work of different halves sit in the
+      // same scheduling group: QK(0) | QK(1) + softmax(0) | PV(0) + softmax(1)
+      // | PV(1). With both waves of a SIMD in step, this is what keeps the
+      // matrix core busy while the scores are exponentiated.
+      const bool need_mask = own ? ((tile.info & kTileMulti) != 0 || j0 + kAttnKeys > tile.t0)
+                                 : (j0 + kAttnKeys > hi_);
       f32x16_t s[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
+      auto qk = [&](int b) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < C::NKF; ++ks) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int ks = 0; ks < C::NKF; ++ks) {
           if constexpr (BF16) {
-            const bf16x8_t a = *(const bf16x8_t*)(Ks + (32 * b + l32) * C::KS + 16 * ks + 8 * hi);
+            const int kr = 32 * b + l32;
+            const bf16x8_t a = *(const bf16x8_t*)(Ks + kr * D + 8 * k_chunk_pos(kr, 2 * ks + hi));
             s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[b], 0, 0, 0);
           } else {
             const float a = Ks[(32 * b + l32) * C::KS + 2 * ks + hi];
             s[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[ks], s[b], 0, 0, 0);
           }
         }
-      }
-
-      // Online softmax in log2 units, p = exp2(s * c - m) with c = scale * log2(e).
-      // A lane raises its running max m only when the tile's max exceeds it by
-      // more than 8 (a factor of 256); otherwise the stale max is kept. That is
-      // exact (numerator and denominator share m), keeps p <= 256, and skips
-      // rescaling the accumulators unless some lane of the wave raised its max.
-      const bool need_mask = own ? ((tile.info & kTileMulti) != 0 || j0 + kAttnKeys > tile.t0)
-                                 : (j0 + kAttnKeys > hi_);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
+      };
+      // Online softmax in log2 units, p = exp2(s * c - m) with c = scale * log2(e),
+      // one 32-key half at a time, in two parts. sm_max: tree mask, row max and
+      // the running-max update (a lane raises its max m only when the half's
+      // max exceeds it by more than 8, a factor of 256; otherwise the stale max
+      // is kept, which is exact since numerator and denominator share m, keeps
+      // p <= 256 and makes rescaling rare). sm_exp: the exponentials, row sums
+      // and bf16 packing, free of branches so that they can share a
+      // scheduling group with MFMAs.
+      float alpha[2];
+      bool grew[2];
+      auto sm_max = [&](int b) {
+        if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = j0 + 32 * b + 8 * (i >> 2) + 4 * hi + (i & 3);
             const bool vis = (j < hi_) & (!own | ((j >= lo_row) & (j <= t_row)));
             s[b][i] = vis ? s[b][i] : -INFINITY;
           }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * args.scale_log2;
-      const bool grow = mx > m_run + 8.f;
-      float alpha = 1.f;
-      if (grow) {
-        alpha = __builtin_amdgcn_exp2f(m_run - mx);
-        m_run = mx;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * args.scale_log2;
+        const bool grow = mx > m_run + 8.f;
+        alpha[b] = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        m_run = grow ? mx : m_run;
+        grew[b] = __any(grow);
+        l_run *= alpha[b];
+      };
+      typename std::conditional<BF16, bf16x8_t, float>::type pb[2][2];
+      auto sm_exp = [&](int b) {
+        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[b][i], args.scale_log2, mneg));
           s[b][i] = p;
           psum += p;
         }
-      l_run = l_run * alpha + psum;
-
-      // O^T += V^T P^T
+        l_run += psum;
+        if constexpr (BF16) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) pb[b][hf][jj] = (__bf16)s[b][8 * hf + jj];
+        }
+      };
+      auto rescale = [&](int b) {
+        if (grew[b]) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha[b];
+        }
+      };
+      // O^T += V^T P^T for one 32-key half
+      auto pv = [&](int b) {
         if constexpr (BF16) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            bf16x8_t pb;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) pb[jj] = (__bf16)s[b][8 * hf + jj];
             // A = V^T fragments by transposing LDS reads: within each group of
             // 16 lanes, lane L points at key row (L / 4) of a 4-key block and
             // d column 4 (L % 4); lane i of the group receives the 4 keys at
@@ -381,13 +426,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
               const int col = 32 * db + 16 * (g16 & 1) + 4 * (L16 & 3);
-              const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + krow * C::VS + col));
+              // col = 8 * chunk + 4 * half; krow and krow + 8 agree mod 4
+              const int vpos = 8 * v_chunk_pos(krow, col >> 3) + (col & 7);
+              const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + krow * D + vpos));
               const s16x4_t hi4 =
-                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + (krow + 8) * C::VS + col));
+                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + (krow + 8) * D + vpos));
               typedef short s16x8_t __attribute__((ext_vector_type(8)));
               const s16x8_t w8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
               const bf16x8_t va = __builtin_bit_cast(bf16x8_t, w8);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[b][hf], oacc[db], 0, 0, 0);
             }
           }
         } else {
@@ -401,23 +448,106 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
             }
           }
         }
+      };
+      // Pipeline over the two halves. The running max may rise at either half:
+      // half 0's rise rescales the accumulators before anything of this tile is
+      // added; half 1's rise rescales them after half 0's products are in, so
+      // that both halves' products end up relative to the final max. Scheduling
+      // groups (masks: 0x008 MFMA, 0x002 VALU, 0x100 LDS read) alternate one
+      // MFMA with a run of VALU instructions in the two mixed groups.
+      qk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      sm_max(0);
+      rescale(0);
+      __builtin_amdgcn_sched_barrier(0);
+      qk(1);
+      sm_exp(0);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < C::NKF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      sm_max(1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(0);
+      sm_exp(1);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 2 * C::NDB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      rescale(1);
+      pv(1);
     };
 
-    // software pipeline: tile i+1 is loaded into registers while tile i computes
     TileIter it;
     iter_init(it, tile, parent, seg_start, seg_len);
-    KVRegs<BF16, D> rg;
-    kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
-    while (!it.done) {
-      const int j0 = it.j0, hi_ = it.hi;
-      const bool own = it.own;
-      __syncthreads();  // every wave is done with the previous tile
-      kv_store<BF16, D, E>(rg, Ks, Vt, tid);
-      __syncthreads();
-      iter_next(it, tile, parent, seg_start, seg_len);
-      if (!it.done) kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
-      kv_compute(j0, hi_, own);
+    if constexpr (BF16) {
+      // Software pipeline over three LDS buffers: the DMAs of tiles i+1 and
+      // i+2 are in flight while tile i computes. Per tile: wait for this
+      // wave's DMA of tile i (its DMA of tile i+1 may stay in flight), one
+      // barrier (every wave's DMA of tile i landed; every wave is done with
+      // tile i-1, whose buffer tile i+2 then fills), issue that DMA, compute.
+      // The loop is unrolled by three so that each step reads and fills fixed
+      // buffers.
+      constexpr int DMA_PER_TILE = 2 * (kAttnKeys * D * 2 / 1024) / (kAttnThreads / 64);
+      static_assert(DMA_PER_TILE < 16, "vmcnt field");
+      __syncthreads();  // the previous item's last tiles are no longer read
+      int pj[3], ph[3];
+      bool po[3];
+      int nq = 0;  // tiles issued and not yet computed
+      auto issue = [&](unsigned char* buf, int slot) {
+        if (it.done) return;
+        pj[slot] = it.j0;
+        ph[slot] = it.hi;
+        po[slot] = it.own;
+        kv_dma<D>(buf, K, V, it.j0, it.hi - 1, g, Hkv, wave, lane);
+        ++nq;
+        iter_next(it, tile, parent, seg_start, seg_len);
+      };
+      issue(lds0, 0);
+      issue(lds1, 1);
+      auto step = [&](unsigned char* cur, int slot, unsigned char* fill, int fslot) {
+        if (nq > 1)
+          __builtin_amdgcn_s_waitcnt(0x0f70 | DMA_PER_TILE);  // vmcnt: tile i landed, i+1 may fly
+        else
+          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __syncthreads();
+        --nq;
+        issue(fill, fslot);
+        kv_compute((const E*)cur, (const E*)(cur + C::TILE_BYTES), pj[slot], ph[slot], po[slot]);
+      };
+      while (nq > 0) {
+        step(lds0, 0, lds2, 2);
+        if (nq == 0) break;
+        step(lds1, 1, lds0, 0);
+        if (nq == 0) break;
+        step(lds2, 2, lds1, 1);
+      }
+    } else {
+      // fp32: registers hold tile i+1 while tile i computes
+      E* Ks = (E*)lds0;
+      E* Vt = (E*)lds1;
+      KVRegs<BF16, D> rg;
+      kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+      while (!it.done) {
+        const int j0 = it.j0, hi_ = it.hi;
+        const bool own = it.own;
+        __syncthreads();  // every wave is done with the previous tile
+        kv_store<BF16, D, E>(rg, Ks, Vt, tid);
+        __syncthreads();
+        iter_next(it, tile, parent, seg_start, seg_len);
+        if (!it.done) kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+        kv_compute(Ks, Vt, j0, hi_, own);
+      }
     }
 
     // finalize: normalise; whole tiles store the output, parts of a split tile
