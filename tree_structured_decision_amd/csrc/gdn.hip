@@ -19,11 +19,13 @@
 // Kernels:
 //   gdn_prep: one workgroup per (chunk, head), fully parallel. Computes g,
 //     T'' and Q K^T * Gamma into the workspace.
-//   gdn_scan: one launch per tree depth. A work item is (segment, head,
-//     16-row slice of the state); rows of the state evolve independently, so
-//     slices need no communication. It walks its segment's chunks serially
-//     and at the end writes its final state into the first child's start
-//     slot; the other children copy it from there at the next depth.
+//   gdn_coop (bf16) / gdn_scan (fp32): one launch per tree depth. A work
+//     item is (segment, head, slice of state rows); rows of the state evolve
+//     independently, so slices need no communication. It walks its segment's
+//     chunks serially and at the end writes its final state into the first
+//     child's start slot; the other children copy it from there at the next
+//     depth. gdn_coop splits each chunk of a 16-row slice over several waves
+//     (short serial chain per chunk); gdn_scan runs one wave per slice.
 //
 // Precision. In bf16 mode q/k/v are exact bf16, so products with them as the
 // only rounded-free operands use one bf16 MFMA; operands that are computed in
@@ -45,10 +47,24 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int CH = kChunk;  // 64
 constexpr int VSL = 16;     // state rows per scan work item
 
-// Per (chunk, head) workspace block: T'' [64x64] and P = QK^T*Gamma [64x64],
-// each as bf16 hi/lo planes (bf16 mode) or one fp32 plane (fp32 mode), then g.
-constexpr size_t kWsPlane = (size_t)CH * CH * 4;  // bytes of one 64x64 operand
-constexpr size_t kWsChunk = 2 * kWsPlane + 256;   // T'', P, g (64 floats)
+// Per (chunk, head) workspace block.
+// fp32 mode: T'' [64x64] and P = QK^T*Gamma [64x64] as row-major fp32 planes,
+// then g (64 floats).
+// bf16 mode: T'' and P as MFMA operand fragments, then gamma and gamma_C /
+// gamma (64 floats each). A fragment is 1 KB: lane l of a 16x16x32 product
+// holds 8 bf16 of row 16 I + l % 16 at columns 32 kf + 4 q + {0..3} and
+// 32 kf + 16 + 4 q + {0..3}, q = l / 16 (the reduction order of the scan).
+// Both matrices are lower triangular, so row block I keeps only its first
+// I / 2 + 1 column steps: 6 fragments, each as a hi and a lo plane
+// (fragment (I, kf) at index ((tri(I) + kf) * 2 + plane)).
+constexpr size_t kWsPlane = (size_t)CH * CH * 4;  // bytes of one 64x64 fp32 operand
+constexpr size_t kWsChunk = 2 * kWsPlane + 256;   // the larger of the two layouts
+constexpr int kNtri = 6;                          // fragments of a lower-triangular 64x64 operand
+__host__ __device__ constexpr int frag_nk(int I) { return I / 2 + 1; }
+__host__ __device__ constexpr int frag_tri(int I) { return I < 3 ? I : 4; }
+constexpr size_t kWsFrag = (size_t)kNtri * 2 * 1024;  // bytes of T'' (or P) fragments
+constexpr size_t kWsGam = 2 * kWsFrag;                // gamma, then gamma_C / gamma
+static_assert(kWsGam + 1024 <= kWsChunk, "bf16 workspace layout fits the block (gates staged as 1 KB)");
 
 template <bool BF16>
 struct GT {
@@ -190,7 +206,13 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
       }
       gs[i] = la;
       bs[i] = i < len ? rb : 0.f;
-      ((float*)(wsb + 2 * kWsPlane))[i] = la;
+      if constexpr (BF16) {
+        const float gl = __shfl(la, CH - 1);
+        ((float*)(wsb + kWsGam))[i] = __expf(la);
+        ((float*)(wsb + kWsGam))[CH + i] = __expf(gl - la);
+      } else {
+        ((float*)(wsb + 2 * kWsPlane))[i] = la;
+      }
     }
     // zero Ts (upper blocks stay zero)
     for (int i = tid; i < CH * LDA; i += 256) Ts[i] = 0.f;
@@ -269,9 +291,39 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
       __syncthreads();
     }
 
-    // T'' = T diag(b) and P -> workspace, 8 consecutive elements of a row per
-    // task: bf16 hi and lo planes as one 16-byte store each (fp32: two)
-    {
+    // T'' = T diag(b) and P -> workspace
+    if constexpr (BF16) {
+      // operand fragments, hi and lo planes, one 16-byte group per task
+      for (int task = tid; task < kNtri * 64; task += 256) {
+        const int bi = task >> 6, l = task & 63;
+        const int I = bi < 3 ? bi : (bi == 3 ? 2 : 3), kf = bi - frag_tri(I);
+        const int i = 16 * I + (l & 15), j0 = 32 * kf + 4 * (l >> 4);
+        float tv[8], pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + (e & 3) + 16 * (e >> 2);
+          tv[e] = Ts[i * LDA + j] * bs[j];
+          pv[e] = Ps[i * LDA + j];
+        }
+        u32x4_t th, tlo, ph, plo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned wt = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
+          th[q] = wt;
+          tlo[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wt << 16), tv[2 * q + 1] - __uint_as_float(wt & 0xffff0000u));
+          const unsigned wp = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+          ph[q] = wp;
+          plo[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(wp << 16), pv[2 * q + 1] - __uint_as_float(wp & 0xffff0000u));
+        }
+        u32x4_t* Tw = (u32x4_t*)wsb;
+        u32x4_t* Pw = (u32x4_t*)(wsb + kWsFrag);
+        Tw[(2 * bi) * 64 + l] = th;
+        Tw[(2 * bi + 1) * 64 + l] = tlo;
+        Pw[(2 * bi) * 64 + l] = ph;
+        Pw[(2 * bi + 1) * 64 + l] = plo;
+      }
+    } else {
+      // row-major fp32 planes, 8 consecutive elements of a row per task
 #pragma unroll
       for (int k = 0; k < CH * CH / 8 / 256; ++k) {
         const int idx8 = tid + 256 * k, i = idx8 >> 3, j0 = (idx8 & 7) * 8;
@@ -282,31 +334,12 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
           pv[e] = Ps[i * LDA + j0 + e];
         }
         const size_t off = (size_t)i * CH + j0;  // element offset in a 64 x 64 plane
-        if constexpr (BF16) {
-          u32x4_t th, tlo, ph, plo;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const unsigned wt = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
-            th[q] = wt;
-            tlo[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wt << 16), tv[2 * q + 1] - __uint_as_float(wt & 0xffff0000u));
-            const unsigned wp = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
-            ph[q] = wp;
-            plo[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(wp << 16), pv[2 * q + 1] - __uint_as_float(wp & 0xffff0000u));
-          }
-          unsigned short* Tw = (unsigned short*)wsb;
-          unsigned short* Pw = (unsigned short*)(wsb + kWsPlane);
-          *(u32x4_t*)(Tw + off) = th;
-          *(u32x4_t*)(Tw + CH * CH + off) = tlo;
-          *(u32x4_t*)(Pw + off) = ph;
-          *(u32x4_t*)(Pw + CH * CH + off) = plo;
-        } else {
-          float* Tw = (float*)wsb;
-          float* Pw = (float*)(wsb + kWsPlane);
-          *(f32x4_t*)(Tw + off) = f32x4_t{tv[0], tv[1], tv[2], tv[3]};
-          *(f32x4_t*)(Tw + off + 4) = f32x4_t{tv[4], tv[5], tv[6], tv[7]};
-          *(f32x4_t*)(Pw + off) = f32x4_t{pv[0], pv[1], pv[2], pv[3]};
-          *(f32x4_t*)(Pw + off + 4) = f32x4_t{pv[4], pv[5], pv[6], pv[7]};
-        }
+        float* Tw = (float*)wsb;
+        float* Pw = (float*)(wsb + kWsPlane);
+        *(f32x4_t*)(Tw + off) = f32x4_t{tv[0], tv[1], tv[2], tv[3]};
+        *(f32x4_t*)(Tw + off + 4) = f32x4_t{tv[4], tv[5], tv[6], tv[7]};
+        *(f32x4_t*)(Pw + off) = f32x4_t{pv[0], pv[1], pv[2], pv[3]};
+        *(f32x4_t*)(Pw + off + 4) = f32x4_t{pv[4], pv[5], pv[6], pv[7]};
       }
     }
   }
@@ -882,6 +915,508 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 scan, chunk-cooperative with helper waves. One launch per tree depth;
+// a work item is (segment, head, 16-row slice of the state). Its chunks run
+// on a workgroup of 2 NW waves, NW = DK / 32:
+//   chain wave w owns state columns [32 w, 32 w + 32) (two 16x16 blocks of
+//   S^T, the reduction step w of every product over d) and token blocks
+//   w, w + NW, ... (16 rows of the chunk each); it runs the serial part:
+//     (1) X = K S^T, R = V - gamma X         -> exchange (hi, lo)
+//     (3) U = T'' R, U' = diag(gamma_C / gamma) U   -> exchange (hi, lo of both)
+//     (5) S^T = gamma_C S^T + K^T U'         -> exchange (next chunk's S)
+//   helper wave v loads the next task's operands into LDS and computes the
+//   outputs of token blocks v, v + NW, ...:
+//     (4) O^T = scale (S Q^T * gamma + U^T P^T).
+// Three workgroup barriers per chunk separate the exchanges. Each product's
+// reduction index runs in the order of a 16x16 accumulator (lane group q
+// holds rows 4q..4q+3), as written by the exchanges and by the prep kernel's
+// fragments; K and Q are read in the same order (two 8-byte reads, or two
+// transposing reads for K^T).
+// The operands of a chunk (K, Q, T'' and P fragments, the slice's v columns,
+// the decays, and at a segment's first chunk its start state) are fetched by
+// buffer loads straight into LDS, double-buffered: the next task (the next
+// chunk, or the first chunk of the workgroup's next item) loads while the
+// current one computes, its loads spread over the three phases. The buffer
+// range of K, Q and V ends at the chunk's last token, so rows past a ragged
+// chunk read as zeros; a missing start state (a root without root_state) is
+// an empty range and reads as zeros too.
+template <int DK>
+struct CoopCfg {
+  static constexpr int NW = DK / 32;           // chain waves (and helper waves)
+  static constexpr int NT = 128 * NW;
+  static constexpr int TB = 4 / NW;            // token blocks per wave
+  static constexpr int CPR = DK / 8;           // 16-byte chunks per K/Q row
+  static constexpr int NKD = DK / 32;          // reduction steps over d
+  static constexpr int KQ = CH * DK * 2;       // bytes of the K (or Q) tile
+  static constexpr int FR = (int)kWsFrag;      // T'' (or P) fragments
+  static constexpr int VB = CH * 16 * 2;       // v columns of the slice, 64 tokens
+  static constexpr int GB = 1024;              // gamma, gamma_C / gamma (one 1 KB load)
+  static constexpr int SB = 16 * DK * 4;       // start state of the slice (fp32)
+  static constexpr int OQ = KQ, OT = 2 * KQ, OP = OT + FR, OV = OP + FR, OG = OV + VB, OS = OG + GB;
+  static constexpr int BUF = OS + SB;
+  static constexpr int KJ = KQ / 1024;         // 1 KB loads of K (and of Q)
+  static constexpr int FJ = FR / 1024;         // of T'' (and of P)
+  static constexpr int SJ = SB / 1024;         // of the start state
+  static_assert(KJ / NW == 4 && FJ % NW == 0 && SJ % NW == 0, "load split over the helper waves");
+  static constexpr int XB = 2 * NKD * 64 * 16 + 2 * 4 * 64 * 8 + 4 * 4 * 64 * 8 + 4 * 64 * 16;  // exchanges
+  static_assert(2 * BUF + XB <= 160 * 1024, "LDS");
+};
+
+// K/Q tiles in LDS: rows of DK bf16, unpadded; the 16-byte chunks of row r
+// are permuted (chunk c at position c ^ kq_swz(r)) so that the row reads (16
+// rows, one column) meet at most 2-way bank conflicts and the transposing
+// reads (4 rows, 32 bytes) none.
+__device__ __forceinline__ int kq_swz(int r, int cpr) { return (((r & 3) << 1) | ((r >> 2) & 1)) & (cpr - 1); }
+template <int DK>
+__device__ __forceinline__ int kq_off(int r, int col) {
+  return r * DK + 8 * ((col >> 3) ^ kq_swz(r, DK / 8)) + (col & 7);
+}
+// Fragment of K (or Q) rows at reduction step f in accumulator order.
+template <int DK>
+__device__ __forceinline__ bf16x8_t kq_frag(const unsigned short* t, int row, int f, int q4) {
+  const u32x2_t a = *(const u32x2_t*)(t + kq_off<DK>(row, 32 * f + 4 * q4));
+  const u32x2_t b = *(const u32x2_t*)(t + kq_off<DK>(row, 32 * f + 16 + 4 * q4));
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
+}
+// Fragment of K^T (row = column col0 + lane % 16 of K) at step f: two LDS
+// transposing reads; within each 16-lane group lane m supplies row kb + m / 4,
+// column col0 + 4 (m % 4), and lane i receives rows kb .. kb + 3 of column col0 + i.
+template <int DK>
+__device__ __forceinline__ bf16x8_t kt_frag(const unsigned short* t, int col0, int f, int lane) {
+  const int q4 = lane >> 4, m = lane & 15;
+  const int r0 = 32 * f + 4 * q4 + (m >> 2), col = col0 + 4 * (m & 3);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(t + kq_off<DK>(r0, col)));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(t + kq_off<DK>(r0 + 16, col)));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The start state of the slice in LDS: 16 rows of DK floats; the 16-byte
+// chunks of row r are permuted (chunk c at position c ^ (r mod 8)) so that a
+// read of one column group by 16 rows spreads over the banks.
+template <int DK>
+__device__ __forceinline__ f32x4_t st_read(const float* t, int r, int col) {
+  return *(const f32x4_t*)(t + r * DK + 4 * ((col >> 2) ^ (r & 7)));
+}
+// hi and lo bf16 parts of four floats (one accumulator block of a lane)
+__device__ __forceinline__ void split4(const f32x4_t& x, u32x2_t& hi, u32x2_t& lo) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const unsigned w = pack_bf16x2(x[2 * p], x[2 * p + 1]);
+    hi[p] = w;
+    lo[p] = pack_bf16x2(x[2 * p] - __uint_as_float(w << 16), x[2 * p + 1] - __uint_as_float(w & 0xffff0000u));
+  }
+}
+__device__ __forceinline__ bf16x8_t join_frag(u32x2_t a, u32x2_t b) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
+}
+__device__ __forceinline__ bf16x8_t join_or_zero(bool live, u32x2_t a, u32x2_t b) {
+  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8_t, live ? u32x4_t{a.x, a.y, b.x, b.y} : z4);
+}
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations but
+// not for its loads into LDS still in flight (the next task's operands).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Raw buffer resource: 64-bit base, no stride, num_records bytes in range;
+// dword 3 selects the 32-bit data format. Loads past num_records return zeros.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buf_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4_t{(int)(unsigned)a, (int)(unsigned)((a >> 32) & 0xffffu), bytes, 0x00020000};
+}
+// 16 bytes per lane from buffer r at voff + soff into LDS at lds_base + OFF
+// + 16 * lane. Written as inline assembly so that the compiler does not track these loads:
+// it would otherwise wait for them before unrelated LDS reads. Completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the buffer.
+// The leading s_nop covers the SGPR-write-to-VMEM-read and M0-write-to-LDS-DMA
+// wait states; M0 (the LDS address) is restored afterwards.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(unsigned long long)(lds_void_t*)p; }
+template <int OFF>
+__device__ __forceinline__ void load_lds16(i32x4_t r, unsigned lds_base, int voff, int soff) {
+  unsigned saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(r),
+        "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(OFF)
+      : "memory", "scc");
+}
+
+// One chunk of one work item, with what its loads and stores need (uniform
+// across the workgroup).
+struct CoopTask {
+  int item, ci, nck;
+  int sst, L;      // the segment's first token and length
+  int h, e0, ws0;  // head, first state row of the slice, workspace block of the segment's first chunk
+  int s;           // segment: end state to seg_final_state[s]
+  int src;         // start state: seg_start_state slot src (>= 0), root_state[-2 - src], or zeros (-1)
+  int own;         // copy of the start state into the segment's own slot (s), or -1
+  int fc;          // end state also to the first child's start slot, or -1
+  int valid;
+  __device__ int t0() const { return sst + CH * ci; }
+  __device__ int len() const { return min(CH, L - CH * ci); }
+};
+
+template <int DK>
+__global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t* __restrict__ blob,
+                                                                  GdnArgs args) {
+  using C = CoopCfg<DK>;
+  constexpr int DV = DK;
+  constexpr int NG = DV / 16;  // slices per head
+  typedef unsigned short E;
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[C::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[C::BUF];
+  __shared__ u32x4_t sx[2][C::NKD][64];  // state fragments (hi, lo) of each reduction step
+  __shared__ u32x2_t rx[2][4][64];       // R blocks (hi, lo)
+  __shared__ u32x2_t ux[4][4][64];       // U blocks (hi, lo), U' blocks (hi, lo)
+  __shared__ f32x4_t yx[4][64];          // Y^T blocks
+
+  const int level = args.level;
+  if (level > blob[MH_MAXDEPTH]) return;
+  const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
+  const int32_t* __restrict__ level_seg = blob + blob[MH_OFF_LEVELSEG];
+  const int32_t* __restrict__ parent = blob + blob[MH_OFF_PARENT];
+  const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
+  const int32_t* __restrict__ root_ord = blob + blob[MH_OFF_ROOTORD];
+  const int32_t* __restrict__ first_child = blob + blob[MH_OFF_FIRSTCHILD];
+  const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
+  const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
+  const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
+  const int H = args.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wv < C::NW;
+  const int w = chain ? wv : wv - C::NW;  // chain wave w, or helper wave w
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const E* __restrict__ Kg = (const E*)args.k;
+  const E* __restrict__ Qg = (const E*)args.q;
+  const E* __restrict__ Vg = (const E*)args.v;
+  E* __restrict__ Og = (E*)args.o;
+  const size_t SZ = (size_t)DV * DK;
+
+  // Item i runs on XCD i mod 8 (workgroups are dispatched round-robin over
+  // the 8 XCDs and the grid is a multiple of 8); all slices of a head share
+  // an XCD and its L2.
+  const int NH8 = (H + 7) / 8;
+  const int nitems = nlev * NH8 * 8 * NG;
+  // first chunk of the first valid item at or after `item` of this workgroup
+  auto item_task = [&](int item) {
+    CoopTask t;
+    t.valid = 0;
+    for (; item < nitems; item += gridDim.x) {
+      const int x = item & 7, j = item >> 3;
+      const int sg = j % NG, j2 = j / NG;
+      const int h = (j2 % NH8) * 8 + x, li = j2 / NH8;
+      if (h >= H) continue;
+      const int s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + li]);
+      const int L = __builtin_amdgcn_readfirstlane(seg_len[s]);
+      if (L <= 0) continue;
+      const int p = __builtin_amdgcn_readfirstlane(parent[s]);
+      t.item = item;
+      t.ci = 0;
+      t.nck = (L + CH - 1) / CH;
+      t.sst = __builtin_amdgcn_readfirstlane(seg_start[s]);
+      t.L = L;
+      t.h = h;
+      t.e0 = 16 * sg;
+      t.ws0 = __builtin_amdgcn_readfirstlane(chunk_base[s]) * H + h;
+      t.s = s;
+      if (p < 0) {
+        t.src = args.root_state ? -2 - __builtin_amdgcn_readfirstlane(root_ord[s]) : -1;
+        t.own = s;
+      } else {
+        const int fc_p = __builtin_amdgcn_readfirstlane(first_child[p]);
+        t.src = fc_p;
+        t.own = fc_p != s ? s : -1;
+      }
+      t.fc = __builtin_amdgcn_readfirstlane(first_child[s]);
+      t.valid = 1;
+      break;
+    }
+    return t;
+  };
+  // the task after t: the segment's next chunk, or the next item's first
+  auto next_task = [&](const CoopTask& t) {
+    if (t.ci + 1 < t.nck) {
+      CoopTask n = t;
+      n.ci = t.ci + 1;
+      return n;
+    }
+    return item_task(t.item + gridDim.x);
+  };
+
+  // ---- loads of a task's operands into LDS buffer b (helper waves), in three
+  // parts spread over the phases of the current chunk
+  auto dma = [&](unsigned char* b, const CoopTask& t, int part) {
+    const int t0 = t.t0(), len = t.len();
+    const unsigned lb = lds_addr(b) + 1024 * w;  // this wave's loads: 1 KB blocks w, w + NW, ...
+    const i32x4_t rW = buf_rsrc(args.ws + (size_t)(t.ws0 + t.ci * H) * kWsChunk, (int)kWsChunk);
+    // byte offset of this lane's 16 bytes in K/Q load i (rows past len are out of range)
+    auto kvo = [&](int i) {
+      const int n = 64 * (w + C::NW * i) + lane, r = n / C::CPR, c = (n % C::CPR) ^ kq_swz(r, C::CPR);
+      return (r * H + t.h) * DK * 2 + 16 * c;
+    };
+    constexpr int S1 = 1024 * C::NW;  // stride of a wave's blocks
+    if (part == 0) {
+      const i32x4_t rK = buf_rsrc(Kg + (size_t)t0 * H * DK, len * H * DK * 2);
+      const i32x4_t rQ = buf_rsrc(Qg + (size_t)t0 * H * DK, len * H * DK * 2);
+      load_lds16<0 * S1>(rK, lb, kvo(0), 0);
+      load_lds16<1 * S1>(rK, lb, kvo(1), 0);
+      load_lds16<2 * S1>(rK, lb, kvo(2), 0);
+      load_lds16<3 * S1>(rK, lb, kvo(3), 0);
+      load_lds16<C::OQ + 0 * S1>(rQ, lb, kvo(0), 0);
+      load_lds16<C::OQ + 1 * S1>(rQ, lb, kvo(1), 0);
+    } else if (part == 1) {
+      const i32x4_t rQ = buf_rsrc(Qg + (size_t)t0 * H * DK, len * H * DK * 2);
+      load_lds16<C::OQ + 2 * S1>(rQ, lb, kvo(2), 0);
+      load_lds16<C::OQ + 3 * S1>(rQ, lb, kvo(3), 0);
+      const int wo = 16 * lane + 1024 * w;
+#pragma unroll
+      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OT + i * S1, wo, i * S1);
+    } else {
+      const int wo = 16 * lane + 1024 * w;
+#pragma unroll
+      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OP + i * S1, wo, (int)kWsFrag + i * S1);
+      if (w < 2 || C::NW == 1) {
+        const i32x4_t rV = buf_rsrc(Vg + (size_t)t0 * H * DV, len * H * DV * 2);
+        for (int jv = w; jv < 2; jv += C::NW) {
+          const int n = 64 * jv + lane, r = n >> 1;
+          load_lds16<C::OV>(rV, lds_addr(b) + 1024 * jv, (r * H + t.h) * DV * 2 + 2 * t.e0 + 16 * (n & 1), 0);
+        }
+      }
+      if (w == C::NW - 1) load_lds16<C::OG>(rW, lds_addr(b), 16 * lane, (int)kWsGam);
+      if (t.ci == 0) {
+        // start state rows e0 .. e0 + 15 of DK floats; chunk c of row r at
+        // position c ^ (r mod 8)
+        const float* src = t.src >= 0 ? args.seg_start + ((size_t)t.src * H + t.h) * SZ
+                           : t.src < -1 ? args.root_state + ((size_t)(-2 - t.src) * H + t.h) * SZ
+                                        : args.seg_start;
+        const i32x4_t rS = buf_rsrc(src + (size_t)t.e0 * DK, t.src != -1 ? C::SB : 0);
+#pragma unroll
+        for (int i = 0; i < C::SJ / C::NW; ++i) {
+          const int n = 64 * (w + C::NW * i) + lane, r = n / (DK / 4), c = (n % (DK / 4)) ^ (r & 7);
+          load_lds16<0>(rS, lb + C::OS + i * S1, r * DK * 4 + 16 * c, 0);
+        }
+      }
+    }
+  };
+
+  f32x4_t St[2];        // chain wave: S^T blocks, lane (c16, q4): S[e0 + c16][32 w + 16 jb + 4 q4 + r]
+  f32x4_t oval[C::TB];  // helper wave: O^T blocks of the previous chunk, lane (c16, q4): O[16 I + c16][e0 + 4 q4 + r]
+  int o_t0 = 0, o_len = 0, o_h = 0, o_e0 = 0;
+  auto flush_o = [&]() {
+#pragma unroll
+    for (int bb = 0; bb < C::TB; ++bb) {
+      const int i = 16 * (w + C::NW * bb) + c16;
+      if (i < o_len) {
+        E* d = Og + ((size_t)(o_t0 + i) * H + o_h) * DV + o_e0 + 4 * q4;
+        *(u32x2_t*)d = u32x2_t{pack_bf16x2(oval[bb][0], oval[bb][1]), pack_bf16x2(oval[bb][2], oval[bb][3])};
+      }
+    }
+    o_len = 0;
+  };
+  // S fragments of every reduction step: from the exchange, or at a
+  // segment's first chunk from the start state in LDS
+  auto s_frags = [&](const unsigned char* cb, bool first, bf16x8_t* sh, bf16x8_t* sl) {
+#pragma unroll
+    for (int f = 0; f < C::NKD; ++f) {
+      if (first) {
+        const float* S0 = (const float*)(cb + C::OS);
+        u32x2_t ah, al, bh, bl;
+        split4(st_read<DK>(S0, c16, 32 * f + 4 * q4), ah, al);
+        split4(st_read<DK>(S0, c16, 32 * f + 16 + 4 * q4), bh, bl);
+        sh[f] = join_frag(ah, bh);
+        sl[f] = join_frag(al, bl);
+      } else {
+        sh[f] = __builtin_bit_cast(bf16x8_t, sx[0][f][lane]);
+        sl[f] = __builtin_bit_cast(bf16x8_t, sx[1][f][lane]);
+      }
+    }
+  };
+
+  // One chunk (task c, operands in cur) while the next task's operands load
+  // into nxt; n2 receives the task after that.
+  auto step = [&](const unsigned char* cur, unsigned char* nxt, const CoopTask& c, const CoopTask& n1) {
+    CoopTask n2;
+    const E* Ks = (const E*)cur;
+    const E* Qs = (const E*)(cur + C::OQ);
+    const float* gam = (const float*)(cur + C::OG);
+    const float* rrp = gam + CH;
+    const bool first = c.ci == 0, last = c.ci + 1 == c.nck;
+    if (!chain) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of the chunk landed
+    lds_barrier();  // B0: the chunk's operands and S fragments are in LDS; nxt is no longer read
+    f32x4_t Yt[C::TB];
+    if (chain) {
+      bf16x8_t sh[C::NKD], sl[C::NKD];
+      s_frags(cur, first, sh, sl);
+      if (first) {
+        const float* S0 = (const float*)(cur + C::OS);
+        St[0] = st_read<DK>(S0, c16, 32 * w + 4 * q4);
+        St[1] = st_read<DK>(S0, c16, 32 * w + 16 + 4 * q4);
+        if (c.own >= 0) {
+          float* d = args.seg_start + ((size_t)c.own * H + c.h) * SZ + (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
+          *(f32x4_t*)d = St[0];
+          *(f32x4_t*)(d + 16) = St[1];
+        }
+      }
+      // (1) X = K S^T, R = V - gamma X -> exchange
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        const int I = w + C::NW * bb;
+        f32x4_t X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < C::NKD; ++f) {
+          const bf16x8_t ka = kq_frag<DK>(Ks, 16 * I + c16, f, q4);
+          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh[f], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl[f], X, 0, 0, 0);
+        }
+        const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)((const E*)(cur + C::OV) + (16 * I + 4 * q4 + (c16 >> 2)) * 16 + 4 * (c16 & 3)));
+        const f32x4_t gq = *(const f32x4_t*)(gam + 16 * I + 4 * q4);
+        f32x4_t R;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = bf16_val((unsigned short)t[r]) - gq[r] * X[r];
+        split4(R, rx[0][I][lane], rx[1][I][lane]);
+      }
+      // Y^T = S Q^T (to the helper waves with the exchange of U)
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        const int I = w + C::NW * bb;
+        Yt[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < C::NKD; ++f) {
+          const bf16x8_t qb = kq_frag<DK>(Qs, 16 * I + c16, f, q4);
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[f], qb, Yt[bb], 0, 0, 0);
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[f], qb, Yt[bb], 0, 0, 0);
+        }
+      }
+    } else {
+      if (n1.valid) dma(nxt, n1, 0);
+      flush_o();
+    }
+    lds_barrier();  // B1: R is exchanged
+    if (chain) {
+      // (3) U = T'' R, U' = diag(gamma_C / gamma) U -> exchange. T'' rows of
+      // block I < 2 have no second step: that step multiplies by zeros.
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        const int I = w + C::NW * bb;
+        f32x4_t U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf) {
+          const bool live = kf < frag_nk(I);
+          const bf16x8_t rh = join_or_zero(live, rx[0][2 * kf][lane], rx[0][2 * kf + 1][lane]);
+          const bf16x8_t rl = join_or_zero(live, rx[1][2 * kf][lane], rx[1][2 * kf + 1][lane]);
+          const u32x4_t* tf = (const u32x4_t*)(cur + C::OT) + (frag_tri(I) + (live ? kf : 0)) * 128 + lane;
+          const bf16x8_t th = __builtin_bit_cast(bf16x8_t, tf[0]);
+          const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, tf[64]);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh, U, 0, 0, 0);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl, U, 0, 0, 0);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh, U, 0, 0, 0);
+        }
+        const f32x4_t rq = *(const f32x4_t*)(rrp + 16 * I + 4 * q4);
+        split4(U, ux[0][I][lane], ux[1][I][lane]);
+        split4(U * rq, ux[2][I][lane], ux[3][I][lane]);
+        yx[I][lane] = Yt[bb];
+      }
+    } else {
+      if (n1.valid) dma(nxt, n1, 1);
+    }
+    n2.valid = 0;
+    if (n1.valid) n2 = next_task(n1);
+    lds_barrier();  // B2: U and U' are exchanged
+    if (chain) {
+      // (5) S^T = gamma_C S^T + K^T U'; then the end state, or the next S fragments
+      const float gC = gam[CH - 1];
+      St[0] *= gC;
+      St[1] *= gC;
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        const bf16x8_t uh = join_frag(ux[2][2 * kf][lane], ux[2][2 * kf + 1][lane]);
+        const bf16x8_t ul = join_frag(ux[3][2 * kf][lane], ux[3][2 * kf + 1][lane]);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const bf16x8_t kt = kt_frag<DK>(Ks, 32 * w + 16 * jb, kf, lane);
+          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, uh, St[jb], 0, 0, 0);
+          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ul, St[jb], 0, 0, 0);
+        }
+      }
+      if (last) {
+        const size_t srow = (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
+        if (args.seg_final) {
+          float* d = args.seg_final + ((size_t)c.s * H + c.h) * SZ + srow;
+          *(f32x4_t*)d = St[0];
+          *(f32x4_t*)(d + 16) = St[1];
+        }
+        if (c.fc >= 0) {
+          float* d = args.seg_start + ((size_t)c.fc * H + c.h) * SZ + srow;
+          *(f32x4_t*)d = St[0];
+          *(f32x4_t*)(d + 16) = St[1];
+        }
+      } else {
+        u32x2_t h0, l0, h1, l1;
+        split4(St[0], h0, l0);
+        split4(St[1], h1, l1);
+        sx[0][w][lane] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+        sx[1][w][lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
+      }
+    } else {
+      if (n1.valid) dma(nxt, n1, 2);
+      // (4) O^T = scale (gamma Y^T + U^T P^T), stored during the next chunk
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        const int I = w + C::NW * bb;
+        f32x4_t Zt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf) {
+          const bool live = kf < frag_nk(I);
+          const bf16x8_t uh = join_or_zero(live, ux[0][2 * kf][lane], ux[0][2 * kf + 1][lane]);
+          const bf16x8_t ul = join_or_zero(live, ux[1][2 * kf][lane], ux[1][2 * kf + 1][lane]);
+          const u32x4_t* pf = (const u32x4_t*)(cur + C::OP) + (frag_tri(I) + (live ? kf : 0)) * 128 + lane;
+          const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, pf[0]);
+          const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, pf[64]);
+          Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph, Zt, 0, 0, 0);
+          Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph, Zt, 0, 0, 0);
+          Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl, Zt, 0, 0, 0);
+        }
+        const float gi = gam[16 * I + c16];
+        oval[bb] = args.scale * (gi * yx[I][lane] + Zt);
+      }
+      o_t0 = c.t0();
+      o_len = c.len();
+      o_h = c.h;
+      o_e0 = c.e0;
+    }
+    return n2;
+  };
+
+  CoopTask cur = item_task(blockIdx.x);
+  if (!cur.valid) return;
+  CoopTask n1 = next_task(cur);
+  if (!chain) {
+    dma(buf0, cur, 0);
+    dma(buf0, cur, 1);
+    dma(buf0, cur, 2);
+  }
+  for (;;) {
+    CoopTask n2 = step(buf0, buf1, cur, n1);
+    if (!n1.valid) break;
+    cur = n1;
+    n1 = n2;
+    n2 = step(buf1, buf0, cur, n1);
+    if (!n1.valid) break;
+    cur = n1;
+    n1 = n2;
+  }
+  if (!chain) flush_o();
+}
+
 template <bool BF16, int DK>
 fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const bool cap = stream_capturing(stream);
@@ -900,8 +1435,11 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const int sgrid = (cus + 7) / 8 * 8;  // one workgroup per CU (LDS); a multiple of 8: item i runs on XCD i mod 8
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
-    hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream, a.blob,
-                       a);
+    if constexpr (BF16)
+      hipLaunchKernelGGL((gdn_coop_kernel<DK>), dim3(sgrid), dim3(CoopCfg<DK>::NT), 0, stream, a.blob, a);
+    else
+      hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream,
+                         a.blob, a);
     FORK_HIP_CHECK(hipGetLastError());
   }
   return FORK_OK;
