@@ -67,6 +67,9 @@ typedef struct fork_caps {
                          small tree still fills the GPU; see fork_attn_workspace. */
 } fork_caps;
 
+/* Depths whose segment counts a fork_meta carries for launch planning. */
+#define FORK_PLAN_DEPTHS 32
+
 /* Host descriptor of a built metadata blob. The arrays live in `dev`. */
 typedef struct fork_meta {
   int32_t num_tokens;      /* T */
@@ -80,6 +83,11 @@ typedef struct fork_meta {
   fork_caps caps;
   void* dev;               /* caller-owned device blob, >= fork_meta_size bytes */
   size_t dev_bytes;
+  /* depths 0 .. min(max_depth, FORK_PLAN_DEPTHS - 1): segments at the depth,
+     and those longer than one 64-token Gated DeltaNet chunk (the library uses
+     them to skip kernel launches with no work outside graph capture) */
+  int32_t level_segs[FORK_PLAN_DEPTHS];
+  int32_t level_long[FORK_PLAN_DEPTHS];
 } fork_meta;
 
 /* Array ids for fork_meta_export. */

@@ -20,7 +20,7 @@ H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS
            "OFF_PARENT", "OFF_SEGLEN", "OFF_SEGSTART", "OFF_DEPTH", "OFF_ROOT", "OFF_ROOTORD",
            "OFF_ANCLEN", "OFF_FIRSTCHILD", "OFF_CHUNKBASE", "OFF_LEVELOFF", "OFF_LEVELSEG",
            "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
-           "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS"]
+           "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS", "OFF_LEVELLONG"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
 ATTN_ROWS = int(re.search(r"kAttnRows = (\d+);", open(os.path.join(
     ROOT, "tree_structured_decision_amd", "csrc", "common.h")).read()).group(1))
@@ -87,10 +87,14 @@ def check_plan(parent, seg_len, gqa, kv_heads=0):
     lo = arr(w, "LEVELOFF", maxd + 2)
     ls = arr(w, "LEVELSEG", S)
     assert sorted(ls.tolist()) == list(range(S))
+    ll = arr(w, "LEVELLONG", maxd + 1)
     for d in range(maxd + 1):
         segs = ls[lo[d]:lo[d + 1]]
         assert np.all(ref["depth"][segs] == d)
         assert np.all(np.diff(seg_len[segs]) <= 0)
+        # the depth's segments longer than one 64-token chunk lead its list
+        assert ll[d] == int(np.sum(seg_len[segs] > 64))
+        assert np.all(seg_len[segs[:ll[d]]] > 64) and np.all(seg_len[segs[ll[d]:]] <= 64)
     # chunks: 64-token pieces of each segment, in order
     nch = w[HI["NCHUNKS"]]
     ch = arr(w, "CHUNKS", 2 * nch).reshape(-1, 2)

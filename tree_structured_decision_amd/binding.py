@@ -44,7 +44,8 @@ class fork_meta(ctypes.Structure):
                 ("num_roots", ctypes.c_int32), ("max_depth", ctypes.c_int32),
                 ("num_attn_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("num_attn_merges", ctypes.c_int32),
-                ("caps", fork_caps), ("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_size_t)]
+                ("caps", fork_caps), ("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_size_t),
+                ("level_segs", ctypes.c_int32 * 32), ("level_long", ctypes.c_int32 * 32)]
 
 
 class fork_graph_args(ctypes.Structure):

@@ -142,6 +142,9 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
       std::stable_sort(level_seg.begin() + level_off[d], level_seg.begin() + level_off[d + 1],
                        [&](int32_t x, int32_t y) { return seg_len[x] > seg_len[y]; });
   }
+  std::vector<int32_t> level_long(max_depth + 1, 0);
+  for (int32_t s = 0; s < S; ++s)
+    if (seg_len[s] > kChunk) level_long[depth[s]]++;
 
   // Attention query tiles. Short non-root siblings that follow each other in
   // the stream share their ancestor keys, so they are packed into common
@@ -274,6 +277,7 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   put(MH_OFF_CHUNKBASE, chunk_base.data(), S);
   put(MH_OFF_LEVELOFF, level_off.data(), max_depth + 2);
   put(MH_OFF_LEVELSEG, level_seg.data(), S);
+  put(MH_OFF_LEVELLONG, level_long.data(), max_depth + 1);
   {
     off = (off + 3) & ~int64_t(3);
     w[MH_OFF_CHUNKS] = (int32_t)off;
@@ -314,6 +318,10 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   out->tile_tokens = TT;
   out->num_attn_merges = (int32_t)merges.size();
   out->caps = *caps;
+  for (int32_t d = 0; d <= max_depth && d < FORK_PLAN_DEPTHS; ++d) {
+    out->level_segs[d] = level_off[d + 1] - level_off[d];
+    out->level_long[d] = level_long[d];
+  }
   if (upload_bytes) *upload_bytes = (size_t)off * 4;
   return FORK_OK;
 }

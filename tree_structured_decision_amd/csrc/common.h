@@ -49,6 +49,7 @@ enum MetaHeader : int {
   MH_OFF_MERGE,       // [NMERGE] AttnMerge
   MH_NPARTS,          // partial-result slots used by split tiles (per kv head)
   MH_KV_HEADS,        // kv heads the split plan assumed (0: no splitting)
+  MH_OFF_LEVELLONG,   // [MAXDEPTH + 1] segments longer than one GDN chunk at each depth (they lead its LEVELSEG list)
   MH_WORDS = 64
 };
 // Header words 48..56 hold the attention work counters: the next work item of
@@ -112,9 +113,9 @@ inline BlobLayout blob_layout(const fork_caps& c) {
   L.tile_cap = ((int64_t)c.t_cap + L.tile_tokens - 1) / L.tile_tokens + c.s_cap + kMaxPartSlots;
   L.chunk_cap = ((int64_t)c.t_cap + kChunk - 1) / kChunk + c.s_cap;
   L.merge_cap = kMaxPartSlots / 2;
-  // header + 10 segment arrays + level offsets + 2 words per chunk + 8 per tile
+  // header + 10 segment arrays + level offsets and long counts + 2 words per chunk + 8 per tile
   // + 4 per merge group, each array aligned to 4 words
-  L.upload_cap_words = MH_WORDS + 10 * ((int64_t)c.s_cap + 4) + (c.depth_cap + 2 + 4) +
+  L.upload_cap_words = MH_WORDS + 10 * ((int64_t)c.s_cap + 4) + 2 * (c.depth_cap + 2 + 4) +
                        2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4;
   L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
   L.tok_off_words = L.upload_cap_words;

@@ -66,6 +66,17 @@ constexpr size_t kWsFrag = (size_t)kNtri * 2 * 1024;  // bytes of T'' (or P) fra
 constexpr size_t kWsGam = 2 * kWsFrag;                // gamma, then gamma_C / gamma
 static_assert(kWsGam + 1024 <= kWsChunk, "bf16 workspace layout fits the block (gates staged as 1 KB)");
 
+// bf16 scans split each depth between two kernels: the depth's long segments
+// (more than one chunk; they lead its list) go to the chunk-cooperative kernel
+// when all of its work items fit in one round of the grid (a latency-bound
+// depth such as a single long prefix); everything else goes to the
+// one-wave-per-slice kernel, which has the higher throughput.
+__device__ __forceinline__ int coop_segments(const int32_t* __restrict__ blob, int level, int H, int dv) {
+  const int nlong = blob[blob[MH_OFF_LEVELLONG] + level];
+  const long long items = (long long)nlong * ((H + 7) / 8) * 8 * (dv / 16);
+  return items <= (long long)gridDim.x ? nlong : 0;
+}
+
 template <bool BF16>
 struct GT {
   using E = typename std::conditional<BF16, unsigned short, float>::type;
@@ -127,6 +138,10 @@ struct GdnArgs {
   int H;
   float scale;
   int level;
+  // the depth's segment range [lv_first, lv_first + lv_count) of the blob's
+  // level list and its first lv_take segments for gdn_coop_kernel, when the
+  // host planned the launch; lv_first < 0: read everything from the blob
+  int lv_first, lv_count, lv_take;
 };
 
 // ---------------------------------------------------------------------------
@@ -395,15 +410,18 @@ struct ScanCfg {
   static constexpr int NTRI = tri(4);
   // 16-byte chunks per thread of each staged operand
   static constexpr int KCH = CH * (DK / G::EPC) / NT;
-  static constexpr int WCH = (int)(kWsPlane / 16) / NT;
+  // T'' and P: bf16 fragments (hi, lo) as the prep kernel wrote them; fp32 planes
+  static constexpr int TPB = BF16 ? (int)kWsFrag : (int)kWsPlane;  // bytes of T'' (and of P)
+  static constexpr int WCH = TPB / 16 / NT;
   static constexpr int VCH = CH * (VW / G::EPC) / NT;
   static_assert(KCH * NT == CH * (DK / G::EPC), "K/Q staging must divide evenly");
-  static_assert(WCH * NT == (int)(kWsPlane / 16), "T''/P staging must divide evenly");
+  static_assert(WCH * NT * 16 == TPB, "T''/P staging must divide evenly");
   static_assert(VCH * NT == CH * (VW / G::EPC), "V staging must divide evenly");
   // LDS elements of one buffer's tiles; two buffers when they fit
   static constexpr int SK = CH * LDK, ST = CH * LDT, SV = CH * LDV;
   static constexpr int NPL = BF16 ? 2 : 1;  // planes of T'' and P (hi, lo)
-  static constexpr size_t BUF_BYTES = (size_t)(2 * SK + 2 * NPL * ST + SV) * sizeof(typename G::E) + 2 * CH * 4;
+  static constexpr size_t BUF_BYTES =
+      (size_t)(2 * SK + SV) * sizeof(typename G::E) + (BF16 ? 2 * TPB : 2 * ST * 4) + 2 * CH * 4;
   static constexpr int NBUF = 2 * BUF_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
@@ -462,7 +480,7 @@ __device__ __forceinline__ void prefetch_rest(ScanPrefetch<BF16, DK>& r, const t
   using G = GT<BF16>;
   using C = ScanCfg<BF16, DK>;
   const u32x4_t* Tw = (const u32x4_t*)wsb;
-  const u32x4_t* Pw = (const u32x4_t*)(wsb + kWsPlane);
+  const u32x4_t* Pw = (const u32x4_t*)(wsb + C::TPB);
 #pragma unroll
   for (int i = 0; i < C::WCH; ++i) {
     r.t[i] = Tw[tid + C::NT * i];
@@ -475,9 +493,17 @@ __device__ __forceinline__ void prefetch_rest(ScanPrefetch<BF16, DK>& r, const t
     const int row = min(task / VCPR, len - 1), ch = task % VCPR;
     r.v[i] = *(const u32x4_t*)(Vg + ((size_t)(t0 + row) * H + h) * C::DV + ve0 + ch * G::EPC);
   }
-  const float* gw = (const float*)(wsb + 2 * kWsPlane);
-  r.g = gw[tid & (CH - 1)];
-  r.gl = gw[CH - 1];
+  if constexpr (BF16) {
+    // gamma and gamma_C / gamma
+    const float* gw = (const float*)(wsb + kWsGam);
+    r.g = gw[tid & (CH - 1)];
+    r.gl = gw[CH + (tid & (CH - 1))];
+  } else {
+    // g; the decays are formed at staging
+    const float* gw = (const float*)(wsb + 2 * kWsPlane);
+    r.g = gw[tid & (CH - 1)];
+    r.gl = gw[CH - 1];
+  }
 }
 
 // One LDS buffer of chunk tiles.
@@ -487,10 +513,8 @@ struct ScanTiles {
   using C = ScanCfg<BF16, DK>;
   E* K;
   E* Q;
-  E* Th;
-  E* Tl;
+  E* Th;  // fp32: row-major T'' and P tiles; bf16: their fragments (hi, lo)
   E* Ph;
-  E* Pl;
   E* V;
   float* gam;
   float* rr;
@@ -498,12 +522,11 @@ struct ScanTiles {
     E* e = (E*)base;
     K = e;
     Q = e + C::SK;
-    Th = e + 2 * C::SK;
-    Tl = Th + (C::NPL - 1) * C::ST;
-    Ph = Th + C::NPL * C::ST;
-    Pl = Ph + (C::NPL - 1) * C::ST;
-    V = Ph + C::NPL * C::ST;
-    gam = (float*)(V + C::SV);
+    V = e + 2 * C::SK;
+    unsigned char* tp = (unsigned char*)(V + C::SV);
+    Th = (E*)tp;
+    Ph = (E*)(tp + (BF16 ? C::TPB : C::ST * 4));
+    gam = (float*)(tp + (BF16 ? 2 * C::TPB : 2 * C::ST * 4));
     rr = gam + CH;
   }
 };
@@ -526,11 +549,10 @@ __device__ __forceinline__ void stage_rest(const ScanTiles<BF16, DK>& b, const S
   using C = ScanCfg<BF16, DK>;
 #pragma unroll
   for (int i = 0; i < C::WCH; ++i) {
-    const int cidx = tid + C::NT * i;  // 16-byte chunk of a 16 KB operand region
+    const int cidx = tid + C::NT * i;  // 16-byte chunk of the operand region
     if constexpr (BF16) {
-      const int plane = cidx / (CH * CH / 8), rem = cidx % (CH * CH / 8);
-      tile_put16<BF16, C::LDT>(plane ? b.Tl : b.Th, rem / 8, (rem % 8) * 8, r.t[i]);
-      tile_put16<BF16, C::LDT>(plane ? b.Pl : b.Ph, rem / 8, (rem % 8) * 8, r.p[i]);
+      ((u32x4_t*)b.Th)[cidx] = r.t[i];
+      ((u32x4_t*)b.Ph)[cidx] = r.p[i];
     } else {
       tile_put16<BF16, C::LDT>(b.Th, cidx / 16, (cidx % 16) * 4, r.t[i]);
       tile_put16<BF16, C::LDT>(b.Ph, cidx / 16, (cidx % 16) * 4, r.p[i]);
@@ -543,8 +565,13 @@ __device__ __forceinline__ void stage_rest(const ScanTiles<BF16, DK>& b, const S
     tile_put16<BF16, C::LDV>(b.V, task / VCPR, (task % VCPR) * G::EPC, r.v[i]);
   }
   if (tid < CH) {
-    b.gam[tid] = __expf(r.g);
-    b.rr[tid] = __expf(r.gl - r.g);
+    if constexpr (BF16) {
+      b.gam[tid] = r.g;
+      b.rr[tid] = r.gl;
+    } else {
+      b.gam[tid] = __expf(r.g);
+      b.rr[tid] = __expf(r.gl - r.g);
+    }
   }
 }
 
@@ -626,7 +653,8 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::NBUF * C::BUF_BYTES];
 
   const int level = args.level;
-  if (level > blob[MH_MAXDEPTH]) return;
+  const bool planned = args.lv_first >= 0;
+  if (!planned && level > blob[MH_MAXDEPTH]) return;
   const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
   const int32_t* __restrict__ level_seg = blob + blob[MH_OFF_LEVELSEG];
   const int32_t* __restrict__ parent = blob + blob[MH_OFF_PARENT];
@@ -635,8 +663,11 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
   const int32_t* __restrict__ first_child = blob + blob[MH_OFF_FIRSTCHILD];
   const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
   const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
-  const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
   const int H = args.H;
+  // the depth's first `take` segments are handled by gdn_coop_kernel
+  const int take = planned ? args.lv_take : (BF16 ? coop_segments(blob, level, H, C::DV) : 0);
+  const int lv0 = (planned ? args.lv_first : level_off[level]) + take;
+  const int nlev = (planned ? args.lv_first + args.lv_count : level_off[level + 1]) - lv0;
   const int tid = threadIdx.x, lane = tid & 63, sw = tid >> 6;  // wave = slice within the group
   const int c16 = lane & 15, q4 = lane >> 4;
   const E* __restrict__ Kg = (const E*)args.k;
@@ -784,8 +815,13 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
           for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int kf = 0; kf < C::nk(I); ++kf) {
-              th[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Th, 16 * I + c16, kf, q4);
-              if constexpr (SPLIT) tl[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Tl, 16 * I + c16, kf, q4);
+              if constexpr (BF16) {
+                const u32x4_t* tf = (const u32x4_t*)cur.Th + (C::tri(I) + kf) * 128 + lane;
+                th[C::tri(I) + kf] = __builtin_bit_cast(bf16x8_t, tf[0]);
+                tl[C::tri(I) + kf] = __builtin_bit_cast(bf16x8_t, tf[64]);
+              } else {
+                th[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Th, 16 * I + c16, kf, q4);
+              }
             }
         }
         SCAN_FENCE();
@@ -819,8 +855,13 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
       for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int kf = 0; kf < C::nk(I); ++kf) {
-          ph[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Ph, 16 * I + c16, kf, q4);
-          if constexpr (SPLIT) pl[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Pl, 16 * I + c16, kf, q4);
+          if constexpr (BF16) {
+            const u32x4_t* pf = (const u32x4_t*)cur.Ph + (C::tri(I) + kf) * 128 + lane;
+            ph[C::tri(I) + kf] = __builtin_bit_cast(bf16x8_t, pf[0]);
+            pl[C::tri(I) + kf] = __builtin_bit_cast(bf16x8_t, pf[64]);
+          } else {
+            ph[C::tri(I) + kf] = ld_perm<BF16, C::LDT>(cur.Ph, 16 * I + c16, kf, q4);
+          }
         }
       SCAN_FENCE();
       f32x4_t U[4];
@@ -1078,7 +1119,8 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   __shared__ f32x4_t yx[4][64];          // Y^T blocks
 
   const int level = args.level;
-  if (level > blob[MH_MAXDEPTH]) return;
+  const bool planned = args.lv_first >= 0;
+  if (!planned && level > blob[MH_MAXDEPTH]) return;
   const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
   const int32_t* __restrict__ level_seg = blob + blob[MH_OFF_LEVELSEG];
   const int32_t* __restrict__ parent = blob + blob[MH_OFF_PARENT];
@@ -1087,8 +1129,10 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   const int32_t* __restrict__ first_child = blob + blob[MH_OFF_FIRSTCHILD];
   const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
   const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
-  const int lv0 = level_off[level], nlev = level_off[level + 1] - lv0;
   const int H = args.H;
+  const int lv0 = planned ? args.lv_first : level_off[level];
+  const int nlev = planned ? args.lv_take : coop_segments(blob, level, H, DV);
+  if (nlev == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool chain = wv < C::NW;
@@ -1428,19 +1472,42 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   }
   hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
-  // One scan launch per depth (children start after their parents ended).
-  // Under capture, every depth up to the capacity is recorded; depths beyond
-  // the current tree exit at once.
+  // Scan launches per depth (children start after their parents ended): the
+  // chunk-cooperative kernel for a latency-bound set of long segments, the
+  // per-slice kernel for the rest. Under capture, every depth up to the
+  // capacity is recorded with both kernels, which split the depth from the
+  // blob; depths beyond the current tree exit at once.
   const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
   const int sgrid = (cus + 7) / 8 * 8;  // one workgroup per CU (LDS); a multiple of 8: item i runs on XCD i mod 8
+  int first = 0;                        // first segment of the depth in the blob's level list
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
-    if constexpr (BF16)
-      hipLaunchKernelGGL((gdn_coop_kernel<DK>), dim3(sgrid), dim3(CoopCfg<DK>::NT), 0, stream, a.blob, a);
-    else
+    bool run_coop = BF16, run_scan = true;
+    a.lv_first = a.lv_count = a.lv_take = -1;
+    if (!cap && lv < FORK_PLAN_DEPTHS) {
+      // the kernels' split of the depth (coop_segments), decided here so that
+      // launches without work are skipped
+      const int nseg = m->level_segs[lv], nlong = m->level_long[lv];
+      const long long coop_items = (long long)nlong * ((a.H + 7) / 8) * 8 * (DK / 16);
+      const int take = BF16 && coop_items <= sgrid ? nlong : 0;
+      a.lv_first = first;
+      a.lv_count = nseg;
+      a.lv_take = take;
+      run_coop = take > 0;
+      run_scan = nseg - take > 0;
+      first += nseg;
+    }
+    if constexpr (BF16) {
+      if (run_coop) {
+        hipLaunchKernelGGL((gdn_coop_kernel<DK>), dim3(sgrid), dim3(CoopCfg<DK>::NT), 0, stream, a.blob, a);
+        FORK_HIP_CHECK(hipGetLastError());
+      }
+    }
+    if (run_scan) {
       hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream,
                          a.blob, a);
-    FORK_HIP_CHECK(hipGetLastError());
+      FORK_HIP_CHECK(hipGetLastError());
+    }
   }
   return FORK_OK;
 }
@@ -1475,6 +1542,7 @@ fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const v
   g.H = H;
   g.scale = scale;
   g.level = 0;
+  g.lv_first = g.lv_count = g.lv_take = -1;
   if (dt == FORK_BF16) {
     if (dk == 128) return launch_gdn_t<true, 128>(m, g, stream);
     if (dk == 64) return launch_gdn_t<true, 64>(m, g, stream);
