@@ -144,6 +144,11 @@ struct GdnArgs {
   int lv_first, lv_count, lv_take;
 };
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// but not for its global loads still in flight (prefetches of the next work
+// item, or loads into LDS of the next task, which are awaited explicitly).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Prep: per (chunk, head) compute g, T'' = (I + A)^-1 diag(b), P = QK^T * Gamma.
 template <bool BF16, int DK>
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
     const int c = item / H, h = item - c * H;
     unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
 
-    __syncthreads();  // LDS reuse across items
+    lds_barrier();  // LDS reuse across items
     const int len = rlen;
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -231,7 +236,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
     }
     // zero Ts (upper blocks stay zero)
     for (int i = tid; i < CH * LDA; i += 256) Ts[i] = 0.f;
-    __syncthreads();
+    lds_barrier();
     if (item + (int)gridDim.x < nchunks * H) prep_load(item + gridDim.x);
 
     // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal).
@@ -250,7 +255,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
           qk[J] = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk[J]);
         }
       }
-      __syncthreads();  // every wave is done reading Ks / Qs
+      lds_barrier();  // every wave is done reading Ks / Qs
 #pragma unroll
       for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -261,7 +266,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
           Ps[i * LDA + j] = dec * qk[J][r];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution
     if (lane < 16) {
@@ -277,7 +282,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
 #pragma unroll
       for (int i = 0; i < 16; ++i) Ts[(base + i) * LDA + base + col] = x[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // off-diagonal blocks: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, by distance
 #pragma unroll
@@ -294,7 +299,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
 #pragma unroll
         for (int r = 0; r < 4; ++r) Zs[w][(4 * q4 + r) * 20 + c16] = z[r];
       }
-      __syncthreads();
+      lds_barrier();
       if (act) {
         f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -303,7 +308,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * q4 + r) * LDA + 16 * J + c16] = -t[r];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // T'' = T diag(b) and P -> workspace
@@ -978,7 +983,7 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
 // the decays, and at a segment's first chunk its start state) are fetched by
 // buffer loads straight into LDS, double-buffered: the next task (the next
 // chunk, or the first chunk of the workgroup's next item) loads while the
-// current one computes, its loads spread over the three phases. The buffer
+// current one computes, its loads spread over the first two phases. The buffer
 // range of K, Q and V ends at the chunk's last token, so rows past a ragged
 // chunk read as zeros; a missing start state (a root without root_state) is
 // an empty range and reads as zeros too.
@@ -1054,9 +1059,6 @@ __device__ __forceinline__ bf16x8_t join_or_zero(bool live, u32x2_t a, u32x2_t b
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
   return __builtin_bit_cast(bf16x8_t, live ? u32x4_t{a.x, a.y, b.x, b.y} : z4);
 }
-// Workgroup barrier for LDS traffic: waits for this wave's LDS operations but
-// not for its loads into LDS still in flight (the next task's operands).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Raw buffer resource: 64-bit base, no stride, num_records bytes in range;
 // dword 3 selects the 32-bit data format. Loads past num_records return zeros.
@@ -1195,8 +1197,9 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
     return item_task(t.item + gridDim.x);
   };
 
-  // ---- loads of a task's operands into LDS buffer b (helper waves), in three
-  // parts spread over the phases of the current chunk
+  // ---- loads of a task's operands into LDS buffer b (helper waves), in two
+  // parts spread over the first two phases of the current chunk: K, Q and (at
+  // a segment's first chunk) the start state; T'', P, v and the decays
   auto dma = [&](unsigned char* b, const CoopTask& t, int part) {
     const int t0 = t.t0(), len = t.len();
     const unsigned lb = lds_addr(b) + 1024 * w;  // this wave's loads: 1 KB blocks w, w + NW, ...
@@ -1216,25 +1219,8 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
       load_lds16<3 * S1>(rK, lb, kvo(3), 0);
       load_lds16<C::OQ + 0 * S1>(rQ, lb, kvo(0), 0);
       load_lds16<C::OQ + 1 * S1>(rQ, lb, kvo(1), 0);
-    } else if (part == 1) {
-      const i32x4_t rQ = buf_rsrc(Qg + (size_t)t0 * H * DK, len * H * DK * 2);
       load_lds16<C::OQ + 2 * S1>(rQ, lb, kvo(2), 0);
       load_lds16<C::OQ + 3 * S1>(rQ, lb, kvo(3), 0);
-      const int wo = 16 * lane + 1024 * w;
-#pragma unroll
-      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OT + i * S1, wo, i * S1);
-    } else {
-      const int wo = 16 * lane + 1024 * w;
-#pragma unroll
-      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OP + i * S1, wo, (int)kWsFrag + i * S1);
-      if (w < 2 || C::NW == 1) {
-        const i32x4_t rV = buf_rsrc(Vg + (size_t)t0 * H * DV, len * H * DV * 2);
-        for (int jv = w; jv < 2; jv += C::NW) {
-          const int n = 64 * jv + lane, r = n >> 1;
-          load_lds16<C::OV>(rV, lds_addr(b) + 1024 * jv, (r * H + t.h) * DV * 2 + 2 * t.e0 + 16 * (n & 1), 0);
-        }
-      }
-      if (w == C::NW - 1) load_lds16<C::OG>(rW, lds_addr(b), 16 * lane, (int)kWsGam);
       if (t.ci == 0) {
         // start state rows e0 .. e0 + 15 of DK floats; chunk c of row r at
         // position c ^ (r mod 8)
@@ -1248,6 +1234,20 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
           load_lds16<0>(rS, lb + C::OS + i * S1, r * DK * 4 + 16 * c, 0);
         }
       }
+    } else {
+      const int wo = 16 * lane + 1024 * w;
+#pragma unroll
+      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OT + i * S1, wo, i * S1);
+#pragma unroll
+      for (int i = 0; i < C::FJ / C::NW; ++i) load_lds16<0>(rW, lb + C::OP + i * S1, wo, (int)kWsFrag + i * S1);
+      if (w < 2 || C::NW == 1) {
+        const i32x4_t rV = buf_rsrc(Vg + (size_t)t0 * H * DV, len * H * DV * 2);
+        for (int jv = w; jv < 2; jv += C::NW) {
+          const int n = 64 * jv + lane, r = n >> 1;
+          load_lds16<C::OV>(rV, lds_addr(b) + 1024 * jv, (r * H + t.h) * DV * 2 + 2 * t.e0 + 16 * (n & 1), 0);
+        }
+      }
+      if (w == C::NW - 1) load_lds16<C::OG>(rW, lds_addr(b), 16 * lane, (int)kWsGam);
     }
   };
 
@@ -1411,7 +1411,6 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
         sx[1][w][lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
       }
     } else {
-      if (n1.valid) dma(nxt, n1, 2);
       // (4) O^T = scale (gamma Y^T + U^T P^T), stored during the next chunk
 #pragma unroll
       for (int bb = 0; bb < C::TB; ++bb) {
@@ -1446,7 +1445,6 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   if (!chain) {
     dma(buf0, cur, 0);
     dma(buf0, cur, 1);
-    dma(buf0, cur, 2);
   }
   for (;;) {
     CoopTask n2 = step(buf0, buf1, cur, n1);
