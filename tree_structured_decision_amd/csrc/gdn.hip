@@ -1296,19 +1296,42 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
     if (!chain) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of the chunk landed
     lds_barrier();  // B0: the chunk's operands and S fragments are in LDS; nxt is no longer read
     f32x4_t Yt[C::TB];
+    bf16x8_t th[C::TB][2], tl[C::TB][2], kt[2][2];
+    f32x4_t rq[C::TB];
     if (chain) {
-      bf16x8_t sh[C::NKD], sl[C::NKD];
+      // every LDS read of this phase first (one round trip), then the products;
+      // T'' and the decays of phase (3) are read here too
+      bf16x8_t sh[C::NKD], sl[C::NKD], ka[C::TB][C::NKD], qb[C::TB][C::NKD];
+      s16x4_t vt[C::TB];
+      f32x4_t gq[C::TB];
       s_frags(cur, first, sh, sl);
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        const int I = w + C::NW * bb;
+#pragma unroll
+        for (int f = 0; f < C::NKD; ++f) {
+          ka[bb][f] = kq_frag<DK>(Ks, 16 * I + c16, f, q4);
+          qb[bb][f] = kq_frag<DK>(Qs, 16 * I + c16, f, q4);
+        }
+        vt[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)((const E*)(cur + C::OV) + (16 * I + 4 * q4 + (c16 >> 2)) * 16 + 4 * (c16 & 3)));
+        gq[bb] = *(const f32x4_t*)(gam + 16 * I + 4 * q4);
+        rq[bb] = *(const f32x4_t*)(rrp + 16 * I + 4 * q4);
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf) {
+          // T'' rows of block I < 2 have no second step: it reuses the first
+          // fragment against zeros (below)
+          const u32x4_t* tf = (const u32x4_t*)(cur + C::OT) + (frag_tri(I) + (kf < frag_nk(I) ? kf : 0)) * 128 + lane;
+          th[bb][kf] = __builtin_bit_cast(bf16x8_t, tf[0]);
+          tl[bb][kf] = __builtin_bit_cast(bf16x8_t, tf[64]);
+        }
+      }
       if (first) {
         const float* S0 = (const float*)(cur + C::OS);
         St[0] = st_read<DK>(S0, c16, 32 * w + 4 * q4);
         St[1] = st_read<DK>(S0, c16, 32 * w + 16 + 4 * q4);
-        if (c.own >= 0) {
-          float* d = args.seg_start + ((size_t)c.own * H + c.h) * SZ + (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
-          *(f32x4_t*)d = St[0];
-          *(f32x4_t*)(d + 16) = St[1];
-        }
       }
+      SCAN_FENCE();
       // (1) X = K S^T, R = V - gamma X -> exchange
 #pragma unroll
       for (int bb = 0; bb < C::TB; ++bb) {
@@ -1316,29 +1339,28 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
         f32x4_t X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int f = 0; f < C::NKD; ++f) {
-          const bf16x8_t ka = kq_frag<DK>(Ks, 16 * I + c16, f, q4);
-          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh[f], X, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl[f], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[bb][f], sh[f], X, 0, 0, 0);
+          X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[bb][f], sl[f], X, 0, 0, 0);
         }
-        const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)((const E*)(cur + C::OV) + (16 * I + 4 * q4 + (c16 >> 2)) * 16 + 4 * (c16 & 3)));
-        const f32x4_t gq = *(const f32x4_t*)(gam + 16 * I + 4 * q4);
         f32x4_t R;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = bf16_val((unsigned short)t[r]) - gq[r] * X[r];
+        for (int r = 0; r < 4; ++r) R[r] = bf16_val((unsigned short)vt[bb][r]) - gq[bb][r] * X[r];
         split4(R, rx[0][I][lane], rx[1][I][lane]);
       }
       // Y^T = S Q^T (to the helper waves with the exchange of U)
 #pragma unroll
       for (int bb = 0; bb < C::TB; ++bb) {
-        const int I = w + C::NW * bb;
         Yt[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int f = 0; f < C::NKD; ++f) {
-          const bf16x8_t qb = kq_frag<DK>(Qs, 16 * I + c16, f, q4);
-          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[f], qb, Yt[bb], 0, 0, 0);
-          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[f], qb, Yt[bb], 0, 0, 0);
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[f], qb[bb][f], Yt[bb], 0, 0, 0);
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[f], qb[bb][f], Yt[bb], 0, 0, 0);
         }
+      }
+      if (first && c.own >= 0) {
+        float* d = args.seg_start + ((size_t)c.own * H + c.h) * SZ + (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
+        *(f32x4_t*)d = St[0];
+        *(f32x4_t*)(d + 16) = St[1];
       }
     } else {
       if (n1.valid) dma(nxt, n1, 0);
@@ -1346,8 +1368,17 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
     }
     lds_barrier();  // B1: R is exchanged
     if (chain) {
-      // (3) U = T'' R, U' = diag(gamma_C / gamma) U -> exchange. T'' rows of
-      // block I < 2 have no second step: that step multiplies by zeros.
+      // (3) U = T'' R, U' = diag(gamma_C / gamma) U -> exchange; the K^T
+      // fragments of phase (5) are read with R
+      bf16x8_t rh[2], rl[2];
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        rh[kf] = join_frag(rx[0][2 * kf][lane], rx[0][2 * kf + 1][lane]);
+        rl[kf] = join_frag(rx[1][2 * kf][lane], rx[1][2 * kf + 1][lane]);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) kt[kf][jb] = kt_frag<DK>(Ks, 32 * w + 16 * jb, kf, lane);
+      }
+      SCAN_FENCE();
 #pragma unroll
       for (int bb = 0; bb < C::TB; ++bb) {
         const int I = w + C::NW * bb;
@@ -1355,18 +1386,15 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf) {
           const bool live = kf < frag_nk(I);
-          const bf16x8_t rh = join_or_zero(live, rx[0][2 * kf][lane], rx[0][2 * kf + 1][lane]);
-          const bf16x8_t rl = join_or_zero(live, rx[1][2 * kf][lane], rx[1][2 * kf + 1][lane]);
-          const u32x4_t* tf = (const u32x4_t*)(cur + C::OT) + (frag_tri(I) + (live ? kf : 0)) * 128 + lane;
-          const bf16x8_t th = __builtin_bit_cast(bf16x8_t, tf[0]);
-          const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, tf[64]);
-          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh, U, 0, 0, 0);
-          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl, U, 0, 0, 0);
-          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh, U, 0, 0, 0);
+          const u32x4_t z4 = {0u, 0u, 0u, 0u};
+          const bf16x8_t h = live ? rh[kf] : __builtin_bit_cast(bf16x8_t, z4);
+          const bf16x8_t l = live ? rl[kf] : __builtin_bit_cast(bf16x8_t, z4);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th[bb][kf], h, U, 0, 0, 0);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th[bb][kf], l, U, 0, 0, 0);
+          U = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl[bb][kf], h, U, 0, 0, 0);
         }
-        const f32x4_t rq = *(const f32x4_t*)(rrp + 16 * I + 4 * q4);
         split4(U, ux[0][I][lane], ux[1][I][lane]);
-        split4(U * rq, ux[2][I][lane], ux[3][I][lane]);
+        split4(U * rq[bb], ux[2][I][lane], ux[3][I][lane]);
         yx[I][lane] = Yt[bb];
       }
     } else {
@@ -1377,20 +1405,22 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
     lds_barrier();  // B2: U and U' are exchanged
     if (chain) {
       // (5) S^T = gamma_C S^T + K^T U'; then the end state, or the next S fragments
+      bf16x8_t uh[2], ul[2];
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        uh[kf] = join_frag(ux[2][2 * kf][lane], ux[2][2 * kf + 1][lane]);
+        ul[kf] = join_frag(ux[3][2 * kf][lane], ux[3][2 * kf + 1][lane]);
+      }
       const float gC = gam[CH - 1];
       St[0] *= gC;
       St[1] *= gC;
 #pragma unroll
-      for (int kf = 0; kf < 2; ++kf) {
-        const bf16x8_t uh = join_frag(ux[2][2 * kf][lane], ux[2][2 * kf + 1][lane]);
-        const bf16x8_t ul = join_frag(ux[3][2 * kf][lane], ux[3][2 * kf + 1][lane]);
+      for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const bf16x8_t kt = kt_frag<DK>(Ks, 32 * w + 16 * jb, kf, lane);
-          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, uh, St[jb], 0, 0, 0);
-          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ul, St[jb], 0, 0, 0);
+          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[kf][jb], uh[kf], St[jb], 0, 0, 0);
+          St[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[kf][jb], ul[kf], St[jb], 0, 0, 0);
         }
-      }
       if (last) {
         const size_t srow = (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
         if (args.seg_final) {
