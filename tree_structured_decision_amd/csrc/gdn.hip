@@ -166,7 +166,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
   __shared__ float As[CH * LDA];
   __shared__ float Ts[CH * LDA];
   __shared__ float Zs[4][16 * 20];
-  __shared__ float gs[CH], bs[CH];
+  __shared__ __attribute__((aligned(16))) float gs[CH];
+  __shared__ __attribute__((aligned(16))) float bs[CH];
 
   const int nchunks = blob[MH_NCHUNKS];
   const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
@@ -255,14 +256,20 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
           qk[J] = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk[J]);
         }
       }
+      // the decays and b of this lane's rows and columns, read once
+      const f32x4_t gi4 = *(const f32x4_t*)(gs + 16 * w + 4 * q4);
+      const f32x4_t bi4 = *(const f32x4_t*)(bs + 16 * w + 4 * q4);
+      float gj[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) gj[J] = gs[16 * J + c16];
       lds_barrier();  // every wave is done reading Ks / Qs
 #pragma unroll
       for (int J = 0; J < 4; ++J)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * w + 4 * q4 + r, j = 16 * J + c16;
-          const float dec = j <= i ? __expf(gs[i] - gs[j]) : 0.f;
-          As[i * LDA + j] = j < i ? bs[i] * dec * kk[J][r] : 0.f;
+          const float dec = j <= i ? __expf(gi4[r] - gj[J]) : 0.f;
+          As[i * LDA + j] = j < i ? bi4[r] * dec * kk[J][r] : 0.f;
           Ps[i * LDA + j] = dec * qk[J][r];
         }
     }
