@@ -187,8 +187,8 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   }
 
   // Split plan: when the tiles are too few to keep every resident workgroup
-  // busy, a tile whose key-tile count exceeds the fair share P of the total
-  // work is cut into parts of about P key tiles; each part writes a partial
+  // busy, a tile whose key-tile count exceeds the share P = total /
+  // kAttnSlots is cut into parts of about P key tiles; each part writes a partial
   // result (normalised output and log-sum-exp per row) that a merge pass
   // combines. P doubles until the partial slots fit the workspace.
   const int64_t Hkv = caps->kv_heads;

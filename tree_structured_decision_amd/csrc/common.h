@@ -66,11 +66,13 @@ constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
 constexpr int kAttnRows = 256;              // query rows (token x GQA head) per attention tile
 constexpr int kAttnKeys = 64;               // keys per staged key/value tile
 constexpr int kMaxDepthCap = 4096;
-// Split plan for query tiles with long key ranges: the target number of
-// concurrently resident attention workgroups (1 per CU on a 256-CU MI355X),
-// the smallest part (in 64-key tiles), the most parts per tile, and the
-// partial-result slots the workspace holds (parts x kv heads).
-constexpr int kAttnSlots = 256;
+// Split plan for query tiles with long key ranges: the number of shares the
+// total work is cut into (the part size is total / kAttnSlots key tiles;
+// about 1.6 parts per resident workgroup on a 256-CU MI355X, measured best
+// on the one-request tree), the smallest part (in 64-key tiles), the most
+// parts per tile, and the partial-result slots the workspace holds (parts x
+// kv heads).
+constexpr int kAttnSlots = 416;
 constexpr int kMinPartTiles = 4;
 constexpr int kMaxSplit = 16;
 constexpr int kMaxPartSlots = 1024;
