@@ -692,17 +692,43 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
   // the grid is a multiple of 8), so item i runs on XCD i mod 8. Heads are
   // assigned so that all slice groups of one head share an XCD and its L2.
   const int NH8 = (H + 7) / 8;
-  for (int item = blockIdx.x; item < nlev * NH8 * 8 * C::NG; item += gridDim.x) {
-    const int x = item & 7, j = item >> 3;
-    const int sg = j % C::NG, j2 = j / C::NG;
-    const int h = (j2 % NH8) * 8 + x, li = j2 / NH8;
-    if (h >= H) continue;
+  const int nitems = nlev * NH8 * 8 * C::NG;
+  // work item -> (segment, head, slice group); uniform (scalar loads)
+  struct ItemRef {
+    int item, s, h, sg, L, st, cb;
+  };
+  auto find_item = [&](int from) {
+    ItemRef r;
+    r.item = nitems;
+    for (int it = from; it < nitems; it += gridDim.x) {
+      const int x = it & 7, j = it >> 3, j2 = j / C::NG;
+      const int h = (j2 % NH8) * 8 + x;
+      if (h >= H) continue;
+      r.item = it;
+      r.sg = j % C::NG;
+      r.h = h;
+      r.s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + j2 / NH8]);
+      r.L = __builtin_amdgcn_readfirstlane(seg_len[r.s]);
+      r.st = __builtin_amdgcn_readfirstlane(seg_start[r.s]);
+      r.cb = __builtin_amdgcn_readfirstlane(chunk_base[r.s]);
+      break;
+    }
+    return r;
+  };
+  // The first chunk of the workgroup's next item is prefetched during the
+  // current item's last chunk, so only the first item waits for its loads.
+  PF nx;
+  ItemRef cur = find_item(blockIdx.x);
+  if (cur.item < nitems) {
+    prefetch_kq<BF16, DK>(nx, Kg, Qg, cur.st, min(CH, cur.L), H, cur.h, tid);
+    prefetch_rest<BF16, DK>(nx, Vg, args.ws + ((size_t)cur.cb * H + cur.h) * kWsChunk, cur.st, min(CH, cur.L), H,
+                            cur.h, C::VW * cur.sg, tid);
+  }
+  for (; cur.item < nitems;) {
+    const ItemRef nxi = find_item(cur.item + gridDim.x);
+    const int sg = cur.sg, h = cur.h, s = cur.s, L = cur.L, st = cur.st, cb = cur.cb;
     // per-item metadata, uniform across the workgroup (scalar loads)
-    const int s = __builtin_amdgcn_readfirstlane(level_seg[lv0 + li]);
     const int p = __builtin_amdgcn_readfirstlane(parent[s]);
-    const int L = __builtin_amdgcn_readfirstlane(seg_len[s]);
-    const int st = __builtin_amdgcn_readfirstlane(seg_start[s]);
-    const int cb = __builtin_amdgcn_readfirstlane(chunk_base[s]);
     const int fc_p = p >= 0 ? __builtin_amdgcn_readfirstlane(first_child[p]) : -1;
     const int ro = p < 0 ? __builtin_amdgcn_readfirstlane(root_ord[s]) : 0;
     const int ve0 = C::VW * sg;    // first v column (state row) of the group
@@ -732,9 +758,6 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
       const f32x4_t xv = *(const f32x4_t*)(lsrc + srow + 16 * db);
       St[db] = has_src ? xv : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    PF nx;
-    prefetch_kq<BF16, DK>(nx, Kg, Qg, st, min(CH, L), H, h, tid);
-    prefetch_rest<BF16, DK>(nx, Vg, args.ws + ((size_t)cb * H + h) * kWsChunk, st, min(CH, L), H, h, ve0, tid);
     if (dst) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) *(f32x4_t*)(dst + srow + 16 * db) = St[db];
@@ -785,7 +808,10 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
         stage_rest<BF16, DK>(cur, nx, tid);
         __syncthreads();
       }
-      if (more) prefetch_kq<BF16, DK>(nx, Kg, Qg, nt0, nlen, H, h, tid);
+      if (more)
+        prefetch_kq<BF16, DK>(nx, Kg, Qg, nt0, nlen, H, h, tid);
+      else if (nxi.item < nitems)
+        prefetch_kq<BF16, DK>(nx, Kg, Qg, nxi.st, min(CH, nxi.L), H, nxi.h, tid);
 
       // (1) X = K S^T and Y^T = S Q^T, LDS reads one reduction step ahead
       f32x4_t X[4], Yt[4];
@@ -850,7 +876,11 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
         }
         SCAN_FENCE();
       }
-      if (more) prefetch_rest<BF16, DK>(nx, Vg, nws, nt0, nlen, H, h, ve0, tid);
+      if (more)
+        prefetch_rest<BF16, DK>(nx, Vg, nws, nt0, nlen, H, h, ve0, tid);
+      else if (nxi.item < nitems)
+        prefetch_rest<BF16, DK>(nx, Vg, args.ws + ((size_t)nxi.cb * H + nxi.h) * kWsChunk, nxi.st, min(CH, nxi.L),
+                                H, nxi.h, C::VW * nxi.sg, tid);
       flush_o();
 
       // (2) R = V - gamma X  (lane (c16, q4), block I holds rows 16 I + 4 q4 + r)
@@ -965,6 +995,7 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
         if (d2) *(f32x4_t*)(d2 + srow + 16 * db) = St[db];
       }
     }
+    cur = nxi;
   }
 }
 
