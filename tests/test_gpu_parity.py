@@ -131,6 +131,21 @@ def test_long_segment_chain_ragged_tail():
     full_check(wl)
 
 
+def test_gdn_depth_split_mixed():
+    """Depths that mix long segments (several chunks: the chunk-cooperative
+    scan while they fit one round of workgroups) with short ones (the
+    per-slice scan), two roots with a root state, ragged tails, a segment of
+    exactly one chunk, and a third depth whose long segments are too many for
+    the cooperative scan."""
+    parent = np.array([-1, -1, 0, 0, 0, 1, 1, 2, 2, 2, 5, 5, 5], np.int32)
+    seg_len = np.array([300, 150, 70, 30, 64, 129, 65, 200, 90, 3, 66, 130, 17], np.int32)
+    for gH in (16, 4):
+        log(f"depth split: gH={gH}")
+        wl = W.make_workload("split", "bf16", parent, seg_len, H=8, Hkv=2, D=128, gH=gH, dk=128,
+                             dv=128, gates="sigmoid", root_state_std=0.1, seed=4242 + gH)
+        full_check(wl, attn=False)
+
+
 # ---------------------------------------------------------------- workloads
 
 def test_tiny_one_level_full():
