@@ -14,7 +14,11 @@ Also reported on the same JSON line:
   fidelity      total-variation distance of per-option softmax scores vs the
                 float32 oracle, argmax agreement;
   workloads     throughput of all five synthetic workloads (the request mix
-                runs as graph replay of a capacity bucket).
+                runs as graph replay of a capacity bucket);
+  rates         option tokens/s, isolated-equivalent tokens/s, us per option;
+  cold_cache    the layer pair's kernel times with caches evicted between steps;
+  measured_peaks  a bf16 GEMM and a device copy on this GPU, the achievable
+                peaks the roofline fraction is also given against.
 """
 from __future__ import annotations
 
@@ -42,19 +46,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per call of `kernel` from the committed counter runs
-    (profiles/hbm_traffic.json), or None when the kernel's source has changed
-    since those counters were taken."""
+def sources_sha256() -> str:
+    """Hash of every native source (kernels, host plan, public header): the
+    counter runs stand only for the code they were taken on."""
     import hashlib
 
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_structured_decision_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../include/fork.h"]:
+        path = os.path.join(csrc, f)
+        if os.path.isfile(path):
+            h.update(f.encode())
+            h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per call of `kernel` from the committed counter runs
+    (profiles/hbm_traffic.json), or None when any native source has changed
+    since those counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))[kernel]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
     except (OSError, KeyError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if rec.get("sources_sha256") != sources_sha256():
         return None
     return dict(bytes=rec["read_bytes"] + rec["write_bytes"], read=rec["read_bytes"],
                 write=rec["write_bytes"], workload=rec["workload"], summary=rec["summary"])
@@ -88,6 +104,56 @@ def gdn_work(parent, seg_len, H, dk, dv, elt, root_state: bool):
     fork = S * H * dk * dv * 4                         # every segment's start state written once
     rs = R * H * dk * dv * 4 if root_state else 0
     return float(io + fork + rs)
+
+
+def tree_rates(parent, seg_len):
+    """Option (leaf) count, option tokens and isolated-equivalent tokens (sum
+    over leaves of the leaf's root-to-leaf path length: what per-branch
+    recompute would process)."""
+    parent = np.asarray(parent)
+    seg_len = np.asarray(seg_len, np.int64)
+    S = len(parent)
+    anc = np.zeros(S, np.int64)
+    has_child = np.zeros(S, bool)
+    for s in range(S):
+        if parent[s] >= 0:
+            anc[s] = anc[parent[s]] + seg_len[parent[s]]
+            has_child[parent[s]] = True
+    leaves = ~has_child
+    return int(leaves.sum()), int(seg_len[leaves].sum()), int((anc + seg_len)[leaves].sum())
+
+
+def measured_peaks():
+    """Achievable peaks on this GPU: a bf16 8192^3 GEMM (the vendor library,
+    dense) and a 1 GiB device-to-device copy."""
+    import torch
+
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * 8192 ** 3 * n / (e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * (1 << 30) * n / (e0.elapsed_time(e1) * 1e-3)  # read + write bytes
+    del src, dst
+    return dict(bf16_gemm_tflops=gemm / 1e12, copy_gbs=copy / 1e9)
 
 
 # ------------------------------------------------------------------ runners
@@ -157,7 +223,10 @@ class Runner:
             ev[2].record()
 
 
-def time_runner(r: Runner, steps: int, warmup: int):
+def time_runner(r: Runner, steps: int, warmup: int, evict=None):
+    """Times `steps` steps after `warmup`. evict: a large device buffer written
+    before every timed step (outside the kernel events), so that the step's
+    inputs come from HBM rather than the L2 / Infinity Cache."""
     import torch
 
     for _ in range(warmup):
@@ -166,6 +235,8 @@ def time_runner(r: Runner, steps: int, warmup: int):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
+        if evict is not None:
+            evict.fill_(k & 0xff)
         r.step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -255,6 +326,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-workloads", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache and measured-peak passes (counter runs of the warm step)")
     ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with three plain 512 MiB device copies (counter calibration)")
@@ -284,6 +357,12 @@ def main():
     r = Runner(meta, tensors_from_numpy(wl), graph=False)
     log(f"headline {wl.name}: T={wl.T} S={wl.S}; warmup {args.warmup}, steps {args.steps}")
     res = time_runner(r, args.steps, args.warmup)
+    import torch
+    cold = None
+    if not args.no_cold:
+        evict = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = time_runner(r, max(10, args.steps // 2), 2, evict=evict)
+        del evict
     T = wl.T
     fl, ab = attn_work(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, 2)
     gb = gdn_work(wl.parent, wl.seg_len, wl.gH, wl.dk, wl.dv, 2, wl.root_state is not None)
@@ -328,6 +407,18 @@ def main():
                    gdn=metrics.decision_fidelity(go_gpu, go_ref, wl.w_gdn, wl.parent, wl.seg_len),
                    reference="float32 oracle")
 
+    n_opt, opt_tok, iso_tok = tree_rates(wl.parent, wl.seg_len)
+    step_s = res["ms_per_step"] * 1e-3
+    rates = dict(options=n_opt, option_tokens_per_s=opt_tok / step_s,
+                 isolated_equivalent_tokens_per_s=iso_tok / step_s, us_per_option=step_s / n_opt * 1e6,
+                 note="per step (wall); isolated-equivalent = sum over options of root-to-option path length")
+    peaks = None
+    if not args.no_cold:
+        peaks = measured_peaks()
+        if roof["bound"] == "mfma":
+            roof["frac_measured_peak"] = roof["achieved"] / peaks["bf16_gemm_tflops"]
+        else:
+            roof["frac_measured_peak"] = roof["achieved"] / peaks["copy_gbs"]
     out = {
         "metric": METRIC,
         "value": T / (res["ms_per_step"] * 1e-3),
@@ -351,6 +442,13 @@ def main():
         "layer_pair_p50_us": res["pair_p50"] * 1e6,
         "layer_pair_p95_us": res["pair_p95"] * 1e6,
         "fidelity": fid,
+        "rates": rates,
+        "cold_cache": None if cold is None else dict(
+            pair_p50_us=cold["pair_p50"] * 1e6, attn_p50_us=cold["attn_p50"] * 1e6,
+            gdn_p50_us=cold["gdn_p50"] * 1e6,
+            note="512 MiB written between steps (outside the kernel events) to evict the L2 and "
+                 "the Infinity Cache"),
+        "measured_peaks": peaks,
     }
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
