@@ -224,14 +224,26 @@ class Runner:
 
 
 def time_runner(r: Runner, steps: int, warmup: int, evict=None):
-    """Times `steps` steps after `warmup`. evict: a large device buffer written
-    before every timed step (outside the kernel events), so that the step's
-    inputs come from HBM rather than the L2 / Infinity Cache."""
+    """Times `steps` steps after `warmup`, twice: first the plain steps between
+    two synchronisations (the wall time per step: nothing else is enqueued),
+    then the same number of steps with HIP events around each layer (per-layer
+    durations; an event record costs a few microseconds of GPU time, so this
+    pass is not the one the wall time comes from). evict: a large device buffer
+    written before every step of the event pass (outside the events), so that
+    the step's inputs come from HBM rather than the L2 / Infinity Cache; then
+    the wall pass is skipped."""
     import torch
 
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
+    wall = None
+    if evict is None:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            r.step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
@@ -239,7 +251,8 @@ def time_runner(r: Runner, steps: int, warmup: int, evict=None):
             evict.fill_(k & 0xff)
         r.step(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if wall is None:
+        wall = time.perf_counter() - t0
     if r.graph:
         pair = [e[0].elapsed_time(e[2]) for e in evs]
         attn = gdn = None
