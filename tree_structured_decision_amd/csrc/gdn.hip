@@ -122,6 +122,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+// hi and lo bf16 parts of four floats (one accumulator block of a lane)
+__device__ __forceinline__ void split4(const f32x4_t& x, u32x2_t& hi, u32x2_t& lo) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const unsigned w = pack_bf16x2(x[2 * p], x[2 * p + 1]);
+    hi[p] = w;
+    lo[p] = pack_bf16x2(x[2 * p] - __uint_as_float(w << 16), x[2 * p + 1] - __uint_as_float(w & 0xffff0000u));
+  }
+}
 
 struct GdnArgs {
   const int32_t* blob;
@@ -151,23 +161,115 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // ---------------------------------------------------------------------------
 // Prep: per (chunk, head) compute g, T'' = (I + A)^-1 diag(b), P = QK^T * Gamma.
+//
+// The products are formed transposed: wave w computes, for each 16-column
+// block J <= w, Pt_J = K_J Q_w^T and At_J = K_J K_w^T. Their accumulators give
+// lane (c16, q4) row i = 16 w + c16 of QK^T (or of KK^T) at columns
+// j = 16 J + 4 q4 + r, r = 0..3: the elements of a P fragment of row block w in
+// the scan's reduction order, so P goes to the workspace straight from
+// registers, and a row of A goes to LDS as one 16-byte store per block.
+// Blocks J > w lie above the diagonal and are zero.
+// T = (I + A)^-1 is then formed block-wise: the four diagonal 16x16 blocks by
+// forward substitution (one block per wave), the blocks below the diagonal by
+// distance, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
+
+// DPP lane moves: row_shr:n, and quad permutations (lane ^ 1, lane ^ 2).
+// Lanes without a source read zero.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppRowShr = 0x110;    // + n: row_shr:n (within rows of 16 lanes)
+constexpr int kDppQuadXor1 = 0xb1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;   // quad_perm [2,3,0,1]
+__device__ __forceinline__ float lane_val(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (within rows of 16 lanes by
+// DPP shifts, then each row adds the totals of the rows before it).
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+  x += dpp_mov<kDppRowShr + 1>(x);
+  x += dpp_mov<kDppRowShr + 2>(x);
+  x += dpp_mov<kDppRowShr + 4>(x);
+  x += dpp_mov<kDppRowShr + 8>(x);
+  const float r0 = lane_val(x, 15), r1 = lane_val(x, 31), r2 = lane_val(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+
+// Diagonal block [b0, b0 + 16)^2 of T = (I + A)^-1 by forward substitution,
+// x_i = e_i - sum_{j<i} A_ij x_j for the 16 columns, by one wave with four lanes
+// per column (lane = 4 c + p): lane (c, p) owns the unknowns x_{4p+t} of column
+// c and holds A[i][b0 + 4p + t] for every row i. Rows are solved in groups of
+// four: the sum over the groups already solved is four partial sums added
+// across the quad, then the lanes p of the group finish its rows in order.
+// A's entries on and above the diagonal are zero.
+__device__ __forceinline__ void diag_inverse(const float* __restrict__ As, float* __restrict__ Ts, int lda,
+                                             int b0, int lane) {
+  const int c = lane >> 2, p = lane & 3;
+  f32x4_t a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = *(const f32x4_t*)(As + (b0 + i) * lda + b0 + 4 * p);
+  f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    float sm[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4_t& ai = a[4 * blk + r];
+      float v = ai[0] * x[0] + ai[1] * x[1] + ai[2] * x[2] + ai[3] * x[3];
+      v += dpp_mov<kDppQuadXor1>(v);
+      v += dpp_mov<kDppQuadXor2>(v);
+      sm[r] = v;
+    }
+    const bool mine = p == blk;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * blk + r;
+      float v = (i == c ? 1.f : 0.f) - sm[r];
+#pragma unroll
+      for (int t = 0; t < r; ++t) v -= a[i][t] * x[t];
+      x[r] = mine ? v : x[r];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) Ts[(b0 + 4 * p + t) * lda + b0 + c] = x[t];
+}
+
 template <bool BF16, int DK>
-__global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
+struct PrepCfg {
+  using G = GT<BF16>;
+  static constexpr int LDK = DK + G::PAD;
+  static constexpr int LDA = CH + 4;  // fp32 64x64 tiles
+  // K and Q tiles; once the products are formed, the same bytes hold A (fp32)
+  static constexpr int KQ_BYTES = 2 * CH * LDK * (int)sizeof(typename G::E);
+  static constexpr int KQA_BYTES = KQ_BYTES > CH * LDA * 4 ? KQ_BYTES : CH * LDA * 4;
+  static constexpr int LDS = KQA_BYTES + CH * LDA * 4 + 4 * CH * 4;
+  // workgroups per CU: as many as the LDS holds, up to 3 (bf16; the register
+  // budget of 3 waves per SIMD) or 2 (fp32)
+  static constexpr int FIT = 160 * 1024 / LDS;
+  static constexpr int WANT = BF16 ? 3 : 2;
+  static constexpr int PER_CU = FIT < 1 ? 1 : (FIT < WANT ? FIT : WANT);
+};
+
+template <bool BF16, int DK>
+__global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
+    gdn_prep_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
   using G = GT<BF16>;
   using E = typename G::E;
-  constexpr int LDK = DK + G::PAD;
-  constexpr int LDA = CH + 4;  // fp32 64x64 tiles
-  // K and Q tiles; once the products are formed, the same bytes hold P (fp32)
-  constexpr size_t KQ_BYTES = 2 * CH * LDK * sizeof(E);
-  constexpr size_t KQP_BYTES = KQ_BYTES > CH * LDA * 4 ? KQ_BYTES : CH * LDA * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char kqp[KQP_BYTES];
-  E* Ks = (E*)kqp;
+  using C = PrepCfg<BF16, DK>;
+  constexpr int LDK = C::LDK, LDA = C::LDA;
+  constexpr int NKS = DK / G::KSTEP;  // reduction steps of the products
+  __shared__ __attribute__((aligned(16))) unsigned char kqa[C::KQA_BYTES];
+  E* Ks = (E*)kqa;
   E* Qs = Ks + CH * LDK;
-  __shared__ float As[CH * LDA];
-  __shared__ float Ts[CH * LDA];
-  __shared__ float Zs[4][16 * 20];
-  __shared__ __attribute__((aligned(16))) float gs[CH];
-  __shared__ __attribute__((aligned(16))) float bs[CH];
+  float* As = (float*)kqa;
+  __shared__ __attribute__((aligned(16))) float Ts[CH * LDA];
+  // g and b of the chunk, two copies by item parity (an item's writes never
+  // meet the previous item's reads, so items need no barrier between them)
+  __shared__ __attribute__((aligned(16))) float gsb[2][CH];
+  __shared__ __attribute__((aligned(16))) float bsb[2][CH];
 
   const int nchunks = blob[MH_NCHUNKS];
   const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
@@ -203,11 +305,15 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
   };
   if (blockIdx.x < nchunks * H) prep_load(blockIdx.x);
 
-  for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x) {
+  int par = 0;
+  for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x, par ^= 1) {
     const int c = item / H, h = item - c * H;
     unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
+    float* gs = gsb[par];
+    float* bs = bsb[par];
 
-    lds_barrier();  // LDS reuse across items
+    // ---- stage K and Q; wave 0: g = inclusive cumulative sum of log a
+    // (padding rows: a = 1, b = 0)
     const int len = rlen;
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -217,156 +323,146 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(const int32_t* __restrict
       *(u32x4_t*)(Qs + row * LDK + ch * G::EPC) = row < len ? rq[i] : z4;
     }
     if (w == 0) {
-      // g = inclusive cumulative sum of log a (padding: a = 1, b = 0)
-      const int i = lane;
-      float la = i < len ? logf(ra) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(la, off);
-        if (i >= off) la += y;
-      }
-      gs[i] = la;
-      bs[i] = i < len ? rb : 0.f;
+      const float la = wave_incl_scan(lane < len ? logf(ra) : 0.f, lane);
+      gs[lane] = la;
+      bs[lane] = lane < len ? rb : 0.f;
       if constexpr (BF16) {
-        const float gl = __shfl(la, CH - 1);
-        ((float*)(wsb + kWsGam))[i] = __expf(la);
-        ((float*)(wsb + kWsGam))[CH + i] = __expf(gl - la);
+        const float gl = lane_val(la, CH - 1);
+        ((float*)(wsb + kWsGam))[lane] = __expf(la);
+        ((float*)(wsb + kWsGam))[CH + lane] = __expf(gl - la);
       } else {
-        ((float*)(wsb + 2 * kWsPlane))[i] = la;
+        ((float*)(wsb + 2 * kWsPlane))[lane] = la;
       }
     }
-    // zero Ts (upper blocks stay zero)
-    for (int i = tid; i < CH * LDA; i += 256) Ts[i] = 0.f;
-    lds_barrier();
     if (item + (int)gridDim.x < nchunks * H) prep_load(item + gridDim.x);
+    lds_barrier();  // K, Q, g and b are staged
 
-    // K K^T -> A (strictly lower, scaled);  Q K^T -> P (lower incl. diagonal).
-    // P is staged in LDS over the K/Q tiles (dead once every wave has its
-    // products) and written out below in 16-byte groups.
-    float* Ps = (float*)kqp;
+    // ---- products Pt_J = K_J Q_w^T, At_J = K_J K_w^T (J <= w)
+    f32x4_t pt[4], at[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) pt[J] = at[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
-      f32x4_t kk[4], qk[4];
+      typename G::F bq[NKS], bk[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        bq[ks] = ld_rowk<BF16>(Qs, LDK, 16 * w + c16, ks * G::KSTEP, q4);
+        bk[ks] = ld_rowk<BF16>(Ks, LDK, 16 * w + c16, ks * G::KSTEP, q4);
+      }
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        kk[J] = qk[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (J <= w) {
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += G::KSTEP) {
-          const typename G::F bK = ld_rowk<BF16>(Ks, LDK, 16 * J + c16, k0, q4);
-          kk[J] = mma<BF16>(ld_rowk<BF16>(Ks, LDK, 16 * w + c16, k0, q4), bK, kk[J]);
-          qk[J] = mma<BF16>(ld_rowk<BF16>(Qs, LDK, 16 * w + c16, k0, q4), bK, qk[J]);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const typename G::F aK = ld_rowk<BF16>(Ks, LDK, 16 * J + c16, ks * G::KSTEP, q4);
+            pt[J] = mma<BF16>(aK, bq[ks], pt[J]);
+            at[J] = mma<BF16>(aK, bk[ks], at[J]);
+          }
         }
       }
-      // the decays and b of this lane's rows and columns, read once
-      const f32x4_t gi4 = *(const f32x4_t*)(gs + 16 * w + 4 * q4);
-      const f32x4_t bi4 = *(const f32x4_t*)(bs + 16 * w + 4 * q4);
-      float gj[4];
+    }
+    const int i = 16 * w + c16;  // this lane's row of P and A
+    const float gi = gs[i], bi = bs[i];
+    f32x4_t gj4[4];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) gj[J] = gs[16 * J + c16];
-      lds_barrier();  // every wave is done reading Ks / Qs
+    for (int J = 0; J < 4; ++J) gj4[J] = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
+    lds_barrier();  // every wave is done reading Ks / Qs (A overwrites them)
+
+    // ---- decays: P_ij = exp(g_i - g_j) (q_i . k_j) for j <= i, and
+    // A_ij = b_i exp(g_i - g_j) (k_i . k_j) for j < i; A rows to LDS, P out
+    f32x4_t pv[4];
 #pragma unroll
-      for (int J = 0; J < 4; ++J)
+    for (int J = 0; J < 4; ++J) {
+      pv[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (J <= w) {
+        f32x4_t av;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * w + 4 * q4 + r, j = 16 * J + c16;
-          const float dec = j <= i ? __expf(gi4[r] - gj[J]) : 0.f;
-          As[i * LDA + j] = j < i ? bi4[r] * dec * kk[J][r] : 0.f;
-          Ps[i * LDA + j] = dec * qk[J][r];
+          const int j = 16 * J + 4 * q4 + r;
+          const float dec = j <= i ? __expf(gi - gj4[J][r]) : 0.f;
+          pv[J][r] = dec * pt[J][r];
+          av[r] = j < i ? bi * dec * at[J][r] : 0.f;
         }
+        *(f32x4_t*)(As + i * LDA + 16 * J + 4 * q4) = av;
+      }
     }
+    if constexpr (BF16) {
+      u32x4_t* Pw = (u32x4_t*)(wsb + kWsFrag);
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        if (kf < frag_nk(w)) {
+          const int fb = frag_tri(w) + kf;
+          u32x2_t h0, l0, h1, l1;
+          split4(pv[2 * kf], h0, l0);
+          split4(pv[2 * kf + 1], h1, l1);
+          Pw[(2 * fb) * 64 + lane] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+          Pw[(2 * fb + 1) * 64 + lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
+        }
+      }
+    } else {
+      float* Pw = (float*)(wsb + kWsPlane);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) *(f32x4_t*)(Pw + i * CH + 16 * J + 4 * q4) = pv[J];
+    }
+
+    // ---- diagonal blocks of T (wave w: block w; its rows of A are its own stores)
+    diag_inverse(As, Ts, LDA, 16 * w, lane);
     lds_barrier();
 
-    // diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution
-    if (lane < 16) {
-      const int base = 16 * w, col = lane;
-      float x[16];
+    // ---- blocks below the diagonal, by distance d = I - J (wave w: J = w).
+    // Z = sum_K A_IK T_KJ comes out of the MFMA in accumulator order (lane
+    // (c16, q4) holds Z[4 q4 + r][c16]), which is the B operand of T_II Z when
+    // the reduction index of step r is 4 q4 + r; T_II is read in that order.
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == col) ? 1.f : 0.f;
+    for (int d = 1; d < 4; ++d) {
+      const int I = w + d, J = w;
+      if (I < 4) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        for (int Kb = J; Kb < I; ++Kb) {
+          const f32x4_t a4 = *(const f32x4_t*)(As + (16 * I + c16) * LDA + 16 * Kb + 4 * q4);
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc -= As[(base + i) * LDA + base + j] * x[j];
-        x[i] = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Ts[(base + i) * LDA + base + col] = x[i];
-    }
-    lds_barrier();
-
-    // off-diagonal blocks: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, by distance
-#pragma unroll
-    for (int dist = 1; dist < 4; ++dist) {
-      const int I = w + dist, J = w;
-      const bool act = I < 4;
-      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      if (act) {
-        for (int Kb = J; Kb < I; ++Kb)
-#pragma unroll
-          for (int k0 = 0; k0 < 16; k0 += 4)
-            z = mma_f32(As[(16 * I + c16) * LDA + 16 * Kb + k0 + q4],
-                        Ts[(16 * Kb + k0 + q4) * LDA + 16 * J + c16], z);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Zs[w][(4 * q4 + r) * 20 + c16] = z[r];
-      }
-      lds_barrier();
-      if (act) {
+          for (int r = 0; r < 4; ++r) z = mma_f32(a4[r], Ts[(16 * Kb + 4 * q4 + r) * LDA + 16 * J + c16], z);
+        }
+        const f32x4_t t4 = *(const f32x4_t*)(Ts + (16 * I + c16) * LDA + 16 * I + 4 * q4);
         f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4)
-          t = mma_f32(Ts[(16 * I + c16) * LDA + 16 * I + k0 + q4], Zs[w][(k0 + q4) * 20 + c16], t);
+        for (int r = 0; r < 4; ++r) t = mma_f32(t4[r], z[r], t);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * q4 + r) * LDA + 16 * J + c16] = -t[r];
       }
       lds_barrier();
     }
 
-    // T'' = T diag(b) and P -> workspace
+    // ---- T'' = T diag(b) (zero above the diagonal) -> workspace
     if constexpr (BF16) {
       // operand fragments, hi and lo planes, one 16-byte group per task
       for (int task = tid; task < kNtri * 64; task += 256) {
-        const int bi = task >> 6, l = task & 63;
-        const int I = bi < 3 ? bi : (bi == 3 ? 2 : 3), kf = bi - frag_tri(I);
-        const int i = 16 * I + (l & 15), j0 = 32 * kf + 4 * (l >> 4);
-        float tv[8], pv[8];
+        const int fb = task >> 6, l = task & 63;
+        const int I = fb < 3 ? fb : (fb == 3 ? 2 : 3), kf = fb - frag_tri(I);
+        const int ti = 16 * I + (l & 15), j0 = 32 * kf + 4 * (l >> 4);
+        f32x4_t t0, t1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + (e & 3) + 16 * (e >> 2);
-          tv[e] = Ts[i * LDA + j] * bs[j];
-          pv[e] = Ps[i * LDA + j];
+        for (int e = 0; e < 4; ++e) {
+          t0[e] = j0 + e <= ti ? Ts[ti * LDA + j0 + e] * bs[j0 + e] : 0.f;
+          t1[e] = j0 + 16 + e <= ti ? Ts[ti * LDA + j0 + 16 + e] * bs[j0 + 16 + e] : 0.f;
         }
-        u32x4_t th, tlo, ph, plo;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const unsigned wt = pack_bf16x2(tv[2 * q], tv[2 * q + 1]);
-          th[q] = wt;
-          tlo[q] = pack_bf16x2(tv[2 * q] - __uint_as_float(wt << 16), tv[2 * q + 1] - __uint_as_float(wt & 0xffff0000u));
-          const unsigned wp = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
-          ph[q] = wp;
-          plo[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(wp << 16), pv[2 * q + 1] - __uint_as_float(wp & 0xffff0000u));
-        }
+        u32x2_t h0, l0, h1, l1;
+        split4(t0, h0, l0);
+        split4(t1, h1, l1);
         u32x4_t* Tw = (u32x4_t*)wsb;
-        u32x4_t* Pw = (u32x4_t*)(wsb + kWsFrag);
-        Tw[(2 * bi) * 64 + l] = th;
-        Tw[(2 * bi + 1) * 64 + l] = tlo;
-        Pw[(2 * bi) * 64 + l] = ph;
-        Pw[(2 * bi + 1) * 64 + l] = plo;
+        Tw[(2 * fb) * 64 + l] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+        Tw[(2 * fb + 1) * 64 + l] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
       }
     } else {
-      // row-major fp32 planes, 8 consecutive elements of a row per task
+      // row-major fp32 plane, 8 consecutive elements of a row per task
 #pragma unroll
       for (int k = 0; k < CH * CH / 8 / 256; ++k) {
-        const int idx8 = tid + 256 * k, i = idx8 >> 3, j0 = (idx8 & 7) * 8;
-        float tv[8], pv[8];
+        const int idx8 = tid + 256 * k, ti = idx8 >> 3, j0 = (idx8 & 7) * 8;
+        float tv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          tv[e] = Ts[i * LDA + j0 + e] * bs[j0 + e];
-          pv[e] = Ps[i * LDA + j0 + e];
-        }
-        const size_t off = (size_t)i * CH + j0;  // element offset in a 64 x 64 plane
-        float* Tw = (float*)wsb;
-        float* Pw = (float*)(wsb + kWsPlane);
-        *(f32x4_t*)(Tw + off) = f32x4_t{tv[0], tv[1], tv[2], tv[3]};
-        *(f32x4_t*)(Tw + off + 4) = f32x4_t{tv[4], tv[5], tv[6], tv[7]};
-        *(f32x4_t*)(Pw + off) = f32x4_t{pv[0], pv[1], pv[2], pv[3]};
-        *(f32x4_t*)(Pw + off + 4) = f32x4_t{pv[4], pv[5], pv[6], pv[7]};
+        for (int e = 0; e < 8; ++e) tv[e] = j0 + e <= ti ? Ts[ti * LDA + j0 + e] * bs[j0 + e] : 0.f;
+        float* Tw = (float*)wsb + (size_t)ti * CH + j0;
+        *(f32x4_t*)Tw = f32x4_t{tv[0], tv[1], tv[2], tv[3]};
+        *(f32x4_t*)(Tw + 4) = f32x4_t{tv[4], tv[5], tv[6], tv[7]};
       }
     }
   }
@@ -586,8 +682,6 @@ __device__ __forceinline__ void stage_rest(const ScanTiles<BF16, DK>& b, const S
     }
   }
 }
-
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Reduction step f of accumulator blocks X[] as an operand fragment (hi part,
 // and in bf16 mode the lo part x - hi). Values are converted in pairs: one
@@ -1081,15 +1175,6 @@ template <int DK>
 __device__ __forceinline__ f32x4_t st_read(const float* t, int r, int col) {
   return *(const f32x4_t*)(t + r * DK + 4 * ((col >> 2) ^ (r & 7)));
 }
-// hi and lo bf16 parts of four floats (one accumulator block of a lane)
-__device__ __forceinline__ void split4(const f32x4_t& x, u32x2_t& hi, u32x2_t& lo) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const unsigned w = pack_bf16x2(x[2 * p], x[2 * p + 1]);
-    hi[p] = w;
-    lo[p] = pack_bf16x2(x[2 * p] - __uint_as_float(w << 16), x[2 * p + 1] - __uint_as_float(w & 0xffff0000u));
-  }
-}
 __device__ __forceinline__ bf16x8_t join_frag(u32x2_t a, u32x2_t b) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
 }
@@ -1531,7 +1616,7 @@ template <bool BF16, int DK>
 fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const bool cap = stream_capturing(stream);
   const int cus = device_cu_count();
-  int grid = 2 * cus;
+  int grid = PrepCfg<BF16, DK>::PER_CU * cus;
   if (!cap) {
     const long long items = (long long)m->num_chunks * a.H;
     if (items < grid) grid = (int)(items > 0 ? items : 1);
