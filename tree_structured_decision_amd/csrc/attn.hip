@@ -287,13 +287,24 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
   // it started with, so their keys and values stay in its L2. The counters are
   // zero when the blob is built; the last workgroup to run out of work resets
   // them for the next launch.
+  // The first item of a workgroup is static (item blockIdx.x: the XCD's
+  // counter starts past the first items of its workgroups), so no workgroup
+  // waits on a contended counter at the start. The next item is requested
+  // when the current item's last key tile starts, so the request's latency
+  // is hidden behind that tile's compute while the assignment stays dynamic.
   const int xcd = blockIdx.x & (kNumXcd - 1);
+  const int per_xcd = gridDim.x / kNumXcd;
+  int item = blockIdx.x;
   for (;;) {
-    __syncthreads();  // every thread has read the previous item
-    if (tid == 0) s_item = atomicAdd(args.ctr + xcd, 1) * kNumXcd + xcd;
-    __syncthreads();
-    const int item = s_item;
     if (item >= nitems) break;
+    bool requested = false;
+    int nxt = 0;  // thread 0: the XCD counter's value for the next item
+    auto request_next = [&]() {
+      if (!requested) {
+        requested = true;
+        if (tid == 0) nxt = atomicAdd(args.ctr + xcd, 1);
+      }
+    };
     const int ti = item / Hkv, g = item - ti * Hkv;
     AttnTile tile;  // uniform across the workgroup: keep it in scalar registers
     tile.t0 = __builtin_amdgcn_readfirstlane(tiles[ti].t0);
@@ -305,7 +316,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     tile.slot = __builtin_amdgcn_readfirstlane(tiles[ti].slot);
 
     // this lane's query row (rows past the tile are clamped and not stored)
-    const int r = wave * 32 + l32;
+    // per item, from the thread id: the row math is recomputed rather than
+    // kept in registers (or spilled) across the key loop
+    int tt = (int)threadIdx.x;
+    asm volatile("" : "+v"(tt));
+    const int r = (tt >> 6) * 32 + (tt & 31);
     const int tl = r / G, hg = r - tl * G;
     const bool valid = tl < TT && tile.t0 + tl < tile.t1;
     const int t_row = valid ? tile.t0 + tl : tile.t1 - 1;
@@ -314,13 +329,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
 
     QF qf[C::NKF];
     {
+      int hq = hi;
+      asm volatile("" : "+v"(hq));  // (as r above: no 64-bit base + hi offset kept across items)
       const E* qrow = Q + ((size_t)t_row * H + h) * D;
 #pragma unroll
       for (int ks = 0; ks < C::NKF; ++ks) {
         if constexpr (BF16)
-          qf[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * hi);
+          qf[ks] = *(const bf16x8_t*)(qrow + 16 * ks + 8 * hq);
         else
-          qf[ks] = qrow[2 * ks + hi];
+          qf[ks] = qrow[2 * ks + hq];
       }
     }
 
@@ -522,6 +539,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
           __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
         --nq;
+        // the last tile: every DMA of this wave has landed, so the request
+        // (a returning atomic, counted with them) delays no tile wait
+        if (nq == 0 && it.done) request_next();
         issue(fill, fslot);
         kv_compute((const E*)cur, (const E*)(cur + C::TILE_BYTES), pj[slot], ph[slot], po[slot]);
       };
@@ -545,51 +565,98 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         kv_store<BF16, D, E>(rg, Ks, Vt, tid);
         __syncthreads();
         iter_next(it, tile, parent, seg_start, seg_len);
-        if (!it.done) kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+        if (!it.done)
+          kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+        else
+          request_next();
         kv_compute(Ks, Vt, j0, hi_, own);
       }
     }
 
+    // the next item: requested at the last tile, long returned by now; written
+    // before this item's stores are issued, so reading it waits for nothing
+    // (every thread read the current item before the first tile's barrier)
+    request_next();  // (an item whose tiles never triggered it)
+    if (tid == 0) s_item = (nxt + per_xcd) * kNumXcd + xcd;
+    // s_item is visible, and every wave is done with the last key/value tile
+    // (its buffers stage the output below); this barrier waits for no store
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int next_item = s_item;
+
     // finalize: normalise; whole tiles store the output, parts of a split tile
-    // store fp32 partials (normalised rows + log-sum-exp) for the merge pass
+    // store their normalised rows (output dtype) and log-sum-exps into the
+    // tile's slot for the merge pass
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_row = l_tot > 0.f ? m_run * 0.6931471805599453f + __logf(l_tot) : -INFINITY;
-    // whole tiles store the output row; parts of a split tile store their
-    // normalised row (output dtype) and log-sum-exp into the tile's slot
     constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;
     unsigned char* part = tile.slot >= 0 ? args.ws + ((size_t)tile.slot * Hkv + g) * SLOT : nullptr;
-    if (valid) {
-      E* orow = tile.slot >= 0 ? (E*)part + r * D : O + ((size_t)t_row * H + h) * D;
+    if (valid && hi == 0) {
+      if (tile.slot >= 0)
+        ((float*)((E*)part + kAttnRows * D))[r] = lse_row;
+      else if (args.lse)
+        args.lse[(size_t)t_row * H + h] = lse_row;
+    }
+    if constexpr (BF16) {
+      // A lane's accumulators hold 4-element pieces of one row (the piece at d
+      // = 32 db + 8 rq + 4 hi), so storing them directly writes 8 bytes into
+      // each of 32 rows per instruction. Instead each wave stages its 32 rows
+      // in the free key/value buffers (rows padded by 16 bytes against bank
+      // conflicts) and stores whole rows, 16 bytes per lane: one instruction
+      // writes D * 2 * 64 / 16 contiguous bytes per row group.
+      constexpr int OST = D * 2 + 16;  // bytes per staged row
+      static_assert(3 * 32 * OST <= C::BUF_BYTES, "three waves' rows per buffer");
+      // lane-derived indices are recomputed here rather than hoisted out of
+      // the item loop, where they would hold registers through the key loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      unsigned char* stg = (wv < 3 ? lds0 : wv < 6 ? lds1 : lds2) + (wv % 3) * 32 * OST;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = 32 * db + 8 * rq + 4 * hi;
-          const float v0 = oacc[db][4 * rq + 0] * inv, v1 = oacc[db][4 * rq + 1] * inv;
-          const float v2 = oacc[db][4 * rq + 2] * inv, v3 = oacc[db][4 * rq + 3] * inv;
-          if constexpr (BF16) {
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            bf16x2_t p0, p1;
-            p0[0] = (__bf16)v0;
-            p0[1] = (__bf16)v1;
-            p1[0] = (__bf16)v2;
-            p1[1] = (__bf16)v3;
-            uint2 pk;
-            pk.x = __builtin_bit_cast(unsigned, p0);
-            pk.y = __builtin_bit_cast(unsigned, p1);
-            *(uint2*)(orow + d0) = pk;
-          } else {
-            *(float4*)(orow + d0) = make_float4(v0, v1, v2, v3);
-          }
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          bf16x2_t p0, p1;
+          p0[0] = (__bf16)(oacc[db][4 * rq + 0] * inv);
+          p0[1] = (__bf16)(oacc[db][4 * rq + 1] * inv);
+          p1[0] = (__bf16)(oacc[db][4 * rq + 2] * inv);
+          p1[1] = (__bf16)(oacc[db][4 * rq + 3] * inv);
+          uint2 pk;
+          pk.x = __builtin_bit_cast(unsigned, p0);
+          pk.y = __builtin_bit_cast(unsigned, p1);
+          *(uint2*)(stg + (ln & 31) * OST + 2 * (32 * db + 8 * rq + 4 * (ln >> 5))) = pk;
         }
-      if (hi == 0) {
-        if (tile.slot >= 0)
-          ((float*)((E*)part + kAttnRows * D))[r] = lse_row;
-        else if (args.lse)
-          args.lse[(size_t)t_row * H + h] = lse_row;
+      constexpr int LPR = D * 2 / 16;  // lanes per row
+      constexpr int RPI = 64 / LPR;    // rows per store instruction
+      constexpr int NST = 32 / RPI;    // store instructions per wave
+      // all reads first (one LDS round trip), then the stores
+      u32x4_t v[NST];
+#pragma unroll
+      for (int k = 0; k < NST; ++k) v[k] = *(const u32x4_t*)(stg + (k * RPI + ln / LPR) * OST + 16 * (ln % LPR));
+#pragma unroll
+      for (int k = 0; k < NST; ++k) {
+        const int rr = wv * 32 + k * RPI + ln / LPR;
+        const int tl2 = rr / G, hg2 = rr - tl2 * G;
+        if (tl2 < TT && tile.t0 + tl2 < tile.t1) {
+          E* dst = tile.slot >= 0 ? (E*)part + rr * D : O + ((size_t)(tile.t0 + tl2) * H + g * G + hg2) * D;
+          *(u32x4_t*)(dst + 8 * (ln % LPR)) = v[k];
+        }
+      }
+    } else {
+      if (valid) {
+        E* orow = tile.slot >= 0 ? (E*)part + r * D : O + ((size_t)t_row * H + h) * D;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = 32 * db + 8 * rq + 4 * hi;
+            *(float4*)(orow + d0) = make_float4(oacc[db][4 * rq + 0] * inv, oacc[db][4 * rq + 1] * inv,
+                                                oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
+          }
       }
     }
+    item = next_item;
   }
   if (tid == 0 && atomicAdd(args.ctr + kNumXcd, 1) == (int)gridDim.x - 1) {
     // every other workgroup has taken its last item: reset for the next launch
