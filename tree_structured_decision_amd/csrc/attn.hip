@@ -294,7 +294,50 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
   // is hidden behind that tile's compute while the assignment stays dynamic.
   const int xcd = blockIdx.x & (kNumXcd - 1);
   const int per_xcd = gridDim.x / kNumXcd;
+  // quotients by G of row indices < 256 (G <= 128): (n + 1/2) / G in fp32 is
+  // off by far less than 1 / (2 G), so truncation gives the exact quotient
+  const float inv_g = 1.f / (float)G;
+  auto div_g = [&](int n) { return (int)(((float)n + 0.5f) * inv_g); };
+
+  // The current item's tile (uniform across the workgroup: scalar registers)
+  // and kv head; the next item's are loaded, and its first key/value tile's
+  // DMA issued, while the current item's output is stored.
+  AttnTile tile;
+  int g = 0;
+  auto load_tile = [&](int itm) {
+    const int tix = itm / Hkv;
+    g = itm - tix * Hkv;
+    tile.t0 = __builtin_amdgcn_readfirstlane(tiles[tix].t0);
+    tile.t1 = __builtin_amdgcn_readfirstlane(tiles[tix].t1);
+    tile.own_lo = __builtin_amdgcn_readfirstlane(tiles[tix].own_lo);
+    tile.info = __builtin_amdgcn_readfirstlane(tiles[tix].info);
+    tile.kt0 = __builtin_amdgcn_readfirstlane(tiles[tix].kt0);
+    tile.kt1 = __builtin_amdgcn_readfirstlane(tiles[tix].kt1);
+    tile.slot = __builtin_amdgcn_readfirstlane(tiles[tix].slot);
+  };
+  TileIter it;
+  // bf16 key/value tiles in flight: DMA of the iterator's next tile into a
+  // buffer, with the tile's range kept per buffer slot
+  int pj[3], ph[3];
+  bool po[3];
+  int nq = 0;  // tiles issued and not yet computed
+  auto issue = [&](unsigned char* buf, int slot) {
+    if (it.done) return;
+    pj[slot] = it.j0;
+    ph[slot] = it.hi;
+    po[slot] = it.own;
+    if constexpr (BF16) kv_dma<D>(buf, K, V, it.j0, it.hi - 1, g, Hkv, wave, lane);
+    ++nq;
+    iter_next(it, tile, parent, seg_start, seg_len);
+  };
+  auto start_item = [&](int itm) {
+    load_tile(itm);
+    iter_init(it, tile, parent, seg_start, seg_len);
+    if constexpr (BF16) issue(lds2, 2);  // an item's first tile goes to lds2
+  };
+
   int item = blockIdx.x;
+  if (item < nitems) start_item(item);
   for (;;) {
     if (item >= nitems) break;
     bool requested = false;
@@ -305,15 +348,6 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         if (tid == 0) nxt = atomicAdd(args.ctr + xcd, 1);
       }
     };
-    const int ti = item / Hkv, g = item - ti * Hkv;
-    AttnTile tile;  // uniform across the workgroup: keep it in scalar registers
-    tile.t0 = __builtin_amdgcn_readfirstlane(tiles[ti].t0);
-    tile.t1 = __builtin_amdgcn_readfirstlane(tiles[ti].t1);
-    tile.own_lo = __builtin_amdgcn_readfirstlane(tiles[ti].own_lo);
-    tile.info = __builtin_amdgcn_readfirstlane(tiles[ti].info);
-    tile.kt0 = __builtin_amdgcn_readfirstlane(tiles[ti].kt0);
-    tile.kt1 = __builtin_amdgcn_readfirstlane(tiles[ti].kt1);
-    tile.slot = __builtin_amdgcn_readfirstlane(tiles[ti].slot);
 
     // this lane's query row (rows past the tile are clamped and not stored)
     // per item, from the thread id: the row math is recomputed rather than
@@ -321,7 +355,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     int tt = (int)threadIdx.x;
     asm volatile("" : "+v"(tt));
     const int r = (tt >> 6) * 32 + (tt & 31);
-    const int tl = r / G, hg = r - tl * G;
+    const int tl = div_g(r), hg = r - tl * G;
     const bool valid = tl < TT && tile.t0 + tl < tile.t1;
     const int t_row = valid ? tile.t0 + tl : tile.t1 - 1;
     const int h = g * G + (valid ? hg : 0);
@@ -505,33 +539,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       pv(1);
     };
 
-    TileIter it;
-    iter_init(it, tile, parent, seg_start, seg_len);
     if constexpr (BF16) {
       // Software pipeline over three LDS buffers: the DMAs of tiles i+1 and
       // i+2 are in flight while tile i computes. Per tile: wait for this
       // wave's DMA of tile i (its DMA of tile i+1 may stay in flight), one
       // barrier (every wave's DMA of tile i landed; every wave is done with
       // tile i-1, whose buffer tile i+2 then fills), issue that DMA, compute.
-      // The loop is unrolled by three so that each step reads and fills fixed
-      // buffers.
+      // Tiles cycle through lds2, lds0, lds1 (tile 0 was issued into lds2
+      // while the previous item stored its output); the loop is unrolled by
+      // three so that each step reads and fills fixed buffers.
       constexpr int DMA_PER_TILE = 2 * (kAttnKeys * D * 2 / 1024) / (kAttnThreads / 64);
       static_assert(DMA_PER_TILE < 16, "vmcnt field");
-      __syncthreads();  // the previous item's last tiles are no longer read
-      int pj[3], ph[3];
-      bool po[3];
-      int nq = 0;  // tiles issued and not yet computed
-      auto issue = [&](unsigned char* buf, int slot) {
-        if (it.done) return;
-        pj[slot] = it.j0;
-        ph[slot] = it.hi;
-        po[slot] = it.own;
-        kv_dma<D>(buf, K, V, it.j0, it.hi - 1, g, Hkv, wave, lane);
-        ++nq;
-        iter_next(it, tile, parent, seg_start, seg_len);
-      };
+      __syncthreads();  // the previous item's output rows staged in lds0 / lds1 are read
       issue(lds0, 0);
-      issue(lds1, 1);
       auto step = [&](unsigned char* cur, int slot, unsigned char* fill, int fslot) {
         if (nq > 1)
           __builtin_amdgcn_s_waitcnt(0x0f70 | DMA_PER_TILE);  // vmcnt: tile i landed, i+1 may fly
@@ -546,11 +566,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         kv_compute((const E*)cur, (const E*)(cur + C::TILE_BYTES), pj[slot], ph[slot], po[slot]);
       };
       while (nq > 0) {
+        step(lds2, 2, lds1, 1);
+        if (nq == 0) break;
         step(lds0, 0, lds2, 2);
         if (nq == 0) break;
         step(lds1, 1, lds0, 0);
-        if (nq == 0) break;
-        step(lds2, 2, lds1, 1);
       }
     } else {
       // fp32: registers hold tile i+1 while tile i computes
@@ -579,9 +599,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     request_next();  // (an item whose tiles never triggered it)
     if (tid == 0) s_item = (nxt + per_xcd) * kNumXcd + xcd;
     // s_item is visible, and every wave is done with the last key/value tile
-    // (its buffers stage the output below); this barrier waits for no store
+    // (its buffers are reused below); this barrier waits for no store
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int next_item = s_item;
+    // this item's tile fields for the stores below; then the next item's tile
+    // record and first DMA, in flight while this item's output is stored
+    const int f_t0 = tile.t0, f_t1 = tile.t1, f_slot = tile.slot, f_g = g;
+    if (next_item < nitems) start_item(next_item);
 
     // finalize: normalise; whole tiles store the output, parts of a split tile
     // store their normalised rows (output dtype) and log-sum-exps into the
@@ -590,9 +614,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_row = l_tot > 0.f ? m_run * 0.6931471805599453f + __logf(l_tot) : -INFINITY;
     constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;
-    unsigned char* part = tile.slot >= 0 ? args.ws + ((size_t)tile.slot * Hkv + g) * SLOT : nullptr;
+    unsigned char* part = f_slot >= 0 ? args.ws + ((size_t)f_slot * Hkv + f_g) * SLOT : nullptr;
     if (valid && hi == 0) {
-      if (tile.slot >= 0)
+      if (f_slot >= 0)
         ((float*)((E*)part + kAttnRows * D))[r] = lse_row;
       else if (args.lse)
         args.lse[(size_t)t_row * H + h] = lse_row;
@@ -601,17 +625,21 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       // A lane's accumulators hold 4-element pieces of one row (the piece at d
       // = 32 db + 8 rq + 4 hi), so storing them directly writes 8 bytes into
       // each of 32 rows per instruction. Instead each wave stages its 32 rows
-      // in the free key/value buffers (rows padded by 16 bytes against bank
-      // conflicts) and stores whole rows, 16 bytes per lane: one instruction
-      // writes D * 2 * 64 / 16 contiguous bytes per row group.
-      constexpr int OST = D * 2 + 16;  // bytes per staged row
-      static_assert(3 * 32 * OST <= C::BUF_BYTES, "three waves' rows per buffer");
+      // in lds0 (waves 0-3) or lds1 (waves 4-7), the 16-byte chunk c of row r
+      // at position c ^ (r mod LPR) against bank conflicts, and stores whole
+      // rows, 16 bytes per lane.
+      constexpr int ORB = D * 2;       // bytes per staged row
+      constexpr int LPR = ORB / 16;    // lanes (16-byte chunks) per row
+      constexpr int RPI = 64 / LPR;    // rows per store instruction
+      constexpr int NST = 32 / RPI;    // store instructions per wave
+      static_assert(4 * 32 * ORB <= C::BUF_BYTES, "four waves' rows per buffer");
       // lane-derived indices are recomputed here rather than hoisted out of
       // the item loop, where they would hold registers through the key loop
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int wv = __builtin_amdgcn_readfirstlane(wave);
-      unsigned char* stg = (wv < 3 ? lds0 : wv < 6 ? lds1 : lds2) + (wv % 3) * 32 * OST;
+      unsigned char* stg = (wv < 4 ? lds0 : lds1) + (wv & 3) * 32 * ORB;
+      const int srow = ln & 31;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -625,27 +653,28 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
           uint2 pk;
           pk.x = __builtin_bit_cast(unsigned, p0);
           pk.y = __builtin_bit_cast(unsigned, p1);
-          *(uint2*)(stg + (ln & 31) * OST + 2 * (32 * db + 8 * rq + 4 * (ln >> 5))) = pk;
+          const int ch = 4 * db + rq;  // 16-byte chunk of the row
+          *(uint2*)(stg + srow * ORB + 16 * (ch ^ (srow % LPR)) + 8 * (ln >> 5)) = pk;
         }
-      constexpr int LPR = D * 2 / 16;  // lanes per row
-      constexpr int RPI = 64 / LPR;    // rows per store instruction
-      constexpr int NST = 32 / RPI;    // store instructions per wave
       // all reads first (one LDS round trip), then the stores
       u32x4_t v[NST];
 #pragma unroll
-      for (int k = 0; k < NST; ++k) v[k] = *(const u32x4_t*)(stg + (k * RPI + ln / LPR) * OST + 16 * (ln % LPR));
+      for (int k = 0; k < NST; ++k) {
+        const int rl = k * RPI + ln / LPR;
+        v[k] = *(const u32x4_t*)(stg + rl * ORB + 16 * ((ln % LPR) ^ (rl % LPR)));
+      }
 #pragma unroll
       for (int k = 0; k < NST; ++k) {
         const int rr = wv * 32 + k * RPI + ln / LPR;
-        const int tl2 = rr / G, hg2 = rr - tl2 * G;
-        if (tl2 < TT && tile.t0 + tl2 < tile.t1) {
-          E* dst = tile.slot >= 0 ? (E*)part + rr * D : O + ((size_t)(tile.t0 + tl2) * H + g * G + hg2) * D;
+        const int tl2 = div_g(rr), hg2 = rr - tl2 * G;
+        if (tl2 < TT && f_t0 + tl2 < f_t1) {
+          E* dst = f_slot >= 0 ? (E*)part + rr * D : O + ((size_t)(f_t0 + tl2) * H + f_g * G + hg2) * D;
           *(u32x4_t*)(dst + 8 * (ln % LPR)) = v[k];
         }
       }
     } else {
       if (valid) {
-        E* orow = tile.slot >= 0 ? (E*)part + r * D : O + ((size_t)t_row * H + h) * D;
+        E* orow = f_slot >= 0 ? (E*)part + r * D : O + ((size_t)t_row * H + h) * D;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
