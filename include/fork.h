@@ -65,6 +65,8 @@ typedef struct fork_caps {
   int32_t kv_heads;   /* Hkv of those layers, or 0. When given, query tiles with long
                          key ranges are split into parts (merged by log-sum-exp) so a
                          small tree still fills the GPU; see fork_attn_workspace. */
+  int32_t ctx_cap;    /* rows of the key/value cache that cached contexts index
+                         (fork_meta_build_ctx), or 0: no cached context */
 } fork_caps;
 
 /* Depths whose segment counts a fork_meta carries for launch planning. */
@@ -98,7 +100,9 @@ enum {
   FORK_ARR_SEG_START = 3,    /* [S] first token of each segment */
   FORK_ARR_DEPTH = 4,        /* [S] number of ancestors */
   FORK_ARR_ANC_LEN = 5,      /* [S] total tokens of the ancestors */
-  FORK_ARR_ROOT = 6          /* [S] root segment of each segment */
+  FORK_ARR_ROOT = 6,         /* [S] root segment of each segment */
+  FORK_ARR_CTX_START = 7,    /* [S] first cache row of each root's context (0 if none) */
+  FORK_ARR_CTX_LEN = 8       /* [S] cached context rows of each root (0 for non-roots) */
 };
 
 /* Bytes of device memory (dev) and of host staging a blob with these
@@ -133,6 +137,31 @@ fork_status fork_meta_plan(const int32_t* parent_h, const int32_t* seg_len_h,
                            void* staging_h, size_t staging_bytes,
                            size_t* upload_bytes_h, fork_meta* out_h);
 
+/*
+ * Checkpoint resume: roots whose prefix was computed by an earlier pass. The
+ * keys and values of that prefix stay in a caller-owned cache kc/vc
+ * [ctx_cap, Hkv, D] and the stream holds only the new segments (Flide,
+ * kongchang.com page, section "ForkAttention: exact forking in GPU indices":
+ * growing agent histories resume from checkpoints saved by earlier passes
+ * instead of being recomputed; the recurrent state of the prefix is the
+ * root_state of gdn_fork_forward). For
+ * root s, ctx_len_h[s] >= 0 cache rows from ctx_start_h[s] precede its first
+ * token: every token of s's tree attends to them, and tok_iso_pos counts
+ * them. Several roots may name the same rows (siblings resumed from one
+ * shared prefix). Non-roots must have ctx_len_h 0. Ranges must lie within
+ * [0, caps.ctx_cap). Both arrays null: no context (as fork_meta_build).
+ * Attention over such a blob goes through fork_attn_forward_ctx.
+ */
+fork_status fork_meta_build_ctx(const int32_t* parent_h, const int32_t* seg_len_h,
+                                const int32_t* ctx_start_h, const int32_t* ctx_len_h,
+                                int32_t num_segments, const fork_caps* caps_h, void* dev,
+                                size_t dev_bytes, void* staging_h, size_t staging_bytes,
+                                fork_meta* out_h, void* stream);
+fork_status fork_meta_plan_ctx(const int32_t* parent_h, const int32_t* seg_len_h,
+                               const int32_t* ctx_start_h, const int32_t* ctx_len_h,
+                               int32_t num_segments, const fork_caps* caps_h, void* staging_h,
+                               size_t staging_bytes, size_t* upload_bytes_h, fork_meta* out_h);
+
 /* Copy one metadata array (FORK_ARR_*) from the device into dst_h (int32,
  * T or S entries). Synchronises the stream. For tests. */
 fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_h, void* stream);
@@ -163,6 +192,15 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
                               void* o, float* lse, int32_t H, int32_t Hkv, int32_t D,
                               float scale, fork_dtype dt, void* ws, size_t ws_bytes,
                               void* stream);
+/* The same with cached contexts (fork_meta_build_ctx): kc/vc [caps.ctx_cap, Hkv, D]
+ * of dtype dt hold the resumed prefixes' keys and values; required (non-null)
+ * when caps.ctx_cap > 0. Each context is read like a fully visible ancestor
+ * range. fork_attn_forward is this call with no cache and requires
+ * caps.ctx_cap == 0. */
+fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void* k, const void* v,
+                                  const void* kc, const void* vc, void* o, float* lse, int32_t H,
+                                  int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------- Gated DeltaNet
  * Forked Gated DeltaNet: per head, the dv x dk state follows
@@ -216,6 +254,9 @@ typedef struct fork_graph_args {
   void* gdn_ws;
   size_t gdn_ws_bytes;
   fork_dtype dt;
+  /* key/value cache of resumed contexts, [caps.ctx_cap, Hkv, D]; required when
+     caps.ctx_cap > 0, else null */
+  const void *kc, *vc;
 } fork_graph_args;
 
 typedef struct fork_graph fork_graph;

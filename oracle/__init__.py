@@ -51,6 +51,9 @@ def _lib(prec: str):
         vp = ctypes.c_void_p
         c_int = ctypes.c_int
         lib.oracle_meta.argtypes = [c_int, i32p, i32p] + [i32p] * 7
+        lib.oracle_meta_ctx.argtypes = [c_int, i32p, i32p, vp] + [i32p] * 7
+        lib.oracle_attention_ctx.argtypes = [c_int, i32p, i32p, vp, vp, c_int, c_int, c_int,
+                                             ctypes.c_double, f32p, f32p, f32p, vp, vp, vp, rp, vp]
         lib.oracle_mask.argtypes = [c_int, i32p, i32p, np.ctypeslib.ndpointer(np.uint8)]
         lib.oracle_attention.argtypes = [c_int, i32p, i32p, c_int, c_int, c_int, ctypes.c_double,
                                          f32p, f32p, f32p, vp, rp, vp]
@@ -93,16 +96,20 @@ def num_tokens(parent, seg_len) -> int:
     return int(T.value)
 
 
-def meta(parent, seg_len) -> dict:
-    """Segment and token index arrays (int32), see ``oracle_meta``."""
+def meta(parent, seg_len, ctx_len=None) -> dict:
+    """Segment and token index arrays (int32), see ``oracle_meta``; with
+    ``ctx_len`` ([S], roots only) the positions count resumed contexts
+    (``oracle_meta_ctx``)."""
     parent, seg_len = _tree(parent, seg_len)
     S = len(parent)
     T = num_tokens(parent, seg_len)
     out = {n: np.zeros(S, np.int32) for n in ("seg_start", "depth", "root", "anc_len")}
     out.update({n: np.zeros(T, np.int32) for n in ("tok_seg", "tok_pos", "tok_iso_pos")})
-    _check(_lib("f64").oracle_meta(S, parent, seg_len, out["seg_start"], out["depth"], out["root"],
-                                   out["anc_len"], out["tok_seg"], out["tok_pos"],
-                                   out["tok_iso_pos"]))
+    cl = None if ctx_len is None else np.ascontiguousarray(ctx_len, np.int32)
+    _check(_lib("f64").oracle_meta_ctx(S, parent, seg_len, None if cl is None else cl.ctypes.data,
+                                       out["seg_start"], out["depth"], out["root"],
+                                       out["anc_len"], out["tok_seg"], out["tok_pos"],
+                                       out["tok_iso_pos"]))
     return out
 
 
@@ -116,10 +123,13 @@ def mask(parent, seg_len) -> np.ndarray:
 
 
 def attention(parent, seg_len, q, k, v, scale: Optional[float] = None, prec: str = "f64",
-              tok_select: Optional[np.ndarray] = None):
+              tok_select: Optional[np.ndarray] = None, ctx_start=None, ctx_len=None, kc=None,
+              vc=None):
     """Tree attention by isolated per-segment sequences.
     q [T,H,D], k/v [T,Hkv,D] float32. Returns (o [T,H,D], lse [T,H]) in the
-    oracle's precision; rows outside ``tok_select`` are NaN."""
+    oracle's precision; rows outside ``tok_select`` are NaN. Resumed contexts:
+    ctx_start/ctx_len [S] (roots only) index rows of kc/vc [C,Hkv,D] that
+    precede the root's tokens (``oracle_attention_ctx``)."""
     parent, seg_len = _tree(parent, seg_len)
     q = np.ascontiguousarray(q, np.float32)
     k = np.ascontiguousarray(k, np.float32)
@@ -135,9 +145,19 @@ def attention(parent, seg_len, q, k, v, scale: Optional[float] = None, prec: str
     if tok_select is not None:
         sel = np.ascontiguousarray(tok_select, np.uint8)
         assert sel.shape == (T,)
-    _check(_lib(prec).oracle_attention(len(parent), parent, seg_len, H, Hkv, D, float(scale),
-                                       q, k, v, None if sel is None else sel.ctypes.data, o,
-                                       lse.ctypes.data))
+    cs = cl = kcc = vcc = None
+    if ctx_len is not None:
+        cs = np.ascontiguousarray(ctx_start, np.int32)
+        cl = np.ascontiguousarray(ctx_len, np.int32)
+        kcc = np.ascontiguousarray(kc, np.float32)
+        vcc = np.ascontiguousarray(vc, np.float32)
+        assert cs.shape == cl.shape == (len(parent),) and kcc.shape == vcc.shape
+        assert kcc.shape[1:] == (Hkv, D) and int((cs + cl).max(initial=0)) <= kcc.shape[0]
+    ptr = lambda x: None if x is None else x.ctypes.data
+    _check(_lib(prec).oracle_attention_ctx(len(parent), parent, seg_len, ptr(cs), ptr(cl), H, Hkv,
+                                           D, float(scale), q, k, v, ptr(kcc), ptr(vcc),
+                                           None if sel is None else sel.ctypes.data, o,
+                                           lse.ctypes.data))
     return o, lse
 
 

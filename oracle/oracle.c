@@ -100,11 +100,38 @@ int oracle_num_tokens(int S, const int32_t* parent, const int32_t* seg_len, long
  *   tok_iso_pos[t] = anc_len[seg] + tok_pos[t], the token's position in the
  *                    isolated sequence of its segment.
  */
+/* Resumed contexts (kongchang.com page, section "ForkAttention: exact forking
+ * in GPU indices": agent histories resume from checkpoints of earlier passes).
+ * ctx_len[s] (nullable) cached tokens precede root s; non-roots have none. */
+static int check_ctx(int S, const int32_t* parent, const int32_t* ctx_start, const int32_t* ctx_len) {
+  if ((ctx_start == NULL) != (ctx_len == NULL)) return ORACLE_E_ARG;
+  if (!ctx_len) return ORACLE_OK;
+  for (int s = 0; s < S; ++s)
+    if (ctx_len[s] < 0 || (ctx_len[s] > 0 && (parent[s] >= 0 || ctx_start[s] < 0))) return ORACLE_E_ARG;
+  return ORACLE_OK;
+}
+
+/* As oracle_meta, with the positions counting the root's resumed context:
+ * tok_iso_pos[t] = ctx_len[root] + anc_len[seg] + tok_pos[t]. */
+int oracle_meta_ctx(int S, const int32_t* parent, const int32_t* seg_len, const int32_t* ctx_len,
+                    int32_t* seg_start, int32_t* depth, int32_t* root, int32_t* anc_len,
+                    int32_t* tok_seg, int32_t* tok_pos, int32_t* tok_iso_pos);
+
 int oracle_meta(int S, const int32_t* parent, const int32_t* seg_len,
                 int32_t* seg_start, int32_t* depth, int32_t* root, int32_t* anc_len,
                 int32_t* tok_seg, int32_t* tok_pos, int32_t* tok_iso_pos) {
+  return oracle_meta_ctx(S, parent, seg_len, NULL, seg_start, depth, root, anc_len, tok_seg, tok_pos,
+                         tok_iso_pos);
+}
+
+int oracle_meta_ctx(int S, const int32_t* parent, const int32_t* seg_len, const int32_t* ctx_len,
+                    int32_t* seg_start, int32_t* depth, int32_t* root, int32_t* anc_len,
+                    int32_t* tok_seg, int32_t* tok_pos, int32_t* tok_iso_pos) {
   int e = check_tree(S, parent, seg_len);
   if (e) return e;
+  if (ctx_len)
+    for (int s = 0; s < S; ++s)
+      if (ctx_len[s] < 0 || (ctx_len[s] > 0 && parent[s] >= 0)) return ORACLE_E_ARG;
   int32_t acc = 0;
   for (int s = 0; s < S; ++s) {
     seg_start[s] = acc;
@@ -127,7 +154,7 @@ int oracle_meta(int S, const int32_t* parent, const int32_t* seg_len,
       int32_t t = seg_start[s] + i;
       tok_seg[t] = s;
       tok_pos[t] = i;
-      tok_iso_pos[t] = anc_len[s] + i;
+      tok_iso_pos[t] = (ctx_len ? ctx_len[root[s]] : 0) + anc_len[s] + i;
     }
   return ORACLE_OK;
 }
@@ -166,16 +193,39 @@ int oracle_mask(int S, const int32_t* parent, const int32_t* seg_len, uint8_t* m
  * s, head h, own token at isolated position n: z_j = scale * q.k_j over the
  * first n+1 tokens of X_s, m = max z, l = sum_j exp(z_j - m) in j order,
  * o = sum_j exp(z_j - m) v_j / l, lse = m + log l.
+ * With resumed contexts (ctx_start/ctx_len non-null, kc/vc [*, Hkv, D] float32),
+ * X_s begins with the context of s's root: cache rows ctx_start[r] ..
+ * ctx_start[r] + ctx_len[r] - 1 of kc/vc, before the ancestors' tokens.
  * tok_select (nullable, [T]): compute only the rows of tokens with a nonzero
  * flag. o [T,H,D], lse [T,H] (nullable). Rows not computed are left untouched.
  */
+int oracle_attention_ctx(int S, const int32_t* parent, const int32_t* seg_len,
+                         const int32_t* ctx_start, const int32_t* ctx_len,
+                         int H, int Hkv, int D, double scale,
+                         const float* q, const float* k, const float* v,
+                         const float* kc, const float* vc,
+                         const uint8_t* tok_select, REAL* o, REAL* lse);
+
 int oracle_attention(int S, const int32_t* parent, const int32_t* seg_len,
                      int H, int Hkv, int D, double scale,
                      const float* q, const float* k, const float* v,
                      const uint8_t* tok_select, REAL* o, REAL* lse) {
+  return oracle_attention_ctx(S, parent, seg_len, NULL, NULL, H, Hkv, D, scale, q, k, v, NULL, NULL,
+                              tok_select, o, lse);
+}
+
+int oracle_attention_ctx(int S, const int32_t* parent, const int32_t* seg_len,
+                         const int32_t* ctx_start, const int32_t* ctx_len,
+                         int H, int Hkv, int D, double scale,
+                         const float* q, const float* k, const float* v,
+                         const float* kc, const float* vc,
+                         const uint8_t* tok_select, REAL* o, REAL* lse) {
   int e = check_tree(S, parent, seg_len);
   if (e) return e;
   if (H <= 0 || Hkv <= 0 || D <= 0 || H % Hkv != 0 || !q || !k || !v || !o) return ORACLE_E_ARG;
+  e = check_ctx(S, parent, ctx_start, ctx_len);
+  if (e) return e;
+  if (ctx_len && (!kc || !vc)) return ORACLE_E_ARG;
   const int G = H / Hkv;
   int32_t* start = (int32_t*)malloc(sizeof(int32_t) * S);
   int32_t acc = 0;
@@ -192,11 +242,15 @@ int oracle_attention(int S, const int32_t* parent, const int32_t* seg_len,
       const int g = h / G;
       int32_t path[ORACLE_MAX_PATH];
       int np = build_path(s, parent, path, ORACLE_MAX_PATH);
-      /* token ids of X_s in order */
-      long long N = 0;
+      /* X_s in order: the root's context rows (cache row c as -1 - c), then
+         the stream token ids of the path's segments */
+      const int r = path[0];
+      const int nc = ctx_len ? ctx_len[r] : 0;
+      long long N = nc;
       for (int i = 0; i < np; ++i) N += seg_len[path[i]];
       int32_t* X = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
       long long n = 0;
+      for (int j = 0; j < nc; ++j) X[n++] = -1 - (ctx_start[r] + j);
       for (int i = 0; i < np; ++i)
         for (int j = 0; j < seg_len[path[i]]; ++j) X[n++] = start[path[i]] + j;
       REAL* z = (REAL*)malloc(sizeof(REAL) * (size_t)N);
@@ -207,7 +261,8 @@ int oracle_attention(int S, const int32_t* parent, const int32_t* seg_len,
         const float* qt = q + (t * H + h) * D;
         REAL m = -INFINITY;
         for (long long j = 0; j <= pos; ++j) {
-          const float* kj = k + ((long long)X[j] * Hkv + g) * D;
+          const float* kj = X[j] >= 0 ? k + ((long long)X[j] * Hkv + g) * D
+                                      : kc + ((long long)(-1 - X[j]) * Hkv + g) * D;
           REAL dot = 0;
           for (int d = 0; d < D; ++d) dot += (REAL)qt[d] * (REAL)kj[d];
           z[j] = (REAL)scale * dot;
@@ -222,7 +277,8 @@ int oracle_attention(int S, const int32_t* parent, const int32_t* seg_len,
         for (int d = 0; d < D; ++d) {
           REAL sacc = 0;
           for (long long j = 0; j <= pos; ++j)
-            sacc += z[j] * (REAL)v[((long long)X[j] * Hkv + g) * D + d];
+            sacc += z[j] * (REAL)(X[j] >= 0 ? v[((long long)X[j] * Hkv + g) * D + d]
+                                            : vc[((long long)(-1 - X[j]) * Hkv + g) * D + d]);
           ot[d] = sacc / l;
         }
         if (lse) lse[t * H + h] = m + log(l);

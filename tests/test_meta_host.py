@@ -20,7 +20,8 @@ H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS
            "OFF_PARENT", "OFF_SEGLEN", "OFF_SEGSTART", "OFF_DEPTH", "OFF_ROOT", "OFF_ROOTORD",
            "OFF_ANCLEN", "OFF_FIRSTCHILD", "OFF_CHUNKBASE", "OFF_LEVELOFF", "OFF_LEVELSEG",
            "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
-           "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS", "OFF_LEVELLONG"]
+           "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS", "OFF_LEVELLONG", "OFF_CTXSTART",
+           "OFF_CTXLEN", "NCTX"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
 ATTN_ROWS = int(re.search(r"kAttnRows = (\d+);", open(os.path.join(
     ROOT, "tree_structured_decision_amd", "csrc", "common.h")).read()).group(1))
@@ -43,13 +44,22 @@ def test_exports_every_declared_symbol():
     assert B.fork_version().startswith("forkattn")
 
 
-def plan(parent, seg_len, gqa=8, t_cap=None, s_cap=None, depth_cap=8, kv_heads=0):
+def plan(parent, seg_len, gqa=8, t_cap=None, s_cap=None, depth_cap=8, kv_heads=0, ctx=None,
+         ctx_cap=None):
+    """ctx: (ctx_start, ctx_len) int32 arrays of resumed contexts, or None."""
     parent = np.asarray(parent, np.int32)
     seg_len = np.asarray(seg_len, np.int32)
-    caps = B.make_caps(t_cap or int(seg_len.sum()), s_cap or len(parent), depth_cap, gqa, kv_heads)
+    if ctx_cap is None:
+        ctx_cap = 0 if ctx is None else int((ctx[0] + ctx[1]).max(initial=0))
+    caps = B.make_caps(t_cap or int(seg_len.sum()), s_cap or len(parent), depth_cap, gqa, kv_heads,
+                       ctx_cap)
     _, stg = B.fork_meta_size(caps)
     staging = np.zeros(stg // 4, np.int32)
-    meta, up = B.fork_meta_plan(parent, seg_len, caps, staging)
+    if ctx is None:
+        meta, up = B.fork_meta_plan(parent, seg_len, caps, staging)
+    else:
+        meta, up = B.fork_meta_plan_ctx(parent, seg_len, np.asarray(ctx[0], np.int32),
+                                        np.asarray(ctx[1], np.int32), caps, staging)
     return meta, staging, up
 
 
@@ -58,11 +68,16 @@ def arr(w, name, n):
     return w[off:off + n]
 
 
-def check_plan(parent, seg_len, gqa, kv_heads=0):
+def check_plan(parent, seg_len, gqa, kv_heads=0, ctx=None):
     parent = np.asarray(parent, np.int32)
     seg_len = np.asarray(seg_len, np.int32)
-    meta, w, up = plan(parent, seg_len, gqa, kv_heads=kv_heads)
+    meta, w, up = plan(parent, seg_len, gqa, kv_heads=kv_heads, ctx=ctx)
     S, T = len(parent), int(seg_len.sum())
+    ctx_start = np.zeros(S, np.int32) if ctx is None else np.asarray(ctx[0], np.int32)
+    ctx_len = np.zeros(S, np.int32) if ctx is None else np.asarray(ctx[1], np.int32)
+    np.testing.assert_array_equal(arr(w, "CTXLEN", S), ctx_len)
+    np.testing.assert_array_equal(arr(w, "CTXSTART", S), np.where(ctx_len > 0, ctx_start, 0))
+    assert w[HI["NCTX"]] == int(np.sum(ctx_len > 0))
     assert w[HI["MAGIC"]] == 0x464B4D31
     assert (w[HI["T"]], w[HI["S"]]) == (T, S) == (meta.num_tokens, meta.num_segments)
     assert up == 4 * w[HI["UPLOAD_WORDS"]]
@@ -113,12 +128,16 @@ def check_plan(parent, seg_len, gqa, kv_heads=0):
     ent = arr(w, "TILES", 8 * nt).reshape(-1, 8)
     tok_seg = ref["tok_seg"]
     st = ref["seg_start"]
+    # a tile's key tiles: its ancestors' ranges, its root's context, its own range
     anc_kt = np.zeros(S, np.int64)
     for s_ in range(S):
         if parent[s_] >= 0:
             anc_kt[s_] = anc_kt[parent[s_]] + -(-int(seg_len[parent[s_]]) // 64)
+        else:
+            anc_kt[s_] = -(-int(ctx_len[s_]) // 64)
     parts = {}
-    for t0, t1, own_lo, info, kt0, kt1, slot, _ in ent:
+    for t0, t1, own_lo, info, kt0, kt1, slot, root in ent:
+        assert root == ref["root"][tok_seg[t0]]
         parts.setdefault((t0, t1), []).append((kt0, kt1, slot))
     cover = np.zeros(T, np.int32)
     used_slots = []
@@ -256,3 +275,60 @@ def test_forward_argument_errors_without_gpu():
                                                B.FORK_BF16, stream=0)) == -4
     assert _status(lambda: B.fork_meta_build(parent, seg_len, meta.caps, 0, np.zeros(4096, np.uint8),
                                              stream=0)) == -1
+
+
+def forest_with_contexts(rng, parent, seg_len, shared=True):
+    """Context ranges for the roots of a forest: fresh rows, and (shared) the
+    second root naming the first root's rows."""
+    parent = np.asarray(parent, np.int32)
+    S = len(parent)
+    cs, cl = np.zeros(S, np.int32), np.zeros(S, np.int32)
+    rows = 0
+    for i, r in enumerate(np.flatnonzero(parent < 0)):
+        if shared and i == 1:
+            cs[r], cl[r] = cs[np.flatnonzero(parent < 0)[0]], cl[np.flatnonzero(parent < 0)[0]]
+            continue
+        n = int(rng.choice([0, 1, 63, 64, 65, 300]))
+        cs[r], cl[r] = rows, n
+        rows += n
+    return cs, cl
+
+
+def test_plan_with_contexts():
+    """Resumed contexts: the tiles of a root's tree count the context's key
+    tiles, carry their root, and the blob holds the context ranges."""
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        parent, seg_len = W.random_tree(rng, int(rng.integers(1, 25)), int(rng.integers(1, 90)),
+                                        max_depth=4, roots=int(rng.integers(1, 4)))
+        ctx = forest_with_contexts(rng, parent, seg_len, shared=bool(rng.integers(0, 2)))
+        gqa = int(rng.choice([1, 8, 16]))
+        check_plan(parent, seg_len, gqa, ctx=ctx)
+        check_plan(parent, seg_len, gqa, kv_heads=2, ctx=ctx)
+    parent, seg_len = W.tree_three_level(64, 8, 512, 32, 24)
+    check_plan(parent[1:] - (parent[1:] >= 0), seg_len[1:], 8, kv_heads=2,
+               ctx=(np.zeros(len(parent) - 1, np.int32),
+                    np.where(parent[1:] == 0, 4096, 0).astype(np.int32)))
+
+
+def test_context_arguments_rejected():
+    parent = np.array([-1, 0, -1], np.int32)
+    seg_len = np.array([3, 2, 4], np.int32)
+    z = np.zeros(3, np.int32)
+    cases = [((z, np.array([0, 2, 0], np.int32)), B.ForkError, -2),      # context on a non-root
+             ((z, np.array([-1, 0, 0], np.int32)), B.ForkError, -1),     # negative length
+             ((np.array([0, 0, 9], np.int32), np.array([0, 0, 2], np.int32)), B.ForkError, -5)]  # past ctx_cap
+    for ctx, exc, status in cases:
+        with pytest.raises(exc) as e:
+            plan(parent, seg_len, ctx=ctx, ctx_cap=10)
+        assert e.value.status == status
+    # one of the two arrays missing
+    caps = B.make_caps(9, 3, 2, 8, 0, 10)
+    _, stg = B.fork_meta_size(caps)
+    staging = np.zeros(stg // 4, np.int32)
+    with pytest.raises(B.ForkError) as e:
+        B.fork_meta_plan_ctx(parent, seg_len, None, np.zeros(3, np.int32), caps, staging)
+    assert e.value.status == -1
+    # no context arrays: as fork_meta_plan
+    meta, w, _ = plan(parent, seg_len, ctx=(z, z), ctx_cap=10)
+    assert w[HI["NCTX"]] == 0

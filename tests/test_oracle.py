@@ -341,3 +341,91 @@ def test_f32_build_close_to_f64():
     g64 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b)[0]
     g32 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b, prec="f32")[0]
     np.testing.assert_allclose(g32, g64, atol=1e-4)
+
+
+# ---------------------------------------------------------------- resumed contexts
+
+def resumed_forest(rng, n_roots, shared):
+    """A forest whose roots resume cached contexts, and the same computation as
+    one plain tree: each distinct cache range becomes an explicit root segment
+    (its tokens the cached rows) and the roots that resume it its children.
+    shared: the first two roots name the same cache rows."""
+    parent, seg_len = [], []
+    for r in range(n_roots):
+        base = len(parent)
+        n = int(rng.integers(1, 4))
+        for i in range(n):
+            parent.append(-1 if i == 0 else base + int(rng.integers(0, i)))
+            seg_len.append(int(rng.integers(1, 6)))
+    parent, seg_len = np.array(parent, np.int32), np.array(seg_len, np.int32)
+    S = len(parent)
+    roots = np.flatnonzero(parent < 0)
+    ctx_start = np.zeros(S, np.int32)
+    ctx_len = np.zeros(S, np.int32)
+    rows = 0
+    for i, r in enumerate(roots):
+        if shared and i == 1:
+            ctx_start[r], ctx_len[r] = ctx_start[roots[0]], ctx_len[roots[0]]
+            continue
+        n = int(rng.choice([0, 1, 4, 7]))
+        if i == 0:
+            n = max(n, 3)
+        ctx_start[r], ctx_len[r] = rows, n
+        rows += n
+    # the plain tree: one segment per distinct nonempty cache range first
+    ranges = sorted({(int(ctx_start[r]), int(ctx_len[r])) for r in roots if ctx_len[r] > 0})
+    rid = {c: i for i, c in enumerate(ranges)}
+    nc = len(ranges)
+    full_parent = [-1] * nc + [(-1 if ctx_len[s] == 0 else rid[(int(ctx_start[s]), int(ctx_len[s]))])
+                               if parent[s] < 0 else int(parent[s]) + nc for s in range(S)]
+    full_len = [n for _, n in ranges] + list(seg_len)
+    cache_rows = [c0 + j for c0, n in ranges for j in range(n)]
+    return (parent, seg_len, ctx_start, ctx_len, rows,
+            np.array(full_parent, np.int32), np.array(full_len, np.int32), cache_rows)
+
+
+@pytest.mark.parametrize("seed,shared", [(11, False), (12, True), (13, True), (14, False)])
+def test_attention_with_context_equals_plain_tree_brute_force(seed, shared):
+    """Attention over a resumed forest (contexts read from a key/value cache)
+    equals, on the new tokens, brute-force masked attention over the plain
+    tree in which every cached prefix is an explicit root segment."""
+    rng = np.random.default_rng(seed)
+    H, Hkv, D = 4, 2, 8
+    parent, seg_len, cs, cl, C, fp, fl, cache_rows = resumed_forest(rng, 3, shared)
+    T = int(seg_len.sum())
+    kc = rng.standard_normal((max(C, 1), Hkv, D)).astype(np.float32)
+    vc = rng.standard_normal((max(C, 1), Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    o, lse = oracle.attention(parent, seg_len, q, k, v, ctx_start=cs, ctx_len=cl, kc=kc, vc=vc)
+    Tc = len(cache_rows)
+    fq = np.concatenate([np.zeros((Tc, H, D), np.float32), q])
+    fk = np.concatenate([kc[cache_rows], k]) if Tc else k
+    fv = np.concatenate([vc[cache_rows], v]) if Tc else v
+    bo, blse = brute.brute_attention(fp, fl, fq, fk, fv)
+    np.testing.assert_allclose(o, bo[Tc:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse[Tc:], rtol=0, atol=1e-12)
+
+
+def test_positions_count_the_context():
+    """tok_iso_pos with resumed contexts is the number of keys a token sees
+    before itself in the plain tree (a row count of the brute-force mask)."""
+    rng = np.random.default_rng(21)
+    parent, seg_len, cs, cl, C, fp, fl, cache_rows = resumed_forest(rng, 4, True)
+    m = oracle.meta(parent, seg_len, ctx_len=cl)
+    M = brute.brute_mask(fp, fl)
+    Tc = len(cache_rows)
+    np.testing.assert_array_equal(m["tok_iso_pos"], M.sum(axis=1)[Tc:] - 1)
+
+
+def test_context_on_non_root_rejected():
+    parent = np.array([-1, 0], np.int32)
+    seg_len = np.array([2, 2], np.int32)
+    with pytest.raises(oracle.OracleError):
+        oracle.meta(parent, seg_len, ctx_len=np.array([0, 3], np.int32))
+    q = np.zeros((4, 1, 4), np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.attention(parent, seg_len, q, q, q, ctx_start=np.zeros(2, np.int32),
+                         ctx_len=np.array([0, 1], np.int32), kc=np.zeros((2, 1, 4), np.float32),
+                         vc=np.zeros((2, 1, 4), np.float32))

@@ -18,11 +18,13 @@ LIB_PATH = os.path.join(HERE, "libforkattn.so")
 FORK_F32, FORK_BF16 = 0, 1
 STATUS = {0: "FORK_OK", -1: "FORK_E_ARG", -2: "FORK_E_TREE", -3: "FORK_E_UNSUPPORTED",
           -4: "FORK_E_WORKSPACE", -5: "FORK_E_CAPACITY", -6: "FORK_E_HIP"}
-ARR_TOK_SEG, ARR_TOK_POS, ARR_TOK_ISO_POS, ARR_SEG_START, ARR_DEPTH, ARR_ANC_LEN, ARR_ROOT = range(7)
+(ARR_TOK_SEG, ARR_TOK_POS, ARR_TOK_ISO_POS, ARR_SEG_START, ARR_DEPTH, ARR_ANC_LEN, ARR_ROOT,
+ ARR_CTX_START, ARR_CTX_LEN) = range(9)
 
 # every symbol include/fork.h declares
-EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_export",
-           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward",
+EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
+           "fork_meta_plan_ctx", "fork_meta_export",
+           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
 
@@ -36,7 +38,7 @@ class ForkError(RuntimeError):
 class fork_caps(ctypes.Structure):
     _fields_ = [("t_cap", ctypes.c_int32), ("s_cap", ctypes.c_int32),
                 ("depth_cap", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
-                ("kv_heads", ctypes.c_int32)]
+                ("kv_heads", ctypes.c_int32), ("ctx_cap", ctypes.c_int32)]
 
 
 class fork_meta(ctypes.Structure):
@@ -60,7 +62,8 @@ class fork_graph_args(ctypes.Structure):
                 ("seg_final_state", ctypes.c_void_p),
                 ("gH", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("gscale", ctypes.c_float), ("gdn_ws", ctypes.c_void_p),
-                ("gdn_ws_bytes", ctypes.c_size_t), ("dt", ctypes.c_int32)]
+                ("gdn_ws_bytes", ctypes.c_size_t), ("dt", ctypes.c_int32),
+                ("kc", ctypes.c_void_p), ("vc", ctypes.c_void_p)]
 
 
 _lib = None
@@ -80,11 +83,16 @@ def lib() -> ctypes.CDLL:
             "fork_meta_size": [P(fork_caps), P(sz), P(sz)],
             "fork_meta_build": [vp, vp, i32, P(fork_caps), vp, sz, vp, sz, P(fork_meta), vp],
             "fork_meta_plan": [vp, vp, i32, P(fork_caps), vp, sz, P(sz), P(fork_meta)],
+            "fork_meta_build_ctx": [vp, vp, vp, vp, i32, P(fork_caps), vp, sz, vp, sz,
+                                    P(fork_meta), vp],
+            "fork_meta_plan_ctx": [vp, vp, vp, vp, i32, P(fork_caps), vp, sz, P(sz), P(fork_meta)],
             "fork_meta_export": [P(fork_meta), i32, vp, vp],
             "fork_meta_dense_mask": [P(fork_meta), vp, vp],
             "fork_attn_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "fork_attn_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, f32, i32,
                                   vp, sz, vp],
+            "fork_attn_forward_ctx": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                      f32, i32, vp, sz, vp],
             "gdn_fork_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
@@ -147,8 +155,10 @@ def fork_version() -> str:
     return lib().fork_version().decode()
 
 
-def make_caps(t_cap: int, s_cap: int, depth_cap: int, gqa_group: int, kv_heads: int = 0) -> fork_caps:
-    return fork_caps(int(t_cap), int(s_cap), int(depth_cap), int(gqa_group), int(kv_heads))
+def make_caps(t_cap: int, s_cap: int, depth_cap: int, gqa_group: int, kv_heads: int = 0,
+              ctx_cap: int = 0) -> fork_caps:
+    return fork_caps(int(t_cap), int(s_cap), int(depth_cap), int(gqa_group), int(kv_heads),
+                     int(ctx_cap))
 
 
 def fork_meta_size(caps: fork_caps):
@@ -175,6 +185,26 @@ def fork_meta_build(parent, seg_len, caps: fork_caps, dev, staging, stream=None)
     return out
 
 
+def fork_meta_plan_ctx(parent, seg_len, ctx_start, ctx_len, caps: fork_caps, staging):
+    """As fork_meta_plan, with resumed contexts (int32 arrays or None)."""
+    out = fork_meta()
+    up = ctypes.c_size_t(0)
+    _check(lib().fork_meta_plan_ctx(_ptr(parent), _ptr(seg_len), _ptr(ctx_start), _ptr(ctx_len),
+                                    len(parent), ctypes.byref(caps), _ptr(staging),
+                                    _nbytes(staging), ctypes.byref(up), ctypes.byref(out)))
+    return out, up.value
+
+
+def fork_meta_build_ctx(parent, seg_len, ctx_start, ctx_len, caps: fork_caps, dev, staging,
+                        stream=None) -> fork_meta:
+    out = fork_meta()
+    _check(lib().fork_meta_build_ctx(_ptr(parent), _ptr(seg_len), _ptr(ctx_start), _ptr(ctx_len),
+                                     len(parent), ctypes.byref(caps), _ptr(dev), _nbytes(dev),
+                                     _ptr(staging), _nbytes(staging), ctypes.byref(out),
+                                     _stream(stream)))
+    return out
+
+
 def fork_meta_export(meta: fork_meta, array_id: int, dst, stream=None) -> None:
     _check(lib().fork_meta_export(ctypes.byref(meta), int(array_id), _ptr(dst), _stream(stream)))
 
@@ -194,6 +224,13 @@ def fork_attn_forward(meta: fork_meta, q, k, v, o, lse, H: int, Hkv: int, D: int
     _check(lib().fork_attn_forward(ctypes.byref(meta), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                    _ptr(lse), H, Hkv, D, float(scale), dt, _ptr(ws),
                                    int(ws_bytes), _stream(stream)))
+
+
+def fork_attn_forward_ctx(meta: fork_meta, q, k, v, kc, vc, o, lse, H: int, Hkv: int, D: int,
+                          scale: float, dt: int, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().fork_attn_forward_ctx(ctypes.byref(meta), _ptr(q), _ptr(k), _ptr(v), _ptr(kc),
+                                       _ptr(vc), _ptr(o), _ptr(lse), H, Hkv, D, float(scale), dt,
+                                       _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def gdn_fork_workspace(meta: fork_meta, H: int, dk: int, dv: int, dt: int) -> int:

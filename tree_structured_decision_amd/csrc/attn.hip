@@ -96,6 +96,8 @@ struct AttnArgs {
   const void* q;
   const void* k;
   const void* v;
+  const void* kc;  // key/value cache of resumed contexts (null: none)
+  const void* vc;
   void* o;
   float* lse;
   unsigned char* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
@@ -186,40 +188,77 @@ __device__ __forceinline__ void kv_store(const KVRegs<BF16, D>& r, E* __restrict
 
 // Walks the key tiles of a work entry: the query tile's key-tile sequence is
 // every ancestor segment's range (fully visible), nearest ancestor first, then
-// the tile's own range (tree-masked), 64 keys per tile; the entry covers tiles
-// [kt0, kt1) of it.
+// the root's resumed context (cache rows, fully visible), then the tile's own
+// range (tree-masked), 64 keys per tile; the entry covers tiles [kt0, kt1) of
+// it. ph: 0 ancestors (segment a), 1 the context [c0, c1), 2 the own range;
+// cx marks a range of cache rows.
 struct TileIter {
-  int a, j0, hi, left;
-  bool own, done;
+  int a, j0, hi, left, ph, c0, c1;
+  bool own, cx, done;
 };
 
+// Positions it at the start of the range of (ph, a), moving on past empty ones.
+__device__ __forceinline__ void iter_range(TileIter& it, const AttnTile& tile,
+                                           const int32_t* __restrict__ seg_start,
+                                           const int32_t* __restrict__ seg_len) {
+  if (it.ph == 0) {
+    if (it.a >= 0) {
+      it.j0 = seg_start[it.a];
+      it.hi = it.j0 + seg_len[it.a];
+      it.own = it.cx = false;
+      return;
+    }
+    it.ph = 1;
+  }
+  if (it.ph == 1) {
+    if (it.c1 > it.c0) {
+      it.j0 = it.c0;
+      it.hi = it.c1;
+      it.own = false;
+      it.cx = true;
+      return;
+    }
+    it.ph = 2;
+  }
+  it.j0 = tile.own_lo;
+  it.hi = tile.t1;
+  it.own = true;
+  it.cx = false;
+}
+
+__device__ __forceinline__ void iter_advance(TileIter& it, const AttnTile& tile,
+                                             const int32_t* __restrict__ parent,
+                                             const int32_t* __restrict__ seg_start,
+                                             const int32_t* __restrict__ seg_len) {
+  if (it.ph == 0)
+    it.a = parent[it.a];
+  else
+    it.ph = 2;
+  iter_range(it, tile, seg_start, seg_len);
+}
+
+// ctx_start / ctx_len: the blob's context arrays, or null (no context)
 __device__ __forceinline__ void iter_init(TileIter& it, const AttnTile& tile,
                                           const int32_t* __restrict__ parent,
                                           const int32_t* __restrict__ seg_start,
-                                          const int32_t* __restrict__ seg_len) {
+                                          const int32_t* __restrict__ seg_len,
+                                          const int32_t* __restrict__ ctx_start,
+                                          const int32_t* __restrict__ ctx_len) {
   int skip = tile.kt0;
   it.left = tile.kt1 - tile.kt0;
   it.done = it.left <= 0;
   it.a = (tile.info & kTileAncMask) - 1;
-  for (;;) {
-    if (it.a >= 0) {
-      const int lo = seg_start[it.a], len = seg_len[it.a];
-      const int n = (len + kAttnKeys - 1) / kAttnKeys;
-      if (skip < n) {
-        it.own = false;
-        it.j0 = lo + kAttnKeys * skip;
-        it.hi = lo + len;
-        return;
-      }
-      skip -= n;
-      it.a = parent[it.a];
-    } else {
-      it.own = true;
-      it.j0 = tile.own_lo + kAttnKeys * skip;
-      it.hi = tile.t1;
-      return;
-    }
+  it.c0 = ctx_len ? ctx_start[tile.root] : 0;
+  it.c1 = ctx_len ? it.c0 + ctx_len[tile.root] : 0;
+  it.ph = 0;
+  iter_range(it, tile, seg_start, seg_len);
+  while (!it.own) {
+    const int n = (it.hi - it.j0 + kAttnKeys - 1) / kAttnKeys;
+    if (skip < n) break;
+    skip -= n;
+    iter_advance(it, tile, parent, seg_start, seg_len);
   }
+  it.j0 += kAttnKeys * skip;
 }
 
 __device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
@@ -232,19 +271,11 @@ __device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
   }
   it.j0 += kAttnKeys;
   if (it.j0 < it.hi) return;
-  if (!it.own) {
-    it.a = parent[it.a];
-    if (it.a >= 0) {
-      it.j0 = seg_start[it.a];
-      it.hi = it.j0 + seg_len[it.a];
-    } else {
-      it.own = true;
-      it.j0 = tile.own_lo;
-      it.hi = tile.t1;
-    }
+  if (it.own) {
+    it.done = true;
     return;
   }
-  it.done = true;
+  iter_advance(it, tile, parent, seg_start, seg_len);
 }
 
 // One workgroup of 8 waves per CU: two waves per SIMD, <= 256 VGPRs each.
@@ -268,9 +299,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
   const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
   const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
   const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
+  // resumed contexts: only when the blob has any and the cache is given
+  const bool has_ctx = args.kc != nullptr && blob[MH_NCTX] > 0;
+  const int32_t* __restrict__ ctx_start = has_ctx ? blob + blob[MH_OFF_CTXSTART] : nullptr;
+  const int32_t* __restrict__ ctx_len = has_ctx ? blob + blob[MH_OFF_CTXLEN] : nullptr;
   const E* __restrict__ Q = (const E*)args.q;
   const E* __restrict__ K = (const E*)args.k;
   const E* __restrict__ V = (const E*)args.v;
+  const E* __restrict__ Kc = (const E*)args.kc;
+  const E* __restrict__ Vc = (const E*)args.vc;
   E* __restrict__ O = (E*)args.o;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,6 +351,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     tile.kt0 = __builtin_amdgcn_readfirstlane(tiles[tix].kt0);
     tile.kt1 = __builtin_amdgcn_readfirstlane(tiles[tix].kt1);
     tile.slot = __builtin_amdgcn_readfirstlane(tiles[tix].slot);
+    tile.root = __builtin_amdgcn_readfirstlane(tiles[tix].root);
   };
   TileIter it;
   // bf16 key/value tiles in flight: DMA of the iterator's next tile into a
@@ -326,13 +364,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     pj[slot] = it.j0;
     ph[slot] = it.hi;
     po[slot] = it.own;
-    if constexpr (BF16) kv_dma<D>(buf, K, V, it.j0, it.hi - 1, g, Hkv, wave, lane);
+    if constexpr (BF16) kv_dma<D>(buf, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, wave, lane);
     ++nq;
     iter_next(it, tile, parent, seg_start, seg_len);
   };
   auto start_item = [&](int itm) {
     load_tile(itm);
-    iter_init(it, tile, parent, seg_start, seg_len);
+    iter_init(it, tile, parent, seg_start, seg_len, ctx_start, ctx_len);
     if constexpr (BF16) issue(lds2, 2);  // an item's first tile goes to lds2
   };
 
@@ -577,7 +615,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       E* Ks = (E*)lds0;
       E* Vt = (E*)lds1;
       KVRegs<BF16, D> rg;
-      kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+      kv_load<BF16, D, E>(rg, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, tid);
       while (!it.done) {
         const int j0 = it.j0, hi_ = it.hi;
         const bool own = it.own;
@@ -586,7 +624,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         __syncthreads();
         iter_next(it, tile, parent, seg_start, seg_len);
         if (!it.done)
-          kv_load<BF16, D, E>(rg, K, V, it.j0, it.hi - 1, g, Hkv, tid);
+          kv_load<BF16, D, E>(rg, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, tid);
         else
           request_next();
         kv_compute(Ks, Vt, j0, hi_, own);
@@ -799,14 +837,16 @@ size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt) {
   return c.kv_heads > 0 ? (size_t)kMaxPartSlots * attn_slot_bytes(D, dt) : 0;
 }
 
-fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v, void* o,
-                             float* lse, int H, int Hkv, int D, float scale, fork_dtype dt, void* ws,
-                             hipStream_t stream) {
+fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
+                             const void* kc, const void* vc, void* o, float* lse, int H, int Hkv, int D,
+                             float scale, fork_dtype dt, void* ws, hipStream_t stream) {
   AttnArgs a;
   a.blob = (const int32_t*)m->dev;
   a.q = q;
   a.k = k;
   a.v = v;
+  a.kc = kc;
+  a.vc = vc;
   a.o = o;
   a.lse = lse;
   a.ws = (unsigned char*)ws;

@@ -64,6 +64,8 @@ static fork_status check_caps(const fork_caps* c) {
     return fail(FORK_E_UNSUPPORTED, "gqa_group %d out of range [1, %d]", c->gqa_group, kAttnRows);
   if (c->kv_heads < 0 || c->kv_heads > kMaxPartSlots)
     return fail(FORK_E_ARG, "kv_heads %d out of range [0, %d]", c->kv_heads, kMaxPartSlots);
+  if (c->ctx_cap < 0 || c->ctx_cap > (1 << 29))
+    return fail(FORK_E_ARG, "ctx_cap %d out of range [0, 2^29]", c->ctx_cap);
   return FORK_OK;
 }
 
@@ -82,9 +84,9 @@ fork_status check_meta(const fork_meta* m) {
 
 // ---------------------------------------------------------------------------
 // The plan: everything the kernels need that depends on the tree only.
-static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int32_t S,
-                             const fork_caps* caps, void* staging, size_t staging_bytes,
-                             size_t* upload_bytes, fork_meta* out) {
+static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, const int32_t* ctx_start_in,
+                             const int32_t* ctx_len_in, int32_t S, const fork_caps* caps, void* staging,
+                             size_t staging_bytes, size_t* upload_bytes, fork_meta* out) {
   fork_status st = check_caps(caps);
   if (st) return st;
   if (!parent || !seg_len || !staging || !out) return fail(FORK_E_ARG, "null pointer argument");
@@ -123,6 +125,26 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
     max_depth = std::max(max_depth, depth[s]);
   }
 
+  // resumed contexts: cache rows [ctx_start, ctx_start + ctx_len) of a root
+  if ((ctx_start_in == nullptr) != (ctx_len_in == nullptr))
+    return fail(FORK_E_ARG, "ctx_start and ctx_len must both be given or both be null");
+  std::vector<int32_t> ctx_start(S, 0), ctx_len(S, 0);
+  int32_t nctx = 0;
+  if (ctx_len_in) {
+    for (int32_t s = 0; s < S; ++s) {
+      const int32_t c0 = ctx_start_in[s], n = ctx_len_in[s];
+      if (n < 0) return fail(FORK_E_ARG, "segment %d has context length %d", s, n);
+      if (n == 0) continue;
+      if (parent[s] >= 0) return fail(FORK_E_TREE, "segment %d has a context but is not a root", s);
+      if (c0 < 0 || (int64_t)c0 + n > caps->ctx_cap)
+        return fail(FORK_E_CAPACITY, "context rows [%d, %lld) of root %d exceed ctx_cap %d", c0,
+                    (long long)c0 + n, s, caps->ctx_cap);
+      ctx_start[s] = c0;
+      ctx_len[s] = n;
+      ++nctx;
+    }
+  }
+
   // GDN chunks: never cross a segment boundary; the last one may be partial
   std::vector<int32_t> chunk_base(S);
   int64_t nchunks = 0;
@@ -149,12 +171,13 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   // Attention query tiles. Short non-root siblings that follow each other in
   // the stream share their ancestor keys, so they are packed into common
   // tiles: every staged ancestor key/value tile then serves all their rows.
-  // A tile's work is measured in 64-key tiles: its ancestors' (anc_kt) plus
-  // its own range's.
+  // A tile's work is measured in 64-key tiles: its ancestors' and its root's
+  // context's (anc_kt) plus its own range's.
   const int32_t TT = L.tile_tokens;
   std::vector<int64_t> anc_kt(S);
   for (int32_t s = 0; s < S; ++s)
-    anc_kt[s] = parent[s] < 0 ? 0 : anc_kt[parent[s]] + (seg_len[parent[s]] + kAttnKeys - 1) / kAttnKeys;
+    anc_kt[s] = parent[s] < 0 ? (ctx_len[s] + kAttnKeys - 1) / kAttnKeys
+                              : anc_kt[parent[s]] + (seg_len[parent[s]] + kAttnKeys - 1) / kAttnKeys;
   std::vector<AttnTile> tiles;
   std::vector<int64_t> ktiles;
   tiles.reserve((size_t)(T / TT + S));
@@ -179,7 +202,7 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
       tl.kt0 = 0;
       tl.kt1 = (int32_t)(anc_kt[s] + (t1 - tl.own_lo + kAttnKeys - 1) / kAttnKeys);
       tl.slot = -1;
-      tl.pad = 0;
+      tl.root = root[s];
       tiles.push_back(tl);
       ktiles.push_back(tl.kt1);
     }
@@ -278,6 +301,8 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   put(MH_OFF_LEVELOFF, level_off.data(), max_depth + 2);
   put(MH_OFF_LEVELSEG, level_seg.data(), S);
   put(MH_OFF_LEVELLONG, level_long.data(), max_depth + 1);
+  put(MH_OFF_CTXSTART, ctx_start.data(), S);
+  put(MH_OFF_CTXLEN, ctx_len.data(), S);
   {
     off = (off + 3) & ~int64_t(3);
     w[MH_OFF_CHUNKS] = (int32_t)off;
@@ -307,6 +332,7 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, int3
   w[MH_NMERGE] = (int32_t)merges.size();
   w[MH_NPARTS] = nslots;
   w[MH_KV_HEADS] = (int32_t)Hkv;
+  w[MH_NCTX] = nctx;
 
   memset(out, 0, sizeof(*out));
   out->num_tokens = (int32_t)T;
@@ -346,17 +372,33 @@ fork_status fork_meta_size(const fork_caps* caps_h, size_t* dev_bytes_h, size_t*
   return FORK_OK;
 }
 
+fork_status fork_meta_plan_ctx(const int32_t* parent_h, const int32_t* seg_len_h, const int32_t* ctx_start_h,
+                               const int32_t* ctx_len_h, int32_t num_segments, const fork_caps* caps_h,
+                               void* staging_h, size_t staging_bytes, size_t* upload_bytes_h,
+                               fork_meta* out_h) {
+  g_err[0] = 0;
+  return plan_impl(parent_h, seg_len_h, ctx_start_h, ctx_len_h, num_segments, caps_h, staging_h,
+                   staging_bytes, upload_bytes_h, out_h);
+}
+
 fork_status fork_meta_plan(const int32_t* parent_h, const int32_t* seg_len_h, int32_t num_segments,
                            const fork_caps* caps_h, void* staging_h, size_t staging_bytes,
                            size_t* upload_bytes_h, fork_meta* out_h) {
-  g_err[0] = 0;
-  return plan_impl(parent_h, seg_len_h, num_segments, caps_h, staging_h, staging_bytes,
-                   upload_bytes_h, out_h);
+  return fork_meta_plan_ctx(parent_h, seg_len_h, nullptr, nullptr, num_segments, caps_h, staging_h,
+                            staging_bytes, upload_bytes_h, out_h);
 }
 
 fork_status fork_meta_build(const int32_t* parent_h, const int32_t* seg_len_h, int32_t num_segments,
                             const fork_caps* caps_h, void* dev, size_t dev_bytes, void* staging_h,
                             size_t staging_bytes, fork_meta* out_h, void* stream) {
+  return fork_meta_build_ctx(parent_h, seg_len_h, nullptr, nullptr, num_segments, caps_h, dev, dev_bytes,
+                             staging_h, staging_bytes, out_h, stream);
+}
+
+fork_status fork_meta_build_ctx(const int32_t* parent_h, const int32_t* seg_len_h, const int32_t* ctx_start_h,
+                                const int32_t* ctx_len_h, int32_t num_segments, const fork_caps* caps_h,
+                                void* dev, size_t dev_bytes, void* staging_h, size_t staging_bytes,
+                                fork_meta* out_h, void* stream) {
   g_err[0] = 0;
   if (!dev) return fail(FORK_E_ARG, "dev is null");
   fork_status st = check_caps(caps_h);
@@ -367,7 +409,8 @@ fork_status fork_meta_build(const int32_t* parent_h, const int32_t* seg_len_h, i
                 (long long)L.total_words * 4);
   fork_meta m;
   size_t up = 0;
-  st = plan_impl(parent_h, seg_len_h, num_segments, caps_h, staging_h, staging_bytes, &up, &m);
+  st = plan_impl(parent_h, seg_len_h, ctx_start_h, ctx_len_h, num_segments, caps_h, staging_h, staging_bytes,
+                 &up, &m);
   if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   FORK_HIP_CHECK(hipMemcpyAsync(dev, staging_h, up, hipMemcpyHostToDevice, s));
@@ -398,6 +441,8 @@ fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_
     case FORK_ARR_DEPTH: slot = MH_OFF_DEPTH; n = hdr[MH_S]; break;
     case FORK_ARR_ANC_LEN: slot = MH_OFF_ANCLEN; n = hdr[MH_S]; break;
     case FORK_ARR_ROOT: slot = MH_OFF_ROOT; n = hdr[MH_S]; break;
+    case FORK_ARR_CTX_START: slot = MH_OFF_CTXSTART; n = hdr[MH_S]; break;
+    case FORK_ARR_CTX_LEN: slot = MH_OFF_CTXLEN; n = hdr[MH_S]; break;
     default: return fail(FORK_E_ARG, "unknown array id %d", array_id);
   }
   FORK_HIP_CHECK(hipMemcpyAsync(dst_h, (const int32_t*)m->dev + hdr[slot], (size_t)n * 4,
@@ -430,10 +475,23 @@ fork_status fork_attn_workspace(const fork_meta* m, int32_t H, int32_t Hkv, int3
 fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, const void* v, void* o,
                               float* lse, int32_t H, int32_t Hkv, int32_t D, float scale,
                               fork_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  return fork_attn_forward_ctx(m, q, k, v, nullptr, nullptr, o, lse, H, Hkv, D, scale, dt, ws, ws_bytes,
+                               stream);
+}
+
+fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void* k, const void* v,
+                                  const void* kc, const void* vc, void* o, float* lse, int32_t H,
+                                  int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
+                                  size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   fork_status st = check_meta(m);
   if (st) return st;
   if (!q || !k || !v || !o) return fail(FORK_E_ARG, "q, k, v and o must be non-null");
+  if (m->caps.ctx_cap > 0 && (!kc || !vc))
+    return fail(FORK_E_ARG, "the metadata was built for cached contexts (ctx_cap %d): kc and vc are required",
+                m->caps.ctx_cap);
+  if (m->caps.ctx_cap == 0 && (kc || vc))
+    return fail(FORK_E_ARG, "kc / vc given but the metadata has no context capacity (ctx_cap 0)");
   if (H < 1 || Hkv < 1 || H % Hkv) return fail(FORK_E_ARG, "H=%d must be a positive multiple of Hkv=%d", H, Hkv);
   if (H / Hkv != m->caps.gqa_group)
     return fail(FORK_E_ARG, "H/Hkv=%d differs from the gqa_group %d the metadata was built for", H / Hkv,
@@ -446,7 +504,7 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
   const size_t need = attn_workspace_bytes(m->caps, D, dt);
   if (need && (!ws || ws_bytes < need))
     return fail(FORK_E_WORKSPACE, "attention workspace holds %zu bytes, needs %zu", ws_bytes, need);
-  return launch_attention(m, q, k, v, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);
+  return launch_attention(m, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);
 }
 
 fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv, fork_dtype dt,

@@ -50,6 +50,9 @@ enum MetaHeader : int {
   MH_NPARTS,          // partial-result slots used by split tiles (per kv head)
   MH_KV_HEADS,        // kv heads the split plan assumed (0: no splitting)
   MH_OFF_LEVELLONG,   // [MAXDEPTH + 1] segments longer than one GDN chunk at each depth (they lead its LEVELSEG list)
+  MH_OFF_CTXSTART,    // [S] first key/value cache row of a root's resumed context (0 if none)
+  MH_OFF_CTXLEN,      // [S] cache rows of a root's resumed context (0 for non-roots)
+  MH_NCTX,            // roots with a nonempty context
   MH_WORDS = 64
 };
 // Header words 48..56 hold the attention work counters: the next work item of
@@ -84,10 +87,12 @@ constexpr int kMaxPartSlots = 1024;
 // segment whose ancestor path (itself included) every row sees in full
 // (anc + 1, 0 for a root tile) in bits 0..29 and "tile spans several
 // segments" in bit 30. slot is -1 for a whole tile (written straight to the
-// output) or the partial-result slot of a split tile's part.
+// output) or the partial-result slot of a split tile's part. root is the
+// root segment of the tile's rows: its resumed context (if any) follows the
+// ancestors in the key-tile sequence, before the own range.
 struct AttnTile {
   int32_t t0, t1, own_lo, info;
-  int32_t kt0, kt1, slot, pad;
+  int32_t kt0, kt1, slot, root;
 };
 // A split query tile: its tokens and the `nparts` consecutive partial slots
 // (from slot0) its parts wrote.
@@ -115,9 +120,9 @@ inline BlobLayout blob_layout(const fork_caps& c) {
   L.tile_cap = ((int64_t)c.t_cap + L.tile_tokens - 1) / L.tile_tokens + c.s_cap + kMaxPartSlots;
   L.chunk_cap = ((int64_t)c.t_cap + kChunk - 1) / kChunk + c.s_cap;
   L.merge_cap = kMaxPartSlots / 2;
-  // header + 10 segment arrays + level offsets and long counts + 2 words per chunk + 8 per tile
+  // header + 12 segment arrays + level offsets and long counts + 2 words per chunk + 8 per tile
   // + 4 per merge group, each array aligned to 4 words
-  L.upload_cap_words = MH_WORDS + 10 * ((int64_t)c.s_cap + 4) + 2 * (c.depth_cap + 2 + 4) +
+  L.upload_cap_words = MH_WORDS + 12 * ((int64_t)c.s_cap + 4) + 2 * (c.depth_cap + 2 + 4) +
                        2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4;
   L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
   L.tok_off_words = L.upload_cap_words;
@@ -156,8 +161,8 @@ inline size_t attn_slot_bytes(int D, fork_dtype dt) {
 }
 size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
-                             void* o, float* lse, int H, int Hkv, int D, float scale,
-                             fork_dtype dt, void* ws, hipStream_t stream);
+                             const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
+                             int D, float scale, fork_dtype dt, void* ws, hipStream_t stream);
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);
 fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v,
                        const float* a, const float* b, const float* root_state, void* o,

@@ -39,6 +39,11 @@ fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* a, void
     return fail(FORK_E_WORKSPACE, "attention workspace too small");
   if (a->dk != a->dv || (a->dk != 32 && a->dk != 64 && a->dk != 128))
     return fail(FORK_E_UNSUPPORTED, "dk=%d dv=%d unsupported", a->dk, a->dv);
+  if (m->caps.ctx_cap > 0 && (!a->kc || !a->vc))
+    return fail(FORK_E_ARG, "the bucket allows cached contexts (ctx_cap %d): kc and vc are required",
+                m->caps.ctx_cap);
+  if (m->caps.ctx_cap == 0 && (a->kc || a->vc))
+    return fail(FORK_E_ARG, "kc / vc given but the bucket has no context capacity (ctx_cap 0)");
 
   hipStream_t s = (hipStream_t)stream;
   hipStream_t own = nullptr;
@@ -54,7 +59,8 @@ fork_status fork_graph_create(const fork_meta* m, const fork_graph_args* a, void
     if (own) (void)hipStreamDestroy(own);
     return fail(FORK_E_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
   }
-  st = launch_attention(m, a->q, a->k, a->v, a->o, a->lse, a->H, a->Hkv, a->D, a->scale, a->dt, a->attn_ws, s);
+  st = launch_attention(m, a->q, a->k, a->v, a->kc, a->vc, a->o, a->lse, a->H, a->Hkv, a->D, a->scale, a->dt,
+                        a->attn_ws, s);
   if (st == FORK_OK)
     st = launch_gdn(m, a->gq, a->gk, a->gv, a->a, a->b, a->root_state, a->go, a->seg_start_state,
                     a->seg_final_state, a->gH, a->dk, a->dv, a->gscale, a->dt, a->gdn_ws, a->gdn_ws_bytes, s);

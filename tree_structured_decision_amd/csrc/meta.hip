@@ -2,8 +2,9 @@
 // into per-token arrays, and a dense visibility mask for tests.
 //
 // Per token t of segment s: tok_seg = s, tok_pos = t - seg_start[s],
-// tok_iso_pos = anc_len[s] + tok_pos, the token's position in the isolated
-// root-to-segment sequence (where a positional encoding would place it).
+// tok_iso_pos = ctx_len[root] + anc_len[s] + tok_pos, the token's position in
+// the isolated root-to-segment sequence, after its root's resumed context
+// (where a positional encoding would place it).
 #include "common.h"
 
 namespace fork {
@@ -15,11 +16,13 @@ __global__ void __launch_bounds__(256) meta_expand_kernel(int32_t* __restrict__ 
   const int32_t* seg_len = blob + hdr[MH_OFF_SEGLEN];
   const int32_t* seg_start = blob + hdr[MH_OFF_SEGSTART];
   const int32_t* anc_len = blob + hdr[MH_OFF_ANCLEN];
+  const int32_t* root = blob + hdr[MH_OFF_ROOT];
+  const int32_t* ctx_len = blob + hdr[MH_OFF_CTXLEN];
   int32_t* tok_seg = blob + hdr[MH_OFF_TOKSEG];
   int32_t* tok_pos = blob + hdr[MH_OFF_TOKPOS];
   int32_t* tok_iso = blob + hdr[MH_OFF_TOKISO];
   for (int s = blockIdx.x; s < S; s += gridDim.x) {
-    const int st = seg_start[s], L = seg_len[s], al = anc_len[s];
+    const int st = seg_start[s], L = seg_len[s], al = ctx_len[root[s]] + anc_len[s];
     for (int i = threadIdx.x; i < L; i += blockDim.x) {
       tok_seg[st + i] = s;
       tok_pos[st + i] = i;

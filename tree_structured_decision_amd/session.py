@@ -25,8 +25,8 @@ class ForkSession:
 
     def __init__(self, t_cap: int, s_cap: int, depth_cap: int, gqa_group: int,
                  kv_heads: int = 0, D: int = 0, gH: int = 0, dk: int = 0, dv: int = 0,
-                 device: str = "cuda", ring: int = 2):
-        self.caps = B.make_caps(t_cap, s_cap, depth_cap, gqa_group, kv_heads)
+                 device: str = "cuda", ring: int = 2, ctx_cap: int = 0):
+        self.caps = B.make_caps(t_cap, s_cap, depth_cap, gqa_group, kv_heads, ctx_cap)
         dev_bytes, stg_bytes = B.fork_meta_size(self.caps)
         self.device = torch.device(device)
         self.blob = torch.empty(dev_bytes, dtype=torch.uint8, device=self.device)
@@ -50,28 +50,34 @@ class ForkSession:
         self.graph = None
 
     # -- metadata -----------------------------------------------------------
-    def build(self, parent, seg_len, stream=None) -> B.fork_meta:
+    def build(self, parent, seg_len, stream=None, ctx_start=None, ctx_len=None) -> B.fork_meta:
+        """ctx_start / ctx_len: resumed contexts of the roots (cache rows), or None."""
         parent = np.ascontiguousarray(parent, np.int32)
         seg_len = np.ascontiguousarray(seg_len, np.int32)
+        if ctx_len is not None:
+            ctx_start = np.ascontiguousarray(ctx_start, np.int32)
+            ctx_len = np.ascontiguousarray(ctx_len, np.int32)
         i = self._slot
         self._slot = (i + 1) % len(self.staging)
         if self.events[i] is not None:
             self.events[i].synchronize()  # the upload that last used this buffer is done
-        self.meta = B.fork_meta_build(parent, seg_len, self.caps, self.blob, self.staging[i],
-                                      stream=stream)
+        self.meta = B.fork_meta_build_ctx(parent, seg_len, ctx_start, ctx_len, self.caps, self.blob,
+                                          self.staging[i], stream=stream)
         ev = torch.cuda.Event()
         ev.record(torch.cuda.current_stream() if stream is None else stream)
         self.events[i] = ev
         return self.meta
 
     # -- layers -------------------------------------------------------------
-    def attention(self, q, k, v, o, lse=None, scale: float = 0.0, stream=None):
+    def attention(self, q, k, v, o, lse=None, scale: float = 0.0, stream=None, kc=None, vc=None):
+        """kc / vc: key/value cache of resumed contexts [ctx_cap, Hkv, D] (required when the
+        session has a context capacity)."""
         T, H, D = q.shape
         Hkv = k.shape[1]
         dt = B.FORK_BF16 if q.dtype == torch.bfloat16 else B.FORK_F32
         ws = self.attn_ws
-        B.fork_attn_forward(self.meta, q, k, v, o, lse, H, Hkv, D, scale, dt, ws,
-                            0 if ws is None else ws.numel(), stream=stream)
+        B.fork_attn_forward_ctx(self.meta, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws,
+                                0 if ws is None else ws.numel(), stream=stream)
 
     def gdn(self, q, k, v, a, b, o, seg_start_state, seg_final_state=None, root_state=None,
             scale: float = 1.0, stream=None):
@@ -84,7 +90,8 @@ class ForkSession:
 
     # -- graphs -------------------------------------------------------------
     def capture(self, attn: dict, gdn: dict, stream=None) -> int:
-        """Record both layers for this bucket. attn: q, k, v, o, lse, scale;
+        """Record both layers for this bucket. attn: q, k, v, o, lse, scale (and kc, vc
+        when the bucket has a context capacity);
         gdn: q, k, v, a, b, root_state, o, seg_start_state, seg_final_state, scale.
         Tensors must be sized for the bucket capacity."""
         A = B.fork_graph_args()
@@ -105,6 +112,7 @@ class ForkSession:
         A.gscale = float(gdn.get("scale", 1.0))
         A.gdn_ws, A.gdn_ws_bytes = p(self.gdn_ws), self.gdn_ws.numel()
         A.dt = B.FORK_BF16 if attn["q"].dtype == torch.bfloat16 else B.FORK_F32
+        A.kc, A.vc = p(attn.get("kc")), p(attn.get("vc"))
         if self.graph is not None:
             B.fork_graph_destroy(self.graph)
         self.graph = B.fork_graph_create(self.meta, A, stream=stream)
@@ -126,7 +134,7 @@ class ForkSession:
 
 
 def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=None,
-             kv_heads: int = 0):
+             kv_heads: int = 0, ctx_cap: int = 0):
     """Exact capacities of one tree (eager use)."""
     parent = np.asarray(parent)
     depth = np.zeros(len(parent), np.int64)
@@ -135,7 +143,7 @@ def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=
             depth[s] = depth[parent[s]] + 1
     return dict(t_cap=t_cap or int(np.sum(seg_len)), s_cap=s_cap or len(parent),
                 depth_cap=depth_cap if depth_cap is not None else int(depth.max()),
-                gqa_group=gqa_group, kv_heads=kv_heads)
+                gqa_group=gqa_group, kv_heads=kv_heads, ctx_cap=ctx_cap)
 
 
 def to_device(wl, device="cuda"):
