@@ -78,21 +78,26 @@ def measured_traffic(kernel: str):
 
 # ------------------------------------------------------------ algorithmic work
 
-def visible_pairs(parent, seg_len) -> int:
-    """Sum over tokens of (ancestor tokens + position in segment + 1)."""
+def visible_pairs(parent, seg_len, ctx_len=None) -> int:
+    """Sum over tokens of (ancestor tokens + resumed context of the root +
+    position in segment + 1)."""
     parent = np.asarray(parent)
     seg_len = np.asarray(seg_len, np.int64)
     anc = np.zeros(len(parent), np.int64)
     for s in range(len(parent)):
         if parent[s] >= 0:
             anc[s] = anc[parent[s]] + seg_len[parent[s]]
+        elif ctx_len is not None:
+            anc[s] = int(ctx_len[s])
     return int(np.sum(anc * seg_len + seg_len * (seg_len + 1) // 2))
 
 
-def attn_work(parent, seg_len, H, Hkv, D, elt):
+def attn_work(parent, seg_len, H, Hkv, D, elt, ctx_len=None, ctx_rows=0):
+    """Algorithmic flops (visible pairs) and bytes (q, k, v, o of the stream,
+    plus the cached context's k, v read once)."""
     T = int(np.sum(seg_len))
-    flops = 4.0 * D * H * visible_pairs(parent, seg_len)
-    bytes_ = float(T * (2 * H + 2 * Hkv) * D * elt)
+    flops = 4.0 * D * H * visible_pairs(parent, seg_len, ctx_len)
+    bytes_ = float(T * (2 * H + 2 * Hkv) * D * elt + ctx_rows * 2 * Hkv * D * elt)
     return flops, bytes_
 
 
@@ -183,9 +188,11 @@ class Runner:
         else:
             t_cap, s_cap, depth_cap = T, S, depth
         self.caps = (t_cap, s_cap, depth_cap)
+        self.ctx = wl_meta.get("ctx")  # (ctx_start, ctx_len, cache rows) of a resumed tree
         self.sess = ForkSession(t_cap, s_cap, depth_cap, wl_meta["H"] // wl_meta["Hkv"],
                                 kv_heads=wl_meta["Hkv"], D=wl_meta["D"],
-                                gH=wl_meta["gH"], dk=wl_meta["dk"], dv=wl_meta["dv"])
+                                gH=wl_meta["gH"], dk=wl_meta["dk"], dv=wl_meta["dv"],
+                                ctx_cap=0 if self.ctx is None else self.ctx[2])
         dev = "cuda"
         qd = tensors["q"].dtype
         H, D, gH, dv, dk = wl_meta["H"], wl_meta["D"], wl_meta["gH"], wl_meta["dv"], wl_meta["dk"]
@@ -194,7 +201,7 @@ class Runner:
         self.go = torch.empty((t_cap, gH, dv), dtype=qd, device=dev)
         self.st0 = torch.empty((s_cap, gH, dv, dk), dtype=torch.float32, device=dev)
         self.graph = graph
-        self.sess.build(wl_meta["parent"], wl_meta["seg_len"])
+        self._build()
         if graph:
             t = tensors
             self.sess.capture(dict(q=t["q"], k=t["k"], v=t["v"], o=self.o, lse=self.lse),
@@ -202,9 +209,16 @@ class Runner:
                                    root_state=t.get("root_state"), o=self.go,
                                    seg_start_state=self.st0))
 
+    def _build(self):
+        if self.ctx is None:
+            self.sess.build(self.m["parent"], self.m["seg_len"])
+        else:
+            self.sess.build(self.m["parent"], self.m["seg_len"], ctx_start=self.ctx[0],
+                            ctx_len=self.ctx[1])
+
     def step(self, ev=None):
         t = self.t
-        self.sess.build(self.m["parent"], self.m["seg_len"])
+        self._build()
         if self.graph:
             if ev:
                 ev[0].record()
@@ -214,7 +228,7 @@ class Runner:
             return
         if ev:
             ev[0].record()
-        self.sess.attention(t["q"], t["k"], t["v"], self.o, self.lse)
+        self.sess.attention(t["q"], t["k"], t["v"], self.o, self.lse, kc=t.get("kc"), vc=t.get("vc"))
         if ev:
             ev[1].record()
         self.sess.gdn(t["gq"], t["gk"], t["gv"], t["a"], t["b"], self.go, self.st0,
@@ -491,12 +505,32 @@ def build_workload(name):
     if name in ("tiny_one_level", "one_request", "agent_history"):
         wl = W.WORKLOADS[name]()
         meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
+        meta["root_state"] = wl.root_state is not None
         return meta, tensors_from_numpy(wl), False, wl.dtype
     if name == "wide_options":
         parent, seg_len = W.tree_one_level(8192, [8] * 256)
         meta = wl_meta_of(parent, seg_len, 32, 4, 128, 16, 128, 128)
         t = tensors_on_device(name, parent, seg_len, 32, 4, 128, 16, 128, 128, 1003, "uniform", None)
         return meta, t, False, "bf16"
+    if name == "agent_history_resume":
+        # the agent-history request resumed from a checkpoint of its 4096-token
+        # root: that prefix's keys/values come from the cache (shared by the 8
+        # children, now roots of the stream) and its recurrent state is the
+        # children's root state; the stream holds the 8 x 512 children and the
+        # options only
+        wl = W.agent_history()
+        P = int(wl.seg_len[0])
+        parent = (wl.parent[1:] - (wl.parent[1:] >= 0)).astype(np.int32)
+        seg_len = wl.seg_len[1:].astype(np.int32)
+        roots = parent < 0
+        meta = wl_meta_of(parent, seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
+        meta["ctx"] = (np.zeros(len(parent), np.int32), np.where(roots, P, 0).astype(np.int32), P)
+        meta["root_state"] = True
+        full = tensors_from_numpy(wl)
+        t = {n: full[n][P:].contiguous() for n in ("q", "k", "v", "gq", "gk", "gv", "a", "b")}
+        t["kc"], t["vc"] = full["k"][:P].contiguous(), full["v"][:P].contiguous()
+        t["root_state"] = full["root_state"].expand(int(roots.sum()), -1, -1, -1).contiguous()
+        return meta, t, False, wl.dtype
     if name == "request_mix":
         rng = np.random.Generator(np.random.PCG64(W.SEED_BASE + 5))
         parent, seg_len = W.request_mix_tree(rng)
@@ -508,8 +542,11 @@ def build_workload(name):
 
 def workload_report(name, meta, res, graph, dtype):
     elt = 2 if dtype == "bf16" else 4
-    fl, ab = attn_work(meta["parent"], meta["seg_len"], meta["H"], meta["Hkv"], meta["D"], elt)
-    gb = gdn_work(meta["parent"], meta["seg_len"], meta["gH"], meta["dk"], meta["dv"], elt, False)
+    ctx = meta.get("ctx")
+    fl, ab = attn_work(meta["parent"], meta["seg_len"], meta["H"], meta["Hkv"], meta["D"], elt,
+                       ctx_len=None if ctx is None else ctx[1], ctx_rows=0 if ctx is None else ctx[2])
+    gb = gdn_work(meta["parent"], meta["seg_len"], meta["gH"], meta["dk"], meta["dv"], elt,
+                  meta.get("root_state", False))
     peak = PEAK_BF16_MFMA if dtype == "bf16" else PEAK_F32_MFMA
     roof_t = max(fl / peak, ab / PEAK_HBM) + gb / PEAK_HBM
     pair = res["pair_p50"]
@@ -530,7 +567,8 @@ def all_workloads(steps, warmup):
     import torch
 
     rep = {}
-    for name in ("tiny_one_level", "one_request", "wide_options", "agent_history", "request_mix"):
+    for name in ("tiny_one_level", "one_request", "wide_options", "agent_history",
+                 "agent_history_resume", "request_mix"):
         log(f"workload {name}")
         meta, t, graph, dtype = build_workload(name)
         r = Runner(meta, t, graph)

@@ -160,3 +160,64 @@ def test_resume_graph_replay():
                                     ctx_start=c["ctx_start"], ctx_len=c["ctx_len"], kc=c["kc"], vc=c["vc"])
         check_close("graph resume.o", o[:c["T"]].float().cpu().numpy().astype(np.float64), ref_o, "bf16")
     log("resume graph replay: 2 trees, replay == eager bitwise")
+
+
+def test_agent_history_resume_sampled():
+    """The benchmark's resumed agent history at full size (the 4096-token root
+    cached and shared by its 8 children, now roots; 10,240 stream tokens),
+    split tiles on as the benchmark runs it: sampled rows against the oracle,
+    and the GDN layer resumed from the checkpointed state."""
+    wl = W.agent_history()
+    P = int(wl.seg_len[0])
+    parent = (wl.parent[1:] - (wl.parent[1:] >= 0)).astype(np.int32)
+    seg_len = wl.seg_len[1:].astype(np.int32)
+    roots = parent < 0
+    S, T = len(parent), int(seg_len.sum())
+    cs, cl = np.zeros(S, np.int32), np.where(roots, P, 0).astype(np.int32)
+    q, k, v = wl.q[P:], wl.k[P:], wl.v[P:]
+    kc, vc = wl.k[:P], wl.v[:P]
+    caps = caps_for(parent, seg_len, wl.H // wl.Hkv, kv_heads=wl.Hkv, ctx_cap=P)
+    sess = ForkSession(**caps, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv)
+    bf = torch.bfloat16
+    dev = lambda x, dt=bf: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    sess.build(parent, seg_len, ctx_start=cs, ctx_len=cl)
+    o = torch.full((T, wl.H, wl.D), float("nan"), dtype=bf, device="cuda")
+    lse = torch.full((T, wl.H), float("nan"), device="cuda")
+    sess.attention(dev(q), dev(k), dev(v), o, lse, kc=dev(kc), vc=dev(vc))
+    # GDN: each new root starts from the checkpointed state (here the
+    # workload's root state, the same for the 8 roots)
+    R = int(roots.sum())
+    rs = np.repeat(wl.root_state, R, axis=0)
+    go = torch.full((T, wl.gH, wl.dv), float("nan"), dtype=bf, device="cuda")
+    s0 = torch.full((S, wl.gH, wl.dv, wl.dk), float("nan"), device="cuda")
+    sess.gdn(dev(wl.gq[P:]), dev(wl.gk[P:]), dev(wl.gv[P:]), dev(wl.a[P:], torch.float32),
+             dev(wl.b[P:], torch.float32), go, s0, root_state=dev(rs, torch.float32))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    st = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
+    picks = []
+    for s in (0, 5, 7, 8, 100, 263):
+        L = int(seg_len[s])
+        picks += [st[s], st[s] + L - 1] + list(st[s] + rng.integers(0, L, 5))
+    sel = np.zeros(T, np.uint8)
+    sel[np.unique(picks)] = 1
+    ref_o, ref_lse = oracle.attention(parent, seg_len, q, k, v, tok_select=sel, ctx_start=cs,
+                                      ctx_len=cl, kc=kc, vc=vc)
+    rows = sel.astype(bool)
+    got_o = o.float().cpu().numpy().astype(np.float64)
+    check_close("resume attn.o[sampled]", got_o, ref_o, "bf16", rows=rows)
+    check_close("resume attn.lse[sampled]", lse.cpu().numpy().astype(np.float64), ref_lse, "bf16",
+                kind="f32", rows=rows)
+    assert np.isfinite(got_o).all()
+    seg_pick = [0, 8, 263]
+    ssel = np.zeros(S, np.uint8)
+    ssel[seg_pick] = 1
+    ref_go, ref_s0, _ = oracle.gdn(parent, seg_len, wl.gq[P:], wl.gk[P:], wl.gv[P:], wl.a[P:],
+                                   wl.b[P:], root_state=rs, seg_select=ssel)
+    trows = np.zeros(T, bool)
+    for s in seg_pick:
+        trows[st[s]:st[s] + seg_len[s]] = True
+    check_close("resume gdn.o[sampled]", go.float().cpu().numpy().astype(np.float64), ref_go, "bf16",
+                rows=trows)
+    check_close("resume gdn.start_state[sampled]", s0.cpu().numpy().astype(np.float64), ref_s0, "bf16",
+                kind="f32", rows=seg_pick)
