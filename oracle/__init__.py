@@ -60,6 +60,8 @@ def _lib(prec: str):
         lib.oracle_gdn.argtypes = [c_int, i32p, i32p, c_int, c_int, c_int, ctypes.c_double,
                                    f32p, f32p, f32p, f32p, f32p, vp, vp, rp, vp, vp]
         lib.oracle_num_tokens.argtypes = [c_int, i32p, i32p, ctypes.POINTER(ctypes.c_longlong)]
+        lib.oracle_rope.argtypes = [c_int, i32p, i32p, vp, c_int, c_int, ctypes.c_double, f32p, rp]
+        lib.oracle_conv.argtypes = [c_int, i32p, i32p, c_int, c_int, c_int, f32p, f32p, vp, vp, rp]
         lib.oracle_set_threads.argtypes = [c_int]
         lib.oracle_max_threads.restype = c_int
         lib.oracle_real_bytes.restype = c_int
@@ -192,3 +194,36 @@ def gdn(parent, seg_len, q, k, v, a, b, root_state=None, scale: float = 1.0, pre
                                  None if sel is None else sel.ctypes.data, o,
                                  st0.ctypes.data, st1.ctypes.data))
     return o, st0, st1
+
+
+def rope(parent, seg_len, x, theta: float = 10000.0, ctx_len=None, prec: str = "f64"):
+    """Rotary position embedding at the isolated positions (``oracle_rope``).
+    x [T,nh,D] float32 -> [T,nh,D] in the oracle's precision."""
+    parent, seg_len = _tree(parent, seg_len)
+    x = np.ascontiguousarray(x, np.float32)
+    T, nh, D = x.shape
+    y = np.full((T, nh, D), np.nan, _REAL[prec][1])
+    cl = None if ctx_len is None else np.ascontiguousarray(ctx_len, np.int32)
+    _check(_lib(prec).oracle_rope(len(parent), parent, seg_len, None if cl is None else cl.ctypes.data,
+                                  nh, D, float(theta), x, y))
+    return y
+
+
+def conv(parent, seg_len, x, w, bias=None, conv_state=None, act: int = 1, prec: str = "f64"):
+    """Causal depthwise convolution along the isolated sequences
+    (``oracle_conv``). x [T,C], w [C,K], bias [C], conv_state [R,C,K-1]."""
+    parent, seg_len = _tree(parent, seg_len)
+    x = np.ascontiguousarray(x, np.float32)
+    w = np.ascontiguousarray(w, np.float32)
+    T, C = x.shape
+    K = w.shape[1]
+    assert w.shape == (C, K)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    cs = None if conv_state is None else np.ascontiguousarray(conv_state, np.float32)
+    if cs is not None:
+        assert cs.shape == (int((parent < 0).sum()), C, K - 1)
+    y = np.full((T, C), np.nan, _REAL[prec][1])
+    _check(_lib(prec).oracle_conv(len(parent), parent, seg_len, C, K, int(act), x, w,
+                                  None if b is None else b.ctypes.data,
+                                  None if cs is None else cs.ctypes.data, y))
+    return y

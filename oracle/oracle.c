@@ -379,6 +379,110 @@ int oracle_gdn(int S, const int32_t* parent, const int32_t* seg_len,
   return ORACLE_OK;
 }
 
+/*
+ * Fork-aware pieces of a hybrid block around the two layers. Each branch must
+ * evaluate exactly as an isolated forward pass (kongchang.com page, section
+ * "ForkAttention: exact forking in GPU indices"), so anything that reads a
+ * token's position or its predecessors reads them in the isolated sequence:
+ *
+ * Rotary position embedding at the isolated position n of token t (its
+ * root's resumed context, ancestors and own predecessors counted): for each
+ * head and i < D/2 the pair (x_i, x_{i+D/2}) rotates by the angle
+ * n * theta^(-2i/D):
+ *   y_i = x_i cos(a) - x_{i+D/2} sin(a),  y_{i+D/2} = x_{i+D/2} cos(a) + x_i sin(a).
+ * x [T,nh,D] float32 stream layout, y [T,nh,D]; ctx_len nullable.
+ */
+int oracle_rope(int S, const int32_t* parent, const int32_t* seg_len, const int32_t* ctx_len,
+                int nh, int D, double theta, const float* x, REAL* y) {
+  int e = check_tree(S, parent, seg_len);
+  if (e) return e;
+  if (nh <= 0 || D <= 0 || D % 2 || !x || !y) return ORACLE_E_ARG;
+  int32_t* start = (int32_t*)malloc(sizeof(int32_t) * S);
+  int32_t acc = 0;
+  for (int s = 0; s < S; ++s) { start[s] = acc; acc += seg_len[s]; }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < S; ++s) {
+    int32_t path[ORACLE_MAX_PATH];
+    const int np = build_path(s, parent, path, ORACLE_MAX_PATH);
+    long long n0 = ctx_len ? ctx_len[path[0]] : 0;  /* isolated position of s's first token */
+    for (int i = 0; i + 1 < np; ++i) n0 += seg_len[path[i]];
+    for (int j = 0; j < seg_len[s]; ++j) {
+      const long long t = start[s] + j;
+      const REAL n = (REAL)(n0 + j);
+      for (int h = 0; h < nh; ++h) {
+        const float* xt = x + (t * nh + h) * D;
+        REAL* yt = y + (t * nh + h) * D;
+        for (int i = 0; i < D / 2; ++i) {
+          const REAL ang = n * pow((REAL)theta, -2.0 * i / D);
+          const REAL c = cos(ang), sn = sin(ang);
+          yt[i] = (REAL)xt[i] * c - (REAL)xt[i + D / 2] * sn;
+          yt[i + D / 2] = (REAL)xt[i + D / 2] * c + (REAL)xt[i] * sn;
+        }
+      }
+    }
+  }
+  free(start);
+  return ORACLE_OK;
+}
+
+/*
+ * Causal depthwise convolution along the isolated sequence (the short
+ * convolution a Gated DeltaNet block applies to its q, k, v before the
+ * recurrence; not on the pages, it follows from the isolated-pass rule): for
+ * channel c and the token at isolated position n,
+ *   u = bias[c] + sum_{j=0}^{K-1} w[c*K + K-1-j] * in(n - j),
+ * in(m) the channel's input at isolated position m: the token there for
+ * m >= 0, else (m >= -(K-1)) conv_state[r][c][K-1+m] of the sequence's root
+ * (the last K-1 inputs of its resumed context, oldest first) when given,
+ * else 0. act 1: y = u * sigmoid(u) (SiLU); act 0: y = u.
+ * x [T,C] float32, w [C,K], bias [C] (nullable), conv_state [R,C,K-1] (nullable,
+ * roots in index order), y [T,C].
+ */
+int oracle_conv(int S, const int32_t* parent, const int32_t* seg_len, int C, int K, int act,
+                const float* x, const float* w, const float* bias, const float* conv_state, REAL* y) {
+  int e = check_tree(S, parent, seg_len);
+  if (e) return e;
+  if (C <= 0 || K <= 0 || act < 0 || act > 1 || !x || !w || !y) return ORACLE_E_ARG;
+  int32_t* start = (int32_t*)malloc(sizeof(int32_t) * S);
+  int32_t* root_ord = (int32_t*)malloc(sizeof(int32_t) * S);
+  int32_t acc = 0, R = 0;
+  for (int s = 0; s < S; ++s) {
+    start[s] = acc;
+    acc += seg_len[s];
+    root_ord[s] = parent[s] < 0 ? R++ : -1;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < S; ++s) {
+    int32_t path[ORACLE_MAX_PATH];
+    const int np = build_path(s, parent, path, ORACLE_MAX_PATH);
+    long long N = 0;
+    for (int i = 0; i < np; ++i) N += seg_len[path[i]];
+    int32_t* X = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    long long n = 0;
+    for (int i = 0; i < np; ++i)
+      for (int j = 0; j < seg_len[path[i]]; ++j) X[n++] = start[path[i]] + j;
+    const int r = root_ord[path[0]];
+    for (long long pos = N - seg_len[s]; pos < N; ++pos) {
+      const long long t = X[pos];
+      for (int c = 0; c < C; ++c) {
+        REAL u = bias ? (REAL)bias[c] : (REAL)0;
+        for (int j = 0; j < K; ++j) {
+          const long long m = pos - j;
+          REAL in = 0;
+          if (m >= 0) in = (REAL)x[(long long)X[m] * C + c];
+          else if (conv_state && m >= -(K - 1)) in = (REAL)conv_state[((long long)r * C + c) * (K - 1) + (K - 1) + m];
+          u += (REAL)w[c * K + K - 1 - j] * in;
+        }
+        y[t * C + c] = act ? u / (1 + exp(-u)) : u;
+      }
+    }
+    free(X);
+  }
+  free(root_ord);
+  free(start);
+  return ORACLE_OK;
+}
+
 int oracle_real_bytes(void) { return (int)sizeof(REAL); }
 
 #ifdef _OPENMP
