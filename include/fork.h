@@ -225,6 +225,38 @@ fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, c
                              int32_t H, int32_t dk, int32_t dv, float scale, fork_dtype dt,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ block pieces
+ * Fork-aware operations around the two layers of a hybrid block. Each branch
+ * must evaluate exactly as its isolated forward pass (kongchang.com page,
+ * section "ForkAttention: exact forking in GPU indices"), so an operation that
+ * reads a token's position or its predecessors reads them in the token's
+ * isolated sequence, from the same metadata. Both calls read T from the blob
+ * (capture-safe) and touch rows < T only.
+ */
+
+/* Rotary position embedding, in place, at each token's isolated position
+ * (tok_iso_pos: its root's resumed context, its ancestors' tokens, then its
+ * own position). x [T, nheads, D] of dtype dt; for i < D/2 the pair
+ * (x_i, x_{i+D/2}) of each head rotates by the angle tok_iso_pos * theta^(-2i/D).
+ * D a multiple of 8 in 8..256; theta > 1. */
+fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32_t D, float theta,
+                              fork_dtype dt, void* stream);
+
+/* Causal depthwise convolution of width K (2..8) along each token's isolated
+ * sequence (the short convolution in front of a Gated DeltaNet layer):
+ *   y[t][c] = act(bias[c] + sum_{j<K} w[c*K + K-1-j] * in_c(t, j)),
+ * in_c(t, j) channel c of the input j tokens before t in its isolated
+ * sequence: within t's segment, then the parent's last tokens (and further
+ * ancestors when a parent is shorter than the window); before a root's first
+ * token, conv_state[r][c][K-1-j'] for the j'-th input before it (the saved
+ * last K-1 inputs of a resumed context, oldest first; r the root's ordinal
+ * among roots), or zero when conv_state is null. x, y [T, C] of dtype dt, not
+ * overlapping, C a multiple of 8; w [C, K], bias [C] (or null) and
+ * conv_state [R, C, K-1] (or null) fp32. act: 0 identity, 1 SiLU. */
+fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w, const float* bias,
+                              const float* conv_state, void* y, int32_t C, int32_t K, int32_t act,
+                              fork_dtype dt, void* stream);
+
 /* ------------------------------------------------------------ graph buckets
  * A compact set of pre-recorded execution graphs serves varied request mixes
  * (kongchang.com page, section "pre-recorded execution graphs"). A fork_graph

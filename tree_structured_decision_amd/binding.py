@@ -25,7 +25,8 @@ STATUS = {0: "FORK_OK", -1: "FORK_E_ARG", -2: "FORK_E_TREE", -3: "FORK_E_UNSUPPO
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
            "fork_meta_plan_ctx", "fork_meta_export",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
-           "gdn_fork_workspace", "gdn_fork_forward", "fork_graph_create", "fork_graph_launch",
+           "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_conv_forward",
+           "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
 
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "gdn_fork_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
+            "fork_rope_forward": [P(fork_meta), vp, i32, i32, f32, i32, vp],
+            "fork_conv_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
             "fork_graph_create": [P(fork_meta), P(fork_graph_args), vp, P(vp)],
             "fork_graph_launch": [vp, vp],
             "fork_graph_destroy": [vp],
@@ -246,6 +249,18 @@ def gdn_fork_forward(meta: fork_meta, q, k, v, a, b, root_state, o, seg_start_st
                                   _ptr(root_state), _ptr(o), _ptr(seg_start_state),
                                   _ptr(seg_final_state), H, dk, dv, float(scale), dt, _ptr(ws),
                                   int(ws_bytes), _stream(stream)))
+
+
+def fork_rope_forward(meta: fork_meta, x, nheads: int, D: int, theta: float, dt: int,
+                      stream=None) -> None:
+    _check(lib().fork_rope_forward(ctypes.byref(meta), _ptr(x), nheads, D, float(theta), dt,
+                                   _stream(stream)))
+
+
+def fork_conv_forward(meta: fork_meta, x, w, bias, conv_state, y, C: int, K: int, act: int, dt: int,
+                      stream=None) -> None:
+    _check(lib().fork_conv_forward(ctypes.byref(meta), _ptr(x), _ptr(w), _ptr(bias),
+                                   _ptr(conv_state), _ptr(y), C, K, act, dt, _stream(stream)))
 
 
 def fork_graph_create(meta: fork_meta, args: fork_graph_args, stream=None) -> int:

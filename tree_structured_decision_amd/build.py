@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libforkattn.so")
-SOURCES = ["capi.cpp", "meta.hip", "attn.hip", "gdn.hip", "graph.cpp"]
+SOURCES = ["capi.cpp", "meta.hip", "attn.hip", "gdn.hip", "block.hip", "graph.cpp"]
 ARCH = "gfx950"
 
 

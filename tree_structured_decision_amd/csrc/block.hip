@@ -1,0 +1,219 @@
+// Fork-aware pieces of a hybrid block around the attention and Gated DeltaNet
+// layers. Every branch must evaluate exactly as its isolated forward pass
+// (Flide, kongchang.com page, section "ForkAttention: exact forking in GPU
+// indices"), so an operation that reads a token's position or its
+// predecessors reads them in the token's isolated sequence, through the same
+// GPU-resident segment metadata:
+//   - rotary position embedding at tok_iso_pos (resumed context, ancestors'
+//     tokens and own position counted);
+//   - the short causal depthwise convolution of a Gated DeltaNet block, whose
+//     window at a segment's first tokens continues into the parent's tail
+//     (further ancestors for short parents) and, before a root, into the
+//     root's saved convolution state.
+// Both are streaming kernels bound by HBM: one read and one write of the
+// activations (the convolution's earlier taps are cache hits), coalesced in
+// 16-byte vectors along the channel dimension.
+#include <math.h>
+
+#include "common.h"
+
+namespace fork {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f(unsigned short u) { return __uint_as_float((unsigned)u << 16); }
+__device__ __forceinline__ unsigned short f_to_bf16(float x) { return __builtin_bit_cast(unsigned short, (__bf16)x); }
+
+// ---------------------------------------------------------------- rotary
+// A thread rotates 4 pairs (i, i + D/2), i = 4 k .. 4 k + 3, of one (token,
+// head). The angle pos * theta^(-2i/D) is formed and reduced modulo 2 pi in
+// double precision (positions reach 10^5..10^6, where a float angle would
+// be off by ~0.01 rad), then its sine and cosine are taken in float.
+constexpr int kRopeThreads = 256;
+constexpr int kMaxRopeD = 256;
+
+template <bool BF16>
+__global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __restrict__ blob, void* x, int nh,
+                                                            int D, double log2_theta) {
+  __shared__ double inv_freq[kMaxRopeD / 2];
+  const int half = D / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) inv_freq[i] = exp2(-(2.0 * i / D) * log2_theta);
+  __syncthreads();
+  const int T = blob[MH_T];
+  const int32_t* __restrict__ iso = blob + blob[MH_OFF_TOKISO];
+  const int per_row = half / 4;  // threads per (token, head)
+  const long long n = (long long)T * nh * per_row;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(idx % per_row);
+    const long long th = idx / per_row;  // token * nh + head
+    const int t = (int)(th / nh);
+    const double pos = (double)iso[t];
+    float c[4], s[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      double a = pos * inv_freq[4 * k + e];
+      a -= two_pi * rint(a / two_pi);
+      sincosf((float)a, &s[e], &c[e]);
+    }
+    if constexpr (BF16) {
+      unsigned short* row = (unsigned short*)x + th * D;
+      const u32x2_t lo = *(const u32x2_t*)(row + 4 * k);
+      const u32x2_t hi = *(const u32x2_t*)(row + half + 4 * k);
+      float a0[4] = {bf16_to_f(lo.x & 0xffff), bf16_to_f(lo.x >> 16), bf16_to_f(lo.y & 0xffff), bf16_to_f(lo.y >> 16)};
+      float b0[4] = {bf16_to_f(hi.x & 0xffff), bf16_to_f(hi.x >> 16), bf16_to_f(hi.y & 0xffff), bf16_to_f(hi.y >> 16)};
+      unsigned short ra[4], rb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ra[e] = f_to_bf16(a0[e] * c[e] - b0[e] * s[e]);
+        rb[e] = f_to_bf16(b0[e] * c[e] + a0[e] * s[e]);
+      }
+      *(u32x2_t*)(row + 4 * k) = u32x2_t{ra[0] | ((unsigned)ra[1] << 16), ra[2] | ((unsigned)ra[3] << 16)};
+      *(u32x2_t*)(row + half + 4 * k) = u32x2_t{rb[0] | ((unsigned)rb[1] << 16), rb[2] | ((unsigned)rb[3] << 16)};
+    } else {
+      float* row = (float*)x + th * D;
+      const f32x4_t a0 = *(const f32x4_t*)(row + 4 * k);
+      const f32x4_t b0 = *(const f32x4_t*)(row + half + 4 * k);
+      f32x4_t ra, rb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ra[e] = a0[e] * c[e] - b0[e] * s[e];
+        rb[e] = b0[e] * c[e] + a0[e] * s[e];
+      }
+      *(f32x4_t*)(row + 4 * k) = ra;
+      *(f32x4_t*)(row + half + 4 * k) = rb;
+    }
+  }
+}
+
+// ------------------------------------------------------------ convolution
+// A thread computes 8 consecutive channels of one token. The K - 1 earlier
+// inputs of the token's isolated sequence are located by walking back
+// through the segment metadata: within the segment, then into the parent's
+// last tokens (repeatedly, for parents shorter than the window); before a
+// root's first token the root's convolution state supplies them (or zeros).
+constexpr int kConvThreads = 256;
+constexpr int kMaxConvK = 8;
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, long long off, float* v) {
+  if constexpr (BF16) {
+    const u32x4_t p = *(const u32x4_t*)((const unsigned short*)base + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_to_f(p[e] & 0xffff);
+      v[2 * e + 1] = bf16_to_f(p[e] >> 16);
+    }
+  } else {
+    const f32x4_t a = *(const f32x4_t*)((const float*)base + off);
+    const f32x4_t b = *(const f32x4_t*)((const float*)base + off + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __restrict__ blob, const void* x,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias,
+                                                            const float* __restrict__ state, void* y, int C,
+                                                            int K, int act) {
+  const int T = blob[MH_T];
+  const int32_t* __restrict__ tok_seg = blob + blob[MH_OFF_TOKSEG];
+  const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
+  const int32_t* __restrict__ parent = blob + blob[MH_OFF_PARENT];
+  const int32_t* __restrict__ seg_start = blob + blob[MH_OFF_SEGSTART];
+  const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
+  const int32_t* __restrict__ root_ord = blob + blob[MH_OFF_ROOTORD];
+  const int per_tok = C / 8;
+  const long long n = (long long)T * per_tok;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int t = (int)(idx / per_tok);
+    const int c0 = 8 * (int)(idx - (long long)t * per_tok);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = bias ? bias[c0 + e] : 0.f;
+    // tap j multiplies the input j tokens back: w[c][K-1-j]
+    int s = tok_seg[t], p = tok_pos[t];
+    for (int j = 0; j < K; ++j) {
+      // position p - j of segment s, walked back into ancestors
+      int cs = s, cp = p - j;
+      while (cp < 0 && parent[cs] >= 0) {
+        cs = parent[cs];
+        cp += seg_len[cs];
+      }
+      float v[8];
+      if (cp >= 0) {
+        load8<BF16>(x, (long long)(seg_start[cs] + cp) * C + c0, v);
+      } else if (state && cp >= -(K - 1)) {
+        // cs is the root: its state holds the K-1 inputs before its first token
+        const float* st = state + ((long long)root_ord[cs] * C + c0) * (K - 1) + (K - 1) + cp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = st[e * (K - 1)];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w[(c0 + e) * K + K - 1 - j] * v[e];
+    }
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] / (1.f + __expf(-acc[e]));
+    }
+    if constexpr (BF16) {
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f_to_bf16(acc[2 * e]) | ((unsigned)f_to_bf16(acc[2 * e + 1]) << 16);
+      *(u32x4_t*)((unsigned short*)y + (long long)t * C + c0) = o;
+    } else {
+      float* o = (float*)y + (long long)t * C + c0;
+      *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4_t*)(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+int stream_grid(long long threads, int per_block) {
+  const long long want = (threads + per_block - 1) / per_block;
+  const long long cap = (long long)device_cu_count() * 16;
+  return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+fork_status launch_rope(const fork_meta* m, void* x, int nh, int D, float theta, fork_dtype dt, hipStream_t stream) {
+  const long long threads = (long long)m->caps.t_cap * nh * (D / 8);
+  const int grid = stream_grid(threads, kRopeThreads);
+  const double l2t = log2((double)theta);
+  if (dt == FORK_BF16)
+    hipLaunchKernelGGL(rope_kernel<true>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, x, nh, D, l2t);
+  else
+    hipLaunchKernelGGL(rope_kernel<false>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, x, nh, D, l2t);
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
+}
+
+fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
+                        void* y, int C, int K, int act, fork_dtype dt, hipStream_t stream) {
+  const long long threads = (long long)m->caps.t_cap * (C / 8);
+  const int grid = stream_grid(threads, kConvThreads);
+  if (dt == FORK_BF16)
+    hipLaunchKernelGGL(conv_kernel<true>, dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
+                       bias, state, y, C, K, act);
+  else
+    hipLaunchKernelGGL(conv_kernel<false>, dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
+                       bias, state, y, C, K, act);
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
+}
+
+}  // namespace fork

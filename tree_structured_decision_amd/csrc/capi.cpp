@@ -539,4 +539,32 @@ fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, c
                     dt, ws, ws_bytes, (hipStream_t)stream);
 }
 
+fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32_t D, float theta,
+                              fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!x) return fail(FORK_E_ARG, "x is null");
+  if (nheads < 1) return fail(FORK_E_ARG, "nheads=%d", nheads);
+  if (D < 8 || D > 256 || D % 8) return fail(FORK_E_UNSUPPORTED, "rotary dim %d unsupported (multiple of 8, 8..256)", D);
+  if (!(theta > 1.f)) return fail(FORK_E_ARG, "theta must be > 1");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_rope(m, x, nheads, D, theta, dt, (hipStream_t)stream);
+}
+
+fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w, const float* bias,
+                              const float* conv_state, void* y, int32_t C, int32_t K, int32_t act,
+                              fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!x || !w || !y) return fail(FORK_E_ARG, "x, w and y must be non-null");
+  if (x == y) return fail(FORK_E_ARG, "x and y must not overlap");
+  if (C < 8 || C % 8) return fail(FORK_E_UNSUPPORTED, "channels %d unsupported (a positive multiple of 8)", C);
+  if (K < 2 || K > 8) return fail(FORK_E_UNSUPPORTED, "kernel width %d unsupported (2..8)", K);
+  if (act != 0 && act != 1) return fail(FORK_E_ARG, "act %d (0 identity, 1 SiLU)", act);
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_conv(m, x, w, bias, conv_state, y, C, K, act, dt, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -88,6 +88,20 @@ class ForkSession:
                            seg_final_state, H, dk, dv, scale, dt, self.gdn_ws,
                            self.gdn_ws.numel(), stream=stream)
 
+    # -- block pieces -------------------------------------------------------
+    def rope(self, x, theta: float = 10000.0, stream=None):
+        """Rotary embedding in place at the isolated positions; x [T, nheads, D]."""
+        T, nh, D = x.shape
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_rope_forward(self.meta, x, nh, D, theta, dt, stream=stream)
+
+    def conv(self, x, w, y, bias=None, conv_state=None, act: int = 1, stream=None):
+        """Causal depthwise convolution along the isolated sequences; x, y [T, C],
+        w [C, K] fp32, bias [C], conv_state [R, C, K-1]."""
+        T, C = x.shape
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_conv_forward(self.meta, x, w, bias, conv_state, y, C, w.shape[1], act, dt, stream=stream)
+
     # -- graphs -------------------------------------------------------------
     def capture(self, attn: dict, gdn: dict, stream=None) -> int:
         """Record both layers for this bucket. attn: q, k, v, o, lse, scale (and kc, vc
