@@ -477,10 +477,50 @@ def main():
                  "the Infinity Cache"),
         "measured_peaks": peaks,
     }
+    out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
     print(json.dumps(out), flush=True)
     calib_copy(args.calib_copy)
+
+
+def block_ops(wl, sess, iters=50):
+    """The fork-aware block pieces on a workload's tree (metadata already built in
+    sess): rotary embedding of the attention q and k heads, and the short
+    convolution of the Gated DeltaNet q | k | v channels (width 4, SiLU). Each
+    is HBM-bound: algorithmic bytes = one read and one write of the
+    activations; timed with HIP events on the launch stream."""
+    import torch
+
+    bf = torch.bfloat16
+    T = wl.T
+    q = torch.randn(T, wl.H, wl.D, device="cuda").to(bf)
+    k = torch.randn(T, wl.Hkv, wl.D, device="cuda").to(bf)
+    C = 3 * wl.gH * wl.dk
+    x = torch.randn(T, C, device="cuda").to(bf)
+    y = torch.empty_like(x)
+    w = torch.randn(C, 4, device="cuda") * 0.5
+    ops = {
+        "rope_q_k": (lambda: (sess.rope(q), sess.rope(k)), 2.0 * (q.numel() + k.numel()) * 2),
+        "conv_qkv": (lambda: sess.conv(x, w, y, act=1), 2.0 * x.numel() * 2 + w.numel() * 4),
+    }
+    rep = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / iters
+        rep[name] = dict(us=t * 1e6, algorithmic_bytes=nbytes, achieved_gbs=nbytes / t / 1e9,
+                         hbm_frac=nbytes / t / PEAK_HBM)
+    rep["note"] = ("fork_rope_forward on q [T,16,128] and k [T,2,128]; fork_conv_forward on "
+                   f"[T,{C}] (q | k | v of the Gated DeltaNet), width 4, SiLU; bf16")
+    return rep
 
 
 def calib_copy(enabled: bool):

@@ -251,8 +251,8 @@ fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32
  * token, conv_state[r][c][K-1-j'] for the j'-th input before it (the saved
  * last K-1 inputs of a resumed context, oldest first; r the root's ordinal
  * among roots), or zero when conv_state is null. x, y [T, C] of dtype dt, not
- * overlapping, C a multiple of 8; w [C, K], bias [C] (or null) and
- * conv_state [R, C, K-1] (or null) fp32. act: 0 identity, 1 SiLU. */
+ * overlapping, C a multiple of 8; w [C, K] (16-byte aligned), bias [C] (or
+ * null) and conv_state [R, C, K-1] (or null) fp32. act: 0 identity, 1 SiLU. */
 fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w, const float* bias,
                               const float* conv_state, void* y, int32_t C, int32_t K, int32_t act,
                               fork_dtype dt, void* stream);

@@ -64,7 +64,8 @@ def test_rope_long_positions():
 
 
 @pytest.mark.parametrize("dtype,K,act,bias,state,seed", [
-    ("f32", 4, 1, True, True, 5), ("f32", 2, 0, False, False, 6), ("bf16", 4, 1, True, False, 7),
+    ("f32", 4, 1, True, True, 5), ("f32", 2, 0, False, False, 6), ("bf16", 3, 1, True, False, 7),
+    ("bf16", 4, 1, True, True, 10),
     ("bf16", 8, 1, False, True, 8), ("f32", 8, 0, True, True, 9)])
 def test_conv_parity(dtype, K, act, bias, state, seed):
     rng, parent, seg_len, cs, cl = tree_case(seed, ctx=False)

@@ -91,16 +91,18 @@ __global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __res
 }
 
 // ------------------------------------------------------------ convolution
-// A thread computes 8 consecutive channels of one token. The K - 1 earlier
-// inputs of the token's isolated sequence are located by walking back
-// through the segment metadata: within the segment, then into the parent's
-// last tokens (repeatedly, for parents shorter than the window); before a
-// root's first token the root's convolution state supplies them (or zeros).
+// A thread computes 8 consecutive channels of a run of kConvRun consecutive
+// tokens, with the channels' taps and a sliding window of the last K inputs
+// in registers, so every input row and weight is read once per run. Inside a
+// segment the window shifts by one token; at a segment's first K - 1 tokens
+// (and at the run's first token) it is refilled by walking back through the
+// segment metadata: within the segment, then into the parent's last tokens
+// (repeatedly, for parents shorter than the window); before a root's first
+// token the root's convolution state supplies the inputs (or zeros).
 constexpr int kConvThreads = 256;
-constexpr int kMaxConvK = 8;
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, long long off, float* v) {
+__device__ __forceinline__ void load8(const void* __restrict__ base, long long off, float* v) {
   if constexpr (BF16) {
     const u32x4_t p = *(const u32x4_t*)((const unsigned short*)base + off);
 #pragma unroll
@@ -119,12 +121,15 @@ __device__ __forceinline__ void load8(const void* base, long long off, float* v)
   }
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __restrict__ blob, const void* x,
+constexpr int kConvRun = 8;
+
+template <bool BF16, int K>
+__global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __restrict__ blob,
+                                                            const void* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
-                                                            const float* __restrict__ state, void* y, int C,
-                                                            int K, int act) {
+                                                            const float* __restrict__ state,
+                                                            void* __restrict__ y, int C, int act) {
   const int T = blob[MH_T];
   const int32_t* __restrict__ tok_seg = blob + blob[MH_OFF_TOKSEG];
   const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
@@ -133,51 +138,82 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __res
   const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
   const int32_t* __restrict__ root_ord = blob + blob[MH_OFF_ROOTORD];
   const int per_tok = C / 8;
-  const long long n = (long long)T * per_tok;
+  const long long n = (long long)((T + kConvRun - 1) / kConvRun) * per_tok;
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
        idx += (long long)gridDim.x * blockDim.x) {
-    const int t = (int)(idx / per_tok);
-    const int c0 = 8 * (int)(idx - (long long)t * per_tok);
-    float acc[8];
+    const int run = (int)(idx / per_tok);
+    const int c0 = 8 * (int)(idx - (long long)run * per_tok);
+    const int t0 = run * kConvRun, t1 = min(T, t0 + kConvRun);
+    // the 8 channels' taps: 8 K consecutive floats of w
+    float wt[8 * K];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = bias ? bias[c0 + e] : 0.f;
-    // tap j multiplies the input j tokens back: w[c][K-1-j]
-    int s = tok_seg[t], p = tok_pos[t];
-    for (int j = 0; j < K; ++j) {
-      // position p - j of segment s, walked back into ancestors
-      int cs = s, cp = p - j;
-      while (cp < 0 && parent[cs] >= 0) {
-        cs = parent[cs];
-        cp += seg_len[cs];
-      }
-      float v[8];
-      if (cp >= 0) {
-        load8<BF16>(x, (long long)(seg_start[cs] + cp) * C + c0, v);
-      } else if (state && cp >= -(K - 1)) {
-        // cs is the root: its state holds the K-1 inputs before its first token
-        const float* st = state + ((long long)root_ord[cs] * C + c0) * (K - 1) + (K - 1) + cp;
+    for (int i = 0; i < 2 * K; ++i) {
+      const f32x4_t v = *(const f32x4_t*)(w + (long long)c0 * K + 4 * i);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = st[e * (K - 1)];
+      for (int e = 0; e < 4; ++e) wt[4 * i + e] = v[e];
+    }
+    float b8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b8[e] = bias ? bias[c0 + e] : 0.f;
+    float win[K][8];  // win[K-1-j]: the input j tokens back
+    for (int t = t0; t < t1; ++t) {
+      const int p = tok_pos[t];
+      if (t > t0 && p > 0) {
+        // same segment as t - 1: shift the window by one token
+#pragma unroll
+        for (int i = 0; i + 1 < K; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) win[i][e] = win[i + 1][e];
+        load8<BF16>(x, (long long)t * C + c0, win[K - 1]);
       } else {
+        const int s = tok_seg[t];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        for (int j = 0; j < K; ++j) {
+          float* v = win[K - 1 - j];
+          if (p >= j) {
+            load8<BF16>(x, (long long)(t - j) * C + c0, v);
+            continue;
+          }
+          // position p - j of segment s, walked back into ancestors
+          int cs = s, cp = p - j;
+          while (cp < 0 && parent[cs] >= 0) {
+            cs = parent[cs];
+            cp += seg_len[cs];
+          }
+          if (cp >= 0) {
+            load8<BF16>(x, (long long)(seg_start[cs] + cp) * C + c0, v);
+          } else if (state && cp >= -(K - 1)) {
+            // cs is the root: its state holds the K-1 inputs before its first token
+            const float* st = state + ((long long)root_ord[cs] * C + c0) * (K - 1) + (K - 1) + cp;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = st[e * (K - 1)];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+          }
+        }
       }
+      float acc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w[(c0 + e) * K + K - 1 - j] * v[e];
-    }
-    if (act) {
+      for (int e = 0; e < 8; ++e) {
+        acc[e] = b8[e];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] / (1.f + __expf(-acc[e]));
-    }
-    if constexpr (BF16) {
-      u32x4_t o;
+        for (int i = 0; i < K; ++i) acc[e] += wt[e * K + i] * win[i][e];
+      }
+      if (act) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f_to_bf16(acc[2 * e]) | ((unsigned)f_to_bf16(acc[2 * e + 1]) << 16);
-      *(u32x4_t*)((unsigned short*)y + (long long)t * C + c0) = o;
-    } else {
-      float* o = (float*)y + (long long)t * C + c0;
-      *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4_t*)(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] / (1.f + __expf(-acc[e]));
+      }
+      if constexpr (BF16) {
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f_to_bf16(acc[2 * e]) | ((unsigned)f_to_bf16(acc[2 * e + 1]) << 16);
+        *(u32x4_t*)((unsigned short*)y + (long long)t * C + c0) = o;
+      } else {
+        float* o = (float*)y + (long long)t * C + c0;
+        *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4_t*)(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+      }
     }
   }
 }
@@ -202,18 +238,35 @@ fork_status launch_rope(const fork_meta* m, void* x, int nh, int D, float theta,
   return FORK_OK;
 }
 
-fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
-                        void* y, int C, int K, int act, fork_dtype dt, hipStream_t stream) {
-  const long long threads = (long long)m->caps.t_cap * (C / 8);
+template <bool BF16, int K>
+fork_status launch_conv_k(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
+                          void* y, int C, int act, hipStream_t stream) {
+  const long long threads = (long long)((m->caps.t_cap + kConvRun - 1) / kConvRun) * (C / 8);
   const int grid = stream_grid(threads, kConvThreads);
-  if (dt == FORK_BF16)
-    hipLaunchKernelGGL(conv_kernel<true>, dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
-                       bias, state, y, C, K, act);
-  else
-    hipLaunchKernelGGL(conv_kernel<false>, dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
-                       bias, state, y, C, K, act);
+  hipLaunchKernelGGL((conv_kernel<BF16, K>), dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
+                     bias, state, y, C, act);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
+}
+
+template <bool BF16>
+fork_status launch_conv_t(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
+                          void* y, int C, int K, int act, hipStream_t stream) {
+  switch (K) {
+    case 2: return launch_conv_k<BF16, 2>(m, x, w, bias, state, y, C, act, stream);
+    case 3: return launch_conv_k<BF16, 3>(m, x, w, bias, state, y, C, act, stream);
+    case 4: return launch_conv_k<BF16, 4>(m, x, w, bias, state, y, C, act, stream);
+    case 5: return launch_conv_k<BF16, 5>(m, x, w, bias, state, y, C, act, stream);
+    case 6: return launch_conv_k<BF16, 6>(m, x, w, bias, state, y, C, act, stream);
+    case 7: return launch_conv_k<BF16, 7>(m, x, w, bias, state, y, C, act, stream);
+    default: return launch_conv_k<BF16, 8>(m, x, w, bias, state, y, C, act, stream);
+  }
+}
+
+fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
+                        void* y, int C, int K, int act, fork_dtype dt, hipStream_t stream) {
+  if (dt == FORK_BF16) return launch_conv_t<true>(m, x, w, bias, state, y, C, K, act, stream);
+  return launch_conv_t<false>(m, x, w, bias, state, y, C, K, act, stream);
 }
 
 }  // namespace fork

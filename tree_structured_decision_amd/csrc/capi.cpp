@@ -560,6 +560,7 @@ fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w,
   if (st) return st;
   if (!x || !w || !y) return fail(FORK_E_ARG, "x, w and y must be non-null");
   if (x == y) return fail(FORK_E_ARG, "x and y must not overlap");
+  if ((uintptr_t)w % 16) return fail(FORK_E_ARG, "w must be 16-byte aligned");
   if (C < 8 || C % 8) return fail(FORK_E_UNSUPPORTED, "channels %d unsupported (a positive multiple of 8)", C);
   if (K < 2 || K > 8) return fail(FORK_E_UNSUPPORTED, "kernel width %d unsupported (2..8)", K);
   if (act != 0 && act != 1) return fail(FORK_E_ARG, "act %d (0 identity, 1 SiLU)", act);
