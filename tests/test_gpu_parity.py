@@ -131,6 +131,43 @@ def test_long_segment_chain_ragged_tail():
     full_check(wl)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deep_chain_past_planned_depths(dtype):
+    """A path 40 segments deep (beyond the depths whose segment counts the
+    host plans, so deeper launches split their depth from the blob), short
+    segments mixed with multi-chunk ones, plus side branches."""
+    rng = np.random.default_rng(40)
+    n = 40
+    parent = [-1] + list(range(n - 1))
+    seg_len = list(rng.integers(3, 30, n))
+    for d in (5, 20, 33, 38):
+        seg_len[d] = int(rng.integers(65, 140))
+    # side branches off deep segments
+    for d in (10, 31, 35, 39):
+        parent.append(d)
+        seg_len.append(int(rng.integers(1, 90)))
+    parent = np.array(parent, np.int32)
+    seg_len = np.array(seg_len, np.int32)
+    wl = W.make_workload("deep", dtype, parent, seg_len, H=4, Hkv=2, D=64, gH=2,
+                         dk=64 if dtype == "bf16" else 32, dv=64 if dtype == "bf16" else 32,
+                         gates="sigmoid", root_state_std=0.1, seed=4040)
+    log(f"deep chain {dtype}: S={wl.S} T={wl.T} depth={n - 1}")
+    full_check(wl)
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 1), (64, 2), (3, 1)])
+def test_large_and_odd_gqa_groups(H, Hkv):
+    """GQA groups of 32 and 64 query heads per kv head (8 and 4 tokens per
+    256-row tile) and 3 (rows not a multiple of the group)."""
+    rng = np.random.default_rng(H * 7 + Hkv)
+    for trial in range(2):
+        parent, seg_len = W.random_tree(rng, 7, 120, max_depth=3, roots=1 + trial)
+        wl = W.make_workload("gqa", "bf16", parent, seg_len, H=H, Hkv=Hkv, D=64, gH=2, dk=32,
+                             dv=32, gates="sigmoid", root_state_std=None, seed=500 + trial)
+        log(f"gqa {H}/{Hkv} trial {trial}: S={wl.S} T={wl.T}")
+        full_check(wl, gdn=False)
+
+
 def test_gdn_depth_split_mixed():
     """Depths that mix long segments (several chunks: the chunk-cooperative
     scan while they fit one round of workgroups) with short ones (the
