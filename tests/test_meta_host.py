@@ -332,3 +332,36 @@ def test_context_arguments_rejected():
     # no context arrays: as fork_meta_plan
     meta, w, _ = plan(parent, seg_len, ctx=(z, z), ctx_cap=10)
     assert w[HI["NCTX"]] == 0
+
+
+def test_resume_and_block_argument_errors_without_gpu():
+    """The resume and block-piece entry points reject bad arguments before any
+    HIP call (the device pointers below are never dereferenced)."""
+    parent, seg_len = np.array([-1, 0], np.int32), np.array([4, 2], np.int32)
+    fake = 0x2000
+
+    def fake_meta(ctx_cap):
+        meta, _, _ = plan(parent, seg_len, gqa=2, ctx=(np.zeros(2, np.int32), np.zeros(2, np.int32)),
+                          ctx_cap=ctx_cap)
+        meta.dev = 0x1000
+        meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
+        return meta
+
+    m0, m1 = fake_meta(0), fake_meta(64)
+    # a context capacity needs the cache; none forbids one
+    assert _status(lambda: B.fork_attn_forward(m1, fake, fake, fake, fake, None, 4, 2, 64, 0.0,
+                                               B.FORK_BF16, stream=0)) == -1
+    assert _status(lambda: B.fork_attn_forward_ctx(m0, fake, fake, fake, fake, fake, fake, None, 4, 2,
+                                                   64, 0.0, B.FORK_BF16, stream=0)) == -1
+    # rotary embedding: head size, theta, null input
+    assert _status(lambda: B.fork_rope_forward(m0, fake, 2, 12, 10000.0, B.FORK_BF16, stream=0)) == -3
+    assert _status(lambda: B.fork_rope_forward(m0, fake, 2, 64, 1.0, B.FORK_BF16, stream=0)) == -1
+    assert _status(lambda: B.fork_rope_forward(m0, None, 2, 64, 10000.0, B.FORK_BF16, stream=0)) == -1
+    # convolution: channels, width, activation, in place, misaligned weights
+    conv = lambda C=16, K=4, act=1, x=fake, w=fake, y=0x3000: _status(
+        lambda: B.fork_conv_forward(m0, x, w, None, None, y, C, K, act, B.FORK_BF16, stream=0))
+    assert conv(C=12) == -3
+    assert conv(K=9) == -3 and conv(K=1) == -3
+    assert conv(act=2) == -1
+    assert conv(y=fake) == -1
+    assert conv(w=fake + 4) == -1
