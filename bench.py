@@ -415,6 +415,10 @@ def main():
                     peak=PEAK_HBM / 1e9, unit="GB/s", frac=gdn_ach / PEAK_HBM,
                     traffic=None if tr is None else tr["bytes"])
     roof["algorithmic_per_launch"] = fl if roof["bound"] == "mfma" else gb
+    roof["launches"] = (["fork_attn_kernel", "fork_attn_merge_kernel"] if roof["bound"] == "mfma" else
+                        ["gdn_prep_kernel", "gdn_coop_kernel", "gdn_scan_kernel"])
+    roof["note"] = ("one call of the layer, timed with HIP events on its stream; its kernels' "
+                    "rocprofv3 averages are in profiles/one_request_kernels.md")
     kernels["fork_attn_forward"]["hbm_traffic_bytes"] = (measured_traffic("fork_attn_forward") or {}).get("bytes")
     kernels["gdn_fork_forward"]["hbm_traffic_bytes"] = (measured_traffic("gdn_fork_forward") or {}).get("bytes")
 
