@@ -1137,7 +1137,7 @@ struct CoopCfg {
   static constexpr int FJ = FR / 1024;         // of T'' (and of P)
   static constexpr int SJ = SB / 1024;         // of the start state
   static_assert(KJ / NW == 4 && FJ % NW == 0 && SJ % NW == 0, "load split over the helper waves");
-  static constexpr int XB = 2 * NKD * 64 * 16 + 2 * 4 * 64 * 8 + 4 * 4 * 64 * 8 + 4 * 64 * 16;  // exchanges
+  static constexpr int XB = 2 * NKD * 64 * 16 + 2 * 4 * 64 * 8 + 4 * 4 * 64 * 8;  // exchanges
   static_assert(2 * BUF + XB <= 160 * 1024, "LDS");
 };
 
@@ -1241,7 +1241,6 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   __shared__ u32x4_t sx[2][C::NKD][64];  // state fragments (hi, lo) of each reduction step
   __shared__ u32x2_t rx[2][4][64];       // R blocks (hi, lo)
   __shared__ u32x2_t ux[4][4][64];       // U blocks (hi, lo), U' blocks (hi, lo)
-  __shared__ f32x4_t yx[4][64];          // Y^T blocks
 
   const int level = args.level;
   const bool planned = args.lv_first >= 0;
@@ -1424,7 +1423,7 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
     if (chain) {
       // every LDS read of this phase first (one round trip), then the products;
       // T'' and the decays of phase (3) are read here too
-      bf16x8_t sh[C::NKD], sl[C::NKD], ka[C::TB][C::NKD], qb[C::TB][C::NKD];
+      bf16x8_t sh[C::NKD], sl[C::NKD], ka[C::TB][C::NKD];
       s16x4_t vt[C::TB];
       f32x4_t gq[C::TB];
       s_frags(cur, first, sh, sl);
@@ -1434,7 +1433,6 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
 #pragma unroll
         for (int f = 0; f < C::NKD; ++f) {
           ka[bb][f] = kq_frag<DK>(Ks, 16 * I + c16, f, q4);
-          qb[bb][f] = kq_frag<DK>(Qs, 16 * I + c16, f, q4);
         }
         vt[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t*)((const E*)(cur + C::OV) + (16 * I + 4 * q4 + (c16 >> 2)) * 16 + 4 * (c16 & 3)));
@@ -1470,23 +1468,16 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
         for (int r = 0; r < 4; ++r) R[r] = bf16_val((unsigned short)vt[bb][r]) - gq[bb][r] * X[r];
         split4(R, rx[0][I][lane], rx[1][I][lane]);
       }
-      // Y^T = S Q^T (to the helper waves with the exchange of U)
-#pragma unroll
-      for (int bb = 0; bb < C::TB; ++bb) {
-        Yt[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int f = 0; f < C::NKD; ++f) {
-          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[f], qb[bb][f], Yt[bb], 0, 0, 0);
-          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[f], qb[bb][f], Yt[bb], 0, 0, 0);
-        }
-      }
       if (first && c.own >= 0) {
         float* d = args.seg_start + ((size_t)c.own * H + c.h) * SZ + (size_t)(c.e0 + c16) * DK + 32 * w + 4 * q4;
         *(f32x4_t*)d = St[0];
         *(f32x4_t*)(d + 16) = St[1];
       }
     } else {
-      if (n1.valid) dma(nxt, n1, 0);
+      if (n1.valid) {
+        dma(nxt, n1, 0);
+        dma(nxt, n1, 1);
+      }
       flush_o();
     }
     lds_barrier();  // B1: R is exchanged
@@ -1518,10 +1509,27 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
         }
         split4(U, ux[0][I][lane], ux[1][I][lane]);
         split4(U * rq[bb], ux[2][I][lane], ux[3][I][lane]);
-        yx[I][lane] = Yt[bb];
       }
     } else {
-      if (n1.valid) dma(nxt, n1, 1);
+      // Y^T = S Q^T for this wave's token blocks (the chunk's S fragments stay
+      // in the exchange, or at a segment's first chunk in the start state,
+      // until the state update after B2)
+      bf16x8_t sh[C::NKD], sl[C::NKD], qb[C::TB][C::NKD];
+      s_frags(cur, first, sh, sl);
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb)
+#pragma unroll
+        for (int f = 0; f < C::NKD; ++f) qb[bb][f] = kq_frag<DK>(Qs, 16 * (w + C::NW * bb) + c16, f, q4);
+      SCAN_FENCE();
+#pragma unroll
+      for (int bb = 0; bb < C::TB; ++bb) {
+        Yt[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < C::NKD; ++f) {
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[f], qb[bb][f], Yt[bb], 0, 0, 0);
+          Yt[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[f], qb[bb][f], Yt[bb], 0, 0, 0);
+        }
+      }
     }
     n2.valid = 0;
     if (n1.valid) n2 = next_task(n1);
@@ -1582,7 +1590,7 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
           Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl, Zt, 0, 0, 0);
         }
         const float gi = gam[16 * I + c16];
-        oval[bb] = args.scale * (gi * yx[I][lane] + Zt);
+        oval[bb] = args.scale * (gi * Yt[bb] + Zt);
       }
       o_t0 = c.t0();
       o_len = c.len();
