@@ -257,6 +257,49 @@ fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w,
                               const float* conv_state, void* y, int32_t C, int32_t K, int32_t act,
                               fork_dtype dt, void* stream);
 
+/* ------------------------------------------------------------ mixer pieces
+ * Per-token operations of the two token mixers of a hybrid block. They read
+ * no other token, so on the flattened stream every branch gets exactly its
+ * isolated result and the shared prefix is processed once (kongchang.com
+ * page, section "ForkAttention: exact forking in GPU indices"). The pages do
+ * not spell out the block around the layers; these forms follow the published
+ * Gated DeltaNet layer (short convolution + SiLU, L2-normalised query and
+ * key, softplus decay, sigmoid write strength, gated RMS norm at the output)
+ * and a sigmoid output gate on attention. */
+
+/* Gate / norm over rows of D elements, T * nheads rows (T from the blob):
+ *   mode 0: y = x * sigmoid(g)
+ *   mode 1: y = x / sqrt(mean(x^2) + eps) * w * silu(g),  silu(g) = g sigmoid(g)
+ *   mode 2: y = x / sqrt(mean(x^2) + eps) * w             (g unused, may be null)
+ * x, g, y [T, nheads, D] of dtype dt (y may be x); w [D] fp32, 16-byte aligned,
+ * the same for every head (modes 1, 2). D a multiple of 8 in 8..65536;
+ * eps > 0 for modes 1, 2. */
+fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, const float* w, void* y,
+                              int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt, void* stream);
+
+/* Gated DeltaNet inputs after the short convolution, per token t and head h:
+ *   q[t,h] = c_q / sqrt(|c_q|^2 + eps),  k[t,h] = c_k / sqrt(|c_k|^2 + eps),
+ *   v[t,h] = c_v,
+ *   a[t,h] = exp(-exp(a_log[h]) * softplus(ab[t,h] + dt_bias[h])),
+ *   b[t,h] = sigmoid(ab[t,H+h]),
+ * with c [T, 2 H dk + H dv] holding the query heads, then the key heads, then
+ * the value heads of each token, and ab [T, 2 H] the decay and write-strength
+ * projections, both of dtype dt; q, k [T,H,dk], v [T,H,dv] of dtype dt, and
+ * a, b [T,H] fp32: the inputs of gdn_fork_forward. a_log, dt_bias [H] fp32.
+ * dk, dv multiples of 8 in 8..1024; eps > 0. T from the blob. */
+fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+                               const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
+                               int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream);
+
+/* Projection y [M, N] = x [M, K] w [N, K]^T, all row-major of dtype dt, fp32
+ * accumulation (hipBLASLt). Rows are tokens of the flattened stream: one call
+ * projects every branch, the shared prefix once. y must not overlap x or w.
+ * The first call on a device creates a hipBLASLt handle and a 32 MiB
+ * workspace, kept for the process; the first call per (M, N, K, dt) picks the
+ * algorithm and keeps it. Calls are serialised by a lock. */
+fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
+                                fork_dtype dt, void* stream);
+
 /* ------------------------------------------------------------ graph buckets
  * A compact set of pre-recorded execution graphs serves varied request mixes
  * (kongchang.com page, section "pre-recorded execution graphs"). A fork_graph

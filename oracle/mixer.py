@@ -1,0 +1,125 @@
+"""Oracle of the two token mixers of a hybrid block on the flattened stream.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: the test suite, the
+smoke check and the benchmark's CPU-baseline leg are its only callers.
+
+The pages describe the attention and Gated DeltaNet layers and the exactness
+of forking (kongchang.com page, section "ForkAttention: exact forking in GPU
+indices"; techfi24.com page, "Exact State Forking"), not the block around
+them. The forms here follow the published Gated DeltaNet layer (Yang, Kautz,
+Hatamizadeh, "Gated Delta Networks", 2024: short causal convolution with
+SiLU, L2-normalised query and key, decay exp(-exp(a_log) softplus(.)),
+sigmoid write strength, gated RMS norm at the output) and sigmoid output
+gating of attention:
+
+  attention mixer:  q, k, v, g = x Wq^T, x Wk^T, x Wv^T, x Wg^T
+                    q, k <- rotary(q), rotary(k) at the isolated positions
+                    y = (attention(q, k, v) * sigmoid(g)) Wo^T
+  GDN mixer:        c = silu(conv(x Wqkv^T)) along the isolated sequences
+                    q, k = l2norm(c_q), l2norm(c_k);  v = c_v
+                    alpha, beta = x Wab^T
+                    a = exp(-exp(a_log) softplus(alpha + dt_bias)),  b = sigmoid(beta)
+                    o = gated_deltanet(q, k, v, a, b), scale 1/sqrt(dk)
+                    y = (rmsnorm(o) * w * silu(x Wz^T)) Wo^T
+
+Per-token steps are numpy float64; the tree-dependent steps call the oracle's
+rotary, convolution, attention and Gated DeltaNet (oracle.c). With
+``bf16=True`` every stored intermediate is rounded to bf16 (nearest, ties to
+even, from float64) at the points where the GPU path stores bf16 tensors.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (8 significant bits, ties to
+    even) directly, without passing through float32; float64 out."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)                    # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)  # numpy rounds halves to even
+
+
+def linear(x, w) -> np.ndarray:
+    """y = x w^T (w stored [out, in])."""
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def sigmoid(x) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))
+
+
+def softplus(x) -> np.ndarray:
+    """log(1 + e^x), evaluated without overflow."""
+    return np.logaddexp(0.0, np.asarray(x, np.float64))
+
+
+def gate(x, g, w, mode: int, eps: float = 1e-6) -> np.ndarray:
+    """Over the last axis (D): mode 0 x sigmoid(g); mode 1
+    x / sqrt(mean(x^2) + eps) w silu(g); mode 2 x / sqrt(mean(x^2) + eps) w."""
+    x = np.asarray(x, np.float64)
+    if mode == 0:
+        return x * sigmoid(g)
+    r = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(w, np.float64)
+    if mode == 1:
+        g = np.asarray(g, np.float64)
+        r = r * g * sigmoid(g)
+    return r
+
+
+def gdn_inputs(c, ab, a_log, dt_bias, H: int, dk: int, dv: int, eps: float = 1e-6):
+    """Split c [T, 2 H dk + H dv] into L2-normalised query and key heads and the
+    value heads; decay and write strength from ab [T, 2 H]."""
+    c = np.asarray(c, np.float64)
+    ab = np.asarray(ab, np.float64)
+    T = c.shape[0]
+    cq = c[:, :H * dk].reshape(T, H, dk)
+    ck = c[:, H * dk:2 * H * dk].reshape(T, H, dk)
+    v = c[:, 2 * H * dk:].reshape(T, H, dv)
+    q = cq / np.sqrt(np.sum(cq * cq, axis=-1, keepdims=True) + eps)
+    k = ck / np.sqrt(np.sum(ck * ck, axis=-1, keepdims=True) + eps)
+    a = np.exp(-np.exp(np.asarray(a_log, np.float64)) * softplus(ab[:, :H] + np.asarray(dt_bias, np.float64)))
+    b = sigmoid(ab[:, H:])
+    return q, k, v, a, b
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, np.float32)
+
+
+def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: bool = False) -> np.ndarray:
+    """y [T, dm] of the attention mixer (weights as workloads.mixer_weights()['attn'])."""
+    from . import attention, rope
+    r = to_bf16 if bf16 else (lambda t: t)
+    T = x.shape[0]
+    H, Hkv, D = W["H"], W["Hkv"], W["D"]
+    q = r(linear(x, W["wq"])).reshape(T, H, D)
+    k = r(linear(x, W["wk"])).reshape(T, Hkv, D)
+    v = r(linear(x, W["wv"])).reshape(T, Hkv, D)
+    g = r(linear(x, W["wg"])).reshape(T, H, D)
+    q = r(rope(parent, seg_len, _f32(q), theta=theta))
+    k = r(rope(parent, seg_len, _f32(k), theta=theta))
+    o, _ = attention(parent, seg_len, _f32(q), _f32(k), _f32(v))
+    u = r(gate(r(o), g, None, 0))
+    return r(linear(u.reshape(T, H * D), W["wo"]))
+
+
+def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False,
+              return_state: bool = False):
+    """y [T, dm] of the Gated DeltaNet mixer (weights as
+    workloads.mixer_weights()['gdn']); with return_state also the per-segment
+    start and end states."""
+    from . import conv, gdn
+    r = to_bf16 if bf16 else (lambda t: t)
+    T = x.shape[0]
+    H, dk, dv = W["H"], W["dk"], W["dv"]
+    p = r(linear(x, W["wqkv"]))
+    c = r(conv(parent, seg_len, _f32(p), W["conv_w"], act=1))
+    ab = r(linear(x, W["wab"]))
+    q, k, v, a, b = gdn_inputs(c, ab, W["a_log"], W["dt_bias"], H, dk, dv, eps)
+    o, st0, st1 = gdn(parent, seg_len, _f32(r(q)), _f32(r(k)), _f32(r(v)), _f32(a), _f32(b),
+                      scale=1.0 / np.sqrt(dk))
+    z = r(linear(x, W["wz"])).reshape(T, H, dv)
+    u = r(gate(r(o), z, W["norm_w"], 1, eps))
+    y = r(linear(u.reshape(T, H * dv), W["wo"]))
+    return (y, st0, st1) if return_state else y

@@ -365,3 +365,36 @@ def test_resume_and_block_argument_errors_without_gpu():
     assert conv(act=2) == -1
     assert conv(y=fake) == -1
     assert conv(w=fake + 4) == -1
+
+
+def test_mixer_piece_argument_errors_without_gpu():
+    """The gate, Gated DeltaNet input and projection entry points reject bad
+    arguments before any HIP call (device pointers are never dereferenced)."""
+    parent, seg_len = np.array([-1, 0], np.int32), np.array([4, 2], np.int32)
+    meta, _, _ = plan(parent, seg_len, gqa=2)
+    meta.dev = 0x1000
+    meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
+    fake = 0x2000
+    gate = lambda mode=1, g=fake, w=fake, D=64, nh=2, eps=1e-6, dt=B.FORK_BF16: _status(
+        lambda: B.fork_gate_forward(meta, fake, g, w, 0x3000, nh, D, mode, eps, dt, stream=0))
+    assert gate(mode=3) == -1 and gate(mode=-1) == -1
+    assert gate(mode=0, g=None) == -1 and gate(mode=1, g=None) == -1
+    assert gate(mode=1, w=None) == -1 and gate(mode=2, w=None) == -1
+    assert gate(w=fake + 4) == -1
+    assert gate(D=12) == -3 and gate(D=0) == -3
+    assert gate(nh=0) == -1
+    assert gate(eps=0.0) == -1
+    assert gate(dt=7) == -3
+    gi = lambda H=2, dk=64, dv=64, eps=1e-6, q=fake: _status(
+        lambda: B.gdn_inputs_forward(meta, fake, fake, fake, fake, q, fake, fake, fake, fake, H, dk, dv,
+                                     eps, B.FORK_BF16, stream=0))
+    assert gi(q=None) == -1
+    assert gi(H=0) == -1
+    assert gi(dk=12) == -3 and gi(dv=2048) == -3
+    assert gi(eps=-1.0) == -1
+    lin = lambda M=4, N=8, K=16, x=fake, y=0x3000, dt=B.FORK_BF16: _status(
+        lambda: B.fork_linear_forward(x, 0x4000, y, M, N, K, dt, stream=0))
+    assert lin(M=0) == -1 and lin(K=-1) == -1
+    assert lin(x=None) == -1
+    assert lin(y=fake) == -1
+    assert lin(dt=9) == -3

@@ -1,0 +1,176 @@
+"""Pins of the mixer oracle (oracle/mixer.py) against what mathematics fixes:
+rounding ties, symmetries of sigmoid and softplus, the scale invariance of
+the RMS norm, brute-force products, a one-token stream where attention and
+the Gated DeltaNet have closed forms, and the exactness of forking
+(kongchang.com page, section "ForkAttention: exact forking in GPU indices":
+every branch equals its isolated forward pass)."""
+import numpy as np
+import pytest
+
+from oracle import mixer as M
+from tree_structured_decision_amd import workloads as W
+
+
+def test_to_bf16_ties_and_bit_rounding():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even mantissa (1)
+    assert M.to_bf16(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6
+    assert M.to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert M.to_bf16(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+    assert M.to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7  # above the tie
+    assert M.to_bf16(0.0) == 0.0
+    # on float32 inputs it agrees with the bit-level rounding of the input module
+    x = np.random.default_rng(0).standard_normal(20000).astype(np.float32) * 37.0
+    assert np.array_equal(M.to_bf16(x.astype(np.float64)), W.round_bf16(x).astype(np.float64))
+
+
+def test_linear_brute_force():
+    rng = np.random.default_rng(1)
+    x, w = rng.standard_normal((5, 7)), rng.standard_normal((3, 7))
+    y = M.linear(x, w)
+    for i in range(5):
+        for j in range(3):
+            assert abs(y[i, j] - sum(x[i, t] * w[j, t] for t in range(7))) < 1e-12
+
+
+def test_sigmoid_gate_symmetry():
+    rng = np.random.default_rng(2)
+    x, g = rng.standard_normal((6, 3, 16)), 3 * rng.standard_normal((6, 3, 16))
+    # sigmoid(g) + sigmoid(-g) = 1
+    assert np.allclose(M.gate(x, g, None, 0) + M.gate(x, -g, None, 0), x, atol=1e-14)
+    assert np.allclose(M.gate(x, np.zeros_like(g), None, 0), x / 2, atol=1e-15)
+
+
+def test_rms_norm_properties():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 2, 64)) * 5
+    w = 1.0 + 0.1 * rng.standard_normal(64)
+    g = rng.standard_normal((4, 2, 64))
+    one = np.ones(64)
+    y = M.gate(x, None, one, 2, eps=1e-12)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-9)  # unit mean square
+    assert np.allclose(M.gate(7.5 * x, None, w, 2, eps=1e-12), M.gate(x, None, w, 2, eps=1e-12), atol=1e-10)
+    # eps enters as mean(x^2) + eps
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(M.gate(x, None, one, 2, eps=0.5) ** 2, axis=-1), ms / (ms + 0.5), atol=1e-12)
+    # silu(g) - silu(-g) = g
+    d = M.gate(x, g, w, 1, eps=1e-6) - M.gate(x, -g, w, 1, eps=1e-6)
+    assert np.allclose(d, M.gate(x, None, w, 2, eps=1e-6) * g, atol=1e-12)
+
+
+def test_gdn_inputs_properties():
+    rng = np.random.default_rng(4)
+    T, H, dk, dv = 9, 3, 16, 8
+    c = rng.standard_normal((T, 2 * H * dk + H * dv)) * 2
+    u = rng.standard_normal((T, H)) * 4
+    beta = rng.standard_normal((T, H)) * 3
+    a_log = np.log(rng.uniform(1, 16, H))
+    zero = np.zeros(H)
+    q, k, v, a, b = M.gdn_inputs(c, np.concatenate([u, beta], 1), a_log, zero, H, dk, dv, eps=1e-12)
+    _, _, _, a_neg, b_neg = M.gdn_inputs(c, np.concatenate([-u, -beta], 1), a_log, zero, H, dk, dv, eps=1e-12)
+    assert np.allclose(np.linalg.norm(q, axis=-1), 1.0, atol=1e-9)
+    assert np.allclose(np.linalg.norm(k, axis=-1), 1.0, atol=1e-9)
+    cq = c[:, :H * dk].reshape(T, H, dk)
+    ck = c[:, H * dk:2 * H * dk].reshape(T, H, dk)
+    assert np.allclose(q * np.linalg.norm(cq, axis=-1, keepdims=True), cq, atol=1e-9)  # direction kept
+    assert np.allclose(k * np.linalg.norm(ck, axis=-1, keepdims=True), ck, atol=1e-9)
+    assert np.array_equal(v, c[:, 2 * H * dk:].reshape(T, H, dv))
+    # softplus(u) - softplus(-u) = u, so log a(u) - log a(-u) = -exp(a_log) u
+    assert np.allclose(np.log(a) - np.log(a_neg), -np.exp(a_log) * u, atol=1e-10)
+    assert np.allclose(b + b_neg, 1.0, atol=1e-14)
+    assert ((a > 0) & (a < 1)).all()
+    # dt_bias shifts the softplus argument
+    _, _, _, a_b, _ = M.gdn_inputs(c, np.concatenate([u - 0.3, beta], 1), a_log, zero + 0.3, H, dk, dv)
+    assert np.allclose(a_b, a, rtol=1e-12)
+    # eps enters as |c|^2 + eps
+    q1, _, _, _, _ = M.gdn_inputs(c, np.concatenate([u, beta], 1), a_log, zero, H, dk, dv, eps=2.0)
+    n2 = np.sum(cq * cq, axis=-1)
+    assert np.allclose(np.linalg.norm(q1, axis=-1) ** 2, n2 / (n2 + 2.0), atol=1e-12)
+
+
+def small_weights(seed=5, dm=32):
+    return W.mixer_weights(seed, dm, H=4, Hkv=2, D=16, gH=2, dk=16, dv=16, conv_k=4, dtype="f32")
+
+
+def test_one_token_closed_forms():
+    """One token, one segment: attention over a single key returns its value
+    (for query head h the value of kv head h // (H / Hkv)), rotary position 0
+    is the identity; the Gated DeltaNet from a zero state gives
+    o = scale b (k . q) v, and the convolution sees only its last tap."""
+    dm = 32
+    Wt = small_weights(6, dm)
+    x = W.mixer_input(7, 1, dm, "f32").astype(np.float64)
+    parent, seg_len = np.array([-1], np.int32), np.array([1], np.int32)
+    A = Wt["attn"]
+    v = (x @ A["wv"].T).reshape(1, 2, 16)
+    g = (x @ A["wg"].T).reshape(1, 4, 16)
+    o = v[:, [0, 0, 1, 1], :]
+    y_ref = ((o / (1 + np.exp(-g))).reshape(1, 64)) @ A["wo"].T
+    y = M.attention_mixer(parent, seg_len, x, A)
+    assert np.allclose(y, y_ref, rtol=1e-5, atol=1e-5)  # the layer oracle takes float32 inputs
+
+    G = Wt["gdn"]
+    H, dk, dv = 2, 16, 16
+    p = x @ G["wqkv"].T
+    c = p * G["conv_w"][:, -1][None, :]
+    c = c / (1 + np.exp(-c))
+    cq, ck = c[:, :H * dk].reshape(H, dk), c[:, H * dk:2 * H * dk].reshape(H, dk)
+    cv = c[:, 2 * H * dk:].reshape(H, dv)
+    qn = cq / np.sqrt((cq ** 2).sum(-1, keepdims=True) + 1e-6)
+    kn = ck / np.sqrt((ck ** 2).sum(-1, keepdims=True) + 1e-6)
+    beta = (x @ G["wab"].T)[0, H:]
+    bb = 1 / (1 + np.exp(-beta))
+    og = (bb * (kn * qn).sum(-1) / np.sqrt(dk))[:, None] * cv
+    z = (x @ G["wz"].T).reshape(H, dv)
+    u = og / np.sqrt((og ** 2).mean(-1, keepdims=True) + 1e-6) * G["norm_w"] * z / (1 + np.exp(-z))
+    y_ref = u.reshape(1, H * dv) @ G["wo"].T
+    y = M.gdn_mixer(parent, seg_len, x, G)
+    assert np.allclose(y, y_ref, rtol=1e-4, atol=1e-5)
+
+
+def path_segments(parent, s):
+    p = []
+    while s >= 0:
+        p.append(s)
+        s = parent[s]
+    return p[::-1]
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_mixers_equal_isolated_paths(seed):
+    """Each leaf's path through the tree, run as one isolated sequence, gives
+    the same rows as the tree run (rotary positions, convolution windows that
+    cross segment boundaries, attention visibility, forked states)."""
+    rng = np.random.default_rng(seed)
+    parent, seg_len = W.random_tree(rng, 9, 7, max_depth=4, roots=2)
+    seg_len[rng.integers(0, 9, 3)] = 1  # windows reach past short parents
+    T = int(seg_len.sum())
+    dm = 32
+    Wt = small_weights(seed, dm)
+    x = W.mixer_input(seed + 1, T, dm, "f32").astype(np.float64)
+    ya = M.attention_mixer(parent, seg_len, x, Wt["attn"])
+    yg = M.gdn_mixer(parent, seg_len, x, Wt["gdn"])
+    start = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
+    leaves = [s for s in range(len(parent)) if not (parent == s).any()]
+    for leaf in leaves:
+        rows = np.concatenate([np.arange(start[s], start[s] + seg_len[s]) for s in path_segments(parent, leaf)])
+        one = (np.array([-1], np.int32), np.array([len(rows)], np.int32))
+        ia = M.attention_mixer(*one, x[rows], Wt["attn"])
+        ig = M.gdn_mixer(*one, x[rows], Wt["gdn"])
+        assert np.allclose(ya[rows], ia, rtol=1e-9, atol=1e-9)
+        assert np.allclose(yg[rows], ig, rtol=1e-9, atol=1e-9)
+
+
+def test_bf16_rounding_points_stay_close():
+    """Rounding the stored intermediates to bf16 moves the mixers' outputs by
+    about the bf16 resolution, not more."""
+    rng = np.random.default_rng(13)
+    parent, seg_len = W.random_tree(rng, 6, 12, max_depth=3)
+    T = int(seg_len.sum())
+    Wt = W.mixer_weights(14, 64, H=4, Hkv=2, D=16, gH=2, dk=16, dv=16, dtype="bf16")
+    x = W.mixer_input(15, T, 64, "bf16").astype(np.float64)
+    for f in (M.attention_mixer, M.gdn_mixer):
+        key = "attn" if f is M.attention_mixer else "gdn"
+        y64, y16 = f(parent, seg_len, x, Wt[key]), f(parent, seg_len, x, Wt[key], bf16=True)
+        rel = np.linalg.norm(y16 - y64) / np.linalg.norm(y64)
+        assert 1e-5 < rel < 2 ** -6, rel

@@ -26,6 +26,7 @@ EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_bui
            "fork_meta_plan_ctx", "fork_meta_export",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_conv_forward",
+           "fork_gate_forward", "gdn_inputs_forward", "fork_linear_forward",
            "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
 
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
                                  f32, i32, vp, sz, vp],
             "fork_rope_forward": [P(fork_meta), vp, i32, i32, f32, i32, vp],
             "fork_conv_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
+            "fork_gate_forward": [P(fork_meta), vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
+            "gdn_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                   f32, i32, vp],
+            "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, vp],
             "fork_graph_create": [P(fork_meta), P(fork_graph_args), vp, P(vp)],
             "fork_graph_launch": [vp, vp],
             "fork_graph_destroy": [vp],
@@ -261,6 +266,23 @@ def fork_conv_forward(meta: fork_meta, x, w, bias, conv_state, y, C: int, K: int
                       stream=None) -> None:
     _check(lib().fork_conv_forward(ctypes.byref(meta), _ptr(x), _ptr(w), _ptr(bias),
                                    _ptr(conv_state), _ptr(y), C, K, act, dt, _stream(stream)))
+
+
+def fork_gate_forward(meta: fork_meta, x, g, w, y, nheads: int, D: int, mode: int, eps: float,
+                      dt: int, stream=None) -> None:
+    _check(lib().fork_gate_forward(ctypes.byref(meta), _ptr(x), _ptr(g), _ptr(w), _ptr(y), nheads, D,
+                                   mode, float(eps), dt, _stream(stream)))
+
+
+def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H: int, dk: int,
+                       dv: int, eps: float, dt: int, stream=None) -> None:
+    _check(lib().gdn_inputs_forward(ctypes.byref(meta), _ptr(c), _ptr(ab), _ptr(a_log),
+                                    _ptr(dt_bias), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), H,
+                                    dk, dv, float(eps), dt, _stream(stream)))
+
+
+def fork_linear_forward(x, w, y, M: int, N: int, K: int, dt: int, stream=None) -> None:
+    _check(lib().fork_linear_forward(_ptr(x), _ptr(w), _ptr(y), M, N, K, dt, _stream(stream)))
 
 
 def fork_graph_create(meta: fork_meta, args: fork_graph_args, stream=None) -> int:

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libforkattn.so")
-SOURCES = ["capi.cpp", "meta.hip", "attn.hip", "gdn.hip", "block.hip", "graph.cpp"]
+SOURCES = ["capi.cpp", "meta.hip", "attn.hip", "gdn.hip", "block.hip", "mixer.hip", "linear.cpp", "graph.cpp"]
 ARCH = "gfx950"
 
 
@@ -51,7 +51,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -568,4 +568,47 @@ fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w,
   return launch_conv(m, x, w, bias, conv_state, y, C, K, act, dt, (hipStream_t)stream);
 }
 
+fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, const float* w, void* y,
+                              int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (mode < 0 || mode > 2) return fail(FORK_E_ARG, "mode %d (0 sigmoid gate, 1 gated RMS norm, 2 RMS norm)", mode);
+  if (!x || !y) return fail(FORK_E_ARG, "x and y must be non-null");
+  if (mode != 2 && !g) return fail(FORK_E_ARG, "mode %d needs the gate g", mode);
+  if (mode != 0 && !w) return fail(FORK_E_ARG, "mode %d needs the weight w", mode);
+  if (w && (uintptr_t)w % 16) return fail(FORK_E_ARG, "w must be 16-byte aligned");
+  if (nheads < 1) return fail(FORK_E_ARG, "nheads=%d", nheads);
+  if (D < 8 || D > 65536 || D % 8) return fail(FORK_E_UNSUPPORTED, "row size %d unsupported (multiple of 8, 8..65536)", D);
+  if (mode != 0 && !(eps > 0.f)) return fail(FORK_E_ARG, "eps must be > 0");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_gate(m, x, g, w, y, nheads, D, mode, eps, dt, (hipStream_t)stream);
+}
+
+fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+                               const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
+                               int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!c || !ab || !a_log || !dt_bias || !q || !k || !v || !a || !b)
+    return fail(FORK_E_ARG, "every pointer must be non-null");
+  if (H < 1) return fail(FORK_E_ARG, "H=%d", H);
+  if (dk < 8 || dk > 1024 || dk % 8 || dv < 8 || dv > 1024 || dv % 8)
+    return fail(FORK_E_UNSUPPORTED, "head sizes dk=%d dv=%d unsupported (multiples of 8, 8..1024)", dk, dv);
+  if (!(eps > 0.f)) return fail(FORK_E_ARG, "eps must be > 0");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_gdn_inputs(m, c, ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt, (hipStream_t)stream);
+}
+
+fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
+                                fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  if (!x || !w || !y) return fail(FORK_E_ARG, "x, w and y must be non-null");
+  if (M < 1 || N < 1 || K < 1) return fail(FORK_E_ARG, "M=%d N=%d K=%d", M, N, K);
+  if (y == x || y == w) return fail(FORK_E_ARG, "y must not overlap x or w");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_linear(x, w, y, M, N, K, dt, (hipStream_t)stream);
+}
+
 }  // extern "C"

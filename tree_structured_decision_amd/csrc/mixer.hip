@@ -1,0 +1,250 @@
+// Per-token pieces of the two token mixers of a hybrid block, on the
+// flattened stream. None of them looks at other tokens, so a token of any
+// branch is processed exactly as in its isolated forward pass (Flide,
+// kongchang.com page, section "ForkAttention: exact forking in GPU indices")
+// and the shared prefix is processed once:
+//   - the output gate of the attention mixer, o * sigmoid(g);
+//   - the gated RMS norm at the output of the Gated DeltaNet mixer,
+//     rmsnorm(o) * w * silu(z), and the plain RMS norm in front of a mixer;
+//   - the Gated DeltaNet inputs after the short convolution: L2-normalised
+//     query and key heads, the value heads, and the per-head decay and
+//     write strength from their projections.
+// The pages describe the layers, not these surroundings; the forms follow the
+// published Gated DeltaNet layer (Yang, Kautz, Hatamizadeh, "Gated Delta
+// Networks", 2024) and sigmoid output gating of attention.
+// All are streaming kernels bound by HBM: a group of L lanes (a power of two
+// up to 64) owns one row of D elements and moves it in 16-byte vectors; the
+// second read of a normalised row is a cache hit.
+#include <math.h>
+
+#include "common.h"
+
+namespace fork {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMixThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f(unsigned short u) { return __uint_as_float((unsigned)u << 16); }
+__device__ __forceinline__ unsigned short f_to_bf16(float x) { return __builtin_bit_cast(unsigned short, (__bf16)x); }
+
+// Elements i .. i + 7 of p (i a multiple of 8).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, size_t i, float* v) {
+  if constexpr (BF16) {
+    const u32x4_t u = *(const u32x4_t*)((const unsigned short*)p + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(u[e] << 16);
+      v[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+  } else {
+    const f32x4_t a = *(const f32x4_t*)((const float*)p + i), b = *(const f32x4_t*)((const float*)p + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void* p, size_t i, const float* v) {
+  if constexpr (BF16) {
+    u32x4_t u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = (unsigned)f_to_bf16(v[2 * e]) | ((unsigned)f_to_bf16(v[2 * e + 1]) << 16);
+    *(u32x4_t*)((unsigned short*)p + i) = u;
+  } else {
+    *(f32x4_t*)((float*)p + i) = f32x4_t{v[0], v[1], v[2], v[3]};
+    *(f32x4_t*)((float*)p + i + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+
+// Sum over the L lanes of a row group (groups are aligned runs of L lanes).
+__device__ __forceinline__ float group_sum(float s, int L) {
+  for (int o = L >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
+// mode 0: y = x * sigmoid(g)
+// mode 1: y = x / sqrt(mean(x^2) + eps) * w * silu(g)
+// mode 2: y = x / sqrt(mean(x^2) + eps) * w
+// over rows of D elements; T * nh rows, T read from the blob.
+template <bool BF16, int MODE>
+__global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __restrict__ blob, const void* x,
+                                                           const void* g, const float* __restrict__ w, void* y,
+                                                           int nh, int D, int L, float eps) {
+  const long long rows = (long long)blob[MH_T] * nh;
+  const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L, nc = D / 8;
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
+  for (long long r0 = wave * rpw; r0 < rows; r0 += nwaves * rpw) {  // uniform over the wave
+    const long long r = r0 + lane / L;
+    const bool live = r < rows;
+    const size_t base = (size_t)r * D;
+    float scale = 1.f;
+    if constexpr (MODE != 0) {
+      float ss = 0.f;
+      if (live)
+        for (int j = li; j < nc; j += L) {
+          float v[8];
+          load8<BF16>(x, base + 8 * j, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        }
+      ss = group_sum(ss, L);
+      scale = 1.f / sqrtf(ss / (float)D + eps);
+    }
+    if (!live) continue;
+    for (int j = li; j < nc; j += L) {
+      float v[8], gv[8], o[8];
+      load8<BF16>(x, base + 8 * j, v);
+      if constexpr (MODE != 2) load8<BF16>(g, base + 8 * j, gv);
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[e] * sigmoid(gv[e]);
+      } else {
+        const f32x4_t w0 = *(const f32x4_t*)(w + 8 * j), w1 = *(const f32x4_t*)(w + 8 * j + 4);
+        const float ww[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = v[e] * scale * ww[e];
+          if constexpr (MODE == 1) o[e] *= gv[e] * sigmoid(gv[e]);
+        }
+      }
+      store8<BF16>(y, base + 8 * j, o);
+    }
+  }
+}
+
+// One (token, head) row per group of L lanes: c [T, 2 H dk + H dv] holds
+// the convolved query, key and value heads side by side; ab [T, 2 H] the
+// decay and write-strength projections.
+template <bool BF16>
+__global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
+    const int32_t* __restrict__ blob, const void* c, const void* ab, const float* __restrict__ a_log,
+    const float* __restrict__ dt_bias, void* q, void* k, void* v, float* __restrict__ a, float* __restrict__ b, int H,
+    int dk, int dv, int L, float eps) {
+  const long long rows = (long long)blob[MH_T] * H;
+  const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L;
+  const size_t cw = (size_t)2 * H * dk + (size_t)H * dv;
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
+  for (long long r0 = wave * rpw; r0 < rows; r0 += nwaves * rpw) {
+    const long long r = r0 + lane / L;
+    const bool live = r < rows;
+    const long long t = r / H;
+    const int h = (int)(r % H);
+    const size_t cq = (size_t)t * cw + (size_t)h * dk, ck = cq + (size_t)H * dk,
+                 cv = (size_t)t * cw + (size_t)2 * H * dk + (size_t)h * dv;
+    float sq = 0.f, sk = 0.f;
+    if (live)
+      for (int j = li; j < dk / 8; j += L) {
+        float vq[8], vk[8];
+        load8<BF16>(c, cq + 8 * j, vq);
+        load8<BF16>(c, ck + 8 * j, vk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sq += vq[e] * vq[e];
+          sk += vk[e] * vk[e];
+        }
+      }
+    sq = group_sum(sq, L);
+    sk = group_sum(sk, L);
+    if (!live) continue;
+    const float rq = 1.f / sqrtf(sq + eps), rk = 1.f / sqrtf(sk + eps);
+    for (int j = li; j < dk / 8; j += L) {
+      float vq[8], vk[8];
+      load8<BF16>(c, cq + 8 * j, vq);
+      load8<BF16>(c, ck + 8 * j, vk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vq[e] *= rq;
+        vk[e] *= rk;
+      }
+      store8<BF16>(q, (size_t)r * dk + 8 * j, vq);
+      store8<BF16>(k, (size_t)r * dk + 8 * j, vk);
+    }
+    for (int j = li; j < dv / 8; j += L) {
+      float vv[8];
+      load8<BF16>(c, cv + 8 * j, vv);
+      store8<BF16>(v, (size_t)r * dv + 8 * j, vv);
+    }
+    if (li == 0) {
+      float al, be;
+      if constexpr (BF16) {
+        al = bf16_to_f(((const unsigned short*)ab)[(size_t)t * 2 * H + h]);
+        be = bf16_to_f(((const unsigned short*)ab)[(size_t)t * 2 * H + H + h]);
+      } else {
+        al = ((const float*)ab)[(size_t)t * 2 * H + h];
+        be = ((const float*)ab)[(size_t)t * 2 * H + H + h];
+      }
+      // softplus in the form that neither overflows nor cancels
+      const float u = al + dt_bias[h];
+      const float sp = fmaxf(u, 0.f) + log1pf(expf(-fabsf(u)));
+      a[r] = expf(-expf(a_log[h]) * sp);
+      b[r] = sigmoid(be);
+    }
+  }
+}
+
+// Lanes per row: the largest power of two <= min(64, D / 8).
+int lanes_per_row(int D) {
+  int L = 1;
+  while (2 * L <= 64 && 2 * L <= D / 8) L *= 2;
+  return L;
+}
+
+int row_grid(long long rows, int L) {
+  const long long rows_per_block = (long long)(kMixThreads / 64) * (64 / L);
+  const long long want = (rows + rows_per_block - 1) / rows_per_block;
+  const long long cap = (long long)device_cu_count() * 16;
+  return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+template <bool BF16>
+fork_status launch_gate_t(const fork_meta* m, const void* x, const void* g, const float* w, void* y, int nh, int D,
+                          int mode, float eps, hipStream_t stream) {
+  const int L = lanes_per_row(D);
+  const int grid = row_grid((long long)m->caps.t_cap * nh, L);
+  const int32_t* blob = (const int32_t*)m->dev;
+  if (mode == 0)
+    hipLaunchKernelGGL((gate_kernel<BF16, 0>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+  else if (mode == 1)
+    hipLaunchKernelGGL((gate_kernel<BF16, 1>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+  else
+    hipLaunchKernelGGL((gate_kernel<BF16, 2>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
+}
+
+}  // namespace
+
+fork_status launch_gate(const fork_meta* m, const void* x, const void* g, const float* w, void* y, int nh, int D,
+                        int mode, float eps, fork_dtype dt, hipStream_t stream) {
+  if (dt == FORK_BF16) return launch_gate_t<true>(m, x, g, w, y, nh, D, mode, eps, stream);
+  return launch_gate_t<false>(m, x, g, w, y, nh, D, mode, eps, stream);
+}
+
+fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+                              const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int H, int dk,
+                              int dv, float eps, fork_dtype dt, hipStream_t stream) {
+  const int L = lanes_per_row(dk < dv ? dk : dv);
+  const int grid = row_grid((long long)m->caps.t_cap * H, L);
+  const int32_t* blob = (const int32_t*)m->dev;
+  if (dt == FORK_BF16)
+    hipLaunchKernelGGL(gdn_inputs_kernel<true>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
+                       q, k, v, a, b, H, dk, dv, L, eps);
+  else
+    hipLaunchKernelGGL(gdn_inputs_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
+                       q, k, v, a, b, H, dk, dv, L, eps);
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
+}
+
+}  // namespace fork

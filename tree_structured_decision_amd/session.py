@@ -102,6 +102,93 @@ class ForkSession:
         dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
         B.fork_conv_forward(self.meta, x, w, bias, conv_state, y, C, w.shape[1], act, dt, stream=stream)
 
+    # -- mixer pieces -------------------------------------------------------
+    def gate(self, x, g, w, y, mode: int, eps: float = 1e-6, stream=None):
+        """Gate / norm over the last axis of x [T, nheads, D] (mode 0 x sigmoid(g),
+        1 rmsnorm(x) w silu(g), 2 rmsnorm(x) w)."""
+        T, nh, D = x.shape
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_gate_forward(self.meta, x, g, w, y, nh, D, mode, eps, dt, stream=stream)
+
+    def gdn_inputs(self, c, ab, a_log, dt_bias, q, k, v, a, b, eps: float = 1e-6, stream=None):
+        """Gated DeltaNet inputs from the convolved projections c [T, 2 H dk + H dv]
+        and the decay / write-strength projections ab [T, 2 H]."""
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        dt = B.FORK_BF16 if c.dtype == torch.bfloat16 else B.FORK_F32
+        B.gdn_inputs_forward(self.meta, c, ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt,
+                             stream=stream)
+
+    @staticmethod
+    def linear(x, w, y, stream=None):
+        """y [M, N] = x [M, K] w [N, K]^T."""
+        M, K = x.shape
+        N = w.shape[0]
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_linear_forward(x, w, y, M, N, K, dt, stream=stream)
+
+    def attention_mixer(self, x, W: dict, theta: float = 10000.0, stream=None, bufs: dict = None):
+        """Attention mixer of a hybrid block on the current tree: projections, rotary
+        embedding at the isolated positions, tree attention, sigmoid output gate,
+        output projection. x [T, dm]; W holds device tensors wq, wk, wv, wg, wo and
+        the ints H, Hkv, D. Returns y [T, dm]. bufs: optional dict reused across
+        calls for the intermediates."""
+        T, dm = x.shape
+        H, Hkv, D = W["H"], W["Hkv"], W["D"]
+        b = self._bufs(bufs, x, dict(q=(T, H, D), k=(T, Hkv, D), v=(T, Hkv, D), g=(T, H, D),
+                                     o=(T, H, D), u=(T, H, D), y=(T, dm)))
+        self.linear(x, W["wq"], b["q"], stream)
+        self.linear(x, W["wk"], b["k"], stream)
+        self.linear(x, W["wv"], b["v"], stream)
+        self.linear(x, W["wg"], b["g"], stream)
+        self.rope(b["q"], theta, stream)
+        self.rope(b["k"], theta, stream)
+        self.attention(b["q"], b["k"], b["v"], b["o"], stream=stream)
+        self.gate(b["o"], b["g"], None, b["u"], 0, stream=stream)
+        self.linear(b["u"].view(T, H * D), W["wo"], b["y"], stream)
+        return b["y"]
+
+    def gdn_mixer(self, x, W: dict, eps: float = 1e-6, stream=None, bufs: dict = None,
+                  seg_start_state=None):
+        """Gated DeltaNet mixer of a hybrid block on the current tree: projections,
+        causal convolution along the isolated sequences (+ SiLU), normalised inputs and
+        gates, forked Gated DeltaNet, gated RMS norm, output projection. x [T, dm]; W
+        holds device tensors wqkv, wab, wz, wo, conv_w, a_log, dt_bias, norm_w and the
+        ints H, dk, dv. Returns y [T, dm]."""
+        T, dm = x.shape
+        H, dk, dv = W["H"], W["dk"], W["dv"]
+        C = 2 * H * dk + H * dv
+        b = self._bufs(bufs, x, dict(p=(T, C), c=(T, C), ab=(T, 2 * H), q=(T, H, dk), k=(T, H, dk),
+                                     v=(T, H, dv), o=(T, H, dv), z=(T, H, dv), u=(T, H, dv),
+                                     y=(T, dm)))
+        for n, shape in (("a", (T, H)), ("b", (T, H))):
+            if n not in b or b[n].shape != shape:
+                b[n] = torch.empty(shape, dtype=torch.float32, device=x.device)
+        S = int(self.meta.num_segments)
+        st = seg_start_state
+        if st is None:
+            if "st" not in b or b["st"].shape[0] < S:
+                b["st"] = torch.empty((S, H, dv, dk), dtype=torch.float32, device=x.device)
+            st = b["st"]
+        self.linear(x, W["wqkv"], b["p"], stream)
+        self.linear(x, W["wab"], b["ab"], stream)
+        self.linear(x, W["wz"], b["z"].view(T, H * dv), stream)
+        self.conv(b["p"], W["conv_w"], b["c"], act=1, stream=stream)
+        self.gdn_inputs(b["c"], b["ab"], W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"],
+                        b["b"], eps, stream)
+        self.gdn(b["q"], b["k"], b["v"], b["a"], b["b"], b["o"], st, scale=dk ** -0.5, stream=stream)
+        self.gate(b["o"], b["z"], W["norm_w"], b["u"], 1, eps, stream)
+        self.linear(b["u"].view(T, H * dv), W["wo"], b["y"], stream)
+        return b["y"]
+
+    @staticmethod
+    def _bufs(bufs, x, shapes):
+        b = {} if bufs is None else bufs
+        for n, shape in shapes.items():
+            if n not in b or tuple(b[n].shape) != tuple(shape):
+                b[n] = torch.empty(shape, dtype=x.dtype, device=x.device)
+        return b
+
     # -- graphs -------------------------------------------------------------
     def capture(self, attn: dict, gdn: dict, stream=None) -> int:
         """Record both layers for this bucket. attn: q, k, v, o, lse, scale (and kc, vc

@@ -298,3 +298,41 @@ def group_options(parent: np.ndarray, seg_len: np.ndarray):
         if not has_child[s] and parent[s] >= 0:
             groups.setdefault(int(parent[s]), []).append(s)
     return sorted(groups.items())
+
+
+# --------------------------------------------------------------------------
+# hybrid block weights (random init, no trained values)
+
+def mixer_weights(seed: int, dm: int, *, H: int, Hkv: int, D: int, gH: int, dk: int, dv: int,
+                  conv_k: int = 4, dtype: str = "bf16") -> dict:
+    """Random weights of one attention mixer and one Gated DeltaNet mixer of
+    model width dm. Projections are [out, in] with N(0, 1/in) entries (rounded
+    to bf16 for bf16 runs); the convolution taps [C, conv_k] are N(0, 1/conv_k);
+    a_log = log U(1, 16) and dt_bias = log(expm1(dt)) with dt log-uniform in
+    [1e-3, 1e-1] (the usual decay initialisation); the output norm weight is
+    1 + N(0, 0.1^2). Draw order: attention wq, wk, wv, wg, wo, then the
+    Gated DeltaNet wqkv, wab, wz, wo, conv taps, a_log, dt_bias, norm weight."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def proj(n_out, n_in):
+        w = _normal(rng, (n_out, n_in)) * np.float32(1.0 / np.sqrt(n_in))
+        return round_bf16(w) if dtype == "bf16" else w.astype(np.float32)
+
+    attn = dict(wq=proj(H * D, dm), wk=proj(Hkv * D, dm), wv=proj(Hkv * D, dm),
+                wg=proj(H * D, dm), wo=proj(dm, H * D), H=H, Hkv=Hkv, D=D)
+    C = 2 * gH * dk + gH * dv
+    gdn = dict(wqkv=proj(C, dm), wab=proj(2 * gH, dm), wz=proj(gH * dv, dm), wo=proj(dm, gH * dv))
+    gdn["conv_w"] = (_normal(rng, (C, conv_k)) * np.float32(1.0 / np.sqrt(conv_k))).astype(np.float32)
+    gdn["a_log"] = np.log(rng.uniform(1.0, 16.0, size=gH)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=gH))
+    gdn["dt_bias"] = np.log(np.expm1(dt)).astype(np.float32)
+    gdn["norm_w"] = (1.0 + 0.1 * _normal(rng, (dv,))).astype(np.float32)
+    gdn.update(H=gH, dk=dk, dv=dv)
+    return {"attn": attn, "gdn": gdn}
+
+
+def mixer_input(seed: int, T: int, dm: int, dtype: str = "bf16") -> np.ndarray:
+    """Token activations x [T, dm] ~ N(0, 1) (bf16-rounded for bf16 runs)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal(rng, (T, dm))
+    return round_bf16(x) if dtype == "bf16" else x
