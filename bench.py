@@ -37,6 +37,7 @@ METRIC = "branch tokens/s for ForkAttention + GDN fork layer; % of HBM/MFMA roof
 PEAK_BF16_MFMA = 2.5e15      # dense, FLOP/s
 PEAK_F32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12            # B/s
+SEED_MIXER = 2048             # seed of the mixer weights and input
 # capacity buckets for graph replay (tokens, segments)
 BUCKETS_T = [1 << 16, 1 << 17, 1 << 18, 3 << 17, 1 << 19]
 BUCKETS_S = [1 << 9, 1 << 12, 1 << 13]
@@ -482,6 +483,7 @@ def main():
         "measured_peaks": peaks,
     }
     out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
+    out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
     print(json.dumps(out), flush=True)
@@ -524,6 +526,93 @@ def block_ops(wl, sess, iters=50):
                          hbm_frac=nbytes / t / PEAK_HBM)
     rep["note"] = ("fork_rope_forward on q [T,16,128] and k [T,2,128]; fork_conv_forward on "
                    f"[T,{C}] (q | k | v of the Gated DeltaNet), width 4, SiLU; bf16")
+    return rep
+
+
+def mixer_ops(wl, sess, iters=20, dm=2048):
+    """Both token mixers of a hybrid block of model width dm on a workload's tree
+    (metadata already built in sess), random bf16 weights: the attention mixer
+    (q, k, v, gate projections, rotary embedding, tree attention, sigmoid gate,
+    output projection) and the Gated DeltaNet mixer (q | k | v, decay / strength
+    and output-gate projections, convolution, normalised inputs, forked Gated
+    DeltaNet, gated RMS norm, output projection). Timed with HIP events on the
+    launch stream; the projections alone are timed too, as plain GEMMs against
+    the bf16 MFMA peak, and the per-token kernels against HBM."""
+    import torch
+
+    from tree_structured_decision_amd import workloads as W
+
+    T = wl.T
+    Wt = W.mixer_weights(SEED_MIXER, dm, H=wl.H, Hkv=wl.Hkv, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv)
+    dev = lambda a, dt=torch.bfloat16: torch.from_numpy(a).to("cuda", dt)
+    A = {n: (dev(v) if isinstance(v, np.ndarray) else v) for n, v in Wt["attn"].items()}
+    G = {n: (dev(v) if isinstance(v, np.ndarray) and n.startswith("w") else
+             dev(v, torch.float32) if isinstance(v, np.ndarray) else v) for n, v in Wt["gdn"].items()}
+    x = dev(W.mixer_input(SEED_MIXER + 1, T, dm))
+    ab, gb = {}, {}
+    C = 2 * wl.gH * wl.dk + wl.gH * wl.dv
+    proj = [(A["wq"], "q"), (A["wk"], "k"), (A["wv"], "v"), (A["wg"], "g"),
+            (G["wqkv"], "p"), (G["wab"], "ab"), (G["wz"], "z")]
+    outs = {}
+
+    def projections():
+        for w, n in proj:
+            if n not in outs:
+                outs[n] = torch.empty(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
+            sess.linear(x, w, outs[n])
+        if "u" not in outs:
+            outs["u"] = torch.randn(T, wl.H * wl.D, device="cuda").to(torch.bfloat16)
+            outs["ug"] = torch.randn(T, wl.gH * wl.dv, device="cuda").to(torch.bfloat16)
+            outs["y"] = torch.empty(T, dm, dtype=torch.bfloat16, device="cuda")
+        sess.linear(outs["u"], A["wo"], outs["y"])
+        sess.linear(outs["ug"], G["wo"], outs["y"])
+
+    flop = 2.0 * T * dm * (sum(w.shape[0] for w, _ in proj) + wl.H * wl.D + wl.gH * wl.dv)
+    o = torch.randn(T, wl.H, wl.D, device="cuda").to(torch.bfloat16)
+    g = torch.randn_like(o)
+    og = torch.randn(T, wl.gH, wl.dv, device="cuda").to(torch.bfloat16)
+    zg = torch.randn_like(og)
+    u = torch.empty_like(o)
+    ug = torch.empty_like(og)
+    c = torch.randn(T, C, device="cuda").to(torch.bfloat16)
+    abp = torch.randn(T, 2 * wl.gH, device="cuda").to(torch.bfloat16)
+    q = torch.empty(T, wl.gH, wl.dk, dtype=torch.bfloat16, device="cuda")
+    k, v = torch.empty_like(q), torch.empty(T, wl.gH, wl.dv, dtype=torch.bfloat16, device="cuda")
+    aa = torch.empty(T, wl.gH, device="cuda")
+    bb = torch.empty_like(aa)
+    ops = {
+        "attention_mixer": (lambda: sess.attention_mixer(x, A, bufs=ab), None, None),
+        "gdn_mixer": (lambda: sess.gdn_mixer(x, G, bufs=gb), None, None),
+        "projections": (projections, "mfma", flop),
+        "gate_sigmoid": (lambda: sess.gate(o, g, None, u, 0), "hbm", 3.0 * o.numel() * 2),
+        "gated_rmsnorm": (lambda: sess.gate(og, zg, G["norm_w"], ug, 1), "hbm", 3.0 * og.numel() * 2),
+        "gdn_inputs": (lambda: sess.gdn_inputs(c, abp, G["a_log"], G["dt_bias"], q, k, v, aa, bb), "hbm",
+                       2.0 * c.numel() * 2 + abp.numel() * 2 + 2 * aa.numel() * 4),
+    }
+    rep = {}
+    for name, (fn, bound, work) in ops.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / iters
+        r = dict(us=t * 1e6)
+        if bound == "mfma":
+            r.update(algorithmic_flop=work, achieved_tflops=work / t / 1e12, mfma_frac=work / t / PEAK_BF16_MFMA)
+        elif bound == "hbm":
+            r.update(algorithmic_bytes=work, achieved_gbs=work / t / 1e9, hbm_frac=work / t / PEAK_HBM)
+        rep[name] = r
+    pair = rep["attention_mixer"]["us"] + rep["gdn_mixer"]["us"]
+    rep["mixer_pair_us"] = pair
+    rep["mixer_pair_tokens_per_s"] = T / (pair * 1e-6)
+    rep["note"] = (f"model width {dm}; attention 16 q / 2 kv heads x 128, Gated DeltaNet 16 heads x 128, "
+                   "convolution width 4; random bf16 weights; projections = the 9 GEMMs of both "
+                   "mixers (hipBLASLt, fp32 accumulation)")
     return rep
 
 
