@@ -291,14 +291,16 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
                                const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
                                int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream);
 
-/* Projection y [M, N] = x [M, K] w [N, K]^T, all row-major of dtype dt, fp32
- * accumulation (hipBLASLt). Rows are tokens of the flattened stream: one call
- * projects every branch, the shared prefix once. y must not overlap x or w.
+/* Projection y [M, N] = x [M, K] w [N, K]^T, or with accumulate = 1
+ * y += x w^T (a residual connection folded into the product), all row-major
+ * of dtype dt, fp32 accumulation (hipBLASLt). Rows are tokens of the
+ * flattened stream: one call projects every branch, the shared prefix once.
+ * y must not overlap x or w.
  * The first call on a device creates a hipBLASLt handle and a 32 MiB
  * workspace, kept for the process; the first call per (M, N, K, dt) picks the
  * algorithm and keeps it. Calls are serialised by a lock. */
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
-                                fork_dtype dt, void* stream);
+                                int32_t accumulate, fork_dtype dt, void* stream);
 
 /* ------------------------------------------------------------ graph buckets
  * A compact set of pre-recorded execution graphs serves varied request mixes

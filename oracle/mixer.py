@@ -22,6 +22,10 @@ gating of attention:
                     o = gated_deltanet(q, k, v, a, b), scale 1/sqrt(dk)
                     y = (rmsnorm(o) * w * silu(x Wz^T)) Wo^T
 
+A stack applies pre-norm residual layers, x <- x + mixer(rmsnorm(x) w_l),
+then a final RMS norm; the residual add happens before the one rounding of
+the sum, as in a product that accumulates into its output.
+
 Per-token steps are numpy float64; the tree-dependent steps call the oracle's
 rotary, convolution, attention and Gated DeltaNet (oracle.c). With
 ``bf16=True`` every stored intermediate is rounded to bf16 (nearest, ties to
@@ -87,8 +91,16 @@ def _f32(x):
     return np.ascontiguousarray(x, np.float32)
 
 
-def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: bool = False) -> np.ndarray:
-    """y [T, dm] of the attention mixer (weights as workloads.mixer_weights()['attn'])."""
+def _out(r, u, wo, residual):
+    """Output projection, with the residual added before the one rounding of the sum."""
+    y = linear(u, wo)
+    return r(y if residual is None else np.asarray(residual, np.float64) + y)
+
+
+def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: bool = False,
+                    residual=None, prec: str = "f64") -> np.ndarray:
+    """y [T, dm] of the attention mixer (weights as workloads.mixer_weights()['attn']);
+    with residual, residual + y. prec: precision of the attention oracle."""
     from . import attention, rope
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
@@ -99,16 +111,17 @@ def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: b
     g = r(linear(x, W["wg"])).reshape(T, H, D)
     q = r(rope(parent, seg_len, _f32(q), theta=theta))
     k = r(rope(parent, seg_len, _f32(k), theta=theta))
-    o, _ = attention(parent, seg_len, _f32(q), _f32(k), _f32(v))
+    o, _ = attention(parent, seg_len, _f32(q), _f32(k), _f32(v), prec=prec)
     u = r(gate(r(o), g, None, 0))
-    return r(linear(u.reshape(T, H * D), W["wo"]))
+    return _out(r, u.reshape(T, H * D), W["wo"], residual)
 
 
 def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False,
-              return_state: bool = False):
+              return_state: bool = False, residual=None, prec: str = "f64"):
     """y [T, dm] of the Gated DeltaNet mixer (weights as
-    workloads.mixer_weights()['gdn']); with return_state also the per-segment
-    start and end states."""
+    workloads.mixer_weights()['gdn']); with residual, residual + y; with
+    return_state also the per-segment start and end states. prec: precision
+    of the Gated DeltaNet oracle."""
     from . import conv, gdn
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
@@ -118,8 +131,25 @@ def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False
     ab = r(linear(x, W["wab"]))
     q, k, v, a, b = gdn_inputs(c, ab, W["a_log"], W["dt_bias"], H, dk, dv, eps)
     o, st0, st1 = gdn(parent, seg_len, _f32(r(q)), _f32(r(k)), _f32(r(v)), _f32(a), _f32(b),
-                      scale=1.0 / np.sqrt(dk))
+                      scale=1.0 / np.sqrt(dk), prec=prec)
     z = r(linear(x, W["wz"])).reshape(T, H, dv)
     u = r(gate(r(o), z, W["norm_w"], 1, eps))
-    y = r(linear(u.reshape(T, H * dv), W["wo"]))
+    y = _out(r, u.reshape(T, H * dv), W["wo"], residual)
     return (y, st0, st1) if return_state else y
+
+
+def stack(parent, seg_len, x, layers, final_norm, theta: float = 10000.0, eps: float = 1e-6,
+          bf16: bool = False, prec: str = "f64") -> np.ndarray:
+    """A pre-norm residual stack of mixers on the flattened stream:
+    x <- x + mixer(rmsnorm(x) w_l) for each layer, then h = rmsnorm(x) w_final.
+    layers: list of (kind, weights, norm weight [dm]) with kind "attn" or "gdn"."""
+    r = to_bf16 if bf16 else (lambda t: t)
+    x = np.asarray(x, np.float64)
+    for kind, W, nw in layers:
+        hn = r(gate(x, None, nw, 2, eps))
+        if kind == "attn":
+            x = attention_mixer(parent, seg_len, hn, W, theta, bf16, residual=x, prec=prec)
+        else:
+            x = gdn_mixer(parent, seg_len, hn, W, eps, bf16, residual=x, prec=prec)
+    return r(gate(x, None, final_norm, 2, eps))
+

@@ -13,13 +13,18 @@ Tolerances:
 * mixers end to end, oracle with every stored intermediate rounded to bf16 at
   the same points: relative RMS error <= 1e-2 and max error <= 5e-2 of the
   largest output (each intermediate may differ by one bf16 rounding where
-  fp32 and fp64 straddle a rounding boundary; fp32 runs: 1e-4 relative)."""
+  fp32 and fp64 straddle a rounding boundary; fp32 runs: 1e-4 relative);
+* stacks of four layers: the same bar on the final hidden states, and the
+  total-variation distance of every decision group's option softmax (the
+  scoring head of the fidelity measure) within 1e-2 of the bf16-rounded
+  oracle's (1e-5 in fp32) and within 2e-2 of the exact oracle's."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import mixer as OM
 from tests.gpu_helpers import check_close, log
+from tree_structured_decision_amd import metrics
 from tree_structured_decision_amd import workloads as W
 from tree_structured_decision_amd.session import ForkSession, caps_for
 
@@ -173,3 +178,48 @@ def test_mixers_one_request_full_size():
     yg = host(sess.gdn_mixer(xd, to_dev_weights(Wt["gdn"], "bf16")))
     compare_mixer("attention mixer one_request", ya, OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], bf16=True), "bf16")
     compare_mixer("GDN mixer one_request", yg, OM.gdn_mixer(wl.parent, wl.seg_len, x, Wt["gdn"], bf16=True), "bf16")
+
+
+def dev_stack(layers, fn, dtype):
+    return [(k, to_dev_weights(Wl, dtype), dev(nw)) for k, Wl, nw in layers], dev(fn)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stack_small_tree(dtype):
+    """Four pre-norm residual layers (GDN, attention, GDN, attention) on a
+    ragged forest; the residual add happens inside the output projections."""
+    # two requests whose decision groups hold 2-3 options each
+    rng = np.random.default_rng(61)
+    parent = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 2, 3, 3, -1, 11, 11, 11], np.int32)
+    seg_len = rng.integers(1, 41, parent.size).astype(np.int32)
+    seg_len[[4, 7]] = 1
+    T = int(seg_len.sum())
+    layers, fn, w_head = W.stack_weights(62, 256, H=4, Hkv=2, D=64, gH=2, dk=64, dv=64, dtype=dtype)
+    x = W.mixer_input(63, T, 256, dtype)
+    sess = session(parent, seg_len, group=2, kv_heads=2, D=64, gH=2, dk=64, dv=64)
+    dl, dfn = dev_stack(layers, fn, dtype)
+    xd = dev(x, dtype)
+    h = host(sess.stack(xd, dl, dfn))
+    ref = OM.stack(parent, seg_len, x, layers, fn, bf16=dtype == "bf16")
+    compare_mixer(f"stack of 4 {dtype}", h, ref, dtype)
+    fid = metrics.decision_fidelity(h, ref, w_head, parent, seg_len)
+    log(f"  option distributions vs oracle: {fid}")
+    assert fid["groups"] == 4 and fid["tvd_max"] <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def test_stack_one_request_full_size():
+    """The one-request tree at model width 2048, four layers: hidden states
+    against the bf16-rounded oracle, and the options' softmax against the
+    exact (fp64, unrounded) oracle, the pages' fidelity measure."""
+    wl = W.one_request()
+    layers, fn, w_head = W.stack_weights(71, 2048, H=16, Hkv=2, D=128, gH=16, dk=128, dv=128)
+    x = W.mixer_input(72, wl.T, 2048)
+    sess = session(wl.parent, wl.seg_len, group=8, kv_heads=2, D=128, gH=16, dk=128, dv=128)
+    dl, dfn = dev_stack(layers, fn, "bf16")
+    h = host(sess.stack(dev(x, "bf16"), dl, dfn))
+    ref16 = OM.stack(wl.parent, wl.seg_len, x, layers, fn, bf16=True)
+    compare_mixer("stack of 4 one_request", h, ref16, "bf16")
+    ref64 = OM.stack(wl.parent, wl.seg_len, x, layers, fn)
+    fid = metrics.decision_fidelity(h, ref64, w_head, wl.parent, wl.seg_len)
+    log(f"  option distributions vs the exact oracle: {fid}")
+    assert fid["tvd_max"] <= 2e-2

@@ -392,8 +392,9 @@ def test_mixer_piece_argument_errors_without_gpu():
     assert gi(H=0) == -1
     assert gi(dk=12) == -3 and gi(dv=2048) == -3
     assert gi(eps=-1.0) == -1
-    lin = lambda M=4, N=8, K=16, x=fake, y=0x3000, dt=B.FORK_BF16: _status(
-        lambda: B.fork_linear_forward(x, 0x4000, y, M, N, K, dt, stream=0))
+    lin = lambda M=4, N=8, K=16, x=fake, y=0x3000, acc=0, dt=B.FORK_BF16: _status(
+        lambda: B.fork_linear_forward(x, 0x4000, y, M, N, K, acc, dt, stream=0))
+    assert lin(acc=2) == -1
     assert lin(M=0) == -1 and lin(K=-1) == -1
     assert lin(x=None) == -1
     assert lin(y=fake) == -1

@@ -174,3 +174,36 @@ def test_bf16_rounding_points_stay_close():
         y64, y16 = f(parent, seg_len, x, Wt[key]), f(parent, seg_len, x, Wt[key], bf16=True)
         rel = np.linalg.norm(y16 - y64) / np.linalg.norm(y64)
         assert 1e-5 < rel < 2 ** -6, rel
+
+
+def test_stack_with_silent_layers_is_the_final_norm():
+    """With every output projection zero, the residual stream is never
+    changed: the stack returns rmsnorm(x) w_final of the input."""
+    rng = np.random.default_rng(16)
+    parent, seg_len = W.random_tree(rng, 5, 6, max_depth=3)
+    T = int(seg_len.sum())
+    layers, fn, _ = W.stack_weights(17, 32, H=4, Hkv=2, D=16, gH=2, dk=16, dv=16, dtype="f32")
+    silent = []
+    for kind, Wl, nw in layers:
+        Wl = dict(Wl)
+        Wl["wo"] = np.zeros_like(Wl["wo"])
+        silent.append((kind, Wl, nw))
+    x = W.mixer_input(18, T, 32, "f32").astype(np.float64)
+    h = M.stack(parent, seg_len, x, silent, fn)
+    ref = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + 1e-6) * fn
+    assert np.allclose(h, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_stack_equals_isolated_paths():
+    rng = np.random.default_rng(19)
+    parent, seg_len = W.random_tree(rng, 8, 6, max_depth=4)
+    seg_len[rng.integers(0, 8, 3)] = 1
+    T = int(seg_len.sum())
+    layers, fn, _ = W.stack_weights(20, 32, H=4, Hkv=2, D=16, gH=2, dk=16, dv=16, dtype="f32")
+    x = W.mixer_input(21, T, 32, "f32").astype(np.float64)
+    h = M.stack(parent, seg_len, x, layers, fn)
+    start = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
+    for leaf in [s for s in range(len(parent)) if not (parent == s).any()]:
+        rows = np.concatenate([np.arange(start[s], start[s] + seg_len[s]) for s in path_segments(parent, leaf)])
+        hi = M.stack(np.array([-1], np.int32), np.array([len(rows)], np.int32), x[rows], layers, fn)
+        assert np.allclose(h[rows], hi, rtol=1e-9, atol=1e-9)

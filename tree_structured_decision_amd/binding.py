@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
             "fork_gate_forward": [P(fork_meta), vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
             "gdn_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                    f32, i32, vp],
-            "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, vp],
+            "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, i32, vp],
             "fork_graph_create": [P(fork_meta), P(fork_graph_args), vp, P(vp)],
             "fork_graph_launch": [vp, vp],
             "fork_graph_destroy": [vp],
@@ -281,8 +281,8 @@ def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H:
                                     dk, dv, float(eps), dt, _stream(stream)))
 
 
-def fork_linear_forward(x, w, y, M: int, N: int, K: int, dt: int, stream=None) -> None:
-    _check(lib().fork_linear_forward(_ptr(x), _ptr(w), _ptr(y), M, N, K, dt, _stream(stream)))
+def fork_linear_forward(x, w, y, M: int, N: int, K: int, accumulate: int, dt: int, stream=None) -> None:
+    _check(lib().fork_linear_forward(_ptr(x), _ptr(w), _ptr(y), M, N, K, accumulate, dt, _stream(stream)))
 
 
 def fork_graph_create(meta: fork_meta, args: fork_graph_args, stream=None) -> int:

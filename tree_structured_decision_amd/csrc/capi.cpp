@@ -602,13 +602,14 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
 }
 
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
-                                fork_dtype dt, void* stream) {
+                                int32_t accumulate, fork_dtype dt, void* stream) {
   g_err[0] = 0;
   if (!x || !w || !y) return fail(FORK_E_ARG, "x, w and y must be non-null");
   if (M < 1 || N < 1 || K < 1) return fail(FORK_E_ARG, "M=%d N=%d K=%d", M, N, K);
   if (y == x || y == w) return fail(FORK_E_ARG, "y must not overlap x or w");
+  if (accumulate != 0 && accumulate != 1) return fail(FORK_E_ARG, "accumulate %d (0 or 1)", accumulate);
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  return launch_linear(x, w, y, M, N, K, dt, (hipStream_t)stream);
+  return launch_linear(x, w, y, M, N, K, accumulate, dt, (hipStream_t)stream);
 }
 
 }  // extern "C"

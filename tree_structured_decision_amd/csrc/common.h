@@ -173,8 +173,8 @@ fork_status launch_gate(const fork_meta* m, const void* x, const void* g, const 
 fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, const float* a_log,
                               const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int H, int dk,
                               int dv, float eps, fork_dtype dt, hipStream_t stream);
-fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, fork_dtype dt,
-                          hipStream_t stream);
+fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, int accumulate,
+                          fork_dtype dt, hipStream_t stream);
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);
 fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v,
                        const float* a, const float* b, const float* root_state, void* o,

@@ -1,5 +1,6 @@
-// Dense projections of a hybrid block: y [M, N] = x [M, K] w[N, K]^T on
-// the flattened stream, fp32 accumulation. Rows are tokens, so one product
+// Dense projections of a hybrid block: y [M, N] = x [M, K] w[N, K]^T (or
+// y += x w^T, the residual connection folded into the product) on the
+// flattened stream, fp32 accumulation. Rows are tokens, so one product
 // covers every branch and the shared prefix is projected once. These are
 // plain GEMMs and go to hipBLASLt: in its column-major terms y^T = w x^T,
 // i.e. D (N x M, ld N) = op(A) B with A = w stored K x N (ld K) and
@@ -70,8 +71,8 @@ fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, LtPlan& 
 
 }  // namespace
 
-fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, fork_dtype dt,
-                          hipStream_t stream) {
+fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, int accumulate,
+                          fork_dtype dt, hipStream_t stream) {
   int dev = 0;
   FORK_HIP_CHECK(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) return fail(FORK_E_UNSUPPORTED, "device %d", dev);
@@ -90,7 +91,7 @@ fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, i
     it = d.plans.emplace(key, p).first;
   }
   const LtPlan& p = it->second;
-  const float alpha = 1.f, beta = 0.f;
+  const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
   LT_CHECK(hipblasLtMatmul(d.h, p.desc, &alpha, w, p.la, x, p.lb, &beta, y, p.lc, y, p.lc, &p.algo, d.ws, p.ws,
                            stream));
   return FORK_OK;

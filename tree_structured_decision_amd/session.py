@@ -120,19 +120,21 @@ class ForkSession:
                              stream=stream)
 
     @staticmethod
-    def linear(x, w, y, stream=None):
-        """y [M, N] = x [M, K] w [N, K]^T."""
+    def linear(x, w, y, stream=None, accumulate: bool = False):
+        """y [M, N] = x [M, K] w [N, K]^T (accumulate: y += x w^T)."""
         M, K = x.shape
         N = w.shape[0]
         dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
-        B.fork_linear_forward(x, w, y, M, N, K, dt, stream=stream)
+        B.fork_linear_forward(x, w, y, M, N, K, int(accumulate), dt, stream=stream)
 
-    def attention_mixer(self, x, W: dict, theta: float = 10000.0, stream=None, bufs: dict = None):
+    def attention_mixer(self, x, W: dict, theta: float = 10000.0, stream=None, bufs: dict = None,
+                        residual=None):
         """Attention mixer of a hybrid block on the current tree: projections, rotary
         embedding at the isolated positions, tree attention, sigmoid output gate,
         output projection. x [T, dm]; W holds device tensors wq, wk, wv, wg, wo and
-        the ints H, Hkv, D. Returns y [T, dm]. bufs: optional dict reused across
-        calls for the intermediates."""
+        the ints H, Hkv, D. Returns y [T, dm], or with residual [T, dm] adds y into it
+        (inside the output projection) and returns it. bufs: optional dict reused
+        across calls for the intermediates."""
         T, dm = x.shape
         H, Hkv, D = W["H"], W["Hkv"], W["D"]
         b = self._bufs(bufs, x, dict(q=(T, H, D), k=(T, Hkv, D), v=(T, Hkv, D), g=(T, H, D),
@@ -145,16 +147,20 @@ class ForkSession:
         self.rope(b["k"], theta, stream)
         self.attention(b["q"], b["k"], b["v"], b["o"], stream=stream)
         self.gate(b["o"], b["g"], None, b["u"], 0, stream=stream)
+        if residual is not None:
+            self.linear(b["u"].view(T, H * D), W["wo"], residual, stream, accumulate=True)
+            return residual
         self.linear(b["u"].view(T, H * D), W["wo"], b["y"], stream)
         return b["y"]
 
     def gdn_mixer(self, x, W: dict, eps: float = 1e-6, stream=None, bufs: dict = None,
-                  seg_start_state=None):
+                  seg_start_state=None, residual=None):
         """Gated DeltaNet mixer of a hybrid block on the current tree: projections,
         causal convolution along the isolated sequences (+ SiLU), normalised inputs and
         gates, forked Gated DeltaNet, gated RMS norm, output projection. x [T, dm]; W
         holds device tensors wqkv, wab, wz, wo, conv_w, a_log, dt_bias, norm_w and the
-        ints H, dk, dv. Returns y [T, dm]."""
+        ints H, dk, dv. Returns y [T, dm] (or residual + y in residual, as
+        attention_mixer)."""
         T, dm = x.shape
         H, dk, dv = W["H"], W["dk"], W["dv"]
         C = 2 * H * dk + H * dv
@@ -178,8 +184,30 @@ class ForkSession:
                         b["b"], eps, stream)
         self.gdn(b["q"], b["k"], b["v"], b["a"], b["b"], b["o"], st, scale=dk ** -0.5, stream=stream)
         self.gate(b["o"], b["z"], W["norm_w"], b["u"], 1, eps, stream)
+        if residual is not None:
+            self.linear(b["u"].view(T, H * dv), W["wo"], residual, stream, accumulate=True)
+            return residual
         self.linear(b["u"].view(T, H * dv), W["wo"], b["y"], stream)
         return b["y"]
+
+    def stack(self, x, layers, final_norm, theta: float = 10000.0, eps: float = 1e-6,
+              stream=None, bufs: dict = None):
+        """Pre-norm residual stack on the current tree, in place on x [T, dm]:
+        x <- x + mixer(rmsnorm(x) w_l) for each (kind, weights, norm weight) in
+        layers (kind "attn" or "gdn"; the add happens in the output projection),
+        then returns h = rmsnorm(x) w_final."""
+        T, dm = x.shape
+        b = self._bufs(bufs, x, dict(hn=(T, 1, dm), h=(T, 1, dm)))
+        b.setdefault("mixers", {})
+        for i, (kind, W, nw) in enumerate(layers):
+            mb = b["mixers"].setdefault(i, {})
+            self.gate(x.view(T, 1, dm), None, nw, b["hn"], 2, eps, stream)
+            if kind == "attn":
+                self.attention_mixer(b["hn"].view(T, dm), W, theta, stream, mb, residual=x)
+            else:
+                self.gdn_mixer(b["hn"].view(T, dm), W, eps, stream, mb, residual=x)
+        self.gate(x.view(T, 1, dm), None, final_norm, b["h"], 2, eps, stream)
+        return b["h"].view(T, dm)
 
     @staticmethod
     def _bufs(bufs, x, shapes):

@@ -336,3 +336,20 @@ def mixer_input(seed: int, T: int, dm: int, dtype: str = "bf16") -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     x = _normal(rng, (T, dm))
     return round_bf16(x) if dtype == "bf16" else x
+
+
+def stack_weights(seed: int, dm: int, kinds=("gdn", "attn", "gdn", "attn"), *, H: int, Hkv: int, D: int,
+                  gH: int, dk: int, dv: int, conv_k: int = 4, dtype: str = "bf16"):
+    """Weights of a pre-norm residual stack of mixers: for each layer
+    (kind, mixer weights, pre-norm weight [dm]); then the final norm weight
+    [dm] and the option readout vector w_head [dm] ~ N(0, 1). Norm weights are
+    1 + N(0, 0.1^2). Layer l's mixer weights come from mixer_weights(seed + 1 + l)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    layers = []
+    for i, kind in enumerate(kinds):
+        mw = mixer_weights(seed + 1 + i, dm, H=H, Hkv=Hkv, D=D, gH=gH, dk=dk, dv=dv, conv_k=conv_k, dtype=dtype)
+        nw = (1.0 + 0.1 * _normal(rng, (dm,))).astype(np.float32)
+        layers.append((kind, mw[kind], nw))
+    final_norm = (1.0 + 0.1 * _normal(rng, (dm,))).astype(np.float32)
+    w_head = _normal(rng, (dm,))
+    return layers, final_norm, w_head
