@@ -18,7 +18,13 @@ Also reported on the same JSON line:
   rates         option tokens/s, isolated-equivalent tokens/s, us per option;
   cold_cache    the layer pair's kernel times with caches evicted between steps;
   measured_peaks  a bf16 GEMM and a device copy on this GPU, the achievable
-                peaks the roofline fraction is also given against.
+                peaks the roofline fraction is also given against;
+  block_ops     the fork-aware rotary embedding and short convolution;
+  mixers        both token mixers of a hybrid block (model width 2048): the
+                projections against the MFMA peak, the per-token kernels
+                against HBM;
+  stack         a four-layer hybrid stack and the option distributions' TVD
+                to the float32 oracle (computed in the CPU-baseline leg).
 """
 from __future__ import annotations
 
@@ -347,6 +353,22 @@ def cpu_baseline(wl, threads):
     return dt, o, go
 
 
+def cpu_stack_fidelity(wl, stack_inputs):
+    """The float32 oracle of the hybrid stack (unrounded intermediates) as the
+    reference of the option distributions' total-variation distance."""
+    import oracle
+    from oracle import mixer as OM
+    from tree_structured_decision_amd import metrics
+
+    h_gpu, x0, layers, fn, w_head = stack_inputs
+    t0 = time.perf_counter()
+    ref = OM.stack(wl.parent, wl.seg_len, x0, layers, fn, prec="f32")
+    fid = metrics.decision_fidelity(h_gpu, ref, w_head, wl.parent, wl.seg_len)
+    fid["reference"] = "float32 oracle (unrounded intermediates)"
+    fid["oracle_s"] = time.perf_counter() - t0
+    return fid
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,6 +506,10 @@ def main():
     }
     out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
     out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
+    st, st_inputs = stack_ops(wl, r.sess)
+    if not args.no_cpu:
+        st["fidelity"] = cpu_stack_fidelity(wl, st_inputs)
+    out["stack"] = {"one_request": st}
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
     print(json.dumps(out), flush=True)
@@ -614,6 +640,58 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
                    "convolution width 4; random bf16 weights; projections = the 9 GEMMs of both "
                    "mixers (hipBLASLt, fp32 accumulation)")
     return rep
+
+
+def stack_ops(wl, sess, iters=10, dm=2048):
+    """A four-layer hybrid stack (Gated DeltaNet, attention, Gated DeltaNet,
+    attention; pre-norm residual, model width dm, random bf16 weights) on a
+    workload's tree, then the option readout: per decision group, the softmax
+    of <w_head, h at each option's last token>. Reports the time per stack pass
+    (HIP events on the launch stream) and the total-variation distance of the
+    option distributions to the float32 oracle's (the fidelity measure of the
+    pages, computed in the CPU-baseline leg), with argmax agreement. Returns the
+    report and what that leg needs (the GPU's final hidden states, the inputs
+    and weights)."""
+    import torch
+
+    from tree_structured_decision_amd import workloads as W
+
+    T = wl.T
+    layers, fn, w_head = W.stack_weights(SEED_MIXER + 10, dm, H=wl.H, Hkv=wl.Hkv, D=wl.D, gH=wl.gH,
+                                         dk=wl.dk, dv=wl.dv)
+
+    def dev(a, bf=False):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(
+            "cuda", torch.bfloat16 if bf else torch.float32)
+
+    dl = [(k, {n: (dev(v, n.startswith("w") and v.ndim == 2) if isinstance(v, np.ndarray) else v)
+               for n, v in Wl.items()}, dev(nw)) for k, Wl, nw in layers]
+    dfn = dev(fn)
+    x0 = W.mixer_input(SEED_MIXER + 20, T, dm)
+    x0d = dev(x0, True)
+    x = torch.empty_like(x0d)
+    bufs = {}
+
+    def once():
+        x.copy_(x0d)
+        return sess.stack(x, dl, dfn, bufs=bufs)
+
+    for _ in range(2):
+        once()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        h = once()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / iters
+    rep = dict(layers=[k for k, _, _ in layers], model_width=dm, us=t * 1e6, tokens_per_s=T / t,
+               fidelity=None)
+    rep["note"] = ("pre-norm residual stack; the residual add happens in the output projections; "
+                   "each pass includes a copy of the input into the residual stream")
+    h_gpu = h.float().cpu().numpy().astype(np.float64)
+    return rep, (h_gpu, x0, layers, fn, w_head)
 
 
 def calib_copy(enabled: bool):
