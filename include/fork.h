@@ -302,6 +302,33 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
                                 int32_t accumulate, fork_dtype dt, void* stream);
 
+/* ------------------------------------------------------------------ FP8
+ * FP8 execution where the hardware has it (techfi24.com page, "Exact State
+ * Forking" section: the kernels use FP8 when available and a large model is
+ * run quantised to FP8). Format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals, largest finite 448, no
+ * infinities), one byte per value, with one fp32 scale per row:
+ * value = decode(code) * scale[row]. A row of activations is one token, so a
+ * token's codes depend on that token alone and every branch of the stream is
+ * quantised exactly as in its isolated pass. */
+
+/* Row-wise quantisation of x [rows, K] (dtype dt) to codes q [rows, K] (bytes):
+ *   scales[r] = max_k |x[r][k]| / 448 (1 for an all-zero row),
+ *   q[r][k]   = E4M3 nearest-even rounding of clamp(x[r][k] / scales[r], -448, 448),
+ * both divisions correctly rounded fp32. scales [rows] fp32 (device). K a
+ * positive multiple of 8; x 16-byte and q 8-byte aligned. */
+fork_status fork_quantize_fp8(const void* x, void* q, float* scales, int64_t rows, int32_t K, fork_dtype dt,
+                              void* stream);
+
+/* FP8 projection y [M, N] (bf16) with
+ *   y[m][n] = (sum_k xq[m][k] wq[n][k]) * x_scale[m] * w_scale[n]
+ * (or y += that with accumulate = 1): E4M3 codes with row scales as written
+ * by fork_quantize_fp8 (x_scale [M], w_scale [N], device), fp32 accumulation
+ * on the FP8 matrix cores (hipBLASLt). K a multiple of 16. Handle, workspace
+ * and algorithm choice as fork_linear_forward. */
+fork_status fork_linear_fp8_forward(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                                    void* y, int32_t M, int32_t N, int32_t K, int32_t accumulate, void* stream);
+
 /* ------------------------------------------------------------ graph buckets
  * A compact set of pre-recorded execution graphs serves varied request mixes
  * (kongchang.com page, section "pre-recorded execution graphs"). A fork_graph

@@ -22,6 +22,11 @@ gating of attention:
                     o = gated_deltanet(q, k, v, a, b), scale 1/sqrt(dk)
                     y = (rmsnorm(o) * w * silu(x Wz^T)) Wo^T
 
+With ``fp8=True`` every projection takes E4M3 operands: its input (per token)
+and its weight (per output channel) are quantised as ``quantize_fp8`` (row
+scale = max|.| / 448, nearest-even codes, decided in fp32 as on the GPU) and
+the product is taken on the decoded values.
+
 A stack applies pre-norm residual layers, x <- x + mixer(rmsnorm(x) w_l),
 then a final RMS norm; the residual add happens before the one rounding of
 the sum, as in a product that accumulates into its output.
@@ -91,55 +96,66 @@ def _f32(x):
     return np.ascontiguousarray(x, np.float32)
 
 
-def _out(r, u, wo, residual):
+def _lin(x, w, fp8):
+    """A projection; with fp8 both operands are quantised row-wise first."""
+    if not fp8:
+        return linear(x, w)
+    qx, sx = quantize_fp8(x)
+    qw, sw = quantize_fp8(w)
+    return linear_fp8(qx, sx, qw, sw)
+
+
+def _out(r, u, wo, residual, fp8=False):
     """Output projection, with the residual added before the one rounding of the sum."""
-    y = linear(u, wo)
+    y = _lin(u, wo, fp8)
     return r(y if residual is None else np.asarray(residual, np.float64) + y)
 
 
 def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: bool = False,
-                    residual=None, prec: str = "f64") -> np.ndarray:
+                    residual=None, prec: str = "f64", fp8: bool = False) -> np.ndarray:
     """y [T, dm] of the attention mixer (weights as workloads.mixer_weights()['attn']);
-    with residual, residual + y. prec: precision of the attention oracle."""
+    with residual, residual + y. prec: precision of the attention oracle. fp8:
+    every projection takes E4M3 operands (input per token and weight per
+    output channel, quantised as quantize_fp8)."""
     from . import attention, rope
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
     H, Hkv, D = W["H"], W["Hkv"], W["D"]
-    q = r(linear(x, W["wq"])).reshape(T, H, D)
-    k = r(linear(x, W["wk"])).reshape(T, Hkv, D)
-    v = r(linear(x, W["wv"])).reshape(T, Hkv, D)
-    g = r(linear(x, W["wg"])).reshape(T, H, D)
+    q = r(_lin(x, W["wq"], fp8)).reshape(T, H, D)
+    k = r(_lin(x, W["wk"], fp8)).reshape(T, Hkv, D)
+    v = r(_lin(x, W["wv"], fp8)).reshape(T, Hkv, D)
+    g = r(_lin(x, W["wg"], fp8)).reshape(T, H, D)
     q = r(rope(parent, seg_len, _f32(q), theta=theta))
     k = r(rope(parent, seg_len, _f32(k), theta=theta))
     o, _ = attention(parent, seg_len, _f32(q), _f32(k), _f32(v), prec=prec)
     u = r(gate(r(o), g, None, 0))
-    return _out(r, u.reshape(T, H * D), W["wo"], residual)
+    return _out(r, u.reshape(T, H * D), W["wo"], residual, fp8)
 
 
 def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False,
-              return_state: bool = False, residual=None, prec: str = "f64"):
+              return_state: bool = False, residual=None, prec: str = "f64", fp8: bool = False):
     """y [T, dm] of the Gated DeltaNet mixer (weights as
     workloads.mixer_weights()['gdn']); with residual, residual + y; with
     return_state also the per-segment start and end states. prec: precision
-    of the Gated DeltaNet oracle."""
+    of the Gated DeltaNet oracle. fp8: as attention_mixer."""
     from . import conv, gdn
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
     H, dk, dv = W["H"], W["dk"], W["dv"]
-    p = r(linear(x, W["wqkv"]))
+    p = r(_lin(x, W["wqkv"], fp8))
     c = r(conv(parent, seg_len, _f32(p), W["conv_w"], act=1))
-    ab = r(linear(x, W["wab"]))
+    ab = r(_lin(x, W["wab"], fp8))
     q, k, v, a, b = gdn_inputs(c, ab, W["a_log"], W["dt_bias"], H, dk, dv, eps)
     o, st0, st1 = gdn(parent, seg_len, _f32(r(q)), _f32(r(k)), _f32(r(v)), _f32(a), _f32(b),
                       scale=1.0 / np.sqrt(dk), prec=prec)
-    z = r(linear(x, W["wz"])).reshape(T, H, dv)
+    z = r(_lin(x, W["wz"], fp8)).reshape(T, H, dv)
     u = r(gate(r(o), z, W["norm_w"], 1, eps))
-    y = _out(r, u.reshape(T, H * dv), W["wo"], residual)
+    y = _out(r, u.reshape(T, H * dv), W["wo"], residual, fp8)
     return (y, st0, st1) if return_state else y
 
 
 def stack(parent, seg_len, x, layers, final_norm, theta: float = 10000.0, eps: float = 1e-6,
-          bf16: bool = False, prec: str = "f64") -> np.ndarray:
+          bf16: bool = False, prec: str = "f64", fp8: bool = False) -> np.ndarray:
     """A pre-norm residual stack of mixers on the flattened stream:
     x <- x + mixer(rmsnorm(x) w_l) for each layer, then h = rmsnorm(x) w_final.
     layers: list of (kind, weights, norm weight [dm]) with kind "attn" or "gdn"."""
@@ -148,8 +164,67 @@ def stack(parent, seg_len, x, layers, final_norm, theta: float = 10000.0, eps: f
     for kind, W, nw in layers:
         hn = r(gate(x, None, nw, 2, eps))
         if kind == "attn":
-            x = attention_mixer(parent, seg_len, hn, W, theta, bf16, residual=x, prec=prec)
+            x = attention_mixer(parent, seg_len, hn, W, theta, bf16, residual=x, prec=prec, fp8=fp8)
         else:
-            x = gdn_mixer(parent, seg_len, hn, W, eps, bf16, residual=x, prec=prec)
+            x = gdn_mixer(parent, seg_len, hn, W, eps, bf16, residual=x, prec=prec, fp8=fp8)
     return r(gate(x, None, final_norm, 2, eps))
 
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+# OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+# field 0 holds subnormals m/8 * 2^-6; the largest finite value is
+# 1.75 * 2^8 = 448 (code 0x7E; 0x7F is NaN, there are no infinities).
+
+def e4m3_encode(t) -> np.ndarray:
+    """Nearest-even E4M3 codes (uint8) of values with |t| <= 448."""
+    t = np.asarray(t, np.float64)
+    a = np.abs(t)
+    assert (a <= 448.0).all()
+    sign = (np.signbit(t)).astype(np.int64) << 7
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    normal = a >= 2.0 ** -6
+    # normals: 3 fraction bits at exponent e; subnormals: steps of 2^-9
+    m = np.where(normal, np.round((a / np.ldexp(1.0, e) - 1.0) * 8.0), np.round(a / 2.0 ** -9))
+    m = m.astype(np.int64)
+    ef = np.where(normal, e + 7, 0)
+    up = normal & (m == 8)            # rounding carried into the next binade
+    ef = np.where(up, ef + 1, ef)
+    m = np.where(up, 0, m)
+    sub_up = (~normal) & (m == 8)     # largest subnormal rounded up to 2^-6
+    ef = np.where(sub_up, 1, ef)
+    m = np.where(sub_up, 0, m)
+    return (sign | (ef << 3) | m).astype(np.uint8)
+
+
+def e4m3_decode(c) -> np.ndarray:
+    """Values of E4M3 codes (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(c, np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = c & 7
+    v = np.where(ef == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, ef - 7))
+    v = np.where((ef == 15) & (m == 7), np.nan, v)
+    return s * v
+
+
+def quantize_fp8(x):
+    """Row-wise quantisation (rows along the last axis), decided in fp32 as on
+    the GPU: scale_r = fp32(max_k |x[r][k]|) / 448 (1 for an all-zero row),
+    code = E4M3(clamp(fp32(x) / scale_r, -448, 448)) with correctly rounded
+    fp32 divisions. Returns (codes uint8, scales float32 [rows])."""
+    x32 = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x32), axis=-1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    t = np.clip(x32 / scale[..., None], np.float32(-448.0), np.float32(448.0))
+    return e4m3_encode(t.astype(np.float64)), scale
+
+
+def dequantize_fp8(codes, scale) -> np.ndarray:
+    return e4m3_decode(codes) * np.asarray(scale, np.float64)[..., None]
+
+
+def linear_fp8(xq, x_scale, wq, w_scale) -> np.ndarray:
+    """y[m][n] = (sum_k decode(xq[m][k]) decode(wq[n][k])) x_scale[m] w_scale[n]."""
+    return (e4m3_decode(xq) @ e4m3_decode(wq).T) * np.outer(np.asarray(x_scale, np.float64),
+                                                          np.asarray(w_scale, np.float64))

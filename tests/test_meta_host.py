@@ -399,3 +399,18 @@ def test_mixer_piece_argument_errors_without_gpu():
     assert lin(x=None) == -1
     assert lin(y=fake) == -1
     assert lin(dt=9) == -3
+
+
+def test_fp8_argument_errors_without_gpu():
+    fake = 0x2000
+    qz = lambda rows=4, K=64, x=fake, q=0x3000, dt=B.FORK_BF16: _status(
+        lambda: B.fork_quantize_fp8(x, q, 0x4000, rows, K, dt, stream=0))
+    assert qz(rows=0) == -1 and qz(x=None) == -1
+    assert qz(K=12) == -3 and qz(K=0) == -3
+    assert qz(x=fake + 8) == -1 and qz(q=0x3004) == -1
+    assert qz(dt=5) == -3
+    lf = lambda M=4, N=8, K=64, acc=0, y=0x5000: _status(
+        lambda: B.fork_linear_fp8_forward(fake, 0x3000, 0x4000, 0x4800, y, M, N, K, acc, stream=0))
+    assert lf(K=24) == -3
+    assert lf(M=0) == -1 and lf(acc=3) == -1
+    assert lf(y=fake) == -1

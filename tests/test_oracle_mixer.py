@@ -207,3 +207,71 @@ def test_stack_equals_isolated_paths():
         rows = np.concatenate([np.arange(start[s], start[s] + seg_len[s]) for s in path_segments(parent, leaf)])
         hi = M.stack(np.array([-1], np.int32), np.array([len(rows)], np.int32), x[rows], layers, fn)
         assert np.allclose(h[rows], hi, rtol=1e-9, atol=1e-9)
+
+
+def test_e4m3_codes_from_the_format_definition():
+    # every non-NaN code decodes and re-encodes to itself
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    v = M.e4m3_decode(codes)
+    back = M.e4m3_encode(v)
+    assert np.array_equal(back[np.abs(v) > 0], codes[np.abs(v) > 0])
+    assert M.e4m3_decode(0x7E) == 448.0 and M.e4m3_decode(0x38) == 1.0 and M.e4m3_decode(0xB8) == -1.0
+    assert M.e4m3_decode(0x01) == 2.0 ** -9 and M.e4m3_decode(0x08) == 2.0 ** -6
+    assert np.isnan(M.e4m3_decode(0x7F))
+    # values are strictly increasing over the positive codes
+    pos = M.e4m3_decode(np.arange(0, 0x7F))
+    assert (np.diff(pos) > 0).all()
+    # ties go to the even mantissa: 1 + 1/16 between 1 and 1.125 -> 1; 1 + 3/16 -> 1.25
+    assert M.e4m3_encode(1.0625) == 0x38 and M.e4m3_encode(1.1875) == 0x3A
+    # a subnormal tie (2.5 * 2^-9) goes to 2 * 2^-9; the largest subnormal rounds up to 2^-6
+    assert M.e4m3_encode(2.5 * 2.0 ** -9) == 0x02 and M.e4m3_encode(7.75 * 2.0 ** -9) == 0x08
+    # carries into the next binade: 1.9375 is halfway between 1.875 and 2 -> 2 (even)
+    assert M.e4m3_encode(1.9375) == 0x40
+    # nearest: on random values the error is at most half a step
+    x = np.random.default_rng(22).uniform(-448, 448, 5000)
+    d = M.e4m3_decode(M.e4m3_encode(x))
+    step = np.where(np.abs(x) >= 2.0 ** -6, np.ldexp(1.0, np.floor(np.log2(np.abs(x))).astype(int) - 3), 2.0 ** -9)
+    assert (np.abs(d - x) <= step / 2 + 1e-12).all()
+
+
+def test_quantize_fp8_row_scales_and_extremes():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((6, 512)) * rng.uniform(0.01, 30, (6, 1))).astype(np.float32)
+    q, s = M.quantize_fp8(x)
+    amax = np.abs(x).max(axis=1)
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    # each row's largest magnitude maps to +-448 (code 0x7E / 0xFE)
+    assert ((q[np.arange(6), np.argmax(np.abs(x), axis=1)] & 0x7F) == 0x7E).all()
+    # relative error of values in the normal range is at most 2^-4
+    d = M.dequantize_fp8(q, s)
+    big = np.abs(x) >= 2.0 ** -6 * s[:, None]
+    assert (np.abs(d - x)[big] <= 2.0 ** -4 * np.abs(x)[big] * (1 + 1e-6)).all()
+    # rows are independent: quantising one row alone gives the same codes
+    q1, s1 = M.quantize_fp8(x[3:4])
+    assert np.array_equal(q1[0], q[3]) and s1[0] == s[3]
+    z, sz = M.quantize_fp8(np.zeros((2, 16), np.float32))
+    assert (sz == 1.0).all() and (z == 0).all()
+    # a product of quantised operands is the product of their decoded values
+    w = rng.standard_normal((5, 64)).astype(np.float32)
+    xx = rng.standard_normal((3, 64)).astype(np.float32)
+    qx, sx = M.quantize_fp8(xx)
+    qw, sw = M.quantize_fp8(w)
+    assert np.allclose(M.linear_fp8(qx, sx, qw, sw), M.dequantize_fp8(qx, sx) @ M.dequantize_fp8(qw, sw).T, rtol=1e-12)
+
+
+def test_fp8_mixers_equal_isolated_paths():
+    """With per-token activation scales the FP8 mixers keep the isolated-pass
+    equivalence: each leaf's path alone gives the tree's rows."""
+    rng = np.random.default_rng(24)
+    parent, seg_len = W.random_tree(rng, 7, 6, max_depth=3)
+    T = int(seg_len.sum())
+    Wt = small_weights(25, 32)
+    x = W.mixer_input(26, T, 32, "f32").astype(np.float64)
+    ya = M.attention_mixer(parent, seg_len, x, Wt["attn"], fp8=True)
+    yg = M.gdn_mixer(parent, seg_len, x, Wt["gdn"], fp8=True)
+    start = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
+    for leaf in [s for s in range(len(parent)) if not (parent == s).any()]:
+        rows = np.concatenate([np.arange(start[s], start[s] + seg_len[s]) for s in path_segments(parent, leaf)])
+        one = (np.array([-1], np.int32), np.array([len(rows)], np.int32))
+        assert np.allclose(ya[rows], M.attention_mixer(*one, x[rows], Wt["attn"], fp8=True), rtol=1e-9, atol=1e-9)
+        assert np.allclose(yg[rows], M.gdn_mixer(*one, x[rows], Wt["gdn"], fp8=True), rtol=1e-9, atol=1e-9)

@@ -27,6 +27,7 @@ EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_bui
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "fork_linear_forward",
+           "fork_quantize_fp8", "fork_linear_fp8_forward",
            "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
 
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
             "gdn_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                    f32, i32, vp],
             "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, i32, vp],
+            "fork_quantize_fp8": [vp, vp, vp, ctypes.c_int64, i32, i32, vp],
+            "fork_linear_fp8_forward": [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
             "fork_graph_create": [P(fork_meta), P(fork_graph_args), vp, P(vp)],
             "fork_graph_launch": [vp, vp],
             "fork_graph_destroy": [vp],
@@ -283,6 +286,16 @@ def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H:
 
 def fork_linear_forward(x, w, y, M: int, N: int, K: int, accumulate: int, dt: int, stream=None) -> None:
     _check(lib().fork_linear_forward(_ptr(x), _ptr(w), _ptr(y), M, N, K, accumulate, dt, _stream(stream)))
+
+
+def fork_quantize_fp8(x, q, scales, rows: int, K: int, dt: int, stream=None) -> None:
+    _check(lib().fork_quantize_fp8(_ptr(x), _ptr(q), _ptr(scales), rows, K, dt, _stream(stream)))
+
+
+def fork_linear_fp8_forward(xq, x_scale, wq, w_scale, y, M: int, N: int, K: int, accumulate: int,
+                            stream=None) -> None:
+    _check(lib().fork_linear_fp8_forward(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(y), M, N, K,
+                                         accumulate, _stream(stream)))
 
 
 def fork_graph_create(meta: fork_meta, args: fork_graph_args, stream=None) -> int:

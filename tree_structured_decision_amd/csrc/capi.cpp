@@ -612,4 +612,26 @@ fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M
   return launch_linear(x, w, y, M, N, K, accumulate, dt, (hipStream_t)stream);
 }
 
+fork_status fork_quantize_fp8(const void* x, void* q, float* scales, int64_t rows, int32_t K, fork_dtype dt,
+                              void* stream) {
+  g_err[0] = 0;
+  if (!x || !q || !scales) return fail(FORK_E_ARG, "x, q and scales must be non-null");
+  if (rows < 1) return fail(FORK_E_ARG, "rows=%lld", (long long)rows);
+  if (K < 8 || K % 8) return fail(FORK_E_UNSUPPORTED, "row length %d (a positive multiple of 8)", K);
+  if ((uintptr_t)x % 16 || (uintptr_t)q % 8) return fail(FORK_E_ARG, "x must be 16-byte and q 8-byte aligned");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_quantize_fp8(x, q, scales, (long long)rows, K, dt, (hipStream_t)stream);
+}
+
+fork_status fork_linear_fp8_forward(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                                    void* y, int32_t M, int32_t N, int32_t K, int32_t accumulate, void* stream) {
+  g_err[0] = 0;
+  if (!xq || !x_scale || !wq || !w_scale || !y) return fail(FORK_E_ARG, "every pointer must be non-null");
+  if (M < 1 || N < 1 || K < 1) return fail(FORK_E_ARG, "M=%d N=%d K=%d", M, N, K);
+  if (K % 16) return fail(FORK_E_UNSUPPORTED, "K=%d (fp8 products need a multiple of 16)", K);
+  if (y == xq || y == wq) return fail(FORK_E_ARG, "y must not overlap xq or wq");
+  if (accumulate != 0 && accumulate != 1) return fail(FORK_E_ARG, "accumulate %d (0 or 1)", accumulate);
+  return launch_linear_fp8(xq, x_scale, wq, w_scale, y, M, N, K, accumulate, (hipStream_t)stream);
+}
+
 }  // extern "C"

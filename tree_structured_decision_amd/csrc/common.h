@@ -175,6 +175,10 @@ fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab,
                               int dv, float eps, fork_dtype dt, hipStream_t stream);
 fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, int accumulate,
                           fork_dtype dt, hipStream_t stream);
+fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long rows, int K, fork_dtype dt,
+                                hipStream_t stream);
+fork_status launch_linear_fp8(const void* xq, const float* x_scale, const void* wq, const float* w_scale, void* y,
+                              int M, int N, int K, int accumulate, hipStream_t stream);
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);
 fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const void* v,
                        const float* a, const float* b, const float* root_state, void* o,

@@ -6,6 +6,13 @@
 // i.e. D (N x M, ld N) = op(A) B with A = w stored K x N (ld K) and
 // transposed, B = x stored K x M (ld K).
 //
+// FP8 projections take E4M3 operands with one fp32 scale per row of each
+// operand (per token of x, per output channel of w; device vectors, so
+// scales computed on the GPU are used without a host round trip) and write
+// bf16: y[m][n] = (sum_k xq[m][k] wq[n][k]) * x_scale[m] * w_scale[n]. In
+// hipBLASLt's terms these are the outer-vector scales of A (w, N entries)
+// and B (x, M entries).
+//
 // Per device: one hipBLASLt handle and one workspace, created at the first
 // call; per (M, N, K, dtype): the descriptors and the heuristic's first
 // algorithm, kept for the life of the process.
@@ -45,14 +52,24 @@ LtDevice g_lt[kMaxDevices];
     if (s_ != HIPBLAS_STATUS_SUCCESS) return fail(FORK_E_HIP, "%s: hipblasLt status %d", #expr, (int)s_); \
   } while (0)
 
-fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, LtPlan& p) {
+// ty: the input type; the output has type oty. fp8 inputs carry per-tensor
+// scale pointers (set on the descriptor before each product).
+fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, hipDataType oty, LtPlan& p,
+                      const float* a_scale = nullptr, const float* b_scale = nullptr) {
   LT_CHECK(hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
   const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
   LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)));
   LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)));
   LT_CHECK(hipblasLtMatrixLayoutCreate(&p.la, ty, K, N, K));
   LT_CHECK(hipblasLtMatrixLayoutCreate(&p.lb, ty, K, M, K));
-  LT_CHECK(hipblasLtMatrixLayoutCreate(&p.lc, ty, N, M, N));
+  LT_CHECK(hipblasLtMatrixLayoutCreate(&p.lc, oty, N, M, N));
+  if (a_scale) {
+    const hipblasLtMatmulMatrixScale_t vec = HIPBLASLT_MATMUL_MATRIX_SCALE_OUTER_VEC_32F;
+    LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_A_SCALE_MODE, &vec, sizeof(vec)));
+    LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_B_SCALE_MODE, &vec, sizeof(vec)));
+    LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_A_SCALE_POINTER, &a_scale, sizeof(a_scale)));
+    LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_B_SCALE_POINTER, &b_scale, sizeof(b_scale)));
+  }
   hipblasLtMatmulPreference_t pref;
   LT_CHECK(hipblasLtMatmulPreferenceCreate(&pref));
   const uint64_t wsmax = kLtWorkspace;
@@ -69,30 +86,65 @@ fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, LtPlan& 
   return FORK_OK;
 }
 
-}  // namespace
-
-fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, int accumulate,
-                          fork_dtype dt, hipStream_t stream) {
+fork_status device_state(LtDevice** out) {
   int dev = 0;
   FORK_HIP_CHECK(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) return fail(FORK_E_UNSUPPORTED, "device %d", dev);
-  std::lock_guard<std::mutex> lk(g_lt_mu);
   LtDevice& d = g_lt[dev];
   if (!d.h) {
     LT_CHECK(hipblasLtCreate(&d.h));
     FORK_HIP_CHECK(hipMalloc(&d.ws, kLtWorkspace));
   }
+  *out = &d;
+  return FORK_OK;
+}
+
+}  // namespace
+
+fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, int K, int accumulate,
+                          fork_dtype dt, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_lt_mu);
+  LtDevice* dp = nullptr;
+  fork_status st = device_state(&dp);
+  if (st) return st;
+  LtDevice& d = *dp;
   const auto key = std::make_tuple(M, N, K, (int)dt);
   auto it = d.plans.find(key);
   if (it == d.plans.end()) {
     LtPlan p;
-    const fork_status st = make_plan(d, M, N, K, dt == FORK_BF16 ? HIP_R_16BF : HIP_R_32F, p);
+    const hipDataType ty = dt == FORK_BF16 ? HIP_R_16BF : HIP_R_32F;
+    st = make_plan(d, M, N, K, ty, ty, p);
     if (st) return st;
     it = d.plans.emplace(key, p).first;
   }
   const LtPlan& p = it->second;
   const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
   LT_CHECK(hipblasLtMatmul(d.h, p.desc, &alpha, w, p.la, x, p.lb, &beta, y, p.lc, y, p.lc, &p.algo, d.ws, p.ws,
+                           stream));
+  return FORK_OK;
+}
+
+fork_status launch_linear_fp8(const void* xq, const float* x_scale, const void* wq, const float* w_scale, void* y,
+                              int M, int N, int K, int accumulate, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_lt_mu);
+  LtDevice* dp = nullptr;
+  fork_status st = device_state(&dp);
+  if (st) return st;
+  LtDevice& d = *dp;
+  const auto key = std::make_tuple(M, N, K, 8);
+  auto it = d.plans.find(key);
+  if (it == d.plans.end()) {
+    LtPlan p;
+    st = make_plan(d, M, N, K, HIP_R_8F_E4M3, HIP_R_16BF, p, w_scale, x_scale);
+    if (st) return st;
+    it = d.plans.emplace(key, p).first;
+  }
+  const LtPlan& p = it->second;
+  // A is w, B is x in the column-major terms above
+  LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_A_SCALE_POINTER, &w_scale, sizeof(w_scale)));
+  LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_B_SCALE_POINTER, &x_scale, sizeof(x_scale)));
+  const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
+  LT_CHECK(hipblasLtMatmul(d.h, p.desc, &alpha, wq, p.la, xq, p.lb, &beta, y, p.lc, y, p.lc, &p.algo, d.ws, p.ws,
                            stream));
   return FORK_OK;
 }

@@ -8,7 +8,8 @@
 //     rmsnorm(o) * w * silu(z), and the plain RMS norm in front of a mixer;
 //   - the Gated DeltaNet inputs after the short convolution: L2-normalised
 //     query and key heads, the value heads, and the per-head decay and
-//     write strength from their projections.
+//     write strength from their projections;
+//   - row-wise FP8 (E4M3) quantisation of the projections' operands.
 // The pages describe the layers, not these surroundings; the forms follow the
 // published Gated DeltaNet layer (Yang, Kautz, Hatamizadeh, "Gated Delta
 // Networks", 2024) and sigmoid output gating of attention.
@@ -193,6 +194,52 @@ __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
   }
 }
 
+// ------------------------------------------------------------ FP8 (E4M3)
+// Row-wise quantisation to the OCP FP8 E4M3 format (bias 7, 3 mantissa bits,
+// largest finite 448): for each row of K values, scale = amax / 448 (1 for an
+// all-zero row) and code = RNE_e4m3(clamp(x / scale, -448, 448)), both
+// divisions correctly rounded fp32, the conversion the hardware's
+// nearest-even one. A row is one token (activations) or one output channel
+// (weights), so a token's codes depend on that token alone: quantising the
+// flattened stream gives every branch what its isolated pass would get.
+template <bool BF16>
+__global__ void __launch_bounds__(kMixThreads) quant_rows_kernel(const void* x, unsigned char* __restrict__ q,
+                                                                 float* __restrict__ scales, long long rows, int K,
+                                                                 int L) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L, nc = K / 8;
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
+  for (long long r0 = wave * rpw; r0 < rows; r0 += nwaves * rpw) {  // uniform over the wave
+    const long long r = r0 + lane / L;
+    const bool live = r < rows;
+    const size_t base = (size_t)r * K;
+    float m = 0.f;
+    if (live)
+      for (int j = li; j < nc; j += L) {
+        float v[8];
+        load8<BF16>(x, base + 8 * j, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+      }
+    for (int o = L >> 1; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (!live) continue;
+    const float scale = m > 0.f ? m / 448.f : 1.f;
+    if (li == 0) scales[r] = scale;
+    for (int j = li; j < nc; j += L) {
+      float v[8];
+      load8<BF16>(x, base + 8 * j, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] / scale, -448.f), 448.f);
+      unsigned lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+      unsigned hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+      *(u32x2_t*)(q + base + 8 * j) = u32x2_t{lo, hi};
+    }
+  }
+}
+
 // Lanes per row: the largest power of two <= min(64, D / 8).
 int lanes_per_row(int D) {
   int L = 1;
@@ -229,6 +276,20 @@ fork_status launch_gate(const fork_meta* m, const void* x, const void* g, const 
                         int mode, float eps, fork_dtype dt, hipStream_t stream) {
   if (dt == FORK_BF16) return launch_gate_t<true>(m, x, g, w, y, nh, D, mode, eps, stream);
   return launch_gate_t<false>(m, x, g, w, y, nh, D, mode, eps, stream);
+}
+
+fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long rows, int K, fork_dtype dt,
+                                hipStream_t stream) {
+  const int L = lanes_per_row(K);
+  const int grid = row_grid(rows, L);
+  if (dt == FORK_BF16)
+    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(grid), dim3(kMixThreads), 0, stream, x, (unsigned char*)q, scales,
+                       rows, K, L);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, x, (unsigned char*)q,
+                       scales, rows, K, L);
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
 }
 
 fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, const float* a_log,

@@ -127,34 +127,83 @@ class ForkSession:
         dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
         B.fork_linear_forward(x, w, y, M, N, K, int(accumulate), dt, stream=stream)
 
+    # -- FP8 ----------------------------------------------------------------
+    def quantize_fp8(self, x, q=None, scale=None, stream=None):
+        """Row-wise E4M3 quantisation on the GPU of x [rows, K]: returns (codes uint8
+        of x's shape, scales [rows] fp32 on the device)."""
+        rows, K = x.shape
+        if q is None:
+            q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if scale is None or scale.numel() != rows:
+            scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_quantize_fp8(x, q, scale, rows, K, dt, stream=stream)
+        return q, scale
+
+    @staticmethod
+    def linear_fp8(xq, x_scale, wq, w_scale, y, stream=None, accumulate: bool = False):
+        """y [M, N] bf16 = (xq [M, K] wq [N, K]^T) scaled by x_scale [M] and w_scale [N]
+        (E4M3 codes with row scales)."""
+        M, K = xq.shape
+        N = wq.shape[0]
+        B.fork_linear_fp8_forward(xq, x_scale, wq, w_scale, y, M, N, K, int(accumulate), stream=stream)
+
+    def quantize_weights(self, W: dict, stream=None) -> dict:
+        """A copy of mixer weights W with every projection (2-D "w*" entry) replaced
+        by its (codes, scale) pair: the weights of an FP8 mixer."""
+        out = {}
+        for n, v in W.items():
+            if n.startswith("w") and isinstance(v, torch.Tensor) and v.dim() == 2:
+                out[n] = self.quantize_fp8(v, stream=stream)
+            else:
+                out[n] = v
+        return out
+
+    def _proj(self, fp8, xin, name, W, y, stream, accumulate=False):
+        """One projection of a mixer: bf16/fp32, or FP8 with xin = (codes, scale)."""
+        if fp8:
+            wq, ws = W[name]
+            self.linear_fp8(xin[0], xin[1], wq, ws, y, stream, accumulate)
+        else:
+            self.linear(xin, W[name], y, stream, accumulate)
+
+    def _proj_in(self, fp8, x, b, key, stream):
+        if not fp8:
+            return x
+        q = b.get(key + "_q")
+        if q is None or q.shape != x.shape:
+            q = None
+        return self.quantize_fp8(x, q, b.get(key + "_s"), stream)
+
     def attention_mixer(self, x, W: dict, theta: float = 10000.0, stream=None, bufs: dict = None,
-                        residual=None):
+                        residual=None, fp8: bool = False):
         """Attention mixer of a hybrid block on the current tree: projections, rotary
         embedding at the isolated positions, tree attention, sigmoid output gate,
         output projection. x [T, dm]; W holds device tensors wq, wk, wv, wg, wo and
         the ints H, Hkv, D. Returns y [T, dm], or with residual [T, dm] adds y into it
         (inside the output projection) and returns it. bufs: optional dict reused
-        across calls for the intermediates."""
+        across calls for the intermediates. fp8: W from quantize_weights; the
+        projections' inputs are quantised per token on the GPU."""
         T, dm = x.shape
         H, Hkv, D = W["H"], W["Hkv"], W["D"]
         b = self._bufs(bufs, x, dict(q=(T, H, D), k=(T, Hkv, D), v=(T, Hkv, D), g=(T, H, D),
                                      o=(T, H, D), u=(T, H, D), y=(T, dm)))
-        self.linear(x, W["wq"], b["q"], stream)
-        self.linear(x, W["wk"], b["k"], stream)
-        self.linear(x, W["wv"], b["v"], stream)
-        self.linear(x, W["wg"], b["g"], stream)
+        xin = self._proj_in(fp8, x, b, "x", stream)
+        for n in ("q", "k", "v", "g"):
+            self._proj(fp8, xin, "w" + n, W, b[n], stream)
         self.rope(b["q"], theta, stream)
         self.rope(b["k"], theta, stream)
         self.attention(b["q"], b["k"], b["v"], b["o"], stream=stream)
         self.gate(b["o"], b["g"], None, b["u"], 0, stream=stream)
-        if residual is not None:
-            self.linear(b["u"].view(T, H * D), W["wo"], residual, stream, accumulate=True)
-            return residual
-        self.linear(b["u"].view(T, H * D), W["wo"], b["y"], stream)
-        return b["y"]
+        uin = self._proj_in(fp8, b["u"].view(T, H * D), b, "u", stream)
+        if fp8:
+            b["x_q"], b["x_s"], b["u_q"], b["u_s"] = xin[0], xin[1], uin[0], uin[1]
+        out = b["y"] if residual is None else residual
+        self._proj(fp8, uin, "wo", W, out, stream, accumulate=residual is not None)
+        return out
 
     def gdn_mixer(self, x, W: dict, eps: float = 1e-6, stream=None, bufs: dict = None,
-                  seg_start_state=None, residual=None):
+                  seg_start_state=None, residual=None, fp8: bool = False):
         """Gated DeltaNet mixer of a hybrid block on the current tree: projections,
         causal convolution along the isolated sequences (+ SiLU), normalised inputs and
         gates, forked Gated DeltaNet, gated RMS norm, output projection. x [T, dm]; W
@@ -176,26 +225,29 @@ class ForkSession:
             if "st" not in b or b["st"].shape[0] < S:
                 b["st"] = torch.empty((S, H, dv, dk), dtype=torch.float32, device=x.device)
             st = b["st"]
-        self.linear(x, W["wqkv"], b["p"], stream)
-        self.linear(x, W["wab"], b["ab"], stream)
-        self.linear(x, W["wz"], b["z"].view(T, H * dv), stream)
+        xin = self._proj_in(fp8, x, b, "x", stream)
+        self._proj(fp8, xin, "wqkv", W, b["p"], stream)
+        self._proj(fp8, xin, "wab", W, b["ab"], stream)
+        self._proj(fp8, xin, "wz", W, b["z"].view(T, H * dv), stream)
         self.conv(b["p"], W["conv_w"], b["c"], act=1, stream=stream)
         self.gdn_inputs(b["c"], b["ab"], W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"],
                         b["b"], eps, stream)
         self.gdn(b["q"], b["k"], b["v"], b["a"], b["b"], b["o"], st, scale=dk ** -0.5, stream=stream)
         self.gate(b["o"], b["z"], W["norm_w"], b["u"], 1, eps, stream)
-        if residual is not None:
-            self.linear(b["u"].view(T, H * dv), W["wo"], residual, stream, accumulate=True)
-            return residual
-        self.linear(b["u"].view(T, H * dv), W["wo"], b["y"], stream)
-        return b["y"]
+        uin = self._proj_in(fp8, b["u"].view(T, H * dv), b, "u", stream)
+        if fp8:
+            b["x_q"], b["x_s"], b["u_q"], b["u_s"] = xin[0], xin[1], uin[0], uin[1]
+        out = b["y"] if residual is None else residual
+        self._proj(fp8, uin, "wo", W, out, stream, accumulate=residual is not None)
+        return out
 
     def stack(self, x, layers, final_norm, theta: float = 10000.0, eps: float = 1e-6,
-              stream=None, bufs: dict = None):
+              stream=None, bufs: dict = None, fp8: bool = False):
         """Pre-norm residual stack on the current tree, in place on x [T, dm]:
         x <- x + mixer(rmsnorm(x) w_l) for each (kind, weights, norm weight) in
         layers (kind "attn" or "gdn"; the add happens in the output projection),
-        then returns h = rmsnorm(x) w_final."""
+        then returns h = rmsnorm(x) w_final. fp8: layers' weights from
+        quantize_weights, projections in FP8."""
         T, dm = x.shape
         b = self._bufs(bufs, x, dict(hn=(T, 1, dm), h=(T, 1, dm)))
         b.setdefault("mixers", {})
@@ -203,9 +255,9 @@ class ForkSession:
             mb = b["mixers"].setdefault(i, {})
             self.gate(x.view(T, 1, dm), None, nw, b["hn"], 2, eps, stream)
             if kind == "attn":
-                self.attention_mixer(b["hn"].view(T, dm), W, theta, stream, mb, residual=x)
+                self.attention_mixer(b["hn"].view(T, dm), W, theta, stream, mb, residual=x, fp8=fp8)
             else:
-                self.gdn_mixer(b["hn"].view(T, dm), W, eps, stream, mb, residual=x)
+                self.gdn_mixer(b["hn"].view(T, dm), W, eps, stream, mb, residual=x, fp8=fp8)
         self.gate(x.view(T, 1, dm), None, final_norm, b["h"], 2, eps, stream)
         return b["h"].view(T, dm)
 
