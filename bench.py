@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "branch tokens/s for ForkAttention + GDN fork layer; % of HBM/MFMA roofline"
 PEAK_BF16_MFMA = 2.5e15      # dense, FLOP/s
+PEAK_FP8_MFMA = 5.0e15
 PEAK_F32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12            # B/s
 SEED_MIXER = 2048             # seed of the mixer weights and input
@@ -360,13 +361,15 @@ def cpu_stack_fidelity(wl, stack_inputs):
     from oracle import mixer as OM
     from tree_structured_decision_amd import metrics
 
-    h_gpu, x0, layers, fn, w_head = stack_inputs
+    h_gpu, h8_gpu, x0, layers, fn, w_head = stack_inputs
     t0 = time.perf_counter()
     ref = OM.stack(wl.parent, wl.seg_len, x0, layers, fn, prec="f32")
     fid = metrics.decision_fidelity(h_gpu, ref, w_head, wl.parent, wl.seg_len)
     fid["reference"] = "float32 oracle (unrounded intermediates)"
     fid["oracle_s"] = time.perf_counter() - t0
-    return fid
+    fid8 = metrics.decision_fidelity(h8_gpu, ref, w_head, wl.parent, wl.seg_len)
+    fid8["reference"] = "float32 oracle without quantisation (the cost of FP8 projections)"
+    return fid, fid8
 
 
 def main():
@@ -508,7 +511,7 @@ def main():
     out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
     st, st_inputs = stack_ops(wl, r.sess)
     if not args.no_cpu:
-        st["fidelity"] = cpu_stack_fidelity(wl, st_inputs)
+        st["fidelity"], st["fp8_fidelity"] = cpu_stack_fidelity(wl, st_inputs)
     out["stack"] = {"one_request": st}
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
@@ -606,8 +609,33 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     k, v = torch.empty_like(q), torch.empty(T, wl.gH, wl.dv, dtype=torch.bfloat16, device="cuda")
     aa = torch.empty(T, wl.gH, device="cuda")
     bb = torch.empty_like(aa)
+    # FP8: weights quantised per output channel once; activations per token inside
+    A8, G8 = sess.quantize_weights(A), sess.quantize_weights(G)
+    ab8, gb8, outs8 = {}, {}, {}
+    xq, xs = sess.quantize_fp8(x)
+    proj8 = [(A8["wq"], "q"), (A8["wk"], "k"), (A8["wv"], "v"), (A8["wg"], "g"),
+             (G8["wqkv"], "p"), (G8["wab"], "ab"), (G8["wz"], "z")]
+
+    def projections_fp8():
+        for (wq_, ws_), n in proj8:
+            if n not in outs8:
+                outs8[n] = torch.empty(T, wq_.shape[0], dtype=torch.bfloat16, device="cuda")
+            sess.linear_fp8(xq, xs, wq_, ws_, outs8[n])
+        if "u" not in outs8:
+            outs8["u"] = sess.quantize_fp8(torch.randn(T, wl.H * wl.D, device="cuda").to(torch.bfloat16))
+            outs8["ug"] = sess.quantize_fp8(torch.randn(T, wl.gH * wl.dv, device="cuda").to(torch.bfloat16))
+            outs8["y"] = torch.empty(T, dm, dtype=torch.bfloat16, device="cuda")
+        sess.linear_fp8(*outs8["u"], *A8["wo"], outs8["y"])
+        sess.linear_fp8(*outs8["ug"], *G8["wo"], outs8["y"])
+
+    xq_buf = torch.empty(T, dm, dtype=torch.uint8, device="cuda")
+    xs_buf = torch.empty(T, device="cuda")
     ops = {
         "attention_mixer": (lambda: sess.attention_mixer(x, A, bufs=ab), None, None),
+        "attention_mixer_fp8": (lambda: sess.attention_mixer(x, A8, bufs=ab8, fp8=True), None, None),
+        "gdn_mixer_fp8": (lambda: sess.gdn_mixer(x, G8, bufs=gb8, fp8=True), None, None),
+        "projections_fp8": (projections_fp8, "mfma8", flop),
+        "quantize_fp8": (lambda: sess.quantize_fp8(x, xq_buf, xs_buf), "hbm", x.numel() * 3.0 + T * 4),
         "gdn_mixer": (lambda: sess.gdn_mixer(x, G, bufs=gb), None, None),
         "projections": (projections, "mfma", flop),
         "gate_sigmoid": (lambda: sess.gate(o, g, None, u, 0), "hbm", 3.0 * o.numel() * 2),
@@ -630,15 +658,22 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
         r = dict(us=t * 1e6)
         if bound == "mfma":
             r.update(algorithmic_flop=work, achieved_tflops=work / t / 1e12, mfma_frac=work / t / PEAK_BF16_MFMA)
+        elif bound == "mfma8":
+            r.update(algorithmic_flop=work, achieved_tflops=work / t / 1e12, mfma_frac=work / t / PEAK_FP8_MFMA)
         elif bound == "hbm":
             r.update(algorithmic_bytes=work, achieved_gbs=work / t / 1e9, hbm_frac=work / t / PEAK_HBM)
         rep[name] = r
     pair = rep["attention_mixer"]["us"] + rep["gdn_mixer"]["us"]
     rep["mixer_pair_us"] = pair
     rep["mixer_pair_tokens_per_s"] = T / (pair * 1e-6)
+    pair8 = rep["attention_mixer_fp8"]["us"] + rep["gdn_mixer_fp8"]["us"]
+    rep["mixer_pair_fp8_us"] = pair8
+    rep["mixer_pair_fp8_tokens_per_s"] = T / (pair8 * 1e-6)
     rep["note"] = (f"model width {dm}; attention 16 q / 2 kv heads x 128, Gated DeltaNet 16 heads x 128, "
                    "convolution width 4; random bf16 weights; projections = the 9 GEMMs of both "
-                   "mixers (hipBLASLt, fp32 accumulation)")
+                   "mixers (hipBLASLt, fp32 accumulation); *_fp8: E4M3 projections with per-token "
+                   "activation and per-channel weight scales (quantisation inside the mixers, "
+                   "against the fp8 MFMA peak)")
     return rep
 
 
@@ -670,28 +705,33 @@ def stack_ops(wl, sess, iters=10, dm=2048):
     x0 = W.mixer_input(SEED_MIXER + 20, T, dm)
     x0d = dev(x0, True)
     x = torch.empty_like(x0d)
-    bufs = {}
+    dl8 = [(k, sess.quantize_weights(Wl), nw) for k, Wl, nw in dl]
 
-    def once():
-        x.copy_(x0d)
-        return sess.stack(x, dl, dfn, bufs=bufs)
+    def timed(fp8):
+        bufs = {}
 
-    for _ in range(2):
-        once()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(iters):
-        h = once()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / iters
+        def once():
+            x.copy_(x0d)
+            return sess.stack(x, dl8 if fp8 else dl, dfn, bufs=bufs, fp8=fp8)
+
+        for _ in range(2):
+            once()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            h = once()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters, h.float().cpu().numpy().astype(np.float64)
+
+    t, h_gpu = timed(False)
+    t8, h8_gpu = timed(True)
     rep = dict(layers=[k for k, _, _ in layers], model_width=dm, us=t * 1e6, tokens_per_s=T / t,
-               fidelity=None)
+               fp8_us=t8 * 1e6, fp8_tokens_per_s=T / t8, fidelity=None, fp8_fidelity=None)
     rep["note"] = ("pre-norm residual stack; the residual add happens in the output projections; "
                    "each pass includes a copy of the input into the residual stream")
-    h_gpu = h.float().cpu().numpy().astype(np.float64)
-    return rep, (h_gpu, x0, layers, fn, w_head)
+    return rep, (h_gpu, h8_gpu, x0, layers, fn, w_head)
 
 
 def calib_copy(enabled: bool):

@@ -297,8 +297,10 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
  * flattened stream: one call projects every branch, the shared prefix once.
  * y must not overlap x or w.
  * The first call on a device creates a hipBLASLt handle and a 32 MiB
- * workspace, kept for the process; the first call per (M, N, K, dt) picks the
- * algorithm and keeps it. Calls are serialised by a lock. */
+ * workspace, kept for the process. The first call per (M, N, K, dt) times
+ * the heuristic's candidate algorithms once on its operands (into a scratch
+ * output it allocates and frees; it synchronises the stream) and keeps the
+ * fastest. Calls are serialised by a lock. */
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
                                 int32_t accumulate, fork_dtype dt, void* stream);
 

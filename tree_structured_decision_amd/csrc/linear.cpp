@@ -14,8 +14,10 @@
 // and B (x, M entries).
 //
 // Per device: one hipBLASLt handle and one workspace, created at the first
-// call; per (M, N, K, dtype): the descriptors and the heuristic's first
-// algorithm, kept for the life of the process.
+// call; per (M, N, K, dtype): the descriptors and an algorithm, kept for the
+// life of the process. The algorithm is the fastest of the heuristic's
+// candidates, each timed once at that first call on the caller's operands
+// (into a scratch output; the call synchronises the stream then).
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
@@ -54,8 +56,16 @@ LtDevice g_lt[kMaxDevices];
 
 // ty: the input type; the output has type oty. fp8 inputs carry per-tensor
 // scale pointers (set on the descriptor before each product).
+struct TuneArgs {
+  const void* x;
+  const void* w;
+};
+constexpr int kCandidates = 16;
+constexpr int kTuneReps = 5;
+
 fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, hipDataType oty, LtPlan& p,
-                      const float* a_scale = nullptr, const float* b_scale = nullptr) {
+                      const TuneArgs* tune, hipStream_t stream, const float* a_scale = nullptr,
+                      const float* b_scale = nullptr) {
   LT_CHECK(hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
   const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
   LT_CHECK(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)));
@@ -75,14 +85,49 @@ fork_status make_plan(LtDevice& d, int M, int N, int K, hipDataType ty, hipDataT
   const uint64_t wsmax = kLtWorkspace;
   LT_CHECK(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax,
                                                  sizeof(wsmax)));
-  hipblasLtMatmulHeuristicResult_t res[1];
+  hipblasLtMatmulHeuristicResult_t res[kCandidates];
   int n = 0;
-  const hipblasStatus_t hs = hipblasLtMatmulAlgoGetHeuristic(d.h, p.desc, p.la, p.lb, p.lc, p.lc, pref, 1, res, &n);
+  const hipblasStatus_t hs =
+      hipblasLtMatmulAlgoGetHeuristic(d.h, p.desc, p.la, p.lb, p.lc, p.lc, pref, kCandidates, res, &n);
   hipblasLtMatmulPreferenceDestroy(pref);
   if (hs != HIPBLAS_STATUS_SUCCESS || n < 1)
     return fail(FORK_E_UNSUPPORTED, "hipblasLt has no algorithm for M=%d N=%d K=%d (status %d)", M, N, K, (int)hs);
   p.algo = res[0].algo;
   p.ws = res[0].workspaceSize;
+  if (n == 1 || !tune) return FORK_OK;
+  // time the candidates once on the caller's operands (into a scratch output,
+  // so the caller's y is untouched) and keep the fastest
+  void* tmp = nullptr;
+  const size_t ybytes = (size_t)M * N * (oty == HIP_R_32F ? 4 : 2);
+  FORK_HIP_CHECK(hipMalloc(&tmp, ybytes));
+  hipEvent_t e0, e1;
+  FORK_HIP_CHECK(hipEventCreate(&e0));
+  FORK_HIP_CHECK(hipEventCreate(&e1));
+  const float alpha = 1.f, beta = 0.f;
+  float best = 1e30f;
+  for (int i = 0; i < n; ++i) {
+    if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > kLtWorkspace) continue;
+    bool ok = true;
+    for (int r = 0; r < 2 + kTuneReps && ok; ++r) {
+      if (r == 2) hipEventRecord(e0, stream);
+      ok = hipblasLtMatmul(d.h, p.desc, &alpha, tune->w, p.la, tune->x, p.lb, &beta, tmp, p.lc, tmp, p.lc,
+                           &res[i].algo, d.ws, res[i].workspaceSize, stream) == HIPBLAS_STATUS_SUCCESS;
+    }
+    if (!ok) continue;
+    hipEventRecord(e1, stream);
+    hipEventSynchronize(e1);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, e0, e1);
+    if (ms < best) {
+      best = ms;
+      p.algo = res[i].algo;
+      p.ws = res[i].workspaceSize;
+    }
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  FORK_HIP_CHECK(hipStreamSynchronize(stream));
+  FORK_HIP_CHECK(hipFree(tmp));
   return FORK_OK;
 }
 
@@ -113,7 +158,8 @@ fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, i
   if (it == d.plans.end()) {
     LtPlan p;
     const hipDataType ty = dt == FORK_BF16 ? HIP_R_16BF : HIP_R_32F;
-    st = make_plan(d, M, N, K, ty, ty, p);
+    const TuneArgs ta{x, w};
+    st = make_plan(d, M, N, K, ty, ty, p, &ta, stream);
     if (st) return st;
     it = d.plans.emplace(key, p).first;
   }
@@ -135,7 +181,8 @@ fork_status launch_linear_fp8(const void* xq, const float* x_scale, const void* 
   auto it = d.plans.find(key);
   if (it == d.plans.end()) {
     LtPlan p;
-    st = make_plan(d, M, N, K, HIP_R_8F_E4M3, HIP_R_16BF, p, w_scale, x_scale);
+    const TuneArgs ta{xq, wq};
+    st = make_plan(d, M, N, K, HIP_R_8F_E4M3, HIP_R_16BF, p, &ta, stream, w_scale, x_scale);
     if (st) return st;
     it = d.plans.emplace(key, p).first;
   }
