@@ -379,6 +379,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-workloads", action="store_true", help="headline workload only")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the block-piece, mixer and stack legs (kernel profiles of the step)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache and measured-peak passes (counter runs of the warm step)")
     ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
@@ -507,12 +509,13 @@ def main():
                  "the Infinity Cache"),
         "measured_peaks": peaks,
     }
-    out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
-    out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
-    st, st_inputs = stack_ops(wl, r.sess)
-    if not args.no_cpu:
-        st["fidelity"], st["fp8_fidelity"] = cpu_stack_fidelity(wl, st_inputs)
-    out["stack"] = {"one_request": st}
+    if not args.no_extras:
+        out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
+        out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
+        st, st_inputs = stack_ops(wl, r.sess)
+        if not args.no_cpu:
+            st["fidelity"], st["fp8_fidelity"] = cpu_stack_fidelity(wl, st_inputs)
+        out["stack"] = {"one_request": st}
     if not args.no_workloads:
         out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
     print(json.dumps(out), flush=True)
