@@ -577,14 +577,14 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     T = wl.T
     Wt = W.mixer_weights(SEED_MIXER, dm, H=wl.H, Hkv=wl.Hkv, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv)
     dev = lambda a, dt=torch.bfloat16: torch.from_numpy(a).to("cuda", dt)
-    A = {n: (dev(v) if isinstance(v, np.ndarray) else v) for n, v in Wt["attn"].items()}
+    A = sess.fuse_attention_weights({n: (dev(v) if isinstance(v, np.ndarray) else v)
+                                     for n, v in Wt["attn"].items()})
     G = {n: (dev(v) if isinstance(v, np.ndarray) and n.startswith("w") else
              dev(v, torch.float32) if isinstance(v, np.ndarray) else v) for n, v in Wt["gdn"].items()}
     x = dev(W.mixer_input(SEED_MIXER + 1, T, dm))
     ab, gb = {}, {}
     C = 2 * wl.gH * wl.dk + wl.gH * wl.dv
-    proj = [(A["wq"], "q"), (A["wk"], "k"), (A["wv"], "v"), (A["wg"], "g"),
-            (G["wqkv"], "p"), (G["wab"], "ab"), (G["wz"], "z")]
+    proj = [(A["wqkvg"], "f"), (G["wqkv"], "p"), (G["wab"], "ab"), (G["wz"], "z")]
     outs = {}
 
     def projections():
@@ -616,8 +616,7 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     A8, G8 = sess.quantize_weights(A), sess.quantize_weights(G)
     ab8, gb8, outs8 = {}, {}, {}
     xq, xs = sess.quantize_fp8(x)
-    proj8 = [(A8["wq"], "q"), (A8["wk"], "k"), (A8["wv"], "v"), (A8["wg"], "g"),
-             (G8["wqkv"], "p"), (G8["wab"], "ab"), (G8["wz"], "z")]
+    proj8 = [(A8["wqkvg"], "f"), (G8["wqkv"], "p"), (G8["wab"], "ab"), (G8["wz"], "z")]
 
     def projections_fp8():
         for (wq_, ws_), n in proj8:
@@ -673,8 +672,10 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     rep["mixer_pair_fp8_us"] = pair8
     rep["mixer_pair_fp8_tokens_per_s"] = T / (pair8 * 1e-6)
     rep["note"] = (f"model width {dm}; attention 16 q / 2 kv heads x 128, Gated DeltaNet 16 heads x 128, "
-                   "convolution width 4; random bf16 weights; projections = the 9 GEMMs of both "
-                   "mixers (hipBLASLt, fp32 accumulation); *_fp8: E4M3 projections with per-token "
+                   "convolution width 4; random bf16 weights; projections = the 6 GEMMs of both "
+                   "mixers (hipBLASLt, fp32 accumulation; the attention mixer's q | k | v | gate "
+                   "projections run as one product whose output is split into heads by the rotary "
+                   "kernel); *_fp8: E4M3 projections with per-token "
                    "activation and per-channel weight scales (quantisation inside the mixers, "
                    "against the fp8 MFMA peak)")
     return rep
@@ -702,8 +703,11 @@ def stack_ops(wl, sess, iters=10, dm=2048):
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(
             "cuda", torch.bfloat16 if bf else torch.float32)
 
-    dl = [(k, {n: (dev(v, n.startswith("w") and v.ndim == 2) if isinstance(v, np.ndarray) else v)
-               for n, v in Wl.items()}, dev(nw)) for k, Wl, nw in layers]
+    dl = []
+    for k, Wl, nw in layers:
+        Wd = {n: (dev(v, n.startswith("w") and v.ndim == 2) if isinstance(v, np.ndarray) else v)
+              for n, v in Wl.items()}
+        dl.append((k, sess.fuse_attention_weights(Wd) if k == "attn" else Wd, dev(nw)))
     dfn = dev(fn)
     x0 = W.mixer_input(SEED_MIXER + 20, T, dm)
     x0d = dev(x0, True)

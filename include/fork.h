@@ -242,6 +242,16 @@ fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, c
 fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32_t D, float theta,
                               fork_dtype dt, void* stream);
 
+/* The same rotation out of place from a strided source: head h of token t is
+ * read at src[t * ld_src + h * D ...] and written to dst [T, nheads, D]
+ * (contiguous). theta 0 copies without rotating. This splits the output of a
+ * fused projection ([T, ld_src], several tensors side by side) into
+ * contiguous heads, rotating q and k on the way. ld_src >= nheads * D and a
+ * multiple of 4; src and dst aligned to 4 elements and not overlapping (over
+ * caps.t_cap rows). */
+fork_status fork_rope_copy_forward(const fork_meta* m, const void* src, int64_t ld_src, void* dst, int32_t nheads,
+                                   int32_t D, float theta, fork_dtype dt, void* stream);
+
 /* Causal depthwise convolution of width K (2..8) along each token's isolated
  * sequence (the short convolution in front of a Gated DeltaNet layer):
  *   y[t][c] = act(bias[c] + sum_{j<K} w[c*K + K-1-j] * in_c(t, j)),

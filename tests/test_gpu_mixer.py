@@ -151,14 +151,17 @@ def compare_mixer(name, got, ref, dtype):
         assert rel <= 1e-4 and mx <= 1e-3, name
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mixers_small_tree(dtype):
+@pytest.mark.parametrize("dtype,fused", [("bf16", False), ("f32", False), ("bf16", True), ("f32", True)])
+def test_mixers_small_tree(dtype, fused):
     rng, parent, seg_len = tree(41)
     heads = dict(H=4, Hkv=2, D=64, gH=2, dk=64, dv=64)
     T, Wt, x = mixer_case(dtype, parent, seg_len, 256, 42, **heads)
     sess = session(parent, seg_len, group=2, kv_heads=2, D=64, gH=2, dk=64, dv=64)
     xd = dev(x, dtype)
-    ya = host(sess.attention_mixer(xd, to_dev_weights(Wt["attn"], dtype)))
+    A = to_dev_weights(Wt["attn"], dtype)
+    if fused:
+        A = ForkSession.fuse_attention_weights(A)
+    ya = host(sess.attention_mixer(xd, A))
     yg = host(sess.gdn_mixer(xd, to_dev_weights(Wt["gdn"], dtype)))
     torch.cuda.synchronize()
     bf = dtype == "bf16"
@@ -174,14 +177,18 @@ def test_mixers_one_request_full_size():
     T, Wt, x = mixer_case("bf16", wl.parent, wl.seg_len, 2048, 51, **heads)
     sess = session(wl.parent, wl.seg_len, group=8, kv_heads=2, D=128, gH=16, dk=128, dv=128)
     xd = dev(x, "bf16")
-    ya = host(sess.attention_mixer(xd, to_dev_weights(Wt["attn"], "bf16")))
+    ya = host(sess.attention_mixer(xd, ForkSession.fuse_attention_weights(to_dev_weights(Wt["attn"], "bf16"))))
     yg = host(sess.gdn_mixer(xd, to_dev_weights(Wt["gdn"], "bf16")))
     compare_mixer("attention mixer one_request", ya, OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], bf16=True), "bf16")
     compare_mixer("GDN mixer one_request", yg, OM.gdn_mixer(wl.parent, wl.seg_len, x, Wt["gdn"], bf16=True), "bf16")
 
 
 def dev_stack(layers, fn, dtype):
-    return [(k, to_dev_weights(Wl, dtype), dev(nw)) for k, Wl, nw in layers], dev(fn)
+    out = []
+    for k, Wl, nw in layers:
+        Wd = to_dev_weights(Wl, dtype)
+        out.append((k, ForkSession.fuse_attention_weights(Wd) if k == "attn" else Wd, dev(nw)))
+    return out, dev(fn)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -223,3 +230,31 @@ def test_stack_one_request_full_size():
     fid = metrics.decision_fidelity(h, ref64, w_head, wl.parent, wl.seg_len)
     log(f"  option distributions vs the exact oracle: {fid}")
     assert fid["tvd_max"] <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,theta,nh,D,extra", [("bf16", 10000.0, 16, 128, 2560), ("f32", 0.0, 3, 64, 8),
+                                                    ("bf16", 0.0, 2, 128, 0), ("f32", 500000.0, 4, 32, 36)])
+def test_rope_copy_parity(dtype, theta, nh, D, extra):
+    """Out-of-place rotation from a strided source (a column block of a fused
+    projection's output), and the plain copy (theta 0)."""
+    rng, parent, seg_len = tree(90 + nh)
+    T = int(seg_len.sum())
+    ld = nh * D + extra
+    off = extra // 2 - (extra // 2) % 4
+    src = rng.standard_normal((T, ld)).astype(np.float32)
+    if dtype == "bf16":
+        src = W.round_bf16(src)
+    sess = session(parent, seg_len)
+    sd = dev(src, dtype)
+    out = torch.full((T, nh, D), float("nan"), device="cuda", dtype=TORCH_DT[dtype])
+    from tree_structured_decision_amd import binding as B
+    dt = B.FORK_BF16 if dtype == "bf16" else B.FORK_F32
+    B.fork_rope_copy_forward(sess.meta, sd.data_ptr() + off * sd.element_size(), ld, out, nh, D, theta, dt)
+    torch.cuda.synchronize()
+    x = src[:, off:off + nh * D].reshape(T, nh, D)
+    if theta == 0.0:
+        assert np.array_equal(host(out), x.astype(np.float64))
+        log(f"  rope copy {dtype}: exact")
+    else:
+        import oracle
+        check_close(f"rope from strided source {dtype} D={D}", host(out), oracle.rope(parent, seg_len, x, theta=theta), dtype)

@@ -414,3 +414,18 @@ def test_fp8_argument_errors_without_gpu():
     assert lf(K=24) == -3
     assert lf(M=0) == -1 and lf(acc=3) == -1
     assert lf(y=fake) == -1
+
+
+def test_rope_copy_argument_errors_without_gpu():
+    parent, seg_len = np.array([-1, 0], np.int32), np.array([4, 2], np.int32)
+    meta, _, _ = plan(parent, seg_len, gqa=2)
+    meta.dev = 0x1000
+    meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
+    rc = lambda src=0x10000, ld=256, dst=0x80000, nh=2, D=128, theta=10000.0, dt=B.FORK_BF16: _status(
+        lambda: B.fork_rope_copy_forward(meta, src, ld, dst, nh, D, theta, dt, stream=0))
+    assert rc(ld=255) == -1 and rc(ld=254) == -1   # below nheads * D / not a multiple of 4
+    assert rc(D=12) == -3
+    assert rc(theta=0.5) == -1
+    assert rc(src=0x10002) == -1                   # misaligned
+    assert rc(dst=0x10000 + 512) == -1             # overlapping
+    assert rc(src=None) == -1

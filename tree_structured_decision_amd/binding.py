@@ -25,7 +25,7 @@ STATUS = {0: "FORK_OK", -1: "FORK_E_ARG", -2: "FORK_E_TREE", -3: "FORK_E_UNSUPPO
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
            "fork_meta_plan_ctx", "fork_meta_export",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
-           "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_conv_forward",
+           "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "fork_linear_forward",
            "fork_quantize_fp8", "fork_linear_fp8_forward",
            "fork_graph_create", "fork_graph_launch",
@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
             "fork_rope_forward": [P(fork_meta), vp, i32, i32, f32, i32, vp],
+            "fork_rope_copy_forward": [P(fork_meta), vp, ctypes.c_int64, vp, i32, i32, f32, i32, vp],
             "fork_conv_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
             "fork_gate_forward": [P(fork_meta), vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
             "gdn_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
@@ -263,6 +264,12 @@ def fork_rope_forward(meta: fork_meta, x, nheads: int, D: int, theta: float, dt:
                       stream=None) -> None:
     _check(lib().fork_rope_forward(ctypes.byref(meta), _ptr(x), nheads, D, float(theta), dt,
                                    _stream(stream)))
+
+
+def fork_rope_copy_forward(meta: fork_meta, src, ld_src: int, dst, nheads: int, D: int, theta: float, dt: int,
+                           stream=None) -> None:
+    _check(lib().fork_rope_copy_forward(ctypes.byref(meta), _ptr(src), ld_src, _ptr(dst), nheads, D,
+                                        float(theta), dt, _stream(stream)))
 
 
 def fork_conv_forward(meta: fork_meta, x, w, bias, conv_state, y, C: int, K: int, act: int, dt: int,

@@ -35,9 +35,14 @@ __device__ __forceinline__ unsigned short f_to_bf16(float x) { return __builtin_
 constexpr int kRopeThreads = 256;
 constexpr int kMaxRopeD = 256;
 
+// The rows are read from src (row stride ld_src elements per token, head h
+// at column h D) and written to dst [T, nh, D] contiguous; src == dst with
+// ld_src = nh D rotates in place. rotate = false copies (the split of a fused
+// projection's output into contiguous heads).
 template <bool BF16>
-__global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __restrict__ blob, void* x, int nh,
-                                                            int D, double log2_theta) {
+__global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __restrict__ blob, const void* src,
+                                                            long long ld_src, void* dst, int nh, int D,
+                                                            double log2_theta, int rotate) {
   __shared__ double inv_freq[kMaxRopeD / 2];
   const int half = D / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x) inv_freq[i] = exp2(-(2.0 * i / D) * log2_theta);
@@ -51,19 +56,23 @@ __global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __res
        idx += (long long)gridDim.x * blockDim.x) {
     const int k = (int)(idx % per_row);
     const long long th = idx / per_row;  // token * nh + head
-    const int t = (int)(th / nh);
-    const double pos = (double)iso[t];
-    float c[4], s[4];
+    const int t = (int)(th / nh), h = (int)(th % nh);
+    float c[4] = {1.f, 1.f, 1.f, 1.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rotate) {
+      const double pos = (double)iso[t];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      double a = pos * inv_freq[4 * k + e];
-      a -= two_pi * rint(a / two_pi);
-      sincosf((float)a, &s[e], &c[e]);
+      for (int e = 0; e < 4; ++e) {
+        double a = pos * inv_freq[4 * k + e];
+        a -= two_pi * rint(a / two_pi);
+        sincosf((float)a, &s[e], &c[e]);
+      }
     }
+    const long long so = (long long)t * ld_src + (long long)h * D;
     if constexpr (BF16) {
-      unsigned short* row = (unsigned short*)x + th * D;
-      const u32x2_t lo = *(const u32x2_t*)(row + 4 * k);
-      const u32x2_t hi = *(const u32x2_t*)(row + half + 4 * k);
+      const unsigned short* in = (const unsigned short*)src + so;
+      unsigned short* row = (unsigned short*)dst + th * D;
+      const u32x2_t lo = *(const u32x2_t*)(in + 4 * k);
+      const u32x2_t hi = *(const u32x2_t*)(in + half + 4 * k);
       float a0[4] = {bf16_to_f(lo.x & 0xffff), bf16_to_f(lo.x >> 16), bf16_to_f(lo.y & 0xffff), bf16_to_f(lo.y >> 16)};
       float b0[4] = {bf16_to_f(hi.x & 0xffff), bf16_to_f(hi.x >> 16), bf16_to_f(hi.y & 0xffff), bf16_to_f(hi.y >> 16)};
       unsigned short ra[4], rb[4];
@@ -75,9 +84,10 @@ __global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __res
       *(u32x2_t*)(row + 4 * k) = u32x2_t{ra[0] | ((unsigned)ra[1] << 16), ra[2] | ((unsigned)ra[3] << 16)};
       *(u32x2_t*)(row + half + 4 * k) = u32x2_t{rb[0] | ((unsigned)rb[1] << 16), rb[2] | ((unsigned)rb[3] << 16)};
     } else {
-      float* row = (float*)x + th * D;
-      const f32x4_t a0 = *(const f32x4_t*)(row + 4 * k);
-      const f32x4_t b0 = *(const f32x4_t*)(row + half + 4 * k);
+      const float* in = (const float*)src + so;
+      float* row = (float*)dst + th * D;
+      const f32x4_t a0 = *(const f32x4_t*)(in + 4 * k);
+      const f32x4_t b0 = *(const f32x4_t*)(in + half + 4 * k);
       f32x4_t ra, rb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -226,14 +236,18 @@ int stream_grid(long long threads, int per_block) {
 
 }  // namespace
 
-fork_status launch_rope(const fork_meta* m, void* x, int nh, int D, float theta, fork_dtype dt, hipStream_t stream) {
+fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, void* dst, int nh, int D, float theta,
+                        fork_dtype dt, hipStream_t stream) {
   const long long threads = (long long)m->caps.t_cap * nh * (D / 8);
   const int grid = stream_grid(threads, kRopeThreads);
-  const double l2t = log2((double)theta);
+  const int rotate = theta > 0.f;
+  const double l2t = rotate ? log2((double)theta) : 0.0;
   if (dt == FORK_BF16)
-    hipLaunchKernelGGL(rope_kernel<true>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, x, nh, D, l2t);
+    hipLaunchKernelGGL(rope_kernel<true>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, src,
+                       ld_src, dst, nh, D, l2t, rotate);
   else
-    hipLaunchKernelGGL(rope_kernel<false>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, x, nh, D, l2t);
+    hipLaunchKernelGGL(rope_kernel<false>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, src,
+                       ld_src, dst, nh, D, l2t, rotate);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

@@ -549,7 +549,27 @@ fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32
   if (D < 8 || D > 256 || D % 8) return fail(FORK_E_UNSUPPORTED, "rotary dim %d unsupported (multiple of 8, 8..256)", D);
   if (!(theta > 1.f)) return fail(FORK_E_ARG, "theta must be > 1");
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  return launch_rope(m, x, nheads, D, theta, dt, (hipStream_t)stream);
+  return launch_rope(m, x, (long long)nheads * D, x, nheads, D, theta, dt, (hipStream_t)stream);
+}
+
+fork_status fork_rope_copy_forward(const fork_meta* m, const void* src, int64_t ld_src, void* dst, int32_t nheads,
+                                   int32_t D, float theta, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!src || !dst) return fail(FORK_E_ARG, "src and dst must be non-null");
+  if (nheads < 1) return fail(FORK_E_ARG, "nheads=%d", nheads);
+  if (D < 8 || D > 256 || D % 8) return fail(FORK_E_UNSUPPORTED, "rotary dim %d unsupported (multiple of 8, 8..256)", D);
+  if (ld_src < (int64_t)nheads * D || ld_src % 4) return fail(FORK_E_ARG, "ld_src %lld (>= nheads * D, a multiple of 4)", (long long)ld_src);
+  const size_t esz = dt == FORK_BF16 ? 2 : 4;
+  if ((uintptr_t)src % (4 * esz) || (uintptr_t)dst % (4 * esz)) return fail(FORK_E_ARG, "src and dst must be aligned to 4 elements");
+  if (theta != 0.f && !(theta > 1.f)) return fail(FORK_E_ARG, "theta must be > 1 (or 0: copy)");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  const char* s0 = (const char*)src;
+  const char* d0 = (const char*)dst;
+  const size_t span = (size_t)m->caps.t_cap * ld_src * esz, dspan = (size_t)m->caps.t_cap * nheads * D * esz;
+  if (d0 < s0 + span && s0 < d0 + dspan) return fail(FORK_E_ARG, "src and dst must not overlap");
+  return launch_rope(m, src, (long long)ld_src, dst, nheads, D, theta, dt, (hipStream_t)stream);
 }
 
 fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w, const float* bias,

@@ -163,8 +163,8 @@ size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
                              int D, float scale, fork_dtype dt, void* ws, hipStream_t stream);
-fork_status launch_rope(const fork_meta* m, void* x, int nh, int D, float theta, fork_dtype dt,
-                        hipStream_t stream);
+fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, void* dst, int nh, int D, float theta,
+                        fork_dtype dt, hipStream_t stream);
 fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias,
                         const float* state, void* y, int C, int K, int act, fork_dtype dt,
                         hipStream_t stream);

@@ -189,10 +189,24 @@ class ForkSession:
         b = self._bufs(bufs, x, dict(q=(T, H, D), k=(T, Hkv, D), v=(T, Hkv, D), g=(T, H, D),
                                      o=(T, H, D), u=(T, H, D), y=(T, dm)))
         xin = self._proj_in(fp8, x, b, "x", stream)
-        for n in ("q", "k", "v", "g"):
-            self._proj(fp8, xin, "w" + n, W, b[n], stream)
-        self.rope(b["q"], theta, stream)
-        self.rope(b["k"], theta, stream)
+        if "wqkvg" in W:
+            # one product for q | k | v | g, then split into contiguous heads
+            # (rotating q and k on the way)
+            nf = 2 * H * D + 2 * Hkv * D
+            if "f" not in b or tuple(b["f"].shape) != (T, nf):
+                b["f"] = torch.empty((T, nf), dtype=x.dtype, device=x.device)
+            self._proj(fp8, xin, "wqkvg", W, b["f"], stream)
+            dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+            base, esz = b["f"].data_ptr(), b["f"].element_size()
+            col = 0
+            for n, nh, th in (("q", H, theta), ("k", Hkv, theta), ("v", Hkv, 0.0), ("g", H, 0.0)):
+                B.fork_rope_copy_forward(self.meta, base + col * esz, nf, b[n], nh, D, th, dt, stream=stream)
+                col += nh * D
+        else:
+            for n in ("q", "k", "v", "g"):
+                self._proj(fp8, xin, "w" + n, W, b[n], stream)
+            self.rope(b["q"], theta, stream)
+            self.rope(b["k"], theta, stream)
         self.attention(b["q"], b["k"], b["v"], b["o"], stream=stream)
         self.gate(b["o"], b["g"], None, b["u"], 0, stream=stream)
         uin = self._proj_in(fp8, b["u"].view(T, H * D), b, "u", stream)
@@ -260,6 +274,16 @@ class ForkSession:
                 self.gdn_mixer(b["hn"].view(T, dm), W, eps, stream, mb, residual=x, fp8=fp8)
         self.gate(x.view(T, 1, dm), None, final_norm, b["h"], 2, eps, stream)
         return b["h"].view(T, dm)
+
+    @staticmethod
+    def fuse_attention_weights(W: dict) -> dict:
+        """A copy of attention-mixer weights with wq | wk | wv | wg stacked into one
+        [(2 H + 2 Hkv) D, dm] projection "wqkvg": attention_mixer then runs one product
+        instead of four. (Row scales of FP8 weights are per output channel, so the
+        stacked matrix quantises to the same codes.)"""
+        out = dict(W)
+        out["wqkvg"] = torch.cat([W["wq"], W["wk"], W["wv"], W["wg"]], dim=0).contiguous()
+        return out
 
     @staticmethod
     def _bufs(bufs, x, shapes):
