@@ -579,12 +579,13 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     dev = lambda a, dt=torch.bfloat16: torch.from_numpy(a).to("cuda", dt)
     A = sess.fuse_attention_weights({n: (dev(v) if isinstance(v, np.ndarray) else v)
                                      for n, v in Wt["attn"].items()})
-    G = {n: (dev(v) if isinstance(v, np.ndarray) and n.startswith("w") else
-             dev(v, torch.float32) if isinstance(v, np.ndarray) else v) for n, v in Wt["gdn"].items()}
+    G = sess.fuse_gdn_weights({n: (dev(v) if isinstance(v, np.ndarray) and n.startswith("w") else
+                                   dev(v, torch.float32) if isinstance(v, np.ndarray) else v)
+                               for n, v in Wt["gdn"].items()})
     x = dev(W.mixer_input(SEED_MIXER + 1, T, dm))
     ab, gb = {}, {}
     C = 2 * wl.gH * wl.dk + wl.gH * wl.dv
-    proj = [(A["wqkvg"], "f"), (G["wqkv"], "p"), (G["wab"], "ab"), (G["wz"], "z")]
+    proj = [(A["wqkvg"], "f"), (G["wqkv"], "p"), (G["wzab"], "zab")]
     outs = {}
 
     def projections():
@@ -599,7 +600,7 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
         sess.linear(outs["u"], A["wo"], outs["y"])
         sess.linear(outs["ug"], G["wo"], outs["y"])
 
-    flop = 2.0 * T * dm * (sum(w.shape[0] for w, _ in proj) + wl.H * wl.D + wl.gH * wl.dv)
+    flop = 2.0 * T * dm * (sum(w.shape[0] for w, _ in proj) + wl.H * wl.D + wl.gH * wl.dv)  # + 2 outputs
     o = torch.randn(T, wl.H, wl.D, device="cuda").to(torch.bfloat16)
     g = torch.randn_like(o)
     og = torch.randn(T, wl.gH, wl.dv, device="cuda").to(torch.bfloat16)
@@ -616,7 +617,7 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     A8, G8 = sess.quantize_weights(A), sess.quantize_weights(G)
     ab8, gb8, outs8 = {}, {}, {}
     xq, xs = sess.quantize_fp8(x)
-    proj8 = [(A8["wqkvg"], "f"), (G8["wqkv"], "p"), (G8["wab"], "ab"), (G8["wz"], "z")]
+    proj8 = [(A8["wqkvg"], "f"), (G8["wqkv"], "p"), (G8["wzab"], "zab")]
 
     def projections_fp8():
         for (wq_, ws_), n in proj8:
@@ -672,10 +673,11 @@ def mixer_ops(wl, sess, iters=20, dm=2048):
     rep["mixer_pair_fp8_us"] = pair8
     rep["mixer_pair_fp8_tokens_per_s"] = T / (pair8 * 1e-6)
     rep["note"] = (f"model width {dm}; attention 16 q / 2 kv heads x 128, Gated DeltaNet 16 heads x 128, "
-                   "convolution width 4; random bf16 weights; projections = the 6 GEMMs of both "
+                   "convolution width 4; random bf16 weights; projections = the 5 GEMMs of both "
                    "mixers (hipBLASLt, fp32 accumulation; the attention mixer's q | k | v | gate "
                    "projections run as one product whose output is split into heads by the rotary "
-                   "kernel); *_fp8: E4M3 projections with per-token "
+                   "kernel, the Gated DeltaNet's output gate and decay / strength projections as "
+                   "another); *_fp8: E4M3 projections with per-token "
                    "activation and per-channel weight scales (quantisation inside the mixers, "
                    "against the fp8 MFMA peak)")
     return rep
@@ -707,7 +709,7 @@ def stack_ops(wl, sess, iters=10, dm=2048):
     for k, Wl, nw in layers:
         Wd = {n: (dev(v, n.startswith("w") and v.ndim == 2) if isinstance(v, np.ndarray) else v)
               for n, v in Wl.items()}
-        dl.append((k, sess.fuse_attention_weights(Wd) if k == "attn" else Wd, dev(nw)))
+        dl.append((k, sess.fuse_attention_weights(Wd) if k == "attn" else sess.fuse_gdn_weights(Wd), dev(nw)))
     dfn = dev(fn)
     x0 = W.mixer_input(SEED_MIXER + 20, T, dm)
     x0d = dev(x0, True)

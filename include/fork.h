@@ -281,11 +281,15 @@ fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w,
  *   mode 0: y = x * sigmoid(g)
  *   mode 1: y = x / sqrt(mean(x^2) + eps) * w * silu(g),  silu(g) = g sigmoid(g)
  *   mode 2: y = x / sqrt(mean(x^2) + eps) * w             (g unused, may be null)
- * x, g, y [T, nheads, D] of dtype dt (y may be x); w [D] fp32, 16-byte aligned,
+ * x, y [T, nheads, D] of dtype dt (y may be x); g of dtype dt with token t's
+ * heads at g + t * ld_g (ld_g = 0 means nheads * D, i.e. g [T, nheads, D];
+ * otherwise >= nheads * D and a multiple of 8, so g can be a column block of
+ * a wider projection output), 16-byte aligned; w [D] fp32, 16-byte aligned,
  * the same for every head (modes 1, 2). D a multiple of 8 in 8..65536;
  * eps > 0 for modes 1, 2. */
-fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, const float* w, void* y,
-                              int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt, void* stream);
+fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, int64_t ld_g, const float* w,
+                              void* y, int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt,
+                              void* stream);
 
 /* Gated DeltaNet inputs after the short convolution, per token t and head h:
  *   q[t,h] = c_q / sqrt(|c_q|^2 + eps),  k[t,h] = c_k / sqrt(|c_k|^2 + eps),
@@ -293,11 +297,12 @@ fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, 
  *   a[t,h] = exp(-exp(a_log[h]) * softplus(ab[t,h] + dt_bias[h])),
  *   b[t,h] = sigmoid(ab[t,H+h]),
  * with c [T, 2 H dk + H dv] holding the query heads, then the key heads, then
- * the value heads of each token, and ab [T, 2 H] the decay and write-strength
- * projections, both of dtype dt; q, k [T,H,dk], v [T,H,dv] of dtype dt, and
+ * the value heads of each token, and ab the decay and write-strength
+ * projections (2 H values of token t at ab + t * ld_ab; ld_ab = 0 means 2 H,
+ * otherwise >= 2 H), both of dtype dt; q, k [T,H,dk], v [T,H,dv] of dtype dt, and
  * a, b [T,H] fp32: the inputs of gdn_fork_forward. a_log, dt_bias [H] fp32.
  * dk, dv multiples of 8 in 8..1024; eps > 0. T from the blob. */
-fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, int64_t ld_ab, const float* a_log,
                                const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
                                int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream);
 

@@ -83,7 +83,7 @@ def test_fp8_mixers_and_stack_one_request():
     x = W.mixer_input(82, wl.T, 2048)
     xd = dev(x, "bf16")
     A = sess.quantize_weights(ForkSession.fuse_attention_weights(to_dev_weights(Wt["attn"], "bf16")))
-    G = sess.quantize_weights(to_dev_weights(Wt["gdn"], "bf16"))
+    G = sess.quantize_weights(ForkSession.fuse_gdn_weights(to_dev_weights(Wt["gdn"], "bf16")))
     ya = host(sess.attention_mixer(xd, A, fp8=True))
     yg = host(sess.gdn_mixer(xd, G, fp8=True))
     compare_fp8("fp8 attention mixer", ya, OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], bf16=True, fp8=True))

@@ -88,6 +88,14 @@ def test_gate_parity(dtype, mode, nh, D):
     torch.cuda.synchronize()
     ref = OM.gate(x, g, w, mode, 1e-6)
     check_close(f"gate mode {mode} {dtype} D={D}", host(y), ref, dtype)
+    if mode != 2:
+        # the gate as a column block of a wider row (a fused projection's output)
+        wide = np.concatenate([g.reshape(T, nh * D), rng.standard_normal((T, 24)).astype(np.float32)], 1)
+        gd = dev(wide, dtype)
+        y2 = torch.full_like(y, float("nan"))
+        sess.gate(dev(x, dtype), gd.data_ptr(), dev(w) if mode else None, y2, mode, 1e-6, ld_g=nh * D + 24)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y)
 
 
 @pytest.mark.parametrize("dtype,H,dk", [("bf16", 16, 128), ("f32", 3, 64), ("bf16", 2, 32)])
@@ -159,10 +167,11 @@ def test_mixers_small_tree(dtype, fused):
     sess = session(parent, seg_len, group=2, kv_heads=2, D=64, gH=2, dk=64, dv=64)
     xd = dev(x, dtype)
     A = to_dev_weights(Wt["attn"], dtype)
+    G = to_dev_weights(Wt["gdn"], dtype)
     if fused:
-        A = ForkSession.fuse_attention_weights(A)
+        A, G = ForkSession.fuse_attention_weights(A), ForkSession.fuse_gdn_weights(G)
     ya = host(sess.attention_mixer(xd, A))
-    yg = host(sess.gdn_mixer(xd, to_dev_weights(Wt["gdn"], dtype)))
+    yg = host(sess.gdn_mixer(xd, G))
     torch.cuda.synchronize()
     bf = dtype == "bf16"
     compare_mixer(f"attention mixer {dtype}", ya, OM.attention_mixer(parent, seg_len, x, Wt["attn"], bf16=bf), dtype)
@@ -178,7 +187,7 @@ def test_mixers_one_request_full_size():
     sess = session(wl.parent, wl.seg_len, group=8, kv_heads=2, D=128, gH=16, dk=128, dv=128)
     xd = dev(x, "bf16")
     ya = host(sess.attention_mixer(xd, ForkSession.fuse_attention_weights(to_dev_weights(Wt["attn"], "bf16"))))
-    yg = host(sess.gdn_mixer(xd, to_dev_weights(Wt["gdn"], "bf16")))
+    yg = host(sess.gdn_mixer(xd, ForkSession.fuse_gdn_weights(to_dev_weights(Wt["gdn"], "bf16"))))
     compare_mixer("attention mixer one_request", ya, OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], bf16=True), "bf16")
     compare_mixer("GDN mixer one_request", yg, OM.gdn_mixer(wl.parent, wl.seg_len, x, Wt["gdn"], bf16=True), "bf16")
 
@@ -187,7 +196,8 @@ def dev_stack(layers, fn, dtype):
     out = []
     for k, Wl, nw in layers:
         Wd = to_dev_weights(Wl, dtype)
-        out.append((k, ForkSession.fuse_attention_weights(Wd) if k == "attn" else Wd, dev(nw)))
+        out.append((k, ForkSession.fuse_attention_weights(Wd) if k == "attn" else ForkSession.fuse_gdn_weights(Wd),
+                    dev(nw)))
     return out, dev(fn)
 
 

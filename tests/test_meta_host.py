@@ -375,8 +375,10 @@ def test_mixer_piece_argument_errors_without_gpu():
     meta.dev = 0x1000
     meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
     fake = 0x2000
-    gate = lambda mode=1, g=fake, w=fake, D=64, nh=2, eps=1e-6, dt=B.FORK_BF16: _status(
-        lambda: B.fork_gate_forward(meta, fake, g, w, 0x3000, nh, D, mode, eps, dt, stream=0))
+    gate = lambda mode=1, g=fake, w=fake, D=64, nh=2, eps=1e-6, dt=B.FORK_BF16, ld=0: _status(
+        lambda: B.fork_gate_forward(meta, fake, g, w, 0x3000, nh, D, mode, eps, dt, stream=0, ld_g=ld))
+    assert gate(ld=100) == -1 and gate(ld=132) == -1   # below nheads * D / not a multiple of 8
+    assert gate(g=fake + 8) == -1                      # misaligned gate
     assert gate(mode=3) == -1 and gate(mode=-1) == -1
     assert gate(mode=0, g=None) == -1 and gate(mode=1, g=None) == -1
     assert gate(mode=1, w=None) == -1 and gate(mode=2, w=None) == -1
@@ -392,6 +394,8 @@ def test_mixer_piece_argument_errors_without_gpu():
     assert gi(H=0) == -1
     assert gi(dk=12) == -3 and gi(dv=2048) == -3
     assert gi(eps=-1.0) == -1
+    assert _status(lambda: B.gdn_inputs_forward(meta, fake, fake, fake, fake, fake, fake, fake, fake, fake, 2, 64, 64,
+                                                1e-6, B.FORK_BF16, stream=0, ld_ab=3)) == -1
     lin = lambda M=4, N=8, K=16, x=fake, y=0x3000, acc=0, dt=B.FORK_BF16: _status(
         lambda: B.fork_linear_forward(x, 0x4000, y, M, N, K, acc, dt, stream=0))
     assert lin(acc=2) == -1

@@ -102,8 +102,8 @@ def lib() -> ctypes.CDLL:
             "fork_rope_forward": [P(fork_meta), vp, i32, i32, f32, i32, vp],
             "fork_rope_copy_forward": [P(fork_meta), vp, ctypes.c_int64, vp, i32, i32, f32, i32, vp],
             "fork_conv_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
-            "fork_gate_forward": [P(fork_meta), vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
-            "gdn_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+            "fork_gate_forward": [P(fork_meta), vp, vp, ctypes.c_int64, vp, vp, i32, i32, i32, f32, i32, vp],
+            "gdn_inputs_forward": [P(fork_meta), vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                    f32, i32, vp],
             "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, i32, vp],
             "fork_quantize_fp8": [vp, vp, vp, ctypes.c_int64, i32, i32, vp],
@@ -279,14 +279,14 @@ def fork_conv_forward(meta: fork_meta, x, w, bias, conv_state, y, C: int, K: int
 
 
 def fork_gate_forward(meta: fork_meta, x, g, w, y, nheads: int, D: int, mode: int, eps: float,
-                      dt: int, stream=None) -> None:
-    _check(lib().fork_gate_forward(ctypes.byref(meta), _ptr(x), _ptr(g), _ptr(w), _ptr(y), nheads, D,
+                      dt: int, stream=None, ld_g: int = 0) -> None:
+    _check(lib().fork_gate_forward(ctypes.byref(meta), _ptr(x), _ptr(g), ld_g, _ptr(w), _ptr(y), nheads, D,
                                    mode, float(eps), dt, _stream(stream)))
 
 
 def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H: int, dk: int,
-                       dv: int, eps: float, dt: int, stream=None) -> None:
-    _check(lib().gdn_inputs_forward(ctypes.byref(meta), _ptr(c), _ptr(ab), _ptr(a_log),
+                       dv: int, eps: float, dt: int, stream=None, ld_ab: int = 0) -> None:
+    _check(lib().gdn_inputs_forward(ctypes.byref(meta), _ptr(c), _ptr(ab), ld_ab, _ptr(a_log),
                                     _ptr(dt_bias), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), H,
                                     dk, dv, float(eps), dt, _stream(stream)))
 

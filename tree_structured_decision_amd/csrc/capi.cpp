@@ -588,8 +588,9 @@ fork_status fork_conv_forward(const fork_meta* m, const void* x, const float* w,
   return launch_conv(m, x, w, bias, conv_state, y, C, K, act, dt, (hipStream_t)stream);
 }
 
-fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, const float* w, void* y,
-                              int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt, void* stream) {
+fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, int64_t ld_g, const float* w,
+                              void* y, int32_t nheads, int32_t D, int32_t mode, float eps, fork_dtype dt,
+                              void* stream) {
   g_err[0] = 0;
   fork_status st = check_meta(m);
   if (st) return st;
@@ -601,11 +602,15 @@ fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, 
   if (nheads < 1) return fail(FORK_E_ARG, "nheads=%d", nheads);
   if (D < 8 || D > 65536 || D % 8) return fail(FORK_E_UNSUPPORTED, "row size %d unsupported (multiple of 8, 8..65536)", D);
   if (mode != 0 && !(eps > 0.f)) return fail(FORK_E_ARG, "eps must be > 0");
+  if (ld_g == 0) ld_g = (int64_t)nheads * D;
+  if (mode != 2 && (ld_g < (int64_t)nheads * D || ld_g % 8))
+    return fail(FORK_E_ARG, "ld_g %lld (>= nheads * D, a multiple of 8)", (long long)ld_g);
+  if (mode != 2 && (uintptr_t)g % 16) return fail(FORK_E_ARG, "g must be 16-byte aligned");
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  return launch_gate(m, x, g, w, y, nheads, D, mode, eps, dt, (hipStream_t)stream);
+  return launch_gate(m, x, g, (long long)ld_g, w, y, nheads, D, mode, eps, dt, (hipStream_t)stream);
 }
 
-fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, int64_t ld_ab, const float* a_log,
                                const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
                                int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream) {
   g_err[0] = 0;
@@ -617,8 +622,11 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
   if (dk < 8 || dk > 1024 || dk % 8 || dv < 8 || dv > 1024 || dv % 8)
     return fail(FORK_E_UNSUPPORTED, "head sizes dk=%d dv=%d unsupported (multiples of 8, 8..1024)", dk, dv);
   if (!(eps > 0.f)) return fail(FORK_E_ARG, "eps must be > 0");
+  if (ld_ab == 0) ld_ab = 2 * (int64_t)H;
+  if (ld_ab < 2 * (int64_t)H) return fail(FORK_E_ARG, "ld_ab %lld < 2 H", (long long)ld_ab);
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
-  return launch_gdn_inputs(m, c, ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt, (hipStream_t)stream);
+  return launch_gdn_inputs(m, c, ab, (long long)ld_ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt,
+                           (hipStream_t)stream);
 }
 
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,

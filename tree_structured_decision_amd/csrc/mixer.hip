@@ -75,11 +75,12 @@ __device__ __forceinline__ float group_sum(float s, int L) {
 // mode 0: y = x * sigmoid(g)
 // mode 1: y = x / sqrt(mean(x^2) + eps) * w * silu(g)
 // mode 2: y = x / sqrt(mean(x^2) + eps) * w
-// over rows of D elements; T * nh rows, T read from the blob.
+// over rows of D elements; T * nh rows, T read from the blob. g of token t,
+// head h starts at g + t ldg + h D (ldg = nh D when g is [T, nh, D]).
 template <bool BF16, int MODE>
 __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __restrict__ blob, const void* x,
-                                                           const void* g, const float* __restrict__ w, void* y,
-                                                           int nh, int D, int L, float eps) {
+                                                           const void* g, long long ldg, const float* __restrict__ w,
+                                                           void* y, int nh, int D, int L, float eps) {
   const long long rows = (long long)blob[MH_T] * nh;
   const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L, nc = D / 8;
   const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -88,6 +89,7 @@ __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __rest
     const long long r = r0 + lane / L;
     const bool live = r < rows;
     const size_t base = (size_t)r * D;
+    const size_t gbase = (size_t)(r / nh) * ldg + (size_t)(r % nh) * D;
     float scale = 1.f;
     if constexpr (MODE != 0) {
       float ss = 0.f;
@@ -105,7 +107,7 @@ __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __rest
     for (int j = li; j < nc; j += L) {
       float v[8], gv[8], o[8];
       load8<BF16>(x, base + 8 * j, v);
-      if constexpr (MODE != 2) load8<BF16>(g, base + 8 * j, gv);
+      if constexpr (MODE != 2) load8<BF16>(g, gbase + 8 * j, gv);
       if constexpr (MODE == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = v[e] * sigmoid(gv[e]);
@@ -124,13 +126,13 @@ __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __rest
 }
 
 // One (token, head) row per group of L lanes: c [T, 2 H dk + H dv] holds
-// the convolved query, key and value heads side by side; ab [T, 2 H] the
-// decay and write-strength projections.
+// the convolved query, key and value heads side by side; ab the decay and
+// write-strength projections of token t at ab + t ld_ab (2 H values).
 template <bool BF16>
 __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     const int32_t* __restrict__ blob, const void* c, const void* ab, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, void* q, void* k, void* v, float* __restrict__ a, float* __restrict__ b, int H,
-    int dk, int dv, int L, float eps) {
+    int dk, int dv, long long ld_ab, int L, float eps) {
   const long long rows = (long long)blob[MH_T] * H;
   const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L;
   const size_t cw = (size_t)2 * H * dk + (size_t)H * dv;
@@ -179,11 +181,11 @@ __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     if (li == 0) {
       float al, be;
       if constexpr (BF16) {
-        al = bf16_to_f(((const unsigned short*)ab)[(size_t)t * 2 * H + h]);
-        be = bf16_to_f(((const unsigned short*)ab)[(size_t)t * 2 * H + H + h]);
+        al = bf16_to_f(((const unsigned short*)ab)[(size_t)t * ld_ab + h]);
+        be = bf16_to_f(((const unsigned short*)ab)[(size_t)t * ld_ab + H + h]);
       } else {
-        al = ((const float*)ab)[(size_t)t * 2 * H + h];
-        be = ((const float*)ab)[(size_t)t * 2 * H + H + h];
+        al = ((const float*)ab)[(size_t)t * ld_ab + h];
+        be = ((const float*)ab)[(size_t)t * ld_ab + H + h];
       }
       // softplus in the form that neither overflows nor cancels
       const float u = al + dt_bias[h];
@@ -255,27 +257,27 @@ int row_grid(long long rows, int L) {
 }
 
 template <bool BF16>
-fork_status launch_gate_t(const fork_meta* m, const void* x, const void* g, const float* w, void* y, int nh, int D,
-                          int mode, float eps, hipStream_t stream) {
+fork_status launch_gate_t(const fork_meta* m, const void* x, const void* g, long long ldg, const float* w, void* y,
+                          int nh, int D, int mode, float eps, hipStream_t stream) {
   const int L = lanes_per_row(D);
   const int grid = row_grid((long long)m->caps.t_cap * nh, L);
   const int32_t* blob = (const int32_t*)m->dev;
   if (mode == 0)
-    hipLaunchKernelGGL((gate_kernel<BF16, 0>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 0>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
   else if (mode == 1)
-    hipLaunchKernelGGL((gate_kernel<BF16, 1>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 1>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
   else
-    hipLaunchKernelGGL((gate_kernel<BF16, 2>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 2>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
 
 }  // namespace
 
-fork_status launch_gate(const fork_meta* m, const void* x, const void* g, const float* w, void* y, int nh, int D,
-                        int mode, float eps, fork_dtype dt, hipStream_t stream) {
-  if (dt == FORK_BF16) return launch_gate_t<true>(m, x, g, w, y, nh, D, mode, eps, stream);
-  return launch_gate_t<false>(m, x, g, w, y, nh, D, mode, eps, stream);
+fork_status launch_gate(const fork_meta* m, const void* x, const void* g, long long ldg, const float* w, void* y,
+                        int nh, int D, int mode, float eps, fork_dtype dt, hipStream_t stream) {
+  if (dt == FORK_BF16) return launch_gate_t<true>(m, x, g, ldg, w, y, nh, D, mode, eps, stream);
+  return launch_gate_t<false>(m, x, g, ldg, w, y, nh, D, mode, eps, stream);
 }
 
 fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long rows, int K, fork_dtype dt,
@@ -292,7 +294,7 @@ fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long
   return FORK_OK;
 }
 
-fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, const float* a_log,
+fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, long long ld_ab, const float* a_log,
                               const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int H, int dk,
                               int dv, float eps, fork_dtype dt, hipStream_t stream) {
   const int L = lanes_per_row(dk < dv ? dk : dv);
@@ -300,10 +302,10 @@ fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab,
   const int32_t* blob = (const int32_t*)m->dev;
   if (dt == FORK_BF16)
     hipLaunchKernelGGL(gdn_inputs_kernel<true>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
-                       q, k, v, a, b, H, dk, dv, L, eps);
+                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps);
   else
     hipLaunchKernelGGL(gdn_inputs_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
-                       q, k, v, a, b, H, dk, dv, L, eps);
+                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

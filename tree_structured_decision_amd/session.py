@@ -103,21 +103,24 @@ class ForkSession:
         B.fork_conv_forward(self.meta, x, w, bias, conv_state, y, C, w.shape[1], act, dt, stream=stream)
 
     # -- mixer pieces -------------------------------------------------------
-    def gate(self, x, g, w, y, mode: int, eps: float = 1e-6, stream=None):
+    def gate(self, x, g, w, y, mode: int, eps: float = 1e-6, stream=None, ld_g: int = 0):
         """Gate / norm over the last axis of x [T, nheads, D] (mode 0 x sigmoid(g),
-        1 rmsnorm(x) w silu(g), 2 rmsnorm(x) w)."""
+        1 rmsnorm(x) w silu(g), 2 rmsnorm(x) w). g: a tensor [T, nheads, D], or with
+        ld_g a device address whose token rows are ld_g elements apart."""
         T, nh, D = x.shape
         dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
-        B.fork_gate_forward(self.meta, x, g, w, y, nh, D, mode, eps, dt, stream=stream)
+        B.fork_gate_forward(self.meta, x, g, w, y, nh, D, mode, eps, dt, stream=stream, ld_g=ld_g)
 
-    def gdn_inputs(self, c, ab, a_log, dt_bias, q, k, v, a, b, eps: float = 1e-6, stream=None):
+    def gdn_inputs(self, c, ab, a_log, dt_bias, q, k, v, a, b, eps: float = 1e-6, stream=None,
+                   ld_ab: int = 0):
         """Gated DeltaNet inputs from the convolved projections c [T, 2 H dk + H dv]
-        and the decay / write-strength projections ab [T, 2 H]."""
+        and the decay / write-strength projections ab [T, 2 H] (or, with ld_ab, a
+        device address whose token rows are ld_ab elements apart)."""
         T, H, dk = q.shape
         dv = v.shape[2]
         dt = B.FORK_BF16 if c.dtype == torch.bfloat16 else B.FORK_F32
         B.gdn_inputs_forward(self.meta, c, ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt,
-                             stream=stream)
+                             stream=stream, ld_ab=ld_ab)
 
     @staticmethod
     def linear(x, w, y, stream=None, accumulate: bool = False):
@@ -241,13 +244,23 @@ class ForkSession:
             st = b["st"]
         xin = self._proj_in(fp8, x, b, "x", stream)
         self._proj(fp8, xin, "wqkv", W, b["p"], stream)
-        self._proj(fp8, xin, "wab", W, b["ab"], stream)
-        self._proj(fp8, xin, "wz", W, b["z"].view(T, H * dv), stream)
+        if "wzab" in W:
+            # one product for the output gate and the decay / strength projections
+            nz = (W["wzab"][0] if fp8 else W["wzab"]).shape[0]
+            if "zab" not in b or tuple(b["zab"].shape) != (T, nz):
+                b["zab"] = torch.empty((T, nz), dtype=x.dtype, device=x.device)
+            self._proj(fp8, xin, "wzab", W, b["zab"], stream)
+            z, ld_z = b["zab"].data_ptr(), nz
+            ab, ld_ab = b["zab"].data_ptr() + H * dv * b["zab"].element_size(), nz
+        else:
+            self._proj(fp8, xin, "wab", W, b["ab"], stream)
+            self._proj(fp8, xin, "wz", W, b["z"].view(T, H * dv), stream)
+            z, ld_z, ab, ld_ab = b["z"], 0, b["ab"], 0
         self.conv(b["p"], W["conv_w"], b["c"], act=1, stream=stream)
-        self.gdn_inputs(b["c"], b["ab"], W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"],
-                        b["b"], eps, stream)
+        self.gdn_inputs(b["c"], ab, W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"],
+                        b["b"], eps, stream, ld_ab=ld_ab)
         self.gdn(b["q"], b["k"], b["v"], b["a"], b["b"], b["o"], st, scale=dk ** -0.5, stream=stream)
-        self.gate(b["o"], b["z"], W["norm_w"], b["u"], 1, eps, stream)
+        self.gate(b["o"], z, W["norm_w"], b["u"], 1, eps, stream, ld_g=ld_z)
         uin = self._proj_in(fp8, b["u"].view(T, H * dv), b, "u", stream)
         if fp8:
             b["x_q"], b["x_s"], b["u_q"], b["u_s"] = xin[0], xin[1], uin[0], uin[1]
@@ -283,6 +296,22 @@ class ForkSession:
         stacked matrix quantises to the same codes.)"""
         out = dict(W)
         out["wqkvg"] = torch.cat([W["wq"], W["wk"], W["wv"], W["wg"]], dim=0).contiguous()
+        return out
+
+    @staticmethod
+    def fuse_gdn_weights(W: dict) -> dict:
+        """A copy of Gated DeltaNet mixer weights with wz | wab stacked into one
+        [H dv + 2 H, dm] projection "wzab": gdn_mixer then runs one product for the
+        output gate and the decay / strength inputs (the 2 H-wide product alone
+        costs about as much as the H dv-wide one). Zero rows pad it to a multiple of
+        8 outputs, so that each token's gate row stays 16-byte aligned."""
+        out = dict(W)
+        n = W["wz"].shape[0] + W["wab"].shape[0]
+        pad = (-n) % 8
+        parts = [W["wz"], W["wab"]]
+        if pad:
+            parts.append(torch.zeros((pad, W["wz"].shape[1]), dtype=W["wz"].dtype, device=W["wz"].device))
+        out["wzab"] = torch.cat(parts, dim=0).contiguous()
         return out
 
     @staticmethod
