@@ -301,10 +301,24 @@ fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, 
  * projections (2 H values of token t at ab + t * ld_ab; ld_ab = 0 means 2 H,
  * otherwise >= 2 H), both of dtype dt; q, k [T,H,dk], v [T,H,dv] of dtype dt, and
  * a, b [T,H] fp32: the inputs of gdn_fork_forward. a_log, dt_bias [H] fp32.
- * dk, dv multiples of 8 in 8..1024; eps > 0. T from the blob. */
+ * c may be null: then only a and b are formed (q, k, v ignored; see
+ * gdn_conv_inputs_forward). dk, dv multiples of 8 in 8..1024; eps > 0. T
+ * from the blob. */
 fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, int64_t ld_ab, const float* a_log,
                                const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
                                int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream);
+
+/* The short convolution of the Gated DeltaNet projections and their split in
+ * one pass: fork_conv_forward with SiLU over x [T, 2 H dk + H dv] (query
+ * heads, key heads, value heads of each token; same taps, bias and
+ * conv_state conventions, C = 2 H dk + H dv), then the query and key heads
+ * L2-normalised, u / sqrt(|u|^2 + eps), and the three parts written to
+ * q, k [T,H,dk] and v [T,H,dv] (dtype dt), as gdn_inputs_forward would
+ * produce from the convolution's output. dk == dv, a power of two in
+ * 8..512; K 2..8; w 16-byte aligned. */
+fork_status gdn_conv_inputs_forward(const fork_meta* m, const void* x, const float* w, const float* bias,
+                                    const float* conv_state, void* q, void* k, void* v, int32_t H, int32_t dk,
+                                    int32_t dv, int32_t K, float eps, fork_dtype dt, void* stream);
 
 /* Projection y [M, N] = x [M, K] w [N, K]^T, or with accumulate = 1
  * y += x w^T (a residual connection folded into the product), all row-major

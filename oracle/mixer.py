@@ -143,7 +143,9 @@ def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False
     T = x.shape[0]
     H, dk, dv = W["H"], W["dk"], W["dv"]
     p = r(_lin(x, W["wqkv"], fp8))
-    c = r(conv(parent, seg_len, _f32(p), W["conv_w"], act=1))
+    # the convolution's output is normalised and split before it is stored:
+    # q, k and v are the stored (rounded) tensors
+    c = conv(parent, seg_len, _f32(p), W["conv_w"], act=1)
     ab = r(_lin(x, W["wab"], fp8))
     q, k, v, a, b = gdn_inputs(c, ab, W["a_log"], W["dt_bias"], H, dk, dv, eps)
     o, st0, st1 = gdn(parent, seg_len, _f32(r(q)), _f32(r(k)), _f32(r(v)), _f32(a), _f32(b),

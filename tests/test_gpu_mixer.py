@@ -268,3 +268,36 @@ def test_rope_copy_parity(dtype, theta, nh, D, extra):
     else:
         import oracle
         check_close(f"rope from strided source {dtype} D={D}", host(out), oracle.rope(parent, seg_len, x, theta=theta), dtype)
+
+
+@pytest.mark.parametrize("dtype,H,dk,K,state", [("bf16", 16, 128, 4, False), ("f32", 3, 64, 3, True),
+                                                ("bf16", 2, 32, 8, True), ("f32", 1, 8, 2, False)])
+def test_conv_inputs_parity(dtype, H, dk, K, state):
+    """The convolution + L2 norm + split in one pass against the oracle's
+    convolution followed by its Gated DeltaNet input split, on a forest with
+    1-2-token segments (windows that cross several ancestors)."""
+    import oracle
+    rng, parent, seg_len = tree(110 + dk + K)
+    T = int(seg_len.sum())
+    R = int((parent < 0).sum())
+    C = 3 * H * dk
+    x = (2 * rng.standard_normal((T, C))).astype(np.float32)
+    if dtype == "bf16":
+        x = W.round_bf16(x)
+    w = (rng.standard_normal((C, K)) / np.sqrt(K)).astype(np.float32)
+    st = rng.standard_normal((R, C, K - 1)).astype(np.float32) if state else None
+    sess = session(parent, seg_len)
+    tdt = TORCH_DT[dtype]
+    q = torch.full((T, H, dk), float("nan"), device="cuda", dtype=tdt)
+    k, v = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+    from tree_structured_decision_amd import binding as B
+    B.gdn_conv_inputs_forward(sess.meta, dev(x, dtype), dev(w), None, None if st is None else dev(st), q, k, v,
+                              H, dk, dk, K, 1e-6, B.FORK_BF16 if dtype == "bf16" else B.FORK_F32)
+    torch.cuda.synchronize()
+    c = oracle.conv(parent, seg_len, x, w, conv_state=st, act=1)
+    if dtype == "bf16":
+        c = OM.to_bf16(c)  # the unfused path stores the convolution in bf16 first
+    rq, rk, rv, _, _ = OM.gdn_inputs(c, np.zeros((T, 2 * H)), np.zeros(H), np.zeros(H), H, dk, dk, 1e-6)
+    check_close(f"conv+inputs q {dtype}", host(q), rq, dtype)
+    check_close(f"conv+inputs k {dtype}", host(k), rk, dtype)
+    check_close(f"conv+inputs v {dtype}", host(v), rv, dtype)

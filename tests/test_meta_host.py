@@ -433,3 +433,21 @@ def test_rope_copy_argument_errors_without_gpu():
     assert rc(src=0x10002) == -1                   # misaligned
     assert rc(dst=0x10000 + 512) == -1             # overlapping
     assert rc(src=None) == -1
+
+
+def test_conv_inputs_argument_errors_without_gpu():
+    parent, seg_len = np.array([-1, 0], np.int32), np.array([4, 2], np.int32)
+    meta, _, _ = plan(parent, seg_len, gqa=2)
+    meta.dev = 0x1000
+    meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
+    f = 0x2000
+    ci = lambda H=2, dk=64, dv=64, K=4, eps=1e-6, w=0x3000, q=0x4000: _status(
+        lambda: B.gdn_conv_inputs_forward(meta, f, w, None, None, q, 0x5000, 0x6000, H, dk, dv, K, eps,
+                                          B.FORK_BF16, stream=0))
+    assert ci(dk=64, dv=32) == -3 and ci(dk=48, dv=48) == -3 and ci(dk=1024, dv=1024) == -3
+    assert ci(K=9) == -3 and ci(K=1) == -3
+    assert ci(w=0x3004) == -1 and ci(eps=0.0) == -1 and ci(H=0) == -1
+    assert ci(q=f) == -1 and ci(q=None) == -1
+    # gdn_inputs without c needs only ab, the gate parameters and a, b
+    assert _status(lambda: B.gdn_inputs_forward(meta, None, f, 0x3000, 0x4000, None, None, None, None, 0x5000,
+                                                2, 64, 64, 1e-6, B.FORK_BF16, stream=0)) == -1  # a is null

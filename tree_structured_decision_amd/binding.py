@@ -26,7 +26,7 @@ EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_bui
            "fork_meta_plan_ctx", "fork_meta_export",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
-           "fork_gate_forward", "gdn_inputs_forward", "fork_linear_forward",
+           "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
            "fork_quantize_fp8", "fork_linear_fp8_forward",
            "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
             "fork_gate_forward": [P(fork_meta), vp, vp, ctypes.c_int64, vp, vp, i32, i32, i32, f32, i32, vp],
             "gdn_inputs_forward": [P(fork_meta), vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                    f32, i32, vp],
+            "gdn_conv_inputs_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                        i32, vp],
             "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, i32, vp],
             "fork_quantize_fp8": [vp, vp, vp, ctypes.c_int64, i32, i32, vp],
             "fork_linear_fp8_forward": [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
@@ -289,6 +291,13 @@ def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H:
     _check(lib().gdn_inputs_forward(ctypes.byref(meta), _ptr(c), _ptr(ab), ld_ab, _ptr(a_log),
                                     _ptr(dt_bias), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), H,
                                     dk, dv, float(eps), dt, _stream(stream)))
+
+
+def gdn_conv_inputs_forward(meta: fork_meta, x, w, bias, conv_state, q, k, v, H: int, dk: int, dv: int,
+                            K: int, eps: float, dt: int, stream=None) -> None:
+    _check(lib().gdn_conv_inputs_forward(ctypes.byref(meta), _ptr(x), _ptr(w), _ptr(bias), _ptr(conv_state),
+                                         _ptr(q), _ptr(k), _ptr(v), H, dk, dv, K, float(eps), dt,
+                                         _stream(stream)))
 
 
 def fork_linear_forward(x, w, y, M: int, N: int, K: int, accumulate: int, dt: int, stream=None) -> None:

@@ -111,6 +111,21 @@ __global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __res
 // token the root's convolution state supplies the inputs (or zeros).
 constexpr int kConvThreads = 256;
 
+// Gated DeltaNet input split (SPLIT = true): channels [0, Cq) are the query
+// heads, [Cq, 2 Cq) the key heads, the rest the value heads, each head G * 8
+// channels wide; query and key heads are L2-normalised after the activation,
+// x / sqrt(|x|^2 + eps), and the three parts go to separate [T, heads, dk]
+// arrays. The G lanes holding one head's channels for a token run are
+// consecutive and aligned (the per-token channel groups are a multiple of
+// G), and all follow the same run, so the norm is a G-lane shuffle sum.
+struct ConvSplit {
+  void* yk;
+  void* yv;
+  int Cq;
+  int G;
+  float eps;
+};
+
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* __restrict__ base, long long off, float* v) {
   if constexpr (BF16) {
@@ -133,13 +148,13 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, long long o
 
 constexpr int kConvRun = 8;
 
-template <bool BF16, int K>
+template <bool BF16, int K, bool SPLIT>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __restrict__ blob,
                                                             const void* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             const float* __restrict__ state,
-                                                            void* __restrict__ y, int C, int act) {
+                                                            void* __restrict__ y, int C, int act, ConvSplit sp) {
   const int T = blob[MH_T];
   const int32_t* __restrict__ tok_seg = blob + blob[MH_OFF_TOKSEG];
   const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
@@ -214,13 +229,30 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __res
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = acc[e] / (1.f + __expf(-acc[e]));
       }
+      void* out = y;
+      long long orow = (long long)t * C + c0;
+      if constexpr (SPLIT) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += acc[e] * acc[e];
+        for (int o = sp.G >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        const int region = c0 < sp.Cq ? 0 : (c0 < 2 * sp.Cq ? 1 : 2);
+        if (region < 2) {
+          const float r = 1.f / sqrtf(ss + sp.eps);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] *= r;
+        }
+        out = region == 0 ? y : (region == 1 ? sp.yk : sp.yv);
+        orow = region == 2 ? (long long)t * (C - 2 * sp.Cq) + (c0 - 2 * sp.Cq)
+                           : (long long)t * sp.Cq + (c0 - region * sp.Cq);
+      }
       if constexpr (BF16) {
         u32x4_t o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = f_to_bf16(acc[2 * e]) | ((unsigned)f_to_bf16(acc[2 * e + 1]) << 16);
-        *(u32x4_t*)((unsigned short*)y + (long long)t * C + c0) = o;
+        *(u32x4_t*)((unsigned short*)out + orow) = o;
       } else {
-        float* o = (float*)y + (long long)t * C + c0;
+        float* o = (float*)out + orow;
         *(f32x4_t*)o = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
         *(f32x4_t*)(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
       }
@@ -252,35 +284,45 @@ fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, v
   return FORK_OK;
 }
 
-template <bool BF16, int K>
+template <bool BF16, int K, bool SPLIT>
 fork_status launch_conv_k(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
-                          void* y, int C, int act, hipStream_t stream) {
+                          void* y, int C, int act, ConvSplit sp, hipStream_t stream) {
   const long long threads = (long long)((m->caps.t_cap + kConvRun - 1) / kConvRun) * (C / 8);
   const int grid = stream_grid(threads, kConvThreads);
-  hipLaunchKernelGGL((conv_kernel<BF16, K>), dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev, x, w,
-                     bias, state, y, C, act);
+  hipLaunchKernelGGL((conv_kernel<BF16, K, SPLIT>), dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev,
+                     x, w, bias, state, y, C, act, sp);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
 
-template <bool BF16>
+template <bool BF16, bool SPLIT>
 fork_status launch_conv_t(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
-                          void* y, int C, int K, int act, hipStream_t stream) {
+                          void* y, int C, int K, int act, ConvSplit sp, hipStream_t stream) {
   switch (K) {
-    case 2: return launch_conv_k<BF16, 2>(m, x, w, bias, state, y, C, act, stream);
-    case 3: return launch_conv_k<BF16, 3>(m, x, w, bias, state, y, C, act, stream);
-    case 4: return launch_conv_k<BF16, 4>(m, x, w, bias, state, y, C, act, stream);
-    case 5: return launch_conv_k<BF16, 5>(m, x, w, bias, state, y, C, act, stream);
-    case 6: return launch_conv_k<BF16, 6>(m, x, w, bias, state, y, C, act, stream);
-    case 7: return launch_conv_k<BF16, 7>(m, x, w, bias, state, y, C, act, stream);
-    default: return launch_conv_k<BF16, 8>(m, x, w, bias, state, y, C, act, stream);
+    case 2: return launch_conv_k<BF16, 2, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    case 3: return launch_conv_k<BF16, 3, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    case 4: return launch_conv_k<BF16, 4, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    case 5: return launch_conv_k<BF16, 5, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    case 6: return launch_conv_k<BF16, 6, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    case 7: return launch_conv_k<BF16, 7, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
+    default: return launch_conv_k<BF16, 8, SPLIT>(m, x, w, bias, state, y, C, act, sp, stream);
   }
 }
 
 fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias, const float* state,
                         void* y, int C, int K, int act, fork_dtype dt, hipStream_t stream) {
-  if (dt == FORK_BF16) return launch_conv_t<true>(m, x, w, bias, state, y, C, K, act, stream);
-  return launch_conv_t<false>(m, x, w, bias, state, y, C, K, act, stream);
+  const ConvSplit none{nullptr, nullptr, 0, 1, 0.f};
+  if (dt == FORK_BF16) return launch_conv_t<true, false>(m, x, w, bias, state, y, C, K, act, none, stream);
+  return launch_conv_t<false, false>(m, x, w, bias, state, y, C, K, act, none, stream);
+}
+
+fork_status launch_conv_split(const fork_meta* m, const void* x, const float* w, const float* bias,
+                              const float* state, void* q, void* k, void* v, int H, int dk, int dv, int K, float eps,
+                              fork_dtype dt, hipStream_t stream) {
+  const int C = 2 * H * dk + H * dv;
+  const ConvSplit sp{k, v, H * dk, dk / 8, eps};
+  if (dt == FORK_BF16) return launch_conv_t<true, true>(m, x, w, bias, state, q, C, K, 1, sp, stream);
+  return launch_conv_t<false, true>(m, x, w, bias, state, q, C, K, 1, sp, stream);
 }
 
 }  // namespace fork

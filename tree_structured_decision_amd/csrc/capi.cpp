@@ -616,8 +616,8 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
   g_err[0] = 0;
   fork_status st = check_meta(m);
   if (st) return st;
-  if (!c || !ab || !a_log || !dt_bias || !q || !k || !v || !a || !b)
-    return fail(FORK_E_ARG, "every pointer must be non-null");
+  if (!ab || !a_log || !dt_bias || !a || !b) return fail(FORK_E_ARG, "ab, a_log, dt_bias, a and b must be non-null");
+  if (c && (!q || !k || !v)) return fail(FORK_E_ARG, "q, k and v must be non-null when c is given");
   if (H < 1) return fail(FORK_E_ARG, "H=%d", H);
   if (dk < 8 || dk > 1024 || dk % 8 || dv < 8 || dv > 1024 || dv % 8)
     return fail(FORK_E_UNSUPPORTED, "head sizes dk=%d dv=%d unsupported (multiples of 8, 8..1024)", dk, dv);
@@ -627,6 +627,24 @@ fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab
   if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
   return launch_gdn_inputs(m, c, ab, (long long)ld_ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt,
                            (hipStream_t)stream);
+}
+
+fork_status gdn_conv_inputs_forward(const fork_meta* m, const void* x, const float* w, const float* bias,
+                                    const float* conv_state, void* q, void* k, void* v, int32_t H, int32_t dk,
+                                    int32_t dv, int32_t K, float eps, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!x || !w || !q || !k || !v) return fail(FORK_E_ARG, "x, w, q, k and v must be non-null");
+  if (H < 1) return fail(FORK_E_ARG, "H=%d", H);
+  if (dk != dv || dk < 8 || dk > 512 || (dk & (dk - 1)))
+    return fail(FORK_E_UNSUPPORTED, "head sizes dk=%d dv=%d (equal, a power of two in 8..512)", dk, dv);
+  if (K < 2 || K > 8) return fail(FORK_E_UNSUPPORTED, "kernel width %d unsupported (2..8)", K);
+  if ((uintptr_t)w % 16) return fail(FORK_E_ARG, "w must be 16-byte aligned");
+  if (!(eps > 0.f)) return fail(FORK_E_ARG, "eps must be > 0");
+  if (x == q || x == k || x == v) return fail(FORK_E_ARG, "x must not overlap the outputs");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_conv_split(m, x, w, bias, conv_state, q, k, v, H, dk, dv, K, eps, dt, (hipStream_t)stream);
 }
 
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,

@@ -168,6 +168,9 @@ fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, v
 fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias,
                         const float* state, void* y, int C, int K, int act, fork_dtype dt,
                         hipStream_t stream);
+fork_status launch_conv_split(const fork_meta* m, const void* x, const float* w, const float* bias,
+                              const float* state, void* q, void* k, void* v, int H, int dk, int dv, int K, float eps,
+                              fork_dtype dt, hipStream_t stream);
 fork_status launch_gate(const fork_meta* m, const void* x, const void* g, long long ldg, const float* w, void* y,
                         int nh, int D, int mode, float eps, fork_dtype dt, hipStream_t stream);
 fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, long long ld_ab, const float* a_log,

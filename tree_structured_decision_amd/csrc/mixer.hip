@@ -126,8 +126,9 @@ __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __rest
 }
 
 // One (token, head) row per group of L lanes: c [T, 2 H dk + H dv] holds
-// the convolved query, key and value heads side by side; ab the decay and
-// write-strength projections of token t at ab + t ld_ab (2 H values).
+// the convolved query, key and value heads side by side (null: the
+// convolution already wrote q, k and v, only a and b are formed); ab the
+// decay and write-strength projections of token t at ab + t ld_ab (2 H values).
 template <bool BF16>
 __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     const int32_t* __restrict__ blob, const void* c, const void* ab, const float* __restrict__ a_log,
@@ -146,7 +147,7 @@ __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     const size_t cq = (size_t)t * cw + (size_t)h * dk, ck = cq + (size_t)H * dk,
                  cv = (size_t)t * cw + (size_t)2 * H * dk + (size_t)h * dv;
     float sq = 0.f, sk = 0.f;
-    if (live)
+    if (live && c)
       for (int j = li; j < dk / 8; j += L) {
         float vq[8], vk[8];
         load8<BF16>(c, cq + 8 * j, vq);
@@ -161,7 +162,7 @@ __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     sk = group_sum(sk, L);
     if (!live) continue;
     const float rq = 1.f / sqrtf(sq + eps), rk = 1.f / sqrtf(sk + eps);
-    for (int j = li; j < dk / 8; j += L) {
+    for (int j = li; c && j < dk / 8; j += L) {
       float vq[8], vk[8];
       load8<BF16>(c, cq + 8 * j, vq);
       load8<BF16>(c, ck + 8 * j, vk);
@@ -173,7 +174,7 @@ __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
       store8<BF16>(q, (size_t)r * dk + 8 * j, vq);
       store8<BF16>(k, (size_t)r * dk + 8 * j, vk);
     }
-    for (int j = li; j < dv / 8; j += L) {
+    for (int j = li; c && j < dv / 8; j += L) {
       float vv[8];
       load8<BF16>(c, cv + 8 * j, vv);
       store8<BF16>(v, (size_t)r * dv + 8 * j, vv);
@@ -297,7 +298,7 @@ fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long
 fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab, long long ld_ab, const float* a_log,
                               const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int H, int dk,
                               int dv, float eps, fork_dtype dt, hipStream_t stream) {
-  const int L = lanes_per_row(dk < dv ? dk : dv);
+  const int L = c ? lanes_per_row(dk < dv ? dk : dv) : 1;  // decay / strength only: a lane per row
   const int grid = row_grid((long long)m->caps.t_cap * H, L);
   const int32_t* blob = (const int32_t*)m->dev;
   if (dt == FORK_BF16)

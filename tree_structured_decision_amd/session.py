@@ -115,10 +115,11 @@ class ForkSession:
                    ld_ab: int = 0):
         """Gated DeltaNet inputs from the convolved projections c [T, 2 H dk + H dv]
         and the decay / write-strength projections ab [T, 2 H] (or, with ld_ab, a
-        device address whose token rows are ld_ab elements apart)."""
+        device address whose token rows are ld_ab elements apart). c None: only a
+        and b (q, k, v come from gdn_conv_inputs_forward)."""
         T, H, dk = q.shape
         dv = v.shape[2]
-        dt = B.FORK_BF16 if c.dtype == torch.bfloat16 else B.FORK_F32
+        dt = B.FORK_BF16 if q.dtype == torch.bfloat16 else B.FORK_F32
         B.gdn_inputs_forward(self.meta, c, ab, a_log, dt_bias, q, k, v, a, b, H, dk, dv, eps, dt,
                              stream=stream, ld_ab=ld_ab)
 
@@ -230,7 +231,7 @@ class ForkSession:
         T, dm = x.shape
         H, dk, dv = W["H"], W["dk"], W["dv"]
         C = 2 * H * dk + H * dv
-        b = self._bufs(bufs, x, dict(p=(T, C), c=(T, C), ab=(T, 2 * H), q=(T, H, dk), k=(T, H, dk),
+        b = self._bufs(bufs, x, dict(p=(T, C), ab=(T, 2 * H), q=(T, H, dk), k=(T, H, dk),
                                      v=(T, H, dv), o=(T, H, dv), z=(T, H, dv), u=(T, H, dv),
                                      y=(T, dm)))
         for n, shape in (("a", (T, H)), ("b", (T, H))):
@@ -256,9 +257,13 @@ class ForkSession:
             self._proj(fp8, xin, "wab", W, b["ab"], stream)
             self._proj(fp8, xin, "wz", W, b["z"].view(T, H * dv), stream)
             z, ld_z, ab, ld_ab = b["z"], 0, b["ab"], 0
-        self.conv(b["p"], W["conv_w"], b["c"], act=1, stream=stream)
-        self.gdn_inputs(b["c"], ab, W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"],
-                        b["b"], eps, stream, ld_ab=ld_ab)
+        # convolution + SiLU + L2-normalised q / k heads, written straight to q, k, v;
+        # then the decay and write strength
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.gdn_conv_inputs_forward(self.meta, b["p"], W["conv_w"], None, None, b["q"], b["k"], b["v"], H, dk, dv,
+                                  W["conv_w"].shape[1], eps, dt, stream=stream)
+        self.gdn_inputs(None, ab, W["a_log"], W["dt_bias"], b["q"], b["k"], b["v"], b["a"], b["b"], eps, stream,
+                        ld_ab=ld_ab)
         self.gdn(b["q"], b["k"], b["v"], b["a"], b["b"], b["o"], st, scale=dk ** -0.5, stream=stream)
         self.gate(b["o"], z, W["norm_w"], b["u"], 1, eps, stream, ld_g=ld_z)
         uin = self._proj_in(fp8, b["u"].view(T, H * dv), b, "u", stream)
