@@ -174,6 +174,8 @@ class ForkSession:
     def _proj_in(self, fp8, x, b, key, stream):
         if not fp8:
             return x
+        if x.dtype != torch.bfloat16:
+            raise ValueError("FP8 projections write bf16: the mixer's activations must be bf16")
         q = b.get(key + "_q")
         if q is None or q.shape != x.shape:
             q = None
