@@ -329,7 +329,8 @@ fork_status gdn_conv_inputs_forward(const fork_meta* m, const void* x, const flo
  * workspace, kept for the process. The first call per (M, N, K, dt) times
  * the heuristic's candidate algorithms once on its operands (into a scratch
  * output it allocates and frees; it synchronises the stream) and keeps the
- * fastest. Calls are serialised by a lock. */
+ * fastest, so make that first call outside any graph capture. Calls are
+ * serialised by a lock. */
 fork_status fork_linear_forward(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K,
                                 int32_t accumulate, fork_dtype dt, void* stream);
 
