@@ -194,18 +194,19 @@ def test_stack_with_silent_layers_is_the_final_norm():
     assert np.allclose(h, ref, rtol=1e-12, atol=1e-12)
 
 
-def test_stack_equals_isolated_paths():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_stack_equals_isolated_paths(fp8):
     rng = np.random.default_rng(19)
     parent, seg_len = W.random_tree(rng, 8, 6, max_depth=4)
     seg_len[rng.integers(0, 8, 3)] = 1
     T = int(seg_len.sum())
     layers, fn, _ = W.stack_weights(20, 32, H=4, Hkv=2, D=16, gH=2, dk=16, dv=16, dtype="f32")
     x = W.mixer_input(21, T, 32, "f32").astype(np.float64)
-    h = M.stack(parent, seg_len, x, layers, fn)
+    h = M.stack(parent, seg_len, x, layers, fn, fp8=fp8)
     start = np.concatenate([[0], np.cumsum(seg_len)[:-1]])
     for leaf in [s for s in range(len(parent)) if not (parent == s).any()]:
         rows = np.concatenate([np.arange(start[s], start[s] + seg_len[s]) for s in path_segments(parent, leaf)])
-        hi = M.stack(np.array([-1], np.int32), np.array([len(rows)], np.int32), x[rows], layers, fn)
+        hi = M.stack(np.array([-1], np.int32), np.array([len(rows)], np.int32), x[rows], layers, fn, fp8=fp8)
         assert np.allclose(h[rows], hi, rtol=1e-9, atol=1e-9)
 
 
