@@ -276,3 +276,42 @@ def test_fp8_mixers_equal_isolated_paths():
         one = (np.array([-1], np.int32), np.array([len(rows)], np.int32))
         assert np.allclose(ya[rows], M.attention_mixer(*one, x[rows], Wt["attn"], fp8=True), rtol=1e-9, atol=1e-9)
         assert np.allclose(yg[rows], M.gdn_mixer(*one, x[rows], Wt["gdn"], fp8=True), rtol=1e-9, atol=1e-9)
+
+
+def _mutant_gate(x, g, w, mode, eps=1e-6):
+    # silu replaced by sigmoid in the gated norm
+    x = np.asarray(x, np.float64)
+    if mode == 0:
+        return x * M.sigmoid(g)
+    r = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(w, np.float64)
+    return r * M.sigmoid(g) if mode == 1 else r
+
+
+def _mutant_encode(t):
+    # truncation instead of nearest-even rounding
+    t = np.asarray(t, np.float64)
+    a = np.abs(t)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    normal = a >= 2.0 ** -6
+    m = np.where(normal, np.floor((a / np.ldexp(1.0, e) - 1.0) * 8.0), np.floor(a / 2.0 ** -9)).astype(np.int64)
+    ef = np.where(normal, e + 7, 0)
+    return ((np.signbit(t).astype(np.int64) << 7) | (ef << 3) | m).astype(np.uint8)
+
+
+@pytest.mark.parametrize("name,attr,mutant,pin", [
+    ("silu -> sigmoid in the gated norm", "gate", _mutant_gate, "test_rms_norm_properties"),
+    ("softplus sign flipped", "softplus", lambda x: np.logaddexp(0.0, -np.asarray(x, np.float64)),
+     "test_gdn_inputs_properties"),
+    ("bf16 ties away from zero", "to_bf16",
+     lambda x: (lambda m, e: np.ldexp(np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5) / 256.0, e))(*np.frexp(np.asarray(x, np.float64))),
+     "test_to_bf16_ties_and_bit_rounding"),
+    ("e4m3 truncation", "e4m3_encode", _mutant_encode, "test_e4m3_codes_from_the_format_definition"),
+    ("residual dropped", "_out", lambda r, u, wo, residual, fp8=False: r(M._lin(u, wo, fp8)),
+     "test_stack_with_silent_layers_is_the_final_norm"),
+])
+def test_pins_catch_planted_mistakes(monkeypatch, name, attr, mutant, pin):
+    """Each planted mistake in the mixer oracle makes a pin fail (the mistake
+    is planted in the oracle, on the CPU)."""
+    monkeypatch.setattr(M, attr, mutant)
+    with pytest.raises(AssertionError):
+        globals()[pin]()
