@@ -45,9 +45,6 @@ PEAK_FP8_MFMA = 5.0e15
 PEAK_F32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12            # B/s
 SEED_MIXER = 2048             # seed of the mixer weights and input
-# capacity buckets for graph replay (tokens, segments)
-BUCKETS_T = [1 << 16, 1 << 17, 1 << 18, 3 << 17, 1 << 19]
-BUCKETS_S = [1 << 9, 1 << 12, 1 << 13]
 
 
 def log(msg):
@@ -171,14 +168,6 @@ def measured_peaks():
 
 # ------------------------------------------------------------------ runners
 
-def pick_bucket(T, S):
-    for tc in BUCKETS_T:
-        for sc in BUCKETS_S:
-            if T <= tc and S <= sc:
-                return tc, sc
-    return int(T), int(S)
-
-
 class Runner:
     """Device buffers and one step of the path for one workload."""
 
@@ -191,8 +180,10 @@ class Runner:
         T, S = wl_meta["T"], wl_meta["S"]
         depth = wl_meta["depth"]
         if graph:
+            from tree_structured_decision_amd.session import BUCKET_DEPTH, pick_bucket
+
             t_cap, s_cap = pick_bucket(T, S)
-            depth_cap = max(3, depth)
+            depth_cap = max(BUCKET_DEPTH, depth)
         else:
             t_cap, s_cap, depth_cap = T, S, depth
         self.caps = (t_cap, s_cap, depth_cap)

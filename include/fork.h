@@ -50,8 +50,19 @@ typedef enum {
   FORK_E_UNSUPPORTED = -3,  /* head size or dtype with no kernel in the library */
   FORK_E_WORKSPACE = -4,    /* workspace or staging buffer too small */
   FORK_E_CAPACITY = -5,     /* tree larger than the capacities the blob was sized for */
-  FORK_E_HIP = -6           /* a HIP runtime call failed */
+  FORK_E_HIP = -6,          /* a HIP runtime call failed */
+  FORK_E_DEVICE = -7        /* a kernel found the blob unusable (fork_meta_check) */
 } fork_status;
+
+/* Bits of the device error word of a metadata blob (fork_meta_check). Every
+ * kernel that reads a blob first checks its header against the capacities
+ * the launch was made for; on a mismatch the kernel sets a bit and exits
+ * without reading or writing anything else, so the outputs keep their old
+ * contents. fork_meta_build clears the word. */
+#define FORK_DEVERR_MAGIC 1     /* the blob holds no built metadata */
+#define FORK_DEVERR_CAPACITY 2  /* the blob's tree exceeds the launch's capacities (e.g. a
+                                   graph recorded for one bucket replayed on a blob rebuilt
+                                   with larger capacities: its workspaces would overflow) */
 
 typedef enum { FORK_F32 = 0, FORK_BF16 = 1 } fork_dtype;
 
@@ -165,6 +176,15 @@ fork_status fork_meta_plan_ctx(const int32_t* parent_h, const int32_t* seg_len_h
 /* Copy one metadata array (FORK_ARR_*) from the device into dst_h (int32,
  * T or S entries). Synchronises the stream. For tests. */
 fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_h, void* stream);
+
+/* Reads the blob's device error word (FORK_DEVERR_* bits, 0 if no kernel
+ * reported a problem since the last fork_meta_build) into *device_error_h
+ * (may be null). Returns FORK_E_DEVICE if the word is nonzero, FORK_OK
+ * otherwise. Synchronises the stream (so every launch enqueued before it on
+ * `stream` has run). Argument validation happens on the host before any
+ * launch; this word covers what only the kernels can see, such as a blob
+ * rewritten or rebuilt behind a recorded graph. */
+fork_status fork_meta_check(const fork_meta* m, int32_t* device_error_h, void* stream);
 
 /* Dense [T, T] uint8 visibility mask computed on the GPU from the device
  * metadata: mask[t*T + j] = 1 iff token t attends to token j. T <= 8192.

@@ -3,9 +3,13 @@ input and compare with the oracle under the stated tolerances.
 
 Tolerances (max over every output element):
 * fp32 inputs and outputs: |gpu - oracle| <= 1e-4;
-* bf16 inputs and outputs, fp32 accumulation: |gpu - oracle| minus half a
-  bf16 ulp of the value (the rounding any bf16 output must pay) <= 2e-2; fp32
-  outputs of bf16 runs (log-sum-exp, states): |gpu - oracle| <= 2e-2.
+* bf16 inputs and outputs, fp32 accumulation: plain |gpu - oracle| <= 2e-2 on
+  every element whose exact value is below 8 in magnitude. At |value| >= 8 half
+  a bf16 ulp is 1/32 > 2e-2, so a correctly rounded result could not meet the
+  plain bar there: those elements get 2e-2 plus half a bf16 ulp of the value,
+  and their count and largest error in bf16 ulps are printed beside the
+  plain max-abs; fp32 outputs of bf16 runs (log-sum-exp, states):
+  |gpu - oracle| <= 2e-2.
 """
 import numpy as np
 import torch
@@ -54,17 +58,29 @@ def run_hip(wl, *, attn=True, gdn=True, sess=None, final=True, device="cuda", sp
 
 def check_close(name, got, ref, dtype, kind="out", rows=None):
     """kind: 'out' for outputs stored in the workload dtype, 'f32' for fp32
-    outputs (lse, states)."""
+    outputs (lse, states). Returns the plain max-abs error."""
     if rows is not None:
         got, ref = got[rows], ref[rows]
     assert np.isfinite(got).all(), f"{name}: non-finite values (unwritten output?)"
-    if kind == "out" and dtype == "bf16":
-        err = metrics.excess_error(got, ref, "bf16")
-    else:
-        err = np.abs(got - ref)
+    assert np.isfinite(ref).all(), f"{name}: non-finite reference values (unselected rows?)"
+    tol = TOL[dtype]
+    err = np.abs(got - ref)
     m = float(err.max()) if err.size else 0.0
-    log(f"  {name}: max err {m:.3e} (tol {TOL[dtype]:.0e}) over {err.size} values")
-    assert m <= TOL[dtype], f"{name}: max error {m} > {TOL[dtype]}"
+    if kind == "out" and dtype == "bf16":
+        big = np.abs(ref) >= 8.0
+        small_max = float(err[~big].max()) if (~big).any() else 0.0
+        msg = f"  {name}: max-abs {m:.3e} (|ref| < 8: {small_max:.3e}, tol {tol:.0e}) over {err.size} values"
+        if big.any():
+            ulp = 2.0 * metrics.bf16_half_ulp(ref[big])
+            in_ulps = err[big] / ulp
+            msg += f"; {int(big.sum())} values with |ref| >= 8, max error {float(in_ulps.max()):.3f} bf16 ulp"
+            excess = float((err[big] - ulp / 2).max())
+            assert excess <= tol, f"{name}: error at |ref| >= 8 exceeds 2e-2 + half a bf16 ulp by {excess - tol}"
+        log(msg)
+        assert small_max <= tol, f"{name}: max error {small_max} > {tol} where |ref| < 8"
+    else:
+        log(f"  {name}: max-abs {m:.3e} (tol {tol:.0e}) over {err.size} values")
+        assert m <= tol, f"{name}: max error {m} > {tol}"
     return m
 
 

@@ -17,7 +17,7 @@ from tests.gpu_helpers import check_close, log, oracle_attn, oracle_gdn, run_hip
 from tree_structured_decision_amd import binding as B
 from tree_structured_decision_amd import metrics
 from tree_structured_decision_amd import workloads as W
-from tree_structured_decision_amd.session import ForkSession, caps_for
+from tree_structured_decision_amd.session import ForkSession, caps_for, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -268,3 +268,35 @@ def test_split_and_whole_tiles_agree():
     check_close("whole attn.o", b["o"], o, wl.dtype)
     check_close("split attn.lse", a["lse"], lse, wl.dtype, kind="f32")
     check_close("whole attn.lse", b["lse"], lse, wl.dtype, kind="f32")
+
+
+# ------------------------------------------------------------- fork copy
+
+@pytest.mark.parametrize("name", ["one_request", "agent_history"])
+def test_fork_copy_is_bitwise(name):
+    """The fork writes the parent's end state into every child's start slot
+    exactly: start[c] and final[parent[c]] agree bit for bit (fp32 words) on
+    every child, at every depth (the three-level tree forks twice; its root
+    starts from the given root state, copied bit for bit too)."""
+    wl = W.WORKLOADS[name]()
+    caps = caps_for(wl.parent, wl.seg_len, wl.H // wl.Hkv, kv_heads=wl.Hkv)
+    sess = ForkSession(**caps, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv)
+    d = to_device(wl, "cuda")
+    sess.build(wl.parent, wl.seg_len)
+    go = torch.empty((wl.T, wl.gH, wl.dv), device="cuda", dtype=d["gq"].dtype)
+    st0 = torch.full((wl.S, wl.gH, wl.dv, wl.dk), float("nan"), device="cuda")
+    st1 = torch.full_like(st0, float("nan"))
+    sess.gdn(d["gq"], d["gk"], d["gv"], d["a"], d["b"], go, st0, st1, root_state=d["root_state"])
+    torch.cuda.synchronize()
+    assert sess.check() == 0
+    kids = torch.from_numpy(np.flatnonzero(wl.parent >= 0)).cuda()
+    par = torch.from_numpy(wl.parent[wl.parent >= 0].astype(np.int64)).cuda()
+    a = st0.index_select(0, kids).view(torch.int32)
+    b = st1.index_select(0, par).view(torch.int32)
+    assert torch.equal(a, b), "a child's start state differs from its parent's end state"
+    roots = np.flatnonzero(wl.parent < 0)
+    r0 = st0[torch.from_numpy(roots).cuda()]
+    want = torch.zeros_like(r0) if d["root_state"] is None else d["root_state"]
+    assert torch.equal(r0.view(torch.int32), want.contiguous().view(torch.int32))
+    log(f"  {name}: {len(kids)} children start from their parent's end state, bit for bit")
+    sess.close()

@@ -242,6 +242,34 @@ def test_plan_errors():
     assert "staging" in B.fork_last_error()
 
 
+def test_capacities_whose_blob_needs_over_2_31_words_are_rejected():
+    """The header keeps int32 word offsets: capacities whose blob would reach
+    2^31 words are refused at the size query (and so at every later call),
+    not accepted with offsets that wrap."""
+    assert _status(lambda: B.fork_meta_size(B.make_caps(1 << 29, 1 << 10, 4, ATTN_ROWS))) == -5
+    assert "2^31" in B.fork_last_error()
+    dev, _ = B.fork_meta_size(B.make_caps(1 << 20, 1 << 12, 4, 8))  # a large bucket still fits
+    assert dev < (1 << 33)
+
+
+def test_meta_check_argument_errors_without_gpu():
+    """fork_meta_check validates its descriptor on the host before any HIP call."""
+    assert _status(lambda: B.fork_meta_check(B.fork_meta(), stream=0)) == -1  # zero caps, no blob
+    meta, _, _ = plan([-1, 0], [4, 2], gqa=2)
+    assert meta.dev is None  # a plan has no device blob
+    assert _status(lambda: B.fork_meta_check(meta, stream=0)) == -1
+    assert "device blob" in B.fork_last_error()
+
+
+def test_device_error_bits_match_header():
+    """The binding's FORK_DEVERR_* values and FORK_E_DEVICE are the header's."""
+    header = open(os.path.join(ROOT, "include", "fork.h")).read()
+    assert int(re.search(r"#define FORK_DEVERR_MAGIC (\d+)", header).group(1)) == B.FORK_DEVERR_MAGIC
+    assert int(re.search(r"#define FORK_DEVERR_CAPACITY (\d+)", header).group(1)) == B.FORK_DEVERR_CAPACITY
+    assert int(re.search(r"FORK_E_DEVICE = (-\d+)", header).group(1)) == -7
+    assert B.STATUS[-7] == "FORK_E_DEVICE"
+
+
 def test_forward_argument_errors_without_gpu():
     """Argument errors come back before any HIP call, so they work on a host
     without a GPU (the device pointer below is never dereferenced)."""

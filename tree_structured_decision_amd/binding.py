@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(HERE, "libforkattn.so")
 
 FORK_F32, FORK_BF16 = 0, 1
 STATUS = {0: "FORK_OK", -1: "FORK_E_ARG", -2: "FORK_E_TREE", -3: "FORK_E_UNSUPPORTED",
-          -4: "FORK_E_WORKSPACE", -5: "FORK_E_CAPACITY", -6: "FORK_E_HIP"}
+          -4: "FORK_E_WORKSPACE", -5: "FORK_E_CAPACITY", -6: "FORK_E_HIP", -7: "FORK_E_DEVICE"}
+FORK_DEVERR_MAGIC, FORK_DEVERR_CAPACITY = 1, 2
 (ARR_TOK_SEG, ARR_TOK_POS, ARR_TOK_ISO_POS, ARR_SEG_START, ARR_DEPTH, ARR_ANC_LEN, ARR_ROOT,
  ARR_CTX_START, ARR_CTX_LEN) = range(9)
 
 # every symbol include/fork.h declares
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
-           "fork_meta_plan_ctx", "fork_meta_export",
+           "fork_meta_plan_ctx", "fork_meta_export", "fork_meta_check",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
@@ -91,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "fork_meta_plan_ctx": [vp, vp, vp, vp, i32, P(fork_caps), vp, sz, P(sz), P(fork_meta)],
             "fork_meta_export": [P(fork_meta), i32, vp, vp],
             "fork_meta_dense_mask": [P(fork_meta), vp, vp],
+            "fork_meta_check": [P(fork_meta), P(i32), vp],
             "fork_attn_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "fork_attn_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, f32, i32,
                                   vp, sz, vp],
@@ -221,6 +223,16 @@ def fork_meta_build_ctx(parent, seg_len, ctx_start, ctx_len, caps: fork_caps, de
 
 def fork_meta_export(meta: fork_meta, array_id: int, dst, stream=None) -> None:
     _check(lib().fork_meta_export(ctypes.byref(meta), int(array_id), _ptr(dst), _stream(stream)))
+
+
+def fork_meta_check(meta: fork_meta, stream=None, raise_on_error: bool = True) -> int:
+    """The blob's device error word (FORK_DEVERR_* bits); raises ForkError
+    (FORK_E_DEVICE) when it is nonzero, unless raise_on_error is False."""
+    word = ctypes.c_int32(0)
+    st = lib().fork_meta_check(ctypes.byref(meta), ctypes.byref(word), _stream(stream))
+    if st != 0 and (raise_on_error or st != -7):
+        _check(st)
+    return int(word.value)
 
 
 def fork_meta_dense_mask(meta: fork_meta, mask, stream=None) -> None:

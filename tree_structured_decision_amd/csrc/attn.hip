@@ -102,6 +102,7 @@ struct AttnArgs {
   float* lse;
   unsigned char* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
   int32_t* ctr;  // the blob's work counters: next item per XCD (8), finished workgroups
+  BlobGuard guard;
   int H, Hkv, G;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -292,6 +293,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
   __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds2[BF16 ? C::BUF_BYTES : 16];
 
+  if (!blob_ok(blob, args.guard)) return;  // (before any other blob access; no counter touched)
   const int ntiles = blob[MH_NTILES];
   const int TT = blob[MH_TILE_TOKENS];
   const AttnTile* __restrict__ tiles = (const AttnTile*)(blob + blob[MH_OFF_TILES]);
@@ -743,6 +745,7 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
   constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;  // bytes per partial slot
   constexpr int NRG = kAttnRows / kMergeRows;  // row groups per tile
   constexpr int C4 = D / 4 / 16;               // 4-column groups per thread
+  if (!blob_ok(blob, args.guard)) return;
   const int nmerge = blob[MH_NMERGE];
   const int TT = blob[MH_TILE_TOKENS];
   const AttnMerge* __restrict__ merges = (const AttnMerge*)(blob + blob[MH_OFF_MERGE]);
@@ -851,6 +854,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
   a.lse = lse;
   a.ws = (unsigned char*)ws;
   a.ctr = (int32_t*)m->dev + kAttnCtrWord;
+  a.guard = blob_guard(m->caps);
   a.H = H;
   a.Hkv = Hkv;
   a.G = H / Hkv;

@@ -42,8 +42,9 @@ constexpr int kMaxRopeD = 256;
 template <bool BF16>
 __global__ void __launch_bounds__(kRopeThreads) rope_kernel(const int32_t* __restrict__ blob, const void* src,
                                                             long long ld_src, void* dst, int nh, int D,
-                                                            double log2_theta, int rotate) {
+                                                            double log2_theta, int rotate, BlobGuard guard) {
   __shared__ double inv_freq[kMaxRopeD / 2];
+  if (!blob_ok(blob, guard)) return;
   const int half = D / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x) inv_freq[i] = exp2(-(2.0 * i / D) * log2_theta);
   __syncthreads();
@@ -154,7 +155,9 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(const int32_t* __res
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias,
                                                             const float* __restrict__ state,
-                                                            void* __restrict__ y, int C, int act, ConvSplit sp) {
+                                                            void* __restrict__ y, int C, int act, ConvSplit sp,
+                                                            BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
   const int T = blob[MH_T];
   const int32_t* __restrict__ tok_seg = blob + blob[MH_OFF_TOKSEG];
   const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
@@ -276,10 +279,10 @@ fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, v
   const double l2t = rotate ? log2((double)theta) : 0.0;
   if (dt == FORK_BF16)
     hipLaunchKernelGGL(rope_kernel<true>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, src,
-                       ld_src, dst, nh, D, l2t, rotate);
+                       ld_src, dst, nh, D, l2t, rotate, blob_guard(m->caps));
   else
     hipLaunchKernelGGL(rope_kernel<false>, dim3(grid), dim3(kRopeThreads), 0, stream, (const int32_t*)m->dev, src,
-                       ld_src, dst, nh, D, l2t, rotate);
+                       ld_src, dst, nh, D, l2t, rotate, blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
@@ -290,7 +293,7 @@ fork_status launch_conv_k(const fork_meta* m, const void* x, const float* w, con
   const long long threads = (long long)((m->caps.t_cap + kConvRun - 1) / kConvRun) * (C / 8);
   const int grid = stream_grid(threads, kConvThreads);
   hipLaunchKernelGGL((conv_kernel<BF16, K, SPLIT>), dim3(grid), dim3(kConvThreads), 0, stream, (const int32_t*)m->dev,
-                     x, w, bias, state, y, C, act, sp);
+                     x, w, bias, state, y, C, act, sp, blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

@@ -66,6 +66,12 @@ static fork_status check_caps(const fork_caps* c) {
     return fail(FORK_E_ARG, "kv_heads %d out of range [0, %d]", c->kv_heads, kMaxPartSlots);
   if (c->ctx_cap < 0 || c->ctx_cap > (1 << 29))
     return fail(FORK_E_ARG, "ctx_cap %d out of range [0, 2^29]", c->ctx_cap);
+  // the header stores the arrays' word offsets (and the kernels index the
+  // blob) in int32: the whole blob must stay below 2^31 words
+  const BlobLayout L = blob_layout(*c);
+  if (L.total_words >= ((int64_t)1 << 31))
+    return fail(FORK_E_CAPACITY, "capacities t_cap %d, s_cap %d, gqa_group %d need a blob of %lld words (limit 2^31)",
+                c->t_cap, c->s_cap, c->gqa_group, (long long)L.total_words);
   return FORK_OK;
 }
 
@@ -449,6 +455,22 @@ fork_status fork_meta_export(const fork_meta* m, int32_t array_id, int32_t* dst_
                                 hipMemcpyDeviceToHost, s));
   FORK_HIP_CHECK(hipStreamSynchronize(s));
   return FORK_OK;
+}
+
+fork_status fork_meta_check(const fork_meta* m, int32_t* device_error_h, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t word = 0;
+  FORK_HIP_CHECK(hipMemcpyAsync(&word, (const int32_t*)m->dev + kErrWord, sizeof(word), hipMemcpyDeviceToHost, s));
+  FORK_HIP_CHECK(hipStreamSynchronize(s));
+  if (device_error_h) *device_error_h = word;
+  if (word == 0) return FORK_OK;
+  return fail(FORK_E_DEVICE, "a kernel stopped on this blob: %s%s(device error word 0x%x)",
+              (word & FORK_DEVERR_MAGIC) ? "it holds no built metadata; " : "",
+              (word & FORK_DEVERR_CAPACITY) ? "its tree exceeds the capacities the launch was made for; " : "",
+              (unsigned)word);
 }
 
 fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream) {

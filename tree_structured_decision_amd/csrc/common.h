@@ -55,13 +55,16 @@ enum MetaHeader : int {
   MH_NCTX,            // roots with a nonempty context
   MH_WORDS = 64
 };
+// Header word 57 is the device error word (FORK_DEVERR_* bits, fork_meta_check).
+constexpr int kErrWord = 57;
 // Header words 48..56 hold the attention work counters: the next work item of
 // each of the 8 XCDs (workgroup id mod 8), then the number of workgroups that
 // found no more work. They are zero in a freshly built blob and the kernel
 // leaves them zero.
 constexpr int kAttnCtrWord = 48;
 constexpr int kNumXcd = 8;
-static_assert(kAttnCtrWord > MH_KV_HEADS && kAttnCtrWord + kNumXcd < MH_WORDS, "counter words inside the header");
+static_assert(kAttnCtrWord > MH_NCTX && kAttnCtrWord + kNumXcd < kErrWord && kErrWord < MH_WORDS,
+              "counter and error words inside the header, past the plan's words");
 
 
 constexpr int32_t kMetaMagic = 0x464B4D31;  // "FKM1"
@@ -128,6 +131,44 @@ inline BlobLayout blob_layout(const fork_caps& c) {
   L.tok_off_words = L.upload_cap_words;
   L.total_words = L.tok_off_words + 3 * (((int64_t)c.t_cap + 63) / 64 * 64);
   return L;
+}
+
+// What a launch assumes about the blob it reads: the capacities its grids and
+// workspaces were sized for. Every kernel checks the blob's header against
+// it before touching anything else (blob_ok), so a blob that was rebuilt with
+// larger capacities, or overwritten, behind a recorded graph stops the
+// kernel instead of overflowing a workspace.
+struct BlobGuard {
+  int32_t t_cap, s_cap, depth_cap, tile_cap, chunk_cap;
+};
+inline BlobGuard blob_guard(const fork_caps& c) {
+  const BlobLayout L = blob_layout(c);
+  BlobGuard g;
+  g.t_cap = c.t_cap;
+  g.s_cap = c.s_cap;
+  g.depth_cap = c.depth_cap;
+  g.tile_cap = (int32_t)L.tile_cap;
+  g.chunk_cap = (int32_t)L.chunk_cap;
+  return g;
+}
+
+// True when the blob's header fits the guard. Otherwise thread 0 of the
+// workgroup sets the error bit in the header's error word (a vector atomic)
+// and the caller returns at once. Header words are uniform (scalar loads).
+__device__ __forceinline__ bool blob_ok(const int32_t* __restrict__ blob, const BlobGuard& g) {
+  int err = 0;
+  if (blob[MH_MAGIC] != kMetaMagic) {
+    err = FORK_DEVERR_MAGIC;
+  } else {
+    const int T = blob[MH_T], S = blob[MH_S], d = blob[MH_MAXDEPTH];
+    const int nt = blob[MH_NTILES], nc = blob[MH_NCHUNKS];
+    if (T < 1 || T > g.t_cap || S < 1 || S > g.s_cap || d < 0 || d > g.depth_cap || nt < 0 ||
+        nt > g.tile_cap || nc < 0 || nc > g.chunk_cap)
+      err = FORK_DEVERR_CAPACITY;
+  }
+  if (err == 0) return true;
+  if (threadIdx.x == 0 && threadIdx.y == 0) atomicOr((int*)blob + kErrWord, err);
+  return false;
 }
 
 // ---------------------------------------------------------------------------

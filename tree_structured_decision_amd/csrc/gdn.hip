@@ -145,6 +145,7 @@ struct GdnArgs {
   float* seg_start;
   float* seg_final;
   unsigned char* ws;
+  BlobGuard guard;
   int H;
   float scale;
   int level;
@@ -271,6 +272,7 @@ __global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
   __shared__ __attribute__((aligned(16))) float gsb[2][CH];
   __shared__ __attribute__((aligned(16))) float bsb[2][CH];
 
+  if (!blob_ok(blob, args.guard)) return;
   const int nchunks = blob[MH_NCHUNKS];
   const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
   const int H = args.H;
@@ -758,6 +760,7 @@ __global__ void __launch_bounds__((ScanCfg<BF16, DK>::NT)) gdn_scan_kernel(const
   constexpr bool SPLIT = BF16;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::NBUF * C::BUF_BYTES];
 
+  if (!blob_ok(blob, args.guard)) return;
   const int level = args.level;
   const bool planned = args.lv_first >= 0;
   if (!planned && level > blob[MH_MAXDEPTH]) return;
@@ -1242,6 +1245,7 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   __shared__ u32x2_t rx[2][4][64];       // R blocks (hi, lo)
   __shared__ u32x2_t ux[4][4][64];       // U blocks (hi, lo), U' blocks (hi, lo)
 
+  if (!blob_ok(blob, args.guard)) return;
   const int level = args.level;
   const bool planned = args.lv_first >= 0;
   if (!planned && level > blob[MH_MAXDEPTH]) return;
@@ -1698,6 +1702,7 @@ fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const v
   g.seg_start = seg_start_state;
   g.seg_final = seg_final_state;
   g.ws = (unsigned char*)ws;
+  g.guard = blob_guard(m->caps);
   g.H = H;
   g.scale = scale;
   g.level = 0;

@@ -10,7 +10,8 @@
 namespace fork {
 
 // One workgroup per segment (grid-stride); threads stride over its tokens.
-__global__ void __launch_bounds__(256) meta_expand_kernel(int32_t* __restrict__ blob) {
+__global__ void __launch_bounds__(256) meta_expand_kernel(int32_t* __restrict__ blob, BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
   const int32_t* hdr = blob;
   const int S = hdr[MH_S];
   const int32_t* seg_len = blob + hdr[MH_OFF_SEGLEN];
@@ -45,7 +46,8 @@ __device__ inline bool visible(const int32_t* blob, int t, int j) {
 }
 
 __global__ void __launch_bounds__(256) dense_mask_kernel(const int32_t* __restrict__ blob,
-                                                         uint8_t* __restrict__ mask) {
+                                                         uint8_t* __restrict__ mask, BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
   const int T = blob[MH_T];
   const int64_t n = (int64_t)T * T;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -60,7 +62,7 @@ fork_status launch_meta_expand(const fork_meta* m, hipStream_t stream) {
   // the capacity.
   const int S = stream_capturing(stream) ? m->caps.s_cap : m->num_segments;
   const int grid = S < 4096 ? S : 4096;
-  hipLaunchKernelGGL(meta_expand_kernel, dim3(grid), dim3(256), 0, stream, (int32_t*)m->dev);
+  hipLaunchKernelGGL(meta_expand_kernel, dim3(grid), dim3(256), 0, stream, (int32_t*)m->dev, blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
@@ -69,8 +71,11 @@ fork_status launch_dense_mask(const fork_meta* m, uint8_t* mask, hipStream_t str
   const int64_t n = (int64_t)m->num_tokens * m->num_tokens;
   int64_t grid = (n + 255) / 256;
   if (grid > 65536) grid = 65536;
+  // the mask holds the descriptor's T x T entries: the blob's tree must not be larger
+  BlobGuard g = blob_guard(m->caps);
+  g.t_cap = m->num_tokens;
   hipLaunchKernelGGL(dense_mask_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const int32_t*)m->dev, mask);
+                     (const int32_t*)m->dev, mask, g);
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

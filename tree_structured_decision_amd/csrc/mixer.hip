@@ -80,7 +80,9 @@ __device__ __forceinline__ float group_sum(float s, int L) {
 template <bool BF16, int MODE>
 __global__ void __launch_bounds__(kMixThreads) gate_kernel(const int32_t* __restrict__ blob, const void* x,
                                                            const void* g, long long ldg, const float* __restrict__ w,
-                                                           void* y, int nh, int D, int L, float eps) {
+                                                           void* y, int nh, int D, int L, float eps,
+                                                           BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
   const long long rows = (long long)blob[MH_T] * nh;
   const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L, nc = D / 8;
   const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -133,7 +135,8 @@ template <bool BF16>
 __global__ void __launch_bounds__(kMixThreads) gdn_inputs_kernel(
     const int32_t* __restrict__ blob, const void* c, const void* ab, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, void* q, void* k, void* v, float* __restrict__ a, float* __restrict__ b, int H,
-    int dk, int dv, long long ld_ab, int L, float eps) {
+    int dk, int dv, long long ld_ab, int L, float eps, BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
   const long long rows = (long long)blob[MH_T] * H;
   const int lane = threadIdx.x & 63, li = lane & (L - 1), rpw = 64 / L;
   const size_t cw = (size_t)2 * H * dk + (size_t)H * dv;
@@ -264,11 +267,14 @@ fork_status launch_gate_t(const fork_meta* m, const void* x, const void* g, long
   const int grid = row_grid((long long)m->caps.t_cap * nh, L);
   const int32_t* blob = (const int32_t*)m->dev;
   if (mode == 0)
-    hipLaunchKernelGGL((gate_kernel<BF16, 0>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 0>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps,
+                       blob_guard(m->caps));
   else if (mode == 1)
-    hipLaunchKernelGGL((gate_kernel<BF16, 1>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 1>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps,
+                       blob_guard(m->caps));
   else
-    hipLaunchKernelGGL((gate_kernel<BF16, 2>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps);
+    hipLaunchKernelGGL((gate_kernel<BF16, 2>), dim3(grid), dim3(kMixThreads), 0, stream, blob, x, g, ldg, w, y, nh, D, L, eps,
+                       blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }
@@ -303,10 +309,10 @@ fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab,
   const int32_t* blob = (const int32_t*)m->dev;
   if (dt == FORK_BF16)
     hipLaunchKernelGGL(gdn_inputs_kernel<true>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
-                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps);
+                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps, blob_guard(m->caps));
   else
     hipLaunchKernelGGL(gdn_inputs_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
-                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps);
+                       q, k, v, a, b, H, dk, dv, ld_ab, L, eps, blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

@@ -62,15 +62,3 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     ax = np.abs(np.asarray(x, np.float64))
     e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
-
-
-def excess_error(test: np.ndarray, ref: np.ndarray, out_dtype: str) -> np.ndarray:
-    """|test - ref| beyond what storing ref in the output dtype must cost.
-
-    For bf16 outputs an exact value can be off by up to half a bf16 ulp after
-    rounding; that part is subtracted before the tolerance is applied. For
-    fp32 outputs the plain absolute error is returned."""
-    d = np.abs(np.asarray(test, np.float64) - np.asarray(ref, np.float64))
-    if out_dtype == "bf16":
-        d = np.maximum(d - bf16_half_ulp(np.maximum(np.abs(test), np.abs(ref))), 0.0)
-    return d

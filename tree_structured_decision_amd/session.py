@@ -68,6 +68,11 @@ class ForkSession:
         self.events[i] = ev
         return self.meta
 
+    def check(self, stream=None, raise_on_error: bool = True) -> int:
+        """Device error word of the blob (synchronises the stream); raises
+        ForkError (FORK_E_DEVICE) when a kernel stopped on the blob."""
+        return B.fork_meta_check(self.meta, stream=stream, raise_on_error=raise_on_error)
+
     # -- layers -------------------------------------------------------------
     def attention(self, q, k, v, o, lse=None, scale: float = 0.0, stream=None, kc=None, vc=None):
         """kc / vc: key/value cache of resumed contexts [ctx_cap, Hkv, D] (required when the
@@ -374,6 +379,22 @@ class ForkSession:
             pass
 
 
+# Capacity buckets of recorded graphs (tokens x segments; depth capacity 3):
+# a compact set of fixed shapes that every request mix is padded into.
+BUCKETS_T = [1 << 16, 1 << 17, 1 << 18, 3 << 17, 1 << 19]
+BUCKETS_S = [1 << 9, 1 << 12, 1 << 13]
+BUCKET_DEPTH = 3
+
+
+def pick_bucket(T: int, S: int):
+    """The smallest bucket (t_cap, s_cap) that holds T tokens and S segments."""
+    for tc in BUCKETS_T:
+        for sc in BUCKETS_S:
+            if T <= tc and S <= sc:
+                return tc, sc
+    return int(T), int(S)
+
+
 def caps_for(parent, seg_len, gqa_group: int, t_cap=None, s_cap=None, depth_cap=None,
              kv_heads: int = 0, ctx_cap: int = 0):
     """Exact capacities of one tree (eager use)."""
@@ -395,3 +416,48 @@ def to_device(wl, device="cuda"):
                a=t(wl.a, torch.float32), b=t(wl.b, torch.float32))
     out["root_state"] = None if wl.root_state is None else t(wl.root_state, torch.float32)
     return out
+
+
+def request_mix_to_device(seed: int, t_cap: int = 0, device="cuda", threads: int = 8,
+                          n_requests: int = 64, out: dict = None):
+    """The request mix of PCG64 seed `seed` (workloads.request_mix: tree and
+    readout from the seed, each request's tensors from its own child stream)
+    drawn request by request on the host (a thread pool draws ahead) and
+    copied into device tensors of t_cap rows (at least T; rows past T are
+    zero). out: existing tensors (e.g. a recorded graph's) to fill instead.
+    Returns (parent, seg_len, tensors, readout vectors); the host never holds
+    more than a few requests' values."""
+    import concurrent.futures as cf
+
+    from . import workloads as W
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    parent, seg_len = W.request_mix_tree(rng, n_requests)
+    w = (W._normal(rng, (16 * 128,)), W._normal(rng, (16 * 128,)))
+    T = int(np.sum(seg_len))
+    n = max(T, int(t_cap))
+    bf = torch.bfloat16
+    z = lambda *s, d=bf: torch.zeros(*s, dtype=d, device=device)
+    if out is None:
+        out = dict(q=z(n, 16, 128), k=z(n, 2, 128), v=z(n, 2, 128), gq=z(n, 16, 128), gk=z(n, 16, 128),
+                   gv=z(n, 16, 128), a=z(n, 16, d=torch.float32), b=z(n, 16, d=torch.float32),
+                   root_state=None)
+    else:
+        for name in ("q", "k", "v", "gq", "gk", "gv", "a", "b"):
+            assert out[name].shape[0] >= T, f"{name} holds {out[name].shape[0]} rows < T = {T}"
+            out[name][T:].zero_()
+    spans = W.request_spans(parent, seg_len)
+    window = 2 * max(1, threads)  # requests drawn ahead of the copies
+    with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        draw = lambda r: ex.submit(W.request_mix_request, seed, r, parent, seg_len, n_requests)
+        futs = [draw(r) for r in range(min(window, len(spans)))]
+        for r, (a, b, t0, t1) in enumerate(spans):
+            wl = futs[r].result()
+            futs[r] = None
+            if r + window < len(spans):
+                futs.append(draw(r + window))
+            d = to_device(wl, device)
+            for name in ("q", "k", "v", "gq", "gk", "gv", "a", "b"):
+                out[name][t0:t1].copy_(d[name])
+            del wl, d
+    return parent, seg_len, out, w

@@ -32,9 +32,16 @@ SEED_BASE = 1000
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); float32 out."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("round_bf16 takes finite values")
+    # finite floats have bit patterns <= 0xFF7FFFFF, so adding at most 0x8000
+    # stays below 2^32 in uint32 arithmetic
+    u = x.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -147,11 +154,12 @@ def _sigmoid32(x: np.ndarray) -> np.ndarray:
 def make_workload(name: str, dtype: str, parent, seg_len, *, H, Hkv, D, gH, dk, dv,
                   gates: str, root_state_std: Optional[float], seed: int,
                   rng: Optional[np.random.Generator] = None,
-                  description: str = "") -> Workload:
+                  description: str = "", readout: bool = True) -> Workload:
     """Draw every tensor of a workload for a given tree.
 
     gates == "uniform": a ~ U(0.9, 1), b ~ U(0, 1).
     gates == "sigmoid": a = sigmoid(N(3, 0.5)), b = sigmoid(N(0, 1)).
+    readout: draw the readout vectors last (False: leave them None).
     """
     if rng is None:
         rng = np.random.Generator(np.random.PCG64(seed))
@@ -177,8 +185,8 @@ def make_workload(name: str, dtype: str, parent, seg_len, *, H, Hkv, D, gH, dk, 
     if root_state_std is not None:
         root_state = (rng.standard_normal(size=(R, gH, dv, dk), dtype=np.float32)
                       * np.float32(root_state_std)).astype(np.float32)
-    w_attn = _normal(rng, (H * D,))
-    w_gdn = _normal(rng, (gH * dv,))
+    w_attn = _normal(rng, (H * D,)) if readout else None
+    w_gdn = _normal(rng, (gH * dv,)) if readout else None
     if dtype == "bf16":
         q, k, v, gq, gk, gv = (round_bf16(x) for x in (q, k, v, gq, gk, gv))
     elif dtype != "f32":
@@ -247,17 +255,58 @@ def request_mix_tree(rng: np.random.Generator, n_requests: int = 64):
     return tree_requests(prefixes, option_lens)
 
 
-def request_mix(seed: int = SEED_BASE + 5, n_requests: int = 64) -> Workload:
+def request_spans(parent, seg_len):
+    """(first segment, end segment, first token, end token) of every request of
+    a request-major forest (a root followed by its subtree)."""
+    parent = np.asarray(parent)
+    seg_len = np.asarray(seg_len, np.int64)
+    roots = np.flatnonzero(parent < 0)
+    seg_end = np.append(roots[1:], len(parent))
+    tok = np.concatenate([[0], np.cumsum(seg_len)])
+    return [(int(a), int(b), int(tok[a]), int(tok[b])) for a, b in zip(roots, seg_end)]
+
+
+def request_mix_request(seed: int, r: int, parent, seg_len, n_requests: int = 64,
+                        w=None) -> Workload:
+    """Request r of the request mix alone (its root re-indexed to segment 0):
+    its q, k, v, Gated DeltaNet q, k, v, a, b come from the r-th child stream
+    of SeedSequence(seed), in that order, so that one request's inputs can be
+    drawn without the others'. w: the mix's readout vectors (w_attn, w_gdn)."""
+    a, b, _, _ = request_spans(parent, seg_len)[r]
+    p = np.asarray(parent[a:b], np.int32)
+    p = np.where(p >= 0, p - a, -1).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(n_requests)[r]))
+    wl = make_workload(f"request_mix[{r}]", "bf16", p, np.asarray(seg_len[a:b], np.int32), H=16, Hkv=2,
+                       D=128, gH=16, dk=128, dv=128, gates="sigmoid", root_state_std=None, seed=seed,
+                       rng=rng, readout=False)
+    if w is not None:
+        wl.w_attn, wl.w_gdn = w
+    return wl
+
+
+def request_mix(seed: int = SEED_BASE + 5, n_requests: int = 64, select=None) -> Workload:
     """64 requests flattened into one stream, bf16: prefix lengths 1/P on
     256..16384, option counts 1/n on 2..256, option lengths U{4..32};
-    shapes as one_request; zero root states."""
+    shapes as one_request; zero root states. Draws: the tree and the readout
+    vectors from PCG64(seed); each request's tensors from its own child
+    stream (request_mix_request). select: request indices to keep (their
+    sub-forest, in order), or None for the whole mix."""
     rng = np.random.Generator(np.random.PCG64(seed))
     parent, seg_len = request_mix_tree(rng, n_requests)
-    return make_workload("request_mix", "bf16", parent, seg_len, H=16, Hkv=2, D=128,
-                         gH=16, dk=128, dv=128, gates="sigmoid", root_state_std=None,
-                         seed=seed, rng=rng,
-                         description="64 requests: prefixes 1/P on 256-16384, options 1/n on "
-                                     "2-256 of U{4..32} tokens, bf16, attn 16/2/128, GDN 16x128x128")
+    w = (_normal(rng, (16 * 128,)), _normal(rng, (16 * 128,)))
+    rs = range(n_requests) if select is None else list(select)
+    parts = [request_mix_request(seed, r, parent, seg_len, n_requests, w) for r in rs]
+    par, sl = [], []
+    for wl in parts:
+        par.append(np.where(wl.parent >= 0, wl.parent + sum(len(x) for x in sl), -1))
+        sl.append(wl.seg_len)
+    cat = lambda n: np.concatenate([getattr(wl, n) for wl in parts])
+    return Workload(name="request_mix", dtype="bf16", parent=np.concatenate(par).astype(np.int32),
+                    seg_len=np.concatenate(sl).astype(np.int32), H=16, Hkv=2, D=128, q=cat("q"),
+                    k=cat("k"), v=cat("v"), gH=16, dk=128, dv=128, gq=cat("gq"), gk=cat("gk"),
+                    gv=cat("gv"), a=cat("a"), b=cat("b"), root_state=None, w_attn=w[0], w_gdn=w[1],
+                    description="64 requests: prefixes 1/P on 256-16384, options 1/n on 2-256 of "
+                                "U{4..32} tokens, bf16, attn 16/2/128, GDN 16x128x128")
 
 
 WORKLOADS = {
