@@ -101,6 +101,7 @@ typedef struct fork_meta {
      them to skip kernel launches with no work outside graph capture) */
   int32_t level_segs[FORK_PLAN_DEPTHS];
   int32_t level_long[FORK_PLAN_DEPTHS];
+  int32_t num_attn_parts;  /* partial-result slots (per kv head) the split query tiles use */
 } fork_meta;
 
 /* Array ids for fork_meta_export. */
@@ -221,6 +222,24 @@ fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void*
                                   const void* kc, const void* vc, void* o, float* lse, int32_t H,
                                   int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fork_attn_forward_ctx without a workspace argument. The partial results of
+ * split query tiles go to a scratch array compiled into the library, one
+ * copy per GPU, FORK_ATTN_SCRATCH_BYTES bytes, held until the process ends.
+ * The call allocates nothing. It returns FORK_E_CAPACITY when the tree's
+ * split plan needs more than the array holds (num_attn_parts * Hkv slots of
+ * 256 * D output-dtype values and 256 fp32 log-sum-exps each; for the
+ * capacity bound of a stream being captured, every slot the blob may use).
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU race and must not be issued. Nothing in the array needs clearing:
+ * each slot row the merge reads is written earlier in the same call.
+ * Arguments and results are otherwise those of fork_attn_forward_ctx. */
+#define FORK_ATTN_SCRATCH_BYTES ((size_t)64 << 20)
+fork_status fork_attn_forward_noalloc(const fork_meta* m, const void* q, const void* k, const void* v,
+                                      const void* kc, const void* vc, void* o, float* lse, int32_t H,
+                                      int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* stream);
 
 /* ----------------------------------------------------------- Gated DeltaNet
  * Forked Gated DeltaNet: per head, the dv x dk state follows

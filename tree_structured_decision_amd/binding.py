@@ -25,7 +25,7 @@ FORK_DEVERR_MAGIC, FORK_DEVERR_CAPACITY = 1, 2
 # every symbol include/fork.h declares
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
            "fork_meta_plan_ctx", "fork_meta_export", "fork_meta_check",
-           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx",
+           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx", "fork_attn_forward_noalloc",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
            "fork_quantize_fp8", "fork_linear_fp8_forward",
@@ -51,7 +51,8 @@ class fork_meta(ctypes.Structure):
                 ("num_attn_tiles", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("num_attn_merges", ctypes.c_int32),
                 ("caps", fork_caps), ("dev", ctypes.c_void_p), ("dev_bytes", ctypes.c_size_t),
-                ("level_segs", ctypes.c_int32 * 32), ("level_long", ctypes.c_int32 * 32)]
+                ("level_segs", ctypes.c_int32 * 32), ("level_long", ctypes.c_int32 * 32),
+                ("num_attn_parts", ctypes.c_int32)]
 
 
 class fork_graph_args(ctypes.Structure):
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
                                   vp, sz, vp],
             "fork_attn_forward_ctx": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                       f32, i32, vp, sz, vp],
+            "fork_attn_forward_noalloc": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
             "gdn_fork_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
@@ -257,6 +259,13 @@ def fork_attn_forward_ctx(meta: fork_meta, q, k, v, kc, vc, o, lse, H: int, Hkv:
     _check(lib().fork_attn_forward_ctx(ctypes.byref(meta), _ptr(q), _ptr(k), _ptr(v), _ptr(kc),
                                        _ptr(vc), _ptr(o), _ptr(lse), H, Hkv, D, float(scale), dt,
                                        _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def fork_attn_forward_noalloc(meta: fork_meta, q, k, v, kc, vc, o, lse, H: int, Hkv: int, D: int,
+                              scale: float, dt: int, stream=None) -> None:
+    _check(lib().fork_attn_forward_noalloc(ctypes.byref(meta), _ptr(q), _ptr(k), _ptr(v), _ptr(kc),
+                                           _ptr(vc), _ptr(o), _ptr(lse), H, Hkv, D, float(scale), dt,
+                                           _stream(stream)))
 
 
 def gdn_fork_workspace(meta: fork_meta, H: int, dk: int, dv: int, dt: int) -> int:

@@ -25,6 +25,7 @@
 // the V^T operand of O^T = V^T P^T comes from transposing LDS reads; fp32
 // tiles are staged through registers, V transposed on its way to LDS.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -834,7 +835,30 @@ fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStrea
   return FORK_OK;
 }
 
+// Partial results of split query tiles for fork_attn_forward_noalloc: a
+// file-scope device array, one copy per GPU. Host code never passes the
+// array's name to a kernel (on the host it only names the symbol): it takes
+// each device's address once through hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[FORK_ATTN_SCRATCH_BYTES];
+
 }  // namespace
+
+fork_status attn_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  FORK_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(FORK_E_UNSUPPORTED, "device ordinal %d (at most 64 devices)", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    FORK_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(FORK_E_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return FORK_OK;
+}
 
 size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt) {
   return c.kv_heads > 0 ? (size_t)kMaxPartSlots * attn_slot_bytes(D, dt) : 0;

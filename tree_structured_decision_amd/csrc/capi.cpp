@@ -349,6 +349,7 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, cons
   out->num_chunks = (int32_t)nchunks;
   out->tile_tokens = TT;
   out->num_attn_merges = (int32_t)merges.size();
+  out->num_attn_parts = nslots;
   out->caps = *caps;
   for (int32_t d = 0; d <= max_depth && d < FORK_PLAN_DEPTHS; ++d) {
     out->level_segs[d] = level_off[d + 1] - level_off[d];
@@ -501,11 +502,12 @@ fork_status fork_attn_forward(const fork_meta* m, const void* q, const void* k, 
                                stream);
 }
 
-fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void* k, const void* v,
-                                  const void* kc, const void* vc, void* o, float* lse, int32_t H,
-                                  int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
-                                  size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+// Argument checks shared by the attention entry points (everything but the workspace).
+static fork_status check_attn_args(const fork_meta* m, const void* q, const void* k, const void* v,
+                                   const void* kc, const void* vc, const void* o, int32_t H, int32_t Hkv,
+                                   int32_t D, fork_dtype dt) {
   fork_status st = check_meta(m);
   if (st) return st;
   if (!q || !k || !v || !o) return fail(FORK_E_ARG, "q, k, v and o must be non-null");
@@ -523,10 +525,43 @@ fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void*
   if (m->caps.kv_heads != 0 && Hkv != m->caps.kv_heads)
     return fail(FORK_E_ARG, "Hkv=%d differs from the kv_heads %d the metadata was built for", Hkv,
                 m->caps.kv_heads);
+  return FORK_OK;
+}
+
+extern "C" {
+
+fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void* k, const void* v,
+                                  const void* kc, const void* vc, void* o, float* lse, int32_t H,
+                                  int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_attn_args(m, q, k, v, kc, vc, o, H, Hkv, D, dt);
+  if (st) return st;
   const size_t need = attn_workspace_bytes(m->caps, D, dt);
   if (need && (!ws || ws_bytes < need))
     return fail(FORK_E_WORKSPACE, "attention workspace holds %zu bytes, needs %zu", ws_bytes, need);
   return launch_attention(m, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);
+}
+
+fork_status fork_attn_forward_noalloc(const fork_meta* m, const void* q, const void* k, const void* v,
+                                      const void* kc, const void* vc, void* o, float* lse, int32_t H,
+                                      int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_attn_args(m, q, k, v, kc, vc, o, H, Hkv, D, dt);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the slots this launch may touch: the tree's split plan, or under capture
+  // (the tree may change between replays) every slot the blob can plan
+  const size_t slot = attn_slot_bytes(D, dt);
+  const int64_t parts = m->caps.kv_heads == 0 ? 0 : (stream_capturing(s) ? kMaxPartSlots / Hkv : m->num_attn_parts);
+  const size_t need = (size_t)parts * Hkv * slot;
+  if (need > FORK_ATTN_SCRATCH_BYTES)
+    return fail(FORK_E_CAPACITY, "split query tiles need %zu bytes of partial results; the scratch array holds %zu",
+                need, (size_t)FORK_ATTN_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  st = attn_scratch(&scratch);
+  if (st) return st;
+  return launch_attention(m, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, scratch, s);
 }
 
 fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv, fork_dtype dt,

@@ -201,6 +201,9 @@ inline size_t attn_slot_bytes(int D, fork_dtype dt) {
   return (size_t)kAttnRows * D * (dt == FORK_BF16 ? 2 : 4) + (size_t)kAttnRows * 4;
 }
 size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt);
+// Device address of the current GPU's copy of the attention scratch array
+// (FORK_ATTN_SCRATCH_BYTES), looked up once per device.
+fork_status attn_scratch(void** ptr);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
                              int D, float scale, fork_dtype dt, void* ws, hipStream_t stream);
