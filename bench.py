@@ -1,30 +1,34 @@
 """Benchmark of the ForkAttention hot path on one MI355X.
 
-A step is one pass of the whole path over one decision request: segment
-metadata build (host plan + upload + per-token expansion), tree attention and
-the forked Gated DeltaNet layer. The headline workload is one decision request
-(prefix 2048 + 16 options of 16-48 tokens, bf16, attention 16/2/128, Gated
-DeltaNet 16 x 128 x 128). `value` is stream tokens per second (every physical
-token counted once) with inputs resident in HBM.
+A step is one pass of the whole path over one batch of decision requests:
+segment metadata build (host plan, one upload from pinned memory, per-token
+expansion kernel) and both layers, tree attention then the forked Gated
+DeltaNet. The headline workload is the request mix: 64 decision requests
+flattened into one stream (prefix lengths 1/P on 256..16384, option counts
+1/n on 2..256, option lengths U{4..32}; bf16; attention 16 q / 2 kv heads x
+128, Gated DeltaNet 16 heads x 128 x 128), padded into a capacity bucket of
+393,216 tokens x 4,096 segments and run as replay of a graph recorded once
+for that bucket. Inputs are the seeded PCG64 draws the parity tests check,
+resident in HBM before the timed region. `value` is stream tokens per second
+(every physical token counted once).
 
 Also reported on the same JSON line:
-  roofline      the dominant kernel's algorithmic work per launch over its mean
-                launch time (HIP events on the launch stream) vs MI355X peak;
-  cpu_baseline  the CPU oracle timed on this host's cores on the same request;
-  fidelity      total-variation distance of per-option softmax scores vs the
-                float32 oracle, argmax agreement;
-  workloads     throughput of all five synthetic workloads (the request mix
-                runs as graph replay of a capacity bucket);
+  roofline      the dominant kernel (tree attention, fork_attn_kernel): its
+                algorithmic flops per launch over its mean launch time (HIP
+                events on its stream, an eager pass of the same tree) against
+                the bf16 MFMA peak; roofline_gdn the same for the Gated
+                DeltaNet layer against HBM;
+  cpu_baseline  the float32 oracle on a prefix of the mix's requests (about
+                15 s of work on every core of this host);
+  fidelity      total-variation distance of per-option softmax scores of
+                those requests against the float32 oracle;
+  layers        per-layer P50 / P95 / mean (eager) and the graph replay's;
+  workloads     all five workloads (and the resumed agent history), eager and
+                graph replay, P50 / P95, per-layer roofline fractions;
   rates         option tokens/s, isolated-equivalent tokens/s, us per option;
-  cold_cache    the layer pair's kernel times with caches evicted between steps;
-  measured_peaks  a bf16 GEMM and a device copy on this GPU, the achievable
-                peaks the roofline fraction is also given against;
-  block_ops     the fork-aware rotary embedding and short convolution;
-  mixers        both token mixers of a hybrid block (model width 2048): the
-                projections against the MFMA peak, the per-token kernels
-                against HBM;
-  stack         a four-layer hybrid stack and the option distributions' TVD
-                to the float32 oracle (computed in the CPU-baseline leg).
+  measured_peaks  a bf16 GEMM and a device copy on this GPU;
+  block_ops, mixers, stack  the hybrid-block pieces, mixers and a four-layer
+                stack on the one-request tree.
 """
 from __future__ import annotations
 
@@ -45,6 +49,7 @@ PEAK_FP8_MFMA = 5.0e15
 PEAK_F32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12            # B/s
 SEED_MIXER = 2048             # seed of the mixer weights and input
+CPU_BUDGET_S = 15.0           # CPU-baseline sample: about this much oracle work
 
 
 def log(msg):
@@ -66,19 +71,19 @@ def sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per call of `kernel` from the committed counter runs
-    (profiles/hbm_traffic.json), or None when any native source has changed
-    since those counters were taken."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per call of `kernel` on `workload` from the committed counter
+    runs (profiles/hbm_traffic.json), or None when any native source has
+    changed since those counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
-        rec = json.load(open(path))[kernel]
-    except (OSError, KeyError, ValueError):
+        rec = json.load(open(path))[workload][kernel]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if rec.get("sources_sha256") != sources_sha256():
         return None
     return dict(bytes=rec["read_bytes"] + rec["write_bytes"], read=rec["read_bytes"],
-                write=rec["write_bytes"], workload=rec["workload"], summary=rec["summary"])
+                write=rec["write_bytes"], summary=rec["summary"])
 
 
 # ------------------------------------------------------------ algorithmic work
@@ -98,8 +103,8 @@ def visible_pairs(parent, seg_len, ctx_len=None) -> int:
 
 
 def attn_work(parent, seg_len, H, Hkv, D, elt, ctx_len=None, ctx_rows=0):
-    """Algorithmic flops (visible pairs) and bytes (q, k, v, o of the stream,
-    plus the cached context's k, v read once)."""
+    """Algorithmic flops (4 D H per visible pair) and bytes (q, k, v, o of the
+    stream, plus the cached context's k, v read once)."""
     T = int(np.sum(seg_len))
     flops = 4.0 * D * H * visible_pairs(parent, seg_len, ctx_len)
     bytes_ = float(T * (2 * H + 2 * Hkv) * D * elt + ctx_rows * 2 * Hkv * D * elt)
@@ -107,11 +112,14 @@ def attn_work(parent, seg_len, H, Hkv, D, elt, ctx_len=None, ctx_rows=0):
 
 
 def gdn_work(parent, seg_len, H, dk, dv, elt, root_state: bool):
+    """Algorithmic bytes: q, k, v, o of the stream and a, b (fp32), every
+    child's start state written once (the fork copy: S - R states), and the
+    roots' given states read once when there are any."""
     T = int(np.sum(seg_len))
     S = len(parent)
     R = int(np.sum(np.asarray(parent) < 0))
-    io = T * H * ((2 * dk + 2 * dv) * elt + 8)        # q, k, v, o + a, b
-    fork = S * H * dk * dv * 4                         # every segment's start state written once
+    io = T * H * ((2 * dk + 2 * dv) * elt + 8)
+    fork = (S - R) * H * dk * dv * 4
     rs = R * H * dk * dv * 4 if root_state else 0
     return float(io + fork + rs)
 
@@ -166,22 +174,40 @@ def measured_peaks():
     return dict(bf16_gemm_tflops=gemm / 1e12, copy_gbs=copy / 1e9)
 
 
+
 # ------------------------------------------------------------------ runners
 
+def depth_of(parent):
+    parent = np.asarray(parent)
+    d = np.zeros(len(parent), np.int64)
+    for s in range(len(parent)):
+        if parent[s] >= 0:
+            d[s] = d[parent[s]] + 1
+    return int(d.max())
+
+
+def wl_meta_of(parent, seg_len, H, Hkv, D, gH, dk, dv, dtype="bf16"):
+    return dict(parent=np.asarray(parent, np.int32), seg_len=np.asarray(seg_len, np.int32),
+                T=int(np.sum(seg_len)), S=len(parent), depth=depth_of(parent), H=H, Hkv=Hkv, D=D,
+                gH=gH, dk=dk, dv=dv, dtype=dtype)
+
+
 class Runner:
-    """Device buffers and one step of the path for one workload."""
+    """Device buffers and one step of the path for one workload. graph: the
+    session is sized for the workload's capacity bucket and both layers are
+    recorded once into a graph; a step then builds the tree into the blob and
+    replays. Eager steps (also possible on a graph runner) launch both layers
+    directly, each launch sized from the host plan."""
 
     def __init__(self, wl_meta: dict, tensors: dict, graph: bool):
         import torch
-        from tree_structured_decision_amd.session import ForkSession
+        from tree_structured_decision_amd.session import BUCKET_DEPTH, ForkSession, pick_bucket
 
         self.m = wl_meta
         self.t = tensors
         T, S = wl_meta["T"], wl_meta["S"]
         depth = wl_meta["depth"]
         if graph:
-            from tree_structured_decision_amd.session import BUCKET_DEPTH, pick_bucket
-
             t_cap, s_cap = pick_bucket(T, S)
             depth_cap = max(BUCKET_DEPTH, depth)
         else:
@@ -195,30 +221,40 @@ class Runner:
         dev = "cuda"
         qd = tensors["q"].dtype
         H, D, gH, dv, dk = wl_meta["H"], wl_meta["D"], wl_meta["gH"], wl_meta["dv"], wl_meta["dk"]
+        if graph:  # inputs must span the bucket's rows
+            for n in ("q", "k", "v", "gq", "gk", "gv", "a", "b"):
+                x = tensors[n]
+                if x.shape[0] < t_cap:
+                    y = torch.zeros((t_cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+                    y[:x.shape[0]].copy_(x)
+                    tensors[n] = y
         self.o = torch.empty((t_cap, H, D), dtype=qd, device=dev)
         self.lse = torch.empty((t_cap, H), dtype=torch.float32, device=dev)
         self.go = torch.empty((t_cap, gH, dv), dtype=qd, device=dev)
         self.st0 = torch.empty((s_cap, gH, dv, dk), dtype=torch.float32, device=dev)
         self.graph = graph
-        self._build()
+        self.build()
         if graph:
             t = tensors
-            self.sess.capture(dict(q=t["q"], k=t["k"], v=t["v"], o=self.o, lse=self.lse),
+            self.sess.capture(dict(q=t["q"], k=t["k"], v=t["v"], o=self.o, lse=self.lse,
+                                   kc=t.get("kc"), vc=t.get("vc")),
                               dict(q=t["gq"], k=t["gk"], v=t["gv"], a=t["a"], b=t["b"],
                                    root_state=t.get("root_state"), o=self.go,
                                    seg_start_state=self.st0))
 
-    def _build(self):
+    def build(self):
         if self.ctx is None:
             self.sess.build(self.m["parent"], self.m["seg_len"])
         else:
             self.sess.build(self.m["parent"], self.m["seg_len"], ctx_start=self.ctx[0],
                             ctx_len=self.ctx[1])
 
-    def step(self, ev=None):
+    def step(self, ev=None, eager=False):
+        """One step; ev: three events recorded before attention, between the
+        layers (eager only) and after the Gated DeltaNet."""
         t = self.t
-        self._build()
-        if self.graph:
+        self.build()
+        if self.graph and not eager:
             if ev:
                 ev[0].record()
             self.sess.replay()
@@ -235,26 +271,35 @@ class Runner:
         if ev:
             ev[2].record()
 
+    def close(self):
+        self.sess.close()
 
-def time_runner(r: Runner, steps: int, warmup: int, evict=None):
-    """Times `steps` steps after `warmup`, twice: first the plain steps between
-    two synchronisations (the wall time per step: nothing else is enqueued),
-    then the same number of steps with HIP events around each layer (per-layer
-    durations; an event record costs a few microseconds of GPU time, so this
-    pass is not the one the wall time comes from). evict: a large device buffer
-    written before every step of the event pass (outside the events), so that
-    the step's inputs come from HBM rather than the L2 / Infinity Cache; then
-    the wall pass is skipped."""
+
+def stats_us(xs_ms):
+    x = np.asarray(xs_ms, np.float64) * 1e3
+    return dict(p50_us=float(np.percentile(x, 50)), p95_us=float(np.percentile(x, 95)),
+                mean_us=float(x.mean()))
+
+
+def time_runner(r: Runner, steps: int, warmup: int, eager: bool, evict=None):
+    """Times `steps` steps after `warmup`, twice: first plain steps between two
+    synchronisations (the wall time per step: nothing else is enqueued), then
+    the same number of steps with HIP events on the launch stream around each
+    layer (eager) or around the replay (graph): an event record costs a few
+    microseconds of GPU time, so this pass is not the one the wall time
+    comes from. evict: a large device buffer written before every step of the
+    event pass (outside the events) so that the inputs come from HBM rather
+    than the L2 / Infinity Cache; then the wall pass is skipped."""
     import torch
 
     for _ in range(warmup):
-        r.step()
+        r.step(eager=eager)
     torch.cuda.synchronize()
     wall = None
     if evict is None:
         t0 = time.perf_counter()
         for _ in range(steps):
-            r.step()
+            r.step(eager=eager)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -262,22 +307,20 @@ def time_runner(r: Runner, steps: int, warmup: int, evict=None):
     for k in range(steps):
         if evict is not None:
             evict.fill_(k & 0xff)
-        r.step(evs[k])
+        r.step(evs[k], eager=eager)
     torch.cuda.synchronize()
     if wall is None:
         wall = time.perf_counter() - t0
-    if r.graph:
-        pair = [e[0].elapsed_time(e[2]) for e in evs]
-        attn = gdn = None
-    else:
+    out = dict(ms_per_step=wall / steps * 1e3)
+    if eager:
         attn = [e[0].elapsed_time(e[1]) for e in evs]
         gdn = [e[1].elapsed_time(e[2]) for e in evs]
-        pair = [a + g for a, g in zip(attn, gdn)]
-    med = lambda x: None if x is None else float(np.median(x)) * 1e-3  # seconds
-    mean = lambda x: None if x is None else float(np.mean(x)) * 1e-3
-    return dict(wall=wall, ms_per_step=wall / steps * 1e3, attn_mean=mean(attn),
-                attn_p50=med(attn), gdn_mean=mean(gdn), gdn_p50=med(gdn), pair_p50=med(pair),
-                pair_p95=None if pair is None else float(np.percentile(pair, 95)) * 1e-3)
+        out["attention"] = stats_us(attn)
+        out["gdn"] = stats_us(gdn)
+        out["pair"] = stats_us([a + g for a, g in zip(attn, gdn)])
+    else:
+        out["pair"] = stats_us([e[0].elapsed_time(e[2]) for e in evs])
+    return out
 
 
 def tensors_from_numpy(wl):
@@ -286,63 +329,189 @@ def tensors_from_numpy(wl):
     return to_device(wl, "cuda")
 
 
-def tensors_on_device(name, parent, seg_len, H, Hkv, D, gH, dk, dv, seed, gates, root_std):
-    """Draw a workload's tensors directly on the GPU (same shapes and
-    distributions as the numpy workloads; used for the large ones where a
-    host-side draw would dominate the run)."""
+def host_threads() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# --------------------------------------------------------------- workloads
+
+def build_workload(name, threads=8):
+    """(meta dict, device tensors, host workload or None) of a named workload;
+    every input is the seeded PCG64 draw of the workloads module."""
+    from tree_structured_decision_amd import workloads as W
+    from tree_structured_decision_amd.session import request_mix_to_device
+
+    if name in ("tiny_one_level", "one_request", "wide_options", "agent_history"):
+        wl = W.WORKLOADS[name]()
+        meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv, wl.dtype)
+        meta["root_state"] = wl.root_state is not None
+        return meta, tensors_from_numpy(wl), wl
+    if name == "agent_history_resume":
+        # the agent-history request resumed from a checkpoint of its 4096-token
+        # root: that prefix's keys/values come from the cache (shared by the 8
+        # children, now roots of the stream) and its recurrent state is the
+        # children's root state; the stream holds the 8 x 512 children and the
+        # options only
+        wl = W.agent_history()
+        P = int(wl.seg_len[0])
+        parent = (wl.parent[1:] - (wl.parent[1:] >= 0)).astype(np.int32)
+        seg_len = wl.seg_len[1:].astype(np.int32)
+        roots = parent < 0
+        meta = wl_meta_of(parent, seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv, wl.dtype)
+        meta["ctx"] = (np.zeros(len(parent), np.int32), np.where(roots, P, 0).astype(np.int32), P)
+        meta["root_state"] = True
+        full = tensors_from_numpy(wl)
+        t = {n: full[n][P:].contiguous() for n in ("q", "k", "v", "gq", "gk", "gv", "a", "b")}
+        t["kc"], t["vc"] = full["k"][:P].contiguous(), full["v"][:P].contiguous()
+        t["root_state"] = full["root_state"].expand(int(roots.sum()), -1, -1, -1).contiguous()
+        return meta, t, None
+    if name == "request_mix":
+        from tree_structured_decision_amd.session import pick_bucket
+
+        rng = np.random.Generator(np.random.PCG64(W.SEED_BASE + 5))
+        p0, l0 = W.request_mix_tree(rng)
+        t_cap, _ = pick_bucket(int(l0.sum()), len(p0))  # drawn straight into the bucket's rows
+        parent, seg_len, t, w = request_mix_to_device(W.SEED_BASE + 5, t_cap, threads=threads)
+        meta = wl_meta_of(parent, seg_len, 16, 2, 128, 16, 128, 128)
+        meta["root_state"] = False
+        meta["readout"] = w
+        return meta, t, None
+    raise ValueError(name)
+
+
+def layer_fracs(meta, res):
+    """Per-layer roofline fractions of an eager timing (P50 and mean)."""
+    elt = 2 if meta["dtype"] == "bf16" else 4
+    ctx = meta.get("ctx")
+    fl, ab = attn_work(meta["parent"], meta["seg_len"], meta["H"], meta["Hkv"], meta["D"], elt,
+                       ctx_len=None if ctx is None else ctx[1], ctx_rows=0 if ctx is None else ctx[2])
+    gb = gdn_work(meta["parent"], meta["seg_len"], meta["gH"], meta["dk"], meta["dv"], elt,
+                  meta.get("root_state", False))
+    peak = PEAK_BF16_MFMA if meta["dtype"] == "bf16" else PEAK_F32_MFMA
+    a_roof = max(fl / peak, ab / PEAK_HBM)
+    g_roof = gb / PEAK_HBM
+    return dict(attn_flop=fl, attn_bytes=ab, gdn_bytes=gb, attn_roof_s=a_roof, gdn_roof_s=g_roof,
+                attn_bound="mfma" if fl / peak >= ab / PEAK_HBM else "hbm", peak_mfma=peak)
+
+
+def workload_report(meta, eager, graph):
+    f = layer_fracs(meta, eager)
+    T = meta["T"]
+    a, g = eager["attention"], eager["gdn"]
+    rep = dict(tokens=T, segments=meta["S"],
+               eager=dict(stream_tokens_per_s=T / (eager["ms_per_step"] * 1e-3),
+                          ms_per_step=eager["ms_per_step"],
+                          pair_p50_us=eager["pair"]["p50_us"], pair_p95_us=eager["pair"]["p95_us"],
+                          attn_p50_us=a["p50_us"], attn_p95_us=a["p95_us"],
+                          gdn_p50_us=g["p50_us"], gdn_p95_us=g["p95_us"]),
+               attn_tflops=f["attn_flop"] / (a["p50_us"] * 1e-6) / 1e12,
+               attn_frac=f["attn_roof_s"] / (a["p50_us"] * 1e-6), attn_bound=f["attn_bound"],
+               gdn_gbs=f["gdn_bytes"] / (g["p50_us"] * 1e-6) / 1e9,
+               gdn_hbm_frac=f["gdn_roof_s"] / (g["p50_us"] * 1e-6),
+               pair_roofline_frac=(f["attn_roof_s"] + f["gdn_roof_s"]) / (eager["pair"]["p50_us"] * 1e-6))
+    if graph is not None:
+        rep["graph"] = dict(stream_tokens_per_s=T / (graph["ms_per_step"] * 1e-3),
+                            ms_per_step=graph["ms_per_step"], pair_p50_us=graph["pair"]["p50_us"],
+                            pair_p95_us=graph["pair"]["p95_us"],
+                            pair_roofline_frac=(f["attn_roof_s"] + f["gdn_roof_s"]) /
+                            (graph["pair"]["p50_us"] * 1e-6))
+    return rep
+
+
+def run_workload(name, steps, warmup, threads):
+    """Eager and graph-replay timings of one workload (both in one capacity-
+    bucket session: eager launches are sized from the host plan)."""
     import torch
 
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    T = int(np.sum(seg_len))
-    R = int(np.sum(np.asarray(parent) < 0))
-    bf = torch.bfloat16
-    rn = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
-    q = rn(T, H, D).to(bf)
-    k = rn(T, Hkv, D).to(bf)
-    v = rn(T, Hkv, D).to(bf)
-    gq = rn(T, gH, dk).to(bf)
-    gk = rn(T, gH, dk)
-    gk = (gk / gk.norm(dim=-1, keepdim=True)).to(bf)
-    gv = rn(T, gH, dv).to(bf)
-    if gates == "uniform":
-        a = 0.9 + 0.1 * torch.rand(T, gH, generator=g, device="cuda")
-        b = torch.rand(T, gH, generator=g, device="cuda")
-    else:
-        a = torch.sigmoid(3.0 + 0.5 * rn(T, gH))
-        b = torch.sigmoid(rn(T, gH))
-    out = dict(q=q, k=k, v=v, gq=gq, gk=gk, gv=gv, a=a.contiguous(), b=b.contiguous())
-    out["root_state"] = None if root_std is None else (root_std * rn(R, gH, dv, dk)).contiguous()
-    return out
+    meta, t, _ = build_workload(name, threads)
+    r = Runner(meta, t, graph=True)
+    eager = time_runner(r, steps, warmup, eager=True)
+    graph = time_runner(r, steps, warmup, eager=False)
+    rep = workload_report(meta, eager, graph)
+    r.close()
+    del r, t
+    torch.cuda.empty_cache()
+    return rep
 
 
-def depth_of(parent):
-    parent = np.asarray(parent)
-    d = np.zeros(len(parent), np.int64)
-    for s in range(len(parent)):
-        if parent[s] >= 0:
-            d[s] = d[parent[s]] + 1
-    return int(d.max())
-
-
-def wl_meta_of(parent, seg_len, H, Hkv, D, gH, dk, dv):
-    return dict(parent=np.asarray(parent, np.int32), seg_len=np.asarray(seg_len, np.int32),
-                T=int(np.sum(seg_len)), S=len(parent), depth=depth_of(parent), H=H, Hkv=Hkv, D=D,
-                gH=gH, dk=dk, dv=dv)
+def all_workloads(steps, warmup, threads):
+    rep = {}
+    for name in ("tiny_one_level", "one_request", "wide_options", "agent_history", "agent_history_resume"):
+        log(f"workload {name}")
+        rep[name] = run_workload(name, steps, warmup, threads)
+        log(f"  {json.dumps(rep[name])}")
+    return rep
 
 
 # --------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl, threads):
+def request_cost(parent, seg_len):
+    """Relative oracle work of one request: the Gated DeltaNet recurrence runs
+    every segment's whole path (path tokens), attention its visible pairs."""
+    parent = np.asarray(parent)
+    seg_len = np.asarray(seg_len, np.int64)
+    path = np.zeros(len(parent), np.int64)
+    for s in range(len(parent)):
+        path[s] = seg_len[s] + (path[parent[s]] if parent[s] >= 0 else 0)
+    return float(path.sum()) * 6 * 128 * 128 + 2.0 * 128 * visible_pairs(parent, seg_len)
+
+
+def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads):
+    """The float32 oracle (both layers) on a prefix of the request mix's
+    requests, in stream order, about CPU_BUDGET_S seconds of work on `threads`
+    cores: the first request calibrates the cost per work unit, and the
+    prefix stops before the request that would overrun the budget. Returns
+    (cpu_baseline entry, fidelity of those requests' option softmax scores
+    against the oracle). o_gpu_rows(t0, t1) / go_gpu_rows(t0, t1): the GPU
+    outputs of stream rows [t0, t1) as float64 arrays."""
     import oracle
+    from tree_structured_decision_amd import metrics
+    from tree_structured_decision_amd import workloads as W
 
     oracle.set_threads(threads, "f32")
-    t0 = time.perf_counter()
-    o, _ = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, prec="f32")
-    go, _, _ = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b,
-                          root_state=wl.root_state, prec="f32")
-    dt = time.perf_counter() - t0
-    return dt, o, go
+    parent, seg_len = meta["parent"], meta["seg_len"]
+    spans = W.request_spans(parent, seg_len)
+    w = meta["readout"]
+    used, tokens, took, rate = [], 0, 0.0, None
+    fid_a, fid_g = [], []
+    for r, (a, b, t0, t1) in enumerate(spans):
+        cost = request_cost(np.where(parent[a:b] >= 0, parent[a:b] - a, -1), seg_len[a:b])
+        if rate is not None and took + cost / rate > CPU_BUDGET_S:
+            break
+        wl = W.request_mix_request(W.SEED_BASE + 5, r, parent, seg_len, w=w)
+        tic = time.perf_counter()
+        o, _ = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, prec="f32")
+        go, _, _ = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b, prec="f32")
+        dt = time.perf_counter() - tic
+        took += dt
+        if rate is None:
+            rate = cost / dt  # work units per second, from the first request
+        tokens += wl.T
+        used.append(r)
+        fid_a.append(metrics.decision_fidelity(o_gpu_rows(t0, t1), o, wl.w_attn, wl.parent, wl.seg_len))
+        fid_g.append(metrics.decision_fidelity(go_gpu_rows(t0, t1), go, wl.w_gdn, wl.parent, wl.seg_len))
+    agg = lambda fs: dict(groups=len(fs), tvd_max=max(f["tvd_max"] for f in fs),
+                          tvd_mean=float(np.mean([f["tvd_mean"] for f in fs])),
+                          argmax_agreement=float(np.mean([f["argmax_agreement"] for f in fs])))
+    cpu = dict(value=tokens / took, unit="tokens/s", cores=threads, kind="oracle",
+               sample=f"requests 0..{used[-1]} of the request mix ({len(used)} of {len(spans)} requests, "
+                      f"{tokens} of {meta['T']} stream tokens; both layers, float32 oracle, "
+                      f"{took:.1f} s wall on {threads} threads)",
+               cpu_model=cpu_model(), host_cores=os.cpu_count())
+    fid = dict(attention=agg(fid_a), gdn=agg(fid_g),
+               reference=f"float32 oracle, the {len(used)} requests of the CPU-baseline sample, one "
+                         "decision group per request")
+    return cpu, fid
 
 
 def cpu_stack_fidelity(wl, stack_inputs):
@@ -363,18 +532,19 @@ def cpu_stack_fidelity(wl, stack_inputs):
     return fid, fid8
 
 
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-workloads", action="store_true", help="headline workload only")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the block-piece, mixer and stack legs (kernel profiles of the step)")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache and measured-peak passes (counter runs of the warm step)")
-    ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak pass")
+    ap.add_argument("--only", default=None,
+                    help="time just this workload, eager and graph replay (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with three plain 512 MiB device copies (counter calibration)")
     args = ap.parse_args()
@@ -386,129 +556,112 @@ def main():
 
     import torch
 
-    from tree_structured_decision_amd import metrics
-    from tree_structured_decision_amd import workloads as W
-
     torch.cuda.set_device(0)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    threads = host_threads()
 
     if args.only:
-        run_one(args.only, args.steps, args.warmup)
+        print(json.dumps({args.only: run_workload(args.only, args.steps, args.warmup, threads)}), flush=True)
         calib_copy(args.calib_copy)
         return
 
-    # ---------------- headline: one decision request
-    wl = W.one_request()
-    meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
-    r = Runner(meta, tensors_from_numpy(wl), graph=False)
-    log(f"headline {wl.name}: T={wl.T} S={wl.S}; warmup {args.warmup}, steps {args.steps}")
-    res = time_runner(r, args.steps, args.warmup)
-    import torch
-    cold = None
-    if not args.no_cold:
-        evict = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cold = time_runner(r, max(10, args.steps // 2), 2, evict=evict)
-        del evict
-    T = wl.T
-    fl, ab = attn_work(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, 2)
-    gb = gdn_work(wl.parent, wl.seg_len, wl.gH, wl.dk, wl.dv, 2, wl.root_state is not None)
-    attn_ach = fl / res["attn_mean"]
-    gdn_ach = gb / res["gdn_mean"]
-    kernels = {
-        "fork_attn_forward": dict(mean_us=res["attn_mean"] * 1e6, p50_us=res["attn_p50"] * 1e6,
-                                  algorithmic_flop=fl, algorithmic_bytes=ab,
-                                  achieved_tflops=attn_ach / 1e12,
-                                  mfma_frac=attn_ach / PEAK_BF16_MFMA),
-        "gdn_fork_forward": dict(mean_us=res["gdn_mean"] * 1e6, p50_us=res["gdn_p50"] * 1e6,
-                                 algorithmic_bytes=gb, achieved_gbs=gdn_ach / 1e9,
-                                 hbm_frac=gdn_ach / PEAK_HBM),
-    }
-    if res["attn_mean"] >= res["gdn_mean"]:
-        tr = measured_traffic("fork_attn_forward")
-        roof = dict(kernel="fork_attn_forward", bound="mfma", achieved=attn_ach / 1e12,
-                    peak=PEAK_BF16_MFMA / 1e12, unit="TFLOP/s", frac=attn_ach / PEAK_BF16_MFMA,
-                    traffic=None if tr is None else tr["bytes"])
-    else:
-        tr = measured_traffic("gdn_fork_forward")
-        roof = dict(kernel="gdn_fork_forward", bound="hbm", achieved=gdn_ach / 1e9,
-                    peak=PEAK_HBM / 1e9, unit="GB/s", frac=gdn_ach / PEAK_HBM,
-                    traffic=None if tr is None else tr["bytes"])
-    roof["algorithmic_per_launch"] = fl if roof["bound"] == "mfma" else gb
-    roof["launches"] = (["fork_attn_kernel", "fork_attn_merge_kernel"] if roof["bound"] == "mfma" else
-                        ["gdn_prep_kernel", "gdn_coop_kernel", "gdn_scan_kernel"])
-    roof["note"] = ("one call of the layer, timed with HIP events on its stream; its kernels' "
-                    "rocprofv3 averages are in profiles/one_request_kernels.md")
-    kernels["fork_attn_forward"]["hbm_traffic_bytes"] = (measured_traffic("fork_attn_forward") or {}).get("bytes")
-    kernels["gdn_fork_forward"]["hbm_traffic_bytes"] = (measured_traffic("gdn_fork_forward") or {}).get("bytes")
+    # ---------------- headline: the request mix, graph replay of its bucket
+    meta, t, _ = build_workload("request_mix", threads)
+    T, S = meta["T"], meta["S"]
+    r = Runner(meta, t, graph=True)
+    log(f"headline request_mix: T={T} S={S}, bucket {r.caps}; warmup {args.warmup}, steps {args.steps}")
+    graph = time_runner(r, args.steps, args.warmup, eager=False)
+    eager = time_runner(r, args.steps, args.warmup, eager=True)
+    r.step()  # leave the graph replay's outputs in place for the fidelity check
+    torch.cuda.synchronize()
+    f = layer_fracs(meta, eager)
+    a_mean = eager["attention"]["mean_us"] * 1e-6
+    g_mean = eager["gdn"]["mean_us"] * 1e-6
+    attn_ach = f["attn_flop"] / a_mean
+    gdn_ach = f["gdn_bytes"] / g_mean
+    tr_a = measured_traffic("fork_attn_forward", "request_mix")
+    tr_g = measured_traffic("gdn_fork_forward", "request_mix")
+    roof = dict(bound="mfma", achieved=attn_ach / 1e12, peak=PEAK_BF16_MFMA / 1e12, unit="TFLOP/s",
+                frac=attn_ach / PEAK_BF16_MFMA, traffic=None if tr_a is None else tr_a["bytes"],
+                kernel="fork_attn_kernel (fork_attn_forward)",
+                algorithmic_per_launch=f["attn_flop"], launch_mean_us=a_mean * 1e6,
+                algorithmic_bytes=f["attn_bytes"],
+                note="4 D H flops per visible (query, key) pair, 1 launch per step (no split tiles on "
+                     "this tree, so no merge launch); mean duration over the timed steps, HIP events on "
+                     "the launch stream (eager launch of the same tree in the same bucket session); "
+                     "kernel trace in profiles/request_mix_kernels.md")
+    roof_g = dict(bound="hbm", achieved=gdn_ach / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
+                  frac=gdn_ach / PEAK_HBM, traffic=None if tr_g is None else tr_g["bytes"],
+                  kernel="gdn_fork_forward (gdn_prep_kernel + per-depth scans)",
+                  algorithmic_per_launch=f["gdn_bytes"], launch_mean_us=g_mean * 1e6,
+                  note="q, k, v, o, a, b of the stream and S - R fork copies of the fp32 state")
 
-    # fidelity + CPU baseline (the float32 oracle serves both)
-    o_gpu = r.o[:T].float().cpu().numpy()
-    go_gpu = r.go[:T].float().cpu().numpy()
-    cpu = None
-    fid = None
+    cpu = fid = None
     if not args.no_cpu:
-        threads = min(len(os.sched_getaffinity(0)), 16)
-        log(f"cpu baseline: fp32 oracle, {threads} threads")
-        dt, o_ref, go_ref = cpu_baseline(wl, threads)
-        cpu = dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
-                   sample=f"the whole headline request (T={T}, both layers), fp32 oracle, "
-                          f"{dt:.2f} s wall")
-        fid = dict(attention=metrics.decision_fidelity(o_gpu, o_ref, wl.w_attn, wl.parent, wl.seg_len),
-                   gdn=metrics.decision_fidelity(go_gpu, go_ref, wl.w_gdn, wl.parent, wl.seg_len),
-                   reference="float32 oracle")
-
-    n_opt, opt_tok, iso_tok = tree_rates(wl.parent, wl.seg_len)
-    step_s = res["ms_per_step"] * 1e-3
+        log(f"cpu baseline: float32 oracle on a prefix of the requests, {threads} threads")
+        ho = lambda x: (lambda t0, t1: x[t0:t1].float().cpu().numpy().astype(np.float64))
+        cpu, fid = cpu_baseline_mix(meta, ho(r.o), ho(r.go), threads)
+    n_opt, opt_tok, iso_tok = tree_rates(meta["parent"], meta["seg_len"])
+    step_s = graph["ms_per_step"] * 1e-3
     rates = dict(options=n_opt, option_tokens_per_s=opt_tok / step_s,
                  isolated_equivalent_tokens_per_s=iso_tok / step_s, us_per_option=step_s / n_opt * 1e6,
-                 note="per step (wall); isolated-equivalent = sum over options of root-to-option path length")
+                 note="per graph step (wall); isolated-equivalent = sum over options of the root-to-option "
+                      "path length")
+    layers = dict(graph_pair=graph["pair"], eager_attention=eager["attention"], eager_gdn=eager["gdn"],
+                  eager_pair=eager["pair"], eager_ms_per_step=eager["ms_per_step"],
+                  eager_stream_tokens_per_s=T / (eager["ms_per_step"] * 1e-3))
+    r.close()
+    del r, t
+    torch.cuda.empty_cache()
+
     peaks = None
-    if not args.no_cold:
+    if not args.no_peaks:
         peaks = measured_peaks()
-        if roof["bound"] == "mfma":
-            roof["frac_measured_peak"] = roof["achieved"] / peaks["bf16_gemm_tflops"]
-        else:
-            roof["frac_measured_peak"] = roof["achieved"] / peaks["copy_gbs"]
+        roof["frac_measured_peak"] = roof["achieved"] / peaks["bf16_gemm_tflops"]
+        roof_g["frac_measured_peak"] = roof_g["achieved"] / peaks["copy_gbs"]
     out = {
         "metric": METRIC,
-        "value": T / (res["ms_per_step"] * 1e-3),
+        "value": T / step_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": res["ms_per_step"],
+        "ms_per_step": graph["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "one decision request: prefix 2048 + 16 options of 16-48 tokens; "
-                               "attention 16 q / 2 kv heads, head_dim 128; Gated DeltaNet 16 heads, "
-                               "dk = dv = 128",
-                   "tokens": T, "segments": wl.S, "parallelism": "single GPU"},
+        "config": {"workload": "request_mix: 64 decision requests in one stream (prefix 1/P on 256..16384, "
+                               "options 1/n on 2..256 of U{4..32} tokens), bf16, attention 16 q / 2 kv heads "
+                               "x 128, Gated DeltaNet 16 x 128 x 128; graph replay of the 393216-token x "
+                               "4096-segment bucket; seeded PCG64 inputs (seed 1005)",
+                   "tokens": T, "segments": S, "parallelism": "single GPU"},
         "roofline": roof,
+        "roofline_gdn": roof_g,
         "cpu_baseline": cpu,
-        "kernels": kernels,
-        "layer_pair_p50_us": res["pair_p50"] * 1e6,
-        "layer_pair_p95_us": res["pair_p95"] * 1e6,
         "fidelity": fid,
+        "layers": layers,
         "rates": rates,
-        "cold_cache": None if cold is None else dict(
-            pair_p50_us=cold["pair_p50"] * 1e6, attn_p50_us=cold["attn_p50"] * 1e6,
-            gdn_p50_us=cold["gdn_p50"] * 1e6,
-            note="512 MiB written between steps (outside the kernel events) to evict the L2 and "
-                 "the Infinity Cache"),
         "measured_peaks": peaks,
     }
+    if not args.no_workloads:
+        out["workloads"] = all_workloads(max(5, args.steps // 2), 3, threads)
     if not args.no_extras:
-        out["block_ops"] = {"one_request": block_ops(wl, r.sess)}
-        out["mixers"] = {"one_request": mixer_ops(wl, r.sess)}
-        st, st_inputs = stack_ops(wl, r.sess)
+        from tree_structured_decision_amd import workloads as W
+        from tree_structured_decision_amd.session import ForkSession, caps_for
+
+        wl = W.one_request()
+        caps = caps_for(wl.parent, wl.seg_len, wl.H // wl.Hkv, kv_heads=wl.Hkv)
+        sess = ForkSession(**caps, D=wl.D, gH=wl.gH, dk=wl.dk, dv=wl.dv)
+        sess.build(wl.parent, wl.seg_len)
+        out["block_ops"] = {"one_request": block_ops(wl, sess)}
+        out["mixers"] = {"one_request": mixer_ops(wl, sess)}
+        st, st_inputs = stack_ops(wl, sess)
         if not args.no_cpu:
             st["fidelity"], st["fp8_fidelity"] = cpu_stack_fidelity(wl, st_inputs)
         out["stack"] = {"one_request": st}
-    if not args.no_workloads:
-        out["workloads"] = all_workloads(max(5, args.steps // 5), 3)
+        sess.close()
     print(json.dumps(out), flush=True)
     calib_copy(args.calib_copy)
 
@@ -749,94 +902,6 @@ def calib_copy(enabled: bool):
     log(f"calibration: 3 device copies of {n >> 20} MiB")
 
 
-def build_workload(name):
-    """(meta dict, device tensors, graph?) of a named workload."""
-    from tree_structured_decision_amd import workloads as W
-
-    if name in ("tiny_one_level", "one_request", "agent_history"):
-        wl = W.WORKLOADS[name]()
-        meta = wl_meta_of(wl.parent, wl.seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
-        meta["root_state"] = wl.root_state is not None
-        return meta, tensors_from_numpy(wl), False, wl.dtype
-    if name == "wide_options":
-        parent, seg_len = W.tree_one_level(8192, [8] * 256)
-        meta = wl_meta_of(parent, seg_len, 32, 4, 128, 16, 128, 128)
-        t = tensors_on_device(name, parent, seg_len, 32, 4, 128, 16, 128, 128, 1003, "uniform", None)
-        return meta, t, False, "bf16"
-    if name == "agent_history_resume":
-        # the agent-history request resumed from a checkpoint of its 4096-token
-        # root: that prefix's keys/values come from the cache (shared by the 8
-        # children, now roots of the stream) and its recurrent state is the
-        # children's root state; the stream holds the 8 x 512 children and the
-        # options only
-        wl = W.agent_history()
-        P = int(wl.seg_len[0])
-        parent = (wl.parent[1:] - (wl.parent[1:] >= 0)).astype(np.int32)
-        seg_len = wl.seg_len[1:].astype(np.int32)
-        roots = parent < 0
-        meta = wl_meta_of(parent, seg_len, wl.H, wl.Hkv, wl.D, wl.gH, wl.dk, wl.dv)
-        meta["ctx"] = (np.zeros(len(parent), np.int32), np.where(roots, P, 0).astype(np.int32), P)
-        meta["root_state"] = True
-        full = tensors_from_numpy(wl)
-        t = {n: full[n][P:].contiguous() for n in ("q", "k", "v", "gq", "gk", "gv", "a", "b")}
-        t["kc"], t["vc"] = full["k"][:P].contiguous(), full["v"][:P].contiguous()
-        t["root_state"] = full["root_state"].expand(int(roots.sum()), -1, -1, -1).contiguous()
-        return meta, t, False, wl.dtype
-    if name == "request_mix":
-        rng = np.random.Generator(np.random.PCG64(W.SEED_BASE + 5))
-        parent, seg_len = W.request_mix_tree(rng)
-        meta = wl_meta_of(parent, seg_len, 16, 2, 128, 16, 128, 128)
-        t = tensors_on_device(name, parent, seg_len, 16, 2, 128, 16, 128, 128, 1005, "sigmoid", None)
-        return meta, t, True, "bf16"
-    raise ValueError(name)
-
-
-def workload_report(name, meta, res, graph, dtype):
-    elt = 2 if dtype == "bf16" else 4
-    ctx = meta.get("ctx")
-    fl, ab = attn_work(meta["parent"], meta["seg_len"], meta["H"], meta["Hkv"], meta["D"], elt,
-                       ctx_len=None if ctx is None else ctx[1], ctx_rows=0 if ctx is None else ctx[2])
-    gb = gdn_work(meta["parent"], meta["seg_len"], meta["gH"], meta["dk"], meta["dv"], elt,
-                  meta.get("root_state", False))
-    peak = PEAK_BF16_MFMA if dtype == "bf16" else PEAK_F32_MFMA
-    roof_t = max(fl / peak, ab / PEAK_HBM) + gb / PEAK_HBM
-    pair = res["pair_p50"]
-    rep = dict(tokens=meta["T"], segments=meta["S"], graph=graph,
-               stream_tokens_per_s=meta["T"] / (res["ms_per_step"] * 1e-3),
-               layer_pair_p50_us=pair * 1e6,
-               layer_pair_tokens_per_s=meta["T"] / pair,
-               pair_roofline_frac=roof_t / pair)
-    if not graph:
-        rep.update(attn_p50_us=res["attn_p50"] * 1e6, gdn_p50_us=res["gdn_p50"] * 1e6,
-                   attn_frac=max(fl / peak, ab / PEAK_HBM) / res["attn_p50"],
-                   attn_tflops=fl / res["attn_p50"] / 1e12,
-                   gdn_hbm_frac=(gb / PEAK_HBM) / res["gdn_p50"])
-    return rep
-
-
-def all_workloads(steps, warmup):
-    import torch
-
-    rep = {}
-    for name in ("tiny_one_level", "one_request", "wide_options", "agent_history",
-                 "agent_history_resume", "request_mix"):
-        log(f"workload {name}")
-        meta, t, graph, dtype = build_workload(name)
-        r = Runner(meta, t, graph)
-        res = time_runner(r, steps, warmup)
-        rep[name] = workload_report(name, meta, res, graph, dtype)
-        log(f"  {rep[name]}")
-        r.sess.close()
-        del r, t
-        torch.cuda.empty_cache()
-    return rep
-
-
-def run_one(name, steps, warmup):
-    meta, t, graph, dtype = build_workload(name)
-    r = Runner(meta, t, graph)
-    res = time_runner(r, steps, warmup)
-    print(json.dumps({name: workload_report(name, meta, res, graph, dtype)}), flush=True)
 
 
 if __name__ == "__main__":
