@@ -329,6 +329,41 @@ def tensors_from_numpy(wl):
     return to_device(wl, "cuda")
 
 
+def fp8_scores(r: Runner, meta, steps, warmup):
+    """Tree attention with FP8 scores (E4M3 q and k with per-row scales on the
+    FP8 matrix cores, bf16 values) on the runner's tree: the row quantisation
+    runs once outside the timed launches (HIP events on the launch stream,
+    eager). Returns the timing and the output (for the fidelity check)."""
+    import torch
+
+    t = r.t
+    T, H, D, Hkv = meta["T"], meta["H"], meta["D"], meta["Hkv"]
+    q8, qs = r.sess.quantize_fp8(t["q"][:T].reshape(T * H, D))
+    k8, ks = r.sess.quantize_fp8(t["k"][:T].reshape(T * Hkv, D))
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), device="cuda")
+    r.build()
+    run = lambda: r.sess.attention_qk8(q8.view(T, H, D), qs.view(T, H), k8.view(T, Hkv, D), ks.view(T, Hkv),
+                                       t["v"], o, lse)
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    fl = attn_work(meta["parent"], meta["seg_len"], H, Hkv, D, 2)[0]
+    qk_share = 0.5  # QK^T and PV have equal flops: half at the fp8 peak, half at the bf16 peak
+    roof = fl * qk_share / PEAK_FP8_MFMA + fl * (1 - qk_share) / PEAK_BF16_MFMA
+    return dict(p50_us=st["p50_us"], p95_us=st["p95_us"], mean_us=st["mean_us"],
+                achieved_tflops=fl / (st["mean_us"] * 1e-6) / 1e12, roofline_frac=roof / (st["mean_us"] * 1e-6),
+                note="fork_attn_forward_qk8, eager; roofline: QK^T flops at the fp8 peak (5.0 PFLOP/s), PV flops at "
+                     "the bf16 peak; fidelity against the float32 oracle on the unquantised inputs is in "
+                     "fidelity.attention_fp8_scores", o=o)
+
+
 def host_threads() -> int:
     return len(os.sched_getaffinity(0))
 
@@ -466,7 +501,7 @@ def request_cost(parent, seg_len):
     return float(path.sum()) * 6 * 128 * 128 + 2.0 * 128 * visible_pairs(parent, seg_len)
 
 
-def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads):
+def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None):
     """The float32 oracle (both layers) on a prefix of the request mix's
     requests, in stream order, about CPU_BUDGET_S seconds of work on `threads`
     cores: the first request calibrates the cost per work unit, and the
@@ -483,7 +518,7 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads):
     spans = W.request_spans(parent, seg_len)
     w = meta["readout"]
     used, tokens, took, rate = [], 0, 0.0, None
-    fid_a, fid_g = [], []
+    fid_a, fid_g, fid_8 = [], [], []
     for r, (a, b, t0, t1) in enumerate(spans):
         cost = request_cost(np.where(parent[a:b] >= 0, parent[a:b] - a, -1), seg_len[a:b])
         if rate is not None and took + cost / rate > CPU_BUDGET_S:
@@ -500,6 +535,8 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads):
         used.append(r)
         fid_a.append(metrics.decision_fidelity(o_gpu_rows(t0, t1), o, wl.w_attn, wl.parent, wl.seg_len))
         fid_g.append(metrics.decision_fidelity(go_gpu_rows(t0, t1), go, wl.w_gdn, wl.parent, wl.seg_len))
+        if o8_rows is not None:
+            fid_8.append(metrics.decision_fidelity(o8_rows(t0, t1), o, wl.w_attn, wl.parent, wl.seg_len))
     agg = lambda fs: dict(groups=len(fs), tvd_max=max(f["tvd_max"] for f in fs),
                           tvd_mean=float(np.mean([f["tvd_mean"] for f in fs])),
                           argmax_agreement=float(np.mean([f["argmax_agreement"] for f in fs])))
@@ -508,7 +545,7 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads):
                       f"{tokens} of {meta['T']} stream tokens; both layers, float32 oracle, "
                       f"{took:.1f} s wall on {threads} threads)",
                cpu_model=cpu_model(), host_cores=os.cpu_count())
-    fid = dict(attention=agg(fid_a), gdn=agg(fid_g),
+    fid = dict(attention=agg(fid_a), gdn=agg(fid_g), attention_fp8_scores=agg(fid_8) if fid_8 else None,
                reference=f"float32 oracle, the {len(used)} requests of the CPU-baseline sample, one "
                          "decision group per request")
     return cpu, fid
@@ -572,6 +609,7 @@ def main():
     log(f"headline request_mix: T={T} S={S}, bucket {r.caps}; warmup {args.warmup}, steps {args.steps}")
     graph = time_runner(r, args.steps, args.warmup, eager=False)
     eager = time_runner(r, args.steps, args.warmup, eager=True)
+    fp8 = fp8_scores(r, meta, args.steps, args.warmup)
     r.step()  # leave the graph replay's outputs in place for the fidelity check
     torch.cuda.synchronize()
     f = layer_fracs(meta, eager)
@@ -600,7 +638,9 @@ def main():
     if not args.no_cpu:
         log(f"cpu baseline: float32 oracle on a prefix of the requests, {threads} threads")
         ho = lambda x: (lambda t0, t1: x[t0:t1].float().cpu().numpy().astype(np.float64))
-        cpu, fid = cpu_baseline_mix(meta, ho(r.o), ho(r.go), threads)
+        cpu, fid = cpu_baseline_mix(meta, ho(r.o), ho(r.go), threads, o8_rows=ho(fp8.pop("o")))
+    else:
+        fp8.pop("o")
     n_opt, opt_tok, iso_tok = tree_rates(meta["parent"], meta["seg_len"])
     step_s = graph["ms_per_step"] * 1e-3
     rates = dict(options=n_opt, option_tokens_per_s=opt_tok / step_s,
@@ -642,6 +682,7 @@ def main():
         "cpu_baseline": cpu,
         "fidelity": fid,
         "layers": layers,
+        "attention_fp8_scores": fp8,
         "rates": rates,
         "measured_peaks": peaks,
     }

@@ -223,6 +223,22 @@ fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void*
                                   int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* FP8 scores: fork_attn_forward with the queries and keys given as OCP FP8
+ * E4M3 codes with one fp32 scale per (token, head) row (as fork_quantize_fp8
+ * writes them: q8 [T, H, D] bytes with q_scale [T, H], k8 [T, Hkv, D] bytes
+ * with k_scale [T, Hkv]), so that the attention scores
+ *   s = scale * (q8 . k8) * q_scale[t, h] * k_scale[j, h / (H / Hkv)]
+ * are formed on the FP8 matrix cores (E4M3 x E4M3, fp32 accumulation). The
+ * values v [T, Hkv, D], the output o [T, H, D] and the probabilities that
+ * weight the values stay bf16; lse as fork_attn_forward. Scales per row keep
+ * every branch quantised exactly as in its isolated pass (a row is one
+ * token). The pages report FP8 use where the hardware has it (techfi24.com
+ * page, section "Exact State Forking"). Supported: D = 128, metadata without
+ * cached contexts (caps.ctx_cap == 0); workspace as fork_attn_forward (bf16). */
+fork_status fork_attn_forward_qk8(const fork_meta* m, const void* q8, const float* q_scale, const void* k8,
+                                  const float* k_scale, const void* v, void* o, float* lse, int32_t H,
+                                  int32_t Hkv, int32_t D, float scale, void* ws, size_t ws_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * fork_attn_forward_ctx without a workspace argument. The partial results of

@@ -25,7 +25,7 @@ FORK_DEVERR_MAGIC, FORK_DEVERR_CAPACITY = 1, 2
 # every symbol include/fork.h declares
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
            "fork_meta_plan_ctx", "fork_meta_export", "fork_meta_check",
-           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx", "fork_attn_forward_noalloc",
+           "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx", "fork_attn_forward_noalloc", "fork_attn_forward_qk8",
            "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
            "fork_quantize_fp8", "fork_linear_fp8_forward",
@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "fork_attn_forward_ctx": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                       f32, i32, vp, sz, vp],
             "fork_attn_forward_noalloc": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp],
+            "fork_attn_forward_qk8": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, sz, vp],
             "gdn_fork_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
@@ -266,6 +267,13 @@ def fork_attn_forward_noalloc(meta: fork_meta, q, k, v, kc, vc, o, lse, H: int, 
     _check(lib().fork_attn_forward_noalloc(ctypes.byref(meta), _ptr(q), _ptr(k), _ptr(v), _ptr(kc),
                                            _ptr(vc), _ptr(o), _ptr(lse), H, Hkv, D, float(scale), dt,
                                            _stream(stream)))
+
+
+def fork_attn_forward_qk8(meta: fork_meta, q8, q_scale, k8, k_scale, v, o, lse, H: int, Hkv: int, D: int,
+                          scale: float, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().fork_attn_forward_qk8(ctypes.byref(meta), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v),
+                                       _ptr(o), _ptr(lse), H, Hkv, D, float(scale), _ptr(ws), int(ws_bytes),
+                                       _stream(stream)))
 
 
 def gdn_fork_workspace(meta: fork_meta, H: int, dk: int, dv: int, dt: int) -> int:

@@ -35,14 +35,19 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kAttnThreads = 512;  // 8 waves per workgroup, one workgroup per CU
 
-template <bool BF16, int D>
+// F8: queries and keys are E4M3 codes with one fp32 scale per (token, head)
+// row, and S = K Q^T runs on the FP8 matrix cores (32x32x64); values stay
+// bf16. Only with bf16 values and D = 128.
+template <bool BF16, int D, bool F8 = false>
 struct AttnCfg {
+  static_assert(!F8 || (BF16 && D == 128), "FP8 scores with bf16 values, head_dim 128");
   static constexpr int ESZ = BF16 ? 2 : 4;
   static constexpr int EPC = 16 / ESZ;                 // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                  // chunks per K/V row
@@ -55,7 +60,14 @@ struct AttnCfg {
   // bf16 tiles: unpadded rows of D elements (CPR 16-byte chunks), one K and
   // one V tile per buffer
   static constexpr int TILE_BYTES = kAttnKeys * D * ESZ;
-  static constexpr int BUF_BYTES = BF16 ? 2 * TILE_BYTES
+  // a buffer: the K tile (E4M3 rows of D bytes with F8), the V tile (bf16) at
+  // V_OFF, and with F8 the tile's 64 key scales at KS_OFF; at least 32 KB
+  // (four waves' output rows are staged through a buffer)
+  static constexpr int V_OFF = F8 ? kAttnKeys * D : TILE_BYTES;
+  static constexpr int KS_OFF = V_OFF + TILE_BYTES;
+  static constexpr int F8_BYTES = KS_OFF + kAttnKeys * 4 > 32 * 1024 ? KS_OFF + kAttnKeys * 4 : 32 * 1024;
+  static constexpr int BUF_BYTES = F8 ? F8_BYTES
+                                 : BF16 ? 2 * TILE_BYTES
                                         : (kAttnKeys * KS > VROWS * VS ? kAttnKeys * KS : VROWS * VS) * ESZ;
 };
 
@@ -72,6 +84,39 @@ __device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) <
 // one 64-lane instruction (lane l writes 16 bytes at n * 1024 + 16 l); each
 // wave issues its share of the blocks.
 typedef __attribute__((address_space(3))) void lds_void_t;
+// FP8 keys: the K tile is 64 rows of D bytes, chunk c of row r at c ^ (r mod
+// 8) too; each wave also loads 8 of the tile's key scales (one dword per
+// lane, lanes 0-7) to KS_OFF, so every wave issues the same number of DMAs.
+template <int D>
+__device__ __forceinline__ void kv_dma_f8(unsigned char* buf, const unsigned char* __restrict__ K8,
+                                          const float* __restrict__ kscale, const unsigned short* __restrict__ V,
+                                          int j0, int jmax, int g, int Hkv, int wave, int lane) {
+  using C = AttnCfg<true, D, true>;
+  constexpr int KCPR = D / 16;                        // 16-byte chunks per fp8 row
+  constexpr int VCPR = D / 8;                         // 16-byte chunks per bf16 row
+  constexpr int NW = kAttnThreads / 64;
+  static_assert(kAttnKeys * D / 1024 == NW && kAttnKeys * D * 2 / 1024 == 2 * NW, "one K and two V blocks per wave");
+  {
+    const int slot = wave * 64 + lane, r = slot / KCPR, pos = slot % KCPR;
+    const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
+    __builtin_amdgcn_global_load_lds((const void*)(K8 + row * D + 16 * k_chunk_pos(r, pos)),
+                                     (lds_void_t*)(buf + wave * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = wave * 2 + i;
+    const int slot = n * 64 + lane, r = slot / VCPR, pos = slot % VCPR;
+    const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
+    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos(r, pos)),
+                                     (lds_void_t*)(buf + C::V_OFF + n * 1024), 16, 0, 0);
+  }
+  if (lane < 8) {
+    const int r = 8 * wave + lane;
+    __builtin_amdgcn_global_load_lds((const void*)(kscale + (size_t)min(j0 + r, jmax) * Hkv + g),
+                                     (lds_void_t*)(buf + C::KS_OFF + 32 * wave), 4, 0, 0);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void kv_dma(unsigned char* buf, const unsigned short* __restrict__ K,
                                        const unsigned short* __restrict__ V, int j0, int jmax, int g, int Hkv,
@@ -101,6 +146,8 @@ struct AttnArgs {
   const void* vc;
   void* o;
   float* lse;
+  const float* qs;    // FP8 scores: scales of the q rows [T, H] and the k rows [T, Hkv]
+  const float* ks;
   unsigned char* ws;  // partial results of split tiles: [slot][kv head] x (rows x D outputs, rows lse)
   int32_t* ctr;  // the blob's work counters: next item per XCD (8), finished workgroups
   BlobGuard guard;
@@ -281,10 +328,10 @@ __device__ __forceinline__ void iter_next(TileIter& it, const AttnTile& tile,
 }
 
 // One workgroup of 8 waves per CU: two waves per SIMD, <= 256 VGPRs each.
-template <bool BF16, int D>
+template <bool BF16, int D, bool F8>
 __global__ void __launch_bounds__(kAttnThreads, 1)
     fork_attn_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
-  using C = AttnCfg<BF16, D>;
+  using C = AttnCfg<BF16, D, F8>;
   using E = typename std::conditional<BF16, unsigned short, float>::type;
   using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
   // bf16: three K/V tile buffers (static arrays, so the compiler can tell the
@@ -367,7 +414,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     pj[slot] = it.j0;
     ph[slot] = it.hi;
     po[slot] = it.own;
-    if constexpr (BF16) kv_dma<D>(buf, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, wave, lane);
+    if constexpr (F8)
+      kv_dma_f8<D>(buf, (const unsigned char*)args.k, args.ks, V, it.j0, it.hi - 1, g, Hkv, wave, lane);
+    else if constexpr (BF16)
+      kv_dma<D>(buf, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, wave, lane);
     ++nq;
     iter_next(it, tile, parent, seg_start, seg_len);
   };
@@ -402,8 +452,26 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     const int h = g * G + (valid ? hg : 0);
     const int lo_row = t_row - tok_pos[t_row];
 
-    QF qf[C::NKF];
-    {
+    // F8: this lane's 32 bytes of each 64-wide k-step of its q row (A and B
+    // of the FP8 product hold the same d indices at the same byte places), and
+    // the row's scale folded into the softmax factor c
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    i32x8_t qf8[F8 ? D / 64 : 1];
+    float csc = args.scale_log2;
+    if constexpr (F8) {
+      int hq = hi;
+      asm volatile("" : "+v"(hq));
+      const unsigned char* qrow = (const unsigned char*)args.q + ((size_t)t_row * H + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) {
+        const u32x4_t lo = *(const u32x4_t*)(qrow + 64 * ks + 32 * hq);
+        const u32x4_t hi4 = *(const u32x4_t*)(qrow + 64 * ks + 32 * hq + 16);
+        qf8[ks] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+      }
+      csc = args.qs[(size_t)t_row * H + h] * args.scale_log2;
+    }
+    QF qf[F8 ? 1 : C::NKF];
+    if constexpr (!F8) {
       int hq = hi;
       asm volatile("" : "+v"(hq));  // (as r above: no 64-bit base + hi offset kept across items)
       const E* qrow = Q + ((size_t)t_row * H + h) * D;
@@ -436,6 +504,29 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       auto qk = [&](int b) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
+        if constexpr (F8) {
+          // key row 32 b + l32: 32 bytes (16-byte chunks 4 ks + 2 hi, + 1) per k-step
+          const unsigned char* K8 = (const unsigned char*)Ks;
+          const int kr = 32 * b + l32;
+#pragma unroll
+          for (int ks = 0; ks < D / 64; ++ks) {
+            const u32x4_t lo = *(const u32x4_t*)(K8 + kr * D + 16 * k_chunk_pos(kr, 4 * ks + 2 * hi));
+            const u32x4_t hi4 = *(const u32x4_t*)(K8 + kr * D + 16 * k_chunk_pos(kr, 4 * ks + 2 * hi + 1));
+            const i32x8_t a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+            // formats 0 (E4M3) for both operands, unit block scales (E8M0 127)
+            s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[ks], s[b], 0, 0, 0, 127, 0, 127);
+          }
+          // the keys' scales (this lane's 16 keys: 32 b + 8 q + 4 hi + r)
+          const float* kss = (const float*)(K8 + C::KS_OFF);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t k4 = *(const f32x4_t*)(kss + 32 * b + 8 * q + 4 * hi);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[b][4 * q + r] *= k4[r];
+          }
+          return;
+        }
 #pragma unroll
         for (int ks = 0; ks < C::NKF; ++ks) {
           if constexpr (BF16) {
@@ -470,7 +561,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * args.scale_log2;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * csc;
         const bool grow = mx > m_run + 8.f;
         alpha[b] = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
         m_run = grow ? mx : m_run;
@@ -483,7 +574,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][i], args.scale_log2, mneg));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][i], csc, mneg));
           s[b][i] = p;
           psum += p;
         }
@@ -589,7 +680,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       // Tiles cycle through lds2, lds0, lds1 (tile 0 was issued into lds2
       // while the previous item stored its output); the loop is unrolled by
       // three so that each step reads and fills fixed buffers.
-      constexpr int DMA_PER_TILE = 2 * (kAttnKeys * D * 2 / 1024) / (kAttnThreads / 64);
+      // per wave and tile: K and V blocks (FP8: one K block, two V blocks, one dword load of key scales)
+      constexpr int DMA_PER_TILE = F8 ? 4 : 2 * (kAttnKeys * D * 2 / 1024) / (kAttnThreads / 64);
       static_assert(DMA_PER_TILE < 16, "vmcnt field");
       __syncthreads();  // the previous item's output rows staged in lds0 / lds1 are read
       issue(lds0, 0);
@@ -604,7 +696,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         // (a returning atomic, counted with them) delays no tile wait
         if (nq == 0 && it.done) request_next();
         issue(fill, fslot);
-        kv_compute((const E*)cur, (const E*)(cur + C::TILE_BYTES), pj[slot], ph[slot], po[slot]);
+        kv_compute((const E*)cur, (const E*)(cur + C::V_OFF), pj[slot], ph[slot], po[slot]);
       };
       while (nq > 0) {
         step(lds2, 2, lds1, 1);
@@ -819,9 +911,9 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
   }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool F8 = false>
 fork_status launch_one(const fork_meta* m, const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fork_attn_kernel<BF16, D>), dim3(grid), dim3(kAttnThreads), 0, stream, a.blob, a);
+  hipLaunchKernelGGL((fork_attn_kernel<BF16, D, F8>), dim3(grid), dim3(kAttnThreads), 0, stream, a.blob, a);
   FORK_HIP_CHECK(hipGetLastError());
   // merge pass for split tiles: under capture whenever splitting is possible,
   // otherwise only when this tree has split tiles
@@ -867,7 +959,15 @@ size_t attn_workspace_bytes(const fork_caps& c, int D, fork_dtype dt) {
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              const void* kc, const void* vc, void* o, float* lse, int H, int Hkv, int D,
                              float scale, fork_dtype dt, void* ws, hipStream_t stream) {
+  return launch_attention_any(m, q, nullptr, k, nullptr, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws, stream);
+}
+
+fork_status launch_attention_any(const fork_meta* m, const void* q, const float* qs, const void* k, const float* ks,
+                                 const void* v, const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
+                                 int D, float scale, fork_dtype dt, void* ws, hipStream_t stream) {
   AttnArgs a;
+  a.qs = qs;
+  a.ks = ks;
   a.blob = (const int32_t*)m->dev;
   a.q = q;
   a.k = k;
@@ -892,6 +992,7 @@ fork_status launch_attention(const fork_meta* m, const void* q, const void* k, c
     if (items < grid) grid = (int)(items > 0 ? items : 1);
   }
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;  // whole rounds over the XCDs
+  if (qs) return launch_one<true, 128, true>(m, a, grid, stream);  // FP8 scores (checked by the caller)
   if (dt == FORK_BF16)
     return D == 128 ? launch_one<true, 128>(m, a, grid, stream) : launch_one<true, 64>(m, a, grid, stream);
   return D == 128 ? launch_one<false, 128>(m, a, grid, stream) : launch_one<false, 64>(m, a, grid, stream);

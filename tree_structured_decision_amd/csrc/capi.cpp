@@ -543,6 +543,24 @@ fork_status fork_attn_forward_ctx(const fork_meta* m, const void* q, const void*
   return launch_attention(m, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws, (hipStream_t)stream);
 }
 
+fork_status fork_attn_forward_qk8(const fork_meta* m, const void* q8, const float* q_scale, const void* k8,
+                                  const float* k_scale, const void* v, void* o, float* lse, int32_t H,
+                                  int32_t Hkv, int32_t D, float scale, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_attn_args(m, q8, k8, v, nullptr, nullptr, o, H, Hkv, D, FORK_BF16);
+  if (st) return st;
+  if (!q_scale || !k_scale) return fail(FORK_E_ARG, "q_scale and k_scale must be non-null");
+  if (D != 128) return fail(FORK_E_UNSUPPORTED, "FP8 scores need head_dim 128 (got %d)", D);
+  if (m->caps.ctx_cap != 0)
+    return fail(FORK_E_UNSUPPORTED, "FP8 scores are not supported with cached contexts (ctx_cap %d)", m->caps.ctx_cap);
+  if ((uintptr_t)q8 % 16 || (uintptr_t)k8 % 16) return fail(FORK_E_ARG, "q8 and k8 must be 16-byte aligned");
+  const size_t need = attn_workspace_bytes(m->caps, D, FORK_BF16);
+  if (need && (!ws || ws_bytes < need))
+    return fail(FORK_E_WORKSPACE, "attention workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  return launch_attention_any(m, q8, q_scale, k8, k_scale, v, nullptr, nullptr, o, lse, H, Hkv, D, scale, FORK_BF16,
+                              ws, (hipStream_t)stream);
+}
+
 fork_status fork_attn_forward_noalloc(const fork_meta* m, const void* q, const void* k, const void* v,
                                       const void* kc, const void* vc, void* o, float* lse, int32_t H,
                                       int32_t Hkv, int32_t D, float scale, fork_dtype dt, void* stream) {

@@ -207,6 +207,10 @@ fork_status attn_scratch(void** ptr);
 fork_status launch_attention(const fork_meta* m, const void* q, const void* k, const void* v,
                              const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
                              int D, float scale, fork_dtype dt, void* ws, hipStream_t stream);
+// qs non-null: FP8 scores (q, k E4M3 codes with row scales qs [T, H], ks [T, Hkv]; v bf16; D 128)
+fork_status launch_attention_any(const fork_meta* m, const void* q, const float* qs, const void* k, const float* ks,
+                                 const void* v, const void* kc, const void* vc, void* o, float* lse, int H, int Hkv,
+                                 int D, float scale, fork_dtype dt, void* ws, hipStream_t stream);
 fork_status launch_rope(const fork_meta* m, const void* src, long long ld_src, void* dst, int nh, int D, float theta,
                         fork_dtype dt, hipStream_t stream);
 fork_status launch_conv(const fork_meta* m, const void* x, const float* w, const float* bias,

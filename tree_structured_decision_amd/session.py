@@ -84,6 +84,16 @@ class ForkSession:
         B.fork_attn_forward_ctx(self.meta, q, k, v, kc, vc, o, lse, H, Hkv, D, scale, dt, ws,
                                 0 if ws is None else ws.numel(), stream=stream)
 
+    def attention_qk8(self, q8, q_scale, k8, k_scale, v, o, lse=None, scale: float = 0.0, stream=None):
+        """Tree attention with FP8 scores: q8 [T, H, D] / k8 [T, Hkv, D] E4M3 codes
+        (uint8) with row scales q_scale [T, H] / k_scale [T, Hkv] (fork_quantize_fp8
+        over rows of D), v bf16 [T, Hkv, D], o bf16 [T, H, D]."""
+        T, H, D = q8.shape
+        Hkv = k8.shape[1]
+        ws = self.attn_ws
+        B.fork_attn_forward_qk8(self.meta, q8, q_scale, k8, k_scale, v, o, lse, H, Hkv, D, scale, ws,
+                                0 if ws is None else ws.numel(), stream=stream)
+
     def gdn(self, q, k, v, a, b, o, seg_start_state, seg_final_state=None, root_state=None,
             scale: float = 1.0, stream=None):
         T, H, dk = q.shape
