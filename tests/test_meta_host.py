@@ -21,7 +21,7 @@ H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS
            "OFF_ANCLEN", "OFF_FIRSTCHILD", "OFF_CHUNKBASE", "OFF_LEVELOFF", "OFF_LEVELSEG",
            "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
            "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS", "OFF_LEVELLONG", "OFF_CTXSTART",
-           "OFF_CTXLEN", "NCTX"]
+           "OFF_CTXLEN", "NCTX", "OFF_GDNREC"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
 ATTN_ROWS = int(re.search(r"kAttnRows = (\d+);", open(os.path.join(
     ROOT, "tree_structured_decision_amd", "csrc", "common.h")).read()).group(1))
@@ -110,6 +110,15 @@ def check_plan(parent, seg_len, gqa, kv_heads=0, ctx=None):
         # the depth's segments longer than one 64-token chunk lead its list
         assert ll[d] == int(np.sum(seg_len[segs] > 64))
         assert np.all(seg_len[segs[:ll[d]]] > 64) and np.all(seg_len[segs[ll[d]:]] <= 64)
+    # the scan items' records, in level order: segment, first token, length,
+    # the slot holding its start state (first child of its parent; -1 - root
+    # ordinal for a root), first child
+    rec = arr(w, "GDNREC", 8 * S).reshape(S, 8)
+    first = {s: (np.flatnonzero(parent == s)[0] if np.any(parent == s) else -1) for s in range(S)}
+    for i, s in enumerate(ls):
+        src = first[parent[s]] if parent[s] >= 0 else -1 - int(np.flatnonzero(roots == s)[0])
+        want = (s, ref["seg_start"][s], seg_len[s], src, first[s], 0, 0, 0)
+        assert tuple(rec[i]) == want, (i, s, tuple(rec[i]), want)
     # chunks: 64-token pieces of each segment, in order
     nch = w[HI["NCHUNKS"]]
     ch = arr(w, "CHUNKS", 2 * nch).reshape(-1, 2)

@@ -318,6 +318,15 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, cons
         w[off++] = std::min(kChunk, seg_len[s] - c0);
       }
   }
+  {
+    // the scan items' records, in level order (GdnRec)
+    std::vector<GdnRec> rec(S);
+    for (int32_t i = 0; i < S; ++i) {
+      const int32_t s = level_seg[i], p = parent[s];
+      rec[i] = GdnRec{s, start[s], seg_len[s], p < 0 ? -1 - root_ord[s] : first_child[p], first_child[s], 0, 0, 0};
+    }
+    put(MH_OFF_GDNREC, (const int32_t*)rec.data(), (int64_t)S * kGdnRecWords);
+  }
   put(MH_OFF_TILES, (const int32_t*)sorted.data(), (int64_t)sorted.size() * 8);
   put(MH_OFF_MERGE, (const int32_t*)merges.data(), (int64_t)merges.size() * 4);
   if (off > L.upload_cap_words) return fail(FORK_E_CAPACITY, "metadata upload region overflow");

@@ -53,6 +53,7 @@ enum MetaHeader : int {
   MH_OFF_CTXSTART,    // [S] first key/value cache row of a root's resumed context (0 if none)
   MH_OFF_CTXLEN,      // [S] cache rows of a root's resumed context (0 for non-roots)
   MH_NCTX,            // roots with a nonempty context
+  MH_OFF_GDNREC,      // [S x kGdnRecWords] Gated DeltaNet scan items in LEVELSEG order (GdnRec)
   MH_WORDS = 64
 };
 // Header word 57 is the device error word (FORK_DEVERR_* bits, fork_meta_check).
@@ -63,7 +64,12 @@ constexpr int kErrWord = 57;
 // leaves them zero.
 constexpr int kAttnCtrWord = 48;
 constexpr int kNumXcd = 8;
-static_assert(kAttnCtrWord > MH_NCTX && kAttnCtrWord + kNumXcd < kErrWord && kErrWord < MH_WORDS,
+// Header words 58..59 hold the Gated DeltaNet scan's work counters (the next
+// work item of a depth's launch, then the number of workgroups that found no
+// more work), zero between launches like the attention counters.
+constexpr int kGdnCtrWord = 58;
+static_assert(kAttnCtrWord > MH_OFF_GDNREC && kAttnCtrWord + kNumXcd < kErrWord && kErrWord < kGdnCtrWord &&
+                  kGdnCtrWord + 2 <= MH_WORDS,
               "counter and error words inside the header, past the plan's words");
 
 
@@ -72,6 +78,17 @@ constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
 constexpr int kAttnRows = 256;              // query rows (token x GQA head) per attention tile
 constexpr int kAttnKeys = 64;               // keys per staged key/value tile
 constexpr int kMaxDepthCap = 4096;
+// A Gated DeltaNet scan item's record (one per segment, in the blob's level
+// order), so that a scan workgroup learns everything about its next segment
+// from one load: the segment, its first token and length, the slot its start
+// state is copied from (the first child of its parent, which holds the
+// parent's end state; -1 - root ordinal for a root) and its first child (-1
+// for a leaf). Padded to 8 words (two 16-byte loads).
+struct GdnRec {
+  int32_t seg, start, len, src, first_child, pad0, pad1, pad2;
+};
+constexpr int kGdnRecWords = 8;
+static_assert(sizeof(GdnRec) == 4 * kGdnRecWords, "GdnRec layout");
 // Split plan for query tiles with long key ranges: the number of shares the
 // total work is cut into (the part size is total / kAttnSlots key tiles;
 // about 1.6 parts per resident workgroup on a 256-CU MI355X, measured best
@@ -124,9 +141,10 @@ inline BlobLayout blob_layout(const fork_caps& c) {
   L.chunk_cap = ((int64_t)c.t_cap + kChunk - 1) / kChunk + c.s_cap;
   L.merge_cap = kMaxPartSlots / 2;
   // header + 12 segment arrays + level offsets and long counts + 2 words per chunk + 8 per tile
-  // + 4 per merge group, each array aligned to 4 words
+  // + 4 per merge group + the scan items' records, each array aligned to 4 words
   L.upload_cap_words = MH_WORDS + 12 * ((int64_t)c.s_cap + 4) + 2 * (c.depth_cap + 2 + 4) +
-                       2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4;
+                       2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4 +
+                       kGdnRecWords * (int64_t)c.s_cap + 4;
   L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
   L.tok_off_words = L.upload_cap_words;
   L.total_words = L.tok_off_words + 3 * (((int64_t)c.t_cap + 63) / 64 * 64);

@@ -71,10 +71,13 @@ static_assert(kWsGam + 1024 <= kWsChunk, "bf16 workspace layout fits the block (
 // when all of its work items fit in one round of the grid (a latency-bound
 // depth such as a single long prefix); everything else goes to the
 // one-wave-per-slice kernel, which has the higher throughput.
-__device__ __forceinline__ int coop_segments(const int32_t* __restrict__ blob, int level, int H, int dv) {
+__device__ __forceinline__ int coop_take(const int32_t* __restrict__ blob, int level, int H, int dv, int sgrid) {
   const int nlong = blob[blob[MH_OFF_LEVELLONG] + level];
   const long long items = (long long)nlong * ((H + 7) / 8) * 8 * (dv / 16);
-  return items <= (long long)gridDim.x ? nlong : 0;
+  return items <= (long long)sgrid ? nlong : 0;
+}
+__device__ __forceinline__ int coop_segments(const int32_t* __restrict__ blob, int level, int H, int dv) {
+  return coop_take(blob, level, H, dv, (int)gridDim.x);
 }
 
 template <bool BF16>
@@ -145,6 +148,7 @@ struct GdnArgs {
   float* seg_start;
   float* seg_final;
   unsigned char* ws;
+  int32_t* ctr;  // the blob's scan work counters: next item, finished workgroups
   BlobGuard guard;
   int H;
   float scale;
@@ -153,6 +157,9 @@ struct GdnArgs {
   // level list and its first lv_take segments for gdn_coop_kernel, when the
   // host planned the launch; lv_first < 0: read everything from the blob
   int lv_first, lv_count, lv_take;
+  // gdn_prep_kernel: 1 = only the chunks of the segments gdn_coop_kernel takes
+  // (the fused kernel prepares the others itself); sgrid: the scans' grid
+  int prep_coop_only, sgrid;
 };
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
@@ -273,9 +280,37 @@ __global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
   __shared__ __attribute__((aligned(16))) float bsb[2][CH];
 
   if (!blob_ok(blob, args.guard)) return;
-  const int nchunks = blob[MH_NCHUNKS];
   const int2* __restrict__ chunks = (const int2*)(blob + blob[MH_OFF_CHUNKS]);
   const int H = args.H;
+  // the chunks to prepare: all, or those of the segments gdn_coop_kernel takes
+  // (at each depth, its first `take` segments; a handful at most)
+  int nchunks = blob[MH_NCHUNKS];
+  const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
+  const int32_t* __restrict__ level_seg = blob + blob[MH_OFF_LEVELSEG];
+  const int32_t* __restrict__ seg_len = blob + blob[MH_OFF_SEGLEN];
+  const int32_t* __restrict__ chunk_base = blob + blob[MH_OFF_CHUNKBASE];
+  const int maxd = blob[MH_MAXDEPTH];
+  if (args.prep_coop_only) {
+    nchunks = 0;
+    for (int lv = 0; lv <= maxd; ++lv) {
+      const int take = coop_take(blob, lv, H, DK, args.sgrid);
+      for (int k = 0; k < take; ++k) nchunks += (seg_len[level_seg[level_off[lv] + k]] + CH - 1) / CH;
+    }
+  }
+  // chunk index of the n-th prepared chunk
+  auto chunk_of = [&](int n) -> int {
+    if (!args.prep_coop_only) return n;
+    for (int lv = 0; lv <= maxd; ++lv) {
+      const int take = coop_take(blob, lv, H, DK, args.sgrid);
+      for (int k = 0; k < take; ++k) {
+        const int sg = level_seg[level_off[lv] + k];
+        const int nc = (seg_len[sg] + CH - 1) / CH;
+        if (n < nc) return chunk_base[sg] + n;
+        n -= nc;
+      }
+    }
+    return 0;  // (unreachable: n < nchunks)
+  };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c16 = lane & 15, q4 = lane >> 4;
   const E* __restrict__ Kg = (const E*)args.k;
@@ -291,8 +326,8 @@ __global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
   // rows past the chunk are clamped to its last row (in range) and zeroed at
   // the LDS store, so no load sits in a divergent branch
   auto prep_load = [&](int item) {
-    const int c = item / H, h = item - c * H;
-    const int2 ck = chunks[c];
+    const int n = item / H, h = item - n * H;
+    const int2 ck = chunks[chunk_of(n)];
     rlen = ck.y;
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
@@ -309,7 +344,8 @@ __global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
 
   int par = 0;
   for (int item = blockIdx.x; item < nchunks * H; item += gridDim.x, par ^= 1) {
-    const int c = item / H, h = item - c * H;
+    const int n = item / H, h = item - n * H;
+    const int c = chunk_of(n);
     unsigned char* wsb = args.ws + ((size_t)c * H + h) * kWsChunk;
     float* gs = gsb[par];
     float* bs = bsb[par];
@@ -1624,25 +1660,512 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
   if (!chain) flush_o();
 }
 
+// ---------------------------------------------------------------------------
+// Fused bf16 Gated DeltaNet (DK = DV = 128): chunk preparation and scan in one
+// kernel, one work item = (segment, head) on one workgroup of 8 waves. Wave w
+// owns state rows [16 w, 16 w + 16) (slices never communicate). Per chunk:
+//   B0  the chunk's k, q, v, a, b are in LDS (this wave's loads waited, then
+//       the barrier); the next chunk's loads (or the next item's first) are
+//       issued into the other buffer;
+//   prep (waves 0-3; wave 0 first forms the decays): Pt_J = K_J Q_w^T and
+//       At_J = K_J K_w^T (J <= w) on MFMA, P = QK^T * Gamma as hi/lo operand
+//       fragments and A = strictly_lower(diag(b) KK^T * Gamma) in LDS; the
+//       diagonal blocks of T = (I + A)^-1 by forward substitution, the blocks
+//       below by distance; T'' = T diag(b) as hi/lo fragments (all threads);
+//   scan (every wave, its slice): X = K S^T, Y^T = S Q^T, R = V - gamma X,
+//       U = T'' R, O^T = scale (gamma Y^T + U^T P^T), S^T = gamma_C S^T + K^T U'.
+// So the chunk intermediates never leave the CU (no workspace round trip) and
+// each chunk's operands are read once per head instead of once per group of
+// slices. The start state comes from root_state / zero or the parent's end
+// state (the parent's first child's start slot, where the parent's item left
+// it) and is copied into the segment's own slot; the end state goes to
+// seg_final_state and the first child's slot.
+struct FusedCfg {
+  static constexpr int DK = 128, NW = 8, NT = 64 * NW;
+  static constexpr int TB = CH * DK * 2;               // a K, Q or V tile (bf16, kq_off layout)
+  static constexpr int OQ = TB, OV = 2 * TB, OA = 3 * TB, OB = OA + CH * 4;
+  static constexpr int BUF = OB + CH * 4;              // one chunk's operands
+  static constexpr int LDA = CH + 4;                   // fp32 64x64 A and T rows
+  static constexpr int PA = 0, PT = PA + CH * LDA * 4, PTH = PT + CH * LDA * 4, PPH = PTH + (int)kWsFrag;
+  static constexpr int PGAM = PPH + (int)kWsFrag, PRR = PGAM + CH * 4, PGS = PRR + CH * 4, PBS = PGS + CH * 4;
+  static constexpr int PREP = PBS + CH * 4;
+  static_assert(2 * BUF + PREP <= 160 * 1024, "LDS");
+  static constexpr int BLK = 3 * TB / 1024 / NW;       // 1 KB loads of K, Q and V per wave
+  static_assert(BLK * NW * 1024 == 3 * TB, "tiles divide over the waves");
+};
+
+template <int DK>
+__global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
+  using F = FusedCfg;
+  static_assert(DK == F::DK, "fused kernel is for dk = dv = 128");
+  typedef unsigned short E;
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[F::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[F::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char prep[F::PREP];
+
+  if (!blob_ok(blob, args.guard)) return;
+  const int level = args.level;
+  const bool planned = args.lv_first >= 0;
+  if (!planned && level > blob[MH_MAXDEPTH]) return;
+  const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
+  const int32_t* __restrict__ gdn_rec = blob + blob[MH_OFF_GDNREC];
+  const int H = args.H;
+  // the depth's first `take` segments are handled by gdn_coop_kernel
+  const int take = planned ? args.lv_take : coop_segments(blob, level, H, DK);
+  const int lv0 = (planned ? args.lv_first : level_off[level]) + take;
+  const int nlev = (planned ? args.lv_first + args.lv_count : level_off[level + 1]) - lv0;
+  const int nitems = nlev * H;
+  // (the wave index as a scalar: branches on it stay scalar, so the compiler
+  // keeps LDS accesses under them out of its waits for the LDS DMA below)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int e0 = 16 * w;  // this wave's state rows
+  const E* __restrict__ Kg = (const E*)args.k;
+  const E* __restrict__ Qg = (const E*)args.q;
+  const E* __restrict__ Vg = (const E*)args.v;
+  E* __restrict__ Og = (E*)args.o;
+  // (the lambdas below use these copies, not args: a by-reference capture of
+  // the kernel argument would put it in scratch memory)
+  const float* __restrict__ Ag = args.a;
+  const float* __restrict__ Bg = args.b;
+  const float* __restrict__ root_state = args.root_state;
+  float* __restrict__ seg_start_state = args.seg_start;
+  float* __restrict__ seg_final_state = args.seg_final;
+  const float oscale = args.scale;
+  const size_t SZ = (size_t)DK * DK;
+
+  float* As = (float*)(prep + F::PA);
+  float* Ts = (float*)(prep + F::PT);
+  float* gam = (float*)(prep + F::PGAM);
+  float* rrv = (float*)(prep + F::PRR);
+  float* gs = (float*)(prep + F::PGS);
+  float* bs = (float*)(prep + F::PBS);
+
+  // a work item: segment (longest first within the depth) and head, from
+  // the segment's record (one load)
+  struct Item {
+    int s, h, L, st, nck, src, fc;
+  };
+  auto item_at = [&](int it) __attribute__((always_inline)) {
+    Item r;
+    const int li = it / H;
+    const int32_t* rec = gdn_rec + (size_t)(lv0 + li) * kGdnRecWords;
+    const int4 a = *(const int4*)rec;
+    const int4 b = *(const int4*)(rec + 4);
+    r.s = __builtin_amdgcn_readfirstlane(a.x);
+    r.st = __builtin_amdgcn_readfirstlane(a.y);
+    r.L = __builtin_amdgcn_readfirstlane(a.z);
+    r.src = __builtin_amdgcn_readfirstlane(a.w);
+    r.fc = __builtin_amdgcn_readfirstlane(b.x);
+    r.h = it - li * H;
+    r.nck = (r.L + CH - 1) / CH;
+    return r;
+  };
+
+  // loads of chunk ci of item r into buffer b: K, Q and V tiles in the kq_off
+  // layout (chunk c of row i at c ^ kq_swz(i)), rows past the chunk repeat its
+  // last row (they meet b = 0, so they reach no output that is stored); a and
+  // b of the chunk (waves 0 and 1, one dword per lane)
+  // The buffer's address goes through an empty asm statement: the compiler
+  // then does not tie these LDS writes to the buffer, and adds no waits for
+  // them before LDS accesses elsewhere in the step (it cannot tell the
+  // buffers apart reliably); every read of a buffer follows the step's own
+  // vmcnt(0) and barrier.
+  auto issue = [&](unsigned char* b, const Item& r, int ci) __attribute__((always_inline)) {
+    const int t0 = r.st + CH * ci, tl = t0 + min(CH, r.L - CH * ci) - 1;
+    asm volatile("" : "+v"(b));
+    // 1 KB block n = 8 i + w: tile i / 2 (K, Q, V), block (i % 2) 8 + w of it
+    static_assert(F::BLK == 6 && F::NW == 8 && F::TB == 16 * 1024, "two blocks of each tile per wave");
+#pragma unroll
+    for (int i = 0; i < F::BLK; ++i) {
+      const int nb = (i % 2) * 8 + w;
+      const int slot = nb * 64 + lane, row = slot / (DK / 8), pos = slot % (DK / 8);
+      const E* src = i < 2 ? Kg : (i < 4 ? Qg : Vg);
+      const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 8 * (pos ^ kq_swz(row, DK / 8));
+      __builtin_amdgcn_global_load_lds((const void*)(src + g), (lds_void_t*)(b + (i / 2) * F::TB + nb * 1024), 16,
+                                       0, 0);
+    }
+    if (w < 2) {
+      const float* src = w == 0 ? Ag : Bg;
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)min(t0 + lane, tl) * H + r.h),
+                                       (lds_void_t*)(b + (w == 0 ? F::OA : F::OB)), 4, 0, 0);
+    }
+  };
+
+  // ---- chunk preparation (operands of the chunk in b)
+  auto prep_chunk = [&](const unsigned char* b, int len) __attribute__((always_inline)) {
+    const E* Ks = (const E*)b;
+    const E* Qs = (const E*)(b + F::OQ);
+    if (w == 0) {
+      const float a = ((const float*)(b + F::OA))[lane];
+      const float la = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
+      const float gl = lane_val(la, CH - 1);
+      gs[lane] = la;
+      bs[lane] = lane < len ? ((const float*)(b + F::OB))[lane] : 0.f;
+      gam[lane] = __expf(la);
+      rrv[lane] = __expf(gl - la);
+    }
+    lds_barrier();  // g, b, gamma
+    if (w < 4) {
+      // Pt_J = K_J Q_w^T, At_J = K_J K_w^T for J <= w (16x16x32 bf16, k-order of a 16-byte row read)
+      f32x4_t pt[4], at[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) pt[J] = at[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8_t bq = *(const bf16x8_t*)(Qs + kq_off<DK>(16 * w + c16, 32 * ks + 8 * q4));
+        const bf16x8_t bk = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * w + c16, 32 * ks + 8 * q4));
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          if (J <= w) {
+            const bf16x8_t aK = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * J + c16, 32 * ks + 8 * q4));
+            pt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bq, pt[J], 0, 0, 0);
+            at[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bk, at[J], 0, 0, 0);
+          }
+        }
+      }
+      // lane (c16, q4): row i = 16 w + c16, columns j = 16 J + 4 q4 + r
+      const int i = 16 * w + c16;
+      const float gi = gs[i], bi = bs[i];
+      f32x4_t pv[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        pv[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (J <= w) {
+          const f32x4_t gj = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
+          f32x4_t av;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * J + 4 * q4 + r;
+            const float dec = j <= i ? __expf(gi - gj[r]) : 0.f;
+            pv[J][r] = dec * pt[J][r];
+            av[r] = j < i ? bi * dec * at[J][r] : 0.f;
+          }
+          *(f32x4_t*)(As + i * F::LDA + 16 * J + 4 * q4) = av;
+        }
+      }
+      u32x4_t* Pw = (u32x4_t*)(prep + F::PPH);
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        if (kf < frag_nk(w)) {
+          const int fb = frag_tri(w) + kf;
+          u32x2_t h0, l0, h1, l1;
+          split4(pv[2 * kf], h0, l0);
+          split4(pv[2 * kf + 1], h1, l1);
+          Pw[(2 * fb) * 64 + lane] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+          Pw[(2 * fb + 1) * 64 + lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
+        }
+      }
+      // diagonal block w of T (its rows of A are this wave's own stores)
+      diag_inverse(As, Ts, F::LDA, 16 * w, lane);
+    }
+    lds_barrier();
+    // blocks of T below the diagonal, by distance d = I - J (wave J)
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      const int I = w + d, J = w;
+      if (w < 4 && I < 4) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        for (int Kb = J; Kb < I; ++Kb) {
+          const f32x4_t a4 = *(const f32x4_t*)(As + (16 * I + c16) * F::LDA + 16 * Kb + 4 * q4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z = mma_f32(a4[r], Ts[(16 * Kb + 4 * q4 + r) * F::LDA + 16 * J + c16], z);
+        }
+        const f32x4_t t4 = *(const f32x4_t*)(Ts + (16 * I + c16) * F::LDA + 16 * I + 4 * q4);
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t = mma_f32(t4[r], z[r], t);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * q4 + r) * F::LDA + 16 * J + c16] = -t[r];
+      }
+      lds_barrier();
+    }
+    // T'' = T diag(b) (zero above the diagonal) as hi / lo operand fragments
+    if (tid < kNtri * 64) {
+      const int fb = tid >> 6, l = tid & 63;
+      const int I = fb < 3 ? fb : (fb == 3 ? 2 : 3), kf = fb - frag_tri(I);
+      const int ti = 16 * I + (l & 15), j0 = 32 * kf + 4 * (l >> 4);
+      f32x4_t t0, t1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t0[e] = j0 + e <= ti ? Ts[ti * F::LDA + j0 + e] * bs[j0 + e] : 0.f;
+        t1[e] = j0 + 16 + e <= ti ? Ts[ti * F::LDA + j0 + 16 + e] * bs[j0 + 16 + e] : 0.f;
+      }
+      u32x2_t h0, l0, h1, l1;
+      split4(t0, h0, l0);
+      split4(t1, h1, l1);
+      u32x4_t* Tw = (u32x4_t*)(prep + F::PTH);
+      Tw[(2 * fb) * 64 + l] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+      Tw[(2 * fb + 1) * 64 + l] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
+    }
+    lds_barrier();  // T'', P and the decays are complete
+  };
+
+  // ---- one chunk of the scan for this wave's slice (operands in b; the
+  // prepared T'', P and decays in prep). St: lane (c16, q4) holds
+  // S[e0 + c16][16 db + 4 q4 + r] (S^T blocks).
+  f32x4_t St[DK / 16];
+  auto scan_chunk = [&](const unsigned char* b, const Item& r, int t0, int len, bool need_state) __attribute__((always_inline)) {
+    const E* Ks = (const E*)b;
+    const E* Qs = (const E*)(b + F::OQ);
+    const E* Vs = (const E*)(b + F::OV);
+    const u32x4_t* Th = (const u32x4_t*)(prep + F::PTH);
+    const u32x4_t* Ph = (const u32x4_t*)(prep + F::PPH);
+    // (1) X = K S^T, Y^T = S Q^T
+    f32x4_t X[4], Yt[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) X[I] = Yt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < DK / 32; ++f) {
+      bf16x8_t sh, sl;
+      reg_frag<true>(St, f, sh, sl);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const bf16x8_t ka = kq_frag<DK>(Ks, 16 * I + c16, f, q4);
+        const bf16x8_t qb = kq_frag<DK>(Qs, 16 * I + c16, f, q4);
+        X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh, X[I], 0, 0, 0);
+        X[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl, X[I], 0, 0, 0);
+        Yt[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh, qb, Yt[I], 0, 0, 0);
+        Yt[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, qb, Yt[I], 0, 0, 0);
+      }
+    }
+    // (2) R = V - gamma X: lane (c16, q4), block I holds R[16 I + 4 q4 + r][e0 + c16]
+    f32x4_t R[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(Vs + kq_off<DK>(16 * I + 4 * q4 + (c16 >> 2), e0 + 4 * (c16 & 3))));
+      const f32x4_t g4 = *(const f32x4_t*)(gam + 16 * I + 4 * q4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) R[I][k] = bf16_val((unsigned short)v4[k]) - g4[k] * X[I][k];
+    }
+    bf16x8_t rh[2], rl[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) reg_frag<true>(R, f, rh[f], rl[f]);
+    // (3) U = T'' R (T'' lower triangular: row block I reduces over tokens < 16 (I + 1))
+    f32x4_t U[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      U[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kf = 0; kf < frag_nk(I); ++kf) {
+        const bf16x8_t th = __builtin_bit_cast(bf16x8_t, Th[(frag_tri(I) + kf) * 128 + lane]);
+        const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, Th[(frag_tri(I) + kf) * 128 + 64 + lane]);
+        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kf], U[I], 0, 0, 0);
+        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kf], U[I], 0, 0, 0);
+        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kf], U[I], 0, 0, 0);
+      }
+    }
+    // (4) O^T = scale (gamma Y^T + U^T P^T): lane (c16, q4), block I holds
+    // O[16 I + c16][e0 + 4 q4 + r]; stored at once
+    bf16x8_t uh[2], ul[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) reg_frag<true>(U, f, uh[f], ul[f]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4_t Zt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kf = 0; kf < frag_nk(I); ++kf) {
+        const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, Ph[(frag_tri(I) + kf) * 128 + lane]);
+        const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, Ph[(frag_tri(I) + kf) * 128 + 64 + lane]);
+        Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[kf], ph, Zt, 0, 0, 0);
+        Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul[kf], ph, Zt, 0, 0, 0);
+        Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[kf], pl, Zt, 0, 0, 0);
+      }
+      const int i = 16 * I + c16;
+      const f32x4_t o = oscale * (gam[i] * Yt[I] + Zt);
+      if (i < len) {
+        E* d = Og + ((size_t)(t0 + i) * H + r.h) * DK + e0 + 4 * q4;
+        *(u32x2_t*)d = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    }
+    if (!need_state) return;
+    // (5) S^T = gamma_C S^T + K^T U',  U' = diag(gamma_C / gamma) U
+#pragma unroll
+    for (int I = 0; I < 4; ++I) U[I] *= *(const f32x4_t*)(rrv + 16 * I + 4 * q4);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) reg_frag<true>(U, f, uh[f], ul[f]);
+    const float gC = gam[CH - 1];
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db) St[db] *= gC;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int db = 0; db < DK / 16; ++db) {
+        const bf16x8_t kt = kt_frag<DK>(Ks, 16 * db, f, lane);
+        St[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, uh[f], St[db], 0, 0, 0);
+        St[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ul[f], St[db], 0, 0, 0);
+      }
+  };
+
+  // ---- the workgroup's items, chunk by chunk; loads run one chunk ahead
+  // through two buffers (the loop is unrolled by two so each step reads and
+  // fills fixed buffers).
+  // Items are handed out longest first: a workgroup's first item is static
+  // (blockIdx.x), later ones come from the blob's counter (value c: item
+  // c + gridDim.x), so a workgroup that ends a long segment early takes the
+  // next one (greedy longest-processing-time order over the depth's very
+  // uneven segments). The next item is requested just in time: at the start
+  // of the step that loads the current item's last chunk (thread 0's atomic),
+  // published after that step's preparation (the item in s_res, its record
+  // copied into s_rec by wave 0's DMA) and taken at the next step's start,
+  // after its vmcnt(0) and barrier, so no wave waits for a global load there.
+  // The last workgroup to finish resets the counters.
+  __shared__ int s_res;
+  __shared__ __attribute__((aligned(16))) int32_t s_rec[kGdnRecWords];
+  int32_t* __restrict__ ctr = args.ctr;
+  int tk = 0;  // thread 0: the requested item
+  auto request = [&]() __attribute__((always_inline)) {
+    if (tid == 0) tk = atomicAdd(ctr, 1) + (int)gridDim.x;
+  };
+  auto publish = [&]() __attribute__((always_inline)) {
+    if (w == 0) {
+      const int r = __builtin_amdgcn_readfirstlane(tk);
+      if (lane == 0) s_res = r;
+      if (r < nitems && lane < kGdnRecWords) {
+        unsigned char* d = (unsigned char*)s_rec;
+        asm volatile("" : "+v"(d));  // (as in issue: no compiler waits for this DMA)
+        __builtin_amdgcn_global_load_lds((const void*)(gdn_rec + (size_t)(lv0 + r / H) * kGdnRecWords + lane),
+                                         (lds_void_t*)d, 4, 0, 0);
+      }
+    }
+  };
+  int it = blockIdx.x;
+  if (it < nitems) {
+    Item cur = item_at(it);
+    int ci = 0;
+    issue(buf0, cur, 0);
+    if (cur.nck == 1) {  // the next chunk is the next item's
+      request();
+      publish();
+    }
+    const size_t srow = (size_t)(e0 + c16) * DK + 4 * q4;
+    auto step = [&](unsigned char* b, unsigned char* other) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of the chunk landed
+      lds_barrier();                       // B0: every wave's loads landed; `other` is free
+      // the chunk after (cur, ci): cur's next, or the published item's first
+      Item nx = cur;
+      int nci = ci + 1;
+      bool has_next = true;
+      if (nci >= cur.nck) {
+        const int r = __builtin_amdgcn_readfirstlane(s_res);
+        has_next = r < nitems;
+        if (has_next) {
+          const int li = r / H;
+          nx.s = __builtin_amdgcn_readfirstlane(s_rec[0]);
+          nx.st = __builtin_amdgcn_readfirstlane(s_rec[1]);
+          nx.L = __builtin_amdgcn_readfirstlane(s_rec[2]);
+          nx.src = __builtin_amdgcn_readfirstlane(s_rec[3]);
+          nx.fc = __builtin_amdgcn_readfirstlane(s_rec[4]);
+          nx.h = r - li * H;
+          nx.nck = (nx.L + CH - 1) / CH;
+        }
+        nci = 0;
+      }
+      // request the item after nx when nx's chunk is its last
+      const bool req = has_next && nci + 1 >= nx.nck;
+      if (req) request();
+      // start state at an item's first chunk, loaded here (before the next
+      // chunk's loads) so that its latency hides behind the chunk
+      // preparation; copied into the segment's own start slot unless the
+      // parent's item wrote it there (the first child)
+      bool copy = false;
+      float* own = seg_start_state + ((size_t)cur.s * H + cur.h) * SZ;
+      if (ci == 0) {
+        const float* src = nullptr;
+        copy = true;
+        if (cur.src < 0) {
+          if (root_state) src = root_state + ((size_t)(-1 - cur.src) * H + cur.h) * SZ;
+        } else {
+          src = seg_start_state + ((size_t)cur.src * H + cur.h) * SZ;
+          copy = cur.src != cur.s;
+        }
+#pragma unroll
+        for (int db = 0; db < DK / 16; ++db)
+          St[db] = src ? *(const f32x4_t*)(src + srow + 16 * db) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (has_next) issue(other, nx, nci);
+      const int t0 = cur.st + CH * ci, len = min(CH, cur.L - CH * ci);
+      prep_chunk(b, len);
+      if (req) publish();
+      if (copy) {
+#pragma unroll
+        for (int db = 0; db < DK / 16; ++db) *(f32x4_t*)(own + srow + 16 * db) = St[db];
+      }
+      const bool last = ci + 1 == cur.nck;
+      const int fc = cur.fc;
+      const bool need_state = !last || fc >= 0 || seg_final_state != nullptr;
+      scan_chunk(b, cur, t0, len, need_state);
+      if (last) {
+        if (seg_final_state) {
+          float* d = seg_final_state + ((size_t)cur.s * H + cur.h) * SZ;
+#pragma unroll
+          for (int db = 0; db < DK / 16; ++db) *(f32x4_t*)(d + srow + 16 * db) = St[db];
+        }
+        if (fc >= 0) {
+          float* d = seg_start_state + ((size_t)fc * H + cur.h) * SZ;
+#pragma unroll
+          for (int db = 0; db < DK / 16; ++db) *(f32x4_t*)(d + srow + 16 * db) = St[db];
+        }
+      }
+      // the prep region is rewritten by the next chunk only after its B0 and
+      // decay barrier, which every wave reaches after this scan
+      cur = nx;
+      ci = nci;
+      return has_next;
+    };
+    for (;;) {
+      if (!step(buf0, buf1)) break;
+      if (!step(buf1, buf0)) break;
+    }
+  }
+  if (tid == 0) {
+    __threadfence();  // (the last request has returned)
+    if (atomicAdd(ctr + 1, 1) == (int)gridDim.x - 1) {
+      // every other workgroup has made its last request: reset for the next launch
+      atomicExch(ctr, 0);
+      atomicExch(ctr + 1, 0);
+    }
+  }
+}
+
 template <bool BF16, int DK>
 fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   const bool cap = stream_capturing(stream);
   const int cus = device_cu_count();
-  int grid = PrepCfg<BF16, DK>::PER_CU * cus;
+  const int sgrid = (cus + 7) / 8 * 8;  // one workgroup per CU (LDS); a multiple of 8: item i runs on XCD i mod 8
+  // bf16 with dk = 128: the fused kernel prepares and scans every segment
+  // except the latency-bound long ones gdn_coop_kernel takes, whose chunks
+  // alone go through gdn_prep_kernel and the workspace
+  constexpr bool FUSED = BF16 && DK == FusedCfg::DK;
+  a.sgrid = sgrid;
+  a.prep_coop_only = FUSED ? 1 : 0;
+  // per depth: [first segment in the level list, segments, coop's share]
+  // when the host plans (outside capture)
+  const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
+  bool any_coop = false;
   if (!cap) {
-    const long long items = (long long)m->num_chunks * a.H;
-    if (items < grid) grid = (int)(items > 0 ? items : 1);
+    for (int lv = 0; lv < levels && lv < FORK_PLAN_DEPTHS; ++lv) {
+      const long long coop_items = (long long)m->level_long[lv] * ((a.H + 7) / 8) * 8 * (DK / 16);
+      any_coop |= BF16 && m->level_long[lv] > 0 && coop_items <= sgrid;
+    }
+    if (m->max_depth >= FORK_PLAN_DEPTHS) any_coop = true;  // (unplanned depths decide in the kernels)
   }
-  hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a.blob, a);
-  FORK_HIP_CHECK(hipGetLastError());
+  if (!FUSED || cap || any_coop) {
+    int grid = PrepCfg<BF16, DK>::PER_CU * cus;
+    if (!cap && !FUSED) {
+      const long long items = (long long)m->num_chunks * a.H;
+      if (items < grid) grid = (int)(items > 0 ? items : 1);
+    }
+    hipLaunchKernelGGL((gdn_prep_kernel<BF16, DK>), dim3(grid), dim3(256), 0, stream, a.blob, a);
+    FORK_HIP_CHECK(hipGetLastError());
+  }
   // Scan launches per depth (children start after their parents ended): the
   // chunk-cooperative kernel for a latency-bound set of long segments, the
-  // per-slice kernel for the rest. Under capture, every depth up to the
-  // capacity is recorded with both kernels, which split the depth from the
-  // blob; depths beyond the current tree exit at once.
-  const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
-  const int sgrid = (cus + 7) / 8 * 8;  // one workgroup per CU (LDS); a multiple of 8: item i runs on XCD i mod 8
-  int first = 0;                        // first segment of the depth in the blob's level list
+  // fused (bf16, dk 128) or per-slice kernel for the rest. Under capture,
+  // every depth up to the capacity is recorded with both kernels, which split
+  // the depth from the blob; depths beyond the current tree exit at once.
+  int first = 0;  // first segment of the depth in the blob's level list
   for (int lv = 0; lv < levels; ++lv) {
     a.level = lv;
     bool run_coop = BF16, run_scan = true;
@@ -1667,8 +2190,17 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
       }
     }
     if (run_scan) {
-      hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream,
-                         a.blob, a);
+      if constexpr (FUSED) {
+        int grid = sgrid;
+        if (!cap && a.lv_first >= 0) {
+          const long long items = (long long)(a.lv_count - a.lv_take) * a.H;
+          if (items < grid) grid = (int)items;
+        }
+        hipLaunchKernelGGL((gdn_fused_kernel<DK>), dim3(grid), dim3(FusedCfg::NT), 0, stream, a.blob, a);
+      } else {
+        hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream,
+                           a.blob, a);
+      }
       FORK_HIP_CHECK(hipGetLastError());
     }
   }
@@ -1702,11 +2234,14 @@ fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const v
   g.seg_start = seg_start_state;
   g.seg_final = seg_final_state;
   g.ws = (unsigned char*)ws;
+  g.ctr = (int32_t*)m->dev + kGdnCtrWord;
   g.guard = blob_guard(m->caps);
   g.H = H;
   g.scale = scale;
   g.level = 0;
   g.lv_first = g.lv_count = g.lv_take = -1;
+  g.prep_coop_only = 0;
+  g.sgrid = 0;
   if (dt == FORK_BF16) {
     if (dk == 128) return launch_gdn_t<true, 128>(m, g, stream);
     if (dk == 64) return launch_gdn_t<true, 64>(m, g, stream);
