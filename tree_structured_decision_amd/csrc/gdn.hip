@@ -1686,7 +1686,7 @@ struct FusedCfg {
   static constexpr int OQ = TB, OV = 2 * TB, OA = 3 * TB, OB = OA + CH * 4;
   static constexpr int BUF = OB + CH * 4;              // one chunk's operands
   static constexpr int LDA = CH + 4;                   // fp32 64x64 A and T rows
-  static constexpr int PA = 0, PT = PA + CH * LDA * 4, PTH = PT + CH * LDA * 4, PPH = PTH + (int)kWsFrag;
+  static constexpr int PA = 0, PT = PA + CH * LDA * 4, PPH = PT + CH * LDA * 4;
   static constexpr int PGAM = PPH + (int)kWsFrag, PRR = PGAM + CH * 4, PGS = PRR + CH * 4, PBS = PGS + CH * 4;
   static constexpr int PREP = PBS + CH * 4;
   static_assert(2 * BUF + PREP <= 160 * 1024, "LDS");
@@ -1792,127 +1792,14 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     }
   };
 
-  // ---- chunk preparation (operands of the chunk in b)
-  auto prep_chunk = [&](const unsigned char* b, int len) __attribute__((always_inline)) {
+  // The state (St: lane (c16, q4) holds S[e0 + c16][16 db + 4 q4 + r], S^T
+  // blocks) and its products with the chunk, X = K S^T and Y^T = S Q^T
+  // (block I: rows 16 I + 4 q4 + r of X and Y, state row e0 + c16), which
+  // need nothing from the chunk preparation.
+  f32x4_t St[DK / 16], X[4], Yt[4];
+  auto state_products = [&](const unsigned char* b) __attribute__((always_inline)) {
     const E* Ks = (const E*)b;
     const E* Qs = (const E*)(b + F::OQ);
-    if (w == 0) {
-      const float a = ((const float*)(b + F::OA))[lane];
-      const float la = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
-      const float gl = lane_val(la, CH - 1);
-      gs[lane] = la;
-      bs[lane] = lane < len ? ((const float*)(b + F::OB))[lane] : 0.f;
-      gam[lane] = __expf(la);
-      rrv[lane] = __expf(gl - la);
-    }
-    lds_barrier();  // g, b, gamma
-    if (w < 4) {
-      // Pt_J = K_J Q_w^T, At_J = K_J K_w^T for J <= w (16x16x32 bf16, k-order of a 16-byte row read)
-      f32x4_t pt[4], at[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) pt[J] = at[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8_t bq = *(const bf16x8_t*)(Qs + kq_off<DK>(16 * w + c16, 32 * ks + 8 * q4));
-        const bf16x8_t bk = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * w + c16, 32 * ks + 8 * q4));
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          if (J <= w) {
-            const bf16x8_t aK = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * J + c16, 32 * ks + 8 * q4));
-            pt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bq, pt[J], 0, 0, 0);
-            at[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bk, at[J], 0, 0, 0);
-          }
-        }
-      }
-      // lane (c16, q4): row i = 16 w + c16, columns j = 16 J + 4 q4 + r
-      const int i = 16 * w + c16;
-      const float gi = gs[i], bi = bs[i];
-      f32x4_t pv[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        pv[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (J <= w) {
-          const f32x4_t gj = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
-          f32x4_t av;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J + 4 * q4 + r;
-            const float dec = j <= i ? __expf(gi - gj[r]) : 0.f;
-            pv[J][r] = dec * pt[J][r];
-            av[r] = j < i ? bi * dec * at[J][r] : 0.f;
-          }
-          *(f32x4_t*)(As + i * F::LDA + 16 * J + 4 * q4) = av;
-        }
-      }
-      u32x4_t* Pw = (u32x4_t*)(prep + F::PPH);
-#pragma unroll
-      for (int kf = 0; kf < 2; ++kf) {
-        if (kf < frag_nk(w)) {
-          const int fb = frag_tri(w) + kf;
-          u32x2_t h0, l0, h1, l1;
-          split4(pv[2 * kf], h0, l0);
-          split4(pv[2 * kf + 1], h1, l1);
-          Pw[(2 * fb) * 64 + lane] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
-          Pw[(2 * fb + 1) * 64 + lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
-        }
-      }
-      // diagonal block w of T (its rows of A are this wave's own stores)
-      diag_inverse(As, Ts, F::LDA, 16 * w, lane);
-    }
-    lds_barrier();
-    // blocks of T below the diagonal, by distance d = I - J (wave J)
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      const int I = w + d, J = w;
-      if (w < 4 && I < 4) {
-        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        for (int Kb = J; Kb < I; ++Kb) {
-          const f32x4_t a4 = *(const f32x4_t*)(As + (16 * I + c16) * F::LDA + 16 * Kb + 4 * q4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z = mma_f32(a4[r], Ts[(16 * Kb + 4 * q4 + r) * F::LDA + 16 * J + c16], z);
-        }
-        const f32x4_t t4 = *(const f32x4_t*)(Ts + (16 * I + c16) * F::LDA + 16 * I + 4 * q4);
-        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t = mma_f32(t4[r], z[r], t);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * q4 + r) * F::LDA + 16 * J + c16] = -t[r];
-      }
-      lds_barrier();
-    }
-    // T'' = T diag(b) (zero above the diagonal) as hi / lo operand fragments
-    if (tid < kNtri * 64) {
-      const int fb = tid >> 6, l = tid & 63;
-      const int I = fb < 3 ? fb : (fb == 3 ? 2 : 3), kf = fb - frag_tri(I);
-      const int ti = 16 * I + (l & 15), j0 = 32 * kf + 4 * (l >> 4);
-      f32x4_t t0, t1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t0[e] = j0 + e <= ti ? Ts[ti * F::LDA + j0 + e] * bs[j0 + e] : 0.f;
-        t1[e] = j0 + 16 + e <= ti ? Ts[ti * F::LDA + j0 + 16 + e] * bs[j0 + 16 + e] : 0.f;
-      }
-      u32x2_t h0, l0, h1, l1;
-      split4(t0, h0, l0);
-      split4(t1, h1, l1);
-      u32x4_t* Tw = (u32x4_t*)(prep + F::PTH);
-      Tw[(2 * fb) * 64 + l] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
-      Tw[(2 * fb + 1) * 64 + l] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
-    }
-    lds_barrier();  // T'', P and the decays are complete
-  };
-
-  // ---- one chunk of the scan for this wave's slice (operands in b; the
-  // prepared T'', P and decays in prep). St: lane (c16, q4) holds
-  // S[e0 + c16][16 db + 4 q4 + r] (S^T blocks).
-  f32x4_t St[DK / 16];
-  auto scan_chunk = [&](const unsigned char* b, const Item& r, int t0, int len, bool need_state) __attribute__((always_inline)) {
-    const E* Ks = (const E*)b;
-    const E* Qs = (const E*)(b + F::OQ);
-    const E* Vs = (const E*)(b + F::OV);
-    const u32x4_t* Th = (const u32x4_t*)(prep + F::PTH);
-    const u32x4_t* Ph = (const u32x4_t*)(prep + F::PPH);
-    // (1) X = K S^T, Y^T = S Q^T
-    f32x4_t X[4], Yt[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Yt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1929,6 +1816,102 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
         Yt[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, qb, Yt[I], 0, 0, 0);
       }
     }
+  };
+
+  // ---- chunk preparation (operands of the chunk in b). Waves 0-3 form row
+  // block w of P = QK^T * Gamma (as hi / lo fragments), waves 4-7 row block
+  // w - 4 of A and the inverse of its diagonal block; wave 0 then computes
+  // the decays, which the products do not need. Each wave then forms its
+  // state products (they overlap the diagonal inverses on the same SIMDs).
+  auto prep_chunk = [&](const unsigned char* b, int len) __attribute__((always_inline)) {
+    const E* Ks = (const E*)b;
+    const E* Qs = (const E*)(b + F::OQ);
+    const int rb = w & 3;      // this wave's row block
+    const bool kk = w >= 4;    // K K^T (A) rather than Q K^T (P)
+    // Xt_J = K_J X_rb^T for J <= rb, X = Q or K (16x16x32 bf16, k-order of a
+    // 16-byte row read); lane (c16, q4) holds row i = 16 rb + c16 of XK^T at
+    // columns j = 16 J + 4 q4 + r
+    f32x4_t xt[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) xt[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const E* Xs = kk ? Ks : Qs;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const bf16x8_t bx = *(const bf16x8_t*)(Xs + kq_off<DK>(16 * rb + c16, 32 * ks + 8 * q4));
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J <= rb) {
+          const bf16x8_t aK = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * J + c16, 32 * ks + 8 * q4));
+          xt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bx, xt[J], 0, 0, 0);
+        }
+      }
+    }
+    if (w == 0) {
+      const float a = ((const float*)(b + F::OA))[lane];
+      const float la = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
+      const float gl = lane_val(la, CH - 1);
+      gs[lane] = la;
+      bs[lane] = lane < len ? ((const float*)(b + F::OB))[lane] : 0.f;
+      gam[lane] = __expf(la);
+      rrv[lane] = __expf(gl - la);
+    }
+    lds_barrier();  // g, b, gamma
+    const int i = 16 * rb + c16;
+    const float gi = gs[i], bi = bs[i];
+    f32x4_t gj[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) gj[J] = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
+    if (!kk) {
+      // P = Q K^T * Gamma (j <= i), stored as fragments
+      f32x4_t pv[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * J + 4 * q4 + r;
+          pv[J][r] = J <= rb && j <= i ? __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
+        }
+      }
+      u32x4_t* Pw = (u32x4_t*)(prep + F::PPH);
+#pragma unroll
+      for (int kf = 0; kf < 2; ++kf) {
+        if (kf < frag_nk(rb)) {
+          const int fb = frag_tri(rb) + kf;
+          u32x2_t h0, l0, h1, l1;
+          split4(pv[2 * kf], h0, l0);
+          split4(pv[2 * kf + 1], h1, l1);
+          Pw[(2 * fb) * 64 + lane] = u32x4_t{h0.x, h0.y, h1.x, h1.y};
+          Pw[(2 * fb + 1) * 64 + lane] = u32x4_t{l0.x, l0.y, l1.x, l1.y};
+        }
+      }
+    } else {
+      // A = strictly_lower(diag(b) K K^T * Gamma)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J <= rb) {
+          f32x4_t av;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * J + 4 * q4 + r;
+            av[r] = j < i ? bi * __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
+          }
+          *(f32x4_t*)(As + i * F::LDA + 16 * J + 4 * q4) = av;
+        }
+      }
+      // the inverse of diagonal block rb of I + A (its rows of A are this
+      // wave's own stores)
+      diag_inverse(As, Ts, F::LDA, 16 * rb, lane);
+    }
+    state_products(b);
+    lds_barrier();  // P, A, the diagonal inverses and the decays are complete
+  };
+
+  // ---- one chunk of the scan for this wave's slice (operands in b; P, A,
+  // the diagonal inverses and the decays in prep; X and Y^T formed)
+  auto scan_chunk = [&](const unsigned char* b, const Item& r, int t0, int len, bool need_state) __attribute__((always_inline)) {
+    const E* Ks = (const E*)b;
+    const E* Vs = (const E*)(b + F::OV);
+    const u32x4_t* Ph = (const u32x4_t*)(prep + F::PPH);
     // (2) R = V - gamma X: lane (c16, q4), block I holds R[16 I + 4 q4 + r][e0 + c16]
     f32x4_t R[4];
 #pragma unroll
@@ -1939,21 +1922,39 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
 #pragma unroll
       for (int k = 0; k < 4; ++k) R[I][k] = bf16_val((unsigned short)v4[k]) - g4[k] * X[I][k];
     }
-    bf16x8_t rh[2], rl[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) reg_frag<true>(R, f, rh[f], rl[f]);
-    // (3) U = T'' R (T'' lower triangular: row block I reduces over tokens < 16 (I + 1))
+    // (3) U = T'' R = (I + A)^-1 diag(b) R by block forward substitution:
+    // U_I = T_II (b_I R_I - sum_{K<I} A_IK U_K), T_II the inverse of the
+    // diagonal block of I + A (16x16x16 bf16 hi / lo products: a block's
+    // accumulator layout is the B operand layout of the next product)
     f32x4_t U[4];
+    s16x4_t ubh[3], ubl[3];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      U[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc = R[I] * *(const f32x4_t*)(bs + 16 * I + 4 * q4);
 #pragma unroll
-      for (int kf = 0; kf < frag_nk(I); ++kf) {
-        const bf16x8_t th = __builtin_bit_cast(bf16x8_t, Th[(frag_tri(I) + kf) * 128 + lane]);
-        const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, Th[(frag_tri(I) + kf) * 128 + 64 + lane]);
-        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kf], U[I], 0, 0, 0);
-        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kf], U[I], 0, 0, 0);
-        U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kf], U[I], 0, 0, 0);
+      for (int K = 0; K < I; ++K) {
+        const f32x4_t a4 = -*(const f32x4_t*)(As + (16 * I + c16) * F::LDA + 16 * K + 4 * q4);
+        u32x2_t ah, al;
+        split4(a4, ah, al);
+        const s16x4_t ahs = __builtin_bit_cast(s16x4_t, ah), als = __builtin_bit_cast(s16x4_t, al);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahs, ubh[K], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahs, ubl[K], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(als, ubh[K], acc, 0, 0, 0);
+      }
+      u32x2_t ch, cl, th, tl;
+      split4(acc, ch, cl);
+      split4(*(const f32x4_t*)(Ts + (16 * I + c16) * F::LDA + 16 * I + 4 * q4), th, tl);
+      const s16x4_t ths = __builtin_bit_cast(s16x4_t, th), tls = __builtin_bit_cast(s16x4_t, tl);
+      const s16x4_t chs = __builtin_bit_cast(s16x4_t, ch), cls = __builtin_bit_cast(s16x4_t, cl);
+      f32x4_t u = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ths, chs, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ths, cls, u, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tls, chs, u, 0, 0, 0);
+      U[I] = u;
+      if (I < 3) {
+        u32x2_t uh, ul;
+        split4(u, uh, ul);
+        ubh[I] = __builtin_bit_cast(s16x4_t, uh);
+        ubl[I] = __builtin_bit_cast(s16x4_t, ul);
       }
     }
     // (4) O^T = scale (gamma Y^T + U^T P^T): lane (c16, q4), block I holds
