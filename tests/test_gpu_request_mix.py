@@ -12,7 +12,11 @@ and of three options, and their start and final states. Requests never see
 each other, so the oracle runs on each sampled request alone (the inputs are
 drawn per request, so they are the very values the stream holds). The fork
 copy is checked bitwise on every child of the mix: its start state equals its
-parent's final state exactly, and every root starts from zero."""
+parent's final state exactly, and every root starts from zero. A second graph
+of the same bucket, recorded without end states as the benchmark runs it
+(leaf options then run packed, several to a chunk), is checked the same way
+on the Gated DeltaNet (o and start states, and the fork copies bitwise equal
+across siblings)."""
 import os
 
 import numpy as np
@@ -108,7 +112,7 @@ def host(x, rows):
     return x[rows].float().cpu().numpy().astype(np.float64)
 
 
-def check_requests(parent, seg_len, seed, out):
+def check_requests(parent, seg_len, seed, out, attn=True, final=True):
     picks, spans = sample_requests(parent, seg_len, seed)
     for r in picks:
         a, b, t0, t1 = spans[r]
@@ -125,9 +129,10 @@ def check_requests(parent, seg_len, seed, out):
         rows = np.array(sorted(set(rows)))
         sel = np.zeros(wl.T, np.uint8)
         sel[rows] = 1
-        o_ref, lse_ref = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, tok_select=sel)
-        check_close(f"req {r} attn.o", host(out["o"], t0 + rows), o_ref[rows], "bf16")
-        check_close(f"req {r} attn.lse", host(out["lse"], t0 + rows), lse_ref[rows], "bf16", kind="f32")
+        if attn:
+            o_ref, lse_ref = oracle.attention(wl.parent, wl.seg_len, wl.q, wl.k, wl.v, tok_select=sel)
+            check_close(f"req {r} attn.o", host(out["o"], t0 + rows), o_ref[rows], "bf16")
+            check_close(f"req {r} attn.lse", host(out["lse"], t0 + rows), lse_ref[rows], "bf16", kind="f32")
         gsegs = [0, 1, n_opt] if n_opt > 1 else [0, 1]
         gsegs = sorted(set(gsegs + [int(rng.integers(1, n_opt + 1))]))
         ssel = np.zeros(wl.S, np.uint8)
@@ -138,7 +143,9 @@ def check_requests(parent, seg_len, seed, out):
         check_close(f"req {r} gdn.o (segments {gsegs})", host(out["go"], t0 + trows), go_ref[trows], "bf16")
         segs = np.array(gsegs)
         check_close(f"req {r} gdn.start_state", host(out["s0"], a + segs), s0_ref[segs], "bf16", kind="f32")
-        check_close(f"req {r} gdn.final_state", host(out["s1"], a + segs), s1_ref[segs], "bf16", kind="f32")
+        if final:
+            check_close(f"req {r} gdn.final_state", host(out["s1"], a + segs), s1_ref[segs], "bf16",
+                        kind="f32")
 
 
 def test_request_mix_full_size_graph_replay(bucket):
@@ -151,3 +158,52 @@ def test_request_mix_second_seed_same_bucket(bucket):
     parent, seg_len = replay_seed(bucket, SEEDS[1])
     check_fork_bitwise(parent, bucket[2])
     check_requests(parent, seg_len, SEEDS[1], bucket[2])
+
+
+@pytest.fixture(scope="module")
+def bucket_packed(bucket):
+    """A second graph of the same bucket and inputs, recorded without end
+    states, the way the benchmark runs the Gated DeltaNet: leaf siblings then
+    run packed, several to a chunk."""
+    _, t, _, stream = bucket
+    rng = np.random.Generator(np.random.PCG64(SEEDS[0]))
+    parent, seg_len = W.request_mix_tree(rng)
+    t_cap, s_cap = pick_bucket(int(seg_len.sum()), len(parent))
+    sess = ForkSession(t_cap, s_cap, BUCKET_DEPTH, H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
+    dev = "cuda"
+    out = dict(o=torch.empty((t_cap, H, D), dtype=torch.bfloat16, device=dev),
+               lse=torch.empty((t_cap, H), device=dev),
+               go=torch.empty((t_cap, GH, DK), dtype=torch.bfloat16, device=dev),
+               s0=torch.empty((s_cap, GH, DK, DK), device=dev))
+    with torch.cuda.stream(stream):
+        sess.build(parent, seg_len)
+        sess.capture(dict(q=t["q"], k=t["k"], v=t["v"], o=out["o"], lse=out["lse"]),
+                     dict(q=t["gq"], k=t["gk"], v=t["gv"], a=t["a"], b=t["b"], o=out["go"],
+                          seg_start_state=out["s0"]))
+    torch.cuda.synchronize()
+    yield sess, t, out, stream
+    sess.close()
+
+
+def check_siblings_bitwise(parent, out):
+    """Without end states: every child's start state equals, bit for bit, the
+    start state of its parent's first child (where the parent's end state
+    was written); roots start at zero."""
+    s0 = out["s0"]
+    kids = np.flatnonzero(parent >= 0)
+    first = {}
+    for c in kids:
+        first.setdefault(int(parent[c]), int(c))
+    for i in range(0, len(kids), 256):
+        c = torch.from_numpy(kids[i:i + 256]).cuda()
+        f = torch.from_numpy(np.array([first[int(parent[x])] for x in kids[i:i + 256]], np.int64)).cuda()
+        assert torch.equal(s0.index_select(0, c).view(torch.int32), s0.index_select(0, f).view(torch.int32))
+    roots = torch.from_numpy(np.flatnonzero(parent < 0)).cuda()
+    assert torch.equal(s0.index_select(0, roots), torch.zeros_like(s0.index_select(0, roots)))
+    log(f"  fork copies bitwise equal across siblings on {len(kids)} children")
+
+
+def test_request_mix_packed_gdn_graph_replay(bucket_packed):
+    parent, seg_len = replay_seed(bucket_packed, SEEDS[0])
+    check_siblings_bitwise(parent, bucket_packed[2])
+    check_requests(parent, seg_len, SEEDS[0], bucket_packed[2], attn=False, final=False)

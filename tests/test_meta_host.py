@@ -21,7 +21,7 @@ H_NAMES = ["MAGIC", "T", "S", "R", "MAXDEPTH", "NTILES", "NCHUNKS", "TILE_TOKENS
            "OFF_ANCLEN", "OFF_FIRSTCHILD", "OFF_CHUNKBASE", "OFF_LEVELOFF", "OFF_LEVELSEG",
            "OFF_CHUNKS", "OFF_TILES", "OFF_TOKSEG", "OFF_TOKPOS", "OFF_TOKISO", "UPLOAD_WORDS",
            "NMERGE", "OFF_MERGE", "NPARTS", "KV_HEADS", "OFF_LEVELLONG", "OFF_CTXSTART",
-           "OFF_CTXLEN", "NCTX", "OFF_GDNREC"]
+           "OFF_CTXLEN", "NCTX", "OFF_GDNREC", "OFF_GDNPACK", "OFF_PACKOFF"]
 HI = {n: i for i, n in enumerate(H_NAMES)}
 ATTN_ROWS = int(re.search(r"kAttnRows = (\d+);", open(os.path.join(
     ROOT, "tree_structured_decision_amd", "csrc", "common.h")).read()).group(1))
@@ -117,8 +117,37 @@ def check_plan(parent, seg_len, gqa, kv_heads=0, ctx=None):
     first = {s: (np.flatnonzero(parent == s)[0] if np.any(parent == s) else -1) for s in range(S)}
     for i, s in enumerate(ls):
         src = first[parent[s]] if parent[s] >= 0 else -1 - int(np.flatnonzero(roots == s)[0])
-        want = (s, ref["seg_start"][s], seg_len[s], src, first[s], 0, 0, 0)
+        want = (s, ref["seg_start"][s], seg_len[s], src, first[s], 1, 0, 0)
         assert tuple(rec[i]) == want, (i, s, tuple(rec[i]), want)
+    # the packed list: runs of consecutive leaf siblings of at most 64 tokens
+    # in total share a record (greedily, in index order); every other segment
+    # has its own; longest first within a depth, with the segments longer than
+    # a chunk in the level list's order
+    leaf = lambda s: parent[s] >= 0 and first[s] == -1 and seg_len[s] <= 64
+    po = arr(w, "PACKOFF", maxd + 2)
+    pk = arr(w, "GDNPACK", 8 * int(po[maxd + 1])).reshape(-1, 8)
+    covered, pack_of = [], {}
+    for d in range(maxd + 1):
+        items = pk[po[d]:po[d + 1]]
+        assert np.all(np.diff(items[:, 2]) <= 0)
+        np.testing.assert_array_equal(items[:ll[d], 0], ls[lo[d]:lo[d] + ll[d]])
+        for k, (s0, st, L, src, fc, nsib, p0, p1) in enumerate(items):
+            segs = np.arange(s0, s0 + nsib)
+            covered += segs.tolist()
+            for s in segs:
+                pack_of[int(s)] = (d, k)
+            assert np.all(ref["depth"][segs] == d) and (p0, p1) == (0, 0)
+            assert st == ref["seg_start"][s0] and L == seg_len[segs].sum()
+            want_src = first[parent[s0]] if parent[s0] >= 0 else -1 - int(np.flatnonzero(roots == s0)[0])
+            assert src == want_src
+            if nsib > 1:
+                assert L <= 64 and all(leaf(s) for s in segs) and np.all(parent[segs] == parent[s0])
+            assert fc == (-1 if nsib > 1 else first[s0])
+    assert sorted(covered) == list(range(S))
+    for s in range(S - 1):
+        if leaf(s) and leaf(s + 1) and parent[s] == parent[s + 1] and pack_of[s] != pack_of[s + 1]:
+            d, k = pack_of[s]
+            assert pk[po[d] + k][2] + seg_len[s + 1] > 64, "two joinable siblings left apart"
     # chunks: 64-token pieces of each segment, in order
     nch = w[HI["NCHUNKS"]]
     ch = arr(w, "CHUNKS", 2 * nch).reshape(-1, 2)

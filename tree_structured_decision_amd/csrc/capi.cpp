@@ -319,13 +319,44 @@ static fork_status plan_impl(const int32_t* parent, const int32_t* seg_len, cons
       }
   }
   {
-    // the scan items' records, in level order (GdnRec)
+    // the scan items' records (GdnRec): one per segment in level order, and
+    // the packed list (runs of consecutive leaf siblings of at most a chunk
+    // in total share a record), longest first within each depth
+    auto src_of = [&](int32_t s) { return parent[s] < 0 ? -1 - root_ord[s] : first_child[parent[s]]; };
     std::vector<GdnRec> rec(S);
     for (int32_t i = 0; i < S; ++i) {
-      const int32_t s = level_seg[i], p = parent[s];
-      rec[i] = GdnRec{s, start[s], seg_len[s], p < 0 ? -1 - root_ord[s] : first_child[p], first_child[s], 0, 0, 0};
+      const int32_t s = level_seg[i];
+      rec[i] = GdnRec{s, start[s], seg_len[s], src_of(s), first_child[s], 1, 0, 0};
     }
     put(MH_OFF_GDNREC, (const int32_t*)rec.data(), (int64_t)S * kGdnRecWords);
+    auto leaf = [&](int32_t s) { return parent[s] >= 0 && first_child[s] < 0 && seg_len[s] <= kChunk; };
+    std::vector<GdnRec> packs;
+    std::vector<int32_t> pack_depth;
+    for (int32_t s = 0; s < S; ++s) {
+      if (leaf(s) && !packs.empty() && packs.back().seg + packs.back().nsib == s && packs.back().nsib > 0 &&
+          parent[packs.back().seg] == parent[s] && leaf(packs.back().seg) &&
+          packs.back().len + seg_len[s] <= kChunk) {
+        packs.back().len += seg_len[s];
+        packs.back().nsib += 1;
+        continue;
+      }
+      packs.push_back(GdnRec{s, start[s], seg_len[s], src_of(s), first_child[s], 1, 0, 0});
+      pack_depth.push_back(depth[s]);
+    }
+    std::vector<int32_t> pack_off(max_depth + 2, 0), order(packs.size());
+    for (int32_t d : pack_depth) pack_off[d + 1]++;
+    for (int32_t d = 0; d <= max_depth; ++d) pack_off[d + 1] += pack_off[d];
+    {
+      std::vector<int32_t> fill(pack_off.begin(), pack_off.end() - 1);
+      for (size_t i = 0; i < packs.size(); ++i) order[fill[pack_depth[i]]++] = (int32_t)i;
+      for (int32_t d = 0; d <= max_depth; ++d)
+        std::stable_sort(order.begin() + pack_off[d], order.begin() + pack_off[d + 1],
+                         [&](int32_t x, int32_t y) { return packs[x].len > packs[y].len; });
+    }
+    std::vector<GdnRec> sorted_packs(packs.size());
+    for (size_t i = 0; i < packs.size(); ++i) sorted_packs[i] = packs[order[i]];
+    put(MH_OFF_GDNPACK, (const int32_t*)sorted_packs.data(), (int64_t)sorted_packs.size() * kGdnRecWords);
+    put(MH_OFF_PACKOFF, pack_off.data(), max_depth + 2);
   }
   put(MH_OFF_TILES, (const int32_t*)sorted.data(), (int64_t)sorted.size() * 8);
   put(MH_OFF_MERGE, (const int32_t*)merges.data(), (int64_t)merges.size() * 4);

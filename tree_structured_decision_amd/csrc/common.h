@@ -54,6 +54,8 @@ enum MetaHeader : int {
   MH_OFF_CTXLEN,      // [S] cache rows of a root's resumed context (0 for non-roots)
   MH_NCTX,            // roots with a nonempty context
   MH_OFF_GDNREC,      // [S x kGdnRecWords] Gated DeltaNet scan items in LEVELSEG order (GdnRec)
+  MH_OFF_GDNPACK,     // [<= S x kGdnRecWords] scan items with leaf siblings packed (GdnRec), by depth
+  MH_OFF_PACKOFF,     // [MAXDEPTH + 2] start of each depth in GDNPACK
   MH_WORDS = 64
 };
 // Header word 57 is the device error word (FORK_DEVERR_* bits, fork_meta_check).
@@ -68,7 +70,7 @@ constexpr int kNumXcd = 8;
 // work item of a depth's launch, then the number of workgroups that found no
 // more work), zero between launches like the attention counters.
 constexpr int kGdnCtrWord = 58;
-static_assert(kAttnCtrWord > MH_OFF_GDNREC && kAttnCtrWord + kNumXcd < kErrWord && kErrWord < kGdnCtrWord &&
+static_assert(kAttnCtrWord > MH_OFF_PACKOFF && kAttnCtrWord + kNumXcd < kErrWord && kErrWord < kGdnCtrWord &&
                   kGdnCtrWord + 2 <= MH_WORDS,
               "counter and error words inside the header, past the plan's words");
 
@@ -78,14 +80,20 @@ constexpr int kChunk = 64;                  // Gated DeltaNet chunk length
 constexpr int kAttnRows = 256;              // query rows (token x GQA head) per attention tile
 constexpr int kAttnKeys = 64;               // keys per staged key/value tile
 constexpr int kMaxDepthCap = 4096;
-// A Gated DeltaNet scan item's record (one per segment, in the blob's level
-// order), so that a scan workgroup learns everything about its next segment
-// from one load: the segment, its first token and length, the slot its start
-// state is copied from (the first child of its parent, which holds the
-// parent's end state; -1 - root ordinal for a root) and its first child (-1
-// for a leaf). Padded to 8 words (two 16-byte loads).
+// A Gated DeltaNet scan item's record, so that a scan workgroup learns
+// everything about its next item from one load: its first segment, first
+// token and length, the slot its start state is copied from (the first child
+// of its parent, which holds the parent's end state; -1 - root ordinal for a
+// root), the first child (-1 for a leaf) and the number of segments. GDNREC
+// holds one record per segment (nsib = 1) in the level order; GDNPACK the
+// same items except that runs of consecutive leaf siblings of at most one
+// chunk (kChunk tokens) in total share one record: they start from the same
+// state and no end state of theirs is carried on, so one chunk computes them
+// all (used when no end states are requested). Each depth of GDNPACK is
+// sorted longest first (stable), so its segments longer than a chunk lead it
+// in the same order as in LEVELSEG. Padded to 8 words (two 16-byte loads).
 struct GdnRec {
-  int32_t seg, start, len, src, first_child, pad0, pad1, pad2;
+  int32_t seg, start, len, src, first_child, nsib, pad0, pad1;
 };
 constexpr int kGdnRecWords = 8;
 static_assert(sizeof(GdnRec) == 4 * kGdnRecWords, "GdnRec layout");
@@ -144,7 +152,7 @@ inline BlobLayout blob_layout(const fork_caps& c) {
   // + 4 per merge group + the scan items' records, each array aligned to 4 words
   L.upload_cap_words = MH_WORDS + 12 * ((int64_t)c.s_cap + 4) + 2 * (c.depth_cap + 2 + 4) +
                        2 * L.chunk_cap + 4 + 8 * L.tile_cap + 4 + 4 * L.merge_cap + 4 +
-                       kGdnRecWords * (int64_t)c.s_cap + 4;
+                       2 * (kGdnRecWords * (int64_t)c.s_cap + 4) + c.depth_cap + 2 + 4;
   L.upload_cap_words = (L.upload_cap_words + 63) / 64 * 64;
   L.tok_off_words = L.upload_cap_words;
   L.total_words = L.tok_off_words + 3 * (((int64_t)c.t_cap + 63) / 64 * 64);

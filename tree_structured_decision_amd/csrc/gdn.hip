@@ -1683,12 +1683,12 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
 struct FusedCfg {
   static constexpr int DK = 128, NW = 8, NT = 64 * NW;
   static constexpr int TB = CH * DK * 2;               // a K, Q or V tile (bf16, kq_off layout)
-  static constexpr int OQ = TB, OV = 2 * TB, OA = 3 * TB, OB = OA + CH * 4;
-  static constexpr int BUF = OB + CH * 4;              // one chunk's operands
+  static constexpr int OQ = TB, OV = 2 * TB, OA = 3 * TB, OB = OA + CH * 4, OP = OB + CH * 4;
+  static constexpr int BUF = OP + CH * 4;              // one chunk's operands (a, b, positions)
   static constexpr int LDA = CH + 4;                   // fp32 64x64 A and T rows
   static constexpr int PA = 0, PT = PA + CH * LDA * 4, PPH = PT + CH * LDA * 4;
   static constexpr int PGAM = PPH + (int)kWsFrag, PRR = PGAM + CH * 4, PGS = PRR + CH * 4, PBS = PGS + CH * 4;
-  static constexpr int PREP = PBS + CH * 4;
+  static constexpr int PSS = PBS + CH * 4, PREP = PSS + CH * 4;
   static_assert(2 * BUF + PREP <= 160 * 1024, "LDS");
   static constexpr int BLK = 3 * TB / 1024 / NW;       // 1 KB loads of K, Q and V per wave
   static_assert(BLK * NW * 1024 == 3 * TB, "tiles divide over the waves");
@@ -1707,13 +1707,19 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   const int level = args.level;
   const bool planned = args.lv_first >= 0;
   if (!planned && level > blob[MH_MAXDEPTH]) return;
-  const int32_t* __restrict__ level_off = blob + blob[MH_OFF_LEVELOFF];
-  const int32_t* __restrict__ gdn_rec = blob + blob[MH_OFF_GDNREC];
+  // without end states to store, leaf siblings run packed (GdnRec)
+  const bool packed = args.seg_final == nullptr;
+  const int32_t* __restrict__ level_off = blob + blob[packed ? MH_OFF_PACKOFF : MH_OFF_LEVELOFF];
+  const int32_t* __restrict__ gdn_rec = blob + blob[packed ? MH_OFF_GDNPACK : MH_OFF_GDNREC];
+  const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
   const int H = args.H;
   // the depth's first `take` segments are handled by gdn_coop_kernel
   const int take = planned ? args.lv_take : coop_segments(blob, level, H, DK);
-  const int lv0 = (planned ? args.lv_first : level_off[level]) + take;
-  const int nlev = (planned ? args.lv_first + args.lv_count : level_off[level + 1]) - lv0;
+  // (the packed list has its own offsets; its long segments lead each depth
+  // in the level list's order, so `take` skips the same ones)
+  const bool use_plan = planned && !packed;
+  const int lv0 = (use_plan ? args.lv_first : level_off[level]) + take;
+  const int nlev = (use_plan ? args.lv_first + args.lv_count : level_off[level + 1]) - lv0;
   const int nitems = nlev * H;
   // (the wave index as a scalar: branches on it stay scalar, so the compiler
   // keeps LDS accesses under them out of its waits for the LDS DMA below)
@@ -1740,11 +1746,12 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   float* rrv = (float*)(prep + F::PRR);
   float* gs = (float*)(prep + F::PGS);
   float* bs = (float*)(prep + F::PBS);
+  int* ss = (int*)(prep + F::PSS);  // per row: first row of its segment in the chunk (0: at or before it)
 
   // a work item: segment (longest first within the depth) and head, from
   // the segment's record (one load)
   struct Item {
-    int s, h, L, st, nck, src, fc;
+    int s, h, L, st, nck, src, fc, nsib;
   };
   auto item_at = [&](int it) __attribute__((always_inline)) {
     Item r;
@@ -1757,6 +1764,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     r.L = __builtin_amdgcn_readfirstlane(a.z);
     r.src = __builtin_amdgcn_readfirstlane(a.w);
     r.fc = __builtin_amdgcn_readfirstlane(b.x);
+    r.nsib = __builtin_amdgcn_readfirstlane(b.y);
     r.h = it - li * H;
     r.nck = (r.L + CH - 1) / CH;
     return r;
@@ -1789,6 +1797,9 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       const float* src = w == 0 ? Ag : Bg;
       __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)min(t0 + lane, tl) * H + r.h),
                                        (lds_void_t*)(b + (w == 0 ? F::OA : F::OB)), 4, 0, 0);
+    } else if (w == 2) {
+      __builtin_amdgcn_global_load_lds((const void*)(tok_pos + min(t0 + lane, tl)), (lds_void_t*)(b + F::OP), 4,
+                                       0, 0);
     }
   };
 
@@ -1847,9 +1858,17 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       }
     }
     if (w == 0) {
+      // g restarts at each segment's first row (packed siblings): from the
+      // row's position in its segment, sr = the row its segment starts at
+      // (rows past the chunk hold the last row's position and take its sr,
+      // so they keep its decay: g of the last row is the chunk's total)
       const float a = ((const float*)(b + F::OA))[lane];
-      const float la = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
+      const float L = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
+      const int sr = min(lane, len - 1) - ((const int*)(b + F::OP))[lane];
+      const float Lb = __shfl(L, sr > 0 ? sr - 1 : 0);
+      const float la = sr > 0 ? L - Lb : L;
       const float gl = lane_val(la, CH - 1);
+      ss[lane] = sr > 0 ? sr : 0;
       gs[lane] = la;
       bs[lane] = lane < len ? ((const float*)(b + F::OB))[lane] : 0.f;
       gam[lane] = __expf(la);
@@ -1858,9 +1877,18 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     lds_barrier();  // g, b, gamma
     const int i = 16 * rb + c16;
     const float gi = gs[i], bi = bs[i];
+    const int si = ss[i];
     f32x4_t gj[4];
+    int4 sj[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) gj[J] = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
+    for (int J = 0; J < 4; ++J) {
+      gj[J] = *(const f32x4_t*)(gs + 16 * J + 4 * q4);
+      sj[J] = *(const int4*)(ss + 16 * J + 4 * q4);
+    }
+    // (i, j) in one segment: same first row
+    auto same = [&](int J, int r) __attribute__((always_inline)) {
+      return (r == 0 ? sj[J].x : r == 1 ? sj[J].y : r == 2 ? sj[J].z : sj[J].w) == si;
+    };
     if (!kk) {
       // P = Q K^T * Gamma (j <= i), stored as fragments
       f32x4_t pv[4];
@@ -1869,7 +1897,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * J + 4 * q4 + r;
-          pv[J][r] = J <= rb && j <= i ? __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
+          pv[J][r] = J <= rb && j <= i && same(J, r) ? __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
         }
       }
       u32x4_t* Pw = (u32x4_t*)(prep + F::PPH);
@@ -1893,7 +1921,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 16 * J + 4 * q4 + r;
-            av[r] = j < i ? bi * __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
+            av[r] = j < i && same(J, r) ? bi * __expf(gi - gj[J][r]) * xt[J][r] : 0.f;
           }
           *(f32x4_t*)(As + i * F::LDA + 16 * J + 4 * q4) = av;
         }
@@ -2058,6 +2086,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
           nx.L = __builtin_amdgcn_readfirstlane(s_rec[2]);
           nx.src = __builtin_amdgcn_readfirstlane(s_rec[3]);
           nx.fc = __builtin_amdgcn_readfirstlane(s_rec[4]);
+          nx.nsib = __builtin_amdgcn_readfirstlane(s_rec[5]);
           nx.h = r - li * H;
           nx.nck = (nx.L + CH - 1) / CH;
         }
@@ -2068,18 +2097,15 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       if (req) request();
       // start state at an item's first chunk, loaded here (before the next
       // chunk's loads) so that its latency hides behind the chunk
-      // preparation; copied into the segment's own start slot unless the
-      // parent's item wrote it there (the first child)
-      bool copy = false;
-      float* own = seg_start_state + ((size_t)cur.s * H + cur.h) * SZ;
+      // preparation; copied into the start slot of each of the item's
+      // segments except the one the parent's item wrote it to (the first
+      // child)
       if (ci == 0) {
         const float* src = nullptr;
-        copy = true;
         if (cur.src < 0) {
           if (root_state) src = root_state + ((size_t)(-1 - cur.src) * H + cur.h) * SZ;
         } else {
           src = seg_start_state + ((size_t)cur.src * H + cur.h) * SZ;
-          copy = cur.src != cur.s;
         }
 #pragma unroll
         for (int db = 0; db < DK / 16; ++db)
@@ -2089,9 +2115,14 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       const int t0 = cur.st + CH * ci, len = min(CH, cur.L - CH * ci);
       prep_chunk(b, len);
       if (req) publish();
-      if (copy) {
+      if (ci == 0) {
+        for (int q = 0; q < cur.nsib; ++q) {
+          const int sq = cur.s + q;
+          if (sq == cur.src) continue;
+          float* own = seg_start_state + ((size_t)sq * H + cur.h) * SZ;
 #pragma unroll
-        for (int db = 0; db < DK / 16; ++db) *(f32x4_t*)(own + srow + 16 * db) = St[db];
+          for (int db = 0; db < DK / 16; ++db) *(f32x4_t*)(own + srow + 16 * db) = St[db];
+        }
       }
       const bool last = ci + 1 == cur.nck;
       const int fc = cur.fc;
