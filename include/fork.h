@@ -201,8 +201,10 @@ fork_status fork_meta_dense_mask(const fork_meta* m, uint8_t* mask, void* stream
  * LDS once per query tile and reused by every packed query row (GQA heads x
  * tokens of sibling segments). Supported: D in {64, 128}; H / Hkv must equal
  * the gqa_group the metadata was built for, and Hkv its kv_heads when that is
- * nonzero. The workspace holds fp32 partial results of split query tiles
- * (kv_heads != 0): fork_attn_workspace gives its size for the blob's
+ * nonzero. The workspace holds the partial results of split query tiles
+ * (kv_heads != 0): each part's normalised output in the output dtype (so a
+ * split tile's output is rounded to it once more than a whole tile's) and
+ * its fp32 log-sum-exp; fork_attn_workspace gives its size for the blob's
  * capacities; it may be null when that size is 0. Work is handed out from
  * counters kept in the metadata blob (zero after fork_meta_build, reset by
  * each launch): two attention launches on one blob must not overlap in time.
