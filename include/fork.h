@@ -273,6 +273,12 @@ fork_status fork_attn_forward_noalloc(const fork_meta* m, const void* q, const v
  * seg_final_state [S,H,dv,dk] float32 or null. States are row-major dv x dk.
  * Supported: dk == dv in {32, 64, 128}. The workspace holds per-chunk
  * intermediates; gdn_fork_workspace sizes it for the blob's capacities.
+ * With seg_final_state null (bf16, dk == 128), runs of consecutive leaf
+ * siblings of at most 64 tokens in total are computed together in one chunk
+ * from their shared start state (their outputs agree with the one-by-one
+ * computation to rounding; every start state, and so every fork copy, is
+ * bit for bit the same). Work is handed out from counters in the metadata
+ * blob, reset by each launch: two launches on one blob must not overlap.
  */
 fork_status gdn_fork_workspace(const fork_meta* m, int32_t H, int32_t dk, int32_t dv,
                                fork_dtype dt, size_t* bytes_h);
