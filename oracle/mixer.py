@@ -112,11 +112,12 @@ def _out(r, u, wo, residual, fp8=False):
 
 
 def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: bool = False,
-                    residual=None, prec: str = "f64", fp8: bool = False) -> np.ndarray:
+                    residual=None, prec: str = "f64", fp8: bool = False, return_u: bool = False):
     """y [T, dm] of the attention mixer (weights as workloads.mixer_weights()['attn']);
     with residual, residual + y. prec: precision of the attention oracle. fp8:
     every projection takes E4M3 operands (input per token and weight per
-    output channel, quantised as quantize_fp8)."""
+    output channel, quantised as quantize_fp8). return_u: also the output
+    projection's input u [T, H D]."""
     from . import attention, rope
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
@@ -129,15 +130,18 @@ def attention_mixer(parent, seg_len, x, W: dict, theta: float = 10000.0, bf16: b
     k = r(rope(parent, seg_len, _f32(k), theta=theta))
     o, _ = attention(parent, seg_len, _f32(q), _f32(k), _f32(v), prec=prec)
     u = r(gate(r(o), g, None, 0))
-    return _out(r, u.reshape(T, H * D), W["wo"], residual, fp8)
+    y = _out(r, u.reshape(T, H * D), W["wo"], residual, fp8)
+    return (y, u.reshape(T, H * D)) if return_u else y
 
 
 def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False,
-              return_state: bool = False, residual=None, prec: str = "f64", fp8: bool = False):
+              return_state: bool = False, residual=None, prec: str = "f64", fp8: bool = False,
+              return_u: bool = False):
     """y [T, dm] of the Gated DeltaNet mixer (weights as
     workloads.mixer_weights()['gdn']); with residual, residual + y; with
-    return_state also the per-segment start and end states. prec: precision
-    of the Gated DeltaNet oracle. fp8: as attention_mixer."""
+    return_state also the per-segment start and end states, with return_u
+    the output projection's input u [T, H dv] instead. prec: precision of the
+    Gated DeltaNet oracle. fp8: as attention_mixer."""
     from . import conv, gdn
     r = to_bf16 if bf16 else (lambda t: t)
     T = x.shape[0]
@@ -153,6 +157,8 @@ def gdn_mixer(parent, seg_len, x, W: dict, eps: float = 1e-6, bf16: bool = False
     z = r(_lin(x, W["wz"], fp8)).reshape(T, H, dv)
     u = r(gate(r(o), z, W["norm_w"], 1, eps))
     y = _out(r, u.reshape(T, H * dv), W["wo"], residual, fp8)
+    if return_u:
+        return y, u.reshape(T, H * dv)
     return (y, st0, st1) if return_state else y
 
 

@@ -14,6 +14,14 @@ Tolerances:
   the same points: relative RMS error <= 1e-2 and max error <= 5e-2 of the
   largest output (each intermediate may differ by one bf16 rounding where
   fp32 and fp64 straddle a rounding boundary; fp32 runs: 1e-4 relative);
+* bf16 mixers element by element against the exact oracle (fp64, nothing
+  rounded): |gpu - y| <= u0 |y| + kappa u0 (|u| |W_o|^T), u0 = 2^-8 the bf16
+  unit roundoff, u the output projection's input. The first term is the
+  rounding of y itself; the second charges each of the kappa bf16 roundings
+  on the longest path from x to u (projection, rotary embedding or the
+  convolution's normalised q / k / v, the layer's output, the gate) with a
+  relative error u0 of the quantity it rounds, carried to y through the
+  output projection with gain at most one; kappa = 4 for both mixers;
 * stacks of four layers: the same bar on the final hidden states, and the
   total-variation distance of every decision group's option softmax (the
   scoring head of the fidelity measure) within 1e-2 of the bf16-rounded
@@ -148,6 +156,19 @@ def to_dev_weights(Wd, dtype):
     return out
 
 
+KAPPA = 4  # bf16 roundings on the longest path from x to the output projection's input
+
+
+def compare_exact(name, got, y, u, wo):
+    """Element-wise bar against the exact oracle (module docstring)."""
+    u0 = 2.0 ** -8
+    tau = u0 * np.abs(y) + KAPPA * u0 * (np.abs(u) @ np.abs(np.asarray(wo, np.float64)).T)
+    err = np.abs(got - y)
+    ratio = float((err / tau).max())
+    log(f"  {name}: max |gpu - exact| {err.max():.3e}, max error / bound {ratio:.3f} (kappa {KAPPA})")
+    assert ratio <= 1.0, name
+
+
 def compare_mixer(name, got, ref, dtype):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     mx = np.abs(got - ref).max() / np.abs(ref).max()
@@ -176,6 +197,11 @@ def test_mixers_small_tree(dtype, fused):
     bf = dtype == "bf16"
     compare_mixer(f"attention mixer {dtype}", ya, OM.attention_mixer(parent, seg_len, x, Wt["attn"], bf16=bf), dtype)
     compare_mixer(f"GDN mixer {dtype}", yg, OM.gdn_mixer(parent, seg_len, x, Wt["gdn"], bf16=bf), dtype)
+    if bf:
+        y, u = OM.attention_mixer(parent, seg_len, x, Wt["attn"], return_u=True)
+        compare_exact("attention mixer bf16 vs exact", ya, y, u, Wt["attn"]["wo"])
+        y, u = OM.gdn_mixer(parent, seg_len, x, Wt["gdn"], return_u=True)
+        compare_exact("GDN mixer bf16 vs exact", yg, y, u, Wt["gdn"]["wo"])
 
 
 def test_mixers_one_request_full_size():
@@ -190,6 +216,10 @@ def test_mixers_one_request_full_size():
     yg = host(sess.gdn_mixer(xd, ForkSession.fuse_gdn_weights(to_dev_weights(Wt["gdn"], "bf16"))))
     compare_mixer("attention mixer one_request", ya, OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], bf16=True), "bf16")
     compare_mixer("GDN mixer one_request", yg, OM.gdn_mixer(wl.parent, wl.seg_len, x, Wt["gdn"], bf16=True), "bf16")
+    y, u = OM.attention_mixer(wl.parent, wl.seg_len, x, Wt["attn"], return_u=True)
+    compare_exact("attention mixer one_request vs exact", ya, y, u, Wt["attn"]["wo"])
+    y, u = OM.gdn_mixer(wl.parent, wl.seg_len, x, Wt["gdn"], return_u=True)
+    compare_exact("GDN mixer one_request vs exact", yg, y, u, Wt["gdn"]["wo"])
 
 
 def dev_stack(layers, fn, dtype):
