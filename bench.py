@@ -201,7 +201,7 @@ class Runner:
 
     def __init__(self, wl_meta: dict, tensors: dict, graph: bool):
         import torch
-        from tree_structured_decision_amd.session import BUCKET_DEPTH, ForkSession, pick_bucket
+        from tree_structured_decision_amd.session import ForkSession, pick_bucket, pick_depth_cap
 
         self.m = wl_meta
         self.t = tensors
@@ -209,7 +209,7 @@ class Runner:
         depth = wl_meta["depth"]
         if graph:
             t_cap, s_cap = pick_bucket(T, S)
-            depth_cap = max(BUCKET_DEPTH, depth)
+            depth_cap = pick_depth_cap(depth)
         else:
             t_cap, s_cap, depth_cap = T, S, depth
         self.caps = (t_cap, s_cap, depth_cap)

@@ -1,8 +1,8 @@
 """The request mix (64 decision requests flattened into one stream, bf16,
 attention 16/2/128, Gated DeltaNet 16 x 128 x 128) at full size, run the way
 the benchmark runs it: replay of a graph recorded for its capacity bucket
-(393,216 tokens x 4,096 segments, depth 3), on a first tree and then on a
-second seed's tree built into the same bucket.
+(393,216 tokens x 4,096 segments, depth 1: a prefix with its options), on a
+first tree and then on a second seed's tree built into the same bucket.
 
 Checked against the oracle on sampled requests (the one with the longest
 root, the one with the fewest and the one with the most options, and two
@@ -26,7 +26,7 @@ import torch
 import oracle
 from tests.gpu_helpers import check_close, log
 from tree_structured_decision_amd import workloads as W
-from tree_structured_decision_amd.session import (BUCKET_DEPTH, ForkSession, pick_bucket,
+from tree_structured_decision_amd.session import (ForkSession, pick_bucket, pick_depth_cap,
                                                   request_mix_to_device)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -57,7 +57,7 @@ def bucket():
     parent, seg_len = W.request_mix_tree(rng)
     t_cap, s_cap = pick_bucket(int(seg_len.sum()), len(parent))
     assert (t_cap, s_cap) == (3 << 17, 1 << 12)
-    sess = ForkSession(t_cap, s_cap, BUCKET_DEPTH, H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
+    sess = ForkSession(t_cap, s_cap, pick_depth_cap(1), H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
     log(f"bucket {t_cap} x {s_cap}: drawing seed {SEEDS[0]} (T={int(seg_len.sum())}, S={len(parent)})")
     _, _, t, _ = request_mix_to_device(SEEDS[0], t_cap, threads=threads())
     dev = "cuda"
@@ -169,7 +169,7 @@ def bucket_packed(bucket):
     rng = np.random.Generator(np.random.PCG64(SEEDS[0]))
     parent, seg_len = W.request_mix_tree(rng)
     t_cap, s_cap = pick_bucket(int(seg_len.sum()), len(parent))
-    sess = ForkSession(t_cap, s_cap, BUCKET_DEPTH, H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
+    sess = ForkSession(t_cap, s_cap, pick_depth_cap(1), H // HKV, kv_heads=HKV, D=D, gH=GH, dk=DK, dv=DK)
     dev = "cuda"
     out = dict(o=torch.empty((t_cap, H, D), dtype=torch.bfloat16, device=dev),
                lse=torch.empty((t_cap, H), device=dev),

@@ -2039,13 +2039,15 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   // published after that step's preparation (the item in s_res, its record
   // copied into s_rec by wave 0's DMA) and taken at the next step's start,
   // after its vmcnt(0) and barrier, so no wave waits for a global load there.
-  // The last workgroup to finish resets the counters.
+  // The last workgroup to finish resets the counters. A launch with no more
+  // items than workgroups makes no request (every item is a first item).
   __shared__ int s_res;
   __shared__ __attribute__((aligned(16))) int32_t s_rec[kGdnRecWords];
   int32_t* __restrict__ ctr = args.ctr;
   int tk = 0;  // thread 0: the requested item
+  const bool dyn = nitems > (int)gridDim.x;
   auto request = [&]() __attribute__((always_inline)) {
-    if (tid == 0) tk = atomicAdd(ctr, 1) + (int)gridDim.x;
+    if (tid == 0) tk = dyn ? atomicAdd(ctr, 1) + (int)gridDim.x : nitems;
   };
   auto publish = [&]() __attribute__((always_inline)) {
     if (w == 0) {

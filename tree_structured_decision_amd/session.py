@@ -393,7 +393,17 @@ class ForkSession:
 # a compact set of fixed shapes that every request mix is padded into.
 BUCKETS_T = [1 << 16, 1 << 17, 1 << 18, 3 << 17, 1 << 19]
 BUCKETS_S = [1 << 9, 1 << 12, 1 << 13]
-BUCKET_DEPTH = 3
+BUCKETS_DEPTH = [1, 3]  # a prefix with its options; deeper histories
+
+
+def pick_depth_cap(depth: int) -> int:
+    """The smallest depth bucket that holds a tree of this depth (a graph
+    records one scan launch per depth level up to its cap, so shallow trees
+    get a shallow bucket)."""
+    for d in BUCKETS_DEPTH:
+        if depth <= d:
+            return d
+    return int(depth)
 
 
 def pick_bucket(T: int, S: int):
