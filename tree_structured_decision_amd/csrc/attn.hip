@@ -77,6 +77,19 @@ struct AttnCfg {
 // consecutive rows read the same chunk) and at c ^ 2 (r mod 4) in V (4
 // consecutive rows read 2 adjacent chunks through the transposing reads).
 __device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 7); }
+
+// Lanes l and l ^ 32 hold one query row's scores. lane_pair gives every lane
+// both of their values (its own and its partner's, in either order) by one
+// lane swap between the wave's halves, with no round trip through LDS: lanes
+// below 32 get (own, lane l + 32's), the others (lane l - 32's, own).
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair lane_pair(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 __device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) << 1); }
 
 // DMA of keys [j0, j0 + 64) of kv head g (rows past jmax repeat row jmax) into
@@ -561,7 +574,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * csc;
+        const LanePair mp = lane_pair(mx);
+        mx = fmaxf(mp.a, mp.b) * csc;
         const bool grow = mx > m_run + 8.f;
         alpha[b] = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
         m_run = grow ? mx : m_run;
@@ -571,19 +585,32 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
       typename std::conditional<BF16, bf16x8_t, float>::type pb[2][2];
       auto sm_exp = [&](int b) {
         const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-        float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][i], csc, mneg));
-          s[b][i] = p;
-          psum += p;
-        }
-        l_run += psum;
+        for (int i = 0; i < 16; ++i) s[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], csc, mneg));
         if constexpr (BF16) {
+          // bf16 P (the operand of the value product); the row sum adds these
+          // rounded weights, two per dot instruction (exact products by 1,
+          // fp32 sums), so the normaliser matches the weights applied
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+          float ps[2] = {0.f, 0.f};
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
+          for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) pb[b][hf][jj] = (__bf16)s[b][8 * hf + jj];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+            {
+              const bf16x2_t pr = {pb[b][hf][2 * q], pb[b][hf][2 * q + 1]};
+              ps[hf] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[hf], false);
+            }
+          }
+          l_run += ps[0] + ps[1];
+        } else {
+          float psum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) psum += s[b][i];
+          l_run += psum;
         }
       };
       auto rescale = [&](int b) {
@@ -743,7 +770,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     // finalize: normalise; whole tiles store the output, parts of a split tile
     // store their normalised rows (output dtype) and log-sum-exps into the
     // tile's slot for the merge pass
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const LanePair lp = lane_pair(l_run);
+    const float l_tot = lp.a + lp.b;  // (the same sum in both lanes of the row)
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_row = l_tot > 0.f ? m_run * 0.6931471805599453f + __logf(l_tot) : -INFINITY;
     constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;
