@@ -364,6 +364,45 @@ def fp8_scores(r: Runner, meta, steps, warmup):
                      "fidelity.attention_fp8_scores", o=o)
 
 
+def fp8_gdn(r: Runner, meta, steps, warmup):
+    """Gated DeltaNet with FP8 inputs (E4M3 q, k, v with per-row scales, decoded
+    on chip; fp32 state, bf16 output) on the runner's tree: the row quantisation
+    runs once outside the timed launches (HIP events on the launch stream,
+    eager). Algorithmic bytes: those of the bf16 layer with 1-byte q, k, v and
+    three fp32 scales per (token, head). Returns the timing and the output
+    (for the fidelity check)."""
+    import torch
+
+    t = r.t
+    T, gH, dk, dv = meta["T"], meta["gH"], meta["dk"], meta["dv"]
+    q8, qs = r.sess.quantize_fp8(t["gq"][:T].reshape(T * gH, dk))
+    k8, ks = r.sess.quantize_fp8(t["gk"][:T].reshape(T * gH, dk))
+    v8, vs = r.sess.quantize_fp8(t["gv"][:T].reshape(T * gH, dv))
+    go = torch.empty((T, gH, dv), dtype=torch.bfloat16, device="cuda")
+    r.build()
+    run = lambda: r.sess.gdn_fp8(q8.view(T, gH, dk), qs.view(T, gH), k8.view(T, gH, dk), ks.view(T, gH),
+                                 v8.view(T, gH, dv), vs.view(T, gH), t["a"], t["b"], go, r.st0,
+                                 root_state=t.get("root_state"))
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    st = stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    parent, seg_len = meta["parent"], meta["seg_len"]
+    gb = gdn_work(parent, seg_len, gH, dk, dv, 2, meta.get("root_state", False))
+    gb -= T * gH * (2 * dk + dv) * 1.0  # q, k, v: 1 byte per element instead of 2
+    gb += T * gH * 12.0                  # their three row scales
+    return dict(p50_us=st["p50_us"], p95_us=st["p95_us"], mean_us=st["mean_us"],
+                achieved_gbs=gb / (st["mean_us"] * 1e-6) / 1e9, hbm_frac=gb / PEAK_HBM / (st["mean_us"] * 1e-6),
+                algorithmic_bytes=gb,
+                note="gdn_fork_forward_fp8, eager, every segment on gdn_fused_kernel<128, true>; fidelity against "
+                     "the float32 oracle on the unquantised inputs is in fidelity.gdn_fp8_inputs", o=go)
+
+
 def host_threads() -> int:
     return len(os.sched_getaffinity(0))
 
@@ -501,14 +540,15 @@ def request_cost(parent, seg_len):
     return float(path.sum()) * 6 * 128 * 128 + 2.0 * 128 * visible_pairs(parent, seg_len)
 
 
-def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None):
+def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None, go8_rows=None):
     """The float32 oracle (both layers) on a prefix of the request mix's
     requests, in stream order, about CPU_BUDGET_S seconds of work on `threads`
     cores: the first request calibrates the cost per work unit, and the
     prefix stops before the request that would overrun the budget. Returns
     (cpu_baseline entry, fidelity of those requests' option softmax scores
     against the oracle). o_gpu_rows(t0, t1) / go_gpu_rows(t0, t1): the GPU
-    outputs of stream rows [t0, t1) as float64 arrays."""
+    outputs of stream rows [t0, t1) as float64 arrays (o8_rows / go8_rows: those
+    of the FP8 variants, or None)."""
     import oracle
     from tree_structured_decision_amd import metrics
     from tree_structured_decision_amd import workloads as W
@@ -518,7 +558,7 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None):
     spans = W.request_spans(parent, seg_len)
     w = meta["readout"]
     used, tokens, took, rate = [], 0, 0.0, None
-    fid_a, fid_g, fid_8 = [], [], []
+    fid_a, fid_g, fid_8, fid_g8 = [], [], [], []
     for r, (a, b, t0, t1) in enumerate(spans):
         cost = request_cost(np.where(parent[a:b] >= 0, parent[a:b] - a, -1), seg_len[a:b])
         if rate is not None and took + cost / rate > CPU_BUDGET_S:
@@ -537,6 +577,8 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None):
         fid_g.append(metrics.decision_fidelity(go_gpu_rows(t0, t1), go, wl.w_gdn, wl.parent, wl.seg_len))
         if o8_rows is not None:
             fid_8.append(metrics.decision_fidelity(o8_rows(t0, t1), o, wl.w_attn, wl.parent, wl.seg_len))
+        if go8_rows is not None:
+            fid_g8.append(metrics.decision_fidelity(go8_rows(t0, t1), go, wl.w_gdn, wl.parent, wl.seg_len))
     agg = lambda fs: dict(groups=len(fs), tvd_max=max(f["tvd_max"] for f in fs),
                           tvd_mean=float(np.mean([f["tvd_mean"] for f in fs])),
                           argmax_agreement=float(np.mean([f["argmax_agreement"] for f in fs])))
@@ -546,6 +588,7 @@ def cpu_baseline_mix(meta, o_gpu_rows, go_gpu_rows, threads, o8_rows=None):
                       f"{took:.1f} s wall on {threads} threads)",
                cpu_model=cpu_model(), host_cores=os.cpu_count())
     fid = dict(attention=agg(fid_a), gdn=agg(fid_g), attention_fp8_scores=agg(fid_8) if fid_8 else None,
+               gdn_fp8_inputs=agg(fid_g8) if fid_g8 else None,
                reference=f"float32 oracle, the {len(used)} requests of the CPU-baseline sample, one "
                          "decision group per request")
     return cpu, fid
@@ -610,6 +653,7 @@ def main():
     graph = time_runner(r, args.steps, args.warmup, eager=False)
     eager = time_runner(r, args.steps, args.warmup, eager=True)
     fp8 = fp8_scores(r, meta, args.steps, args.warmup)
+    gdn8 = fp8_gdn(r, meta, args.steps, args.warmup)
     r.step()  # leave the graph replay's outputs in place for the fidelity check
     torch.cuda.synchronize()
     f = layer_fracs(meta, eager)
@@ -638,9 +682,11 @@ def main():
     if not args.no_cpu:
         log(f"cpu baseline: float32 oracle on a prefix of the requests, {threads} threads")
         ho = lambda x: (lambda t0, t1: x[t0:t1].float().cpu().numpy().astype(np.float64))
-        cpu, fid = cpu_baseline_mix(meta, ho(r.o), ho(r.go), threads, o8_rows=ho(fp8.pop("o")))
+        cpu, fid = cpu_baseline_mix(meta, ho(r.o), ho(r.go), threads, o8_rows=ho(fp8.pop("o")),
+                                    go8_rows=ho(gdn8.pop("o")))
     else:
         fp8.pop("o")
+        gdn8.pop("o")
     n_opt, opt_tok, iso_tok = tree_rates(meta["parent"], meta["seg_len"])
     step_s = graph["ms_per_step"] * 1e-3
     rates = dict(options=n_opt, option_tokens_per_s=opt_tok / step_s,
@@ -683,6 +729,7 @@ def main():
         "fidelity": fid,
         "layers": layers,
         "attention_fp8_scores": fp8,
+        "gdn_fp8_inputs": gdn8,
         "rates": rates,
         "measured_peaks": peaks,
     }

@@ -288,6 +288,28 @@ fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, c
                              int32_t H, int32_t dk, int32_t dv, float scale, fork_dtype dt,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 inputs: gdn_fork_forward with q, k and v given as OCP FP8 E4M3 codes
+ * with one fp32 scale per (token, head) row, as fork_quantize_fp8 writes
+ * them: q8, k8, v8 [T, H, 128] bytes (16-byte aligned) with q_scale, k_scale,
+ * v_scale [T, H]; the row's values are code * scale. Scales must be positive
+ * normal floats (the quantiser's max|row| / 448, or 1 for a zero row). The
+ * kernel reads the codes (half the bytes of bf16 inputs) and decodes them on
+ * chip exactly; the per-row scales enter as fp32 factors of b, of the value
+ * rows and of the output rows (the recurrence is the same recurrence in the
+ * codes, see gdn.hip), so the state matches the bf16 recurrence on the
+ * decoded values to rounding. The pages' Gated DeltaNet kernel uses FP8
+ * where the hardware has it (techfi24.com page, section "Exact State
+ * Forking"). o [T, H, 128] bf16; a, b, root_state, seg_start_state and
+ * seg_final_state as gdn_fork_forward (leaf siblings packed when
+ * seg_final_state is null). Supported: dk = dv = 128. Every segment runs on
+ * the per-(segment, head) fused kernel, so no workspace is needed. Work
+ * counters as gdn_fork_forward: launches on one blob must not overlap. */
+fork_status gdn_fork_forward_fp8(const fork_meta* m, const void* q8, const float* q_scale, const void* k8,
+                                 const float* k_scale, const void* v8, const float* v_scale, const float* a,
+                                 const float* b, const float* root_state, void* o, float* seg_start_state,
+                                 float* seg_final_state, int32_t H, int32_t dk, int32_t dv, float scale,
+                                 void* stream);
+
 /* ------------------------------------------------------------ block pieces
  * Fork-aware operations around the two layers of a hybrid block. Each branch
  * must evaluate exactly as its isolated forward pass (kongchang.com page,

@@ -26,7 +26,7 @@ FORK_DEVERR_MAGIC, FORK_DEVERR_CAPACITY = 1, 2
 EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_build_ctx",
            "fork_meta_plan_ctx", "fork_meta_export", "fork_meta_check",
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx", "fork_attn_forward_noalloc", "fork_attn_forward_qk8",
-           "gdn_fork_workspace", "gdn_fork_forward", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
+           "gdn_fork_workspace", "gdn_fork_forward", "gdn_fork_forward_fp8", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
            "fork_quantize_fp8", "fork_linear_fp8_forward",
            "fork_graph_create", "fork_graph_launch",
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
             "gdn_fork_workspace": [P(fork_meta), i32, i32, i32, i32, P(sz)],
             "gdn_fork_forward": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                  f32, i32, vp, sz, vp],
+            "gdn_fork_forward_fp8": [P(fork_meta), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                     f32, vp],
             "fork_rope_forward": [P(fork_meta), vp, i32, i32, f32, i32, vp],
             "fork_rope_copy_forward": [P(fork_meta), vp, ctypes.c_int64, vp, i32, i32, f32, i32, vp],
             "fork_conv_forward": [P(fork_meta), vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
@@ -289,6 +291,15 @@ def gdn_fork_forward(meta: fork_meta, q, k, v, a, b, root_state, o, seg_start_st
                                   _ptr(root_state), _ptr(o), _ptr(seg_start_state),
                                   _ptr(seg_final_state), H, dk, dv, float(scale), dt, _ptr(ws),
                                   int(ws_bytes), _stream(stream)))
+
+
+def gdn_fork_forward_fp8(meta: fork_meta, q8, q_scale, k8, k_scale, v8, v_scale, a, b, root_state, o,
+                         seg_start_state, seg_final_state, H: int, dk: int, dv: int, scale: float,
+                         stream=None) -> None:
+    _check(lib().gdn_fork_forward_fp8(ctypes.byref(meta), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
+                                      _ptr(v8), _ptr(v_scale), _ptr(a), _ptr(b), _ptr(root_state), _ptr(o),
+                                      _ptr(seg_start_state), _ptr(seg_final_state), H, dk, dv, float(scale),
+                                      _stream(stream)))
 
 
 def fork_rope_forward(meta: fork_meta, x, nheads: int, D: int, theta: float, dt: int,

@@ -654,6 +654,23 @@ fork_status gdn_fork_forward(const fork_meta* m, const void* q, const void* k, c
                     dt, ws, ws_bytes, (hipStream_t)stream);
 }
 
+fork_status gdn_fork_forward_fp8(const fork_meta* m, const void* q8, const float* q_scale, const void* k8,
+                                 const float* k_scale, const void* v8, const float* v_scale, const float* a,
+                                 const float* b, const float* root_state, void* o, float* seg_start_state,
+                                 float* seg_final_state, int32_t H, int32_t dk, int32_t dv, float scale, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !a || !b || !o || !seg_start_state)
+    return fail(FORK_E_ARG, "q8, k8, v8, their scales, a, b, o and seg_start_state must be non-null");
+  if (H < 1) return fail(FORK_E_ARG, "H=%d", H);
+  if (dk != 128 || dv != 128) return fail(FORK_E_UNSUPPORTED, "FP8 inputs need dk = dv = 128 (got %d, %d)", dk, dv);
+  if ((uintptr_t)q8 % 16 || (uintptr_t)k8 % 16 || (uintptr_t)v8 % 16)
+    return fail(FORK_E_ARG, "q8, k8 and v8 must be 16-byte aligned");
+  return launch_gdn_fp8(m, q8, q_scale, k8, k_scale, v8, v_scale, a, b, root_state, o, seg_start_state,
+                        seg_final_state, H, scale, (hipStream_t)stream);
+}
+
 fork_status fork_rope_forward(const fork_meta* m, void* x, int32_t nheads, int32_t D, float theta,
                               fork_dtype dt, void* stream) {
   g_err[0] = 0;

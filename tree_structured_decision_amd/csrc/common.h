@@ -261,5 +261,9 @@ fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const v
                        const float* a, const float* b, const float* root_state, void* o,
                        float* seg_start_state, float* seg_final_state, int H, int dk, int dv,
                        float scale, fork_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+fork_status launch_gdn_fp8(const fork_meta* m, const void* q8, const float* qs, const void* k8, const float* ks,
+                           const void* v8, const float* vs, const float* a, const float* b, const float* root_state,
+                           void* o, float* seg_start_state, float* seg_final_state, int H, float scale,
+                           hipStream_t stream);
 
 }  // namespace fork

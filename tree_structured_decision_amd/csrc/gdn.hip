@@ -160,6 +160,13 @@ struct GdnArgs {
   // gdn_prep_kernel: 1 = only the chunks of the segments gdn_coop_kernel takes
   // (the fused kernel prepares the others itself); sgrid: the scans' grid
   int prep_coop_only, sgrid;
+  // FP8 inputs (gdn_fused_kernel<.., true>): q, k, v are E4M3 codes with these
+  // per-(token, head) scales [T, H]; no_coop: every segment of a depth goes to
+  // the fused kernel
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  int no_coop;
 };
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
@@ -1692,16 +1699,39 @@ struct FusedCfg {
   static_assert(2 * BUF + PREP <= 160 * 1024, "LDS");
   static constexpr int BLK = 3 * TB / 1024 / NW;       // 1 KB loads of K, Q and V per wave
   static_assert(BLK * NW * 1024 == 3 * TB, "tiles divide over the waves");
+  // FP8 inputs: a staging buffer holds one chunk's K, Q and V codes (row-major,
+  // DK bytes per row) and, from X8, the per-row words a, b, positions, q
+  // scales, v scales and k scales; the codes are decoded into one bf16 tile
+  // buffer (TILES, the kq_off layout of the bf16 path) at the start of each
+  // step
+  static constexpr int TB8 = CH * DK, X8 = 3 * TB8, BUF8 = X8 + 6 * CH * 4, TILES = 3 * TB;
+  static constexpr int XA = 0, XB = CH * 4, XP = 2 * CH * 4, XQS = 3 * CH * 4, XVS = 4 * CH * 4, XKS = 5 * CH * 4;
+  static_assert(OB - OA == XB && OP - OA == XP, "per-row words at the same offsets in both layouts");
+  static_assert(2 * BUF8 + TILES + PREP <= 160 * 1024, "LDS (FP8 inputs)");
+  static constexpr int BLK8 = 3 * TB8 / 1024 / NW;     // 1 KB loads of codes per wave
+  static_assert(BLK8 * NW * 1024 == 3 * TB8, "code tiles divide over the waves");
 };
 
-template <int DK>
+// F8: q, k, v arrive as E4M3 codes with fp32 scales per (token, head) row,
+// q = rho q^, k = kappa k^, v = nu v^. Substituting these into the recurrence
+// gives the same recurrence in the codes, S_t = a_t S_{t-1} (I - b'_t k^ k^T)
+// + b'_t v'_t k^T with b' = b kappa^2 and v' = (nu / kappa) v^, and o_t =
+// rho_t scale S_t q^_t: the kernel decodes the codes exactly into the bf16
+// tiles (E4M3 values are bf16 values), replaces b by b' and scales V rows by
+// nu / kappa where it forms R = V - gamma X in fp32, and scales each output
+// row by rho; the state is the same state.
+template <int DK, bool F8>
 __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_t* __restrict__ blob, GdnArgs args) {
   using F = FusedCfg;
   static_assert(DK == F::DK, "fused kernel is for dk = dv = 128");
   typedef unsigned short E;
-  __shared__ __attribute__((aligned(16))) unsigned char buf0[F::BUF];
-  __shared__ __attribute__((aligned(16))) unsigned char buf1[F::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[F8 ? F::BUF8 : F::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[F8 ? F::BUF8 : F::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles8[F8 ? F::TILES : 16];
   __shared__ __attribute__((aligned(16))) unsigned char prep[F::PREP];
+  // a step's bf16 tiles and its per-row words
+  auto tiles_of = [&](unsigned char* b) __attribute__((always_inline)) { return F8 ? tiles8 : b; };
+  auto words_of = [&](unsigned char* b) __attribute__((always_inline)) { return b + (F8 ? F::X8 : F::OA); };
 
   if (!blob_ok(blob, args.guard)) return;
   const int level = args.level;
@@ -1714,7 +1744,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   const int32_t* __restrict__ tok_pos = blob + blob[MH_OFF_TOKPOS];
   const int H = args.H;
   // the depth's first `take` segments are handled by gdn_coop_kernel
-  const int take = planned ? args.lv_take : coop_segments(blob, level, H, DK);
+  const int take = planned ? args.lv_take : args.no_coop ? 0 : coop_segments(blob, level, H, DK);
   // (the packed list has its own offsets; its long segments lead each depth
   // in the level list's order, so `take` skips the same ones)
   const bool use_plan = planned && !packed;
@@ -1730,6 +1760,9 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   const E* __restrict__ Qg = (const E*)args.q;
   const E* __restrict__ Vg = (const E*)args.v;
   E* __restrict__ Og = (E*)args.o;
+  const float* __restrict__ QSg = args.qs;
+  const float* __restrict__ VSg = args.vs;
+  const float* __restrict__ KSg = args.ks;
   // (the lambdas below use these copies, not args: a by-reference capture of
   // the kernel argument would put it in scratch memory)
   const float* __restrict__ Ag = args.a;
@@ -1771,9 +1804,11 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   };
 
   // loads of chunk ci of item r into buffer b: K, Q and V tiles in the kq_off
-  // layout (chunk c of row i at c ^ kq_swz(i)), rows past the chunk repeat its
-  // last row (they meet b = 0, so they reach no output that is stored); a and
-  // b of the chunk (waves 0 and 1, one dword per lane)
+  // layout (chunk c of row i at c ^ kq_swz(i)), or with F8 their code tiles
+  // row-major; rows past the chunk repeat its last row (they meet b = 0, so
+  // they reach no output that is stored); the per-row words (a, b, positions,
+  // and with F8 the q, v and k scales), one dword per lane, wave n loading the
+  // n-th
   // The buffer's address goes through an empty asm statement: the compiler
   // then does not tie these LDS writes to the buffer, and adds no waits for
   // them before LDS accesses elsewhere in the step (it cannot tell the
@@ -1782,24 +1817,74 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   auto issue = [&](unsigned char* b, const Item& r, int ci) __attribute__((always_inline)) {
     const int t0 = r.st + CH * ci, tl = t0 + min(CH, r.L - CH * ci) - 1;
     asm volatile("" : "+v"(b));
-    // 1 KB block n = 8 i + w: tile i / 2 (K, Q, V), block (i % 2) 8 + w of it
-    static_assert(F::BLK == 6 && F::NW == 8 && F::TB == 16 * 1024, "two blocks of each tile per wave");
+    if constexpr (F8) {
+      // code tile i (K, Q, V): wave w loads its rows 8 w .. 8 w + 7 (1 KB)
+      static_assert(F::BLK8 == 3 && F::NW == 8 && F::TB8 == 8 * 1024, "one 1 KB block of each code tile per wave");
+      const int row = 8 * w + (lane >> 3);
+      const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 16 * (lane & 7);
 #pragma unroll
-    for (int i = 0; i < F::BLK; ++i) {
-      const int nb = (i % 2) * 8 + w;
-      const int slot = nb * 64 + lane, row = slot / (DK / 8), pos = slot % (DK / 8);
-      const E* src = i < 2 ? Kg : (i < 4 ? Qg : Vg);
-      const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 8 * (pos ^ kq_swz(row, DK / 8));
-      __builtin_amdgcn_global_load_lds((const void*)(src + g), (lds_void_t*)(b + (i / 2) * F::TB + nb * 1024), 16,
-                                       0, 0);
+      for (int i = 0; i < 3; ++i) {
+        const unsigned char* src = (const unsigned char*)(i == 0 ? Kg : (i == 1 ? Qg : Vg));
+        __builtin_amdgcn_global_load_lds((const void*)(src + g), (lds_void_t*)(b + i * F::TB8 + w * 1024), 16, 0, 0);
+      }
+    } else {
+      // 1 KB block n = 8 i + w: tile i / 2 (K, Q, V), block (i % 2) 8 + w of it
+      static_assert(F::BLK == 6 && F::NW == 8 && F::TB == 16 * 1024, "two blocks of each tile per wave");
+#pragma unroll
+      for (int i = 0; i < F::BLK; ++i) {
+        const int nb = (i % 2) * 8 + w;
+        const int slot = nb * 64 + lane, row = slot / (DK / 8), pos = slot % (DK / 8);
+        const E* src = i < 2 ? Kg : (i < 4 ? Qg : Vg);
+        const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 8 * (pos ^ kq_swz(row, DK / 8));
+        __builtin_amdgcn_global_load_lds((const void*)(src + g), (lds_void_t*)(b + (i / 2) * F::TB + nb * 1024), 16,
+                                         0, 0);
+      }
     }
+    unsigned char* x = words_of(b);
     if (w < 2) {
       const float* src = w == 0 ? Ag : Bg;
       __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)min(t0 + lane, tl) * H + r.h),
-                                       (lds_void_t*)(b + (w == 0 ? F::OA : F::OB)), 4, 0, 0);
+                                       (lds_void_t*)(x + (w == 0 ? F::XA : F::XB)), 4, 0, 0);
     } else if (w == 2) {
-      __builtin_amdgcn_global_load_lds((const void*)(tok_pos + min(t0 + lane, tl)), (lds_void_t*)(b + F::OP), 4,
+      __builtin_amdgcn_global_load_lds((const void*)(tok_pos + min(t0 + lane, tl)), (lds_void_t*)(x + F::XP), 4,
                                        0, 0);
+    } else if (F8 && w < 6) {
+      const size_t ri = (size_t)min(t0 + lane, tl) * H + r.h;
+      if (w == 3)
+        __builtin_amdgcn_global_load_lds((const void*)(QSg + ri), (lds_void_t*)(x + F::XQS), 4, 0, 0);
+      else if (w == 4)
+        __builtin_amdgcn_global_load_lds((const void*)(VSg + ri), (lds_void_t*)(x + F::XVS), 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(KSg + ri), (lds_void_t*)(x + F::XKS), 4, 0, 0);
+    }
+  };
+
+  // F8: decode the codes staged in b into the bf16 tiles (thread t: 16 codes
+  // of row t / 8 of each tile), and replace the row words b by b kappa^2 and
+  // the v scales by nu / kappa (wave 0)
+  auto decode = [&](unsigned char* b) __attribute__((always_inline)) {
+    const int row = tid >> 3, c0 = 16 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x4_t c = *(const u32x4_t*)(b + i * F::TB8 + row * DK + c0);
+      unsigned pk[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // bytes 0, 1 and 2, 3 of dword d: codes c0 + 4 d + 0 .. 3 (exact in fp32 and in bf16)
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], true);
+        pk[2 * d] = pack_bf16x2(lo[0], lo[1]);
+        pk[2 * d + 1] = pack_bf16x2(hi[0], hi[1]);
+      }
+      E* t = (E*)(tiles8 + i * F::TB);
+      *(u32x4_t*)(t + kq_off<DK>(row, c0)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+      *(u32x4_t*)(t + kq_off<DK>(row, c0 + 8)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+    }
+    if (w == 0) {
+      float* x = (float*)(b + F::X8);
+      const float kap = x[F::XKS / 4 + lane];
+      x[F::XB / 4 + lane] *= kap * kap;
+      x[F::XVS / 4 + lane] /= kap;
     }
   };
 
@@ -1808,9 +1893,9 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   // (block I: rows 16 I + 4 q4 + r of X and Y, state row e0 + c16), which
   // need nothing from the chunk preparation.
   f32x4_t St[DK / 16], X[4], Yt[4];
-  auto state_products = [&](const unsigned char* b) __attribute__((always_inline)) {
-    const E* Ks = (const E*)b;
-    const E* Qs = (const E*)(b + F::OQ);
+  auto state_products = [&](const unsigned char* t) __attribute__((always_inline)) {
+    const E* Ks = (const E*)t;
+    const E* Qs = (const E*)(t + F::OQ);
 #pragma unroll
     for (int I = 0; I < 4; ++I) X[I] = Yt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1834,9 +1919,10 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   // w - 4 of A and the inverse of its diagonal block; wave 0 then computes
   // the decays, which the products do not need. Each wave then forms its
   // state products (they overlap the diagonal inverses on the same SIMDs).
-  auto prep_chunk = [&](const unsigned char* b, int len) __attribute__((always_inline)) {
-    const E* Ks = (const E*)b;
-    const E* Qs = (const E*)(b + F::OQ);
+  // (t: the bf16 tiles; x: the per-row words)
+  auto prep_chunk = [&](const unsigned char* t, const unsigned char* x, int len) __attribute__((always_inline)) {
+    const E* Ks = (const E*)t;
+    const E* Qs = (const E*)(t + F::OQ);
     const int rb = w & 3;      // this wave's row block
     const bool kk = w >= 4;    // K K^T (A) rather than Q K^T (P)
     // Xt_J = K_J X_rb^T for J <= rb, X = Q or K (16x16x32 bf16, k-order of a
@@ -1862,15 +1948,15 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       // row's position in its segment, sr = the row its segment starts at
       // (rows past the chunk hold the last row's position and take its sr,
       // so they keep its decay: g of the last row is the chunk's total)
-      const float a = ((const float*)(b + F::OA))[lane];
+      const float a = ((const float*)(x + F::XA))[lane];
       const float L = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
-      const int sr = min(lane, len - 1) - ((const int*)(b + F::OP))[lane];
+      const int sr = min(lane, len - 1) - ((const int*)(x + F::XP))[lane];
       const float Lb = __shfl(L, sr > 0 ? sr - 1 : 0);
       const float la = sr > 0 ? L - Lb : L;
       const float gl = lane_val(la, CH - 1);
       ss[lane] = sr > 0 ? sr : 0;
       gs[lane] = la;
-      bs[lane] = lane < len ? ((const float*)(b + F::OB))[lane] : 0.f;
+      bs[lane] = lane < len ? ((const float*)(x + F::XB))[lane] : 0.f;
       gam[lane] = __expf(la);
       rrv[lane] = __expf(gl - la);
     }
@@ -1930,15 +2016,16 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       // wave's own stores)
       diag_inverse(As, Ts, F::LDA, 16 * rb, lane);
     }
-    state_products(b);
+    state_products(t);
     lds_barrier();  // P, A, the diagonal inverses and the decays are complete
   };
 
   // ---- one chunk of the scan for this wave's slice (operands in b; P, A,
   // the diagonal inverses and the decays in prep; X and Y^T formed)
-  auto scan_chunk = [&](const unsigned char* b, const Item& r, int t0, int len, bool need_state) __attribute__((always_inline)) {
-    const E* Ks = (const E*)b;
-    const E* Vs = (const E*)(b + F::OV);
+  auto scan_chunk = [&](const unsigned char* t, const unsigned char* x, const Item& r, int t0, int len,
+                        bool need_state) __attribute__((always_inline)) {
+    const E* Ks = (const E*)t;
+    const E* Vs = (const E*)(t + F::OV);
     const u32x4_t* Ph = (const u32x4_t*)(prep + F::PPH);
     // (2) R = V - gamma X: lane (c16, q4), block I holds R[16 I + 4 q4 + r][e0 + c16]
     f32x4_t R[4];
@@ -1947,8 +2034,10 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4_t*)(Vs + kq_off<DK>(16 * I + 4 * q4 + (c16 >> 2), e0 + 4 * (c16 & 3))));
       const f32x4_t g4 = *(const f32x4_t*)(gam + 16 * I + 4 * q4);
+      // (F8: V rows times nu / kappa)
+      const f32x4_t f4 = F8 ? *(const f32x4_t*)(x + F::XVS + 4 * (16 * I + 4 * q4)) : f32x4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) R[I][k] = bf16_val((unsigned short)v4[k]) - g4[k] * X[I][k];
+      for (int k = 0; k < 4; ++k) R[I][k] = fmaf(-g4[k], X[I][k], bf16_val((unsigned short)v4[k]) * f4[k]);
     }
     // (3) U = T'' R = (I + A)^-1 diag(b) R by block forward substitution:
     // U_I = T_II (b_I R_I - sum_{K<I} A_IK U_K), T_II the inverse of the
@@ -2002,7 +2091,9 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
         Zt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[kf], pl, Zt, 0, 0, 0);
       }
       const int i = 16 * I + c16;
-      const f32x4_t o = oscale * (gam[i] * Yt[I] + Zt);
+      // (F8: the row's q scale rho)
+      const float osc = F8 ? oscale * ((const float*)(x + F::XQS))[i] : oscale;
+      const f32x4_t o = osc * (gam[i] * Yt[I] + Zt);
       if (i < len) {
         E* d = Og + ((size_t)(t0 + i) * H + r.h) * DK + e0 + 4 * q4;
         *(u32x2_t*)d = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -2115,7 +2206,11 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       }
       if (has_next) issue(other, nx, nci);
       const int t0 = cur.st + CH * ci, len = min(CH, cur.L - CH * ci);
-      prep_chunk(b, len);
+      if constexpr (F8) {
+        decode(b);
+        lds_barrier();  // the decoded tiles and the scaled row words
+      }
+      prep_chunk(tiles_of(b), words_of(b), len);
       if (req) publish();
       if (ci == 0) {
         for (int q = 0; q < cur.nsib; ++q) {
@@ -2129,7 +2224,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       const bool last = ci + 1 == cur.nck;
       const int fc = cur.fc;
       const bool need_state = !last || fc >= 0 || seg_final_state != nullptr;
-      scan_chunk(b, cur, t0, len, need_state);
+      scan_chunk(tiles_of(b), words_of(b), cur, t0, len, need_state);
       if (last) {
         if (seg_final_state) {
           float* d = seg_final_state + ((size_t)cur.s * H + cur.h) * SZ;
@@ -2230,7 +2325,7 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
           const long long items = (long long)(a.lv_count - a.lv_take) * a.H;
           if (items < grid) grid = (int)items;
         }
-        hipLaunchKernelGGL((gdn_fused_kernel<DK>), dim3(grid), dim3(FusedCfg::NT), 0, stream, a.blob, a);
+        hipLaunchKernelGGL((gdn_fused_kernel<DK, false>), dim3(grid), dim3(FusedCfg::NT), 0, stream, a.blob, a);
       } else {
         hipLaunchKernelGGL((gdn_scan_kernel<BF16, DK>), dim3(sgrid), dim3(ScanCfg<BF16, DK>::NT), 0, stream,
                            a.blob, a);
@@ -2241,7 +2336,69 @@ fork_status launch_gdn_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
   return FORK_OK;
 }
 
+// FP8 inputs: every depth runs on gdn_fused_kernel<128, true> (no
+// chunk-cooperative path, hence no preparation kernel and no workspace). Under
+// capture every depth up to the capacity is recorded; depths beyond the
+// current tree exit at once.
+fork_status launch_gdn_fp8_t(const fork_meta* m, GdnArgs a, hipStream_t stream) {
+  const bool cap = stream_capturing(stream);
+  const int sgrid = (device_cu_count() + 7) / 8 * 8;
+  a.sgrid = sgrid;
+  a.no_coop = 1;
+  const int levels = cap ? m->caps.depth_cap + 1 : m->max_depth + 1;
+  int first = 0;
+  for (int lv = 0; lv < levels; ++lv) {
+    a.level = lv;
+    a.lv_first = a.lv_count = a.lv_take = -1;
+    int grid = sgrid;
+    if (!cap && lv < FORK_PLAN_DEPTHS) {
+      const int nseg = m->level_segs[lv];
+      a.lv_first = first;
+      a.lv_count = nseg;
+      a.lv_take = 0;
+      first += nseg;
+      if (nseg == 0) continue;
+      const long long items = (long long)nseg * a.H;
+      if (items < grid) grid = (int)items;
+    }
+    hipLaunchKernelGGL((gdn_fused_kernel<128, true>), dim3(grid), dim3(FusedCfg::NT), 0, stream, a.blob, a);
+    FORK_HIP_CHECK(hipGetLastError());
+  }
+  return FORK_OK;
+}
+
 }  // namespace
+
+fork_status launch_gdn_fp8(const fork_meta* m, const void* q8, const float* qs, const void* k8, const float* ks,
+                           const void* v8, const float* vs, const float* a, const float* b, const float* root_state,
+                           void* o, float* seg_start_state, float* seg_final_state, int H, float scale,
+                           hipStream_t stream) {
+  GdnArgs g;
+  g.blob = (const int32_t*)m->dev;
+  g.q = q8;
+  g.k = k8;
+  g.v = v8;
+  g.qs = qs;
+  g.ks = ks;
+  g.vs = vs;
+  g.a = a;
+  g.b = b;
+  g.root_state = root_state;
+  g.o = o;
+  g.seg_start = seg_start_state;
+  g.seg_final = seg_final_state;
+  g.ws = nullptr;
+  g.ctr = (int32_t*)m->dev + kGdnCtrWord;
+  g.guard = blob_guard(m->caps);
+  g.H = H;
+  g.scale = scale;
+  g.level = 0;
+  g.lv_first = g.lv_count = g.lv_take = -1;
+  g.prep_coop_only = 0;
+  g.sgrid = 0;
+  g.no_coop = 1;
+  return launch_gdn_fp8_t(m, g, stream);
+}
 
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv) {
   (void)dk;
@@ -2276,6 +2433,8 @@ fork_status launch_gdn(const fork_meta* m, const void* q, const void* k, const v
   g.lv_first = g.lv_count = g.lv_take = -1;
   g.prep_coop_only = 0;
   g.sgrid = 0;
+  g.qs = g.ks = g.vs = nullptr;
+  g.no_coop = 0;
   if (dt == FORK_BF16) {
     if (dk == 128) return launch_gdn_t<true, 128>(m, g, stream);
     if (dk == 64) return launch_gdn_t<true, 64>(m, g, stream);

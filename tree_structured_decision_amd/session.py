@@ -103,6 +103,14 @@ class ForkSession:
                            seg_final_state, H, dk, dv, scale, dt, self.gdn_ws,
                            self.gdn_ws.numel(), stream=stream)
 
+    def gdn_fp8(self, q8, q_scale, k8, k_scale, v8, v_scale, a, b, o, seg_start_state, seg_final_state=None,
+                root_state=None, scale: float = 1.0, stream=None):
+        """Gated DeltaNet with FP8 inputs: q8, k8, v8 [T, H, 128] E4M3 codes (uint8)
+        with row scales [T, H] (fork_quantize_fp8 over rows of 128), o bf16."""
+        T, H, dk = q8.shape
+        B.gdn_fork_forward_fp8(self.meta, q8, q_scale, k8, k_scale, v8, v_scale, a, b, root_state, o,
+                               seg_start_state, seg_final_state, H, dk, v8.shape[2], scale, stream=stream)
+
     # -- block pieces -------------------------------------------------------
     def rope(self, x, theta: float = 10000.0, stream=None):
         """Rotary embedding in place at the isolated positions; x [T, nheads, D]."""
