@@ -8,8 +8,9 @@ random trees of several depths and roots with given root states, with and
 without end states (without them, leaf siblings run packed); a long root that
 the bf16 path would give to the chunk-cooperative kernel; the one-request
 tree at full size; the fork copies bit for bit (every child's start state is
-its parent's end state); the FP8 launch bit for bit against the bf16 launch on
-the decoded inputs where those are exact in bf16 (unit scales); and the host
+its parent's end state); the FP8 launch against the bf16 launch on the decoded
+inputs where those are exact in bf16 (unit scales: the two differ only in the
+order the matrix cores sum the products Q K^T and K K^T); and the host
 rejections. The cost of quantising is reported as the option softmax's
 total-variation distance to the float32 oracle on the unquantised inputs."""
 import numpy as np
@@ -119,11 +120,17 @@ def test_fp8_gdn_long_root_and_packed_leaves():
 
 def test_fp8_gdn_unit_scales_match_bf16_launch():
     """Rows whose largest |value| is 448 quantise with scale 1, so their
-    decoded values are the codes, exact in bf16: the FP8 launch and the bf16
-    launch on those bf16 values then form the same products in the same order
-    (b kappa^2 = b, nu / kappa = 1, rho = 1), and agree bit for bit. Segments
-    of at most one chunk, so that the bf16 launch also runs every segment on
-    the fused kernel."""
+    decoded values are the codes, exact in bf16, and the factors are 1 (b
+    kappa^2 = b, nu / kappa = 1, rho = 1): the FP8 launch and the bf16 launch
+    on those values compute the same recurrence with the same bf16 operands,
+    except that Q K^T and K K^T come from the FP8 matrix cores (exact
+    products, fp32 sums in another order). They agree to that rounding: o
+    within one bf16 ulp or 1e-4 of its largest magnitude, states within 1e-4
+    of their largest magnitude: the codes reach 448, and a last-bit difference
+    in a product moves the hi / lo bf16 split of the next operand, whose
+    precision is about 2^-16.
+    Segments of at most one chunk, so that the bf16 launch also runs every
+    segment on the fused kernel."""
     rng = np.random.default_rng(26)
     parent, seg_len = W.random_tree(rng, 16, 64, max_depth=3, roots=2)
     wl = W.make_workload("gdn8_unit", "bf16", parent, seg_len, H=2, Hkv=2, D=64, gH=2, dk=128, dv=128,
@@ -153,11 +160,22 @@ def test_fp8_gdn_unit_scales_match_bf16_launch():
     assert sess.check() == 0
     assert int(np.max(wl.seg_len)) <= 64
     for name, a8, ab in (("o", got8["go"], go), ("start", got8["s0"], st0), ("final", got8["s1"], st1)):
-        a8 = np.ascontiguousarray(a8.astype(np.float32))
-        ab = np.ascontiguousarray(ab.float().cpu().numpy())
-        np.testing.assert_array_equal(a8.view(np.int32), ab.view(np.int32), err_msg=name)
-    go_ref, s0_ref, s1_ref = oracle_on(wl, qkv)
-    check_close("gdn8_unit.o", got8["go"], go_ref, "bf16")
+        ab = ab.float().cpu().numpy().astype(np.float64)
+        err = np.abs(a8 - ab)
+        if name == "o":
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ab), 1e-30))) - 7)
+            bad = err > np.maximum(ulp * 1.0001, 1e-4 * np.abs(ab).max())
+            same = float(np.mean(err == 0))
+            log(f"  unit scales, FP8 vs bf16 launch, o: {same:.4f} of values equal, max difference "
+                f"{err.max():.2e} (largest |o| {np.abs(ab).max():.2e})")
+        else:
+            bad = err > 1e-4 * np.abs(ab).max()
+            log(f"  unit scales, FP8 vs bf16 launch, {name} state: max difference {err.max():.2e} "
+                f"(largest |state| {np.abs(ab).max():.2e})")
+        assert not bad.any(), name
+    # (o reaches ~900 here, beyond what the absolute bf16 bar is for; the states stay O(1))
+    _, s0_ref, s1_ref = oracle_on(wl, qkv)
+    check_close("gdn8_unit.start_state", got8["s0"], s0_ref, "bf16", kind="f32")
     check_close("gdn8_unit.final_state", got8["s1"], s1_ref, "bf16", kind="f32")
     sess.close()
 

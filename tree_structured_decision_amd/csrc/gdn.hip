@@ -1687,6 +1687,15 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
 // state (the parent's first child's start slot, where the parent's item left
 // it) and is copied into the segment's own slot; the end state goes to
 // seg_final_state and the first child's slot.
+// FP8 code tiles in LDS: rows of DK bytes whose 32-byte pairs of 16-byte
+// chunks are permuted by row (pair p at position p ^ (r mod 4)), so that the
+// 32-byte reads of 16 rows at one column meet few bank conflicts.
+// code8_pair: the position of pair p in row r (an involution);
+// code8_chunk: the chunk held at 16-byte position c of row r.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ int code8_pair(int r, int p) { return p ^ (r & 3); }
+__device__ __forceinline__ int code8_chunk(int r, int c) { return 2 * code8_pair(r, c >> 1) + (c & 1); }
+
 struct FusedCfg {
   static constexpr int DK = 128, NW = 8, NT = 64 * NW;
   static constexpr int TB = CH * DK * 2;               // a K, Q or V tile (bf16, kq_off layout)
@@ -1818,10 +1827,12 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     const int t0 = r.st + CH * ci, tl = t0 + min(CH, r.L - CH * ci) - 1;
     asm volatile("" : "+v"(b));
     if constexpr (F8) {
-      // code tile i (K, Q, V): wave w loads its rows 8 w .. 8 w + 7 (1 KB)
+      // code tile i (K, Q, V): wave w loads its rows 8 w .. 8 w + 7 (1 KB);
+      // lane l writes 16-byte position l % 8 of its row, which holds the
+      // row's 16-byte chunk code8_chunk(row, l % 8)
       static_assert(F::BLK8 == 3 && F::NW == 8 && F::TB8 == 8 * 1024, "one 1 KB block of each code tile per wave");
       const int row = 8 * w + (lane >> 3);
-      const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 16 * (lane & 7);
+      const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 16 * code8_chunk(row, lane & 7);
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         const unsigned char* src = (const unsigned char*)(i == 0 ? Kg : (i == 1 ? Qg : Vg));
@@ -1859,14 +1870,14 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     }
   };
 
-  // F8: decode the codes staged in b into the bf16 tiles (thread t: 16 codes
-  // of row t / 8 of each tile), and replace the row words b by b kappa^2 and
-  // the v scales by nu / kappa (wave 0)
+  // F8: decode the codes staged in b into the bf16 tiles (thread t: the 16
+  // codes at 16-byte position t % 8 of row t / 8 of each tile), and replace
+  // the row words b by b kappa^2 and the v scales by nu / kappa (wave 0)
   auto decode = [&](unsigned char* b) __attribute__((always_inline)) {
-    const int row = tid >> 3, c0 = 16 * (tid & 7);
+    const int row = tid >> 3, c0 = 16 * code8_chunk(row, tid & 7);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const u32x4_t c = *(const u32x4_t*)(b + i * F::TB8 + row * DK + c0);
+      const u32x4_t c = *(const u32x4_t*)(b + i * F::TB8 + row * DK + 16 * (tid & 7));
       unsigned pk[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -1919,8 +1930,9 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
   // w - 4 of A and the inverse of its diagonal block; wave 0 then computes
   // the decays, which the products do not need. Each wave then forms its
   // state products (they overlap the diagonal inverses on the same SIMDs).
-  // (t: the bf16 tiles; x: the per-row words)
-  auto prep_chunk = [&](const unsigned char* t, const unsigned char* x, int len) __attribute__((always_inline)) {
+  // (t: the bf16 tiles; x: the per-row words; c8: with F8, the code tiles)
+  auto prep_chunk = [&](const unsigned char* t, const unsigned char* x, const unsigned char* c8, int len)
+                        __attribute__((always_inline)) {
     const E* Ks = (const E*)t;
     const E* Qs = (const E*)(t + F::OQ);
     const int rb = w & 3;      // this wave's row block
@@ -1931,15 +1943,32 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     f32x4_t xt[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) xt[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const E* Xs = kk ? Ks : Qs;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const bf16x8_t bx = *(const bf16x8_t*)(Xs + kq_off<DK>(16 * rb + c16, 32 * ks + 8 * q4));
+    if constexpr (F8) {
+      // the products of the codes on the FP8 matrix cores (E4M3 x E4M3, unit
+      // block scales, one 16x16x128 product per block): lane (c16, q4) holds
+      // the 32 codes at k = 32 q4 .. 32 q4 + 31 of its row in both operands
+      const unsigned char* X8 = c8 + (kk ? 0 : F::TB8);
+      const int xr = 16 * rb + c16;
+      const i32x8_t bx = *(const i32x8_t*)(X8 + xr * DK + 32 * code8_pair(xr, q4));
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         if (J <= rb) {
-          const bf16x8_t aK = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * J + c16, 32 * ks + 8 * q4));
-          xt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bx, xt[J], 0, 0, 0);
+          const int kr = 16 * J + c16;
+          const i32x8_t aK = *(const i32x8_t*)(c8 + kr * DK + 32 * code8_pair(kr, q4));
+          xt[J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aK, bx, xt[J], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    } else {
+      const E* Xs = kk ? Ks : Qs;
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8_t bx = *(const bf16x8_t*)(Xs + kq_off<DK>(16 * rb + c16, 32 * ks + 8 * q4));
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          if (J <= rb) {
+            const bf16x8_t aK = *(const bf16x8_t*)(Ks + kq_off<DK>(16 * J + c16, 32 * ks + 8 * q4));
+            xt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aK, bx, xt[J], 0, 0, 0);
+          }
         }
       }
     }
@@ -2210,7 +2239,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
         decode(b);
         lds_barrier();  // the decoded tiles and the scaled row words
       }
-      prep_chunk(tiles_of(b), words_of(b), len);
+      prep_chunk(tiles_of(b), words_of(b), b, len);
       if (req) publish();
       if (ci == 0) {
         for (int q = 0; q < cur.nsib; ++q) {
