@@ -11,7 +11,9 @@ tree at full size; the fork copies bit for bit (every child's start state is
 its parent's end state); the FP8 launch against the bf16 launch on the decoded
 inputs where those are exact in bf16 (unit scales: the two differ only in the
 order the matrix cores sum the products Q K^T and K K^T); and the host
-rejections. The cost of quantising is reported as the option softmax's
+rejections; and the launch recorded once in a graph for a capacity bucket,
+replayed on two trees bit for bit against the eager launch. The cost of
+quantising is reported as the option softmax's
 total-variation distance to the float32 oracle on the unquantised inputs."""
 import numpy as np
 import pytest
@@ -216,4 +218,74 @@ def test_fp8_gdn_rejections():
         B.gdn_fork_forward_fp8(sess.meta, z8.data_ptr() + 1, sc, z8, sc, z8, sc, ab, ab, None, o, st, None, H, 128,
                                128, 1.0)
     assert e.value.status == -1  # (q8 not 16-byte aligned)
+    sess.close()
+
+
+def test_fp8_gdn_graph_replay_two_trees():
+    """The FP8 launch recorded once in a graph for a capacity bucket (every
+    depth up to the bucket's, the tree read from the blob), then replayed after
+    each of two trees is built into the same blob: every replay equals the
+    eager launch on that tree bit for bit (o, start and end states), with
+    eager work and synchronisations between the replays."""
+    t_cap, s_cap, depth_cap, gH = 3072, 96, 3, 4
+    sess = ForkSession(t_cap, s_cap, depth_cap, 1, D=64, gH=gH, dk=128, dv=128)
+    wls = []
+    for seed in (31, 32):
+        rng = np.random.default_rng(seed)
+        parent, seg_len = W.random_tree(rng, int(rng.integers(20, 60)), 90, max_depth=4, roots=2)
+        wls.append(W.make_workload("gdn8_graph", "bf16", parent, seg_len, H=1, Hkv=1, D=64, gH=gH, dk=128,
+                                   dv=128, gates="sigmoid", root_state_std=0.5, seed=seed))
+        assert wls[-1].T <= t_cap and wls[-1].S <= s_cap
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    # bucket-sized inputs and outputs, filled per tree
+    q8, k8, v8 = (torch.zeros((t_cap, gH, 128), dtype=torch.uint8, device="cuda") for _ in range(3))
+    qs, ks, vs = (torch.ones((t_cap, gH), device="cuda") for _ in range(3))
+    a, b = torch.ones((t_cap, gH), device="cuda"), torch.zeros((t_cap, gH), device="cuda")
+    root = torch.zeros((2, gH, 128, 128), device="cuda")
+    go = torch.full((t_cap, gH, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    s0 = torch.full((s_cap, gH, 128, 128), float("nan"), device="cuda")
+    s1 = torch.full_like(s0, float("nan"))
+
+    def load(wl):
+        for (codes, sc), dst, dsc in zip([quantize_rows(x) for x in (wl.gq, wl.gk, wl.gv)], (q8, k8, v8),
+                                         (qs, ks, vs)):
+            dst[:wl.T].copy_(dev(codes, torch.uint8))
+            dsc[:wl.T].copy_(dev(sc, torch.float32))
+        a[:wl.T].copy_(dev(wl.a, torch.float32))
+        b[:wl.T].copy_(dev(wl.b, torch.float32))
+        root.copy_(dev(wl.root_state, torch.float32))
+        sess.build(wl.parent, wl.seg_len)
+
+    def launch():
+        sess.gdn_fp8(q8, qs, k8, ks, v8, vs, a, b, go, s0, s1, root_state=root)
+
+    def snapshot(wl):
+        torch.cuda.synchronize()
+        return [x[:n].float().cpu().numpy().copy() for x, n in ((go, wl.T), (s0, wl.S), (s1, wl.S))]
+
+    eager = []
+    for wl in wls:
+        load(wl)
+        launch()
+        eager.append(snapshot(wl))
+    load(wls[0])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    for rep, i in enumerate((0, 1, 0, 1)):
+        load(wls[i])
+        go.fill_(float("nan"))
+        s0.fill_(float("nan"))
+        s1.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot(wls[i])
+        for name, x, y in zip(("o", "start", "final"), got, eager[i]):
+            np.testing.assert_array_equal(x.view(np.int32), y.view(np.int32), err_msg=f"replay {rep} {name}")
+        log(f"  replay {rep} (tree {i}: T={wls[i].T} S={wls[i].S}) equals the eager launch")
+    go_ref, s0_ref, s1_ref = oracle_on(wls[1], [decoded(*quantize_rows(x)) for x in (wls[1].gq, wls[1].gk,
+                                                                                      wls[1].gv)])
+    check_close("gdn8 graph o", eager[1][0].astype(np.float64), go_ref, "bf16")
+    check_close("gdn8 graph final_state", eager[1][2].astype(np.float64), s1_ref, "bf16", kind="f32")
+    del graph
     sess.close()
