@@ -71,12 +71,22 @@ struct AttnCfg {
                                         : (kAttnKeys * KS > VROWS * VS ? kAttnKeys * KS : VROWS * VS) * ESZ;
 };
 
-// bf16 K/V tiles are written by DMA as whole 16-byte chunks, unpadded, with the
+// K/V tiles are written by DMA as whole 16-byte chunks, unpadded, with the
 // chunks of each row permuted so that the reads below meet no LDS bank
-// conflicts: chunk c of key row r sits at position c ^ (r mod 8) in K (8
-// consecutive rows read the same chunk) and at c ^ 2 (r mod 4) in V (4
-// consecutive rows read 2 adjacent chunks through the transposing reads).
-__device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 7); }
+// conflicts on the 64 banks of 4 bytes (a 16-byte read serves 16 lanes per
+// cycle, an 8-byte read 32). CPR: chunks per row. K: chunk c of key row r at
+// c ^ (r mod CPR), so the 16 rows one cycle reads at one chunk (CPR = 16) take
+// 16 different bank groups. V: at c ^ 4 (r mod 4) (CPR = 16), so the
+// transposing reads of 4 rows x 2 adjacent chunk pairs that one cycle serves
+// take 8 different 32-byte bank groups; c ^ 2 (r mod 4) for rows of 8 chunks.
+template <int CPR>
+__device__ __forceinline__ int k_chunk_pos(int r, int c) {
+  return c ^ (r & (CPR - 1));
+}
+// E4M3 key rows are 128 bytes (8 chunks), two rows per 256-byte bank cycle:
+// chunk c of row r at c ^ ((r / 2) mod 8), so 16 consecutive rows read at one
+// chunk take 16 different bank groups.
+__device__ __forceinline__ int k8_chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Lanes l and l ^ 32 hold one query row's scores. lane_pair gives every lane
 // both of their values (its own and its partner's, in either order) by one
@@ -90,15 +100,18 @@ __device__ __forceinline__ LanePair lane_pair(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
-__device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) << 1); }
+template <int CPR>
+__device__ __forceinline__ int v_chunk_pos(int r, int c) {
+  return CPR >= 16 ? c ^ ((r & 3) << 2) : c ^ ((r & 3) << 1);
+}
 
 // DMA of keys [j0, j0 + 64) of kv head g (rows past jmax repeat row jmax) into
 // one K/V buffer: the buffer is a sequence of 1 KB blocks, block n filled by
 // one 64-lane instruction (lane l writes 16 bytes at n * 1024 + 16 l); each
 // wave issues its share of the blocks.
 typedef __attribute__((address_space(3))) void lds_void_t;
-// FP8 keys: the K tile is 64 rows of D bytes, chunk c of row r at c ^ (r mod
-// 8) too; each wave also loads 8 of the tile's key scales (one dword per
+// FP8 keys: the K tile is 64 rows of D bytes, chunk c of row r at
+// k8_chunk_pos(r, c); each wave also loads 8 of the tile's key scales (one dword per
 // lane, lanes 0-7) to KS_OFF, so every wave issues the same number of DMAs.
 template <int D>
 __device__ __forceinline__ void kv_dma_f8(unsigned char* buf, const unsigned char* __restrict__ K8,
@@ -112,7 +125,7 @@ __device__ __forceinline__ void kv_dma_f8(unsigned char* buf, const unsigned cha
   {
     const int slot = wave * 64 + lane, r = slot / KCPR, pos = slot % KCPR;
     const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
-    __builtin_amdgcn_global_load_lds((const void*)(K8 + row * D + 16 * k_chunk_pos(r, pos)),
+    __builtin_amdgcn_global_load_lds((const void*)(K8 + row * D + 16 * k8_chunk_pos(r, pos)),
                                      (lds_void_t*)(buf + wave * 1024), 16, 0, 0);
   }
 #pragma unroll
@@ -120,7 +133,7 @@ __device__ __forceinline__ void kv_dma_f8(unsigned char* buf, const unsigned cha
     const int n = wave * 2 + i;
     const int slot = n * 64 + lane, r = slot / VCPR, pos = slot % VCPR;
     const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
-    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos(r, pos)),
+    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos<VCPR>(r, pos)),
                                      (lds_void_t*)(buf + C::V_OFF + n * 1024), 16, 0, 0);
   }
   if (lane < 8) {
@@ -143,9 +156,9 @@ __device__ __forceinline__ void kv_dma(unsigned char* buf, const unsigned short*
     const int n = wave * PER_WAVE + i;
     const int slot = n * 64 + lane, r = slot / CPR, pos = slot % CPR;
     const size_t row = (size_t)min(j0 + r, jmax) * Hkv + g;
-    __builtin_amdgcn_global_load_lds((const void*)(K + row * D + 8 * k_chunk_pos(r, pos)),
+    __builtin_amdgcn_global_load_lds((const void*)(K + row * D + 8 * k_chunk_pos<CPR>(r, pos)),
                                      (lds_void_t*)(buf + n * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos(r, pos)),
+    __builtin_amdgcn_global_load_lds((const void*)(V + row * D + 8 * v_chunk_pos<CPR>(r, pos)),
                                      (lds_void_t*)(buf + kAttnKeys * D * 2 + n * 1024), 16, 0, 0);
   }
 }
@@ -523,8 +536,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
           const int kr = 32 * b + l32;
 #pragma unroll
           for (int ks = 0; ks < D / 64; ++ks) {
-            const u32x4_t lo = *(const u32x4_t*)(K8 + kr * D + 16 * k_chunk_pos(kr, 4 * ks + 2 * hi));
-            const u32x4_t hi4 = *(const u32x4_t*)(K8 + kr * D + 16 * k_chunk_pos(kr, 4 * ks + 2 * hi + 1));
+            const u32x4_t lo = *(const u32x4_t*)(K8 + kr * D + 16 * k8_chunk_pos(kr, 4 * ks + 2 * hi));
+            const u32x4_t hi4 = *(const u32x4_t*)(K8 + kr * D + 16 * k8_chunk_pos(kr, 4 * ks + 2 * hi + 1));
             const i32x8_t a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
             // formats 0 (E4M3) for both operands, unit block scales (E8M0 127)
@@ -544,7 +557,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         for (int ks = 0; ks < C::NKF; ++ks) {
           if constexpr (BF16) {
             const int kr = 32 * b + l32;
-            const bf16x8_t a = *(const bf16x8_t*)(Ks + kr * D + 8 * k_chunk_pos(kr, 2 * ks + hi));
+            const bf16x8_t a = *(const bf16x8_t*)(Ks + kr * D + 8 * k_chunk_pos<D / 8>(kr, 2 * ks + hi));
             s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[b], 0, 0, 0);
           } else {
             const float a = Ks[(32 * b + l32) * C::KS + 2 * ks + hi];
@@ -637,7 +650,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
             for (int db = 0; db < C::NDB; ++db) {
               const int col = 32 * db + 16 * (g16 & 1) + 4 * (L16 & 3);
               // col = 8 * chunk + 4 * half; krow and krow + 8 agree mod 4
-              const int vpos = 8 * v_chunk_pos(krow, col >> 3) + (col & 7);
+              const int vpos = 8 * v_chunk_pos<D / 8>(krow, col >> 3) + (col & 7);
               const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + krow * D + vpos));
               const s16x4_t hi4 =
                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + (krow + 8) * D + vpos));

@@ -1188,10 +1188,15 @@ struct CoopCfg {
 };
 
 // K/Q tiles in LDS: rows of DK bf16, unpadded; the 16-byte chunks of row r
-// are permuted (chunk c at position c ^ kq_swz(r)) so that the row reads (16
-// rows, one column) meet at most 2-way bank conflicts and the transposing
-// reads (4 rows, 32 bytes) none.
-__device__ __forceinline__ int kq_swz(int r, int cpr) { return (((r & 3) << 1) | ((r >> 2) & 1)) & (cpr - 1); }
+// are permuted (chunk c at position c ^ kq_swz(r)) against conflicts on the 64
+// banks of 4 bytes (one cycle serves 16 lanes of a 16-byte read, 32 of an
+// 8-byte one). Rows of 16 chunks: kq_swz(r) = 2 (r mod 8) + (r / 8 mod 2), so
+// the row reads (16 rows at one chunk) take 16 different bank groups and the
+// transposing reads (8 rows x 32 bytes per cycle) 8 different pair slots.
+// Rows of 8 chunks: 2 (r mod 4) + (r / 4 mod 2).
+__device__ __forceinline__ int kq_swz(int r, int cpr) {
+  return cpr >= 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r & 3) << 1) | ((r >> 2) & 1)) & (cpr - 1));
+}
 template <int DK>
 __device__ __forceinline__ int kq_off(int r, int col) {
   return r * DK + 8 * ((col >> 3) ^ kq_swz(r, DK / 8)) + (col & 7);
