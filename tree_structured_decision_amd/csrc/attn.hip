@@ -870,15 +870,18 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
 // Combines the parts of split query tiles: for each row,
 // o = sum_p exp(lse_p - lse) o_p with lse = log sum_p exp(lse_p).
 // A work item is (split tile, kv head, group of 16 rows); 16 threads share a
-// row and each combines D / 16 of its columns, with the loads of all parts
-// issued together.
+// row and each combines D / 16 consecutive columns of it. Every load of an
+// item (each part's log-sum-exp and columns) is issued before any of them is
+// used, so an item costs one memory round trip.
 constexpr int kMergeRows = 16;
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __restrict__ blob, AttnArgs args) {
   using E = typename std::conditional<BF16, unsigned short, float>::type;
   constexpr size_t SLOT = (size_t)kAttnRows * D * sizeof(E) + (size_t)kAttnRows * 4;  // bytes per partial slot
   constexpr int NRG = kAttnRows / kMergeRows;  // row groups per tile
-  constexpr int C4 = D / 4 / 16;               // 4-column groups per thread
+  constexpr int CPT = D / 16;                  // columns per thread
+  constexpr int NDW = CPT * (int)sizeof(E) / 4;  // their dwords
+  static_assert(NDW == 2 || NDW % 4 == 0, "8-byte or whole 16-byte loads");
   if (!blob_ok(blob, args.guard)) return;
   const int nmerge = blob[MH_NMERGE];
   const int TT = blob[MH_TILE_TOKENS];
@@ -895,58 +898,72 @@ __global__ void __launch_bounds__(256) fork_attn_merge_kernel(const int32_t* __r
     const unsigned char* part0 = args.ws + ((size_t)s0 * Hkv + g) * SLOT;
     const size_t pstride = (size_t)Hkv * SLOT;
     float lp[kMaxSplit];
-    float m = -INFINITY;
+    unsigned wv[kMaxSplit][NDW];
 #pragma unroll
     for (int p = 0; p < kMaxSplit; ++p) {
-      lp[p] = p < np ? ((const float*)(part0 + p * pstride + (size_t)kAttnRows * D * sizeof(E)))[r] : -INFINITY;
-      m = fmaxf(m, lp[p]);
-    }
-    float den = 0.f;
-    float4 acc[C4];
+      lp[p] = -INFINITY;
+      if (p < np) {
+        const unsigned char* base = part0 + p * pstride;
+        lp[p] = ((const float*)(base + (size_t)kAttnRows * D * sizeof(E)))[r];
+        const unsigned* src = (const unsigned*)((const E*)base + (size_t)r * D + CPT * cq);
+        if constexpr (NDW == 2) {
+          const uint2 u = *(const uint2*)src;
+          wv[p][0] = u.x;
+          wv[p][1] = u.y;
+        } else {
 #pragma unroll
-    for (int c = 0; c < C4; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int q = 0; q < NDW; q += 4) {
+            const uint4 u = *(const uint4*)(src + q);
+            wv[p][q] = u.x;
+            wv[p][q + 1] = u.y;
+            wv[p][q + 2] = u.z;
+            wv[p][q + 3] = u.w;
+          }
+        }
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p) m = fmaxf(m, lp[p]);
+    float den = 0.f;
+    float acc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int p = 0; p < kMaxSplit; ++p) {
       if (p < np) {
         const float wgt = lp[p] == -INFINITY ? 0.f : __expf(lp[p] - m);
         den += wgt;
-        const E* prow = (const E*)(part0 + p * pstride) + (size_t)r * D;
 #pragma unroll
-        for (int c = 0; c < C4; ++c) {
-          float4 x;
-          if constexpr (BF16) {
-            const uint2 u = *(const uint2*)(prow + 4 * (cq + 16 * c));
-            x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-          } else {
-            x = *(const float4*)(prow + 4 * (cq + 16 * c));
-          }
-          acc[c].x += wgt * x.x;
-          acc[c].y += wgt * x.y;
-          acc[c].z += wgt * x.z;
-          acc[c].w += wgt * x.w;
+        for (int j = 0; j < CPT; ++j) {
+          const float x = BF16 ? __uint_as_float((j & 1) ? (wv[p][j >> 1] & 0xffff0000u) : (wv[p][j >> 1] << 16))
+                               : __uint_as_float(wv[p][j]);
+          acc[j] += wgt * x;
         }
       }
     }
     const float inv = 1.f / den;
     const int t = t0 + tl, h = g * G + hg;
+    unsigned* orow = (unsigned*)((E*)args.o + ((size_t)t * H + h) * D + CPT * cq);
+    unsigned ov[NDW];
+    if constexpr (BF16) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int c = 0; c < C4; ++c) {
-      E* orow = (E*)args.o + ((size_t)t * H + h) * D + 4 * (cq + 16 * c);
-      if constexpr (BF16) {
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        bf16x2_t p0, p1;
-        p0[0] = (__bf16)(acc[c].x * inv);
-        p0[1] = (__bf16)(acc[c].y * inv);
-        p1[0] = (__bf16)(acc[c].z * inv);
-        p1[1] = (__bf16)(acc[c].w * inv);
-        uint2 pk;
-        pk.x = __builtin_bit_cast(unsigned, p0);
-        pk.y = __builtin_bit_cast(unsigned, p1);
-        *(uint2*)orow = pk;
-      } else {
-        *(float4*)orow = make_float4(acc[c].x * inv, acc[c].y * inv, acc[c].z * inv, acc[c].w * inv);
+      for (int q = 0; q < NDW; ++q) {
+        bf16x2_t pr;
+        pr[0] = (__bf16)(acc[2 * q] * inv);
+        pr[1] = (__bf16)(acc[2 * q + 1] * inv);
+        ov[q] = __builtin_bit_cast(unsigned, pr);
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NDW; ++q) ov[q] = __float_as_uint(acc[q] * inv);
+    }
+    if constexpr (NDW == 2) {
+      *(uint2*)orow = make_uint2(ov[0], ov[1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NDW; q += 4) *(uint4*)(orow + q) = make_uint4(ov[q], ov[q + 1], ov[q + 2], ov[q + 3]);
     }
     if (args.lse && cq == 0) args.lse[(size_t)t * H + h] = m + __logf(den);
   }
