@@ -6,7 +6,7 @@ validates: the capacity queries and the metadata plan (with and without
 resumed contexts) on the workload trees and on many random trees, at exact
 capacities (no slack in any buffer) and with key-range splitting, plus the
 rejection paths (malformed trees, capacities exceeded, short staging
-buffers). Nothing here touches a GPU. Exits 0 when every call behaved; the
+buffers, the FP8 Gated DeltaNet entry point's argument checks). Nothing here touches a GPU. Exits 0 when every call behaved; the
 sanitizer aborts the process on the first invalid memory access."""
 import sys
 
@@ -96,7 +96,19 @@ def main():
     expect_error(lambda: B.fork_meta_size(big), CODE["FORK_E_CAPACITY"])
     bad_ctx = (np.array([0, 0, 0], np.int32), np.array([0, 4, 0], np.int32))
     expect_error(lambda: plan(p, L, ctx=bad_ctx), CODE["FORK_E_TREE"])
-    print(f"asan driver: {n} plans and 7 rejections checked", flush=True)
+    # argument checks of the FP8 Gated DeltaNet entry point, which run before
+    # any launch: a plan-only descriptor given a stand-in blob address (never
+    # dereferenced on these paths), integer stand-ins for the device pointers
+    meta = plan(p, L)
+    meta.dev = 1 << 20
+    meta.dev_bytes = 1 << 40
+    a16 = 1 << 21
+    fp8 = lambda q8=a16, qs=a16, dk=128: B.gdn_fork_forward_fp8(meta, q8, qs, a16, a16, a16, a16, a16, a16, None,
+                                                                 a16, a16, None, 4, dk, dk, 1.0, stream=0)
+    expect_error(lambda: fp8(qs=None), CODE["FORK_E_ARG"])
+    expect_error(lambda: fp8(dk=64), CODE["FORK_E_UNSUPPORTED"])
+    expect_error(lambda: fp8(q8=a16 + 1), CODE["FORK_E_ARG"])
+    print(f"asan driver: {n} plans and 10 rejections checked", flush=True)
 
 
 if __name__ == "__main__":
