@@ -1692,14 +1692,13 @@ __global__ void __launch_bounds__(CoopCfg<DK>::NT) gdn_coop_kernel(const int32_t
 // state (the parent's first child's start slot, where the parent's item left
 // it) and is copied into the segment's own slot; the end state goes to
 // seg_final_state and the first child's slot.
-// FP8 code tiles in LDS: rows of DK bytes whose 32-byte pairs of 16-byte
-// chunks are permuted by row (pair p at position p ^ (r mod 4)), so that the
-// 32-byte reads of 16 rows at one column meet few bank conflicts.
-// code8_pair: the position of pair p in row r (an involution);
-// code8_chunk: the chunk held at 16-byte position c of row r.
+// FP8 code tiles in LDS: rows of DK = 128 bytes (8 chunks of 16 bytes, two
+// rows per 256-byte bank cycle); chunk c of row r sits at position
+// c ^ ((r / 2) mod 8), so the 16-byte reads of 16 consecutive rows at one
+// chunk take 16 different bank groups. code8_chunk is its own inverse: the
+// position of chunk c, and the chunk held at position c.
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ int code8_pair(int r, int p) { return p ^ (r & 3); }
-__device__ __forceinline__ int code8_chunk(int r, int c) { return 2 * code8_pair(r, c >> 1) + (c & 1); }
+__device__ __forceinline__ int code8_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 struct FusedCfg {
   static constexpr int DK = 128, NW = 8, NT = 64 * NW;
@@ -1834,7 +1833,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
     if constexpr (F8) {
       // code tile i (K, Q, V): wave w loads its rows 8 w .. 8 w + 7 (1 KB);
       // lane l writes 16-byte position l % 8 of its row, which holds the
-      // row's 16-byte chunk code8_chunk(row, l % 8)
+      // row's chunk code8_chunk(row, l % 8)
       static_assert(F::BLK8 == 3 && F::NW == 8 && F::TB8 == 8 * 1024, "one 1 KB block of each code tile per wave");
       const int row = 8 * w + (lane >> 3);
       const size_t g = ((size_t)min(t0 + row, tl) * H + r.h) * DK + 16 * code8_chunk(row, lane & 7);
@@ -1953,13 +1952,17 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       // block scales, one 16x16x128 product per block): lane (c16, q4) holds
       // the 32 codes at k = 32 q4 .. 32 q4 + 31 of its row in both operands
       const unsigned char* X8 = c8 + (kk ? 0 : F::TB8);
-      const int xr = 16 * rb + c16;
-      const i32x8_t bx = *(const i32x8_t*)(X8 + xr * DK + 32 * code8_pair(xr, q4));
+      // the 32 codes of row r at k = 32 q4 .. 32 q4 + 31: chunks 2 q4 and 2 q4 + 1
+      auto codes32 = [&](const unsigned char* t, int r) __attribute__((always_inline)) {
+        const u32x4_t lo = *(const u32x4_t*)(t + r * DK + 16 * code8_chunk(r, 2 * q4));
+        const u32x4_t hi = *(const u32x4_t*)(t + r * DK + 16 * code8_chunk(r, 2 * q4 + 1));
+        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      const i32x8_t bx = codes32(X8, 16 * rb + c16);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         if (J <= rb) {
-          const int kr = 16 * J + c16;
-          const i32x8_t aK = *(const i32x8_t*)(c8 + kr * DK + 32 * code8_pair(kr, q4));
+          const i32x8_t aK = codes32(c8, 16 * J + c16);
           xt[J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aK, bx, xt[J], 0, 0, 0, 127, 0, 127);
         }
       }
