@@ -269,6 +269,8 @@ def test_plan_errors():
     assert _status(lambda: plan([-1, 1], [3, 3])) == -2
     assert _status(lambda: plan([-1, -2], [3, 3])) == -2
     assert _status(lambda: plan([-1, 0], [3, 0])) == -2          # empty segment
+    assert _status(lambda: plan([], [], t_cap=16, s_cap=4)) == -2  # no segments
+    assert "at least one segment" in B.fork_last_error()
     assert _status(lambda: plan(ok_p, ok_l, t_cap=5)) == -5      # token capacity
     assert _status(lambda: plan(ok_p, ok_l, s_cap=1)) == -5      # segment capacity
     assert _status(lambda: plan([-1, 0, 1, 2], [1, 1, 1, 1], depth_cap=2)) == -5
