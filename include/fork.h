@@ -267,7 +267,10 @@ fork_status fork_attn_forward_noalloc(const fork_meta* m, const void* q, const v
  * from root_state or zero. (The pages describe the layer and the fork in
  * prose: techfi24.com page, "Exact State Forking"; kongchang.com page,
  * "Gated DeltaNet layer".)
- * q/k [T,H,dk], v [T,H,dv], o [T,H,dv] of dtype dt; a/b [T,H] float32;
+ * q/k [T,H,dk], v [T,H,dv], o [T,H,dv] of dtype dt; a/b [T,H] float32,
+ * the decay gate a in [0, 1] (a = 0 forgets the state at that token; the
+ * chunked kernels floor log a at -20, so a gate below e^-20 acts as e^-20,
+ * which moves no decay factor by more than 2.1e-9);
  * root_state [R,H,dv,dk] float32 or null (zero; R roots in index order);
  * seg_start_state [S,H,dv,dk] float32 (required: the fork copies);
  * seg_final_state [S,H,dv,dk] float32 or null. States are row-major dv x dk.

@@ -291,6 +291,29 @@ def test_gdn_identity_dynamics_keep_state():
     np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-14)
 
 
+def test_gdn_zero_gate_forgets_history():
+    """a_t = 0: S_t = b_t v_t k_t^T whatever came before, so o_t = b_t (k_t . q_t)
+    v_t, and no output from t on changes when earlier inputs or the root state
+    do (the children fork from the root's end state, which is after t)."""
+    rng = np.random.default_rng(14)
+    parent, lens = W.tree_one_level(6, [4, 3])
+    T = int(lens.sum())
+    _, _, _, gq, gk, gv, a, b = rand_inputs(rng, T, H=2, dk=4, dv=3)
+    z = 3
+    a[z] = 0.0
+    S0 = rng.standard_normal((1, 2, 3, 4)).astype(np.float32)
+    o, _, s1 = oracle.gdn(parent, lens, gq, gk, gv, a, b, root_state=S0)
+    for h in range(2):
+        kq = float(gk[z, h].astype(np.float64) @ gq[z, h].astype(np.float64))
+        np.testing.assert_allclose(o[z, h], float(b[z, h]) * kq * gv[z, h].astype(np.float64), rtol=1e-12)
+    gq2, gk2, gv2, a2, b2 = (x.copy() for x in (gq, gk, gv, a, b))
+    _, _, _, gq2[:z], gk2[:z], gv2[:z], a2[:z], b2[:z] = rand_inputs(rng, z, H=2, dk=4, dv=3)
+    o2, _, s12 = oracle.gdn(parent, lens, gq2, gk2, gv2, a2, b2, root_state=-S0)
+    np.testing.assert_array_equal(o2[z:], o[z:])
+    np.testing.assert_array_equal(s12, s1)
+    assert not np.array_equal(o2[:z], o[:z])
+
+
 def test_fork_copies_parent_end_state():
     wl = W.tiny_one_level()
     o, s0, s1 = oracle.gdn(wl.parent, wl.seg_len, wl.gq, wl.gk, wl.gv, wl.a, wl.b)

@@ -201,6 +201,17 @@ __device__ __forceinline__ float lane_val(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// log a of a decay gate, floored at -20. A gate a = 0 (the state is
+// forgotten at that token) would give -inf, and the chunked form's decay
+// ratios exp(g_i - g_j) of prefix sums g would become -inf - (-inf) = NaN.
+// With the floor, every decay across such a token is at most e^-20 (about
+// 2e-9, far below an fp32 ulp of what it multiplies), and the prefix sums
+// stay small enough that ratios between tokens on one side of it keep fp32
+// accuracy (a floor of -128, which would give exact zeros, costs ~3e-4 on
+// fp32 outputs through the rounding of the larger sums). Gates below e^-20
+// act as e^-20: no decay factor moves by more than 2.1e-9.
+__device__ __forceinline__ float log_gate(float a) { return fmaxf(logf(a), -20.f); }
+
 // Inclusive prefix sum over the 64 lanes of a wave (within rows of 16 lanes by
 // DPP shifts, then each row adds the totals of the rows before it).
 __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
@@ -368,7 +379,7 @@ __global__ void __launch_bounds__(256, (PrepCfg<BF16, DK>::PER_CU))
       *(u32x4_t*)(Qs + row * LDK + ch * G::EPC) = row < len ? rq[i] : z4;
     }
     if (w == 0) {
-      const float la = wave_incl_scan(lane < len ? logf(ra) : 0.f, lane);
+      const float la = wave_incl_scan(lane < len ? log_gate(ra) : 0.f, lane);
       gs[lane] = la;
       bs[lane] = lane < len ? rb : 0.f;
       if constexpr (BF16) {
@@ -1986,7 +1997,7 @@ __global__ void __launch_bounds__(FusedCfg::NT, 1) gdn_fused_kernel(const int32_
       // (rows past the chunk hold the last row's position and take its sr,
       // so they keep its decay: g of the last row is the chunk's total)
       const float a = ((const float*)(x + F::XA))[lane];
-      const float L = wave_incl_scan(lane < len ? logf(a) : 0.f, lane);
+      const float L = wave_incl_scan(lane < len ? log_gate(a) : 0.f, lane);
       const int sr = min(lane, len - 1) - ((const int*)(x + F::XP))[lane];
       const float Lb = __shfl(L, sr > 0 ? sr - 1 : 0);
       const float la = sr > 0 ? L - Lb : L;
