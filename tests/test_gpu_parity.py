@@ -155,10 +155,11 @@ def test_deep_chain_past_planned_depths(dtype):
     full_check(wl)
 
 
-@pytest.mark.parametrize("H,Hkv", [(32, 1), (64, 2), (3, 1)])
+@pytest.mark.parametrize("H,Hkv", [(32, 1), (64, 2), (3, 1), (128, 2), (256, 1)])
 def test_large_and_odd_gqa_groups(H, Hkv):
-    """GQA groups of 32 and 64 query heads per kv head (8 and 4 tokens per
-    256-row tile) and 3 (rows not a multiple of the group)."""
+    """GQA groups of 32, 64 and 128 query heads per kv head (8, 4 and 2 tokens
+    per 256-row tile), 256 (the largest group: one token per tile) and 3 (rows
+    not a multiple of the group)."""
     rng = np.random.default_rng(H * 7 + Hkv)
     for trial in range(2):
         parent, seg_len = W.random_tree(rng, 7, 120, max_depth=3, roots=1 + trial)
