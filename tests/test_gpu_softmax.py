@@ -32,6 +32,7 @@ import pytest
 import oracle
 from tests.gpu_helpers import log, oracle_attn, run_hip
 from tests.test_gpu_attn_fp8 import run_qk8, session_for
+from tree_structured_decision_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +42,6 @@ SEG_LEN = np.array([700, 90, 33, 5, 70], np.int32)
 
 def stressed(dtype, D, pattern, seed, mag=1.0):
     """mag scales the score magnitudes (the keys)."""
-    from tree_structured_decision_amd import workloads as W
     wl = W.make_workload("softmax", dtype, PARENT, SEG_LEN, H=8, Hkv=2, D=D, gH=2, dk=32, dv=32,
                          gates="sigmoid", root_state_std=None, seed=seed)
     q, k = wl.q.copy(), wl.k.copy()
