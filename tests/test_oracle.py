@@ -188,6 +188,34 @@ def test_token_select_matches_full():
 
 # --------------------------------------------------------------------- GDN
 
+def test_attention_dominant_key_at_huge_scores():
+    """Scores of thousands of nats, far past exp's fp64 range: with one visible
+    key ahead of every other by more than 800 nats (exp(-800) is 0 in fp64),
+    o is that key's value row exactly and lse its score; with all of a row's
+    scores shifted by a constant, o stays and lse moves by the constant. (An
+    implementation that exponentiated the scores without subtracting their
+    maximum would return inf or NaN here.)"""
+    parent, lens = W.tree_one_level(5, [3, 2])
+    T, D = int(lens.sum()), 4
+    q = np.zeros((T, 1, D), np.float32)
+    k = np.zeros((T, 1, D), np.float32)
+    v = np.random.default_rng(21).standard_normal((T, 1, D)).astype(np.float32)
+    q[:, 0, 0] = 1.0
+    k[:, 0, 0] = 1000.0 * np.arange(1, T + 1)  # score(t, j) = 1000 (j + 1), scale 1
+    o, lse = oracle.attention(parent, lens, q, k, v, scale=1.0)
+    for t in range(T):
+        # the latest visible key, the row's own token, leads by >= 1000 nats
+        np.testing.assert_array_equal(o[t, 0], v[t, 0].astype(np.float64))
+        assert lse[t, 0] == 1000.0 * (t + 1)
+    k2 = k.copy()
+    k2[:, 0, 1] = 3.0  # + 3 q_1 k_1 ... with q_1 = 0: no change
+    q2 = q.copy()
+    q2[:, 0, 1] = 1.0  # now every score of every row rises by 3
+    o2, lse2 = oracle.attention(parent, lens, q2, k2, v, scale=1.0)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(lse2, lse + 3.0)
+
+
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
 def test_gdn_vs_stream_brute_force(S):
     rng = np.random.default_rng(100 + S)
