@@ -302,6 +302,26 @@ def test_gdn_full_write_reads_back_value():
     np.testing.assert_allclose(s0[2, 0] @ basis[4].astype(np.float64), 0, atol=1e-12)
 
 
+def test_gdn_full_write_reads_back_latest_value_any_unit_keys():
+    """a = 1, b = 1 and unit keys (not orthogonal): S_t = S_{t-1}(I - k_t k_t^T)
+    + v_t k_t^T maps k_t to v_t whatever S_{t-1} was, so reading with q_t = k_t
+    returns v_t, on every branch and from any root state."""
+    rng = np.random.default_rng(15)
+    parent, lens = W.tree_three_level(4, 2, 3, 2, 3)
+    T = int(lens.sum())
+    dk, dv = 6, 5
+    gk = rng.standard_normal((T, 2, dk))
+    gk /= np.linalg.norm(gk, axis=-1, keepdims=True)
+    gk = gk.astype(np.float32)
+    gv = rng.standard_normal((T, 2, dv)).astype(np.float32)
+    a = np.ones((T, 2), np.float32)
+    b = np.ones((T, 2), np.float32)
+    S0 = rng.standard_normal((1, 2, dv, dk)).astype(np.float32)
+    o, _, _ = oracle.gdn(parent, lens, gk.copy(), gk, gv, a, b, root_state=S0)
+    # |k| = 1 only to float32 rounding: k^T k = 1 + O(1e-7)
+    np.testing.assert_allclose(o, gv.astype(np.float64), atol=1e-5)
+
+
 def test_gdn_identity_dynamics_keep_state():
     """a = 1, b = 0: the state never changes, o_t = S0 q_t."""
     rng = np.random.default_rng(13)
