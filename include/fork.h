@@ -449,6 +449,25 @@ fork_status fork_quantize_fp8(const void* x, void* q, float* scales, int64_t row
 fork_status fork_linear_fp8_forward(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                                     void* y, int32_t M, int32_t N, int32_t K, int32_t accumulate, void* stream);
 
+/* ---------------------------------------------------------- decision readout
+ * Per-option probabilities of a decision request: the pages measure the
+ * engine by the probabilities it gives each candidate option, as their total
+ * variation distance to a float32 reference (kongchang.com page, section on
+ * performance) and by whether the chosen option stays the same (openai-hub.com
+ * page, section on the six variables); they define no scoring head. Reading
+ * taken: the options are the leaf segments; leaves sharing a parent form one
+ * decision group; for every option c
+ *   score[c] = sum_i w[i] * x[last token of c, i] / sqrt(C),
+ *   prob[c]  = exp(score[c]) / sum over c' in c's group of exp(score[c']),
+ * with fp32 accumulation (the softmax shifted by the group's maximum). Every
+ * segment that is not an option (roots, segments with children) gets score 0
+ * and prob 0. x [T, C] of dtype dt (a layer's output rows, e.g. o [T, H, D]
+ * with C = H * D), w [C] fp32, score and prob [S] fp32 (device, S from the
+ * blob); x and w 16-byte aligned, C a multiple of 8 in 8..65536. Two kernel
+ * launches, no allocation, no synchronisation, deterministic. */
+fork_status fork_option_readout(const fork_meta* m, const void* x, const float* w, int32_t C, float* score,
+                                float* prob, fork_dtype dt, void* stream);
+
 /* ------------------------------------------------------------ graph buckets
  * A compact set of pre-recorded execution graphs serves varied request mixes
  * (kongchang.com page, section "pre-recorded execution graphs"). A fork_graph

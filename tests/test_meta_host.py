@@ -519,3 +519,19 @@ def test_conv_inputs_argument_errors_without_gpu():
     # gdn_inputs without c needs only ab, the gate parameters and a, b
     assert _status(lambda: B.gdn_inputs_forward(meta, None, f, 0x3000, 0x4000, None, None, None, None, 0x5000,
                                                 2, 64, 64, 1e-6, B.FORK_BF16, stream=0)) == -1  # a is null
+
+
+def test_option_readout_argument_errors_without_gpu():
+    """The decision readout rejects bad arguments before any HIP call (device
+    pointers are never dereferenced)."""
+    parent, seg_len = np.array([-1, 0, 0], np.int32), np.array([4, 2, 3], np.int32)
+    meta, _, _ = plan(parent, seg_len, gqa=2)
+    meta.dev = 0x1000
+    meta.dev_bytes = B.fork_meta_size(meta.caps)[0]
+    fake = 0x2000
+    ro = lambda x=fake, w=fake, C=64, score=0x3000, prob=0x4000, dt=B.FORK_BF16: _status(
+        lambda: B.fork_option_readout(meta, x, w, C, score, prob, dt, stream=0))
+    assert ro(x=None) == -1 and ro(w=None) == -1 and ro(score=None) == -1 and ro(prob=None) == -1
+    assert ro(C=12) == -3 and ro(C=0) == -3 and ro(C=65544) == -3
+    assert ro(x=fake + 8) == -1 and ro(w=fake + 4) == -1
+    assert ro(dt=7) == -3

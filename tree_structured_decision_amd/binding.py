@@ -28,7 +28,7 @@ EXPORTS = ("fork_meta_size", "fork_meta_build", "fork_meta_plan", "fork_meta_bui
            "fork_meta_dense_mask", "fork_attn_workspace", "fork_attn_forward", "fork_attn_forward_ctx", "fork_attn_forward_noalloc", "fork_attn_forward_qk8",
            "gdn_fork_workspace", "gdn_fork_forward", "gdn_fork_forward_fp8", "fork_rope_forward", "fork_rope_copy_forward", "fork_conv_forward",
            "fork_gate_forward", "gdn_inputs_forward", "gdn_conv_inputs_forward", "fork_linear_forward",
-           "fork_quantize_fp8", "fork_linear_fp8_forward",
+           "fork_quantize_fp8", "fork_linear_fp8_forward", "fork_option_readout",
            "fork_graph_create", "fork_graph_launch",
            "fork_graph_destroy", "fork_last_error", "fork_version")
 
@@ -117,6 +117,7 @@ def lib() -> ctypes.CDLL:
             "fork_linear_forward": [vp, vp, vp, i32, i32, i32, i32, i32, vp],
             "fork_quantize_fp8": [vp, vp, vp, ctypes.c_int64, i32, i32, vp],
             "fork_linear_fp8_forward": [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
+            "fork_option_readout": [P(fork_meta), vp, vp, i32, vp, vp, i32, vp],
             "fork_graph_create": [P(fork_meta), P(fork_graph_args), vp, P(vp)],
             "fork_graph_launch": [vp, vp],
             "fork_graph_destroy": [vp],
@@ -324,6 +325,11 @@ def fork_gate_forward(meta: fork_meta, x, g, w, y, nheads: int, D: int, mode: in
                       dt: int, stream=None, ld_g: int = 0) -> None:
     _check(lib().fork_gate_forward(ctypes.byref(meta), _ptr(x), _ptr(g), ld_g, _ptr(w), _ptr(y), nheads, D,
                                    mode, float(eps), dt, _stream(stream)))
+
+
+def fork_option_readout(meta: fork_meta, x, w, C: int, score, prob, dt: int, stream=None) -> None:
+    _check(lib().fork_option_readout(ctypes.byref(meta), _ptr(x), _ptr(w), C, _ptr(score), _ptr(prob), dt,
+                                     _stream(stream)))
 
 
 def gdn_inputs_forward(meta: fork_meta, c, ab, a_log, dt_bias, q, k, v, a, b, H: int, dk: int,

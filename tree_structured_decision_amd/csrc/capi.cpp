@@ -742,6 +742,18 @@ fork_status fork_gate_forward(const fork_meta* m, const void* x, const void* g, 
   return launch_gate(m, x, g, (long long)ld_g, w, y, nheads, D, mode, eps, dt, (hipStream_t)stream);
 }
 
+fork_status fork_option_readout(const fork_meta* m, const void* x, const float* w, int32_t C, float* score,
+                                float* prob, fork_dtype dt, void* stream) {
+  g_err[0] = 0;
+  fork_status st = check_meta(m);
+  if (st) return st;
+  if (!x || !w || !score || !prob) return fail(FORK_E_ARG, "x, w, score and prob must be non-null");
+  if (C < 8 || C > 65536 || C % 8) return fail(FORK_E_UNSUPPORTED, "row size C=%d unsupported (multiple of 8, 8..65536)", C);
+  if ((uintptr_t)x % 16 || (uintptr_t)w % 16) return fail(FORK_E_ARG, "x and w must be 16-byte aligned");
+  if (dt != FORK_F32 && dt != FORK_BF16) return fail(FORK_E_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return launch_readout(m, x, w, C, score, prob, dt, (hipStream_t)stream);
+}
+
 fork_status gdn_inputs_forward(const fork_meta* m, const void* c, const void* ab, int64_t ld_ab, const float* a_log,
                                const float* dt_bias, void* q, void* k, void* v, float* a, float* b, int32_t H,
                                int32_t dk, int32_t dv, float eps, fork_dtype dt, void* stream) {

@@ -254,6 +254,8 @@ fork_status launch_linear(const void* x, const void* w, void* y, int M, int N, i
                           fork_dtype dt, hipStream_t stream);
 fork_status launch_quantize_fp8(const void* x, void* q, float* scales, long long rows, int K, fork_dtype dt,
                                 hipStream_t stream);
+fork_status launch_readout(const fork_meta* m, const void* x, const float* w, int C, float* score, float* prob,
+                           fork_dtype dt, hipStream_t stream);
 fork_status launch_linear_fp8(const void* xq, const float* x_scale, const void* wq, const float* w_scale, void* y,
                               int M, int N, int K, int accumulate, hipStream_t stream);
 size_t gdn_workspace_bytes(const fork_meta* m, int H, int dk, int dv);

@@ -253,6 +253,100 @@ int lanes_per_row(int D) {
   return L;
 }
 
+// Decision readout (a reading: the pages rank engines by the probabilities
+// they give the options, kongchang.com page, section on performance, but
+// define no scoring head). Options are the leaf segments; those sharing a
+// parent form one decision group. Option c's score is <w, x[last token of c]>
+// scaled by 1/sqrt(C), and its probability the softmax of the group's scores.
+//
+// Scores: one wave per segment (grid-stride); lane j sums the products of
+// 8-element column groups j, j + 64, ..., then a butterfly sum. Every
+// segment that is not an option gets score 0 and probability 0 here; the
+// probabilities of options are written by readout_softmax_kernel.
+template <bool BF16>
+__global__ void __launch_bounds__(kMixThreads) readout_score_kernel(const int32_t* __restrict__ blob, const void* x,
+                                                                    const float* __restrict__ w, int C,
+                                                                    float inv_sqrt_c, float* __restrict__ score,
+                                                                    float* __restrict__ prob, BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
+  const int S = blob[MH_S];
+  const int32_t* parent = blob + blob[MH_OFF_PARENT];
+  const int32_t* first_child = blob + blob[MH_OFF_FIRSTCHILD];
+  const int32_t* seg_start = blob + blob[MH_OFF_SEGSTART];
+  const int32_t* seg_len = blob + blob[MH_OFF_SEGLEN];
+  const int lane = threadIdx.x & 63, nc = C / 8;
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int nwaves = (int)((gridDim.x * blockDim.x) >> 6);
+  for (int s = wave; s < S; s += nwaves) {  // uniform over the wave
+    const bool option = parent[s] >= 0 && first_child[s] < 0;
+    float acc = 0.f;
+    if (option) {
+      const size_t base = (size_t)(seg_start[s] + seg_len[s] - 1) * (size_t)C;
+      for (int j = lane; j < nc; j += 64) {
+        float v[8];
+        load8<BF16>(x, base + 8 * (size_t)j, v);
+        const f32x4_t w0 = *(const f32x4_t*)(w + 8 * j), w1 = *(const f32x4_t*)(w + 8 * j + 4);
+        acc += v[0] * w0[0] + v[1] * w0[1] + v[2] * w0[2] + v[3] * w0[3];
+        acc += v[4] * w1[0] + v[5] * w1[1] + v[6] * w1[2] + v[7] * w1[3];
+      }
+      acc = group_sum(acc, 64);
+    }
+    if (lane == 0) {
+      score[s] = option ? acc * inv_sqrt_c : 0.f;
+      if (!option) prob[s] = 0.f;
+    }
+  }
+}
+
+// Probabilities: one wave per segment p that has children (grid-stride). The
+// children of p lie in (p, S) but need not be contiguous, so the wave scans
+// parent[] from p's lowest-index child on, 64 segments per step, each lane
+// keeping a running maximum and a sum of exponentials rescaled to it; the 64
+// partial (max, sum) pairs are then combined by a butterfly, and a second
+// scan writes exp(score - max) / sum for every option of the group. The order
+// of every reduction is fixed, so results are deterministic.
+__global__ void __launch_bounds__(kMixThreads) readout_softmax_kernel(const int32_t* __restrict__ blob,
+                                                                      const float* __restrict__ score,
+                                                                      float* __restrict__ prob, BlobGuard guard) {
+  if (!blob_ok(blob, guard)) return;
+  const int S = blob[MH_S];
+  const int32_t* parent = blob + blob[MH_OFF_PARENT];
+  const int32_t* first_child = blob + blob[MH_OFF_FIRSTCHILD];
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int nwaves = (int)((gridDim.x * blockDim.x) >> 6);
+  for (int p = wave; p < S; p += nwaves) {  // uniform over the wave
+    const int fc = first_child[p];
+    if (fc < 0) continue;
+    float m = -INFINITY, l = 0.f;
+    for (int s0 = fc; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      if (s < S && parent[s] == p && first_child[s] < 0) {
+        const float z = score[s];
+        if (z > m) {
+          l = l * expf(m - z) + 1.f;  // m = -inf, l = 0 on a lane's first option: 0 * 0 + 1
+          m = z;
+        } else {
+          l += expf(z - m);
+        }
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+      const float mx = fmaxf(m, m2);
+      // A lane that saw no option holds (-inf, 0) and contributes nothing;
+      // the guards keep -inf - -inf out of expf.
+      l = (l > 0.f ? l * expf(m - mx) : 0.f) + (l2 > 0.f ? l2 * expf(m2 - mx) : 0.f);
+      m = mx;
+    }
+    const float inv = 1.f / l;  // l = 0 only when no child of p is an option; then nothing is written
+    for (int s0 = fc; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      if (s < S && parent[s] == p && first_child[s] < 0) prob[s] = expf(score[s] - m) * inv;
+    }
+  }
+}
+
 int row_grid(long long rows, int L) {
   const long long rows_per_block = (long long)(kMixThreads / 64) * (64 / L);
   const long long want = (rows + rows_per_block - 1) / rows_per_block;
@@ -313,6 +407,25 @@ fork_status launch_gdn_inputs(const fork_meta* m, const void* c, const void* ab,
   else
     hipLaunchKernelGGL(gdn_inputs_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, blob, c, ab, a_log, dt_bias,
                        q, k, v, a, b, H, dk, dv, ld_ab, L, eps, blob_guard(m->caps));
+  FORK_HIP_CHECK(hipGetLastError());
+  return FORK_OK;
+}
+
+
+fork_status launch_readout(const fork_meta* m, const void* x, const float* w, int C, float* score, float* prob,
+                           fork_dtype dt, hipStream_t stream) {
+  const int32_t* blob = (const int32_t*)m->dev;
+  const int grid = row_grid((long long)m->caps.s_cap, 64);  // a wave per segment
+  const float inv_sqrt_c = (float)(1.0 / sqrt((double)C));
+  if (dt == FORK_BF16)
+    hipLaunchKernelGGL(readout_score_kernel<true>, dim3(grid), dim3(kMixThreads), 0, stream, blob, x, w, C,
+                       inv_sqrt_c, score, prob, blob_guard(m->caps));
+  else
+    hipLaunchKernelGGL(readout_score_kernel<false>, dim3(grid), dim3(kMixThreads), 0, stream, blob, x, w, C,
+                       inv_sqrt_c, score, prob, blob_guard(m->caps));
+  FORK_HIP_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(readout_softmax_kernel, dim3(grid), dim3(kMixThreads), 0, stream, blob,
+                     (const float*)score, prob, blob_guard(m->caps));
   FORK_HIP_CHECK(hipGetLastError());
   return FORK_OK;
 }

@@ -134,6 +134,22 @@ class ForkSession:
         dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
         B.fork_gate_forward(self.meta, x, g, w, y, nh, D, mode, eps, dt, stream=stream, ld_g=ld_g)
 
+    def option_readout(self, x, w, score=None, prob=None, stream=None):
+        """Per-option scores and per-decision-group probabilities of the built
+        tree from a layer's output x [T, ...] (rows of C = x[0].numel() values) and a
+        readout vector w [C] fp32: the options are the leaf segments, grouped by
+        parent. Returns (score, prob), fp32 [S] on the device (0 for segments that
+        are not options)."""
+        S = int(self.meta.num_segments)
+        C = x[0].numel()
+        if score is None:
+            score = torch.empty(S, dtype=torch.float32, device=x.device)
+        if prob is None:
+            prob = torch.empty(S, dtype=torch.float32, device=x.device)
+        dt = B.FORK_BF16 if x.dtype == torch.bfloat16 else B.FORK_F32
+        B.fork_option_readout(self.meta, x, w, C, score, prob, dt, stream=stream)
+        return score, prob
+
     def gdn_inputs(self, c, ab, a_log, dt_bias, q, k, v, a, b, eps: float = 1e-6, stream=None,
                    ld_ab: int = 0):
         """Gated DeltaNet inputs from the convolved projections c [T, 2 H dk + H dv]
