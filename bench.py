@@ -26,6 +26,9 @@ Also reported on the same JSON line:
   workloads     all five workloads (and the resumed agent history), eager and
                 graph replay, P50 / P95, per-layer roofline fractions;
   rates         option tokens/s, isolated-equivalent tokens/s, us per option;
+  readout       the decision readout on the GPU (per-option scores and
+                per-group probabilities of the whole tree), its time per call
+                and its distance to the host float64 readout of the same rows;
   measured_peaks  a bf16 GEMM and a device copy on this GPU;
   block_ops, mixers, stack  the hybrid-block pieces, mixers and a four-layer
                 stack on the one-request tree.
@@ -613,6 +616,39 @@ def cpu_stack_fidelity(wl, stack_inputs):
 
 
 
+def readout_entry(r: "Runner", meta, iters=50):
+    """The decision readout on the GPU (fork_option_readout) over the attention
+    output the last step left in r.o: per-option scores and per-group softmax
+    probabilities of every decision group of the tree. Event-timed over
+    `iters` calls; compared with the host float64 readout of the same rows."""
+    import torch
+    from tree_structured_decision_amd import metrics
+
+    parent = np.asarray(meta["parent"])
+    seg_len = np.asarray(meta["seg_len"], np.int64)
+    C = r.o[0].numel()
+    w = torch.from_numpy(np.random.default_rng(7).standard_normal(C).astype(np.float32)).cuda()
+    score, prob = r.sess.option_readout(r.o, w)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        r.sess.option_readout(r.o, w, score, prob)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    last = torch.from_numpy(np.cumsum(seg_len) - 1).cuda()
+    rows = r.o.index_select(0, last).float().cpu().numpy().astype(np.float64)
+    host = metrics.option_scores(rows, w.cpu().numpy(), parent, np.ones_like(seg_len))
+    p_gpu = prob.cpu().numpy().astype(np.float64)
+    err = max(float(np.abs(p_gpu[list(leaves)] - metrics.softmax64(sc)).max()) for leaves, sc in host.values())
+    n_opt = sum(len(leaves) for leaves, _ in host.values())
+    return dict(us=us, options=n_opt, groups=len(host), row_values=C,
+                max_abs_prob_diff_vs_host_fp64=err,
+                note="fork_option_readout on the attention output [T, 16 x 128] bf16: score = <w, last row> "
+                     "/ sqrt(C) per option, softmax per decision group (leaves sharing a parent); two "
+                     "launches, HIP events over the calls")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -656,6 +692,7 @@ def main():
     gdn8 = fp8_gdn(r, meta, args.steps, args.warmup)
     r.step()  # leave the graph replay's outputs in place for the fidelity check
     torch.cuda.synchronize()
+    readout = readout_entry(r, meta)
     f = layer_fracs(meta, eager)
     a_mean = eager["attention"]["mean_us"] * 1e-6
     g_mean = eager["gdn"]["mean_us"] * 1e-6
@@ -731,6 +768,7 @@ def main():
         "attention_fp8_scores": fp8,
         "gdn_fp8_inputs": gdn8,
         "rates": rates,
+        "readout": readout,
         "measured_peaks": peaks,
     }
     if not args.no_workloads:
