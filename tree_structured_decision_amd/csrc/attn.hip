@@ -477,6 +477,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
     const int t_row = valid ? tile.t0 + tl : tile.t1 - 1;
     const int h = g * G + (valid ? hg : 0);
     const int lo_row = t_row - tok_pos[t_row];
+    // a wave whose 32 rows all lie past the tile's tokens (a partial tile)
+    // skips the arithmetic of the key loop: its rows are never stored, and it
+    // still takes part in every barrier and key/value load. Rows map to tokens
+    // in order, so the wave's first row decides; the test is scalar.
+    const int wv_first = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) * 32;
+    const int ntok = tile.t1 - tile.t0 < TT ? tile.t1 - tile.t0 : TT;
+    const bool wave_live = __builtin_amdgcn_readfirstlane(div_g(wv_first)) < ntok;
 
     // F8: this lane's 32 bytes of each 64-wide k-step of its q row (A and B
     // of the FP8 product hold the same d indices at the same byte places), and
@@ -736,7 +743,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
         // (a returning atomic, counted with them) delays no tile wait
         if (nq == 0 && it.done) request_next();
         issue(fill, fslot);
-        kv_compute((const E*)cur, (const E*)(cur + C::V_OFF), pj[slot], ph[slot], po[slot]);
+        if (wave_live) kv_compute((const E*)cur, (const E*)(cur + C::V_OFF), pj[slot], ph[slot], po[slot]);
       };
       while (nq > 0) {
         step(lds2, 2, lds1, 1);
@@ -762,7 +769,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1)
           kv_load<BF16, D, E>(rg, it.cx ? Kc : K, it.cx ? Vc : V, it.j0, it.hi - 1, g, Hkv, tid);
         else
           request_next();
-        kv_compute(Ks, Vt, j0, hi_, own);
+        if (wave_live) kv_compute(Ks, Vt, j0, hi_, own);
       }
     }
 
