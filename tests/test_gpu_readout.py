@@ -124,3 +124,56 @@ def test_readout_request_mix_full_size():
         _check("request mix", parent, seg_len, x_dev, x64, w, sess)
     finally:
         sess.close()
+
+
+def test_readout_graph_replay_matches_eager():
+    """fork_option_readout recorded once in a graph (for one tree) and replayed
+    four times on two trees built in turn into the same blob, with the inputs
+    rewritten and the outputs poisoned between replays: every replay equals
+    the eager call on that tree bit for bit, and the eager calls meet the
+    oracle bars."""
+    C = 520
+    trees = [FORESTS["nested"], FORESTS["wide"]]
+    trees = [(np.array(p, np.int32), np.array(l, np.int32)) for p, l in trees]
+    t_cap = max(int(l.sum()) for _, l in trees)
+    s_cap = max(len(p) for p, _ in trees)
+    depth = max(caps_for(p, l, 1)["depth_cap"] for p, l in trees)
+    sess = ForkSession(t_cap=t_cap, s_cap=s_cap, depth_cap=depth, gqa_group=1, D=64, gH=1, dk=64, dv=64,
+                       device="cuda")
+    rng = np.random.default_rng(99)
+    xs = [rng.standard_normal((t_cap, C)).astype(np.float32) for _ in trees]
+    x = torch.empty((t_cap, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.from_numpy(rng.standard_normal(C).astype(np.float32)).cuda()
+    score = torch.empty(s_cap, dtype=torch.float32, device="cuda")
+    prob = torch.empty(s_cap, dtype=torch.float32, device="cuda")
+    try:
+        def load(i):
+            sess.build(*trees[i])
+            x.copy_(torch.from_numpy(xs[i]).to(torch.bfloat16))
+
+        eager = []
+        for i, (parent, seg_len) in enumerate(trees):
+            load(i)
+            sess.option_readout(x, w, score, prob)
+            torch.cuda.synchronize()
+            S = len(parent)
+            eager.append((score[:S].clone(), prob[:S].clone()))
+            x64 = x.float().cpu().numpy().astype(np.float64)
+            _check(f"graph tree {i}", parent, seg_len, x, x64[np.cumsum(seg_len) - 1], w.cpu().numpy(), sess)
+        load(0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sess.option_readout(x, w, score, prob)
+        for rep, i in enumerate((0, 1, 0, 1)):
+            load(i)
+            score.fill_(float("nan"))
+            prob.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            S = len(trees[i][0])
+            assert torch.equal(score[:S], eager[i][0]) and torch.equal(prob[:S], eager[i][1]), f"replay {rep}"
+            log(f"  readout replay {rep} (tree {i}) equals the eager call")
+        del graph
+    finally:
+        sess.close()
