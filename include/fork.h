@@ -464,8 +464,7 @@ fork_status fork_linear_fp8_forward(const void* xq, const float* x_scale, const 
  * and prob 0. x [T, C] of dtype dt (a layer's output rows, e.g. o [T, H, D]
  * with C = H * D), w [C] fp32, score and prob [S] fp32 (device, S from the
  * blob); x and w 16-byte aligned, C a multiple of 8 in 8..65536. Two kernel
- * launches, no allocation, no synchronisation, deterministic; may be recorded
- * in a graph (the launches read the tree from the blob at run time). */
+ * launches, no allocation, no synchronisation, deterministic. */
 fork_status fork_option_readout(const fork_meta* m, const void* x, const float* w, int32_t C, float* score,
                                 float* prob, fork_dtype dt, void* stream);
 
