@@ -108,7 +108,12 @@ def main():
     expect_error(lambda: fp8(qs=None), CODE["FORK_E_ARG"])
     expect_error(lambda: fp8(dk=64), CODE["FORK_E_UNSUPPORTED"])
     expect_error(lambda: fp8(q8=a16 + 1), CODE["FORK_E_ARG"])
-    print(f"asan driver: {n} plans and 10 rejections checked", flush=True)
+    # the decision readout's argument checks (same stand-ins)
+    ro = lambda x=a16, C=64: B.fork_option_readout(meta, x, a16, C, a16, a16, B.FORK_BF16, stream=0)
+    expect_error(lambda: ro(x=None), CODE["FORK_E_ARG"])
+    expect_error(lambda: ro(C=12), CODE["FORK_E_UNSUPPORTED"])
+    expect_error(lambda: ro(x=a16 + 8), CODE["FORK_E_ARG"])
+    print(f"asan driver: {n} plans and 13 rejections checked", flush=True)
 
 
 if __name__ == "__main__":
